@@ -1,0 +1,243 @@
+/*
+ * msa_oracle.c -- plain CPU oracle of the MiniMax Sparse Attention (MSA)
+ * forward path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header,
+ * table or constant with the HIP implementation and is never on the product
+ * path.
+ *
+ * Everything is computed straight from the definitions, row by row, in fp64:
+ *
+ *   stage 1  s[t,g,j] = (q^I[t,g] . k^I[j]) / sqrt(d_I)        for j <= p
+ *   stage 2  S[t,g,b] = max over j in block b with j <= p of s[t,g,j]
+ *            (-inf for a block with no visible key)
+ *   stage 3  selection = the forced local block local(t) = floor(p / Bk),
+ *            plus the best min(k-1, local(t)) blocks among 0..local(t)-1,
+ *            ranked by S descending, ties to the lower block index;
+ *            written ascending into k slots, -1 padded
+ *   stage 4  O[t,h] = softmax(q[t,h] K_g^T / sqrt(d_h)) V_g over exactly the
+ *            keys j <= p of the selected blocks of h's group g = h / (Hq/G);
+ *            lse = natural log of the softmax denominator (with the max added
+ *            back)
+ *
+ * Sources (the MSA study-notes page, dimensionstp.github.io/study-concept/msa):
+ *   stages 1-3: section 2-3 "Fixed attention budget", the three displayed
+ *     equations for s, S and the block set B; section 3-2 (max pooling of
+ *     causally visible token scores); section 3-4 (the local block is always
+ *     selected, no sink, no window).
+ *   budget: section 2-3 text (block size 128, top-k 16, at most 2048 tokens
+ *     per query and group counting the local block); the chipsbuilder news
+ *     page ("Che cos'e MSA": k*Bk = 2,048) agrees.
+ *   stage 4: section 1-1 (the causal GQA attention formula) restricted to the
+ *     support, section 2-3 (Main Branch equation), section 3-3 (exact softmax
+ *     on the support, per-head weights, selection shared by the group).
+ *
+ * Readings where the pages are silent (all stated in the design notes):
+ *   - k counts the local block (budget k*Bk tokens including it);
+ *   - ties go to the lower block index;
+ *   - query row t of a sequence sits at position p = N - T + t (prefill
+ *     T == N, decode T == 1 with the new token last in the cache);
+ *   - heads map to groups contiguously, g = h / (Hq / G);
+ *   - a block that is not yet visible scores -inf and is never a candidate;
+ *     the local block's S is its true causal max (selection ignores it).
+ *
+ * Inputs are the raw bf16 bit patterns (uint16); they are widened to fp64
+ * exactly.  Row-subset mode: every function works on a caller-chosen list of
+ * (b, t) query rows so that very long workloads can be checked on a sample.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+    int64_t B, T, N;
+    int32_t Hq, G, d_h, d_I, Bk, k;
+} msa_oracle_dims;
+
+static double widen_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int64_t position_of(const msa_oracle_dims *d, int64_t t)
+{
+    return d->N - d->T + t;
+}
+
+static int64_t block_count(const msa_oracle_dims *d)
+{
+    return (d->N + d->Bk - 1) / d->Bk;
+}
+
+int msa_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Stages 1 and 2.  S[r, g, blk] for every listed row r = (row_b[r], row_t[r]).
+ * qI_rows: [nrows, G, d_I] (the q^I vectors of the listed rows only),
+ * kI: [B, N, d_I]. */
+void msa_oracle_block_scores(const msa_oracle_dims *d, int64_t nrows,
+                             const int64_t *row_b, const int64_t *row_t,
+                             const uint16_t *qI_rows, const uint16_t *kI,
+                             double *S)
+{
+    const int64_t NB = block_count(d);
+    const double root = sqrt((double)d->d_I);
+    const int64_t G = d->G, dI = d->d_I;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t rg = 0; rg < nrows * G; ++rg) {
+        const int64_t r = rg / G, g = rg % G;
+        const int64_t b = row_b[r];
+        const int64_t p = position_of(d, row_t[r]);
+        const uint16_t *qv = qI_rows + (r * G + g) * dI;
+        double *out = S + (r * G + g) * NB;
+        double *qd = (double *)malloc(sizeof(double) * dI);
+        for (int64_t c = 0; c < dI; ++c)
+            qd[c] = widen_bf16(qv[c]);
+        for (int64_t blk = 0; blk < NB; ++blk)
+            out[blk] = -INFINITY;
+        for (int64_t j = 0; j <= p; ++j) {
+            const uint16_t *kv = kI + (b * d->N + j) * dI;
+            double dot = 0.0;
+            for (int64_t c = 0; c < dI; ++c)
+                dot += qd[c] * widen_bf16(kv[c]);
+            const double s = dot / root;
+            const int64_t blk = j / d->Bk;
+            if (s > out[blk])
+                out[blk] = s;
+        }
+        free(qd);
+    }
+}
+
+/* Stage 3.  idx[r, g, 0..k-1] from S[r, g, 0..NB-1]. */
+void msa_oracle_select(const msa_oracle_dims *d, int64_t nrows,
+                       const int64_t *row_t, const double *S, int32_t *idx)
+{
+    const int64_t NB = block_count(d);
+    const int64_t G = d->G, k = d->k;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t rg = 0; rg < nrows * G; ++rg) {
+        const int64_t r = rg / G;
+        const int64_t p = position_of(d, row_t[r]);
+        const int64_t local = p / d->Bk;
+        const double *sc = S + rg * NB;
+        int32_t *out = idx + rg * k;
+        const int64_t want = (k - 1 < local) ? k - 1 : local;
+        char *taken = (char *)calloc((size_t)(local > 0 ? local : 1), 1);
+        int64_t *chosen = (int64_t *)malloc(sizeof(int64_t) * (size_t)(want + 1));
+        /* Repeatedly take the best remaining candidate.  The strict ">" keeps
+         * the earliest (lowest) block among equal scores. */
+        for (int64_t n = 0; n < want; ++n) {
+            int64_t best = -1;
+            for (int64_t c = 0; c < local; ++c) {
+                if (taken[c])
+                    continue;
+                if (best < 0 || sc[c] > sc[best])
+                    best = c;
+            }
+            taken[best] = 1;
+            chosen[n] = best;
+        }
+        free(taken);
+        /* ascending block order */
+        for (int64_t a = 1; a < want; ++a) {
+            int64_t v = chosen[a], z = a - 1;
+            while (z >= 0 && chosen[z] > v) {
+                chosen[z + 1] = chosen[z];
+                --z;
+            }
+            chosen[z + 1] = v;
+        }
+        for (int64_t s = 0; s < k; ++s)
+            out[s] = -1;
+        for (int64_t s = 0; s < want; ++s)
+            out[s] = (int32_t)chosen[s];
+        out[want] = (int32_t)local;
+        free(chosen);
+    }
+}
+
+/* Stage 4.  O[r, h, :] and lse[r, h] for every listed row and every head.
+ * q_rows: [nrows, Hq, d_h]; K, V: [B, G, N, d_h]; idx: [nrows, G, k]. */
+void msa_oracle_attend(const msa_oracle_dims *d, int64_t nrows,
+                       const int64_t *row_b, const int64_t *row_t,
+                       const uint16_t *q_rows, const uint16_t *K,
+                       const uint16_t *V, const int32_t *idx, double *O,
+                       double *lse)
+{
+    const int64_t Hq = d->Hq, G = d->G, dh = d->d_h, k = d->k;
+    const int64_t hg = Hq / G;
+    const double root = sqrt((double)dh);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t rh = 0; rh < nrows * Hq; ++rh) {
+        const int64_t r = rh / Hq, h = rh % Hq;
+        const int64_t g = h / hg;
+        const int64_t b = row_b[r];
+        const int64_t p = position_of(d, row_t[r]);
+        const int32_t *sel = idx + (r * G + g) * k;
+        const uint16_t *qv = q_rows + (r * Hq + h) * dh;
+        double *qd = (double *)malloc(sizeof(double) * dh);
+        double *z = (double *)malloc(sizeof(double) * (size_t)(k * d->Bk));
+        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)(k * d->Bk));
+        for (int64_t c = 0; c < dh; ++c)
+            qd[c] = widen_bf16(qv[c]);
+        /* the support: visible keys of the distinct selected blocks */
+        int64_t n = 0;
+        for (int64_t s = 0; s < k; ++s) {
+            const int64_t blk = sel[s];
+            if (blk < 0)
+                continue;
+            int dup = 0;
+            for (int64_t u = 0; u < s; ++u)
+                if (sel[u] == blk)
+                    dup = 1;
+            if (dup)
+                continue;
+            for (int64_t j = blk * d->Bk; j < (blk + 1) * d->Bk && j <= p; ++j)
+                key[n++] = j;
+        }
+        const uint16_t *Kg = K + (b * G + g) * d->N * dh;
+        const uint16_t *Vg = V + (b * G + g) * d->N * dh;
+        double m = -INFINITY;
+        for (int64_t i = 0; i < n; ++i) {
+            const uint16_t *kv = Kg + key[i] * dh;
+            double dot = 0.0;
+            for (int64_t c = 0; c < dh; ++c)
+                dot += qd[c] * widen_bf16(kv[c]);
+            z[i] = dot / root;
+            if (z[i] > m)
+                m = z[i];
+        }
+        double l = 0.0;
+        double *o = O + (r * Hq + h) * dh;
+        for (int64_t c = 0; c < dh; ++c)
+            o[c] = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            const double w = exp(z[i] - m);
+            l += w;
+            const uint16_t *vv = Vg + key[i] * dh;
+            for (int64_t c = 0; c < dh; ++c)
+                o[c] += w * widen_bf16(vv[c]);
+        }
+        for (int64_t c = 0; c < dh; ++c)
+            o[c] /= l;
+        lse[r * Hq + h] = m + log(l);
+        free(qd);
+        free(z);
+        free(key);
+    }
+}

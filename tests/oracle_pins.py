@@ -1,0 +1,431 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each pin takes an ``oracle.OracleLib`` and raises AssertionError when the
+oracle disagrees with what the MSA pages and the mathematics fix:
+
+* brute force on tiny inputs (a dense score matrix with a causal mask, cut
+  into blocks and max-reduced; exhaustive enumeration of block subsets);
+* closed forms (zero keys, one-hot keys with a linear ramp, all-ties
+  selection, constant values, zero queries);
+* special cases that reduce to a library routine (dense causal GQA attention
+  via torch's scaled_dot_product_attention when k*Bk covers the context,
+  a masked SDPA for any selection, numpy.lexsort ranking);
+* the invariants the pages state (local block always selected, budget of at
+  most k*Bk keys, heads of a group share the selection).
+
+The same functions run against deliberately broken copies of the oracle in
+test_oracle_pins.py to show that each plausible mistake is caught.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from oracle import dims_of
+
+
+def _gen(seed):
+    return torch.Generator().manual_seed(seed)
+
+
+def _int_bf16(g, shape, lo=-4, hi=4):
+    return torch.randint(lo, hi + 1, shape, generator=g).to(torch.bfloat16)
+
+
+def _randn_bf16(g, shape):
+    return torch.randn(shape, generator=g).to(torch.bfloat16)
+
+
+def _all_rows(B, T):
+    return np.repeat(np.arange(B), T), np.tile(np.arange(T), B)
+
+
+def _brute_block_scores(qI, kI, T, N, Bk):
+    """Dense reference for stages 1+2 on one sequence: qI [T,G,dI], kI [N,dI]
+    -> [T, G, NB] with the full score matrix built by einsum and masked."""
+    q = qI.double().numpy()
+    k = kI.double().numpy()
+    dI = q.shape[-1]
+    s = np.einsum("tgc,jc->tgj", q, k) / math.sqrt(dI)
+    pos = (N - T) + np.arange(T)
+    future = np.arange(N)[None, :] > pos[:, None]
+    s = np.where(future[:, None, :], -np.inf, s)
+    NB = -(-N // Bk)
+    pad = np.full((T, s.shape[1], NB * Bk - N), -np.inf)
+    s = np.concatenate([s, pad], axis=2).reshape(T, s.shape[1], NB, Bk)
+    return s.max(axis=3)
+
+
+# ----------------------------------------------------------------- stages 1+2
+def pin_scores_brute_force(orc):
+    cases = [  # B, T, N, G, dI, Bk, integer-valued?
+        (2, 23, 23, 3, 8, 4, True),
+        (1, 7, 30, 2, 16, 8, True),
+        (2, 19, 19, 1, 4, 5, False),
+        (1, 1, 13, 2, 8, 4, False),
+        (1, 40, 40, 2, 32, 128, True),
+    ]
+    for ci, (B, T, N, G, dI, Bk, integer) in enumerate(cases):
+        g = _gen(10 + ci)
+        mk = _int_bf16 if integer else _randn_bf16
+        qI = mk(g, (B, T, G, dI))
+        kI = mk(g, (B, N, dI))
+        d = dims_of(B, T, N, G, G, 128, dI, Bk, 4)
+        rb, rt = _all_rows(B, T)
+        S = orc.block_scores(d, rb, rt, qI.reshape(B * T, G, dI), kI)
+        for b in range(B):
+            ref = _brute_block_scores(qI[b], kI[b], T, N, Bk)
+            got = S[b * T:(b + 1) * T]
+            assert np.array_equal(np.isneginf(got), np.isneginf(ref)), ci
+            fin = np.isfinite(ref)
+            if integer:
+                assert np.array_equal(got[fin], ref[fin]), ci
+            else:
+                assert np.allclose(got[fin], ref[fin], rtol=1e-12, atol=1e-12), ci
+
+
+def pin_scores_zero_keys(orc):
+    B, T, N, G, dI, Bk = 1, 33, 33, 2, 8, 8
+    g = _gen(1)
+    qI = _int_bf16(g, (B, T, G, dI))
+    kI = torch.zeros(B, N, dI, dtype=torch.bfloat16)
+    d = dims_of(B, T, N, G, G, 128, dI, Bk, 4)
+    rb, rt = _all_rows(B, T)
+    S = orc.block_scores(d, rb, rt, qI.reshape(B * T, G, dI), kI)
+    NB = -(-N // Bk)
+    for t in range(T):
+        vis = t // Bk  # last visible block (T == N)
+        for blk in range(NB):
+            want = 0.0 if blk <= vis else -np.inf
+            assert (S[t, :, blk] == want).all(), (t, blk)
+
+
+def pin_scores_ramp_closed_form(orc):
+    """q^I = c * e_0 and k^I[j] = j * e_0 give s_j = c * j / sqrt(d_I); the
+    block max is the last visible key for c > 0 and the first key for c < 0.
+    Uses T < N so that the bottom-right causal alignment is pinned too."""
+    B, T, N, G, dI, Bk = 1, 9, 50, 2, 4, 8
+    qI = torch.zeros(B, T, G, dI)
+    qI[..., 0, 0] = 2.0
+    qI[..., 1, 0] = -3.0
+    kI = torch.zeros(B, N, dI)
+    kI[0, :, 0] = torch.arange(N, dtype=torch.float32)
+    d = dims_of(B, T, N, G, G, 128, dI, Bk, 4)
+    rb, rt = _all_rows(B, T)
+    S = orc.block_scores(d, rb, rt, qI.to(torch.bfloat16).reshape(T, G, dI),
+                         kI.to(torch.bfloat16))
+    NB = -(-N // Bk)
+    for t in range(T):
+        p = N - T + t
+        for blk in range(NB):
+            lo = blk * Bk
+            if lo > p:
+                assert S[t, 0, blk] == -np.inf and S[t, 1, blk] == -np.inf
+                continue
+            hi = min(lo + Bk - 1, p)
+            assert S[t, 0, blk] == 2.0 * hi / 2.0, (t, blk)
+            assert S[t, 1, blk] == -3.0 * lo / 2.0, (t, blk)
+
+
+# ------------------------------------------------------------------- stage 3
+def _expected_ties(p, Bk, k):
+    L = p // Bk
+    m = min(k - 1, L)
+    return list(range(m)) + [L] + [-1] * (k - m - 1)
+
+
+def pin_select_all_ties(orc):
+    """Zero index queries make every visible block score 0: the selection is
+    the lowest min(k-1, L) blocks plus the local block L."""
+    for (B, T, N, G, Bk, k) in [(2, 70, 70, 2, 8, 4), (1, 5, 90, 3, 8, 6),
+                                (1, 300, 300, 1, 16, 16)]:
+        g = _gen(3)
+        qI = torch.zeros(B, T, G, 8, dtype=torch.bfloat16)
+        kI = _int_bf16(g, (B, N, 8))
+        d = dims_of(B, T, N, G, G, 128, 8, Bk, k)
+        rb, rt = _all_rows(B, T)
+        S = orc.block_scores(d, rb, rt, qI.reshape(B * T, G, 8), kI)
+        idx = orc.select(d, rt, S)
+        for r in range(B * T):
+            want = _expected_ties(N - T + rt[r], Bk, k)
+            for gg in range(G):
+                assert idx[r, gg].tolist() == want, (r, gg, idx[r, gg], want)
+
+
+def _best_subset_brute(scores, L, m):
+    """The unique m-subset of 0..L-1 whose every member beats every
+    non-member under (score desc, block asc), found by enumeration."""
+    found = []
+    for A in itertools.combinations(range(L), m):
+        Aset = set(A)
+        ok = True
+        for a in A:
+            for c in range(L):
+                if c in Aset:
+                    continue
+                if not (scores[a] > scores[c] or (scores[a] == scores[c] and a < c)):
+                    ok = False
+                    break
+            if not ok:
+                break
+        if ok:
+            found.append(A)
+    assert len(found) == 1
+    return list(found[0])
+
+
+def pin_select_exhaustive(orc):
+    g = np.random.default_rng(5)
+    Bk = 4
+    for (NB, k, lo, hi) in [(12, 4, -3, 3), (11, 5, 0, 1), (9, 9, -50, 50), (12, 1, 0, 2)]:
+        N = NB * Bk - 1
+        T = N
+        d = dims_of(1, T, N, 2, 2, 128, 8, Bk, k)
+        rt = np.arange(T)
+        S = g.integers(lo, hi + 1, size=(T, 2, NB)).astype(np.float64)
+        idx = orc.select(d, rt, S)
+        for t in range(T):
+            L = t // Bk
+            m = min(k - 1, L)
+            for gg in range(2):
+                best = _best_subset_brute(S[t, gg], L, m)
+                want = sorted(best) + [L] + [-1] * (k - m - 1)
+                assert idx[t, gg].tolist() == want, (t, gg)
+
+
+def pin_select_lexsort(orc):
+    g = np.random.default_rng(6)
+    Bk, k, NB = 16, 16, 200
+    N = T = NB * Bk
+    d = dims_of(1, T, N, 3, 3, 128, 8, Bk, k)
+    rt = g.integers(0, T, size=300)
+    S = np.round(g.normal(size=(rt.size, 3, NB)) * 4)  # many ties
+    idx = orc.select(d, rt, S)
+    for r in range(rt.size):
+        L = rt[r] // Bk
+        m = min(k - 1, L)
+        for gg in range(3):
+            cand = np.arange(L)
+            order = np.lexsort((cand, -S[r, gg, :L]))[:m]
+            want = sorted(cand[order].tolist()) + [L] + [-1] * (k - m - 1)
+            assert idx[r, gg].tolist() == want
+
+
+def pin_select_needle(orc):
+    """A key whose index vector equals the query's wins its block's place in
+    every later query's selection."""
+    B, N, G, dI, Bk, k = 1, 512, 2, 16, 16, 3
+    T = N
+    g = _gen(8)
+    kI = _int_bf16(g, (B, N, dI), -1, 1)
+    qI = _int_bf16(g, (B, T, G, dI), -1, 1)
+    u = torch.full((dI,), 4.0)
+    u[::2] = -4.0
+    kI[0, 77] = u.to(torch.bfloat16)  # block 4
+    qI[0, :, 1] = u.to(torch.bfloat16)
+    d = dims_of(B, T, N, G, G, 128, dI, Bk, k)
+    rb, rt = _all_rows(B, T)
+    S = orc.block_scores(d, rb, rt, qI.reshape(T, G, dI), kI)
+    idx = orc.select(d, rt, S)
+    for t in range(5 * Bk, T):
+        assert 4 in idx[t, 1].tolist(), t
+
+
+def pin_select_invariants(orc):
+    g = _gen(9)
+    B, T, N, G, dI, Bk, k = 2, 200, 200, 3, 8, 8, 5
+    qI = _int_bf16(g, (B, T, G, dI))
+    kI = _int_bf16(g, (B, N, dI))
+    d = dims_of(B, T, N, G, G, 128, dI, Bk, k)
+    rb, rt = _all_rows(B, T)
+    S = orc.block_scores(d, rb, rt, qI.reshape(B * T, G, dI), kI)
+    idx = orc.select(d, rt, S)
+    for r in range(B * T):
+        p = rt[r]
+        L = p // Bk
+        for gg in range(G):
+            sel = [x for x in idx[r, gg].tolist() if x >= 0]
+            assert sel == sorted(set(sel))
+            assert sel[-1] == L
+            assert len(sel) == min(k, L + 1)
+            assert all(x <= L for x in sel)
+            n_keys = sum(min(Bk, p - x * Bk + 1) for x in sel)
+            assert n_keys <= k * Bk
+            pad = idx[r, gg].tolist()[len(sel):]
+            assert all(x == -1 for x in pad)
+
+
+# ------------------------------------------------------------------- stage 4
+def _sdpa_reference(q, K, V, mask, hg):
+    """torch SDPA in fp64 with the K/V heads repeated for GQA.
+    q [T,Hq,dh], K/V [G,N,dh], mask [G or 1, T, N] bool (True = attend)."""
+    qq = q.double().permute(1, 0, 2)  # [Hq, T, dh]
+    kk = K.double().repeat_interleave(hg, dim=0)
+    vv = V.double().repeat_interleave(hg, dim=0)
+    mm = mask.repeat_interleave(hg, dim=0) if mask.shape[0] > 1 else mask
+    out = F.scaled_dot_product_attention(qq.unsqueeze(0), kk.unsqueeze(0),
+                                         vv.unsqueeze(0), attn_mask=mm.unsqueeze(0))
+    scores = (qq @ kk.transpose(1, 2)) / math.sqrt(qq.shape[-1])
+    scores = scores.masked_fill(~mm, -math.inf)
+    lse = torch.logsumexp(scores, dim=-1)  # [Hq, T]
+    return out[0].permute(1, 0, 2).numpy(), lse.permute(1, 0).numpy()
+
+
+def _mask_from_idx(idx, T, N, Bk, G):
+    """[G, T, N] bool: key j visible (j <= p) and in a selected block."""
+    m = torch.zeros(G, T, N, dtype=torch.bool)
+    for t in range(T):
+        p = N - T + t
+        for g in range(G):
+            for blk in idx[t, g].tolist():
+                if blk < 0:
+                    continue
+                lo = blk * Bk
+                hi = min(lo + Bk, p + 1)
+                if hi > lo:
+                    m[g, t, lo:hi] = True
+    return m
+
+
+def _attend_case(orc, B, T, N, Hq, G, dh, Bk, k, seed, idx_maker):
+    g = _gen(seed)
+    q = _randn_bf16(g, (B, T, Hq, dh))
+    K = _randn_bf16(g, (B, G, N, dh))
+    V = _randn_bf16(g, (B, G, N, dh))
+    d = dims_of(B, T, N, Hq, G, dh, 8, Bk, k)
+    rb, rt = _all_rows(B, T)
+    idx = idx_maker(d, rb, rt, g)
+    O, lse = orc.attend(d, rb, rt, q.reshape(B * T, Hq, dh), K, V, idx)
+    return q, K, V, idx, O.reshape(B, T, Hq, dh), lse.reshape(B, T, Hq)
+
+
+def pin_attend_dense_equivalence(orc):
+    """k*Bk covering the context makes MSA dense causal GQA attention."""
+    for (B, T, N, Hq, G, dh, Bk) in [(1, 40, 40, 4, 2, 16, 8),
+                                     (2, 11, 37, 6, 3, 8, 4),
+                                     (1, 130, 130, 2, 1, 32, 16)]:
+        NB = -(-N // Bk)
+        k = NB + 1
+
+        def all_blocks(d, rb, rt, g):
+            idx = np.full((rb.size, d.G, d.k), -1, dtype=np.int32)
+            for r in range(rb.size):
+                L = (N - T + rt[r]) // Bk
+                idx[r, :, :L + 1] = np.arange(L + 1)
+            return idx
+
+        q, K, V, idx, O, lse = _attend_case(orc, B, T, N, Hq, G, dh, Bk, k, 21,
+                                            all_blocks)
+        pos = (N - T) + torch.arange(T)
+        causal = (torch.arange(N)[None, :] <= pos[:, None]).unsqueeze(0)
+        for b in range(B):
+            refO, refL = _sdpa_reference(q[b], K[b], V[b], causal, Hq // G)
+            assert np.allclose(O[b], refO, rtol=1e-10, atol=1e-10)
+            assert np.allclose(lse[b], refL, rtol=1e-10, atol=1e-10)
+
+
+def pin_attend_masked_sdpa(orc):
+    """Any selection: attention over the support equals SDPA with the
+    support's boolean mask."""
+    B, T, N, Hq, G, dh, Bk, k = 1, 64, 64, 6, 3, 16, 4, 4
+
+    def random_sel(d, rb, rt, g):
+        S = torch.randn(rb.size, d.G, -(-N // Bk), generator=g).double().numpy()
+        return orc.select(d, rt, S)
+
+    q, K, V, idx, O, lse = _attend_case(orc, B, T, N, Hq, G, dh, Bk, k, 22,
+                                        random_sel)
+    mask = _mask_from_idx(idx, T, N, Bk, G)
+    refO, refL = _sdpa_reference(q[0], K[0], V[0], mask, Hq // G)
+    assert np.allclose(O[0], refO, rtol=1e-10, atol=1e-10)
+    assert np.allclose(lse[0], refL, rtol=1e-10, atol=1e-10)
+
+
+def pin_attend_k1_block_diagonal(orc):
+    """k = 1 keeps only the local block: block-diagonal causal attention."""
+    B, T, N, Hq, G, dh, Bk = 1, 45, 45, 4, 2, 8, 8
+
+    def local_only(d, rb, rt, g):
+        idx = np.zeros((rb.size, d.G, 1), dtype=np.int32)
+        idx[:, :, 0] = ((N - T + rt) // Bk)[:, None]
+        return idx
+
+    q, K, V, idx, O, lse = _attend_case(orc, B, T, N, Hq, G, dh, Bk, 1, 23,
+                                        local_only)
+    j = torch.arange(N)
+    pos = (N - T) + torch.arange(T)
+    mask = ((j[None, :] // Bk) == (pos[:, None] // Bk)) & (j[None, :] <= pos[:, None])
+    refO, refL = _sdpa_reference(q[0], K[0], V[0], mask.unsqueeze(0), Hq // G)
+    assert np.allclose(O[0], refO, rtol=1e-10, atol=1e-10)
+    assert np.allclose(lse[0], refL, rtol=1e-10, atol=1e-10)
+
+
+def pin_attend_closed_forms(orc):
+    """Zero queries: uniform weights, lse = ln(number of support keys) and O
+    the mean of V over the support.  Constant V: O equals that constant."""
+    B, T, N, Hq, G, dh, Bk, k = 1, 50, 50, 4, 2, 8, 8, 3
+    g = _gen(24)
+    q = torch.zeros(B, T, Hq, dh, dtype=torch.bfloat16)
+    K = _randn_bf16(g, (B, G, N, dh))
+    V = _randn_bf16(g, (B, G, N, dh))
+    d = dims_of(B, T, N, Hq, G, dh, 8, Bk, k)
+    rb, rt = _all_rows(B, T)
+    S = torch.randn(T, G, -(-N // Bk), generator=g).double().numpy()
+    idx = orc.select(d, rt, S)
+    O, lse = orc.attend(d, rb, rt, q.reshape(T, Hq, dh), K, V, idx)
+    for t in range(T):
+        for h in range(Hq):
+            gg = h // (Hq // G)
+            keys = []
+            for blk in idx[t, gg].tolist():
+                if blk >= 0:
+                    keys += list(range(blk * Bk, min(blk * Bk + Bk, t + 1)))
+            assert abs(lse[t, h] - math.log(len(keys))) < 1e-12
+            mean = V[0, gg, keys].double().mean(0).numpy()
+            assert np.allclose(O[t, h], mean, atol=1e-12)
+    Vc = torch.full((B, G, N, dh), 1.5, dtype=torch.bfloat16)
+    q2 = _randn_bf16(g, (B, T, Hq, dh))
+    O2, _ = orc.attend(d, rb, rt, q2.reshape(T, Hq, dh), K, Vc, idx)
+    assert np.allclose(O2, 1.5, atol=1e-12)
+
+
+def pin_decode_is_last_prefill_row(orc):
+    """A single new token at the end of a cache of length L is the last row
+    of the prefill over the same L tokens."""
+    B, N, Hq, G, dh, dI, Bk, k = 2, 77, 4, 2, 16, 8, 8, 3
+    g = _gen(25)
+    qI = _int_bf16(g, (B, N, G, dI))
+    kI = _int_bf16(g, (B, N, dI))
+    q = _randn_bf16(g, (B, N, Hq, dh))
+    K = _randn_bf16(g, (B, G, N, dh))
+    V = _randn_bf16(g, (B, G, N, dh))
+    dp = dims_of(B, N, N, Hq, G, dh, dI, Bk, k)
+    dd = dims_of(B, 1, N, Hq, G, dh, dI, Bk, k)
+    rb = np.arange(B)
+    full = orc.forward(dp, rb, np.full(B, N - 1), qI[:, N - 1], kI, q[:, N - 1], K, V)
+    dec = orc.forward(dd, rb, np.zeros(B, dtype=np.int64), qI[:, N - 1], kI,
+                      q[:, N - 1], K, V)
+    assert np.array_equal(full["idx"], dec["idx"])
+    assert np.array_equal(full["S"], dec["S"])
+    assert np.array_equal(full["O"], dec["O"])
+
+
+ALL_PINS = [
+    pin_scores_brute_force,
+    pin_scores_zero_keys,
+    pin_scores_ramp_closed_form,
+    pin_select_all_ties,
+    pin_select_exhaustive,
+    pin_select_lexsort,
+    pin_select_needle,
+    pin_select_invariants,
+    pin_attend_dense_equivalence,
+    pin_attend_masked_sdpa,
+    pin_attend_k1_block_diagonal,
+    pin_attend_closed_forms,
+    pin_decode_is_last_prefill_row,
+]

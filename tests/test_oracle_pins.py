@@ -1,0 +1,91 @@
+"""The CPU oracle against its pins, and the pins against planted mistakes.
+
+No GPU needed.  The mutation check compiles modified copies of the oracle
+source (each with one plausible mistake) and requires that at least one pin
+fails for every copy; each copy runs in a child process so that a mistake
+that crashes the oracle counts as caught without taking pytest down.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+import oracle_pins
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.OracleLib(oracle.build(force=False))
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(orc, pin):
+    pin(orc)
+
+
+# (name, text in the oracle source, replacement) -- one plausible mistake each
+MUTATIONS = [
+    ("score_drops_own_key", "for (int64_t j = 0; j <= p; ++j) {",
+     "for (int64_t j = 0; j < p; ++j) {"),
+    ("score_scale_inverted", "const double s = dot / root;",
+     "const double s = dot * root;"),
+    ("score_top_left_causal", "return d->N - d->T + t;", "return t;"),
+    ("score_block_of_key_wrong", "const int64_t blk = j / d->Bk;",
+     "const int64_t blk = (j + 1) / d->Bk < block_count(d) ? (j + 1) / d->Bk : j / d->Bk;"),
+    ("select_ties_to_higher_index", "if (best < 0 || sc[c] > sc[best])",
+     "if (best < 0 || sc[c] >= sc[best])"),
+    ("select_local_outside_budget",
+     "const int64_t want = (k - 1 < local) ? k - 1 : local;",
+     "const int64_t want = (k < local) ? k : local;"),
+    ("select_wrong_local", "out[want] = (int32_t)local;",
+     "out[want] = (int32_t)(local > 0 ? local - 1 : 0);"),
+    ("select_not_sorted", "while (z >= 0 && chosen[z] > v) {",
+     "while (z >= 0 && chosen[z] < v) {"),
+    ("select_lowest_score", "if (best < 0 || sc[c] > sc[best])",
+     "if (best < 0 || sc[c] < sc[best])"),
+    ("attend_interleaved_heads", "const int64_t g = h / hg;",
+     "const int64_t g = h % G;"),
+    ("attend_no_causal_mask_in_local_block",
+     "j < (blk + 1) * d->Bk && j <= p; ++j)", "j < (blk + 1) * d->Bk && j < d->N; ++j)"),
+    ("attend_missing_scale", "z[i] = dot / root;", "z[i] = dot;"),
+    ("attend_lse_without_max", "lse[r * Hq + h] = m + log(l);",
+     "lse[r * Hq + h] = log(l);"),
+    ("attend_unnormalised", "o[c] /= l;", "o[c] /= 1.0;"),
+    ("attend_drops_first_block", "if (blk < 0)\n                continue;",
+     "if (blk <= 0)\n                continue;"),
+    ("widen_wrong_shift", "uint32_t u = (uint32_t)bits << 16;",
+     "uint32_t u = (uint32_t)bits << 15;"),
+]
+
+_RUNNER = r"""
+import sys
+sys.path[:0] = [%r, %r]
+import oracle, oracle_pins
+orc = oracle.OracleLib(%r)
+failed = []
+for pin in oracle_pins.ALL_PINS:
+    try:
+        pin(orc)
+    except AssertionError:
+        failed.append(pin.__name__)
+print("FAILED_PINS", ",".join(failed))
+sys.exit(3 if failed else 0)
+"""
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+    src = oracle.source_text()
+    assert src.count(old) >= 1, "mutation anchor vanished: " + name
+    mutated = src.replace(old, new, 1)
+    so = oracle.build_variant(mutated, str(tmp_path), name)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = _RUNNER % (root, here, so)
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                         text=True, timeout=300, env=env)
+    # exit 3: some pin failed; any other non-zero: the mutant crashed
+    assert res.returncode != 0, (name, res.stdout[-2000:], res.stderr[-2000:])
