@@ -3,16 +3,7 @@
 The compute lives in ``libmsa.so`` (hand-written HIP kernels behind a C ABI,
 declared in ``include/msa.h``).  ``ops`` is a thin ctypes binding over it
 that marshals torch tensors (device pointers and the current HIP stream) and
-nothing else.  Importing this package does not load the library; the first
-op call does, and raises if it was not built.
+nothing else; the library is loaded on the first op call, which raises if it
+was not built.  ``accounting`` holds the algorithmic work counts.
 """
-from . import accounting  # noqa: F401
-
 __all__ = ["accounting", "ops"]
-
-
-def __getattr__(name):
-    if name == "ops":
-        from . import ops
-        return ops
-    raise AttributeError(name)

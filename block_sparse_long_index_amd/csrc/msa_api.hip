@@ -1,0 +1,237 @@
+// msa_api.hip -- the C ABI declared in include/msa.h: host-side validation,
+// workspace sizing and the launches.  No device memory is allocated here.
+#include "msa.h"
+#include "msa_internal.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kDefaultWindow = 16384;  // query rows per prefill window
+constexpr int64_t kMaxElems = int64_t(1) << 46;
+
+bool pow2_upto(int v, int hi) { return v >= 1 && v <= hi && (v & (v - 1)) == 0; }
+
+int check_dims(const msa_dims_t* d) {
+  if (!d) return fail(MSA_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (d->B < 1 || d->T < 1 || d->N < 1)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "B, T, N must be >= 1 (B=%lld T=%lld N=%lld)",
+                (long long)d->B, (long long)d->T, (long long)d->N);
+  if (d->T > d->N)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "T (%lld) exceeds N (%lld)", (long long)d->T,
+                (long long)d->N);
+  if (d->Hq < 1 || d->G < 1 || d->Hq % d->G != 0)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "Hq (%d) must be a positive multiple of G (%d)",
+                d->Hq, d->G);
+  if (d->k < 1 || d->Bk < 1 || d->d_h < 1 || d->d_I < 1)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "k, Bk, d_h, d_I must be >= 1");
+  if (d->d_h != 128 || d->d_I != 128 || d->Bk != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "only d_h = d_I = Bk = 128 (got %d, %d, %d)", d->d_h,
+                d->d_I, d->Bk);
+  if (d->k > 16) return fail(MSA_ERR_UNSUPPORTED, "k > 16 (got %d)", d->k);
+  if (!pow2_upto(d->G, 16)) return fail(MSA_ERR_UNSUPPORTED, "G must be 1, 2, 4, 8 or 16");
+  if (!pow2_upto(d->Hq / d->G, 16))
+    return fail(MSA_ERR_UNSUPPORTED, "Hq / G must be 1, 2, 4, 8 or 16");
+  if (d->B > 65535) return fail(MSA_ERR_UNSUPPORTED, "B > 65535");
+  if (d->N > (int64_t(1) << 30)) return fail(MSA_ERR_UNSUPPORTED, "N > 2^30");
+  const int64_t NB = (d->N + 127) / 128;
+  if (d->B * d->T * d->Hq > kMaxElems / 128 || d->B * d->G * d->N > kMaxElems / 128 ||
+      d->B * d->G * d->T * NB > kMaxElems || d->B * d->G * NB > (int64_t(1) << 30))
+    return fail(MSA_ERR_UNSUPPORTED, "problem too large");
+  return MSA_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(MSA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) & 15)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return MSA_OK;
+}
+
+#define MSA_TRY(x)               \
+  do {                           \
+    const int rc_ = (x);         \
+    if (rc_ != MSA_OK) return rc_; \
+  } while (0)
+
+int64_t nblocks(const msa_dims_t* d) { return (d->N + 127) / 128; }
+
+size_t decode_select_ws(const msa_dims_t* d) {
+  return static_cast<size_t>(d->B * d->G * nblocks(d)) * sizeof(float);
+}
+
+int64_t default_window(const msa_dims_t* d) {
+  const int64_t rows = d->B * d->T;
+  return rows < kDefaultWindow ? rows : kDefaultWindow;
+}
+
+size_t prefill_ws(const msa_dims_t* d, int64_t window) {
+  return msa::attn_workspace_bytes(window, d->B, d->N, d->G, d->Hq / d->G, d->k, false);
+}
+
+size_t decode_ws(const msa_dims_t* d) {
+  return msa::attn_workspace_bytes(d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MSA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* msa_last_error(void) { return g_err; }
+
+size_t msa_workspace_bytes(int op, const msa_dims_t* d) {
+  char saved[sizeof g_err];
+  memcpy(saved, g_err, sizeof g_err);
+  const int rc = check_dims(d);
+  memcpy(g_err, saved, sizeof g_err);
+  if (rc != MSA_OK) return 0;
+  switch (op) {
+    case MSA_OP_INDEX_SCORES: return 0;
+    case MSA_OP_SELECT_BLOCKS: return d->T == 1 ? decode_select_ws(d) : 0;
+    case MSA_OP_SELECT_FROM_SCORES: return 0;
+    case MSA_OP_ATTN_PREFILL: return prefill_ws(d, default_window(d));
+    case MSA_OP_ATTN_DECODE: return d->T == 1 ? decode_ws(d) : 0;
+  }
+  return 0;
+}
+
+int msa_index_scores(const msa_dims_t* d, const void* qI, const void* kI, float* S,
+                     void* stream) {
+  MSA_TRY(check_dims(d));
+  MSA_TRY(check_ptr(qI, "qI"));
+  MSA_TRY(check_ptr(kI, "kI"));
+  MSA_TRY(check_ptr(S, "S"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (d->T == 1)
+    e = msa::launch_decode_scan(qI, kI, S, d->B, d->N, d->G, st);
+  else
+    e = msa::launch_index_tiles(true, qI, kI, S, nullptr, d->B, d->T, d->N, d->G, d->k, st);
+  if (e != hipSuccess) return hip_fail(e, "msa_index_scores");
+  return MSA_OK;
+}
+
+int msa_select_blocks(const msa_dims_t* d, const void* qI, const void* kI, int32_t* idx,
+                      void* ws, size_t ws_bytes, void* stream) {
+  MSA_TRY(check_dims(d));
+  MSA_TRY(check_ptr(qI, "qI"));
+  MSA_TRY(check_ptr(kI, "kI"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (d->T == 1) {
+    const size_t need = decode_select_ws(d);
+    MSA_TRY(check_ptr(ws, "ws"));
+    if (ws_bytes < need)
+      return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "select needs %zu workspace bytes, got %zu",
+                  need, ws_bytes);
+    float* S = static_cast<float*>(ws);
+    e = msa::launch_decode_scan(qI, kI, S, d->B, d->N, d->G, st);
+    if (e == hipSuccess) e = msa::launch_topk_rows(S, idx, d->B, 1, d->N, d->G, d->k, st);
+  } else {
+    e = msa::launch_index_tiles(false, qI, kI, nullptr, idx, d->B, d->T, d->N, d->G, d->k, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "msa_select_blocks");
+  return MSA_OK;
+}
+
+int msa_select_blocks_from_scores(const msa_dims_t* d, const float* S, int32_t* idx,
+                                  void* stream) {
+  MSA_TRY(check_dims(d));
+  MSA_TRY(check_ptr(S, "S"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  const hipError_t e = msa::launch_topk_rows(S, idx, d->B, d->T, d->N, d->G, d->k,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_select_blocks_from_scores");
+  return MSA_OK;
+}
+
+int msa_sparse_attn_prefill(const msa_dims_t* d, const void* q, const void* K, const void* V,
+                            const int32_t* idx, void* O, float* lse, void* ws, size_t ws_bytes,
+                            void* stream) {
+  MSA_TRY(check_dims(d));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(K, "K"));
+  MSA_TRY(check_ptr(V, "V"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  MSA_TRY(check_ptr(O, "O"));
+  if (lse) MSA_TRY(check_ptr(lse, "lse"));
+  MSA_TRY(check_ptr(ws, "ws"));
+  // Largest window (query rows per pass) whose workspace fits.
+  int64_t hi = default_window(d);
+  if (prefill_ws(d, 1) > ws_bytes)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "prefill needs at least %zu workspace bytes (%zu for the default window), got %zu",
+                prefill_ws(d, 1), prefill_ws(d, hi), ws_bytes);
+  if (prefill_ws(d, hi) > ws_bytes) {
+    int64_t lo = 1;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo + 1) / 2;
+      if (prefill_ws(d, mid) <= ws_bytes)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    hi = lo;
+  }
+  msa::AttnWorkspace w;
+  msa::attn_workspace_carve(ws, hi, d->B, d->N, d->G, d->Hq / d->G, d->k, false, &w);
+  const hipError_t e = msa::launch_attn_prefill(q, K, V, idx, O, lse, d->B, d->T, d->N, d->Hq,
+                                                d->G, d->k, w, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_prefill");
+  return MSA_OK;
+}
+
+int msa_sparse_attn_decode(const msa_dims_t* d, const void* q, const void* K, const void* V,
+                           const int32_t* idx, void* O, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
+  MSA_TRY(check_dims(d));
+  if (d->T != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "decode needs T == 1 (got %lld)",
+                             (long long)d->T);
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(K, "K"));
+  MSA_TRY(check_ptr(V, "V"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  MSA_TRY(check_ptr(O, "O"));
+  if (lse) MSA_TRY(check_ptr(lse, "lse"));
+  MSA_TRY(check_ptr(ws, "ws"));
+  const size_t need = decode_ws(d);
+  if (ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  msa::AttnWorkspace w;
+  msa::attn_workspace_carve(ws, d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true, &w);
+  const hipError_t e = msa::launch_attn_decode(q, K, V, idx, O, lse, d->B, d->N, d->Hq, d->G,
+                                               d->k, w, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode");
+  return MSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// msa_common.h -- device helpers shared by the MSA kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kHeadDim = 128;   // d_h and d_I supported by these kernels
+constexpr int kBlock = 128;     // Bk supported by these kernels
+constexpr int kRowBytes = kHeadDim * 2;  // one bf16 row of 128 values
+
+// 1/sqrt(128) in double; the fp32 score is the fp32 nearest to dot * this
+// value (one fp64 multiply, one rounding), i.e. the fp32 nearest to the exact
+// score whenever the dot product itself is exact.
+constexpr double kInvSqrt128 = 0.088388347648318440550;
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float bf16_to_f32(u16 h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ u16 f32_to_bf16(float f) {
+  return __builtin_bit_cast(u16, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 2^x with the hardware instruction (no denormal range handling: results
+// below 2^-126 flush to zero, which softmax weights can afford).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.
+//   A: lane l holds row (l % 32), k = 8*(l/32) .. +7
+//   B: lane l holds column (l % 32), k = 8*(l/32) .. +7
+//   D: lane l, element r holds row 8*(r/4) + 4*(l/32) + (r%4), column l % 32
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x32) * B(32x16).
+//   A: lane l holds row (l % 16), k = 8*(l/16) .. +7
+//   B: lane l holds column (l % 16), k = 8*(l/16) .. +7
+//   D: lane l, element r holds row 4*(l/16) + r, column l % 16
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row r of a 128 x 128 bf16 tile in LDS is 256 B = 16 chunks of 16 B.  Chunk
+// c of row r is stored at chunk position c ^ (r & 15): sixteen consecutive
+// rows read at the same logical chunk then hit sixteen different chunk
+// positions, which covers all LDS banks once.
+__device__ __forceinline__ int swz(int r, int c) {
+  return (r << 8) + ((c ^ (r & 15)) << 4);
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return fmaxf(a, fmaxf(b, c));
+}
+
+}  // namespace msa

@@ -1,0 +1,54 @@
+// msa_internal.h -- launchers shared between the kernel files and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+// Stages 1+2 (write S) or stages 1-3 fused (write idx) for T > 1.
+hipError_t launch_index_tiles(bool write_scores, const void* qI, const void* kI,
+                              float* S, int32_t* idx, int64_t B, int64_t T,
+                              int64_t N, int G, int k, hipStream_t st);
+
+// Stages 1+2 for T == 1: streams the index keys, S is [B, G, 1, NB].
+hipError_t launch_decode_scan(const void* qI, const void* kI, float* S,
+                              int64_t B, int64_t N, int G, hipStream_t st);
+
+// Stage 3 from S [B, G, T, NB] (one wave per row).
+hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
+                            int64_t N, int G, int k, hipStream_t st);
+
+struct AttnWorkspace {
+  int32_t* counts;       // [nbins]
+  int32_t* cursor;       // [nbins]
+  int32_t* offsets;      // [nbins]
+  int32_t* chunk_start;  // [nbins]
+  int32_t* totals;       // [4]: entries, chunks
+  int32_t* entries;      // [W * G * k]
+  int4* chunks;          // [max_chunks]
+  uint16_t* opart;       // [W, G, k, hg, 128] bf16
+  float* lpart;          // [W, G, k, hg]
+  int64_t window;        // rows per window
+  int64_t max_chunks;
+  int64_t nbins;
+};
+
+// Bytes of workspace for a window of `window` query rows.
+// decode: one chunk per (sequence, group, slot) instead of the inverted lists.
+size_t attn_workspace_bytes(int64_t window, int64_t B, int64_t N, int G,
+                            int hg, int k, bool decode);
+void attn_workspace_carve(void* ws, int64_t window, int64_t B, int64_t N,
+                          int G, int hg, int k, bool decode, AttnWorkspace* out);
+
+hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
+                               const int32_t* idx, void* O, float* lse,
+                               int64_t B, int64_t T, int64_t N, int Hq, int G,
+                               int k, const AttnWorkspace& w, hipStream_t st);
+
+hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
+                              const int32_t* idx, void* O, float* lse,
+                              int64_t B, int64_t N, int Hq, int G, int k,
+                              const AttnWorkspace& w, hipStream_t st);
+
+}  // namespace msa

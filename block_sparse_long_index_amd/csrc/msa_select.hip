@@ -1,0 +1,571 @@
+// msa_select.hip -- index branch of MSA on gfx950: token scores, causal block
+// max pooling and the exp-free top-k with the forced local block.
+//
+// Method: MSA study notes (dimensionstp.github.io/study-concept/msa), section
+// 2-3, the displayed equations for s, S and the block set; section 3-2 (max
+// pooling over causally visible token scores); section 3-4 (forced local
+// block); section 3-5 "Exp-free Top-k" (ranking raw scores needs no
+// max/exp/sum).  The fused kernel keeps each row's running top-k in registers
+// while key blocks stream by, as the Flash-MSA blog (hackernews.jp) describes
+// for its proxy attention; the blog sets the local block's score to +inf, we
+// leave the local block out of the candidates and append it, which is the
+// same selection.
+#include "msa_common.h"
+#include "msa_internal.h"
+
+#include <limits.h>
+#include <math.h>
+
+namespace msa {
+
+// ---------------------------------------------------------------------------
+// Tile kernel: one workgroup per (sequence, tile of QT consecutive positions).
+// QT divides Bk = 128, so every query of a tile has the same local block L and
+// the candidate blocks 0..L-1 are fully visible: no causal masking is needed
+// except in the local block itself (scored only when S is written).
+//
+// Columns of the score tile are (query, group) pairs c = q * G + g; keys are
+// on the MFMA M side, so each lane's accumulator holds 16 keys of one column
+// and the 128-key block max is an in-register max plus one exchange between
+// the two half-waves.  Each wave owns 64 columns (two 32-column MFMA tiles);
+// its q^I fragments stay in registers for the whole kernel.  k^I blocks
+// (32 KB) stream through double-buffered LDS, shared by all waves.
+// ---------------------------------------------------------------------------
+template <int G>
+struct TileShape {
+  static constexpr int QT = (512 / G) < 128 ? (512 / G) : 128;
+  static constexpr int NCOL = QT * G;
+  static constexpr int NW = NCOL / 64;
+  static constexpr int NT = NW * 64;
+  static constexpr int PF = 2048 / NT;  // 16-B chunks per thread per block
+};
+
+struct TileArgs {
+  const u16* qI;
+  const u16* kI;
+  float* S;
+  int32_t* idx;
+  int64_t T, N;
+  int64_t tile_hi;  // last position tile; workgroups run heaviest first
+  int32_t NB, k, B;
+};
+
+// Insert (x, xi) into a list sorted by score descending, equal scores kept in
+// arrival order; the caller guarantees x > ts[CAP-1].
+template <int CAP>
+__device__ __forceinline__ void topk_insert(float (&ts)[CAP], int (&ti)[CAP],
+                                            float x, int xi) {
+#pragma unroll
+  for (int i = CAP - 1; i >= 0; --i) {
+    const bool stay = ts[i] >= x;
+    float ns;
+    int ni;
+    if (i > 0) {
+      const bool shift = !(ts[i - 1] >= x);
+      ns = stay ? ts[i] : (shift ? ts[i - 1] : x);
+      ni = stay ? ti[i] : (shift ? ti[i - 1] : xi);
+    } else {
+      ns = stay ? ts[i] : x;
+      ni = stay ? ti[i] : xi;
+    }
+    ts[i] = ns;
+    ti[i] = ni;
+  }
+}
+
+template <int CAP>
+__device__ __forceinline__ void sort_ascending(int (&v)[CAP]) {
+#pragma unroll
+  for (int round = 0; round < CAP; ++round) {
+#pragma unroll
+    for (int i = round & 1; i + 1 < CAP; i += 2) {
+      const int lo = min(v[i], v[i + 1]);
+      const int hi = max(v[i], v[i + 1]);
+      v[i] = lo;
+      v[i + 1] = hi;
+    }
+  }
+}
+
+template <int G, int CAP, bool WRITE_S>
+__global__ void __launch_bounds__(TileShape<G>::NT)
+index_tile_kernel(TileArgs a) {
+  using TS = TileShape<G>;
+  constexpr int QT = TS::QT, NT = TS::NT, PF = TS::PF;
+  __shared__ __align__(16) unsigned char kbuf[2][32768];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int b = blockIdx.x % a.B;
+  const int64_t tile = a.tile_hi - blockIdx.x / a.B;
+  const int64_t P0 = tile * QT;
+  const int64_t L = P0 / kBlock;
+  const int64_t row0 = a.N - a.T;
+
+  // Column data for the two MFMA column tiles of this lane.
+  int64_t colp[2];
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = wave * 64 + j * 32 + l32;
+    const int qq = c / G, g = c % G;
+    const int64_t p = P0 + qq;
+    const int64_t t = p - row0;
+    colp[j] = p;
+    const bool ok = (t >= 0) && (t < a.T);
+    const u16* src = a.qI + ((static_cast<int64_t>(b) * a.T + (ok ? t : 0)) * G + g) * kHeadDim;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      uint4 v = ok ? ld16(src + 16 * s + 8 * half) : make_uint4(0, 0, 0, 0);
+      qf[j][s] = as_bf16x8(v);
+    }
+  }
+
+  // The lane's own column (after the half-wave exchange).
+  const int own = wave * 64 + lane;
+  const int own_q = own / G, own_g = own % G;
+  const int64_t own_t = P0 + own_q - row0;
+  const bool own_ok = (own_t >= 0) && (own_t < a.T);
+
+  const int64_t nkb = WRITE_S ? (L + 1) : L;
+  const u16* kbase = a.kI + static_cast<int64_t>(b) * a.N * kHeadDim;
+
+  float ts[CAP];
+  int ti[CAP];
+#pragma unroll
+  for (int i = 0; i < CAP; ++i) {
+    ts[i] = -INFINITY;
+    ti[i] = -1;
+  }
+  float st[4] = {0.f, 0.f, 0.f, 0.f};
+  float* srow = nullptr;
+  if (WRITE_S && own_ok)
+    srow = a.S + ((static_cast<int64_t>(b) * G + own_g) * a.T + own_t) * a.NB;
+  const bool s_vec = (a.NB & 3) == 0;
+
+  uint4 pf[PF];
+  auto load_block = [&](int64_t kb) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int i = tid + j * NT;
+      const int r = i >> 4, c = i & 15;
+      const int64_t key = kb * kBlock + r;
+      pf[j] = key < a.N ? ld16(kbase + key * kHeadDim + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int i = tid + j * NT;
+      const int r = i >> 4, c = i & 15;
+      *reinterpret_cast<uint4*>(&kbuf[buf][swz(r, c)]) = pf[j];
+    }
+  };
+
+  if (nkb > 0) {
+    load_block(0);
+    store_block(0);
+  }
+  __syncthreads();
+
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    const bool more = kb + 1 < nkb;
+    if (more) load_block(kb + 1);
+    const unsigned char* buf = kbuf[kb & 1];
+    float m0 = -INFINITY, m1 = -INFINITY;
+    const bool masked = WRITE_S && (kb == L);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x16 acc0 = {}, acc1 = {};
+      const int r = kt * 32 + l32;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&buf[swz(r, 2 * s + half)]));
+        acc0 = mfma32(av, qf[0][s], acc0);
+        acc1 = mfma32(av, qf[1][s], acc1);
+      }
+      if (masked) {
+        // offsets inside the local block past each column's position
+        const int lim0 = static_cast<int>(colp[0] - kb * kBlock);
+        const int lim1 = static_cast<int>(colp[1] - kb * kBlock);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = kt * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (off > lim0) acc0[e] = -INFINITY;
+          if (off > lim1) acc1[e] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        m0 = max3(m0, acc0[e], acc0[e + 1]);
+        m1 = max3(m1, acc1[e], acc1[e + 1]);
+      }
+      sched_fence();
+    }
+    m0 = fmaxf(m0, __shfl_xor(m0, 32));
+    m1 = fmaxf(m1, __shfl_xor(m1, 32));
+    const float v = half ? m1 : m0;
+
+    if (WRITE_S) {
+      const float sv = static_cast<float>(static_cast<double>(v) * kInvSqrt128);
+      const int slot = static_cast<int>(kb & 3);
+      st[0] = slot == 0 ? sv : st[0];
+      st[1] = slot == 1 ? sv : st[1];
+      st[2] = slot == 2 ? sv : st[2];
+      st[3] = slot == 3 ? sv : st[3];
+      if (srow && (slot == 3 || kb + 1 == nkb)) {
+        const int64_t base = kb & ~static_cast<int64_t>(3);
+        if (slot == 3 && s_vec) {
+          *reinterpret_cast<float4*>(srow + base) = make_float4(st[0], st[1], st[2], st[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e <= slot) srow[base + e] = st[e];
+        }
+      }
+    } else {
+      const bool need = v > ts[CAP - 1];
+      if (__ballot(need)) {
+        if (need) topk_insert<CAP>(ts, ti, v, static_cast<int>(kb));
+      }
+    }
+
+    if (more) store_block((kb + 1) & 1);
+    __syncthreads();
+  }
+
+  if (WRITE_S) {
+    // Blocks after the local block are invisible: -inf.  The workgroup fills
+    // each row's tail together so that consecutive threads write consecutive
+    // addresses.
+    const int64_t tail0 = L + 1;
+    const int64_t len = a.NB - tail0;
+    if (len > 0) {
+      for (int c = 0; c < TS::NCOL; ++c) {
+        const int q = c / G, g = c % G;
+        const int64_t t = P0 + q - row0;
+        if (t < 0 || t >= a.T) continue;
+        float* row = a.S + ((static_cast<int64_t>(b) * G + g) * a.T + t) * a.NB + tail0;
+        for (int64_t e = tid; e < len; e += NT) row[e] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  if (!own_ok) return;
+  const int want = static_cast<int>(L < a.k - 1 ? L : a.k - 1);
+  int sel[CAP];
+#pragma unroll
+  for (int i = 0; i < CAP; ++i) sel[i] = i < want ? ti[i] : INT_MAX;
+  sort_ascending<CAP>(sel);
+  int32_t* out = a.idx + ((static_cast<int64_t>(b) * G + own_g) * a.T + own_t) * a.k;
+#pragma unroll
+  for (int s = 0; s < CAP + 1; ++s) {
+    if (s < a.k) {
+      const int val = s < want ? sel[s < CAP ? s : 0] : (s == want ? static_cast<int>(L) : -1);
+      out[s] = val;
+    }
+  }
+}
+
+template <int G, bool WS>
+static hipError_t launch_tiles_cap(const TileArgs& a, int64_t ntiles, hipStream_t st) {
+  using TS = TileShape<G>;
+  const int64_t grid = ntiles * a.B;
+  const dim3 gd(static_cast<unsigned>(grid)), bd(TS::NT);
+  if (WS || a.k <= 4) {
+    hipLaunchKernelGGL((index_tile_kernel<G, 3, WS>), gd, bd, 0, st, a);
+  } else if (a.k <= 8) {
+    hipLaunchKernelGGL((index_tile_kernel<G, 7, WS>), gd, bd, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((index_tile_kernel<G, 15, WS>), gd, bd, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <bool WS>
+static hipError_t launch_tiles_g(const TileArgs& a, int G, int64_t ntiles, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_tiles_cap<1, WS>(a, ntiles, st);
+    case 2: return launch_tiles_cap<2, WS>(a, ntiles, st);
+    case 4: return launch_tiles_cap<4, WS>(a, ntiles, st);
+    case 8: return launch_tiles_cap<8, WS>(a, ntiles, st);
+    case 16: return launch_tiles_cap<16, WS>(a, ntiles, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+static int tile_queries(int G) { return (512 / G) < 128 ? (512 / G) : 128; }
+
+hipError_t launch_index_tiles(bool write_scores, const void* qI, const void* kI,
+                              float* S, int32_t* idx, int64_t B, int64_t T,
+                              int64_t N, int G, int k, hipStream_t st) {
+  const int QT = tile_queries(G);
+  TileArgs a;
+  a.qI = static_cast<const u16*>(qI);
+  a.kI = static_cast<const u16*>(kI);
+  a.S = S;
+  a.idx = idx;
+  a.T = T;
+  a.N = N;
+  a.NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
+  a.k = k;
+  a.B = static_cast<int32_t>(B);
+  const int64_t tile_lo = (N - T) / QT;
+  a.tile_hi = (N - 1) / QT;
+  const int64_t ntiles = a.tile_hi - tile_lo + 1;
+  if (write_scores) return launch_tiles_g<true>(a, G, ntiles, st);
+  return launch_tiles_g<false>(a, G, ntiles, st);
+}
+
+// ---------------------------------------------------------------------------
+// Decode scan (T == 1): stream the index-key cache once.  A workgroup takes 16
+// consecutive blocks of one sequence, each wave 4 of them.  16x16x32 MFMA with
+// 16 keys on M and the G index queries on N (unused columns are zero).  The
+// 32 16-B loads of a block are all issued before its MFMAs so that each wave
+// keeps 32 KB in flight.  Keys are spread so that each lane reads 64
+// contiguous bytes of its key row: lane quarter qd holds d = 32*qd .. +31, and
+// k-step s takes d = 32*qd + 8*s .. +7 (the q^I fragments use the same map).
+// ---------------------------------------------------------------------------
+struct ScanArgs {
+  const u16* qI;
+  const u16* kI;
+  float* S;
+  int64_t N;
+  int32_t NB, G;
+};
+
+__global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  const int col = lane & 15, qd = lane >> 4;
+  bf16x8 qf[4];
+  const u16* qsrc = a.qI + (static_cast<int64_t>(b) * a.G + (col < a.G ? col : 0)) * kHeadDim;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint4 v = col < a.G ? ld16(qsrc + 32 * qd + 8 * s) : make_uint4(0, 0, 0, 0);
+    qf[s] = as_bf16x8(v);
+  }
+  const u16* kbase = a.kI + static_cast<int64_t>(b) * a.N * kHeadDim;
+  const int64_t blk0 = static_cast<int64_t>(blockIdx.x) * 16 + wave * 4;
+  for (int w = 0; w < 4; ++w) {
+    const int64_t kb = blk0 + w;
+    if (kb >= a.NB) break;
+    uint4 d[8][4];
+#pragma unroll
+    for (int kg = 0; kg < 8; ++kg) {
+      const int64_t key = kb * kBlock + kg * 16 + col;
+      const u16* src = kbase + key * kHeadDim + 32 * qd;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        d[kg][s] = key < a.N ? ld16(src + 8 * s) : make_uint4(0, 0, 0, 0);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int kg = 0; kg < 8; ++kg) {
+      f32x4 acc = {};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = mfma16(as_bf16x8(d[kg][s]), qf[s], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t key = kb * kBlock + kg * 16 + 4 * qd + r;
+        m = fmaxf(m, key < a.N ? acc[r] : -INFINITY);
+      }
+    }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (lane < a.G)
+      a.S[(static_cast<int64_t>(b) * a.G + lane) * a.NB + kb] =
+          static_cast<float>(static_cast<double>(m) * kInvSqrt128);
+  }
+}
+
+hipError_t launch_decode_scan(const void* qI, const void* kI, float* S,
+                              int64_t B, int64_t N, int G, hipStream_t st) {
+  ScanArgs a;
+  a.qI = static_cast<const u16*>(qI);
+  a.kI = static_cast<const u16*>(kI);
+  a.S = S;
+  a.N = N;
+  a.NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
+  a.G = G;
+  const dim3 grid(static_cast<unsigned>((a.NB + 15) / 16), static_cast<unsigned>(B));
+  hipLaunchKernelGGL(decode_scan_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-k from materialised scores: one wave per (sequence, group, row).
+//   1. each lane takes the strided candidates e = lane + 64 i and keeps their
+//      max; the m-th largest lane max (m = min(k-1, L)) is a lower bound tau
+//      for the m-th largest candidate, so every winner scores >= tau;
+//   2. the candidates >= tau are compacted (in index order) through LDS; if
+//      at most 64 survive they are bitonic-sorted across the wave by
+//      (score desc, index asc), otherwise (many equal scores) the survivors
+//      are merged 64 at a time into a running best-64 list;
+//   3. the best m are sorted by block index and written with the local block.
+// ---------------------------------------------------------------------------
+struct TopkArgs {
+  const float* S;
+  int32_t* idx;
+  int64_t T, N, rows;
+  int32_t NB, k;
+};
+
+__device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+// Bitonic sort of one (score, index) pair per lane; best_first puts the best
+// pair in lane 0.
+__device__ __forceinline__ void bitonic64(float& v, int& i, int lane, bool best_first) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const float pv = __shfl_xor(v, stride);
+      const int pi = __shfl_xor(i, stride);
+      const bool lower = (lane & stride) == 0;
+      const bool dir = (((lane & size) == 0) == best_first);
+      const bool swap = (lower == dir) ? beats(pv, pi, v, i) : beats(v, i, pv, pi);
+      if (swap) {
+        v = pv;
+        i = pi;
+      }
+    }
+  }
+}
+
+// Merge of a best-first bitonic sequence into best-first order.
+__device__ __forceinline__ void bitonic_merge64(float& v, int& i, int lane) {
+#pragma unroll
+  for (int stride = 32; stride > 0; stride >>= 1) {
+    const float pv = __shfl_xor(v, stride);
+    const int pi = __shfl_xor(i, stride);
+    const bool lower = (lane & stride) == 0;
+    const bool swap = lower ? beats(pv, pi, v, i) : beats(v, i, pv, pi);
+    if (swap) {
+      v = pv;
+      i = pi;
+    }
+  }
+}
+
+__device__ __forceinline__ float sort_desc_values64(float v, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const float pv = __shfl_xor(v, stride);
+      const bool lower = (lane & stride) == 0;
+      const bool desc = (lane & size) == 0;
+      const bool take = (lower == desc) ? (pv > v) : (pv < v);
+      v = take ? pv : v;
+    }
+  }
+  return v;
+}
+
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0));
+}
+
+__global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
+  __shared__ float cv[4][64];
+  __shared__ int ci[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (row >= a.rows) return;
+  const int64_t t = row % a.T;
+  const int64_t L = (a.N - a.T + t) / kBlock;
+  const int m = static_cast<int>(L < a.k - 1 ? L : a.k - 1);
+  int32_t* out = a.idx + row * a.k;
+  if (m == 0) {
+    if (lane < a.k) out[lane] = lane == 0 ? static_cast<int>(L) : -1;
+    return;
+  }
+  const float* src = a.S + row * a.NB;
+  const int n = static_cast<int>(L);
+
+  float lm = -INFINITY;
+  for (int e = lane; e < n; e += 64) lm = fmaxf(lm, src[e]);
+  const float tau = __shfl(sort_desc_values64(lm, lane), m - 1);
+
+  int cnt = 0;
+  for (int e = lane; e < n; e += 64) cnt += src[e] >= tau ? 1 : 0;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) cnt += __shfl_xor(cnt, s);
+
+  float v = -INFINITY;
+  int vi = INT_MAX;
+  if (cnt <= 64) {
+    int base = 0;
+    for (int e0 = 0; e0 < n; e0 += 64) {
+      const int e = e0 + lane;
+      const float x = e < n ? src[e] : -INFINITY;
+      const bool f = (e < n) && (x >= tau);
+      const unsigned long long bal = __ballot(f);
+      if (f) {
+        const int pos = base + lanes_below(bal);
+        cv[wave][pos] = x;
+        ci[wave][pos] = e;
+      }
+      base += __popcll(bal);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < cnt) {
+      v = cv[wave][lane];
+      vi = ci[wave][lane];
+    }
+    bitonic64(v, vi, lane, true);
+  } else {
+    for (int e0 = 0; e0 < n; e0 += 64) {
+      const int e = e0 + lane;
+      const float x = e < n ? src[e] : -INFINITY;
+      const bool f = (e < n) && (x >= tau);
+      if (!__ballot(f)) continue;
+      float cvv = f ? x : -INFINITY;
+      int cii = f ? e : INT_MAX;
+      bitonic64(cvv, cii, lane, false);
+      if (beats(cvv, cii, v, vi)) {
+        v = cvv;
+        vi = cii;
+      }
+      bitonic_merge64(v, vi, lane);
+    }
+  }
+  // best m are in lanes 0..m-1; order them by block index on lanes 0..15
+  int key = lane < m ? vi : INT_MAX;
+#pragma unroll
+  for (int size = 2; size <= 16; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int pk = __shfl_xor(key, stride);
+      const bool lower = (lane & stride) == 0;
+      const bool asc = (lane & size) == 0 || size == 16;
+      const bool take = (lower == asc) ? (pk < key) : (pk > key);
+      key = take ? pk : key;
+    }
+  }
+  if (lane < a.k) out[lane] = lane < m ? key : (lane == m ? static_cast<int>(L) : -1);
+}
+
+hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
+                            int64_t N, int G, int k, hipStream_t st) {
+  TopkArgs a;
+  a.S = S;
+  a.idx = idx;
+  a.T = T;
+  a.N = N;
+  a.rows = B * G * T;
+  a.NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
+  a.k = k;
+  const int64_t grid = (a.rows + 3) / 4;
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,213 @@
+"""Thin ctypes binding of libmsa.so (include/msa.h).
+
+Every function here only marshals arguments: it checks shapes, dtypes and
+contiguity of torch tensors, allocates outputs and scratch with torch, and
+passes raw device pointers plus the current HIP stream to the C ABI.  All
+arithmetic runs in the library's kernels.  If the library is missing the
+first call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmsa.so")
+
+MSA_OK = 0
+OP_INDEX_SCORES = 0
+OP_SELECT_BLOCKS = 1
+OP_SELECT_FROM_SCORES = 2
+OP_ATTN_PREFILL = 3
+OP_ATTN_DECODE = 4
+
+# Every function the C header declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_SIGS = {
+    "msa_index_scores": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "msa_select_blocks": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_select_blocks_from_scores": (ctypes.c_int, [_P, _P, _P, _P]),
+    "msa_sparse_attn_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P,
+                                               ctypes.c_size_t, _P]),
+    "msa_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P,
+                                              ctypes.c_size_t, _P]),
+    "msa_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _P]),
+    "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "msa_last_error": (ctypes.c_char_p, []),
+}
+
+
+class Dims(ctypes.Structure):
+    """msa_dims_t"""
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("Hq", ctypes.c_int32),
+                ("G", ctypes.c_int32), ("d_h", ctypes.c_int32),
+                ("d_I", ctypes.c_int32), ("Bk", ctypes.c_int32),
+                ("k", ctypes.c_int32)]
+
+
+def dims(B, T, N, Hq, G, k, d_h=128, d_I=128, Bk=128) -> Dims:
+    return Dims(B, T, N, Hq, G, d_h, d_I, Bk, k)
+
+
+class MSAError(RuntimeError):
+    def __init__(self, code, where, text):
+        super().__init__("%s failed (%d): %s" % (where, code, text))
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libmsa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(rc, where):
+    if rc != MSA_OK:
+        L = lib()
+        text = "%s: %s" % (L.msa_status_string(rc).decode(), L.msa_last_error().decode())
+        raise MSAError(rc, where, text)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def workspace_bytes(op: int, d: Dims) -> int:
+    return int(lib().msa_workspace_bytes(op, ctypes.byref(d)))
+
+
+def _workspace(op, d, ws):
+    need = workspace_bytes(op, d)
+    if ws is None:
+        if need == 0:
+            return None, 0
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    return ws, ws.numel() * ws.element_size()
+
+
+def index_scores(qI, kI, out=None):
+    """Stages 1+2.  qI [B,T,G,128] bf16, kI [B,N,128] bf16 -> S [B,G,T,NB] fp32."""
+    B, T, G, dI = qI.shape
+    N = kI.shape[1]
+    _need(qI, "qI", torch.bfloat16)
+    _need(kI, "kI", torch.bfloat16, (B, N, dI))
+    d = dims(B, T, N, G, G, 1, d_I=dI)
+    NB = (N + d.Bk - 1) // d.Bk
+    S = out if out is not None else torch.empty(B, G, T, NB, dtype=torch.float32, device=qI.device)
+    _need(S, "S", torch.float32, (B, G, T, NB))
+    _check(lib().msa_index_scores(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(S), _stream()),
+           "msa_index_scores")
+    return S
+
+
+def select_blocks(qI, kI, k, out=None, workspace=None):
+    """Stages 1-3 fused.  -> idx [B,G,T,k] int32 (ascending, -1 padded)."""
+    B, T, G, dI = qI.shape
+    N = kI.shape[1]
+    _need(qI, "qI", torch.bfloat16)
+    _need(kI, "kI", torch.bfloat16, (B, N, dI))
+    d = dims(B, T, N, G, G, k, d_I=dI)
+    idx = out if out is not None else torch.empty(B, G, T, k, dtype=torch.int32, device=qI.device)
+    _need(idx, "idx", torch.int32, (B, G, T, k))
+    ws, nbytes = _workspace(OP_SELECT_BLOCKS, d, workspace)
+    _check(lib().msa_select_blocks(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(idx), _ptr(ws),
+                                   nbytes, _stream()), "msa_select_blocks")
+    return idx
+
+
+def select_blocks_from_scores(S, k, N, out=None):
+    """Stage 3 from S [B,G,T,NB] fp32 (query row t at position N - T + t)."""
+    B, G, T, NB = S.shape
+    _need(S, "S", torch.float32)
+    d = dims(B, T, N, G, G, k)
+    if NB != (N + d.Bk - 1) // d.Bk:
+        raise ValueError("S has %d blocks, N=%d needs %d" % (NB, N, (N + d.Bk - 1) // d.Bk))
+    idx = out if out is not None else torch.empty(B, G, T, k, dtype=torch.int32, device=S.device)
+    _need(idx, "idx", torch.int32, (B, G, T, k))
+    _check(lib().msa_select_blocks_from_scores(ctypes.byref(d), _ptr(S), _ptr(idx), _stream()),
+           "msa_select_blocks_from_scores")
+    return idx
+
+
+def sparse_attn_prefill(q, K, V, idx, return_lse=False, out=None, workspace=None):
+    """Stage 4, KV-outer.  q [B,T,Hq,128], K/V [B,G,N,128] bf16, idx [B,G,T,k]
+    -> O [B,T,Hq,128] bf16 (and lse [B,Hq,T] fp32)."""
+    B, T, Hq, dh = q.shape
+    _, G, N, _ = K.shape
+    k = idx.shape[-1]
+    _need(q, "q", torch.bfloat16)
+    _need(K, "K", torch.bfloat16, (B, G, N, dh))
+    _need(V, "V", torch.bfloat16, (B, G, N, dh))
+    _need(idx, "idx", torch.int32, (B, G, T, k))
+    d = dims(B, T, N, Hq, G, k, d_h=dh)
+    O = out if out is not None else torch.empty_like(q)
+    _need(O, "O", torch.bfloat16, q.shape)
+    lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device) if return_lse else None
+    ws, nbytes = _workspace(OP_ATTN_PREFILL, d, workspace)
+    _check(lib().msa_sparse_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(K), _ptr(V), _ptr(idx),
+                                         _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()),
+           "msa_sparse_attn_prefill")
+    return (O, lse) if return_lse else O
+
+
+def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None):
+    """Stage 4 for one new token per sequence.  q [B,Hq,128], K/V [B,G,N,128],
+    idx [B,G,1,k] -> O [B,Hq,128] bf16 (and lse [B,Hq] fp32)."""
+    B, Hq, dh = q.shape
+    _, G, N, _ = K.shape
+    k = idx.shape[-1]
+    _need(q, "q", torch.bfloat16)
+    _need(K, "K", torch.bfloat16, (B, G, N, dh))
+    _need(V, "V", torch.bfloat16, (B, G, N, dh))
+    _need(idx, "idx", torch.int32, (B, G, 1, k))
+    d = dims(B, 1, N, Hq, G, k, d_h=dh)
+    O = out if out is not None else torch.empty_like(q)
+    _need(O, "O", torch.bfloat16, q.shape)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
+    ws, nbytes = _workspace(OP_ATTN_DECODE, d, workspace)
+    _check(lib().msa_sparse_attn_decode(ctypes.byref(d), _ptr(q), _ptr(K), _ptr(V), _ptr(idx),
+                                        _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()),
+           "msa_sparse_attn_decode")
+    return (O, lse) if return_lse else O
+
+
+def forward(qI, kI, q, K, V, k, return_lse=False):
+    """The whole path for prefill (T > 1) or decode (T == 1)."""
+    idx = select_blocks(qI, kI, k)
+    if qI.shape[1] == 1:
+        res = sparse_attn_decode(q.reshape(q.shape[0], q.shape[2], q.shape[3]), K, V, idx,
+                                 return_lse=return_lse)
+    else:
+        res = sparse_attn_prefill(q, K, V, idx, return_lse=return_lse)
+    return idx, res

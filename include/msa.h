@@ -1,0 +1,173 @@
+/*
+ * msa.h -- C ABI of the MiniMax Sparse Attention (MSA) forward path for AMD
+ * MI355X (gfx950).  Implemented by libmsa.so (hand-written HIP kernels).
+ *
+ * The method (MSA study notes, dimensionstp.github.io/study-concept/msa,
+ * section 2-3 "Fixed attention budget", its three displayed equations and the
+ * Main Branch equation; section 3 for the branches and the kernel ideas):
+ *
+ *   (1) index score   s[t,g,j] = q^I[t,g] . k^I[j] / sqrt(d_I),  j <= p(t)
+ *   (2) block max     S[t,g,b] = max_{j in block b, j <= p(t)} s[t,g,j]
+ *   (3) selection     the local block local(t) = floor(p(t)/Bk), always,
+ *                     plus the best min(k-1, local(t)) earlier blocks by S
+ *   (4) main branch   O[t,h] = softmax(q[t,h] K_g^T / sqrt(d_h)) V_g over the
+ *                     keys j <= p(t) of the selected blocks of h's group g
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Positions.  Query row t (0 <= t < T) of sequence b sits at absolute position
+ *   p(t) = N - T + t: prefill has T == N; decode has T == 1 and N is the cache
+ *   length including the new token.
+ * Groups.  Query head h belongs to group g = h / (Hq / G).  Every head of a
+ *   group reads the group's selection (study notes, section 3-3).
+ * Budget.  k counts the local block: at most k * Bk keys per query and group
+ *   (study notes, section 2-3: "including the local block, at most 2048").
+ * Ties.  Among equal block scores the lower block index wins.
+ * Slot order.  idx rows list the selected blocks in ascending order; the
+ *   local block is the last valid slot; unused slots hold -1.
+ * Invisible blocks.  Blocks after local(t) have S = -inf and are never
+ *   selected.  The local block's S is its true causal max; selection ignores
+ *   it (it is forced).
+ * Precision.  bf16 inputs, fp32 accumulation.  S is the fp32 value nearest the
+ *   score (exact for integer-valued index inputs).  O is bf16; lse is fp32,
+ *   natural log.
+ * Memory.  Every pointer is a device pointer the caller owns, 16-byte aligned,
+ *   to a contiguous row-major tensor of the layout given.  The library never
+ *   allocates or frees device memory and keeps no pointer after returning.
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *   enqueue work on it; nothing synchronises.  Results are ready when the
+ *   stream reaches them.
+ * Errors.  Arguments are validated on the host before any HIP call; on an
+ *   error nothing is launched and no output is touched.  A HIP launch error
+ *   returns MSA_ERR_HIP (text from msa_last_error()).
+ * Supported now: d_h == d_I == 128, Bk == 128, 1 <= k <= 16,
+ *   G in {1,2,4,8,16}, Hq / G in {1,2,4,8,16,32}; others: MSA_ERR_UNSUPPORTED.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int64_t B;   /* sequences */
+    int64_t T;   /* query rows per sequence (T <= N) */
+    int64_t N;   /* keys per sequence (context length) */
+    int32_t Hq;  /* query heads */
+    int32_t G;   /* GQA groups = KV heads = index query heads */
+    int32_t d_h; /* main-branch head dimension */
+    int32_t d_I; /* index-branch dimension */
+    int32_t Bk;  /* block size in tokens */
+    int32_t k;   /* blocks selected per (query, group), local included */
+} msa_dims_t;
+
+enum {
+    MSA_OK = 0,
+    MSA_ERR_INVALID_ARGUMENT = -1,
+    MSA_ERR_UNSUPPORTED = -2,
+    MSA_ERR_WORKSPACE_TOO_SMALL = -3,
+    MSA_ERR_HIP = -4
+};
+
+/* Operation ids for msa_workspace_bytes. */
+enum {
+    MSA_OP_INDEX_SCORES = 0,
+    MSA_OP_SELECT_BLOCKS = 1,
+    MSA_OP_SELECT_FROM_SCORES = 2,
+    MSA_OP_ATTN_PREFILL = 3,
+    MSA_OP_ATTN_DECODE = 4
+};
+
+/*
+ * Stages 1 and 2 (study notes section 2-3, equations for s and S; section
+ * 3-2 on max pooling of the causally visible token scores).
+ *   qI  bf16 [B, T, G, d_I]   index queries, one per (row, group)
+ *   kI  bf16 [B, N, d_I]      index keys, one shared head
+ *   S   fp32 [B, G, T, ceil(N/Bk)]  out: block scores; -inf where invisible
+ */
+int msa_index_scores(const msa_dims_t *dims, const void *qI, const void *kI,
+                     float *S, void *stream);
+
+/*
+ * Stages 1 to 3 fused: the token scores and block maxima stay on chip and
+ * feed an exp-free streaming top-k (study notes section 3-5 "Exp-free
+ * Top-k"; the Flash-MSA blog on hackernews.jp, section on the proxy
+ * attention, for top-k kept in registers while the keys stream).
+ *   qI, kI as for msa_index_scores
+ *   idx int32 [B, G, T, k]    out: selected blocks (see conventions)
+ *   ws / ws_bytes             scratch, >= msa_workspace_bytes(MSA_OP_SELECT_BLOCKS)
+ *                             (zero bytes for T > 1; decode uses a score row)
+ */
+int msa_select_blocks(const msa_dims_t *dims, const void *qI, const void *kI,
+                      int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Stage 3 alone, from materialised block scores (study notes section 2-3,
+ * the TopK equation; section 3-5 "Exp-free Top-k": only the order of raw
+ * scores matters, no max/exp/sum).
+ *   S   fp32 [B, G, T, ceil(N/Bk)]  as written by msa_index_scores
+ *   idx int32 [B, G, T, k]          out
+ */
+int msa_select_blocks_from_scores(const msa_dims_t *dims, const float *S,
+                                  int32_t *idx, void *stream);
+
+/*
+ * Stage 4 for prefill, scheduled KV-outer (study notes section 3-5
+ * "KV-outer sparse attention": a reverse index gathers, for each KV block,
+ * the queries that chose it; hot blocks are pre-split into chunks; partial
+ * results are merged by a two-phase combine.  The Flash-MSA blog's backward
+ * section describes the same inversion of [batch, head, query, slot] ->
+ * block into [batch, head, block] -> queries.)
+ *   q   bf16 [B, T, Hq, d_h]
+ *   K,V bf16 [B, G, N, d_h]
+ *   idx int32 [B, G, T, k]    as written by msa_select_blocks
+ *   O   bf16 [B, T, Hq, d_h]  out
+ *   lse fp32 [B, Hq, T]       out, may be NULL
+ *   ws / ws_bytes             scratch; msa_workspace_bytes(MSA_OP_ATTN_PREFILL)
+ *                             gives the size for the default query window.  A
+ *                             smaller workspace (down to one query row per
+ *                             window) is accepted and processes the rows in
+ *                             more windows; below that: WORKSPACE_TOO_SMALL.
+ */
+int msa_sparse_attn_prefill(const msa_dims_t *dims, const void *q,
+                            const void *K, const void *V, const int32_t *idx,
+                            void *O, float *lse, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/*
+ * Stage 4 for decode (T must be 1): split over the B * G * k selected KV
+ * blocks, then the same combine (llama.cpp analysis page, section 4: block
+ * scores and max pooling, local block plus top-k, then attention over the
+ * gathered K/V; section 2: only the 256 B/token index keys and the selected
+ * K/V blocks are read).
+ *   q   bf16 [B, Hq, d_h]     (= [B, 1, Hq, d_h])
+ *   K,V bf16 [B, G, N, d_h]   the KV cache, N = cache length
+ *   idx int32 [B, G, 1, k]
+ *   O   bf16 [B, Hq, d_h]     out
+ *   lse fp32 [B, Hq]          out, may be NULL
+ *   ws / ws_bytes             >= msa_workspace_bytes(MSA_OP_ATTN_DECODE)
+ */
+int msa_sparse_attn_decode(const msa_dims_t *dims, const void *q,
+                           const void *K, const void *V, const int32_t *idx,
+                           void *O, float *lse, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* Scratch bytes an operation needs for these dims (0 if none); 0 also for
+ * invalid dims.  Host only, no HIP call. */
+size_t msa_workspace_bytes(int op, const msa_dims_t *dims);
+
+/* Static text for a status code. */
+const char *msa_status_string(int status);
+
+/* Text of the last MSA_ERR_HIP or validation failure on this thread. */
+const char *msa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -1,0 +1,123 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/msa.h declares, and rejects bad arguments on the host (validation
+runs before any HIP call, so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_long_index_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_\w+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    L = ops.lib()
+    names = _declared()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(ops._SIGS)
+
+
+def test_exports_match_nm():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (msa_\w+)", out))
+    assert set(_declared()) <= exported
+
+
+def test_struct_layout():
+    assert ctypes.sizeof(ops.Dims) == 48
+    assert ops.Dims.k.offset == 44
+
+
+def _rc(fn, *args):
+    return fn(*args)
+
+
+def _good(**kw):
+    base = dict(B=1, T=256, N=256, Hq=8, G=2, k=4)
+    base.update(kw)
+    return ops.dims(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)      # aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x1004)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -1), (dict(T=0), -1), (dict(T=300), -1), (dict(N=0, T=0), -1),
+    (dict(Hq=7), -1), (dict(k=0), -1), (dict(G=3, Hq=9), -2), (dict(k=17), -2),
+    (dict(d_h=64), -2), (dict(d_I=64), -2), (dict(Bk=64), -2),
+    (dict(Hq=64, G=2), -2),
+])
+def test_bad_dims(kw, code):
+    L = ops.lib()
+    d = _good(**kw)
+    assert L.msa_index_scores(ctypes.byref(d), FAKE, FAKE, FAKE, None) == code
+    assert L.msa_select_blocks(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == code
+    assert L.msa_workspace_bytes(ops.OP_ATTN_PREFILL, ctypes.byref(d)) == 0
+    assert len(L.msa_last_error()) > 0
+
+
+def test_null_and_misaligned_pointers():
+    L = ops.lib()
+    d = _good()
+    assert L.msa_index_scores(None, FAKE, FAKE, FAKE, None) == -1
+    assert L.msa_index_scores(ctypes.byref(d), None, FAKE, FAKE, None) == -1
+    assert b"qI" in L.msa_last_error()
+    assert L.msa_index_scores(ctypes.byref(d), FAKE, MISALIGNED, FAKE, None) == -1
+    assert b"aligned" in L.msa_last_error()
+    assert L.msa_sparse_attn_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                     None, 1 << 30, None) == -1
+    assert L.msa_sparse_attn_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     MISALIGNED, FAKE, 1 << 30, None) == -1
+
+
+def test_workspace_checks():
+    L = ops.lib()
+    d = _good()
+    need = L.msa_workspace_bytes(ops.OP_ATTN_PREFILL, ctypes.byref(d))
+    assert need > 0
+    assert L.msa_sparse_attn_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                     FAKE, 16, None) == -3
+    dd = _good(T=1)
+    need_d = L.msa_workspace_bytes(ops.OP_ATTN_DECODE, ctypes.byref(dd))
+    assert need_d > 0
+    assert L.msa_sparse_attn_decode(ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                    FAKE, need_d - 1, None) == -3
+    # decode needs T == 1
+    assert L.msa_sparse_attn_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                    FAKE, 1 << 40, None) == -1
+    need_s = L.msa_workspace_bytes(ops.OP_SELECT_BLOCKS, ctypes.byref(dd))
+    assert need_s == 1 * 2 * 2 * 4  # B * G * NB floats
+    assert L.msa_select_blocks(ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, need_s - 4, None) == -3
+    assert L.msa_workspace_bytes(ops.OP_SELECT_BLOCKS, ctypes.byref(d)) == 0
+    assert L.msa_workspace_bytes(99, ctypes.byref(d)) == 0
+
+
+def test_workspace_scales_with_window():
+    """The prefill workspace is bounded by the query window, not by T."""
+    L = ops.lib()
+    small = L.msa_workspace_bytes(ops.OP_ATTN_PREFILL,
+                                  ctypes.byref(_good(T=16384, N=16384, Hq=64, G=8, k=16)))
+    big = L.msa_workspace_bytes(ops.OP_ATTN_PREFILL,
+                                ctypes.byref(_good(T=1 << 20, N=1 << 20, Hq=64, G=8, k=16)))
+    assert big < 2 * small
+
+
+def test_status_strings():
+    L = ops.lib()
+    for c in (0, -1, -2, -3, -4):
+        assert L.msa_status_string(c)
+    assert L.msa_status_string(12345) == b"unknown status"
