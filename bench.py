@@ -1,0 +1,285 @@
+"""Benchmark of the MSA forward path on one MI355X.
+
+One step = the whole prefill hot path on the 128K-token workload (B=1,
+N=T=131072, Hq=64, G=8, d=128, Bk=128, k=16, needles planted): fused index
+scoring + block max + top-k (msa_select_blocks), then KV-outer sparse
+attention with inversion and combine (msa_sparse_attn_prefill).  Inputs are
+generated on the device before timing.  Printed: one JSON line with the
+prefill throughput (algorithmic TFLOP/s), the roofline of the dominant kernel
+(the fused select), the decode leg (B=16 x 256K cache, GB/s), the standalone
+top-k leg on the materialised 128K scores (us), and the CPU oracle baseline
+on a bounded sample of rows.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--only prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from block_sparse_long_index_amd import accounting as acc  # noqa: E402
+from block_sparse_long_index_amd import ops  # noqa: E402
+from msa_inputs import WORKLOADS, make_inputs, sample_rows  # noqa: E402
+
+METRIC = "MSA prefill eff. TFLOP/s & decode HBM GB/s at 128K; top-k select µs (1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def ev():
+    return torch.cuda.Event(enable_timing=True)
+
+
+def prefill_leg(args):
+    w = WORKLOADS[args.workload]
+    log("[bench] generating", w.name)
+    inp = make_inputs(w, device="cuda")
+    qI, kI, q, K, V = inp["qI"], inp["kI"], inp["q"], inp["K"], inp["V"]
+    idx = torch.empty(w.B, w.G, w.T, w.k, dtype=torch.int32, device="cuda")
+    O = torch.empty_like(q)
+    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k)
+    ws = torch.empty(max(1, ops.workspace_bytes(ops.OP_ATTN_PREFILL, d)), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        ops.select_blocks(qI, kI, w.k, out=idx)
+        if evs is not None:
+            evs[1].record()
+        ops.sparse_attn_prefill(q, K, V, idx, out=O, workspace=ws)
+        if evs is not None:
+            evs[2].record()
+
+    log("[bench] warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("[bench] timing", args.steps, "steps")
+    events = [[ev(), ev(), ev()] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sel_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    att_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    fl = acc.prefill_flops(w)
+    res = dict(w=w, inp=inp, idx=idx, O=O, wall=wall, sel_ms=sel_ms, att_ms=att_ms, flops=fl)
+    log("[bench] prefill %.3f ms/step (select %.3f, attention %.3f)"
+        % (1e3 * wall / args.steps, sel_ms.mean(), att_ms.mean()))
+    return res
+
+
+def topk_leg(args, pre):
+    """Stage 3 alone on materialised scores of the same workload."""
+    w, inp = pre["w"], pre["inp"]
+    S = ops.index_scores(inp["qI"], inp["kI"])
+    idx = torch.empty(w.B, w.G, w.T, w.k, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(2):
+        ops.select_blocks_from_scores(S, w.k, w.N, out=idx)
+    evs = [(ev(), ev()) for _ in range(args.topk_reps)]
+    for a, b in evs:
+        a.record()
+        ops.select_blocks_from_scores(S, w.k, w.N, out=idx)
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    same = bool(torch.equal(idx, pre["idx"]))
+    # torch.topk over the same rows, as context only (full rows, no local rule)
+    tk = []
+    for _ in range(3):
+        a, b = ev(), ev()
+        a.record()
+        torch.topk(S, w.k - 1, dim=-1)
+        b.record()
+        torch.cuda.synchronize()
+        tk.append(a.elapsed_time(b) * 1e3)
+    del S
+    torch.cuda.empty_cache()
+    by = acc.topk_bytes(w)
+    med = float(np.median(us))
+    return {"workload": w.name, "rows": w.B * w.G * w.T, "us_p50": med,
+            "us_p95": float(np.percentile(us, 95)), "bytes": by["total"],
+            "GBps": by["total"] / med / 1e3, "frac_hbm": by["total"] / med / 1e3 / PEAK_HBM_GBS,
+            "matches_fused_select": same, "torch_topk_us": float(np.median(tk))}
+
+
+def decode_leg(args):
+    w = WORKLOADS["decode_256k_b16"]
+    log("[bench] generating", w.name)
+    inp = make_inputs(w, device="cuda")
+    qI, kI, K, V = inp["qI"], inp["kI"], inp["K"], inp["V"]
+    q = inp["q"][:, 0].contiguous()
+    idx = torch.empty(w.B, w.G, 1, w.k, dtype=torch.int32, device="cuda")
+    O = torch.empty_like(q)
+    d = ops.dims(w.B, 1, w.N, w.Hq, w.G, w.k)
+    ws_s = torch.empty(ops.workspace_bytes(ops.OP_SELECT_BLOCKS, d), dtype=torch.uint8,
+                       device="cuda")
+    ws_a = torch.empty(ops.workspace_bytes(ops.OP_ATTN_DECODE, d), dtype=torch.uint8,
+                       device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def step():
+        ops.select_blocks(qI, kI, w.k, out=idx, workspace=ws_s)
+        ops.sparse_attn_decode(q, K, V, idx, out=O, workspace=ws_a)
+
+    for _ in range(3):
+        step()
+    times = []
+    for _ in range(args.decode_reps):
+        flush.zero_()  # evict the 256 MB last-level cache between steps
+        a, b = ev(), ev()
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    us = np.array(times)
+    by = acc.decode_bytes(w)
+    med = float(np.median(us))
+    out = {"workload": w.name, "us_p50": med, "us_p95": float(np.percentile(us, 95)),
+           "bytes": by["total"], "GBps": by["total"] / med / 1e3,
+           "frac_hbm": by["total"] / med / 1e3 / PEAK_HBM_GBS,
+           "note": "last-level cache flushed before each step"}
+    del inp, flush
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_leg(args, pre):
+    """The oracle as it stands, on host cores, on a bounded sample of rows of
+    the same workload; scaled to TFLOP/s by the sample's algorithmic FLOPs."""
+    import oracle
+    w, inp = pre["w"], pre["inp"]
+    d = oracle.dims_of(w.B, w.T, w.N, w.Hq, w.G, w.d_h, w.d_I, w.Bk, w.k)
+    kI = inp["kI"].cpu()
+    K = inp["K"].cpu()
+    V = inp["V"].cpu()
+
+    def run(nrows, seed):
+        rb, rt = sample_rows(w, nrows, seed=seed)
+        rbd, rtd = rb.cuda(), rt.cuda()
+        qI_rows = inp["qI"][rbd, rtd].cpu()
+        q_rows = inp["q"][rbd, rtd].cpu()
+        t0 = time.perf_counter()
+        ref = oracle.forward(d, rb.numpy(), rt.numpy(), qI_rows, kI, q_rows, K, V)
+        sec = time.perf_counter() - t0
+        p = (w.N - w.T) + rt.numpy()
+        L = p // w.Bk
+        nsel = np.minimum(L, w.k - 1) * w.Bk + p % w.Bk + 1
+        flops = float((2 * w.G * w.d_I * (p + 1) + 4 * w.Hq * w.d_h * nsel).sum())
+        return rb, rt, ref, sec, flops
+
+    _, _, _, sec0, fl0 = run(16, 1)
+    rate = fl0 / max(sec0, 1e-6)
+    target = args.cpu_seconds
+    n = int(min(4096, max(32, 16 * target / max(sec0, 1e-3))))
+    log("[bench] cpu oracle: %d rows (probe %.2fs for 16 rows)" % (n, sec0))
+    rb, rt, ref, sec, fl = run(n, 2)
+    # parity of the same rows while we have them
+    idx = pre["idx"]
+    got = idx.permute(0, 2, 1, 3)[rb.cuda(), rt.cuda()].cpu().numpy()
+    O = pre["O"][rb.cuda(), rt.cuda()].float().cpu().numpy()
+    err = np.abs(O - ref["O"])
+    parity = {"rows": int(n), "idx_exact": bool(np.array_equal(got, ref["idx"])),
+              "O_max_abs": float(err.max()), "O_mean_abs": float(err.mean())}
+    del rate
+    return {"value": fl / sec / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": sec,
+            "sample": "%d query rows (all %d groups, %d heads) of %s: edge positions plus "
+                      "uniform rows; fp64 plain C, OpenMP over rows" % (n, w.G, w.Hq, w.name)}, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill_128k")
+    ap.add_argument("--only", default="", help="prefill | decode | topk (skip the other legs)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--decode-reps", type=int, default=30)
+    ap.add_argument("--topk-reps", type=int, default=10)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device copy (counter calibration) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if "RANK" in os.environ and int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py is single-GPU only", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    ops.lib()
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": src.numel() * 4}))
+        return
+
+    out = {"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if args.only in ("", "prefill", "topk"):
+        pre = prefill_leg(args)
+        w = pre["w"]
+        fl = pre["flops"]
+        ms = 1e3 * pre["wall"] / args.steps
+        sel = float(pre["sel_ms"].mean())
+        att = float(pre["att_ms"].mean())
+        out.update({"value": fl["total"] / (ms * 1e-3) / 1e12, "ms_per_step": ms})
+        out["config"] = {"workload": w.name, "B": w.B, "N": w.N, "T": w.T, "Hq": w.Hq,
+                         "G": w.G, "d_h": w.d_h, "d_I": w.d_I, "Bk": w.Bk, "k": w.k,
+                         "needles": w.needles, "seed": w.seed}
+        ach = fl["index"] / (sel * 1e-3) / 1e12
+        out["roofline"] = {"kernel": "index_tile_kernel (fused select: scores, block max, "
+                                     "top-k)",
+                           "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                           "flops_per_launch": fl["index"], "avg_launch_ms": sel}
+        out["stages"] = {"select_ms": sel, "attention_ms": att,
+                         "attention_TFLOPs": fl["main"] / (att * 1e-3) / 1e12,
+                         "index_flops": fl["index"], "main_flops": fl["main"]}
+        if args.only in ("", "topk"):
+            log("[bench] top-k leg")
+            out["topk"] = topk_leg(args, pre)
+        if not args.no_cpu and args.only == "":
+            log("[bench] cpu baseline")
+            out["cpu_baseline"], out["parity_sample"] = cpu_leg(args, pre)
+        del pre
+        torch.cuda.empty_cache()
+    if args.only in ("", "decode"):
+        log("[bench] decode leg")
+        out["decode"] = decode_leg(args)
+        if args.only == "decode":
+            out.update({"value": out["decode"]["GBps"], "unit": "GB/s",
+                        "ms_per_step": out["decode"]["us_p50"] / 1e3,
+                        "config": {"workload": out["decode"]["workload"]}})
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
