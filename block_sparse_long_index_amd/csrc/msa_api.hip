@@ -49,7 +49,8 @@ int check_dims(const msa_dims_t* d) {
   if (!pow2_upto(d->Hq / d->G, 16))
     return fail(MSA_ERR_UNSUPPORTED, "Hq / G must be 1, 2, 4, 8 or 16");
   if (d->B > 65535) return fail(MSA_ERR_UNSUPPORTED, "B > 65535");
-  if (d->N > (int64_t(1) << 30)) return fail(MSA_ERR_UNSUPPORTED, "N > 2^30");
+  // block counts of one sequence live in LDS during the inversion (64 KB)
+  if (d->N > (int64_t(1) << 21)) return fail(MSA_ERR_UNSUPPORTED, "N > 2^21");
   const int64_t NB = (d->N + 127) / 128;
   if (d->B * d->T * d->Hq > kMaxElems / 128 || d->B * d->G * d->N > kMaxElems / 128 ||
       d->B * d->G * d->T * NB > kMaxElems || d->B * d->G * NB > (int64_t(1) << 30))
@@ -77,16 +78,15 @@ size_t decode_select_ws(const msa_dims_t* d) {
 }
 
 int64_t default_window(const msa_dims_t* d) {
-  const int64_t rows = d->B * d->T;
-  return rows < kDefaultWindow ? rows : kDefaultWindow;
+  return d->T < kDefaultWindow ? d->T : kDefaultWindow;
 }
 
 size_t prefill_ws(const msa_dims_t* d, int64_t window) {
-  return msa::attn_workspace_bytes(window, d->B, d->N, d->G, d->Hq / d->G, d->k, false);
+  return msa::attn_workspace_bytes(window, d->N, d->G, d->Hq / d->G, d->k, false);
 }
 
 size_t decode_ws(const msa_dims_t* d) {
-  return msa::attn_workspace_bytes(d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true);
+  return msa::attn_workspace_bytes(d->B, d->N, d->G, d->Hq / d->G, d->k, true);
 }
 
 }  // namespace
@@ -202,7 +202,7 @@ int msa_sparse_attn_prefill(const msa_dims_t* d, const void* q, const void* K, c
     hi = lo;
   }
   msa::AttnWorkspace w;
-  msa::attn_workspace_carve(ws, hi, d->B, d->N, d->G, d->Hq / d->G, d->k, false, &w);
+  msa::attn_workspace_carve(ws, hi, d->N, d->G, d->Hq / d->G, d->k, false, &w);
   const hipError_t e = msa::launch_attn_prefill(q, K, V, idx, O, lse, d->B, d->T, d->N, d->Hq,
                                                 d->G, d->k, w, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_prefill");
@@ -227,7 +227,7 @@ int msa_sparse_attn_decode(const msa_dims_t* d, const void* q, const void* K, co
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need,
                 ws_bytes);
   msa::AttnWorkspace w;
-  msa::attn_workspace_carve(ws, d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true, &w);
+  msa::attn_workspace_carve(ws, d->B, d->N, d->G, d->Hq / d->G, d->k, true, &w);
   const hipError_t e = msa::launch_attn_decode(q, K, V, idx, O, lse, d->B, d->N, d->Hq, d->G,
                                                d->k, w, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode");

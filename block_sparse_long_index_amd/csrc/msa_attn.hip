@@ -20,8 +20,17 @@
 namespace msa {
 
 constexpr int kChunkQueries = 64;  // queries per work chunk (rows = 64 * hg)
+constexpr int kScanTile = 4096;    // elements per workgroup in the offset scan
 
 static inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Rows of one histogram unit: about NB/8 so that writing a unit's NB bin counts
+// costs no more than counting its entries; at least 256.
+static int32_t unit_rows(int64_t NB) {
+  int32_t r = 256;
+  while (r < NB / 8) r <<= 1;
+  return r;
+}
 
 static int64_t max_chunks_for(int64_t window, int64_t nbins, int G, int k, bool decode) {
   const int64_t entries = window * G * k;
@@ -29,155 +38,211 @@ static int64_t max_chunks_for(int64_t window, int64_t nbins, int G, int k, bool 
   return entries / kChunkQueries + (nbins < entries ? nbins : entries) + 1;
 }
 
-size_t attn_workspace_bytes(int64_t window, int64_t B, int64_t N, int G, int hg, int k,
-                            bool decode) {
+static void layout(int64_t window, int64_t N, int G, int hg, int k, bool decode, size_t* off,
+                   AttnWorkspace* w) {
   const int64_t NB = (N + kBlock - 1) / kBlock;
-  const int64_t nbins = B * G * NB;
+  const int64_t nbins = G * NB;
+  const int32_t rq = unit_rows(NB);
+  const int32_t nc = decode ? 0 : static_cast<int32_t>((window + rq - 1) / rq);
+  const int64_t nhist = nbins * nc;
+  const int64_t ntiles = (nhist + kScanTile - 1) / kScanTile;
   const int64_t entries = window * G * k;
-  size_t s = 0;
-  s += 4 * align256(sizeof(int32_t) * nbins);                  // counts, cursor, offsets, chunk_start
-  s += align256(sizeof(int32_t) * 4);                          // totals
-  s += align256(sizeof(int32_t) * entries);                    // entries
-  s += align256(sizeof(int4) * max_chunks_for(window, nbins, G, k, decode));
-  s += align256(sizeof(uint16_t) * entries * hg * kHeadDim);   // partial O
-  s += align256(sizeof(float) * entries * hg);                 // partial lse
-  return s;
+  const int64_t mch = max_chunks_for(window, nbins, G, k, decode);
+  size_t o = 0;
+  off[0] = o; o += align256(sizeof(int32_t) * (nhist > 0 ? nhist : 1));
+  off[1] = o; o += align256(sizeof(int32_t) * (ntiles > 0 ? ntiles : 1));
+  off[2] = o; o += align256(sizeof(int32_t) * 4);
+  off[3] = o; o += align256(sizeof(int32_t) * entries);
+  off[4] = o; o += align256(sizeof(int4) * mch);
+  off[5] = o; o += align256(sizeof(uint16_t) * entries * hg * kHeadDim);
+  off[6] = o; o += align256(sizeof(float2) * entries * hg);
+  off[7] = o;
+  if (w) {
+    w->window = window;
+    w->max_chunks = mch;
+    w->nbins = nbins;
+    w->rq = rq;
+    w->nc = nc;
+    w->nhist = nhist;
+    w->ntiles = ntiles;
+  }
 }
 
-void attn_workspace_carve(void* ws, int64_t window, int64_t B, int64_t N, int G,
-                          int hg, int k, bool decode, AttnWorkspace* w) {
-  const int64_t NB = (N + kBlock - 1) / kBlock;
-  const int64_t nbins = B * G * NB;
-  const int64_t entries = window * G * k;
+size_t attn_workspace_bytes(int64_t window, int64_t N, int G, int hg, int k, bool decode) {
+  size_t off[8];
+  layout(window, N, G, hg, k, decode, off, nullptr);
+  return off[7];
+}
+
+void attn_workspace_carve(void* ws, int64_t window, int64_t N, int G, int hg, int k,
+                          bool decode, AttnWorkspace* w) {
+  size_t off[8];
+  layout(window, N, G, hg, k, decode, off, w);
   char* p = static_cast<char*>(ws);
-  auto take = [&](size_t bytes) {
-    char* r = p;
-    p += align256(bytes);
-    return r;
-  };
-  w->counts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * nbins));
-  w->cursor = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * nbins));
-  w->offsets = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * nbins));
-  w->chunk_start = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * nbins));
-  w->totals = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 4));
-  w->entries = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * entries));
-  w->max_chunks = max_chunks_for(window, nbins, G, k, decode);
-  w->chunks = reinterpret_cast<int4*>(take(sizeof(int4) * w->max_chunks));
-  w->opart = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * entries * hg * kHeadDim));
-  w->lpart = reinterpret_cast<float*>(take(sizeof(float) * entries * hg));
-  w->window = window;
-  w->nbins = nbins;
+  w->hist = reinterpret_cast<int32_t*>(p + off[0]);
+  w->tile_sums = reinterpret_cast<int32_t*>(p + off[1]);
+  w->totals = reinterpret_cast<int32_t*>(p + off[2]);
+  w->entries = reinterpret_cast<int32_t*>(p + off[3]);
+  w->chunks = reinterpret_cast<int4*>(p + off[4]);
+  w->opart = reinterpret_cast<uint16_t*>(p + off[5]);
+  w->lpart = reinterpret_cast<float2*>(p + off[6]);
 }
 
 // ---------------------------------------------------------------------------
-// Inversion of the selection for the query rows [r0, r0 + W) (row r is query
-// t = r % T of sequence b = r / T): histogram per (b, g, block), exclusive
-// scan, scatter of the entries e = (r - r0) * k + slot, and the chunk list.
+// Inversion of the selection for the query rows [t0, t0 + W) of sequence b: a
+// counting sort of the entries e = (t - t0) * k + slot by (group, block).
+//   1. unit histograms: workgroup (c, g) counts, in LDS, the blocks chosen by
+//      group g in rows [c*rq, (c+1)*rq) of the window; hist[(g*NB + blk)*nc + c]
+//   2. exclusive scan of hist in that order: the entries of bin (g, blk) are
+//      contiguous, and inside a bin ordered by row unit
+//   3. scatter: each unit writes its entries from its offsets (LDS cursors)
+//   4. chunks: every bin is cut into chunks of at most 64 queries; chunk slots
+//      are allocated with one atomic per wave
+// LDS atomics keep hot blocks (block 0, the local block, needles) from
+// serialising on a global counter.
 // ---------------------------------------------------------------------------
-__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
 struct InvArgs {
   const int32_t* idx;
-  int32_t* counts;
-  int32_t* cursor;
-  const int32_t* offsets;
+  int32_t* hist;
   int32_t* entries;
-  int64_t T, r0, W;
-  int32_t G, k, NB;
+  int64_t T, t0, W;
+  int32_t b, G, k, NB, rq, nc;
 };
 
-__device__ __forceinline__ void entry_bin(const InvArgs& a, int64_t i, int64_t& bin,
-                                          int32_t& e) {
-  // i enumerates (row in window, group, slot)
-  const int32_t s = static_cast<int32_t>(i % a.k);
-  const int64_t rg = i / a.k;
-  const int32_t g = static_cast<int32_t>(rg % a.G);
-  const int64_t rl = rg / a.G;
-  const int64_t r = a.r0 + rl;
-  const int64_t b = r / a.T, t = r % a.T;
-  const int32_t blk = a.idx[((b * a.G + g) * a.T + t) * a.k + s];
-  bin = blk < 0 ? -1 : (b * a.G + g) * a.NB + blk;
-  e = static_cast<int32_t>(rl * a.k + s);
-}
-
-__global__ void count_kernel(InvArgs a) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= a.W * a.G * a.k) return;
-  int64_t bin;
-  int32_t e;
-  entry_bin(a, i, bin, e);
-  if (bin >= 0) atomicAdd(&a.counts[bin], 1);
-}
-
-__global__ void scatter_kernel(InvArgs a) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= a.W * a.G * a.k) return;
-  int64_t bin;
-  int32_t e;
-  entry_bin(a, i, bin, e);
-  if (bin < 0) return;
-  const int32_t pos = a.offsets[bin] + atomicAdd(&a.cursor[bin], 1);
-  a.entries[pos] = e;
-}
-
-// Single-workgroup exclusive scan of the bin counts and of their chunk
-// counts; totals[0] = entries, totals[1] = chunks.
-__global__ void __launch_bounds__(1024) scan_kernel(const int32_t* counts, int32_t* offsets,
-                                                    int32_t* chunk_start, int32_t* totals,
-                                                    int64_t nbins) {
-  __shared__ int32_t s_e[1024], s_c[1024];
-  __shared__ int32_t carry_e, carry_c;
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    carry_e = 0;
-    carry_c = 0;
+__global__ void __launch_bounds__(256) hist_kernel(InvArgs a) {
+  extern __shared__ int32_t sh[];
+  const int c = blockIdx.x, g = blockIdx.y;
+  for (int i = threadIdx.x; i < a.NB; i += 256) sh[i] = 0;
+  __syncthreads();
+  const int64_t r_lo = static_cast<int64_t>(c) * a.rq;
+  const int64_t r_hi = (r_lo + a.rq) < a.W ? (r_lo + a.rq) : a.W;
+  const int32_t* src = a.idx + ((static_cast<int64_t>(a.b) * a.G + g) * a.T + a.t0 + r_lo) * a.k;
+  const int64_t n = (r_hi - r_lo) * a.k;
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    const int32_t blk = src[i];
+    if (blk >= 0 && blk < a.NB) atomicAdd(&sh[blk], 1);
   }
   __syncthreads();
-  for (int64_t base = 0; base < nbins; base += 1024) {
-    const int64_t i = base + tid;
-    const int32_t c = i < nbins ? counts[i] : 0;
-    const int32_t ch = (c + kChunkQueries - 1) / kChunkQueries;
-    s_e[tid] = c;
-    s_c[tid] = ch;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int32_t ve = tid >= off ? s_e[tid - off] : 0;
-      const int32_t vc = tid >= off ? s_c[tid - off] : 0;
-      __syncthreads();
-      s_e[tid] += ve;
-      s_c[tid] += vc;
-      __syncthreads();
+  int32_t* dst = a.hist + static_cast<int64_t>(g) * a.NB * a.nc + c;
+  for (int i = threadIdx.x; i < a.NB; i += 256) dst[static_cast<int64_t>(i) * a.nc] = sh[i];
+}
+
+__global__ void __launch_bounds__(256) scatter_kernel(InvArgs a) {
+  extern __shared__ int32_t sh[];
+  const int c = blockIdx.x, g = blockIdx.y;
+  const int32_t* off = a.hist + static_cast<int64_t>(g) * a.NB * a.nc + c;
+  for (int i = threadIdx.x; i < a.NB; i += 256) sh[i] = off[static_cast<int64_t>(i) * a.nc];
+  __syncthreads();
+  const int64_t r_lo = static_cast<int64_t>(c) * a.rq;
+  const int64_t r_hi = (r_lo + a.rq) < a.W ? (r_lo + a.rq) : a.W;
+  const int32_t* src = a.idx + ((static_cast<int64_t>(a.b) * a.G + g) * a.T + a.t0 + r_lo) * a.k;
+  const int64_t n = (r_hi - r_lo) * a.k;
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    const int32_t blk = src[i];
+    if (blk >= 0 && blk < a.NB) {
+      const int32_t pos = atomicAdd(&sh[blk], 1);
+      a.entries[pos] = static_cast<int32_t>(r_lo * a.k + i);
     }
-    if (i < nbins) {
-      offsets[i] = carry_e + s_e[tid] - c;
-      chunk_start[i] = carry_c + s_c[tid] - ch;
-    }
-    __syncthreads();
-    if (tid == 1023) {
-      carry_e += s_e[1023];
-      carry_c += s_c[1023];
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    totals[0] = carry_e;
-    totals[1] = carry_c;
   }
 }
 
-__global__ void chunk_kernel(const int32_t* counts, const int32_t* offsets,
-                             const int32_t* chunk_start, int4* chunks, int64_t nbins) {
-  const int64_t bin = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (bin >= nbins) return;
-  const int32_t c = counts[bin];
-  const int32_t off = offsets[bin];
-  int32_t cs = chunk_start[bin];
-  for (int32_t j = 0; j < c; j += kChunkQueries, ++cs) {
-    const int32_t n = (c - j) < kChunkQueries ? (c - j) : kChunkQueries;
-    chunks[cs] = make_int4(static_cast<int32_t>(bin), off + j, n, 0);
+// Block-wide exclusive scan of one value per thread (256 threads).
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* sh, int32_t* total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int32_t x = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += x;
+    __syncthreads();
+  }
+  const int32_t incl = sh[tid];
+  *total = sh[255];
+  __syncthreads();
+  return incl - v;
+}
+
+// Scan phase 1: per-tile sums.
+__global__ void __launch_bounds__(256) scan_tiles_kernel(const int32_t* x, int64_t n,
+                                                         int32_t* tile_sums) {
+  __shared__ int32_t sh[256];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanTile + threadIdx.x * 16;
+  int32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += (base + j < n) ? x[base + j] : 0;
+  int32_t total;
+  block_exclusive_scan(s, sh, &total);
+  if (threadIdx.x == 0) tile_sums[blockIdx.x] = total;
+}
+
+// Scan phase 2: exclusive scan of the tile sums (one workgroup); totals[0] =
+// number of entries, totals[1] = 0 (chunk counter for the chunk kernel).
+__global__ void __launch_bounds__(256) scan_sums_kernel(int32_t* tile_sums, int64_t ntiles,
+                                                        int32_t* totals) {
+  __shared__ int32_t sh[256];
+  int32_t carry = 0;
+  for (int64_t base = 0; base < ntiles; base += 256) {
+    const int64_t i = base + threadIdx.x;
+    const int32_t v = i < ntiles ? tile_sums[i] : 0;
+    int32_t total;
+    const int32_t ex = block_exclusive_scan(v, sh, &total);
+    if (i < ntiles) tile_sums[i] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) {
+    totals[0] = carry;
+    totals[1] = 0;
+  }
+}
+
+// Scan phase 3: exclusive offsets in place.
+__global__ void __launch_bounds__(256) scan_apply_kernel(int32_t* x, int64_t n,
+                                                         const int32_t* tile_sums) {
+  __shared__ int32_t sh[256];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanTile + threadIdx.x * 16;
+  int32_t v[16];
+  int32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    v[j] = (base + j < n) ? x[base + j] : 0;
+    s += v[j];
+  }
+  int32_t total;
+  int32_t run = tile_sums[blockIdx.x] + block_exclusive_scan(s, sh, &total);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (base + j < n) x[base + j] = run;
+    run += v[j];
+  }
+}
+
+__global__ void __launch_bounds__(256) chunk_kernel(const int32_t* off, int32_t* totals,
+                                                    int4* chunks, int32_t nbins, int32_t nc,
+                                                    int32_t bin_base) {
+  const int32_t bin = static_cast<int32_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  int32_t start = 0, n = 0;
+  if (bin < nbins) {
+    start = off[static_cast<int64_t>(bin) * nc];
+    const int32_t end = (bin + 1 < nbins) ? off[static_cast<int64_t>(bin + 1) * nc] : totals[0];
+    n = end - start;
+  }
+  const int32_t nch = (n + kChunkQueries - 1) / kChunkQueries;
+  int32_t incl = nch;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  const int32_t wsum = __shfl(incl, 63);
+  int32_t base = 0;
+  if (lane == 63 && wsum > 0) base = atomicAdd(&totals[1], wsum);
+  base = __shfl(base, 63);
+  int32_t cs = base + incl - nch;
+  for (int32_t j = 0; j < n; j += kChunkQueries, ++cs) {
+    const int32_t m = (n - j) < kChunkQueries ? (n - j) : kChunkQueries;
+    chunks[cs] = make_int4(bin_base + bin, start + j, m, 0);
   }
 }
 
@@ -224,7 +289,7 @@ struct AttnArgs {
   const int32_t* entries;
   const int32_t* totals;
   u16* opart;
-  float* lpart;
+  float2* lpart;
   int64_t T, N, r0;
   int32_t Hq, G, NB, k;
 };
@@ -235,11 +300,19 @@ __device__ __forceinline__ int vt_pos(int key) {
 }
 
 template <int HG>
-__global__ void __launch_bounds__(512) kv_outer_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
   __shared__ __align__(16) unsigned char ks[32768];
   __shared__ __align__(16) unsigned char vt[32768];
-  if (static_cast<int>(blockIdx.x) >= a.totals[1]) return;
-  const int4 ch = a.chunks[blockIdx.x];
+  __shared__ __align__(16) unsigned char ostage[4][4096];  // per-wave output staging
+  // Workgroups are dealt to the 8 XCDs round-robin; give XCD x the x-th
+  // contiguous eighth of the chunk list, so that the chunks of one KV block
+  // (and the rows of one group) share an L2.
+  const int nchunks = a.totals[1];
+  const int per_xcd = (nchunks + 7) >> 3;
+  const int xj = static_cast<int>(blockIdx.x >> 3);
+  const int ci = static_cast<int>(blockIdx.x & 7) * per_xcd + xj;
+  if (xj >= per_xcd || ci >= nchunks) return;
+  const int4 ch = a.chunks[ci];
   const int n = ch.z;
   if (n <= 0) return;
   const int64_t bin = ch.x;
@@ -255,24 +328,80 @@ __global__ void __launch_bounds__(512) kv_outer_kernel(AttnArgs a) {
   const int64_t key0 = blk * kBlock;
   const u16* Kb = a.K + (bg * a.N + key0) * kHeadDim;
   const u16* Vb = a.V + (bg * a.N + key0) * kHeadDim;
+  // Issue the K/V block loads first; they are written to LDS after the first
+  // pass's query rows are on their way.
+  uint4 kr[8], v0r[4], v1r[4];
+  // Branch-free loads (keys past N re-read the last key and are zeroed) keep
+  // the number of outstanding loads fixed for the compiler's wait counting.
+  const int nvalid = static_cast<int>(a.N - key0 < kBlock ? a.N - key0 : kBlock);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = tid + j * 512;
+  for (int j = 0; j < 8; ++j) {
+    const int i = tid + j * 256;
     const int r = i >> 4, c = i & 15;
-    const uint4 v = key0 + r < a.N ? ld16(Kb + r * kHeadDim + c * 8) : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(&ks[swz(r, c)]) = v;
+    const uint4 v = ld16(Kb + (r < nvalid ? r : nvalid - 1) * kHeadDim + c * 8);
+    kr[j] = r < nvalid ? v : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = tid + j * 512;
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + j * 256;
     const int kp = i & 63, c = i >> 6;
     const int k0 = 2 * kp;
-    const uint4 v0 = key0 + k0 < a.N ? ld16(Vb + k0 * kHeadDim + c * 8) : make_uint4(0, 0, 0, 0);
-    const uint4 v1 = key0 + k0 + 1 < a.N ? ld16(Vb + (k0 + 1) * kHeadDim + c * 8)
-                                          : make_uint4(0, 0, 0, 0);
-    const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
-    const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
-    const int P = vt_pos(k0);  // even; k0 + 1 lands at P + 1
+    const uint4 x0 = ld16(Vb + (k0 < nvalid ? k0 : nvalid - 1) * kHeadDim + c * 8);
+    const uint4 x1 = ld16(Vb + (k0 + 1 < nvalid ? k0 + 1 : nvalid - 1) * kHeadDim + c * 8);
+    v0r[j] = k0 < nvalid ? x0 : make_uint4(0, 0, 0, 0);
+    v1r[j] = k0 + 1 < nvalid ? x1 : make_uint4(0, 0, 0, 0);
+  }
+
+  // The chunk's (at most 64) entries live in one register per lane; a row
+  // fetches its entry with a lane shuffle.
+  const int ent = lane < n ? a.entries[ch.y + lane] : 0;
+  const int rows = n * HG;
+  // Window rows are rows t0 .. t0+W-1 of sequence b (r0 = b*T + t0), so a
+  // row's query index is t0 + rl and everything fits 32-bit offsets except
+  // the q pointer.
+  const int64_t t0 = a.r0 - b * a.T;
+  struct Row {
+    bool valid;
+    int hh, slot, rl, p;
+    const u16* q;
+  };
+  auto row_of = [&](int pass) {
+    Row r;
+    const int rr = pass * 128 + wave * 32 + l32;
+    r.valid = rr < rows;
+    const int e = __shfl(ent, r.valid ? rr / HG : 0);
+    r.hh = rr % HG;
+    r.rl = e / a.k;
+    r.slot = e - r.rl * a.k;
+    const int64_t t = t0 + r.rl;
+    r.p = static_cast<int>(a.N - a.T + t);
+    r.q = a.q + ((b * a.T + t) * a.Hq + g * HG + r.hh) * kHeadDim;
+    return r;
+  };
+  auto load_q = [&](const Row& r, bf16x8 (&qf)[8]) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint4 v = ld16(r.q + 16 * s + 8 * half);  // r.q is a valid row
+      qf[s] = as_bf16x8(r.valid ? v : make_uint4(0, 0, 0, 0));
+    }
+  };
+
+  Row cur = row_of(0);
+  bf16x8 qf[8];
+  load_q(cur, qf);
+
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = tid + j * 256;
+    *reinterpret_cast<uint4*>(&ks[swz(i >> 4, i & 15)]) = kr[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + j * 256;
+    const int kp = i & 63, c = i >> 6;
+    const int P = vt_pos(2 * kp);  // even; key 2*kp + 1 lands at P + 1
+    const uint32_t w0[4] = {v0r[j].x, v0r[j].y, v0r[j].z, v0r[j].w};
+    const uint32_t w1[4] = {v1r[j].x, v1r[j].y, v1r[j].z, v1r[j].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t lo = (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
@@ -283,40 +412,46 @@ __global__ void __launch_bounds__(512) kv_outer_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  const int rows = n * HG;
   constexpr float kLog2e = 1.4426950408889634f;
   const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  for (int pass = 0; pass * 256 + wave * 32 < rows; ++pass) {
-    const int rr = pass * 256 + wave * 32 + l32;
-    const bool valid = rr < rows;
-    const int e = valid ? a.entries[ch.y + rr / HG] : 0;
-    const int hh = rr % HG;
-    const int64_t rl = e / a.k;
-    const int slot = e % a.k;
-    const int64_t grow = a.r0 + rl;
-    const int64_t t = grow % a.T;
-    const int64_t p = a.N - a.T + t;
-    const u16* qrow = a.q + ((b * a.T + t) * a.Hq + g * HG + hh) * kHeadDim;
-    bf16x8 qf[8];
+  for (int pass = 0; pass * 128 + wave * 32 < rows; ++pass) {
+    const bool valid = cur.valid;
+    const int hh = cur.hh;
+    const int rl = cur.rl;
+    const int slot = cur.slot;
+    const int p = cur.p;
+
+    // S^T = K Q^T, one 32-key tile at a time; the next tile's K fragments are
+    // read from LDS while the current tile's MFMAs run.
+    f32x16 sacc[4];
+    uint4 ka[2][8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      qf[s] = as_bf16x8(valid ? ld16(qrow + 16 * s + 8 * half) : make_uint4(0, 0, 0, 0));
-
-    // S^T = K Q^T, one 32-key tile at a time
-    f32x16 sacc[4];
+      ka[0][s] = *reinterpret_cast<const uint4*>(&ks[swz(l32, 2 * s + half)]);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      sacc[kt] = f32x16{};
-      const int r = kt * 32 + l32;
+      if (kt + 1 < 4) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&ks[swz(r, 2 * s + half)]));
-        sacc[kt] = mfma32(av, qf[s], sacc[kt]);
+        for (int s = 0; s < 8; ++s)
+          ka[(kt + 1) & 1][s] =
+              *reinterpret_cast<const uint4*>(&ks[swz((kt + 1) * 32 + l32, 2 * s + half)]);
       }
+      sacc[kt] = mfma32(as_bf16x8(ka[kt & 1][0]), qf[0], f32x16{});
+#pragma unroll
+      for (int s = 1; s < 8; ++s) sacc[kt] = mfma32(as_bf16x8(ka[kt & 1][s]), qf[s], sacc[kt]);
       sched_fence();
     }
+    // the next pass's query rows load while this pass does softmax and PV
+    const bool more = (pass + 1) * 128 + wave * 32 < rows;
+    Row nxt = cur;
+    bf16x8 qn[8];
+    if (more) {
+      nxt = row_of(pass + 1);
+      load_q(nxt, qn);
+    }
+
     // causal mask: only the local block of a row has keys after the row
-    const int lim = static_cast<int>(p - key0);  // >= 0: block <= local(row)
+    const int lim = p - static_cast<int>(key0);  // >= 0: block <= local(row)
     if (__ballot(lim < kBlock - 1)) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -334,13 +469,19 @@ __global__ void __launch_bounds__(512) kv_outer_kernel(AttnArgs a) {
     m = fmaxf(m, __shfl_xor(m, 32));
     const float mc = m * qscale;
 
-    // P = exp2(s * log2e/sqrt(d) - max), rounded to bf16, then O^T += V^T P^T
+    // P = exp2(s * log2e/sqrt(d) - max) rounded to bf16, O^T += V^T P^T.  The
+    // V^T fragments of a key tile are read before its exponentials.
     f32x16 oacc[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
     float l = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
+      uint4 va[4][2];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          va[dt][hf] = *reinterpret_cast<const uint4*>(
+              &vt[swz(dt * 32 + l32, kt * 4 + hf * 2 + half)]);
       uint4 pb[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -355,33 +496,54 @@ __global__ void __launch_bounds__(512) kv_outer_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int d = dt * 32 + l32;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const bf16x8 av = as_bf16x8(
-              *reinterpret_cast<const uint4*>(&vt[swz(d, kt * 4 + hf * 2 + half)]));
-          oacc[dt] = mfma32(av, as_bf16x8(pb[hf]), oacc[dt]);
-        }
+        oacc[dt] = kt == 0 ? mfma32(as_bf16x8(va[dt][0]), as_bf16x8(pb[0]), f32x16{})
+                           : mfma32(as_bf16x8(va[dt][0]), as_bf16x8(pb[0]), oacc[dt]);
+        oacc[dt] = mfma32(as_bf16x8(va[dt][1]), as_bf16x8(pb[1]), oacc[dt]);
       }
       sched_fence();
     }
     l += __shfl_xor(l, 32);
-    if (valid) {
-      const float inv = 1.f / l;
-      const int64_t prow = ((rl * a.G + g) * a.k + slot) * HG + hh;
-      u16* dst = a.opart + prow * kHeadDim;
+    // Unnormalised partial O (bf16) and its (log2-domain max, sum).  Each row's
+    // 64 values sit in two lanes in MFMA order; the tile goes through this
+    // wave's LDS area, half the columns at a time, so that every global store
+    // writes whole 128-byte row segments.
+    const int prow = valid ? ((rl * a.G + g) * a.k + slot) * HG + hh : -1;
+    if (valid && half == 0) a.lpart[prow] = make_float2(mc, l);
+    unsigned char* st = ostage[wave];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
+    for (int hpart = 0; hpart < 2; ++hpart) {
+#pragma unroll
+      for (int d2 = 0; d2 < 2; ++d2) {
+        const int dt = 2 * hpart + d2;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = dt * 32 + 8 * q4 + 4 * half;
           uint2 w;
-          w.x = pack_bf16x2(oacc[dt][4 * q4 + 0] * inv, oacc[dt][4 * q4 + 1] * inv);
-          w.y = pack_bf16x2(oacc[dt][4 * q4 + 2] * inv, oacc[dt][4 * q4 + 3] * inv);
-          *reinterpret_cast<uint2*>(dst + d0) = w;
+          w.x = pack_bf16x2(oacc[dt][4 * q4 + 0], oacc[dt][4 * q4 + 1]);
+          w.y = pack_bf16x2(oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3]);
+          const int c16 = d2 * 4 + q4;  // 16-B chunk of the 128-B staged row
+          *reinterpret_cast<uint2*>(&st[l32 * 128 + ((c16 ^ (l32 & 7)) << 4) + 8 * half]) = w;
         }
       }
-      if (half == 0) a.lpart[prow] = (mc + __log2f(l)) * 0.6931471805599453f;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (lane >> 3) + 8 * i, seg = lane & 7;
+        const int dst_row = __shfl(prow, row);
+        const uint4 v = *reinterpret_cast<const uint4*>(&st[row * 128 + ((seg ^ (row & 7)) << 4)]);
+        if (dst_row >= 0)
+          *reinterpret_cast<uint4*>(a.opart + static_cast<int64_t>(dst_row) * kHeadDim +
+                                    hpart * 64 + seg * 8) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (more) {
+      cur = nxt;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf[s] = qn[s];
     }
   }
 }
@@ -395,7 +557,7 @@ __global__ void __launch_bounds__(512) kv_outer_kernel(AttnArgs a) {
 struct CombArgs {
   const int32_t* idx;
   const u16* opart;
-  const float* lpart;
+  const float2* lpart;
   u16* O;
   float* lse;
   int64_t T, r0, W;
@@ -420,35 +582,50 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
   const int d0 = (lane % LPH) * VPL;
   const int64_t pbase = (rl * a.G + g) * a.k;
 
-  float ls[16];
+  // All 16 slots are loaded at once (slots past nval re-read slot 0 and get
+  // weight 0) so that every lane has its whole row in flight.
+  float2 ml[16];
   float mx = -INFINITY;
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
-    ls[s] = s < nval ? a.lpart[(pbase + s) * HG + hh] : -INFINITY;
-    mx = fmaxf(mx, ls[s]);
+    const int ss = s < nval ? s : 0;
+    ml[s] = a.lpart[(pbase + ss) * HG + hh];
+    if (s < nval) mx = fmaxf(mx, ml[s].x);
   }
   float acc[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) acc[j] = 0.f;
   float den = 0.f;
+  if constexpr (VPL >= 8) {
+    uint4 raw[16][VPL / 8];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    if (s < nval) {
-      const float w = __expf(ls[s] - mx);
-      den += w;
-      const u16* src = a.opart + ((pbase + s) * HG + hh) * kHeadDim + d0;
-      if constexpr (VPL >= 8) {
+    for (int s = 0; s < 16; ++s) {
+      const int ss = s < nval ? s : 0;
+      const u16* src = a.opart + ((pbase + ss) * HG + hh) * kHeadDim + d0;
 #pragma unroll
-        for (int j = 0; j < VPL; j += 8) {
-          const uint4 v = ld16(src + j);
-          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      for (int j = 0; j < VPL / 8; ++j) raw[s][j] = ld16(src + 8 * j);
+    }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            acc[j + 2 * u] += w * __uint_as_float(wv[u] << 16);
-            acc[j + 2 * u + 1] += w * __uint_as_float(wv[u] & 0xffff0000u);
-          }
+    for (int s = 0; s < 16; ++s) {
+      const float w = s < nval ? fast_exp2(ml[s].x - mx) : 0.f;
+      den += w * ml[s].y;
+#pragma unroll
+      for (int j = 0; j < VPL / 8; ++j) {
+        const uint32_t wv[4] = {raw[s][j].x, raw[s][j].y, raw[s][j].z, raw[s][j].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc[8 * j + 2 * u] += w * __uint_as_float(wv[u] << 16);
+          acc[8 * j + 2 * u + 1] += w * __uint_as_float(wv[u] & 0xffff0000u);
         }
-      } else {
+      }
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if (s < nval) {
+        const float w = fast_exp2(ml[s].x - mx);
+        den += w * ml[s].y;
+        const u16* src = a.opart + ((pbase + s) * HG + hh) * kHeadDim + d0;
 #pragma unroll
         for (int j = 0; j < VPL; ++j) acc[j] += w * bf16_to_f32(src[j]);
       }
@@ -470,16 +647,18 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
 #pragma unroll
     for (int j = 0; j < VPL; ++j) dst[j] = f32_to_bf16(acc[j] * inv);
   }
+  // lse in natural log: (max + log2(sum)) * ln 2, the max being log2-domain
   if (a.lse && (lane % LPH) == 0)
-    a.lse[(b * a.Hq + g * HG + hh) * a.T + t] = mx + logf(den);
+    a.lse[(b * a.Hq + g * HG + hh) * a.T + t] = (mx + __log2f(den)) * 0.6931471805599453f;
 }
 
 // ---------------------------------------------------------------------------
 template <int HG>
 static hipError_t launch_kv_combine(const AttnArgs& aa, const CombArgs& ca, int64_t grid_chunks,
                                     hipStream_t st) {
-  hipLaunchKernelGGL((kv_outer_kernel<HG>), dim3(static_cast<unsigned>(grid_chunks)), dim3(512),
-                     0, st, aa);
+  const int64_t grid = (grid_chunks + 7) & ~static_cast<int64_t>(7);
+  hipLaunchKernelGGL((kv_outer_kernel<HG>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+                     aa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t cgrid = (ca.W * ca.G + 3) / 4;
@@ -504,72 +683,90 @@ static unsigned blocks_for(int64_t n, int per) {
   return static_cast<unsigned>((n + per - 1) / per);
 }
 
+static AttnArgs attn_args(const void* q, const void* K, const void* V, const AttnWorkspace& w,
+                          int64_t T, int64_t N, int64_t r0, int Hq, int G, int32_t NB, int k) {
+  AttnArgs aa;
+  aa.q = static_cast<const u16*>(q);
+  aa.K = static_cast<const u16*>(K);
+  aa.V = static_cast<const u16*>(V);
+  aa.chunks = w.chunks;
+  aa.entries = w.entries;
+  aa.totals = w.totals;
+  aa.opart = w.opart;
+  aa.lpart = w.lpart;
+  aa.T = T;
+  aa.N = N;
+  aa.r0 = r0;
+  aa.Hq = Hq;
+  aa.G = G;
+  aa.NB = NB;
+  aa.k = k;
+  return aa;
+}
+
+static CombArgs comb_args(const int32_t* idx, void* O, float* lse, const AttnWorkspace& w,
+                          int64_t T, int64_t r0, int64_t W, int Hq, int G, int k) {
+  CombArgs ca;
+  ca.idx = idx;
+  ca.opart = w.opart;
+  ca.lpart = w.lpart;
+  ca.O = static_cast<u16*>(O);
+  ca.lse = lse;
+  ca.T = T;
+  ca.r0 = r0;
+  ca.W = W;
+  ca.Hq = Hq;
+  ca.G = G;
+  ca.k = k;
+  return ca;
+}
+
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse, int64_t B,
                                int64_t T, int64_t N, int Hq, int G, int k,
                                const AttnWorkspace& w, hipStream_t st) {
   const int hg = Hq / G;
   const int32_t NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
-  const int64_t rows = B * T;
-  for (int64_t r0 = 0; r0 < rows; r0 += w.window) {
-    const int64_t W = (rows - r0) < w.window ? (rows - r0) : w.window;
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks_for(w.nbins, 256)), dim3(256), 0, st,
-                       w.counts, w.nbins, 0);
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks_for(w.nbins, 256)), dim3(256), 0, st,
-                       w.cursor, w.nbins, 0);
-    InvArgs ia;
-    ia.idx = idx;
-    ia.counts = w.counts;
-    ia.cursor = w.cursor;
-    ia.offsets = w.offsets;
-    ia.entries = w.entries;
-    ia.T = T;
-    ia.r0 = r0;
-    ia.W = W;
-    ia.G = G;
-    ia.k = k;
-    ia.NB = NB;
-    const int64_t n_ent = W * G * k;
-    hipLaunchKernelGGL(count_kernel, dim3(blocks_for(n_ent, 256)), dim3(256), 0, st, ia);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets,
-                       w.chunk_start, w.totals, w.nbins);
-    hipLaunchKernelGGL(scatter_kernel, dim3(blocks_for(n_ent, 256)), dim3(256), 0, st, ia);
-    hipLaunchKernelGGL(chunk_kernel, dim3(blocks_for(w.nbins, 256)), dim3(256), 0, st, w.counts,
-                       w.offsets, w.chunk_start, w.chunks, w.nbins);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    AttnArgs aa;
-    aa.q = static_cast<const u16*>(q);
-    aa.K = static_cast<const u16*>(K);
-    aa.V = static_cast<const u16*>(V);
-    aa.chunks = w.chunks;
-    aa.entries = w.entries;
-    aa.totals = w.totals;
-    aa.opart = w.opart;
-    aa.lpart = w.lpart;
-    aa.T = T;
-    aa.N = N;
-    aa.r0 = r0;
-    aa.Hq = Hq;
-    aa.G = G;
-    aa.NB = NB;
-    aa.k = k;
-    CombArgs ca;
-    ca.idx = idx;
-    ca.opart = w.opart;
-    ca.lpart = w.lpart;
-    ca.O = static_cast<u16*>(O);
-    ca.lse = lse;
-    ca.T = T;
-    ca.r0 = r0;
-    ca.W = W;
-    ca.Hq = Hq;
-    ca.G = G;
-    ca.k = k;
-    const int64_t grid = max_chunks_for(W, w.nbins, G, k, false);
-    e = dispatch_hg(hg, aa, ca, grid, st);
-    if (e != hipSuccess) return e;
+  const size_t lds = sizeof(int32_t) * NB;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t t0 = 0; t0 < T; t0 += w.window) {
+      const int64_t W = (T - t0) < w.window ? (T - t0) : w.window;
+      InvArgs ia;
+      ia.idx = idx;
+      ia.hist = w.hist;
+      ia.entries = w.entries;
+      ia.T = T;
+      ia.t0 = t0;
+      ia.W = W;
+      ia.b = static_cast<int32_t>(b);
+      ia.G = G;
+      ia.k = k;
+      ia.NB = NB;
+      ia.rq = w.rq;
+      ia.nc = static_cast<int32_t>((W + w.rq - 1) / w.rq);
+      const int64_t nhist = static_cast<int64_t>(G) * NB * ia.nc;
+      const int64_t ntiles = (nhist + kScanTile - 1) / kScanTile;
+      const dim3 ugrid(static_cast<unsigned>(ia.nc), static_cast<unsigned>(G));
+      hipLaunchKernelGGL(hist_kernel, ugrid, dim3(256), lds, st, ia);
+      hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, st,
+                         w.hist, nhist, w.tile_sums);
+      hipLaunchKernelGGL(scan_sums_kernel, dim3(1), dim3(256), 0, st, w.tile_sums, ntiles,
+                         w.totals);
+      hipLaunchKernelGGL(scan_apply_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, st,
+                         w.hist, nhist, w.tile_sums);
+      hipLaunchKernelGGL(scatter_kernel, ugrid, dim3(256), lds, st, ia);
+      hipLaunchKernelGGL(chunk_kernel, dim3(blocks_for(static_cast<int64_t>(G) * NB, 256)),
+                         dim3(256), 0, st, w.hist, w.totals, w.chunks, G * NB, ia.nc,
+                         static_cast<int32_t>(b * G * NB));
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t r0 = b * T + t0;
+      const AttnArgs aa = attn_args(q, K, V, w, T, N, r0, Hq, G, NB, k);
+      const CombArgs ca = comb_args(idx, O, lse, w, T, r0, W, Hq, G, k);
+      const int64_t grid = max_chunks_for(W, w.nbins, G, k, false);
+      e = dispatch_hg(hg, aa, ca, grid, st);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
@@ -582,34 +779,8 @@ hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
   const int64_t n = B * G * k;
   hipLaunchKernelGGL(decode_work_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, idx,
                      w.chunks, w.entries, w.totals, B, G, k, NB);
-  AttnArgs aa;
-  aa.q = static_cast<const u16*>(q);
-  aa.K = static_cast<const u16*>(K);
-  aa.V = static_cast<const u16*>(V);
-  aa.chunks = w.chunks;
-  aa.entries = w.entries;
-  aa.totals = w.totals;
-  aa.opart = w.opart;
-  aa.lpart = w.lpart;
-  aa.T = 1;
-  aa.N = N;
-  aa.r0 = 0;
-  aa.Hq = Hq;
-  aa.G = G;
-  aa.NB = NB;
-  aa.k = k;
-  CombArgs ca;
-  ca.idx = idx;
-  ca.opart = w.opart;
-  ca.lpart = w.lpart;
-  ca.O = static_cast<u16*>(O);
-  ca.lse = lse;
-  ca.T = 1;
-  ca.r0 = 0;
-  ca.W = B;
-  ca.Hq = Hq;
-  ca.G = G;
-  ca.k = k;
+  const AttnArgs aa = attn_args(q, K, V, w, 1, N, 0, Hq, G, NB, k);
+  const CombArgs ca = comb_args(idx, O, lse, w, 1, 0, B, Hq, G, k);
   return dispatch_hg(hg, aa, ca, n, st);
 }
 

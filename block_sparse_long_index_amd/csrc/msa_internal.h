@@ -20,26 +20,25 @@ hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
                             int64_t N, int G, int k, hipStream_t st);
 
 struct AttnWorkspace {
-  int32_t* counts;       // [nbins]
-  int32_t* cursor;       // [nbins]
-  int32_t* offsets;      // [nbins]
-  int32_t* chunk_start;  // [nbins]
-  int32_t* totals;       // [4]: entries, chunks
-  int32_t* entries;      // [W * G * k]
-  int4* chunks;          // [max_chunks]
-  uint16_t* opart;       // [W, G, k, hg, 128] bf16
-  float* lpart;          // [W, G, k, hg]
-  int64_t window;        // rows per window
+  int32_t* hist;       // [G * NB * nc]: unit block counts, then exclusive offsets
+  int32_t* tile_sums;  // [ntiles]
+  int32_t* totals;     // [4]: entries, chunks
+  int32_t* entries;    // [W * G * k]
+  int4* chunks;        // [max_chunks]
+  uint16_t* opart;     // [W, G, k, hg, 128] bf16, unnormalised
+  float2* lpart;       // [W, G, k, hg]: (log2-domain row max, row sum)
+  int64_t window;      // query rows per window
   int64_t max_chunks;
-  int64_t nbins;
+  int64_t nbins;       // G * NB
+  int64_t nhist, ntiles;
+  int32_t rq, nc;      // rows per histogram unit, units per full window
 };
 
-// Bytes of workspace for a window of `window` query rows.
+// Bytes of workspace for a window of `window` query rows of one sequence.
 // decode: one chunk per (sequence, group, slot) instead of the inverted lists.
-size_t attn_workspace_bytes(int64_t window, int64_t B, int64_t N, int G,
-                            int hg, int k, bool decode);
-void attn_workspace_carve(void* ws, int64_t window, int64_t B, int64_t N,
-                          int G, int hg, int k, bool decode, AttnWorkspace* out);
+size_t attn_workspace_bytes(int64_t window, int64_t N, int G, int hg, int k, bool decode);
+void attn_workspace_carve(void* ws, int64_t window, int64_t N, int G, int hg, int k,
+                          bool decode, AttnWorkspace* out);
 
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse,

@@ -117,8 +117,8 @@ index_tile_kernel(TileArgs a) {
     const u16* src = a.qI + ((static_cast<int64_t>(b) * a.T + (ok ? t : 0)) * G + g) * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      uint4 v = ok ? ld16(src + 16 * s + 8 * half) : make_uint4(0, 0, 0, 0);
-      qf[j][s] = as_bf16x8(v);
+      const uint4 v = ld16(src + 16 * s + 8 * half);  // src is a valid row
+      qf[j][s] = as_bf16x8(ok ? v : make_uint4(0, 0, 0, 0));
     }
   }
 
@@ -145,13 +145,17 @@ index_tile_kernel(TileArgs a) {
   const bool s_vec = (a.NB & 3) == 0;
 
   uint4 pf[PF];
+  // Branch-free: keys past N re-read key N-1 and are zeroed, so that every
+  // iteration issues the same number of loads and the compiler's wait
+  // counting does not fall back to waiting for the whole prefetch.
   auto load_block = [&](int64_t kb) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int i = tid + j * NT;
       const int r = i >> 4, c = i & 15;
       const int64_t key = kb * kBlock + r;
-      pf[j] = key < a.N ? ld16(kbase + key * kHeadDim + c * 8) : make_uint4(0, 0, 0, 0);
+      const uint4 v = ld16(kbase + (key < a.N ? key : a.N - 1) * kHeadDim + c * 8);
+      pf[j] = key < a.N ? v : make_uint4(0, 0, 0, 0);
     }
   };
   auto store_block = [&](int buf) {
@@ -167,6 +171,7 @@ index_tile_kernel(TileArgs a) {
     load_block(0);
     store_block(0);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // q^I fragments and block 0 have landed
   __syncthreads();
 
   for (int64_t kb = 0; kb < nkb; ++kb) {
@@ -175,16 +180,23 @@ index_tile_kernel(TileArgs a) {
     const unsigned char* buf = kbuf[kb & 1];
     float m0 = -INFINITY, m1 = -INFINITY;
     const bool masked = WRITE_S && (kb == L);
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      f32x16 acc0 = {}, acc1 = {};
+    // One 32-key tile: 8 K fragments from LDS, 16 MFMAs into two column tiles.
+    auto tile = [&](int kt, f32x16& c0, f32x16& c1) {
       const int r = kt * 32 + l32;
+      uint4 av[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&buf[swz(r, 2 * s + half)]));
-        acc0 = mfma32(av, qf[0][s], acc0);
-        acc1 = mfma32(av, qf[1][s], acc1);
+      for (int s = 0; s < 8; ++s)
+        av[s] = *reinterpret_cast<const uint4*>(&buf[swz(r, 2 * s + half)]);
+      c0 = mfma32(as_bf16x8(av[0]), qf[0][0], f32x16{});
+      c1 = mfma32(as_bf16x8(av[0]), qf[1][0], f32x16{});
+#pragma unroll
+      for (int s = 1; s < 8; ++s) {
+        c0 = mfma32(as_bf16x8(av[s]), qf[0][s], c0);
+        c1 = mfma32(as_bf16x8(av[s]), qf[1][s], c1);
       }
+    };
+    // Block max over a finished tile (with the causal mask in the local block).
+    auto reduce = [&](int kt, f32x16& c0, f32x16& c1) {
       if (masked) {
         // offsets inside the local block past each column's position
         const int lim0 = static_cast<int>(colp[0] - kb * kBlock);
@@ -192,17 +204,30 @@ index_tile_kernel(TileArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int off = kt * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (off > lim0) acc0[e] = -INFINITY;
-          if (off > lim1) acc1[e] = -INFINITY;
+          if (off > lim0) c0[e] = -INFINITY;
+          if (off > lim1) c1[e] = -INFINITY;
         }
       }
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        m0 = max3(m0, acc0[e], acc0[e + 1]);
-        m1 = max3(m1, acc1[e], acc1[e + 1]);
+        m0 = max3(m0, c0[e], c0[e + 1]);
+        m1 = max3(m1, c1[e], c1[e + 1]);
       }
-      sched_fence();
-    }
+    };
+    // Software pipeline: the MFMAs of tile kt run while tile kt-1 is reduced.
+    f32x16 ta0, ta1, tb0, tb1;
+    tile(0, ta0, ta1);
+    sched_fence();
+    tile(1, tb0, tb1);
+    reduce(0, ta0, ta1);
+    sched_fence();
+    tile(2, ta0, ta1);
+    reduce(1, tb0, tb1);
+    sched_fence();
+    tile(3, tb0, tb1);
+    reduce(2, ta0, ta1);
+    sched_fence();
+    reduce(3, tb0, tb1);
     m0 = fmaxf(m0, __shfl_xor(m0, 32));
     m1 = fmaxf(m1, __shfl_xor(m1, 32));
     const float v = half ? m1 : m0;
@@ -324,9 +349,9 @@ hipError_t launch_index_tiles(bool write_scores, const void* qI, const void* kI,
 // consecutive blocks of one sequence, each wave 4 of them.  16x16x32 MFMA with
 // 16 keys on M and the G index queries on N (unused columns are zero).  The
 // 32 16-B loads of a block are all issued before its MFMAs so that each wave
-// keeps 32 KB in flight.  Keys are spread so that each lane reads 64
-// contiguous bytes of its key row: lane quarter qd holds d = 32*qd .. +31, and
-// k-step s takes d = 32*qd + 8*s .. +7 (the q^I fragments use the same map).
+// keeps 32 KB in flight.  k-step s covers d = 32*s .. 32*s+31 with lane
+// quarter qd holding d = 32*s + 8*qd .. +7, so one load instruction reads 64
+// contiguous bytes of each of 16 key rows.
 // ---------------------------------------------------------------------------
 struct ScanArgs {
   const u16* qI;
@@ -344,7 +369,7 @@ __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
   const u16* qsrc = a.qI + (static_cast<int64_t>(b) * a.G + (col < a.G ? col : 0)) * kHeadDim;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    uint4 v = col < a.G ? ld16(qsrc + 32 * qd + 8 * s) : make_uint4(0, 0, 0, 0);
+    uint4 v = col < a.G ? ld16(qsrc + 32 * s + 8 * qd) : make_uint4(0, 0, 0, 0);
     qf[s] = as_bf16x8(v);
   }
   const u16* kbase = a.kI + static_cast<int64_t>(b) * a.N * kHeadDim;
@@ -356,10 +381,9 @@ __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int kg = 0; kg < 8; ++kg) {
       const int64_t key = kb * kBlock + kg * 16 + col;
-      const u16* src = kbase + key * kHeadDim + 32 * qd;
+      const u16* src = kbase + (key < a.N ? key : a.N - 1) * kHeadDim + 8 * qd;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        d[kg][s] = key < a.N ? ld16(src + 8 * s) : make_uint4(0, 0, 0, 0);
+      for (int s = 0; s < 4; ++s) d[kg][s] = ld16(src + 32 * s);  // tail keys masked below
     }
     float m = -INFINITY;
 #pragma unroll
