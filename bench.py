@@ -40,6 +40,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def select_traffic():
+    """Bytes per launch of the fused select kernel from the committed counter
+    summary (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None if
+    the kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "fused_select_prefill_128k_traffic.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not (m and t):
+        return None
+    h = hashlib.sha256()
+    for f in ("msa_select.hip", "msa_common.h"):
+        with open(os.path.join(ROOT, "block_sparse_long_index_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return int(t.group(1)) if h.hexdigest() == m.group(1) else None
+
+
 def ev():
     return torch.cuda.Event(enable_timing=True)
 
@@ -258,7 +280,8 @@ def main():
         out["roofline"] = {"kernel": "index_tile_kernel (fused select: scores, block max, "
                                      "top-k)",
                            "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                           "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                           "traffic": select_traffic(),
                            "flops_per_launch": fl["index"], "avg_launch_ms": sel}
         out["stages"] = {"select_ms": sel, "attention_ms": att,
                          "attention_TFLOPs": fl["main"] / (att * 1e-3) / 1e12,

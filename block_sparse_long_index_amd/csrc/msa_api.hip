@@ -23,7 +23,8 @@ int hip_fail(hipError_t e, const char* where) {
   return fail(MSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
-constexpr int64_t kDefaultWindow = 16384;  // query rows per prefill window
+constexpr int64_t kDefaultWindow = int64_t(1) << 20;  // rows per inversion (one sequence)
+constexpr int64_t kStageRows = 4096;                    // rows of one group per KV-outer stage
 constexpr int64_t kMaxElems = int64_t(1) << 46;
 
 bool pow2_upto(int v, int hi) { return v >= 1 && v <= hi && (v & (v - 1)) == 0; }
@@ -81,12 +82,15 @@ int64_t default_window(const msa_dims_t* d) {
   return d->T < kDefaultWindow ? d->T : kDefaultWindow;
 }
 
+int64_t stage_rows_for(int64_t window) { return window < kStageRows ? window : kStageRows; }
+
 size_t prefill_ws(const msa_dims_t* d, int64_t window) {
-  return msa::attn_workspace_bytes(window, d->N, d->G, d->Hq / d->G, d->k, false);
+  return msa::attn_workspace_bytes(window, stage_rows_for(window), d->N, d->G, d->Hq / d->G, d->k,
+                                   false);
 }
 
 size_t decode_ws(const msa_dims_t* d) {
-  return msa::attn_workspace_bytes(d->B, d->N, d->G, d->Hq / d->G, d->k, true);
+  return msa::attn_workspace_bytes(d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true);
 }
 
 }  // namespace
@@ -202,7 +206,8 @@ int msa_sparse_attn_prefill(const msa_dims_t* d, const void* q, const void* K, c
     hi = lo;
   }
   msa::AttnWorkspace w;
-  msa::attn_workspace_carve(ws, hi, d->N, d->G, d->Hq / d->G, d->k, false, &w);
+  msa::attn_workspace_carve(ws, hi, stage_rows_for(hi), d->N, d->G, d->Hq / d->G, d->k, false,
+                            &w);
   const hipError_t e = msa::launch_attn_prefill(q, K, V, idx, O, lse, d->B, d->T, d->N, d->Hq,
                                                 d->G, d->k, w, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_prefill");
@@ -227,7 +232,7 @@ int msa_sparse_attn_decode(const msa_dims_t* d, const void* q, const void* K, co
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need,
                 ws_bytes);
   msa::AttnWorkspace w;
-  msa::attn_workspace_carve(ws, d->B, d->N, d->G, d->Hq / d->G, d->k, true, &w);
+  msa::attn_workspace_carve(ws, d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true, &w);
   const hipError_t e = msa::launch_attn_decode(q, K, V, idx, O, lse, d->B, d->N, d->Hq, d->G,
                                                d->k, w, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode");

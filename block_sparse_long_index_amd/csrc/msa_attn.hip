@@ -32,52 +32,71 @@ static int32_t unit_rows(int64_t NB) {
   return r;
 }
 
-static int64_t max_chunks_for(int64_t window, int64_t nbins, int G, int k, bool decode) {
-  const int64_t entries = window * G * k;
-  if (decode) return entries;  // one chunk per (sequence, group, slot)
-  return entries / kChunkQueries + (nbins < entries ? nbins : entries) + 1;
+// Chunks one stage can produce: its entries in chunks of 64 queries plus at
+// most one partial chunk per block.
+static int64_t stage_max_chunks(int64_t stage_rows, int64_t NB, int k) {
+  const int64_t entries = stage_rows * k;
+  return entries / kChunkQueries + (NB < entries ? NB : entries) + 1;
 }
 
-static void layout(int64_t window, int64_t N, int G, int hg, int k, bool decode, size_t* off,
-                   AttnWorkspace* w) {
+static void layout(int64_t window, int64_t stage_rows, int64_t N, int G, int hg, int k,
+                   bool decode, size_t* off, AttnWorkspace* w) {
   const int64_t NB = (N + kBlock - 1) / kBlock;
-  const int64_t nbins = G * NB;
   const int32_t rq = unit_rows(NB);
-  const int32_t nc = decode ? 0 : static_cast<int32_t>((window + rq - 1) / rq);
-  const int64_t nhist = nbins * nc;
+  int32_t nc = 0;
+  int64_t nstages = 0, maxc = 0, prow_count = 0;
+  if (decode) {
+    // one chunk per (sequence, group, slot); partials for every (row, group)
+    nstages = 1;
+    maxc = window * G * k;
+    prow_count = window * G * k * hg;
+  } else {
+    // stages are whole histogram units, so a stage's entries are a union of
+    // unit ranges of the scanned offsets
+    stage_rows = ((stage_rows + rq - 1) / rq) * rq;
+    nc = static_cast<int32_t>((window + rq - 1) / rq);
+    nstages = G * ((window + stage_rows - 1) / stage_rows);
+    maxc = stage_max_chunks(stage_rows, NB, k);
+    prow_count = stage_rows * k * hg;  // one stage: stage_rows rows of one group
+  }
+  const int64_t nhist = static_cast<int64_t>(G) * NB * nc;
   const int64_t ntiles = (nhist + kScanTile - 1) / kScanTile;
   const int64_t entries = window * G * k;
-  const int64_t mch = max_chunks_for(window, nbins, G, k, decode);
   size_t o = 0;
   off[0] = o; o += align256(sizeof(int32_t) * (nhist > 0 ? nhist : 1));
   off[1] = o; o += align256(sizeof(int32_t) * (ntiles > 0 ? ntiles : 1));
-  off[2] = o; o += align256(sizeof(int32_t) * 4);
+  off[2] = o; o += align256(sizeof(int32_t) * (4 + nstages));
   off[3] = o; o += align256(sizeof(int32_t) * entries);
-  off[4] = o; o += align256(sizeof(int4) * mch);
-  off[5] = o; o += align256(sizeof(uint16_t) * entries * hg * kHeadDim);
-  off[6] = o; o += align256(sizeof(float2) * entries * hg);
+  off[4] = o; o += align256(sizeof(int4) * nstages * maxc);
+  // one extra (sink) row absorbs the stores of rows past a chunk's end
+  off[5] = o; o += align256(sizeof(uint16_t) * (prow_count + 1) * kHeadDim);
+  off[6] = o; o += align256(sizeof(float2) * (prow_count + 1));
   off[7] = o;
   if (w) {
     w->window = window;
-    w->max_chunks = mch;
-    w->nbins = nbins;
+    w->stage_rows = stage_rows;
+    w->max_chunks = maxc;
+    w->nstages = nstages;
+    w->nbins = static_cast<int64_t>(G) * NB;
     w->rq = rq;
     w->nc = nc;
     w->nhist = nhist;
     w->ntiles = ntiles;
+    w->sink = prow_count;
   }
 }
 
-size_t attn_workspace_bytes(int64_t window, int64_t N, int G, int hg, int k, bool decode) {
+size_t attn_workspace_bytes(int64_t window, int64_t stage_rows, int64_t N, int G, int hg, int k,
+                            bool decode) {
   size_t off[8];
-  layout(window, N, G, hg, k, decode, off, nullptr);
+  layout(window, stage_rows, N, G, hg, k, decode, off, nullptr);
   return off[7];
 }
 
-void attn_workspace_carve(void* ws, int64_t window, int64_t N, int G, int hg, int k,
-                          bool decode, AttnWorkspace* w) {
+void attn_workspace_carve(void* ws, int64_t window, int64_t stage_rows, int64_t N, int G, int hg,
+                          int k, bool decode, AttnWorkspace* w) {
   size_t off[8];
-  layout(window, N, G, hg, k, decode, off, w);
+  layout(window, stage_rows, N, G, hg, k, decode, off, w);
   char* p = static_cast<char*>(ws);
   w->hist = reinterpret_cast<int32_t*>(p + off[0]);
   w->tile_sums = reinterpret_cast<int32_t*>(p + off[1]);
@@ -101,6 +120,11 @@ void attn_workspace_carve(void* ws, int64_t window, int64_t N, int G, int hg, in
 // LDS atomics keep hot blocks (block 0, the local block, needles) from
 // serialising on a global counter.
 // ---------------------------------------------------------------------------
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
 struct InvArgs {
   const int32_t* idx;
   int32_t* hist;
@@ -177,7 +201,7 @@ __global__ void __launch_bounds__(256) scan_tiles_kernel(const int32_t* x, int64
 }
 
 // Scan phase 2: exclusive scan of the tile sums (one workgroup); totals[0] =
-// number of entries, totals[1] = 0 (chunk counter for the chunk kernel).
+// number of entries.
 __global__ void __launch_bounds__(256) scan_sums_kernel(int32_t* tile_sums, int64_t ntiles,
                                                         int32_t* totals) {
   __shared__ int32_t sh[256];
@@ -190,10 +214,7 @@ __global__ void __launch_bounds__(256) scan_sums_kernel(int32_t* tile_sums, int6
     if (i < ntiles) tile_sums[i] = carry + ex;
     carry += total;
   }
-  if (threadIdx.x == 0) {
-    totals[0] = carry;
-    totals[1] = 0;
-  }
+  if (threadIdx.x == 0) totals[0] = carry;
 }
 
 // Scan phase 3: exclusive offsets in place.
@@ -217,15 +238,32 @@ __global__ void __launch_bounds__(256) scan_apply_kernel(int32_t* x, int64_t n,
   }
 }
 
-__global__ void __launch_bounds__(256) chunk_kernel(const int32_t* off, int32_t* totals,
-                                                    int4* chunks, int32_t nbins, int32_t nc,
-                                                    int32_t bin_base) {
-  const int32_t bin = static_cast<int32_t>(blockIdx.x) * 256 + threadIdx.x;
+// Stage chunk lists.  Stage (g, s) covers group g and the window rows of
+// sub-window s (units [s*U, (s+1)*U)); thread (g, s, blk) cuts the entries of
+// bin (g, blk) in those units into chunks of at most 64 queries.  A wave
+// holds 64 blocks of one stage and takes its chunk slots with one atomic.
+__global__ void __launch_bounds__(256) stage_chunk_kernel(const int32_t* off, int32_t* totals,
+                                                          int4* chunks, int32_t NB, int64_t nbins,
+                                                          int32_t nc, int32_t U, int32_t S,
+                                                          int64_t maxc, int32_t bin_base) {
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_stage = ((NB + 63) / 64) * 64;  // waves never straddle stages
+  const int64_t st = tid / per_stage;
+  if (st >= nbins / NB * S) return;  // whole waves: st is uniform in a wave
+  const int32_t blk = static_cast<int32_t>(tid % per_stage);
   const int lane = threadIdx.x & 63;
+  const int32_t g = static_cast<int32_t>(st / S), sub = static_cast<int32_t>(st % S);
   int32_t start = 0, n = 0;
-  if (bin < nbins) {
-    start = off[static_cast<int64_t>(bin) * nc];
-    const int32_t end = (bin + 1 < nbins) ? off[static_cast<int64_t>(bin + 1) * nc] : totals[0];
+  if (blk < NB) {
+    const int64_t bin = static_cast<int64_t>(g) * NB + blk;
+    const int32_t u0 = sub * U;
+    const int32_t u1 = (sub + 1) * U < nc ? (sub + 1) * U : nc;
+    start = off[bin * nc + u0];
+    int32_t end;
+    if (u1 < nc)
+      end = off[bin * nc + u1];
+    else  // the flat order continues with the next bin (next group after the last block)
+      end = (bin + 1 < nbins) ? off[(bin + 1) * nc] : totals[0];
     n = end - start;
   }
   const int32_t nch = (n + kChunkQueries - 1) / kChunkQueries;
@@ -237,12 +275,13 @@ __global__ void __launch_bounds__(256) chunk_kernel(const int32_t* off, int32_t*
   }
   const int32_t wsum = __shfl(incl, 63);
   int32_t base = 0;
-  if (lane == 63 && wsum > 0) base = atomicAdd(&totals[1], wsum);
+  if (lane == 63 && wsum > 0) base = atomicAdd(&totals[4 + st], wsum);
   base = __shfl(base, 63);
+  int4* out = chunks + st * maxc;
   int32_t cs = base + incl - nch;
   for (int32_t j = 0; j < n; j += kChunkQueries, ++cs) {
     const int32_t m = (n - j) < kChunkQueries ? (n - j) : kChunkQueries;
-    chunks[cs] = make_int4(bin_base + bin, start + j, m, 0);
+    out[cs] = make_int4(bin_base + g * NB + blk, start + j, m, 0);
   }
 }
 
@@ -285,13 +324,16 @@ struct AttnArgs {
   const u16* q;
   const u16* K;
   const u16* V;
-  const int4* chunks;
+  const int4* chunks;     // this launch's chunk list
   const int32_t* entries;
-  const int32_t* totals;
+  const int32_t* count;   // number of chunks in the list
   u16* opart;
   float2* lpart;
-  int64_t T, N, r0;
+  int64_t T, N, r0;       // r0: global row (b*T + t) of window row 0
   int32_t Hq, G, NB, k;
+  int32_t rl_base;        // first window row of this launch's partial buffer
+  int32_t pgroups;        // groups held by the partial buffer (1 for a stage, G for decode)
+  int32_t sink;           // spare partial row that absorbs rows past a chunk's end
 };
 
 __device__ __forceinline__ int vt_pos(int key) {
@@ -307,7 +349,7 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
   // Workgroups are dealt to the 8 XCDs round-robin; give XCD x the x-th
   // contiguous eighth of the chunk list, so that the chunks of one KV block
   // (and the rows of one group) share an L2.
-  const int nchunks = a.totals[1];
+  const int nchunks = *a.count;
   const int per_xcd = (nchunks + 7) >> 3;
   const int xj = static_cast<int>(blockIdx.x >> 3);
   const int ci = static_cast<int>(blockIdx.x & 7) * per_xcd + xj;
@@ -360,35 +402,33 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
   // row's query index is t0 + rl and everything fits 32-bit offsets except
   // the q pointer.
   const int64_t t0 = a.r0 - b * a.T;
-  struct Row {
-    bool valid;
-    int hh, slot, rl, p;
-    const u16* q;
-  };
-  auto row_of = [&](int pass) {
-    Row r;
+  // A row's bookkeeping lives in plain scalars (a struct here ends up in
+  // scratch memory, whose accesses share the load/store wait counter).
+  auto row_of = [&](int pass, bool& valid, int& hh, int& slot, int& rl, int& p, const u16*& q) {
     const int rr = pass * 128 + wave * 32 + l32;
-    r.valid = rr < rows;
-    const int e = __shfl(ent, r.valid ? rr / HG : 0);
-    r.hh = rr % HG;
-    r.rl = e / a.k;
-    r.slot = e - r.rl * a.k;
-    const int64_t t = t0 + r.rl;
-    r.p = static_cast<int>(a.N - a.T + t);
-    r.q = a.q + ((b * a.T + t) * a.Hq + g * HG + r.hh) * kHeadDim;
-    return r;
+    valid = rr < rows;
+    const int e = __shfl(ent, valid ? rr / HG : 0);
+    hh = rr % HG;
+    rl = e / a.k;
+    slot = e - rl * a.k;
+    const int64_t t = t0 + rl;
+    p = static_cast<int>(a.N - a.T + t);
+    q = a.q + ((b * a.T + t) * a.Hq + g * HG + hh) * kHeadDim;
   };
-  auto load_q = [&](const Row& r, bf16x8 (&qf)[8]) {
+  // Rows past the chunk's end load a real row (entry 0) and are never
+  // stored, so the loads need no masking: using the data immediately would
+  // force a wait right after the prefetch is issued.
+  auto load_q = [&](const u16* q, bf16x8 (&qf)[8]) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint4 v = ld16(r.q + 16 * s + 8 * half);  // r.q is a valid row
-      qf[s] = as_bf16x8(r.valid ? v : make_uint4(0, 0, 0, 0));
-    }
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(ld16(q + 16 * s + 8 * half));
   };
 
-  Row cur = row_of(0);
+  bool valid;
+  int hh, slot, rl, p;
+  const u16* qptr;
+  row_of(0, valid, hh, slot, rl, p, qptr);
   bf16x8 qf[8];
-  load_q(cur, qf);
+  load_q(qptr, qf);
 
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -410,17 +450,14 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
       *reinterpret_cast<uint32_t*>(&vt[swz(d, P >> 3) + ((2 * P) & 15)]) = lo | (hi << 16);
     }
   }
+  // Nothing is left in flight past this point, so the waits inside the pass
+  // loop only ever count the loop's own loads and stores.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   constexpr float kLog2e = 1.4426950408889634f;
   const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   for (int pass = 0; pass * 128 + wave * 32 < rows; ++pass) {
-    const bool valid = cur.valid;
-    const int hh = cur.hh;
-    const int rl = cur.rl;
-    const int slot = cur.slot;
-    const int p = cur.p;
-
     // S^T = K Q^T, one 32-key tile at a time; the next tile's K fragments are
     // read from LDS while the current tile's MFMAs run.
     f32x16 sacc[4];
@@ -443,11 +480,13 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
     }
     // the next pass's query rows load while this pass does softmax and PV
     const bool more = (pass + 1) * 128 + wave * 32 < rows;
-    Row nxt = cur;
+    bool n_valid = false;
+    int n_hh = 0, n_slot = 0, n_rl = 0, n_p = 0;
+    const u16* n_q = qptr;
     bf16x8 qn[8];
     if (more) {
-      nxt = row_of(pass + 1);
-      load_q(nxt, qn);
+      row_of(pass + 1, n_valid, n_hh, n_slot, n_rl, n_p, n_q);
+      load_q(n_q, qn);
     }
 
     // causal mask: only the local block of a row has keys after the row
@@ -500,15 +539,18 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
                            : mfma32(as_bf16x8(va[dt][0]), as_bf16x8(pb[0]), oacc[dt]);
         oacc[dt] = mfma32(as_bf16x8(va[dt][1]), as_bf16x8(pb[1]), oacc[dt]);
       }
-      sched_fence();
     }
     l += __shfl_xor(l, 32);
     // Unnormalised partial O (bf16) and its (log2-domain max, sum).  Each row's
     // 64 values sit in two lanes in MFMA order; the tile goes through this
     // wave's LDS area, half the columns at a time, so that every global store
     // writes whole 128-byte row segments.
-    const int prow = valid ? ((rl * a.G + g) * a.k + slot) * HG + hh : -1;
-    if (valid && half == 0) a.lpart[prow] = make_float2(mc, l);
+    // Rows past the chunk's end write to the buffer's sink row; stores are
+    // unconditional so that no branch hides them from the wait counting.
+    const int prow =
+        valid ? (((rl - a.rl_base) * a.pgroups + (a.pgroups > 1 ? g : 0)) * a.k + slot) * HG + hh
+              : a.sink;
+    a.lpart[prow] = make_float2(mc, l);  // both half-waves hold the same values
     unsigned char* st = ostage[wave];
 #pragma unroll
     for (int hpart = 0; hpart < 2; ++hpart) {
@@ -532,16 +574,19 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
         const int row = (lane >> 3) + 8 * i, seg = lane & 7;
         const int dst_row = __shfl(prow, row);
         const uint4 v = *reinterpret_cast<const uint4*>(&st[row * 128 + ((seg ^ (row & 7)) << 4)]);
-        if (dst_row >= 0)
-          *reinterpret_cast<uint4*>(a.opart + static_cast<int64_t>(dst_row) * kHeadDim +
-                                    hpart * 64 + seg * 8) = v;
+        *reinterpret_cast<uint4*>(a.opart + static_cast<int64_t>(dst_row) * kHeadDim +
+                                  hpart * 64 + seg * 8) = v;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (more) {
-      cur = nxt;
+      valid = n_valid;
+      hh = n_hh;
+      slot = n_slot;
+      rl = n_rl;
+      p = n_p;
 #pragma unroll
       for (int s = 0; s < 8; ++s) qf[s] = qn[s];
     }
@@ -560,8 +605,12 @@ struct CombArgs {
   const float2* lpart;
   u16* O;
   float* lse;
-  int64_t T, r0, W;
+  int64_t T, r0;     // r0: global row of window row 0
+  int64_t rows;      // rows combined by this launch (window rows rl_base ..)
   int32_t Hq, G, k;
+  int32_t rl_base;
+  int32_t group;     // the stage's group, or -1: every group (decode)
+  int32_t pgroups;   // groups held by the partial buffer
 };
 
 template <int HG>
@@ -569,18 +618,19 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
   constexpr int LPH = 64 / HG;          // lanes per head
   constexpr int VPL = kHeadDim / LPH;   // values per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t rg = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  if (rg >= a.W * a.G) return;
-  const int64_t rl = rg / a.G;
-  const int g = static_cast<int>(rg % a.G);
-  const int64_t grow = a.r0 + rl;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const int gper = a.group >= 0 ? 1 : a.G;
+  if (wid >= a.rows * gper) return;
+  const int64_t rl = wid / gper;  // row inside this launch's partial buffer
+  const int g = a.group >= 0 ? a.group : static_cast<int>(wid % gper);
+  const int64_t grow = a.r0 + a.rl_base + rl;
   const int64_t b = grow / a.T, t = grow % a.T;
   const int32_t* ir = a.idx + ((b * a.G + g) * a.T + t) * a.k;
   const bool sv = lane < a.k && ir[lane < a.k ? lane : 0] >= 0;
   const int nval = __popcll(__ballot(sv));
   const int hh = lane / LPH;
   const int d0 = (lane % LPH) * VPL;
-  const int64_t pbase = (rl * a.G + g) * a.k;
+  const int64_t pbase = (rl * a.pgroups + (a.pgroups > 1 ? g : 0)) * a.k;
 
   // All 16 slots are loaded at once (slots past nval re-read slot 0 and get
   // weight 0) so that every lane has its whole row in flight.
@@ -661,9 +711,9 @@ static hipError_t launch_kv_combine(const AttnArgs& aa, const CombArgs& ca, int6
                      aa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t cgrid = (ca.W * ca.G + 3) / 4;
-  hipLaunchKernelGGL((combine_kernel<HG>), dim3(static_cast<unsigned>(cgrid)), dim3(256), 0, st,
-                     ca);
+  const int64_t waves = ca.rows * (ca.group >= 0 ? 1 : ca.G);
+  hipLaunchKernelGGL((combine_kernel<HG>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256),
+                     0, st, ca);
   return hipGetLastError();
 }
 
@@ -683,44 +733,12 @@ static unsigned blocks_for(int64_t n, int per) {
   return static_cast<unsigned>((n + per - 1) / per);
 }
 
-static AttnArgs attn_args(const void* q, const void* K, const void* V, const AttnWorkspace& w,
-                          int64_t T, int64_t N, int64_t r0, int Hq, int G, int32_t NB, int k) {
-  AttnArgs aa;
-  aa.q = static_cast<const u16*>(q);
-  aa.K = static_cast<const u16*>(K);
-  aa.V = static_cast<const u16*>(V);
-  aa.chunks = w.chunks;
-  aa.entries = w.entries;
-  aa.totals = w.totals;
-  aa.opart = w.opart;
-  aa.lpart = w.lpart;
-  aa.T = T;
-  aa.N = N;
-  aa.r0 = r0;
-  aa.Hq = Hq;
-  aa.G = G;
-  aa.NB = NB;
-  aa.k = k;
-  return aa;
-}
-
-static CombArgs comb_args(const int32_t* idx, void* O, float* lse, const AttnWorkspace& w,
-                          int64_t T, int64_t r0, int64_t W, int Hq, int G, int k) {
-  CombArgs ca;
-  ca.idx = idx;
-  ca.opart = w.opart;
-  ca.lpart = w.lpart;
-  ca.O = static_cast<u16*>(O);
-  ca.lse = lse;
-  ca.T = T;
-  ca.r0 = r0;
-  ca.W = W;
-  ca.Hq = Hq;
-  ca.G = G;
-  ca.k = k;
-  return ca;
-}
-
+// Prefill: for every sequence and every window of its rows, one inversion
+// (unit histograms, scan, scatter, stage chunk lists); then the stages in
+// group-major order.  A stage is one group and stage_rows consecutive rows:
+// its KV-outer launch writes the stage's partials (a buffer small enough to
+// stay in the last-level cache next to the group's K/V) and the combine
+// launch right after reads them back.
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse, int64_t B,
                                int64_t T, int64_t N, int Hq, int G, int k,
@@ -746,7 +764,12 @@ hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
       ia.nc = static_cast<int32_t>((W + w.rq - 1) / w.rq);
       const int64_t nhist = static_cast<int64_t>(G) * NB * ia.nc;
       const int64_t ntiles = (nhist + kScanTile - 1) / kScanTile;
+      const int32_t S = static_cast<int32_t>((W + w.stage_rows - 1) / w.stage_rows);
+      const int32_t U = static_cast<int32_t>(w.stage_rows / w.rq);
+      const int64_t nst = static_cast<int64_t>(G) * S;
       const dim3 ugrid(static_cast<unsigned>(ia.nc), static_cast<unsigned>(G));
+      hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks_for(nst, 256)), dim3(256), 0, st,
+                         w.totals + 4, nst, 0);
       hipLaunchKernelGGL(hist_kernel, ugrid, dim3(256), lds, st, ia);
       hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, st,
                          w.hist, nhist, w.tile_sums);
@@ -755,17 +778,56 @@ hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
       hipLaunchKernelGGL(scan_apply_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, st,
                          w.hist, nhist, w.tile_sums);
       hipLaunchKernelGGL(scatter_kernel, ugrid, dim3(256), lds, st, ia);
-      hipLaunchKernelGGL(chunk_kernel, dim3(blocks_for(static_cast<int64_t>(G) * NB, 256)),
-                         dim3(256), 0, st, w.hist, w.totals, w.chunks, G * NB, ia.nc,
-                         static_cast<int32_t>(b * G * NB));
+      const int64_t per_stage = ((NB + 63) / 64) * 64;
+      hipLaunchKernelGGL(stage_chunk_kernel, dim3(blocks_for(nst * per_stage, 256)), dim3(256), 0,
+                         st, w.hist, w.totals, w.chunks, NB, static_cast<int64_t>(G) * NB, ia.nc,
+                         U, S, w.max_chunks, static_cast<int32_t>(b * G * NB));
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t r0 = b * T + t0;
-      const AttnArgs aa = attn_args(q, K, V, w, T, N, r0, Hq, G, NB, k);
-      const CombArgs ca = comb_args(idx, O, lse, w, T, r0, W, Hq, G, k);
-      const int64_t grid = max_chunks_for(W, w.nbins, G, k, false);
-      e = dispatch_hg(hg, aa, ca, grid, st);
-      if (e != hipSuccess) return e;
+      for (int g = 0; g < G; ++g) {
+        for (int32_t sub = 0; sub < S; ++sub) {
+          const int64_t si = static_cast<int64_t>(g) * S + sub;
+          const int32_t rl_base = sub * static_cast<int32_t>(w.stage_rows);
+          const int64_t rows = (W - rl_base) < w.stage_rows ? (W - rl_base) : w.stage_rows;
+          AttnArgs aa;
+          aa.q = static_cast<const u16*>(q);
+          aa.K = static_cast<const u16*>(K);
+          aa.V = static_cast<const u16*>(V);
+          aa.chunks = w.chunks + si * w.max_chunks;
+          aa.entries = w.entries;
+          aa.count = w.totals + 4 + si;
+          aa.opart = w.opart;
+          aa.lpart = w.lpart;
+          aa.T = T;
+          aa.N = N;
+          aa.r0 = r0;
+          aa.Hq = Hq;
+          aa.G = G;
+          aa.NB = NB;
+          aa.k = k;
+          aa.rl_base = rl_base;
+          aa.pgroups = 1;
+          aa.sink = static_cast<int32_t>(w.sink);
+          CombArgs ca;
+          ca.idx = idx;
+          ca.opart = w.opart;
+          ca.lpart = w.lpart;
+          ca.O = static_cast<u16*>(O);
+          ca.lse = lse;
+          ca.T = T;
+          ca.r0 = r0;
+          ca.rows = rows;
+          ca.Hq = Hq;
+          ca.G = G;
+          ca.k = k;
+          ca.rl_base = rl_base;
+          ca.group = g;
+          ca.pgroups = 1;
+          e = dispatch_hg(hg, aa, ca, w.max_chunks, st);
+          if (e != hipSuccess) return e;
+        }
+      }
     }
   }
   return hipSuccess;
@@ -779,8 +841,40 @@ hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
   const int64_t n = B * G * k;
   hipLaunchKernelGGL(decode_work_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, idx,
                      w.chunks, w.entries, w.totals, B, G, k, NB);
-  const AttnArgs aa = attn_args(q, K, V, w, 1, N, 0, Hq, G, NB, k);
-  const CombArgs ca = comb_args(idx, O, lse, w, 1, 0, B, Hq, G, k);
+  AttnArgs aa;
+  aa.q = static_cast<const u16*>(q);
+  aa.K = static_cast<const u16*>(K);
+  aa.V = static_cast<const u16*>(V);
+  aa.chunks = w.chunks;
+  aa.entries = w.entries;
+  aa.count = w.totals + 1;
+  aa.opart = w.opart;
+  aa.lpart = w.lpart;
+  aa.T = 1;
+  aa.N = N;
+  aa.r0 = 0;
+  aa.Hq = Hq;
+  aa.G = G;
+  aa.NB = NB;
+  aa.k = k;
+  aa.rl_base = 0;
+  aa.pgroups = G;
+  aa.sink = static_cast<int32_t>(w.sink);
+  CombArgs ca;
+  ca.idx = idx;
+  ca.opart = w.opart;
+  ca.lpart = w.lpart;
+  ca.O = static_cast<u16*>(O);
+  ca.lse = lse;
+  ca.T = 1;
+  ca.r0 = 0;
+  ca.rows = B;
+  ca.Hq = Hq;
+  ca.G = G;
+  ca.k = k;
+  ca.rl_base = 0;
+  ca.group = -1;
+  ca.pgroups = G;
   return dispatch_hg(hg, aa, ca, n, st);
 }
 

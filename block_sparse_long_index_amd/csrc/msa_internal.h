@@ -22,23 +22,28 @@ hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
 struct AttnWorkspace {
   int32_t* hist;       // [G * NB * nc]: unit block counts, then exclusive offsets
   int32_t* tile_sums;  // [ntiles]
-  int32_t* totals;     // [4]: entries, chunks
-  int32_t* entries;    // [W * G * k]
-  int4* chunks;        // [max_chunks]
-  uint16_t* opart;     // [W, G, k, hg, 128] bf16, unnormalised
-  float2* lpart;       // [W, G, k, hg]: (log2-domain row max, row sum)
-  int64_t window;      // query rows per window
-  int64_t max_chunks;
+  int32_t* totals;     // [4 + nstages]: entries, decode chunks, -, -, chunks per stage
+  int32_t* entries;    // [window * G * k]
+  int4* chunks;        // [nstages][max_chunks]
+  uint16_t* opart;     // one stage's partial O: [stage_rows, k, hg, 128] bf16, unnormalised
+  float2* lpart;       // [stage_rows, k, hg]: (log2-domain row max, row sum)
+  int64_t window;      // query rows of one sequence per inversion
+  int64_t stage_rows;  // rows of one group per KV-outer stage
+  int64_t max_chunks;  // per stage
+  int64_t nstages;
   int64_t nbins;       // G * NB
   int64_t nhist, ntiles;
   int32_t rq, nc;      // rows per histogram unit, units per full window
+  int64_t sink;        // index of the spare partial row
 };
 
-// Bytes of workspace for a window of `window` query rows of one sequence.
-// decode: one chunk per (sequence, group, slot) instead of the inverted lists.
-size_t attn_workspace_bytes(int64_t window, int64_t N, int G, int hg, int k, bool decode);
-void attn_workspace_carve(void* ws, int64_t window, int64_t N, int G, int hg, int k,
-                          bool decode, AttnWorkspace* out);
+// Bytes of workspace for a window of `window` rows of one sequence processed
+// in stages of `stage_rows` rows of one group.  decode: one chunk per
+// (sequence, group, slot), window = B.
+size_t attn_workspace_bytes(int64_t window, int64_t stage_rows, int64_t N, int G, int hg, int k,
+                            bool decode);
+void attn_workspace_carve(void* ws, int64_t window, int64_t stage_rows, int64_t N, int G, int hg,
+                          int k, bool decode, AttnWorkspace* out);
 
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse,

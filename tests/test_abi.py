@@ -106,14 +106,14 @@ def test_workspace_checks():
     assert L.msa_workspace_bytes(99, ctypes.byref(d)) == 0
 
 
-def test_workspace_scales_with_window():
-    """The prefill workspace is bounded by the query window, not by T."""
+def test_workspace_is_bounded():
+    """The prefill partials are held for one stage (rows of one group), not
+    for all queries: at 1M tokens the whole workspace stays near a GB while
+    the all-query partials would be ~280 GB."""
     L = ops.lib()
-    small = L.msa_workspace_bytes(ops.OP_ATTN_PREFILL,
-                                  ctypes.byref(_good(T=16384, N=16384, Hq=64, G=8, k=16)))
     big = L.msa_workspace_bytes(ops.OP_ATTN_PREFILL,
                                 ctypes.byref(_good(T=1 << 20, N=1 << 20, Hq=64, G=8, k=16)))
-    assert big < 2 * small
+    assert 0 < big < 2 * 2**30, big
 
 
 def test_status_strings():
