@@ -83,3 +83,15 @@ def test_workload_totals():
     w0 = WORKLOADS["prefill_2k"]
     assert acc.support_tokens(w0.N, w0.T, w0.Bk, w0.k) == 820224
     assert np.isclose(acc.prefill_flops(w0)["index"], 1.074e9, rtol=1e-3)
+
+
+def test_fp32_score_rounding_identity():
+    """The kernels report S as fp32(fp64(dot) * fp64(1/sqrt(128))) with the
+    dot accumulated exactly; the oracle reports dot / sqrt(128) in fp64 and
+    the tests round it to fp32.  For every integer dot an index score can
+    take (|dot| <= 128 * 16) the two roundings agree bit for bit."""
+    inv = np.float64(0.088388347648318440550)  # the constant the kernels use
+    d = np.arange(-2048, 2049, dtype=np.float64)
+    kernel = (d * inv).astype(np.float32)
+    oracle_side = (d / np.sqrt(np.float64(128.0))).astype(np.float32)
+    assert np.array_equal(kernel.view(np.uint32), oracle_side.view(np.uint32))
