@@ -285,27 +285,6 @@ __global__ void __launch_bounds__(256) stage_chunk_kernel(const int32_t* off, in
   }
 }
 
-// Decode needs no inversion: every (sequence, group, slot) is its own chunk
-// with one entry.  The window is the B decode rows.
-__global__ void decode_work_kernel(const int32_t* idx, int4* chunks, int32_t* entries,
-                                   int32_t* totals, int64_t B, int32_t G, int32_t k,
-                                   int32_t NB) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t n = B * G * k;
-  if (i == 0) {
-    totals[0] = static_cast<int32_t>(n);
-    totals[1] = static_cast<int32_t>(n);
-  }
-  if (i >= n) return;
-  const int32_t s = static_cast<int32_t>(i % k);
-  const int64_t bg = i / k;
-  const int64_t b = bg / G;
-  const int32_t blk = idx[bg * k + s];
-  entries[i] = static_cast<int32_t>(b * k + s);
-  chunks[i] = make_int4(static_cast<int32_t>(bg * NB + (blk < 0 ? 0 : blk)),
-                        static_cast<int32_t>(i), blk < 0 ? 0 : 1, 0);
-}
-
 // ---------------------------------------------------------------------------
 // KV-outer attention.  One workgroup per chunk (b, g, block, <= 64 queries):
 // the block's K (row-major) and V (transposed) go to LDS once and every
@@ -833,33 +812,187 @@ hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Decode attention: one wave per (sequence, group, slot).  With one query per
+// sequence there is nothing to gather, so K is read straight from HBM as the
+// A operand of 16x16x32 MFMAs (16 keys x the hg heads of the group, padded to
+// 16 columns); V goes through 32 KB of LDS, transposed, for O^T = V^T P^T.
+// Inside each 32-key k-step the keys sit in the order the P fragments reach
+// the MFMA's k slots (lane quarter qd holds keys 4qd..4qd+3 of both 16-key
+// tiles), so every A fragment is one 16-B LDS read.  Writes the slot's
+// unnormalised partial O and (log2-domain max, sum) for the combine.
+// ---------------------------------------------------------------------------
+struct DecArgs {
+  const u16* q;        // [B, Hq, 128]
+  const u16* K;        // [B, G, N, 128]
+  const u16* V;
+  const int32_t* idx;  // [B, G, 1, k]
+  u16* opart;          // [B, G, k, hg, 128]
+  float2* lpart;       // [B, G, k, hg]
+  int64_t N;
+  int32_t Hq, G, k;
+};
+
+__device__ __forceinline__ int dec_pos(int key) {  // key offset 0..127 -> V^T column
+  return (key & ~31) + 8 * ((key & 15) >> 2) + 4 * ((key & 31) >> 4) + (key & 3);
+}
+
+template <int HG>
+__global__ void __launch_bounds__(64, 2) decode_attn_kernel(DecArgs a) {
+  __shared__ __align__(16) unsigned char vt[32768];
+  const int64_t item = blockIdx.x;  // (b * G + g) * k + slot
+  const int slot = static_cast<int>(item % a.k);
+  const int64_t bg = item / a.k;
+  const int g = static_cast<int>(bg % a.G);
+  const int64_t b = bg / a.G;
+  const int blk = a.idx[bg * a.k + slot];
+  if (blk < 0 || static_cast<int64_t>(blk) * kBlock >= a.N) return;  // unused slot
+  const int lane = threadIdx.x;
+  const int col = lane & 15, qd = lane >> 4;
+  const int64_t key0 = static_cast<int64_t>(blk) * kBlock;
+  const int nvalid = static_cast<int>(a.N - key0 < kBlock ? a.N - key0 : kBlock);
+  const u16* Kb = a.K + (bg * a.N + key0) * kHeadDim;
+  const u16* Vb = a.V + (bg * a.N + key0) * kHeadDim;
+
+  // V -> LDS (transposed, permuted, chunk-swizzled), two halves of 8 tasks;
+  // a task is a key pair x 8 consecutive d.
+  auto v_half = [&](int h) {
+    uint4 v0[8], v1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tsk = lane + 64 * (8 * h + j);  // 0..1023
+      const int kp = tsk & 63, c = tsk >> 6;
+      const int k0 = 2 * kp;
+      v0[j] = ld16(Vb + (k0 < nvalid ? k0 : nvalid - 1) * kHeadDim + c * 8);
+      v1[j] = ld16(Vb + (k0 + 1 < nvalid ? k0 + 1 : nvalid - 1) * kHeadDim + c * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tsk = lane + 64 * (8 * h + j);
+      const int kp = tsk & 63, c = tsk >> 6;
+      const int k0 = 2 * kp;
+      const int P = dec_pos(k0);  // even; key k0 + 1 lands at P + 1
+      const uint32_t w0[4] = {v0[j].x, v0[j].y, v0[j].z, v0[j].w};
+      const uint32_t w1[4] = {v1[j].x, v1[j].y, v1[j].z, v1[j].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = k0 < nvalid ? (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu : 0u;
+        const uint32_t hi = k0 + 1 < nvalid ? (w1[e >> 1] >> (16 * (e & 1))) & 0xffffu : 0u;
+        const int d = 8 * c + e;
+        *reinterpret_cast<uint32_t*>(&vt[swz(d, P >> 3) + ((2 * P) & 15)]) = lo | (hi << 16);
+      }
+    }
+  };
+  v_half(0);
+
+  // K fragments (A operand): tile t = keys 16t..16t+15, k-step s = d 32s..32s+31
+  uint4 kf[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int key = 16 * t + col;
+    const u16* kr = Kb + (key < nvalid ? key : nvalid - 1) * kHeadDim + 8 * qd;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kf[t][s] = ld16(kr + 32 * s);
+  }
+  const u16* qr = a.q + (b * a.Hq + g * HG + (col < HG ? col : 0)) * kHeadDim + 8 * qd;
+  bf16x8 qf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint4 v = ld16(qr + 32 * s);
+    qf[s] = as_bf16x8(col < HG ? v : make_uint4(0, 0, 0, 0));
+  }
+  v_half(1);
+
+  // S^T tiles: lane holds head `col`, keys 16t + 4qd + r
+  f32x4 sc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    sc[t] = mfma16(as_bf16x8(kf[t][0]), qf[0], f32x4{});
+#pragma unroll
+    for (int s = 1; s < 4; ++s) sc[t] = mfma16(as_bf16x8(kf[t][s]), qf[s], sc[t]);
+  }
+  constexpr float qscale = 1.4426950408889634f * 0.08838834764831845f;
+  float m = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (16 * t + 4 * qd + r >= nvalid) sc[t][r] = -INFINITY;
+      m = fmaxf(m, sc[t][r]);
+    }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float mc = m * qscale;
+  float l = 0.f;
+  uint4 pf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float pv[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pv[r] = fast_exp2(fmaf(sc[2 * s][r], qscale, -mc));
+      pv[4 + r] = fast_exp2(fmaf(sc[2 * s + 1][r], qscale, -mc));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) l += pv[e];
+    pf[s] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                       pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+  }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // O^T tiles: lane holds head `col`, d = 16dt + 4qd + r
+  const int64_t prow = (bg * a.k + slot) * HG + col;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int d = 16 * dt + col;
+    f32x4 o = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 av = *reinterpret_cast<const uint4*>(&vt[swz(d, 4 * s + qd)]);
+      o = mfma16(as_bf16x8(av), as_bf16x8(pf[s]), o);
+    }
+    if (col < HG) {
+      uint2 w;
+      w.x = pack_bf16x2(o[0], o[1]);
+      w.y = pack_bf16x2(o[2], o[3]);
+      *reinterpret_cast<uint2*>(a.opart + prow * kHeadDim + 16 * dt + 4 * qd) = w;
+    }
+  }
+  if (col < HG && qd == 0) a.lpart[prow] = make_float2(mc, l);
+}
+
+template <int HG>
+static hipError_t launch_decode_t(const DecArgs& da, const CombArgs& ca, int64_t n,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL((decode_attn_kernel<HG>), dim3(static_cast<unsigned>(n)), dim3(64), 0, st,
+                     da);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t waves = ca.rows * ca.G;
+  hipLaunchKernelGGL((combine_kernel<HG>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256),
+                     0, st, ca);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse, int64_t B, int64_t N,
                               int Hq, int G, int k, const AttnWorkspace& w, hipStream_t st) {
   const int hg = Hq / G;
-  const int32_t NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
-  const int64_t n = B * G * k;
-  hipLaunchKernelGGL(decode_work_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, st, idx,
-                     w.chunks, w.entries, w.totals, B, G, k, NB);
-  AttnArgs aa;
-  aa.q = static_cast<const u16*>(q);
-  aa.K = static_cast<const u16*>(K);
-  aa.V = static_cast<const u16*>(V);
-  aa.chunks = w.chunks;
-  aa.entries = w.entries;
-  aa.count = w.totals + 1;
-  aa.opart = w.opart;
-  aa.lpart = w.lpart;
-  aa.T = 1;
-  aa.N = N;
-  aa.r0 = 0;
-  aa.Hq = Hq;
-  aa.G = G;
-  aa.NB = NB;
-  aa.k = k;
-  aa.rl_base = 0;
-  aa.pgroups = G;
-  aa.sink = static_cast<int32_t>(w.sink);
+  DecArgs da;
+  da.q = static_cast<const u16*>(q);
+  da.K = static_cast<const u16*>(K);
+  da.V = static_cast<const u16*>(V);
+  da.idx = idx;
+  da.opart = w.opart;
+  da.lpart = w.lpart;
+  da.N = N;
+  da.Hq = Hq;
+  da.G = G;
+  da.k = k;
   CombArgs ca;
   ca.idx = idx;
   ca.opart = w.opart;
@@ -875,7 +1008,15 @@ hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
   ca.rl_base = 0;
   ca.group = -1;
   ca.pgroups = G;
-  return dispatch_hg(hg, aa, ca, n, st);
+  const int64_t n = B * G * k;
+  switch (hg) {
+    case 8: return launch_decode_t<8>(da, ca, n, st);
+    case 4: return launch_decode_t<4>(da, ca, n, st);
+    case 16: return launch_decode_t<16>(da, ca, n, st);
+    case 2: return launch_decode_t<2>(da, ca, n, st);
+    case 1: return launch_decode_t<1>(da, ca, n, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace msa

@@ -496,6 +496,80 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0));
 }
 
+// Best m candidates (score desc, index asc) among src[e] for e = e0 + lane +
+// step*i < n, left best-first in lanes 0..m-1 (m <= 15).  cv/ci: this wave's
+// 64-entry LDS scratch.
+__device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int step, int m,
+                                          int lane, float* cv, int* ci, float& v, int& vi) {
+  float lm = -INFINITY;
+  for (int e = e0 + lane; e < n; e += step) lm = fmaxf(lm, src[e]);
+  const float tau = __shfl(sort_desc_values64(lm, lane), m - 1);
+  int cnt = 0;
+  for (int e = e0 + lane; e < n; e += step) cnt += src[e] >= tau ? 1 : 0;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) cnt += __shfl_xor(cnt, s);
+  v = -INFINITY;
+  vi = INT_MAX;
+  if (cnt <= 64) {
+    int base = 0;
+    for (int c0 = e0; c0 < n; c0 += step) {
+      const int e = c0 + lane;
+      const float x = e < n ? src[e] : -INFINITY;
+      const bool f = (e < n) && (x >= tau);
+      const unsigned long long bal = __ballot(f);
+      if (f) {
+        const int pos = base + lanes_below(bal);
+        cv[pos] = x;
+        ci[pos] = e;
+      }
+      base += __popcll(bal);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < cnt) {
+      v = cv[lane];
+      vi = ci[lane];
+    }
+    bitonic64(v, vi, lane, true);
+  } else {
+    // many equal scores at the threshold: merge 64 candidates at a time into
+    // a running best-64 list
+    for (int c0 = e0; c0 < n; c0 += step) {
+      const int e = c0 + lane;
+      const float x = e < n ? src[e] : -INFINITY;
+      const bool f = (e < n) && (x >= tau);
+      if (!__ballot(f)) continue;
+      float cvv = f ? x : -INFINITY;
+      int cii = f ? e : INT_MAX;
+      bitonic64(cvv, cii, lane, false);
+      if (beats(cvv, cii, v, vi)) {
+        v = cvv;
+        vi = cii;
+      }
+      bitonic_merge64(v, vi, lane);
+    }
+  }
+}
+
+// Lanes 0..m-1 hold block ids; write them ascending, then the local block L,
+// then -1 padding.
+__device__ __forceinline__ void write_selection(int32_t* out, int vi, int m, int L, int k,
+                                                int lane) {
+  int key = lane < m ? vi : INT_MAX;
+#pragma unroll
+  for (int size = 2; size <= 16; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int pk = __shfl_xor(key, stride);
+      const bool lower = (lane & stride) == 0;
+      const bool asc = (lane & size) == 0 || size == 16;
+      const bool take = (lower == asc) ? (pk < key) : (pk > key);
+      key = take ? pk : key;
+    }
+  }
+  if (lane < k) out[lane] = lane < m ? key : (lane == m ? L : -1);
+}
+
 __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
   __shared__ float cv[4][64];
   __shared__ int ci[4][64];
@@ -510,71 +584,44 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
     if (lane < a.k) out[lane] = lane == 0 ? static_cast<int>(L) : -1;
     return;
   }
-  const float* src = a.S + row * a.NB;
-  const int n = static_cast<int>(L);
+  float v;
+  int vi;
+  wave_topk(a.S + row * a.NB, static_cast<int>(L), 0, 64, m, lane, cv[wave], ci[wave], v, vi);
+  write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
+}
 
-  float lm = -INFINITY;
-  for (int e = lane; e < n; e += 64) lm = fmaxf(lm, src[e]);
-  const float tau = __shfl(sort_desc_values64(lm, lane), m - 1);
-
-  int cnt = 0;
-  for (int e = lane; e < n; e += 64) cnt += src[e] >= tau ? 1 : 0;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) cnt += __shfl_xor(cnt, s);
-
-  float v = -INFINITY;
-  int vi = INT_MAX;
-  if (cnt <= 64) {
-    int base = 0;
-    for (int e0 = 0; e0 < n; e0 += 64) {
-      const int e = e0 + lane;
-      const float x = e < n ? src[e] : -INFINITY;
-      const bool f = (e < n) && (x >= tau);
-      const unsigned long long bal = __ballot(f);
-      if (f) {
-        const int pos = base + lanes_below(bal);
-        cv[wave][pos] = x;
-        ci[wave][pos] = e;
-      }
-      base += __popcll(bal);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (lane < cnt) {
-      v = cv[wave][lane];
-      vi = ci[wave][lane];
-    }
-    bitonic64(v, vi, lane, true);
-  } else {
-    for (int e0 = 0; e0 < n; e0 += 64) {
-      const int e = e0 + lane;
-      const float x = e < n ? src[e] : -INFINITY;
-      const bool f = (e < n) && (x >= tau);
-      if (!__ballot(f)) continue;
-      float cvv = f ? x : -INFINITY;
-      int cii = f ? e : INT_MAX;
-      bitonic64(cvv, cii, lane, false);
-      if (beats(cvv, cii, v, vi)) {
-        v = cvv;
-        vi = cii;
-      }
-      bitonic_merge64(v, vi, lane);
-    }
+// Long rows, few of them (decode): four waves per row, each takes every
+// fourth 64-candidate chunk; the four best-m lists meet in LDS and one wave
+// sorts the 64 entries and writes the selection.
+__global__ void __launch_bounds__(256) topk_wide_kernel(TopkArgs a) {
+  __shared__ float cv[4][64];
+  __shared__ int ci[4][64];
+  __shared__ float mv[64];
+  __shared__ int mi[64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  const int64_t t = row % a.T;
+  const int64_t L = (a.N - a.T + t) / kBlock;
+  const int m = static_cast<int>(L < a.k - 1 ? L : a.k - 1);
+  int32_t* out = a.idx + row * a.k;
+  if (m == 0) {
+    if (wave == 0 && lane < a.k) out[lane] = lane == 0 ? static_cast<int>(L) : -1;
+    return;
   }
-  // best m are in lanes 0..m-1; order them by block index on lanes 0..15
-  int key = lane < m ? vi : INT_MAX;
-#pragma unroll
-  for (int size = 2; size <= 16; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int pk = __shfl_xor(key, stride);
-      const bool lower = (lane & stride) == 0;
-      const bool asc = (lane & size) == 0 || size == 16;
-      const bool take = (lower == asc) ? (pk < key) : (pk > key);
-      key = take ? pk : key;
-    }
+  float v;
+  int vi;
+  wave_topk(a.S + row * a.NB, static_cast<int>(L), 64 * wave, 256, m, lane, cv[wave], ci[wave],
+            v, vi);
+  if (lane < 16) {
+    mv[wave * 16 + lane] = lane < m ? v : -INFINITY;
+    mi[wave * 16 + lane] = lane < m ? vi : INT_MAX;
   }
-  if (lane < a.k) out[lane] = lane < m ? key : (lane == m ? static_cast<int>(L) : -1);
+  __syncthreads();
+  if (wave != 0) return;
+  v = mv[lane];
+  vi = mi[lane];
+  bitonic64(v, vi, lane, true);
+  write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
 }
 
 hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
@@ -587,8 +634,13 @@ hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
   a.rows = B * G * T;
   a.NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
   a.k = k;
-  const int64_t grid = (a.rows + 3) / 4;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a);
+  if (a.rows <= 4096 && a.NB >= 1024) {
+    // few long rows: spread each row over a workgroup
+    hipLaunchKernelGGL(topk_wide_kernel, dim3(static_cast<unsigned>(a.rows)), dim3(256), 0, st, a);
+  } else {
+    const int64_t grid = (a.rows + 3) / 4;
+    hipLaunchKernelGGL(topk_rows_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

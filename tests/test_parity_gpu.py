@@ -208,6 +208,25 @@ def test_topk_random_scores():
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("scale", [3.0, 0.0])
+def test_topk_wide_rows(scale):
+    """Few long rows (the decode shape) take the four-waves-per-row top-k:
+    rounded normals (frequent ties) and all-equal rows (every candidate
+    survives the threshold)."""
+    B, G, T, N, k = 3, 8, 1, 200000, 16
+    NB = (N + 127) // 128
+    g = torch.Generator(device="cuda").manual_seed(5)
+    S = torch.round(torch.randn(B, G, T, NB, device="cuda", generator=g) * scale)
+    idx = ops.select_blocks_from_scores(S, k, N)
+    torch.cuda.synchronize()
+    d = oracle.dims_of(B, T, N, G, G, 128, 128, 128, k)
+    for b in range(B):
+        ref = oracle.select(d, np.zeros(1, dtype=np.int64),
+                            S[b].permute(1, 0, 2).double().cpu().numpy())
+        got = idx[b].permute(1, 0, 2).cpu().numpy()
+        assert np.array_equal(got, ref), b
+
+
 def test_determinism():
     w = WORKLOADS["prefill_2k"].replace(T=3000, N=3000, Hq=64, G=8, k=16)
     inp = make_inputs(w, device="cuda")
