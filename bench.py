@@ -157,7 +157,10 @@ def decode_leg(args):
                        device="cuda")
     ws_a = torch.empty(ops.workspace_bytes(ops.OP_ATTN_DECODE, d), dtype=torch.uint8,
                        device="cuda")
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # a 1 GiB read evicts the 256 MB last-level cache and leaves it clean (a
+    # write flush would leave dirty lines whose write-back lands in the step)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def step():
         ops.select_blocks(qI, kI, w.k, out=idx, workspace=ws_s)
@@ -167,7 +170,7 @@ def decode_leg(args):
         step()
     times = []
     for _ in range(args.decode_reps):
-        flush.zero_()  # evict the 256 MB last-level cache between steps
+        torch.sum(flush, dim=0, out=sink)
         a, b = ev(), ev()
         a.record()
         step()

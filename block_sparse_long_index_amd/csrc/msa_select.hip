@@ -345,8 +345,9 @@ hipError_t launch_index_tiles(bool write_scores, const void* qI, const void* kI,
 }
 
 // ---------------------------------------------------------------------------
-// Decode scan (T == 1): stream the index-key cache once.  A workgroup takes 16
-// consecutive blocks of one sequence, each wave 4 of them.  16x16x32 MFMA with
+// Decode scan (T == 1): stream the index-key cache once.  A workgroup takes 4
+// consecutive blocks of one sequence, one per wave (many short waves keep
+// more loads in flight across the chip than fewer long ones).  16x16x32 MFMA with
 // 16 keys on M and the G index queries on N (unused columns are zero).  The
 // 32 16-B loads of a block are all issued before its MFMAs so that each wave
 // keeps 32 KB in flight.  k-step s covers d = 32*s .. 32*s+31 with lane
@@ -373,10 +374,9 @@ __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
     qf[s] = as_bf16x8(v);
   }
   const u16* kbase = a.kI + static_cast<int64_t>(b) * a.N * kHeadDim;
-  const int64_t blk0 = static_cast<int64_t>(blockIdx.x) * 16 + wave * 4;
-  for (int w = 0; w < 4; ++w) {
-    const int64_t kb = blk0 + w;
-    if (kb >= a.NB) break;
+  {
+    const int64_t kb = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (kb >= a.NB) return;
     uint4 d[8][4];
 #pragma unroll
     for (int kg = 0; kg < 8; ++kg) {
@@ -414,7 +414,7 @@ hipError_t launch_decode_scan(const void* qI, const void* kI, float* S,
   a.N = N;
   a.NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
   a.G = G;
-  const dim3 grid(static_cast<unsigned>((a.NB + 15) / 16), static_cast<unsigned>(B));
+  const dim3 grid(static_cast<unsigned>((a.NB + 3) / 4), static_cast<unsigned>(B));
   hipLaunchKernelGGL(decode_scan_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -497,32 +497,63 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 }
 
 // Best m candidates (score desc, index asc) among src[e] for e = e0 + lane +
-// step*i < n, left best-first in lanes 0..m-1 (m <= 15).  cv/ci: this wave's
-// 64-entry LDS scratch.
+// step*i < n, left best-first in lanes 0..m-1 (m <= 15).  The first R strided
+// chunks are loaded once into registers, all loads in flight together; any
+// remainder is re-read from memory.  cv/ci: this wave's 64-entry LDS scratch.
+template <int R>
 __device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int step, int m,
                                           int lane, float* cv, int* ci, float& v, int& vi) {
+  float x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = e0 + lane + step * r;
+    x[r] = src[e < n ? e : n - 1];
+  }
+  const int rest = e0 + step * R;
   float lm = -INFINITY;
-  for (int e = e0 + lane; e < n; e += step) lm = fmaxf(lm, src[e]);
+#pragma unroll
+  for (int r = 0; r < R; ++r) lm = fmaxf(lm, e0 + lane + step * r < n ? x[r] : -INFINITY);
+  for (int e = rest + lane; e < n; e += step) lm = fmaxf(lm, src[e]);
   const float tau = __shfl(sort_desc_values64(lm, lane), m - 1);
   int cnt = 0;
-  for (int e = e0 + lane; e < n; e += step) cnt += src[e] >= tau ? 1 : 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) cnt += (e0 + lane + step * r < n && x[r] >= tau) ? 1 : 0;
+  for (int e = rest + lane; e < n; e += step) cnt += src[e] >= tau ? 1 : 0;
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) cnt += __shfl_xor(cnt, s);
   v = -INFINITY;
   vi = INT_MAX;
+  auto chunk = [&](int c0, float xv, int& base) {
+    const int e = c0 + lane;
+    const bool f = (e < n) && (xv >= tau);
+    const unsigned long long bal = __ballot(f);
+    if (f) {
+      const int pos = base + lanes_below(bal);
+      cv[pos] = xv;
+      ci[pos] = e;
+    }
+    base += __popcll(bal);
+  };
+  auto merge = [&](int c0, float xv) {
+    const int e = c0 + lane;
+    const bool f = (e < n) && (xv >= tau);
+    if (!__ballot(f)) return;
+    float cvv = f ? xv : -INFINITY;
+    int cii = f ? e : INT_MAX;
+    bitonic64(cvv, cii, lane, false);
+    if (beats(cvv, cii, v, vi)) {
+      v = cvv;
+      vi = cii;
+    }
+    bitonic_merge64(v, vi, lane);
+  };
   if (cnt <= 64) {
     int base = 0;
-    for (int c0 = e0; c0 < n; c0 += step) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) chunk(e0 + step * r, x[r], base);
+    for (int c0 = rest; c0 < n; c0 += step) {
       const int e = c0 + lane;
-      const float x = e < n ? src[e] : -INFINITY;
-      const bool f = (e < n) && (x >= tau);
-      const unsigned long long bal = __ballot(f);
-      if (f) {
-        const int pos = base + lanes_below(bal);
-        cv[pos] = x;
-        ci[pos] = e;
-      }
-      base += __popcll(bal);
+      chunk(c0, e < n ? src[e] : -INFINITY, base);
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -534,19 +565,11 @@ __device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int s
   } else {
     // many equal scores at the threshold: merge 64 candidates at a time into
     // a running best-64 list
-    for (int c0 = e0; c0 < n; c0 += step) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) merge(e0 + step * r, x[r]);
+    for (int c0 = rest; c0 < n; c0 += step) {
       const int e = c0 + lane;
-      const float x = e < n ? src[e] : -INFINITY;
-      const bool f = (e < n) && (x >= tau);
-      if (!__ballot(f)) continue;
-      float cvv = f ? x : -INFINITY;
-      int cii = f ? e : INT_MAX;
-      bitonic64(cvv, cii, lane, false);
-      if (beats(cvv, cii, v, vi)) {
-        v = cvv;
-        vi = cii;
-      }
-      bitonic_merge64(v, vi, lane);
+      merge(c0, e < n ? src[e] : -INFINITY);
     }
   }
 }
@@ -586,7 +609,7 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
   }
   float v;
   int vi;
-  wave_topk(a.S + row * a.NB, static_cast<int>(L), 0, 64, m, lane, cv[wave], ci[wave], v, vi);
+  wave_topk<16>(a.S + row * a.NB, static_cast<int>(L), 0, 64, m, lane, cv[wave], ci[wave], v, vi);
   write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
 }
 
@@ -610,7 +633,7 @@ __global__ void __launch_bounds__(256) topk_wide_kernel(TopkArgs a) {
   }
   float v;
   int vi;
-  wave_topk(a.S + row * a.NB, static_cast<int>(L), 64 * wave, 256, m, lane, cv[wave], ci[wave],
+  wave_topk<8>(a.S + row * a.NB, static_cast<int>(L), 64 * wave, 256, m, lane, cv[wave], ci[wave],
             v, vi);
   if (lane < 16) {
     mv[wave * 16 + lane] = lane < m ? v : -INFINITY;
