@@ -833,13 +833,28 @@ struct DecArgs {
   int32_t Hq, G, k;
 };
 
-__device__ __forceinline__ int dec_pos(int key) {  // key offset 0..127 -> V^T column
-  return (key & ~31) + 8 * ((key & 15) >> 2) + 4 * ((key & 31) >> 4) + (key & 3);
+// Key offset 0..31 within a wave's quarter -> its column in that wave's V^T
+// rows, matching the k order of the P^T operand (lane quarter qd holds keys
+// 4qd..4qd+3 of both 16-key score tiles).
+__device__ __forceinline__ int dec_pos(int key) {
+  return 8 * ((key & 15) >> 2) + 4 * (key >> 4) + (key & 3);
 }
 
+// V^T byte offset of (d, 16-byte chunk c) in a wave's 8 KB region: 64-byte
+// rows, chunk index xor-ed with (d >> 2) so that the 8 lanes of one LDS read
+// phase (consecutive d) hit distinct banks.
+__device__ __forceinline__ int dec_vt(int d, int c) { return d * 64 + ((c ^ (d >> 2)) & 3) * 16; }
+
+// One workgroup of four waves per (sequence, group, selected block); wave w
+// takes keys 32w..32w+31 of the block.  Each wave: K rows straight from HBM as
+// the A operand of 16x16x32 MFMAs (keys on M, the group's heads on N), its own
+// max / sum, V^T of its 32 keys through 8 KB of LDS, and a PV product over its
+// keys.  The four (max, sum, O) meet in LDS (log-sum-exp merge) and the
+// workgroup writes one unnormalised partial per head, like a prefill slot.
 template <int HG>
-__global__ void __launch_bounds__(64, 2) decode_attn_kernel(DecArgs a) {
-  __shared__ __align__(16) unsigned char vt[32768];
+__global__ void __launch_bounds__(256) decode_attn_kernel(DecArgs a) {
+  __shared__ __align__(16) unsigned char lds[32768];  // V^T, then the O merge
+  __shared__ float wm[4][16], wl[4][16];
   const int64_t item = blockIdx.x;  // (b * G + g) * k + slot
   const int slot = static_cast<int>(item % a.k);
   const int64_t bg = item / a.k;
@@ -847,74 +862,71 @@ __global__ void __launch_bounds__(64, 2) decode_attn_kernel(DecArgs a) {
   const int64_t b = bg / a.G;
   const int blk = a.idx[bg * a.k + slot];
   if (blk < 0 || static_cast<int64_t>(blk) * kBlock >= a.N) return;  // unused slot
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, qd = lane >> 4;
-  const int64_t key0 = static_cast<int64_t>(blk) * kBlock;
-  const int nvalid = static_cast<int>(a.N - key0 < kBlock ? a.N - key0 : kBlock);
-  const u16* Kb = a.K + (bg * a.N + key0) * kHeadDim;
-  const u16* Vb = a.V + (bg * a.N + key0) * kHeadDim;
+  const int64_t kblk = static_cast<int64_t>(blk) * kBlock;
+  // keys of the block inside the sequence (>= 1); loads clamp to the last of
+  // them, and this wave's quarter holds nvalid of them (<= 0: none)
+  const int nblk = static_cast<int>(a.N - kblk < kBlock ? a.N - kblk : kBlock);
+  const int nvalid = nblk - 32 * wave < 32 ? nblk - 32 * wave : 32;
+  const u16* Kb = a.K + (bg * a.N + kblk) * kHeadDim;
+  const u16* Vb = a.V + (bg * a.N + kblk) * kHeadDim;
+  auto krow = [&](int kk) { return (32 * wave + kk < nblk ? 32 * wave + kk : nblk - 1) * kHeadDim; };
+  unsigned char* vt = lds + wave * 8192;
 
-  // V -> LDS (transposed, permuted, chunk-swizzled), two halves of 8 tasks;
-  // a task is a key pair x 8 consecutive d.
-  auto v_half = [&](int h) {
-    uint4 v0[8], v1[8];
+  // issue every load: V (4 tasks of a key pair x 8 d), K (2 tiles x 4 k-steps), q
+  uint4 v0[4], v1[4], kf[2][4], qv[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tsk = lane + 64 * (8 * h + j);  // 0..1023
-      const int kp = tsk & 63, c = tsk >> 6;
-      const int k0 = 2 * kp;
-      v0[j] = ld16(Vb + (k0 < nvalid ? k0 : nvalid - 1) * kHeadDim + c * 8);
-      v1[j] = ld16(Vb + (k0 + 1 < nvalid ? k0 + 1 : nvalid - 1) * kHeadDim + c * 8);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int tsk = lane + 64 * j;  // 0..255
+    const int kp = tsk & 15, c = tsk >> 4;
+    const int k0 = 2 * kp;
+    v0[j] = ld16(Vb + krow(k0) + c * 8);
+    v1[j] = ld16(Vb + krow(k0 + 1) + c * 8);
+  }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tsk = lane + 64 * (8 * h + j);
-      const int kp = tsk & 63, c = tsk >> 6;
-      const int k0 = 2 * kp;
-      const int P = dec_pos(k0);  // even; key k0 + 1 lands at P + 1
-      const uint32_t w0[4] = {v0[j].x, v0[j].y, v0[j].z, v0[j].w};
-      const uint32_t w1[4] = {v1[j].x, v1[j].y, v1[j].z, v1[j].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = k0 < nvalid ? (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu : 0u;
-        const uint32_t hi = k0 + 1 < nvalid ? (w1[e >> 1] >> (16 * (e & 1))) & 0xffffu : 0u;
-        const int d = 8 * c + e;
-        *reinterpret_cast<uint32_t*>(&vt[swz(d, P >> 3) + ((2 * P) & 15)]) = lo | (hi << 16);
-      }
-    }
-  };
-  v_half(0);
-
-  // K fragments (A operand): tile t = keys 16t..16t+15, k-step s = d 32s..32s+31
-  uint4 kf[8][4];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
+  for (int t = 0; t < 2; ++t) {
     const int key = 16 * t + col;
-    const u16* kr = Kb + (key < nvalid ? key : nvalid - 1) * kHeadDim + 8 * qd;
+    const u16* kr = Kb + krow(key) + 8 * qd;
 #pragma unroll
     for (int s = 0; s < 4; ++s) kf[t][s] = ld16(kr + 32 * s);
   }
   const u16* qr = a.q + (b * a.Hq + g * HG + (col < HG ? col : 0)) * kHeadDim + 8 * qd;
-  bf16x8 qf[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint4 v = ld16(qr + 32 * s);
-    qf[s] = as_bf16x8(col < HG ? v : make_uint4(0, 0, 0, 0));
+  for (int s = 0; s < 4; ++s) qv[s] = ld16(qr + 32 * s);
+
+  // V -> V^T: key pair (k0, k0 + 1) x d = 8c..8c+7, one 32-bit word per d
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tsk = lane + 64 * j;
+    const int kp = tsk & 15, c = tsk >> 4;
+    const int k0 = 2 * kp;
+    const int P = dec_pos(k0);  // even; key k0 + 1 lands at P + 1
+    const uint32_t w0[4] = {v0[j].x, v0[j].y, v0[j].z, v0[j].w};
+    const uint32_t w1[4] = {v1[j].x, v1[j].y, v1[j].z, v1[j].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t lo = k0 < nvalid ? (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu : 0u;
+      const uint32_t hi = k0 + 1 < nvalid ? (w1[e >> 1] >> (16 * (e & 1))) & 0xffffu : 0u;
+      const int d = 8 * c + e;
+      *reinterpret_cast<uint32_t*>(&vt[dec_vt(d, P >> 3) + 2 * (P & 7)]) = lo | (hi << 16);
+    }
   }
-  v_half(1);
 
   // S^T tiles: lane holds head `col`, keys 16t + 4qd + r
-  f32x4 sc[8];
+  f32x4 sc[2];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    sc[t] = mfma16(as_bf16x8(kf[t][0]), qf[0], f32x4{});
+  for (int t = 0; t < 2; ++t) {
+    sc[t] = f32x4{};
 #pragma unroll
-    for (int s = 1; s < 4; ++s) sc[t] = mfma16(as_bf16x8(kf[t][s]), qf[s], sc[t]);
+    for (int s = 0; s < 4; ++s)
+      sc[t] = mfma16(as_bf16x8(kf[t][s]), as_bf16x8(col < HG ? qv[s] : make_uint4(0, 0, 0, 0)),
+                     sc[t]);
   }
   constexpr float qscale = 1.4426950408889634f * 0.08838834764831845f;
   float m = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (16 * t + 4 * qd + r >= nvalid) sc[t][r] = -INFINITY;
@@ -922,53 +934,75 @@ __global__ void __launch_bounds__(64, 2) decode_attn_kernel(DecArgs a) {
     }
   m = fmaxf(m, __shfl_xor(m, 16));
   m = fmaxf(m, __shfl_xor(m, 32));
-  const float mc = m * qscale;
-  float l = 0.f;
-  uint4 pf[4];
+  const float mc = m == -INFINITY ? 0.f : m * qscale;  // all-masked quarter: p = 0
+  float pv[8];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    float pv[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pv[r] = fast_exp2(fmaf(sc[2 * s][r], qscale, -mc));
-      pv[4 + r] = fast_exp2(fmaf(sc[2 * s + 1][r], qscale, -mc));
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) l += pv[e];
-    pf[s] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                       pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+  for (int r = 0; r < 4; ++r) {
+    pv[r] = fast_exp2(fmaf(sc[0][r], qscale, -mc));
+    pv[4 + r] = fast_exp2(fmaf(sc[1][r], qscale, -mc));
   }
+  float l = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) l += pv[e];
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  const uint4 pf = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                              pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
 
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // O^T tiles: lane holds head `col`, d = 16dt + 4qd + r
-  const int64_t prow = (bg * a.k + slot) * HG + col;
+  f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    const int d = 16 * dt + col;
-    f32x4 o = {};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint4 av = *reinterpret_cast<const uint4*>(&vt[swz(d, 4 * s + qd)]);
-      o = mfma16(as_bf16x8(av), as_bf16x8(pf[s]), o);
-    }
-    if (col < HG) {
-      uint2 w;
-      w.x = pack_bf16x2(o[0], o[1]);
-      w.y = pack_bf16x2(o[2], o[3]);
-      *reinterpret_cast<uint2*>(a.opart + prow * kHeadDim + 16 * dt + 4 * qd) = w;
-    }
+    const uint4 av = *reinterpret_cast<const uint4*>(&vt[dec_vt(16 * dt + col, qd)]);
+    o[dt] = mfma16(as_bf16x8(av), as_bf16x8(pf), f32x4{});
   }
-  if (col < HG && qd == 0) a.lpart[prow] = make_float2(mc, l);
+  if (qd == 0) {
+    wm[wave][col] = m == -INFINITY ? -INFINITY : mc;
+    wl[wave][col] = l;
+  }
+  __syncthreads();  // every wave is done with its V^T; the merge reuses the LDS
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][col]);
+  const float sw = fast_exp2(wm[wave][col] - M);  // 0 for an all-masked quarter
+  float* red = reinterpret_cast<float*>(lds);  // [4][HG][128]
+  if (col < HG) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<f32x4*>(&red[(wave * HG + col) * kHeadDim + 16 * dt + 4 * qd]) =
+          o[dt] * sw;
+  }
+  __syncthreads();
+  const int64_t prow0 = (bg * a.k + slot) * HG;
+  for (int e = threadIdx.x; e < HG * 32; e += 256) {
+    const int h = e >> 5, d0 = 4 * (e & 31);
+    f32x4 acc = *reinterpret_cast<const f32x4*>(&red[h * kHeadDim + d0]);
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      acc += *reinterpret_cast<const f32x4*>(&red[(w * HG + h) * kHeadDim + d0]);
+    uint2 st;
+    st.x = pack_bf16x2(acc[0], acc[1]);
+    st.y = pack_bf16x2(acc[2], acc[3]);
+    *reinterpret_cast<uint2*>(a.opart + (prow0 + h) * kHeadDim + d0) = st;
+  }
+  if (threadIdx.x < HG) {
+    const int h = threadIdx.x;
+    float Mh = -INFINITY, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Mh = fmaxf(Mh, wm[w][h]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += wl[w][h] * fast_exp2(wm[w][h] - Mh);
+    a.lpart[prow0 + h] = make_float2(Mh, L);
+  }
 }
 
 template <int HG>
 static hipError_t launch_decode_t(const DecArgs& da, const CombArgs& ca, int64_t n,
                                   hipStream_t st) {
-  hipLaunchKernelGGL((decode_attn_kernel<HG>), dim3(static_cast<unsigned>(n)), dim3(64), 0, st,
+  hipLaunchKernelGGL((decode_attn_kernel<HG>), dim3(static_cast<unsigned>(n)), dim3(256), 0, st,
                      da);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -141,8 +141,11 @@ def test_prefill_small_all_rows(name, B, T, N, Hq, G, k):
     compare_rows(w, inp, idx, O, lse, rb, rt, S=S, tag=name)
 
 
-def test_decode_small():
-    w = Workload("decode_small", B=3, T=1, N=1000, Hq=64, G=8, k=16, seed=5)
+@pytest.mark.parametrize("N,Hq,G", [(1000, 64, 8), (916, 64, 8), (129, 16, 4), (200, 16, 1)])
+def test_decode_small(N, Hq, G):
+    """Cache tails of 104, 20, 1 and 72 keys: the last block's key quarters
+    are partly or wholly past the end."""
+    w = Workload("decode_small", B=3, T=1, N=N, Hq=Hq, G=G, k=16, seed=5)
     inp = make_inputs(w, device="cuda")
     idx = ops.select_blocks(inp["qI"], inp["kI"], w.k)
     S = ops.index_scores(inp["qI"], inp["kI"])
