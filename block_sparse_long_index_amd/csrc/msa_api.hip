@@ -24,7 +24,10 @@ int hip_fail(hipError_t e, const char* where) {
 }
 
 constexpr int64_t kDefaultWindow = int64_t(1) << 20;  // rows per inversion (one sequence)
-constexpr int64_t kStageRows = 4096;                    // rows of one group per KV-outer stage
+// Partial results of one KV-outer stage (rows x k slots x heads x 256 B) are
+// sized to the 256 MB last-level cache, so that the combine reads them back
+// from it; within that, more rows per stage fill the chunks better.
+constexpr int64_t kStagePartialBytes = int64_t(1) << 28;
 constexpr int64_t kMaxElems = int64_t(1) << 46;
 
 bool pow2_upto(int v, int hi) { return v >= 1 && v <= hi && (v & (v - 1)) == 0; }
@@ -82,11 +85,16 @@ int64_t default_window(const msa_dims_t* d) {
   return d->T < kDefaultWindow ? d->T : kDefaultWindow;
 }
 
-int64_t stage_rows_for(int64_t window) { return window < kStageRows ? window : kStageRows; }
+int64_t stage_rows_for(const msa_dims_t* d, int64_t window) {
+  const int64_t per_row = int64_t(d->k) * (d->Hq / d->G) * 256;
+  int64_t rows = 1024;
+  while (rows * 2 * per_row <= kStagePartialBytes) rows *= 2;
+  return window < rows ? window : rows;
+}
 
 size_t prefill_ws(const msa_dims_t* d, int64_t window) {
-  return msa::attn_workspace_bytes(window, stage_rows_for(window), d->N, d->G, d->Hq / d->G, d->k,
-                                   false);
+  return msa::attn_workspace_bytes(window, stage_rows_for(d, window), d->N, d->G, d->Hq / d->G,
+                                   d->k, false);
 }
 
 size_t decode_ws(const msa_dims_t* d) {
@@ -206,7 +214,7 @@ int msa_sparse_attn_prefill(const msa_dims_t* d, const void* q, const void* K, c
     hi = lo;
   }
   msa::AttnWorkspace w;
-  msa::attn_workspace_carve(ws, hi, stage_rows_for(hi), d->N, d->G, d->Hq / d->G, d->k, false,
+  msa::attn_workspace_carve(ws, hi, stage_rows_for(d, hi), d->N, d->G, d->Hq / d->G, d->k, false,
                             &w);
   const hipError_t e = msa::launch_attn_prefill(q, K, V, idx, O, lse, d->B, d->T, d->N, d->Hq,
                                                 d->G, d->k, w, static_cast<hipStream_t>(stream));
