@@ -68,9 +68,9 @@ static void layout(int64_t window, int64_t stage_rows, int64_t N, int G, int hg,
   off[2] = o; o += align256(sizeof(int32_t) * (4 + nstages));
   off[3] = o; o += align256(sizeof(int32_t) * entries);
   off[4] = o; o += align256(sizeof(int4) * nstages * maxc);
-  // one extra (sink) row absorbs the stores of rows past a chunk's end
-  off[5] = o; o += align256(sizeof(uint16_t) * (prow_count + 1) * kHeadDim);
-  off[6] = o; o += align256(sizeof(float2) * (prow_count + 1));
+  // one extra (sink) entry of hg rows absorbs the stores of rows past a chunk's end
+  off[5] = o; o += align256(sizeof(uint16_t) * (prow_count + hg) * kHeadDim);
+  off[6] = o; o += align256(sizeof(float2) * (prow_count + hg));
   off[7] = o;
   if (w) {
     w->window = window;
@@ -109,7 +109,7 @@ void attn_workspace_carve(void* ws, int64_t window, int64_t stage_rows, int64_t 
 
 // ---------------------------------------------------------------------------
 // Inversion of the selection for the query rows [t0, t0 + W) of sequence b: a
-// counting sort of the entries e = (t - t0) * k + slot by (group, block).
+// counting sort of the entries e = (t - t0) << 4 | slot by (group, block).
 //   1. unit histograms: workgroup (c, g) counts, in LDS, the blocks chosen by
 //      group g in rows [c*rq, (c+1)*rq) of the window; hist[(g*NB + blk)*nc + c]
 //   2. exclusive scan of hist in that order: the entries of bin (g, blk) are
@@ -165,7 +165,8 @@ __global__ void __launch_bounds__(256) scatter_kernel(InvArgs a) {
     const int32_t blk = src[i];
     if (blk >= 0 && blk < a.NB) {
       const int32_t pos = atomicAdd(&sh[blk], 1);
-      a.entries[pos] = static_cast<int32_t>(r_lo * a.k + i);
+      // entry = window row << 4 | slot (k <= 16), decoded with a shift
+      a.entries[pos] = static_cast<int32_t>(((r_lo + i / a.k) << 4) | (i % a.k));
     }
   }
 }
@@ -245,7 +246,7 @@ __global__ void __launch_bounds__(256) scan_apply_kernel(int32_t* x, int64_t n,
 __global__ void __launch_bounds__(256) stage_chunk_kernel(const int32_t* off, int32_t* totals,
                                                           int4* chunks, int32_t NB, int64_t nbins,
                                                           int32_t nc, int32_t U, int32_t S,
-                                                          int64_t maxc, int32_t bin_base) {
+                                                          int64_t maxc, int32_t bg_base) {
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t per_stage = ((NB + 63) / 64) * 64;  // waves never straddle stages
   const int64_t st = tid / per_stage;
@@ -281,7 +282,7 @@ __global__ void __launch_bounds__(256) stage_chunk_kernel(const int32_t* off, in
   int32_t cs = base + incl - nch;
   for (int32_t j = 0; j < n; j += kChunkQueries, ++cs) {
     const int32_t m = (n - j) < kChunkQueries ? (n - j) : kChunkQueries;
-    out[cs] = make_int4(bin_base + g * NB + blk, start + j, m, 0);
+    out[cs] = make_int4(bg_base + g, start + j, m, blk);
   }
 }
 
@@ -291,14 +292,26 @@ __global__ void __launch_bounds__(256) stage_chunk_kernel(const int32_t* off, in
 // gathered (query, head) row is processed against them: S^T = K Q^T with keys
 // on the MFMA M side (a lane holds 16 keys of one row, so the row max and sum
 // are in-register plus one half-wave exchange), softmax in fp32 with exp2,
-// P rounded to bf16, O^T = V^T P^T.  Each row writes its normalised partial O
-// (bf16) and lse (fp32, natural log) for the combine.
+// P rounded to bf16, O^T = V^T P^T.  Each row writes its unnormalised partial
+// O (bf16) and (log2-domain max, sum) for the combine.
 //
-// V^T layout: row d holds the 128 keys of the block; inside every 16-key group
-// the keys are stored in the order 0-3, 8-11, 4-7, 12-15, which is the order
-// in which one half-wave's P values reach the PV MFMA's k slots, so each
-// lane's A operand is one 16-B read.  Rows are chunk-swizzled like K.
+// LDS rows (keys of K, dims of V^T) are 272 bytes apart: 16 lanes reading the
+// same 16-B column of 16 consecutive rows hit distinct banks, and every
+// fragment address is a per-lane base plus a constant.  V^T row d holds the
+// 128 keys of the block; inside every 16-key group the keys are stored in the
+// order 0-3, 8-11, 4-7, 12-15, which is the order in which one half-wave's P
+// values reach the PV MFMA's k slots, so each lane's A operand is one 16-B read.
+//
+// Partial layout ("MFMA order"): the partial of entry E (a (row, slot) pair,
+// hg heads) is 256*hg bytes: piece (j, half, head) at byte
+// E*256*hg + j*32*hg + (half*hg + head)*16 holds the 8 values
+// d = 32*(j/2) + 16*(j%2) + 4*half + {0,1,2,3, 8,9,10,11}, which is what one
+// lane holds after the PV MFMAs (j = 0..7 over its 64 accumulators).  Each
+// lane thus stores its registers directly, and each store instruction writes
+// runs of 32*hg contiguous bytes.
 // ---------------------------------------------------------------------------
+constexpr int kPitch = 272;  // LDS row pitch of the K and V^T tiles
+
 struct AttnArgs {
   const u16* q;
   const u16* K;
@@ -312,7 +325,7 @@ struct AttnArgs {
   int32_t Hq, G, NB, k;
   int32_t rl_base;        // first window row of this launch's partial buffer
   int32_t pgroups;        // groups held by the partial buffer (1 for a stage, G for decode)
-  int32_t sink;           // spare partial row that absorbs rows past a chunk's end
+  int32_t sink;           // spare partial entry (hg rows) that absorbs rows past a chunk's end
 };
 
 __device__ __forceinline__ int vt_pos(int key) {
@@ -322,9 +335,8 @@ __device__ __forceinline__ int vt_pos(int key) {
 
 template <int HG>
 __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
-  __shared__ __align__(16) unsigned char ks[32768];
-  __shared__ __align__(16) unsigned char vt[32768];
-  __shared__ __align__(16) unsigned char ostage[4][4096];  // per-wave output staging
+  __shared__ __align__(16) unsigned char ks[128 * kPitch];
+  __shared__ __align__(16) unsigned char vt[128 * kPitch];
   // Workgroups are dealt to the 8 XCDs round-robin; give XCD x the x-th
   // contiguous eighth of the chunk list, so that the chunks of one KV block
   // (and the rows of one group) share an L2.
@@ -336,11 +348,10 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
   const int4 ch = a.chunks[ci];
   const int n = ch.z;
   if (n <= 0) return;
-  const int64_t bin = ch.x;
-  const int64_t blk = bin % a.NB;
-  const int64_t bg = bin / a.NB;
-  const int g = static_cast<int>(bg % a.G);
-  const int64_t b = bg / a.G;
+  const int64_t blk = ch.w;
+  const int64_t bg = ch.x;
+  const int g = static_cast<int>(bg) & (a.G - 1);  // G is a power of two
+  const int64_t b = bg >> __builtin_ctz(a.G);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -388,8 +399,8 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
     valid = rr < rows;
     const int e = __shfl(ent, valid ? rr / HG : 0);
     hh = rr % HG;
-    rl = e / a.k;
-    slot = e - rl * a.k;
+    rl = e >> 4;
+    slot = e & 15;
     const int64_t t = t0 + rl;
     p = static_cast<int>(a.N - a.T + t);
     q = a.q + ((b * a.T + t) * a.Hq + g * HG + hh) * kHeadDim;
@@ -412,7 +423,7 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = tid + j * 256;
-    *reinterpret_cast<uint4*>(&ks[swz(i >> 4, i & 15)]) = kr[j];
+    *reinterpret_cast<uint4*>(&ks[(i >> 4) * kPitch + (i & 15) * 16]) = kr[j];
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -426,7 +437,7 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
       const uint32_t lo = (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
       const uint32_t hi = (w1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
       const int d = 8 * c + e;
-      *reinterpret_cast<uint32_t*>(&vt[swz(d, P >> 3) + ((2 * P) & 15)]) = lo | (hi << 16);
+      *reinterpret_cast<uint32_t*>(&vt[d * kPitch + 2 * P]) = lo | (hi << 16);
     }
   }
   // Nothing is left in flight past this point, so the waits inside the pass
@@ -434,29 +445,23 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  const unsigned char* kbase = ks + l32 * kPitch + half * 16;
+  const unsigned char* vbase = vt + l32 * kPitch + half * 16;
   constexpr float kLog2e = 1.4426950408889634f;
   const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   for (int pass = 0; pass * 128 + wave * 32 < rows; ++pass) {
-    // S^T = K Q^T, one 32-key tile at a time; the next tile's K fragments are
-    // read from LDS while the current tile's MFMAs run.
+    // S^T = K Q^T, one 32-key tile at a time
     f32x16 sacc[4];
-    uint4 ka[2][8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      ka[0][s] = *reinterpret_cast<const uint4*>(&ks[swz(l32, 2 * s + half)]);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      if (kt + 1 < 4) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-          ka[(kt + 1) & 1][s] =
-              *reinterpret_cast<const uint4*>(&ks[swz((kt + 1) * 32 + l32, 2 * s + half)]);
+      for (int s = 0; s < 8; ++s) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(kbase + kt * 32 * kPitch + s * 32);
+        sacc[kt] = s == 0 ? mfma32(as_bf16x8(ka), qf[0], f32x16{})
+                          : mfma32(as_bf16x8(ka), qf[s], sacc[kt]);
       }
-      sacc[kt] = mfma32(as_bf16x8(ka[kt & 1][0]), qf[0], f32x16{});
-#pragma unroll
-      for (int s = 1; s < 8; ++s) sacc[kt] = mfma32(as_bf16x8(ka[kt & 1][s]), qf[s], sacc[kt]);
-      sched_fence();
     }
+    sched_fence();
     // the next pass's query rows load while this pass does softmax and PV
     const bool more = (pass + 1) * 128 + wave * 32 < rows;
     bool n_valid = false;
@@ -498,8 +503,7 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-          va[dt][hf] = *reinterpret_cast<const uint4*>(
-              &vt[swz(dt * 32 + l32, kt * 4 + hf * 2 + half)]);
+          va[dt][hf] = *reinterpret_cast<const uint4*>(vbase + dt * 32 * kPitch + kt * 64 + hf * 32);
       uint4 pb[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -520,45 +524,25 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
       }
     }
     l += __shfl_xor(l, 32);
-    // Unnormalised partial O (bf16) and its (log2-domain max, sum).  Each row's
-    // 64 values sit in two lanes in MFMA order; the tile goes through this
-    // wave's LDS area, half the columns at a time, so that every global store
-    // writes whole 128-byte row segments.
-    // Rows past the chunk's end write to the buffer's sink row; stores are
-    // unconditional so that no branch hides them from the wait counting.
+    // Unnormalised partial O (bf16, MFMA order) and its (log2-domain max,
+    // sum).  Rows past the chunk's end write to the buffer's sink entry;
+    // stores are unconditional so that no branch hides them from the wait
+    // counting.
     const int prow =
-        valid ? (((rl - a.rl_base) * a.pgroups + (a.pgroups > 1 ? g : 0)) * a.k + slot) * HG + hh
-              : a.sink;
+        (valid ? (((rl - a.rl_base) * a.pgroups + (a.pgroups > 1 ? g : 0)) * a.k + slot) * HG
+               : a.sink) + hh;
     a.lpart[prow] = make_float2(mc, l);  // both half-waves hold the same values
-    unsigned char* st = ostage[wave];
+    u16* dst = a.opart + static_cast<int64_t>(prow - hh) * kHeadDim + (half * HG + hh) * 8;
 #pragma unroll
-    for (int hpart = 0; hpart < 2; ++hpart) {
-#pragma unroll
-      for (int d2 = 0; d2 < 2; ++d2) {
-        const int dt = 2 * hpart + d2;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          uint2 w;
-          w.x = pack_bf16x2(oacc[dt][4 * q4 + 0], oacc[dt][4 * q4 + 1]);
-          w.y = pack_bf16x2(oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3]);
-          const int c16 = d2 * 4 + q4;  // 16-B chunk of the 128-B staged row
-          *reinterpret_cast<uint2*>(&st[l32 * 128 + ((c16 ^ (l32 & 7)) << 4) + 8 * half]) = w;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (lane >> 3) + 8 * i, seg = lane & 7;
-        const int dst_row = __shfl(prow, row);
-        const uint4 v = *reinterpret_cast<const uint4*>(&st[row * 128 + ((seg ^ (row & 7)) << 4)]);
-        *reinterpret_cast<uint4*>(a.opart + static_cast<int64_t>(dst_row) * kHeadDim +
-                                  hpart * 64 + seg * 8) = v;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int j = 0; j < 8; ++j) {
+      const f32x16& o = oacc[j >> 1];
+      const int i0 = 8 * (j & 1);
+      uint4 w;
+      w.x = pack_bf16x2(o[i0 + 0], o[i0 + 1]);
+      w.y = pack_bf16x2(o[i0 + 2], o[i0 + 3]);
+      w.z = pack_bf16x2(o[i0 + 4], o[i0 + 5]);
+      w.w = pack_bf16x2(o[i0 + 6], o[i0 + 7]);
+      *reinterpret_cast<uint4*>(dst + j * 16 * HG) = w;
     }
     if (more) {
       valid = n_valid;
@@ -594,8 +578,10 @@ struct CombArgs {
 
 template <int HG>
 __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
-  constexpr int LPH = 64 / HG;          // lanes per head
-  constexpr int VPL = kHeadDim / LPH;   // values per lane
+  // A row's partial is 16 pieces of 8 values per head (MFMA order, see the
+  // KV-outer kernel); a lane takes PPL consecutive pieces of one head.
+  constexpr int LPH = HG >= 4 ? 64 / HG : 16;  // lanes per head
+  constexpr int PPL = 16 / LPH;                // pieces per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   const int gper = a.group >= 0 ? 1 : a.G;
@@ -607,8 +593,10 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
   const int32_t* ir = a.idx + ((b * a.G + g) * a.T + t) * a.k;
   const bool sv = lane < a.k && ir[lane < a.k ? lane : 0] >= 0;
   const int nval = __popcll(__ballot(sv));
-  const int hh = lane / LPH;
-  const int d0 = (lane % LPH) * VPL;
+  // lanes past HG * LPH (only when HG < 4) take head 0's pieces and store nothing
+  const bool active = lane < HG * LPH;
+  const int hh = active ? lane / LPH : 0;
+  const int li = lane % LPH;
   const int64_t pbase = (rl * a.pgroups + (a.pgroups > 1 ? g : 0)) * a.k;
 
   // All 16 slots are loaded at once (slots past nval re-read slot 0 and get
@@ -621,63 +609,56 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
     ml[s] = a.lpart[(pbase + ss) * HG + hh];
     if (s < nval) mx = fmaxf(mx, ml[s].x);
   }
-  float acc[VPL];
+  uint4 raw[16][PPL];
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) acc[j] = 0.f;
+  for (int s = 0; s < 16; ++s) {
+    const int ss = s < nval ? s : 0;
+    const u16* src = a.opart + (pbase + ss) * HG * kHeadDim;
+#pragma unroll
+    for (int q = 0; q < PPL; ++q) {
+      const int pc = li * PPL + q, j = pc >> 1, hf = pc & 1;
+      raw[s][q] = ld16(src + j * 16 * HG + (hf * HG + hh) * 8);
+    }
+  }
+  float acc[PPL][8];
+#pragma unroll
+  for (int q = 0; q < PPL; ++q)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[q][u] = 0.f;
   float den = 0.f;
-  if constexpr (VPL >= 8) {
-    uint4 raw[16][VPL / 8];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int ss = s < nval ? s : 0;
-      const u16* src = a.opart + ((pbase + ss) * HG + hh) * kHeadDim + d0;
+  for (int s = 0; s < 16; ++s) {
+    const float w = s < nval ? fast_exp2(ml[s].x - mx) : 0.f;
+    den += w * ml[s].y;
 #pragma unroll
-      for (int j = 0; j < VPL / 8; ++j) raw[s][j] = ld16(src + 8 * j);
-    }
+    for (int q = 0; q < PPL; ++q) {
+      const uint32_t wv[4] = {raw[s][q].x, raw[s][q].y, raw[s][q].z, raw[s][q].w};
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const float w = s < nval ? fast_exp2(ml[s].x - mx) : 0.f;
-      den += w * ml[s].y;
-#pragma unroll
-      for (int j = 0; j < VPL / 8; ++j) {
-        const uint32_t wv[4] = {raw[s][j].x, raw[s][j].y, raw[s][j].z, raw[s][j].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          acc[8 * j + 2 * u] += w * __uint_as_float(wv[u] << 16);
-          acc[8 * j + 2 * u + 1] += w * __uint_as_float(wv[u] & 0xffff0000u);
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      if (s < nval) {
-        const float w = fast_exp2(ml[s].x - mx);
-        den += w * ml[s].y;
-        const u16* src = a.opart + ((pbase + s) * HG + hh) * kHeadDim + d0;
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) acc[j] += w * bf16_to_f32(src[j]);
+      for (int u = 0; u < 4; ++u) {
+        acc[q][2 * u] += w * __uint_as_float(wv[u] << 16);
+        acc[q][2 * u + 1] += w * __uint_as_float(wv[u] & 0xffff0000u);
       }
     }
   }
   const float inv = 1.f / den;
-  u16* dst = a.O + ((b * a.T + t) * a.Hq + g * HG + hh) * kHeadDim + d0;
-  if constexpr (VPL >= 8) {
+  u16* dst = a.O + ((b * a.T + t) * a.Hq + g * HG + hh) * kHeadDim;
+  if (active) {
 #pragma unroll
-    for (int j = 0; j < VPL; j += 8) {
-      uint4 w;
-      w.x = pack_bf16x2(acc[j + 0] * inv, acc[j + 1] * inv);
-      w.y = pack_bf16x2(acc[j + 2] * inv, acc[j + 3] * inv);
-      w.z = pack_bf16x2(acc[j + 4] * inv, acc[j + 5] * inv);
-      w.w = pack_bf16x2(acc[j + 6] * inv, acc[j + 7] * inv);
-      *reinterpret_cast<uint4*>(dst + j) = w;
+    for (int q = 0; q < PPL; ++q) {
+      // piece (j, hf): values 0-3 at d0, 4-7 at d0 + 8
+      const int pc = li * PPL + q, j = pc >> 1, hf = pc & 1;
+      const int d0 = 32 * (j >> 1) + 16 * (j & 1) + 4 * hf;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        uint2 w;
+        w.x = pack_bf16x2(acc[q][4 * r + 0] * inv, acc[q][4 * r + 1] * inv);
+        w.y = pack_bf16x2(acc[q][4 * r + 2] * inv, acc[q][4 * r + 3] * inv);
+        *reinterpret_cast<uint2*>(dst + d0 + 8 * r) = w;
+      }
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) dst[j] = f32_to_bf16(acc[j] * inv);
   }
   // lse in natural log: (max + log2(sum)) * ln 2, the max being log2-domain
-  if (a.lse && (lane % LPH) == 0)
+  if (a.lse && active && li == 0)
     a.lse[(b * a.Hq + g * HG + hh) * a.T + t] = (mx + __log2f(den)) * 0.6931471805599453f;
 }
 
@@ -760,7 +741,7 @@ hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
       const int64_t per_stage = ((NB + 63) / 64) * 64;
       hipLaunchKernelGGL(stage_chunk_kernel, dim3(blocks_for(nst * per_stage, 256)), dim3(256), 0,
                          st, w.hist, w.totals, w.chunks, NB, static_cast<int64_t>(G) * NB, ia.nc,
-                         U, S, w.max_chunks, static_cast<int32_t>(b * G * NB));
+                         U, S, w.max_chunks, static_cast<int32_t>(b * G));
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t r0 = b * T + t0;
@@ -976,6 +957,8 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecArgs a) {
           o[dt] * sw;
   }
   __syncthreads();
+  // the partial in MFMA order (the layout the KV-outer kernel writes): d0's
+  // four values sit in piece (j, half) at value offset t0
   const int64_t prow0 = (bg * a.k + slot) * HG;
   for (int e = threadIdx.x; e < HG * 32; e += 256) {
     const int h = e >> 5, d0 = 4 * (e & 31);
@@ -986,7 +969,9 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecArgs a) {
     uint2 st;
     st.x = pack_bf16x2(acc[0], acc[1]);
     st.y = pack_bf16x2(acc[2], acc[3]);
-    *reinterpret_cast<uint2*>(a.opart + (prow0 + h) * kHeadDim + d0) = st;
+    const int dw = d0 & 31;
+    const int j = 2 * (d0 >> 5) + (dw >> 4), hf = (dw >> 2) & 1, t0 = 4 * ((dw >> 3) & 1);
+    *reinterpret_cast<uint2*>(a.opart + prow0 * kHeadDim + j * 16 * HG + (hf * HG + h) * 8 + t0) = st;
   }
   if (threadIdx.x < HG) {
     const int h = threadIdx.x;

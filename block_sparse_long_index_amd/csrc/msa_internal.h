@@ -22,7 +22,7 @@ hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
 struct AttnWorkspace {
   int32_t* hist;       // [G * NB * nc]: unit block counts, then exclusive offsets
   int32_t* tile_sums;  // [ntiles]
-  int32_t* totals;     // [4 + nstages]: entries, decode chunks, -, -, chunks per stage
+  int32_t* totals;     // [4 + nstages]: entries, -, -, -, chunks per stage
   int32_t* entries;    // [window * G * k]
   int4* chunks;        // [nstages][max_chunks]
   uint16_t* opart;     // one stage's partial O: [stage_rows, k, hg, 128] bf16, unnormalised
