@@ -33,6 +33,7 @@ from msa_inputs import WORKLOADS, make_inputs, sample_rows  # noqa: E402
 
 METRIC = "MSA prefill eff. TFLOP/s & decode HBM GB/s at 128K; top-k select µs (1 GPU)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -144,11 +145,47 @@ def topk_leg(args, pre):
             "matches_fused_select": same, "torch_topk_us": float(np.median(tk))}
 
 
-def decode_leg(args):
+def fp8_leg(args, pre):
+    """The index branch on 8-bit (E4M3) q^I / k^I: the fused select alone on the
+    same prefill workload (its selection must equal the bf16 one: the inputs
+    are integers, exact in both formats), and the step with it."""
+    w, inp = pre["w"], pre["inp"]
+    q8 = inp["qI"].float().to(torch.float8_e4m3fn)
+    k8 = inp["kI"].float().to(torch.float8_e4m3fn)
+    idx = torch.empty_like(pre["idx"])
+    for _ in range(2):
+        ops.select_blocks(q8, k8, w.k, out=idx)
+    evs = [(ev(), ev()) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        ops.select_blocks(q8, k8, w.k, out=idx)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    same = bool(torch.equal(idx, pre["idx"]))
+    fl = acc.prefill_flops(w)
+    att = float(pre["att_ms"].mean())
+    step = ms + att
+    ach = fl["index"] / (ms * 1e-3) / 1e12
+    del q8, k8
+    return {"select_ms": ms, "select_TFLOPs": ach,
+            "roofline": {"kernel": "index_tile_kernel (fp8 inputs)", "bound": "mfma",
+                         "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": ach / PEAK_FP8_TFLOPS},
+            "matches_bf16_selection": same,
+            "step_ms": step, "step_TFLOPs": fl["total"] / (step * 1e-3) / 1e12,
+            "note": "step = fp8 select + the bf16 attention of the same run"}
+
+
+def decode_leg(args, fp8=False):
     w = WORKLOADS["decode_256k_b16"]
-    log("[bench] generating", w.name)
+    log("[bench] generating", w.name, "(fp8 index keys)" if fp8 else "")
     inp = make_inputs(w, device="cuda")
     qI, kI, K, V = inp["qI"], inp["kI"], inp["K"], inp["V"]
+    if fp8:
+        qI = qI.float().to(torch.float8_e4m3fn)
+        kI = kI.float().to(torch.float8_e4m3fn)
+        inp["qI"], inp["kI"] = qI, kI
     q = inp["q"][:, 0].contiguous()
     idx = torch.empty(w.B, w.G, 1, w.k, dtype=torch.int32, device="cuda")
     O = torch.empty_like(q)
@@ -178,7 +215,7 @@ def decode_leg(args):
         torch.cuda.synchronize()
         times.append(a.elapsed_time(b) * 1e3)
     us = np.array(times)
-    by = acc.decode_bytes(w)
+    by = acc.decode_bytes(w, index_bytes=1 if fp8 else 2)
     med = float(np.median(us))
     out = {"workload": w.name, "us_p50": med, "us_p95": float(np.percentile(us, 95)),
            "bytes": by["total"], "GBps": by["total"] / med / 1e3,
@@ -239,7 +276,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="prefill_128k")
-    ap.add_argument("--only", default="", help="prefill | decode | topk (skip the other legs)")
+    ap.add_argument("--only", default="",
+                    help="prefill | decode | topk | fp8 (skip the other legs)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-reps", type=int, default=30)
@@ -268,7 +306,7 @@ def main():
     out = {"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
-    if args.only in ("", "prefill", "topk"):
+    if args.only in ("", "prefill", "topk", "fp8"):
         pre = prefill_leg(args)
         w = pre["w"]
         fl = pre["flops"]
@@ -292,6 +330,9 @@ def main():
         if args.only in ("", "topk"):
             log("[bench] top-k leg")
             out["topk"] = topk_leg(args, pre)
+        if args.only in ("", "fp8"):
+            log("[bench] fp8 index leg")
+            out["fp8_index"] = fp8_leg(args, pre)
         if not args.no_cpu and args.only == "":
             log("[bench] cpu baseline")
             out["cpu_baseline"], out["parity_sample"] = cpu_leg(args, pre)
@@ -300,6 +341,7 @@ def main():
     if args.only in ("", "decode"):
         log("[bench] decode leg")
         out["decode"] = decode_leg(args)
+        out["decode_fp8_index"] = decode_leg(args, fp8=True)
         if args.only == "decode":
             out.update({"value": out["decode"]["GBps"], "unit": "GB/s",
                         "ms_per_step": out["decode"]["us_p50"] / 1e3,

@@ -63,13 +63,14 @@ def prefill_flops(w) -> dict:
                 candidates=candidate_flops(w.N, w.T, w.G, w.d_I, w.Bk, w.B))
 
 
-def decode_bytes(w) -> dict:
-    """Bytes one decode step must move: T == 1, cache length N."""
-    kI = w.B * w.N * w.d_I * 2
+def decode_bytes(w, index_bytes: int = 2) -> dict:
+    """Bytes one decode step must move: T == 1, cache length N; the index
+    branch's q^I / k^I take index_bytes per value (2: bf16, 1: fp8)."""
+    kI = w.B * w.N * w.d_I * index_bytes
     nsel_blocks = w.B * w.G * min(w.k, (w.N - 1) // w.Bk + 1)
     kv = nsel_blocks * w.Bk * w.d_h * 2 * 2
     small = (w.B * w.Hq * w.d_h * 2 * 2          # q in, O out
-             + w.B * w.G * w.d_I * 2             # q^I
+             + w.B * w.G * w.d_I * index_bytes   # q^I
              + w.B * w.G * w.k * 4)              # idx
     return dict(index_keys=kI, kv=kv, small=small, total=kI + kv + small)
 

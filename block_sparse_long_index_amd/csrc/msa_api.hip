@@ -134,8 +134,8 @@ size_t msa_workspace_bytes(int op, const msa_dims_t* d) {
   return 0;
 }
 
-int msa_index_scores(const msa_dims_t* d, const void* qI, const void* kI, float* S,
-                     void* stream) {
+static int index_scores_impl(const msa_dims_t* d, const void* qI, const void* kI, float* S,
+                             void* stream, bool fp8, const char* name) {
   MSA_TRY(check_dims(d));
   MSA_TRY(check_ptr(qI, "qI"));
   MSA_TRY(check_ptr(kI, "kI"));
@@ -143,15 +143,17 @@ int msa_index_scores(const msa_dims_t* d, const void* qI, const void* kI, float*
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d->T == 1)
-    e = msa::launch_decode_scan(qI, kI, S, d->B, d->N, d->G, st);
+    e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, st);
   else
-    e = msa::launch_index_tiles(true, qI, kI, S, nullptr, d->B, d->T, d->N, d->G, d->k, st);
-  if (e != hipSuccess) return hip_fail(e, "msa_index_scores");
+    e = msa::launch_index_tiles(true, fp8, qI, kI, S, nullptr, d->B, d->T, d->N, d->G, d->k,
+                                st);
+  if (e != hipSuccess) return hip_fail(e, name);
   return MSA_OK;
 }
 
-int msa_select_blocks(const msa_dims_t* d, const void* qI, const void* kI, int32_t* idx,
-                      void* ws, size_t ws_bytes, void* stream) {
+static int select_blocks_impl(const msa_dims_t* d, const void* qI, const void* kI, int32_t* idx,
+                              void* ws, size_t ws_bytes, void* stream, bool fp8,
+                              const char* name) {
   MSA_TRY(check_dims(d));
   MSA_TRY(check_ptr(qI, "qI"));
   MSA_TRY(check_ptr(kI, "kI"));
@@ -165,13 +167,35 @@ int msa_select_blocks(const msa_dims_t* d, const void* qI, const void* kI, int32
       return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "select needs %zu workspace bytes, got %zu",
                   need, ws_bytes);
     float* S = static_cast<float*>(ws);
-    e = msa::launch_decode_scan(qI, kI, S, d->B, d->N, d->G, st);
+    e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, st);
     if (e == hipSuccess) e = msa::launch_topk_rows(S, idx, d->B, 1, d->N, d->G, d->k, st);
   } else {
-    e = msa::launch_index_tiles(false, qI, kI, nullptr, idx, d->B, d->T, d->N, d->G, d->k, st);
+    e = msa::launch_index_tiles(false, fp8, qI, kI, nullptr, idx, d->B, d->T, d->N, d->G, d->k,
+                                st);
   }
-  if (e != hipSuccess) return hip_fail(e, "msa_select_blocks");
+  if (e != hipSuccess) return hip_fail(e, name);
   return MSA_OK;
+}
+
+int msa_index_scores(const msa_dims_t* d, const void* qI, const void* kI, float* S,
+                     void* stream) {
+  return index_scores_impl(d, qI, kI, S, stream, false, "msa_index_scores");
+}
+
+int msa_index_scores_fp8(const msa_dims_t* d, const void* qI, const void* kI, float* S,
+                         void* stream) {
+  return index_scores_impl(d, qI, kI, S, stream, true, "msa_index_scores_fp8");
+}
+
+int msa_select_blocks(const msa_dims_t* d, const void* qI, const void* kI, int32_t* idx,
+                      void* ws, size_t ws_bytes, void* stream) {
+  return select_blocks_impl(d, qI, kI, idx, ws, ws_bytes, stream, false, "msa_select_blocks");
+}
+
+int msa_select_blocks_fp8(const msa_dims_t* d, const void* qI, const void* kI, int32_t* idx,
+                          void* ws, size_t ws_bytes, void* stream) {
+  return select_blocks_impl(d, qI, kI, idx, ws, ws_bytes, stream, true,
+                            "msa_select_blocks_fp8");
 }
 
 int msa_select_blocks_from_scores(const msa_dims_t* d, const float* S, int32_t* idx,

@@ -66,6 +66,36 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// fp8 (OCP e4m3) operands: 32 values = 8 dwords per lane.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8 as_i32x8(uint4 lo, uint4 hi) {
+  i32x8 v;
+  v[0] = static_cast<int>(lo.x); v[1] = static_cast<int>(lo.y);
+  v[2] = static_cast<int>(lo.z); v[3] = static_cast<int>(lo.w);
+  v[4] = static_cast<int>(hi.x); v[5] = static_cast<int>(hi.y);
+  v[6] = static_cast<int>(hi.z); v[7] = static_cast<int>(hi.w);
+  return v;
+}
+
+// D(32x32) += A(32x64) * B(64x32), e4m3 in (format code 0 for both operands,
+// no block scales), fp32 accumulate.
+//   A: lane l holds row (l % 32) and 32 of the 64 k values, the same 32 for
+//      the lanes of one half-wave (l / 32); B: lane l holds column (l % 32)
+//      and the same k values as A's lanes of its half-wave.  Any fixed
+//      assignment of k to (half, byte) works as long as A and B agree; here
+//      half h holds k = 32h .. 32h+31 in byte order.
+//   D: as for the bf16 32x32 MFMA.
+__device__ __forceinline__ f32x16 mfma32_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// D(16x16) += A(16x128) * B(128x16), e4m3 in: lane quarter l / 16 holds
+// k = 32*(l/16) .. +31 of row / column l % 16; D as for the bf16 16x16 MFMA.
+__device__ __forceinline__ f32x4 mfma16_f8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // Row r of a 128 x 128 bf16 tile in LDS is 256 B = 16 chunks of 16 B.  Chunk
 // c of row r is stored at chunk position c ^ (r & 15): sixteen consecutive
 // rows read at the same logical chunk then hit sixteen different chunk

@@ -6,13 +6,14 @@
 
 namespace msa {
 
-// Stages 1+2 (write S) or stages 1-3 fused (write idx) for T > 1.
-hipError_t launch_index_tiles(bool write_scores, const void* qI, const void* kI,
+// Stages 1+2 (write S) or stages 1-3 fused (write idx) for T > 1; fp8: q^I and
+// k^I are e4m3 bytes instead of bf16.
+hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const void* kI,
                               float* S, int32_t* idx, int64_t B, int64_t T,
                               int64_t N, int G, int k, hipStream_t st);
 
 // Stages 1+2 for T == 1: streams the index keys, S is [B, G, 1, NB].
-hipError_t launch_decode_scan(const void* qI, const void* kI, float* S,
+hipError_t launch_decode_scan(bool fp8, const void* qI, const void* kI, float* S,
                               int64_t B, int64_t N, int G, hipStream_t st);
 
 // Stage 3 from S [B, G, T, NB] (one wave per row).

@@ -37,7 +37,6 @@ struct TileShape {
   static constexpr int NCOL = QT * G;
   static constexpr int NW = NCOL / 64;
   static constexpr int NT = NW * 64;
-  static constexpr int PF = 2048 / NT;  // 16-B chunks per thread per block
 };
 
 struct TileArgs {
@@ -87,12 +86,20 @@ __device__ __forceinline__ void sort_ascending(int (&v)[CAP]) {
   }
 }
 
-template <int G, int CAP, bool WRITE_S>
+// F8: q^I and k^I are OCP e4m3 bytes instead of bf16.  A k^I row is then
+// 128 B; in LDS the rows sit 144 B apart (16 consecutive rows read at the
+// same column hit distinct banks) instead of the bf16 tile's chunk swizzle.
+template <int G, int CAP, bool WRITE_S, bool F8>
 __global__ void __launch_bounds__(TileShape<G>::NT)
 index_tile_kernel(TileArgs a) {
   using TS = TileShape<G>;
-  constexpr int QT = TS::QT, NT = TS::NT, PF = TS::PF;
-  __shared__ __align__(16) unsigned char kbuf[2][32768];
+  constexpr int QT = TS::QT, NT = TS::NT;
+  constexpr int ROWB = F8 ? 128 : 256;      // bytes per k^I / q^I row
+  constexpr int CPR = ROWB / 16;            // 16-B chunks per row
+  constexpr int PITCH = F8 ? 144 : 256;     // LDS row pitch
+  constexpr int PF = 128 * CPR / NT;        // 16-B chunks per thread per block
+  static_assert(PF * NT == 128 * CPR, "block chunks must split evenly over the threads");
+  __shared__ __align__(16) unsigned char kbuf[2][128 * PITCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -105,7 +112,8 @@ index_tile_kernel(TileArgs a) {
 
   // Column data for the two MFMA column tiles of this lane.
   int64_t colp[2];
-  bf16x8 qf[2][8];
+  bf16x8 qf[2][8];   // bf16: k-step s holds d = 16s + 8*half .. +7
+  i32x8 qf8[2][2];   // e4m3: k-step s holds d = 64s + 32*half .. +31
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int c = wave * 64 + j * 32 + l32;
@@ -114,11 +122,22 @@ index_tile_kernel(TileArgs a) {
     const int64_t t = p - row0;
     colp[j] = p;
     const bool ok = (t >= 0) && (t < a.T);
-    const u16* src = a.qI + ((static_cast<int64_t>(b) * a.T + (ok ? t : 0)) * G + g) * kHeadDim;
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.qI) +
+                               ((static_cast<int64_t>(b) * a.T + (ok ? t : 0)) * G + g) * ROWB;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    if constexpr (F8) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint4 v = ld16(src + 16 * s + 8 * half);  // src is a valid row
-      qf[j][s] = as_bf16x8(ok ? v : make_uint4(0, 0, 0, 0));
+      for (int s = 0; s < 2; ++s) {
+        const uint4 lo = ld16(src + 64 * s + 32 * half);  // src is a valid row
+        const uint4 hi = ld16(src + 64 * s + 32 * half + 16);
+        qf8[j][s] = as_i32x8(ok ? lo : z, ok ? hi : z);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint4 v = ld16(src + 32 * s + 16 * half);  // src is a valid row
+        qf[j][s] = as_bf16x8(ok ? v : z);
+      }
     }
   }
 
@@ -129,7 +148,8 @@ index_tile_kernel(TileArgs a) {
   const bool own_ok = (own_t >= 0) && (own_t < a.T);
 
   const int64_t nkb = WRITE_S ? (L + 1) : L;
-  const u16* kbase = a.kI + static_cast<int64_t>(b) * a.N * kHeadDim;
+  const unsigned char* kbase =
+      reinterpret_cast<const unsigned char*>(a.kI) + static_cast<int64_t>(b) * a.N * ROWB;
 
   float ts[CAP];
   int ti[CAP];
@@ -152,9 +172,9 @@ index_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int i = tid + j * NT;
-      const int r = i >> 4, c = i & 15;
+      const int r = i / CPR, c = i % CPR;
       const int64_t key = kb * kBlock + r;
-      const uint4 v = ld16(kbase + (key < a.N ? key : a.N - 1) * kHeadDim + c * 8);
+      const uint4 v = ld16(kbase + (key < a.N ? key : a.N - 1) * ROWB + c * 16);
       pf[j] = key < a.N ? v : make_uint4(0, 0, 0, 0);
     }
   };
@@ -162,8 +182,8 @@ index_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int i = tid + j * NT;
-      const int r = i >> 4, c = i & 15;
-      *reinterpret_cast<uint4*>(&kbuf[buf][swz(r, c)]) = pf[j];
+      const int r = i / CPR, c = i % CPR;
+      *reinterpret_cast<uint4*>(&kbuf[buf][F8 ? r * PITCH + c * 16 : swz(r, c)]) = pf[j];
     }
   };
 
@@ -183,16 +203,30 @@ index_tile_kernel(TileArgs a) {
     // One 32-key tile: 8 K fragments from LDS, 16 MFMAs into two column tiles.
     auto tile = [&](int kt, f32x16& c0, f32x16& c1) {
       const int r = kt * 32 + l32;
-      uint4 av[8];
+      if constexpr (F8) {
+        // two 32x32x64 steps cover the 128 dims
+        const unsigned char* rp = buf + r * PITCH + 32 * half;
+        i32x8 av[2];
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        av[s] = *reinterpret_cast<const uint4*>(&buf[swz(r, 2 * s + half)]);
-      c0 = mfma32(as_bf16x8(av[0]), qf[0][0], f32x16{});
-      c1 = mfma32(as_bf16x8(av[0]), qf[1][0], f32x16{});
+        for (int s = 0; s < 2; ++s)
+          av[s] = as_i32x8(*reinterpret_cast<const uint4*>(rp + 64 * s),
+                           *reinterpret_cast<const uint4*>(rp + 64 * s + 16));
+        c0 = mfma32_f8(av[0], qf8[0][0], f32x16{});
+        c1 = mfma32_f8(av[0], qf8[1][0], f32x16{});
+        c0 = mfma32_f8(av[1], qf8[0][1], c0);
+        c1 = mfma32_f8(av[1], qf8[1][1], c1);
+      } else {
+        uint4 av[8];
 #pragma unroll
-      for (int s = 1; s < 8; ++s) {
-        c0 = mfma32(as_bf16x8(av[s]), qf[0][s], c0);
-        c1 = mfma32(as_bf16x8(av[s]), qf[1][s], c1);
+        for (int s = 0; s < 8; ++s)
+          av[s] = *reinterpret_cast<const uint4*>(&buf[swz(r, 2 * s + half)]);
+        c0 = mfma32(as_bf16x8(av[0]), qf[0][0], f32x16{});
+        c1 = mfma32(as_bf16x8(av[0]), qf[1][0], f32x16{});
+#pragma unroll
+        for (int s = 1; s < 8; ++s) {
+          c0 = mfma32(as_bf16x8(av[s]), qf[0][s], c0);
+          c1 = mfma32(as_bf16x8(av[s]), qf[1][s], c1);
+        }
       }
     };
     // Block max over a finished tile (with the causal mask in the local block).
@@ -294,36 +328,36 @@ index_tile_kernel(TileArgs a) {
   }
 }
 
-template <int G, bool WS>
+template <int G, bool WS, bool F8>
 static hipError_t launch_tiles_cap(const TileArgs& a, int64_t ntiles, hipStream_t st) {
   using TS = TileShape<G>;
   const int64_t grid = ntiles * a.B;
   const dim3 gd(static_cast<unsigned>(grid)), bd(TS::NT);
   if (WS || a.k <= 4) {
-    hipLaunchKernelGGL((index_tile_kernel<G, 3, WS>), gd, bd, 0, st, a);
+    hipLaunchKernelGGL((index_tile_kernel<G, 3, WS, F8>), gd, bd, 0, st, a);
   } else if (a.k <= 8) {
-    hipLaunchKernelGGL((index_tile_kernel<G, 7, WS>), gd, bd, 0, st, a);
+    hipLaunchKernelGGL((index_tile_kernel<G, 7, WS, F8>), gd, bd, 0, st, a);
   } else {
-    hipLaunchKernelGGL((index_tile_kernel<G, 15, WS>), gd, bd, 0, st, a);
+    hipLaunchKernelGGL((index_tile_kernel<G, 15, WS, F8>), gd, bd, 0, st, a);
   }
   return hipGetLastError();
 }
 
-template <bool WS>
+template <bool WS, bool F8>
 static hipError_t launch_tiles_g(const TileArgs& a, int G, int64_t ntiles, hipStream_t st) {
   switch (G) {
-    case 1: return launch_tiles_cap<1, WS>(a, ntiles, st);
-    case 2: return launch_tiles_cap<2, WS>(a, ntiles, st);
-    case 4: return launch_tiles_cap<4, WS>(a, ntiles, st);
-    case 8: return launch_tiles_cap<8, WS>(a, ntiles, st);
-    case 16: return launch_tiles_cap<16, WS>(a, ntiles, st);
+    case 1: return launch_tiles_cap<1, WS, F8>(a, ntiles, st);
+    case 2: return launch_tiles_cap<2, WS, F8>(a, ntiles, st);
+    case 4: return launch_tiles_cap<4, WS, F8>(a, ntiles, st);
+    case 8: return launch_tiles_cap<8, WS, F8>(a, ntiles, st);
+    case 16: return launch_tiles_cap<16, WS, F8>(a, ntiles, st);
   }
   return hipErrorInvalidValue;
 }
 
 static int tile_queries(int G) { return (512 / G) < 128 ? (512 / G) : 128; }
 
-hipError_t launch_index_tiles(bool write_scores, const void* qI, const void* kI,
+hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const void* kI,
                               float* S, int32_t* idx, int64_t B, int64_t T,
                               int64_t N, int G, int k, hipStream_t st) {
   const int QT = tile_queries(G);
@@ -340,8 +374,12 @@ hipError_t launch_index_tiles(bool write_scores, const void* qI, const void* kI,
   const int64_t tile_lo = (N - T) / QT;
   a.tile_hi = (N - 1) / QT;
   const int64_t ntiles = a.tile_hi - tile_lo + 1;
-  if (write_scores) return launch_tiles_g<true>(a, G, ntiles, st);
-  return launch_tiles_g<false>(a, G, ntiles, st);
+  if (fp8) {
+    if (write_scores) return launch_tiles_g<true, true>(a, G, ntiles, st);
+    return launch_tiles_g<false, true>(a, G, ntiles, st);
+  }
+  if (write_scores) return launch_tiles_g<true, false>(a, G, ntiles, st);
+  return launch_tiles_g<false, false>(a, G, ntiles, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -362,35 +400,52 @@ struct ScanArgs {
   int32_t NB, G;
 };
 
+// F8: e4m3 inputs; one 16x16x128 MFMA covers 16 keys x all 128 dims (lane
+// quarter qd holds d = 32*qd .. +31), and a block is 16 KB.
+template <bool F8>
 __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
+  constexpr int ROWB = F8 ? 128 : 256;  // bytes per k^I / q^I row
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
   const int col = lane & 15, qd = lane >> 4;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  const unsigned char* qsrc = reinterpret_cast<const unsigned char*>(a.qI) +
+                              (static_cast<int64_t>(b) * a.G + (col < a.G ? col : 0)) * ROWB;
   bf16x8 qf[4];
-  const u16* qsrc = a.qI + (static_cast<int64_t>(b) * a.G + (col < a.G ? col : 0)) * kHeadDim;
+  i32x8 qf8;
+  if constexpr (F8) {
+    const uint4 lo = col < a.G ? ld16(qsrc + 32 * qd) : z;
+    const uint4 hi = col < a.G ? ld16(qsrc + 32 * qd + 16) : z;
+    qf8 = as_i32x8(lo, hi);
+  } else {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    uint4 v = col < a.G ? ld16(qsrc + 32 * s + 8 * qd) : make_uint4(0, 0, 0, 0);
-    qf[s] = as_bf16x8(v);
+    for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(col < a.G ? ld16(qsrc + 64 * s + 16 * qd) : z);
   }
-  const u16* kbase = a.kI + static_cast<int64_t>(b) * a.N * kHeadDim;
+  const unsigned char* kbase =
+      reinterpret_cast<const unsigned char*>(a.kI) + static_cast<int64_t>(b) * a.N * ROWB;
   {
     const int64_t kb = static_cast<int64_t>(blockIdx.x) * 4 + wave;
     if (kb >= a.NB) return;
-    uint4 d[8][4];
+    constexpr int LPK = F8 ? 2 : 4;  // 16-B loads per key row and lane
+    uint4 d[8][LPK];
 #pragma unroll
     for (int kg = 0; kg < 8; ++kg) {
       const int64_t key = kb * kBlock + kg * 16 + col;
-      const u16* src = kbase + (key < a.N ? key : a.N - 1) * kHeadDim + 8 * qd;
+      const unsigned char* src = kbase + (key < a.N ? key : a.N - 1) * ROWB;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) d[kg][s] = ld16(src + 32 * s);  // tail keys masked below
+      for (int s = 0; s < LPK; ++s)  // tail keys masked below
+        d[kg][s] = F8 ? ld16(src + 32 * qd + 16 * s) : ld16(src + 64 * s + 16 * qd);
     }
     float m = -INFINITY;
 #pragma unroll
     for (int kg = 0; kg < 8; ++kg) {
       f32x4 acc = {};
+      if constexpr (F8) {
+        acc = mfma16_f8(as_i32x8(d[kg][0], d[kg][1]), qf8, acc);
+      } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mfma16(as_bf16x8(d[kg][s]), qf[s], acc);
+        for (int s = 0; s < 4; ++s) acc = mfma16(as_bf16x8(d[kg][s]), qf[s], acc);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t key = kb * kBlock + kg * 16 + 4 * qd + r;
@@ -405,7 +460,7 @@ __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
   }
 }
 
-hipError_t launch_decode_scan(const void* qI, const void* kI, float* S,
+hipError_t launch_decode_scan(bool fp8, const void* qI, const void* kI, float* S,
                               int64_t B, int64_t N, int G, hipStream_t st) {
   ScanArgs a;
   a.qI = static_cast<const u16*>(qI);
@@ -415,7 +470,10 @@ hipError_t launch_decode_scan(const void* qI, const void* kI, float* S,
   a.NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
   a.G = G;
   const dim3 grid(static_cast<unsigned>((a.NB + 3) / 4), static_cast<unsigned>(B));
-  hipLaunchKernelGGL(decode_scan_kernel, grid, dim3(256), 0, st, a);
+  if (fp8)
+    hipLaunchKernelGGL(decode_scan_kernel<true>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(decode_scan_kernel<false>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

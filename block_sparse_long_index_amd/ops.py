@@ -28,6 +28,8 @@ _P = ctypes.c_void_p
 _SIGS = {
     "msa_index_scores": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "msa_select_blocks": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_index_scores_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "msa_select_blocks_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_select_blocks_from_scores": (ctypes.c_int, [_P, _P, _P, _P]),
     "msa_sparse_attn_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P,
                                                ctypes.c_size_t, _P]),
@@ -116,33 +118,45 @@ def _workspace(op, d, ws):
     return ws, ws.numel() * ws.element_size()
 
 
-def index_scores(qI, kI, out=None):
-    """Stages 1+2.  qI [B,T,G,128] bf16, kI [B,N,128] bf16 -> S [B,G,T,NB] fp32."""
+# The index branch takes bf16 or fp8 (OCP e4m3fn) q^I / k^I; the dtype picks
+# the C entry point.
+_INDEX_DTYPES = {torch.bfloat16: "", torch.float8_e4m3fn: "_fp8"}
+
+
+def _index_inputs(qI, kI):
+    if qI.dtype not in _INDEX_DTYPES:
+        raise ValueError("qI must be bfloat16 or float8_e4m3fn, got %s" % qI.dtype)
     B, T, G, dI = qI.shape
     N = kI.shape[1]
-    _need(qI, "qI", torch.bfloat16)
-    _need(kI, "kI", torch.bfloat16, (B, N, dI))
+    _need(qI, "qI", qI.dtype)
+    _need(kI, "kI", qI.dtype, (B, N, dI))
+    return B, T, G, dI, N, _INDEX_DTYPES[qI.dtype]
+
+
+def index_scores(qI, kI, out=None):
+    """Stages 1+2.  qI [B,T,G,128], kI [B,N,128] (both bf16 or both fp8
+    e4m3fn) -> S [B,G,T,NB] fp32."""
+    B, T, G, dI, N, sfx = _index_inputs(qI, kI)
     d = dims(B, T, N, G, G, 1, d_I=dI)
     NB = (N + d.Bk - 1) // d.Bk
     S = out if out is not None else torch.empty(B, G, T, NB, dtype=torch.float32, device=qI.device)
     _need(S, "S", torch.float32, (B, G, T, NB))
-    _check(lib().msa_index_scores(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(S), _stream()),
-           "msa_index_scores")
+    name = "msa_index_scores" + sfx
+    _check(getattr(lib(), name)(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(S), _stream()), name)
     return S
 
 
 def select_blocks(qI, kI, k, out=None, workspace=None):
-    """Stages 1-3 fused.  -> idx [B,G,T,k] int32 (ascending, -1 padded)."""
-    B, T, G, dI = qI.shape
-    N = kI.shape[1]
-    _need(qI, "qI", torch.bfloat16)
-    _need(kI, "kI", torch.bfloat16, (B, N, dI))
+    """Stages 1-3 fused (bf16 or fp8 e4m3fn inputs).  -> idx [B,G,T,k] int32
+    (ascending, -1 padded)."""
+    B, T, G, dI, N, sfx = _index_inputs(qI, kI)
     d = dims(B, T, N, G, G, k, d_I=dI)
     idx = out if out is not None else torch.empty(B, G, T, k, dtype=torch.int32, device=qI.device)
     _need(idx, "idx", torch.int32, (B, G, T, k))
     ws, nbytes = _workspace(OP_SELECT_BLOCKS, d, workspace)
-    _check(lib().msa_select_blocks(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(idx), _ptr(ws),
-                                   nbytes, _stream()), "msa_select_blocks")
+    name = "msa_select_blocks" + sfx
+    _check(getattr(lib(), name)(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(idx), _ptr(ws),
+                                nbytes, _stream()), name)
     return idx
 
 

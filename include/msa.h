@@ -106,6 +106,26 @@ int msa_select_blocks(const msa_dims_t *dims, const void *qI, const void *kI,
                       int32_t *idx, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The index branch (stages 1+2, and 1-3 fused) on 8-bit inputs.  The pages'
+ * kernel co-design section (the Italian news page on MSA, last paragraph)
+ * lists FP8 among the precisions of the authors' kernel; the definitions are
+ * unchanged: s = (q^I . k^I) / sqrt(d_I) with the products and sums in fp32,
+ * then the same block max and selection rules as msa_index_scores and
+ * msa_select_blocks.
+ *   qI  fp8 e4m3 (OCP e4m3fn: bias 7, no infinities) [B, T, G, d_I], one byte
+ *       per value
+ *   kI  fp8 e4m3 [B, N, d_I]
+ *   S, idx, ws, ws_bytes, errors: as for the bf16 calls (the decode workspace
+ *       is the same msa_workspace_bytes(MSA_OP_SELECT_BLOCKS))
+ * Integer-valued inputs with |dot| < 2^24 are exact in any summation order,
+ * so on such inputs S and idx equal the bf16 calls' on the same values.
+ */
+int msa_index_scores_fp8(const msa_dims_t *dims, const void *qI, const void *kI,
+                         float *S, void *stream);
+int msa_select_blocks_fp8(const msa_dims_t *dims, const void *qI, const void *kI,
+                          int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Stage 3 alone, from materialised block scores (study notes section 2-3,
  * the TopK equation; section 3-5 "Exp-free Top-k": only the order of raw
  * scores matters, no max/exp/sum).

@@ -58,6 +58,17 @@ def bits(x) -> np.ndarray:
     return x.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def codes(x) -> np.ndarray:
+    """fp8 e4m3fn torch tensor (any device) or uint8 array -> contiguous uint8
+    numpy codes."""
+    import torch
+    if isinstance(x, np.ndarray):
+        assert x.dtype == np.uint8
+        return np.ascontiguousarray(x)
+    assert x.dtype == torch.float8_e4m3fn
+    return x.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
 def _rows(row_b, row_t):
     rb = np.ascontiguousarray(np.asarray(row_b, dtype=np.int64))
     rt = np.ascontiguousarray(np.asarray(row_t, dtype=np.int64))
@@ -79,10 +90,12 @@ class OracleLib:
         i64 = ctypes.c_int64
         lib.msa_oracle_threads.restype = ctypes.c_int
         lib.msa_oracle_block_scores.argtypes = [ctypes.POINTER(Dims), i64, P, P, P, P, P]
+        lib.msa_oracle_block_scores_fp8.argtypes = [ctypes.POINTER(Dims), i64, P, P, P, P, P]
+        lib.msa_oracle_e4m3_values.argtypes = [P]
         lib.msa_oracle_select.argtypes = [ctypes.POINTER(Dims), i64, P, P, P]
         lib.msa_oracle_attend.argtypes = [ctypes.POINTER(Dims), i64, P, P, P, P, P, P, P, P]
-        for f in (lib.msa_oracle_block_scores, lib.msa_oracle_select,
-                  lib.msa_oracle_attend):
+        for f in (lib.msa_oracle_block_scores, lib.msa_oracle_block_scores_fp8,
+                  lib.msa_oracle_e4m3_values, lib.msa_oracle_select, lib.msa_oracle_attend):
             f.restype = None
         self.lib = lib
         self.path = path
@@ -104,6 +117,28 @@ class OracleLib:
         self.lib.msa_oracle_block_scores(ctypes.byref(d), n, _ptr(rb), _ptr(rt),
                                          _ptr(q), _ptr(kk), _ptr(S))
         return S
+
+    def block_scores_fp8(self, d: Dims, row_b, row_t, qI_rows, kI) -> np.ndarray:
+        """Stages 1+2 on fp8 E4M3 codes.  qI_rows [n, G, d_I], kI [B, N, d_I]
+        (uint8 numpy arrays or float8_e4m3fn tensors) -> S [n, G, NB]."""
+        rb, rt = _rows(row_b, row_t)
+        q = codes(qI_rows)
+        kk = codes(kI)
+        n = rb.size
+        NB = (d.N + d.Bk - 1) // d.Bk
+        assert q.shape == (n, d.G, d.d_I), q.shape
+        assert kk.shape == (d.B, d.N, d.d_I), kk.shape
+        assert ((rt >= 0) & (rt < d.T) & (rb >= 0) & (rb < d.B)).all()
+        S = np.empty((n, d.G, NB), dtype=np.float64)
+        self.lib.msa_oracle_block_scores_fp8(ctypes.byref(d), n, _ptr(rb), _ptr(rt),
+                                             _ptr(q), _ptr(kk), _ptr(S))
+        return S
+
+    def e4m3_values(self) -> np.ndarray:
+        """The oracle's value of each of the 256 E4M3 codes."""
+        out = np.empty(256, dtype=np.float64)
+        self.lib.msa_oracle_e4m3_values(_ptr(out))
+        return out
 
     def select(self, d: Dims, row_t, S) -> np.ndarray:
         """Stage 3.  S [n, G, NB] fp64 -> idx [n, G, k] int32."""
@@ -202,3 +237,11 @@ def s_as_fp32(S: np.ndarray) -> np.ndarray:
     """fp32 value of S as the HIP path reports it: the fp32 nearest to the
     exact score (numpy's round-to-nearest-even cast of the fp64 score)."""
     return S.astype(np.float32)
+
+
+def block_scores_fp8(*a, **kw):
+    return default().block_scores_fp8(*a, **kw)
+
+
+def e4m3_values():
+    return default().e4m3_values()

@@ -42,8 +42,10 @@
  *   - a block that is not yet visible scores -inf and is never a candidate;
  *     the local block's S is its true causal max (selection ignores it).
  *
- * Inputs are the raw bf16 bit patterns (uint16); they are widened to fp64
- * exactly.  Row-subset mode: every function works on a caller-chosen list of
+ * Inputs are the raw bf16 bit patterns (uint16), or for the index branch's
+ * 8-bit variant the OCP E4M3 codes (one byte; the Italian news page on MSA,
+ * "Co-Design Del Kernel", lists FP8 among the authors' kernel precisions);
+ * either is widened to fp64 exactly.  Row-subset mode: every function works on a caller-chosen list of
  * (b, t) query rows so that very long workloads can be checked on a sample.
  */
 #include <math.h>
@@ -86,13 +88,39 @@ int msa_oracle_threads(void)
 #endif
 }
 
-/* Stages 1 and 2.  S[r, g, blk] for every listed row r = (row_b[r], row_t[r]).
- * qI_rows: [nrows, G, d_I] (the q^I vectors of the listed rows only),
- * kI: [B, N, d_I]. */
-void msa_oracle_block_scores(const msa_oracle_dims *d, int64_t nrows,
-                             const int64_t *row_b, const int64_t *row_t,
-                             const uint16_t *qI_rows, const uint16_t *kI,
-                             double *S)
+/* One OCP 8-bit E4M3 value (the "fp8" of the index branch variant): sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes
+ * subnormals M * 2^-9; exponent 15 with mantissa 7 is NaN and there is no
+ * infinity. */
+static double widen_e4m3(uint8_t code)
+{
+    const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+static double elem_bf16(const void *base, int64_t i)
+{
+    return widen_bf16(((const uint16_t *)base)[i]);
+}
+
+static double elem_e4m3(const void *base, int64_t i)
+{
+    return widen_e4m3(((const uint8_t *)base)[i]);
+}
+
+/* Stages 1 and 2 for element format `elem`.  S[r, g, blk] for every listed
+ * row r = (row_b[r], row_t[r]).  qI_rows: [nrows, G, d_I] (the q^I vectors
+ * of the listed rows only), kI: [B, N, d_I]. */
+static void block_scores(const msa_oracle_dims *d, int64_t nrows, const int64_t *row_b,
+                         const int64_t *row_t, const void *qI_rows, const void *kI,
+                         double (*elem)(const void *, int64_t), double *S)
 {
     const int64_t NB = block_count(d);
     const double root = sqrt((double)d->d_I);
@@ -102,18 +130,17 @@ void msa_oracle_block_scores(const msa_oracle_dims *d, int64_t nrows,
         const int64_t r = rg / G, g = rg % G;
         const int64_t b = row_b[r];
         const int64_t p = position_of(d, row_t[r]);
-        const uint16_t *qv = qI_rows + (r * G + g) * dI;
         double *out = S + (r * G + g) * NB;
         double *qd = (double *)malloc(sizeof(double) * dI);
         for (int64_t c = 0; c < dI; ++c)
-            qd[c] = widen_bf16(qv[c]);
+            qd[c] = elem(qI_rows, (r * G + g) * dI + c);
         for (int64_t blk = 0; blk < NB; ++blk)
             out[blk] = -INFINITY;
         for (int64_t j = 0; j <= p; ++j) {
-            const uint16_t *kv = kI + (b * d->N + j) * dI;
+            const int64_t kbase = (b * d->N + j) * dI;
             double dot = 0.0;
             for (int64_t c = 0; c < dI; ++c)
-                dot += qd[c] * widen_bf16(kv[c]);
+                dot += qd[c] * elem(kI, kbase + c);
             const double s = dot / root;
             const int64_t blk = j / d->Bk;
             if (s > out[blk])
@@ -121,6 +148,30 @@ void msa_oracle_block_scores(const msa_oracle_dims *d, int64_t nrows,
         }
         free(qd);
     }
+}
+
+/* Stages 1 and 2 on bf16 inputs (uint16 bit patterns). */
+void msa_oracle_block_scores(const msa_oracle_dims *d, int64_t nrows,
+                             const int64_t *row_b, const int64_t *row_t,
+                             const uint16_t *qI_rows, const uint16_t *kI,
+                             double *S)
+{
+    block_scores(d, nrows, row_b, row_t, qI_rows, kI, elem_bf16, S);
+}
+
+/* Stages 1 and 2 on fp8 E4M3 inputs (one byte per value). */
+void msa_oracle_block_scores_fp8(const msa_oracle_dims *d, int64_t nrows,
+                                 const int64_t *row_b, const int64_t *row_t,
+                                 const uint8_t *qI_rows, const uint8_t *kI, double *S)
+{
+    block_scores(d, nrows, row_b, row_t, qI_rows, kI, elem_e4m3, S);
+}
+
+/* The value of each of the 256 E4M3 codes (for the oracle's own checks). */
+void msa_oracle_e4m3_values(double *out)
+{
+    for (int c = 0; c < 256; ++c)
+        out[c] = widen_e4m3((uint8_t)c);
 }
 
 /* Stage 3.  idx[r, g, 0..k-1] from S[r, g, 0..NB-1]. */

@@ -414,6 +414,39 @@ def pin_decode_is_last_prefill_row(orc):
     assert np.array_equal(full["O"], dec["O"])
 
 
+def pin_e4m3_codes(orc):
+    """The 8-bit E4M3 decoder against torch's float8_e4m3fn conversion for all
+    256 codes (a library routine), and a few codes checked by hand from the
+    format: 0x38 = 1, 0xB8 = -1, 0x7E = 448 (largest finite), 0x08 = 2^-6
+    (smallest normal), 0x01 = 2^-9 (smallest subnormal), 0x7F / 0xFF NaN."""
+    vals = orc.e4m3_values()
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ref = ref.to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(vals), nan)
+    assert np.array_equal(vals[~nan], ref[~nan])
+    hand = {0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+            0x00: 0.0, 0x40: 2.0, 0x44: 3.0, 0x48: 4.0, 0xC8: -4.0}
+    for c, v in hand.items():
+        assert vals[c] == v, (hex(c), vals[c], v)
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF])
+
+
+def pin_fp8_scores_match_bf16_on_integers(orc):
+    """Integers in [-4, 4] are exact in both bf16 and E4M3, so the 8-bit
+    index branch must give the same block scores as the bf16 one."""
+    B, T, N, G, dI, Bk = 2, 45, 70, 3, 16, 8
+    g = _gen(31)
+    qI = _int_bf16(g, (B, T, G, dI))
+    kI = _int_bf16(g, (B, N, dI))
+    d = dims_of(B, T, N, G, G, 16, dI, Bk, 4)
+    rb, rt = _all_rows(B, T)
+    S16 = orc.block_scores(d, rb, rt, qI[rb, rt], kI)
+    S8 = orc.block_scores_fp8(d, rb, rt, qI.float().to(torch.float8_e4m3fn)[rb, rt],
+                              kI.float().to(torch.float8_e4m3fn))
+    assert np.array_equal(S16, S8)
+
+
 ALL_PINS = [
     pin_scores_brute_force,
     pin_scores_zero_keys,
@@ -428,4 +461,6 @@ ALL_PINS = [
     pin_attend_k1_block_diagonal,
     pin_attend_closed_forms,
     pin_decode_is_last_prefill_row,
+    pin_e4m3_codes,
+    pin_fp8_scores_match_bf16_on_integers,
 ]

@@ -57,6 +57,13 @@ MUTATIONS = [
      "if (blk <= 0)\n                continue;"),
     ("widen_wrong_shift", "uint32_t u = (uint32_t)bits << 16;",
      "uint32_t u = (uint32_t)bits << 15;"),
+    ("e4m3_wrong_bias", "v = ldexp(1.0 + m / 8.0, e - 7);", "v = ldexp(1.0 + m / 8.0, e - 8);"),
+    ("e4m3_subnormal_as_normal", "v = ldexp((double)m, -9);", "v = ldexp(1.0 + m / 8.0, -7);"),
+    ("e4m3_mantissa_halved", "v = ldexp(1.0 + m / 8.0, e - 7);",
+     "v = ldexp(1.0 + m / 16.0, e - 7);"),
+    ("e4m3_sign_dropped", "return sign ? -v : v;", "return v;"),
+    ("fp8_scores_use_bf16_decoder", "block_scores(d, nrows, row_b, row_t, qI_rows, kI, elem_e4m3, S);",
+     "block_scores(d, nrows, row_b, row_t, qI_rows, kI, elem_bf16, S);"),
 ]
 
 _RUNNER = r"""
