@@ -99,7 +99,18 @@ index_tile_kernel(TileArgs a) {
   constexpr int PITCH = F8 ? 144 : 256;     // LDS row pitch
   constexpr int PF = 128 * CPR / NT;        // 16-B chunks per thread per block
   static_assert(PF * NT == 128 * CPR, "block chunks must split evenly over the threads");
-  __shared__ __align__(16) unsigned char kbuf[2][128 * PITCH];
+  // A ring of R = 2D block buffers with a prefetch distance of D: block kb+D
+  // is loaded into registers while block kb is scored and stored into buffer
+  // (kb+D) % R afterwards; that buffer was last read for block kb-D.  The
+  // workgroup then needs a barrier only after every D-th block (and after the
+  // last): any D consecutive blocks contain one barrier, which both publishes
+  // each stored block before its use (stored D blocks ahead) and is passed by
+  // every wave after it read the block D back before that buffer is reused.
+  // D = 2 for bf16 (4 x 32 KB of LDS), 4 for fp8 (8 x 18 KB); workgroups of
+  // fewer than 8 waves (G < 4) keep D = 1 so that several fit on a CU.
+  constexpr int D = NT < 512 ? 1 : (F8 ? 4 : 2);
+  constexpr int R = 2 * D;
+  __shared__ __align__(16) unsigned char kbuf[R][128 * PITCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -187,17 +198,20 @@ index_tile_kernel(TileArgs a) {
     }
   };
 
-  if (nkb > 0) {
-    load_block(0);
-    store_block(0);
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    if (j < nkb) {
+      load_block(j);
+      store_block(j);
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // q^I fragments and block 0 have landed
+  __builtin_amdgcn_s_waitcnt(0);  // q^I fragments and blocks 0 .. D-1 have landed
   __syncthreads();
 
   for (int64_t kb = 0; kb < nkb; ++kb) {
-    const bool more = kb + 1 < nkb;
-    if (more) load_block(kb + 1);
-    const unsigned char* buf = kbuf[kb & 1];
+    const bool more = kb + D < nkb;
+    if (more) load_block(kb + D);
+    const unsigned char* buf = kbuf[kb & (R - 1)];
     float m0 = -INFINITY, m1 = -INFINITY;
     const bool masked = WRITE_S && (kb == L);
     // One 32-key tile: 8 K fragments from LDS, 16 MFMAs into two column tiles.
@@ -290,8 +304,8 @@ index_tile_kernel(TileArgs a) {
       }
     }
 
-    if (more) store_block((kb + 1) & 1);
-    __syncthreads();
+    if (more) store_block((kb + D) & (R - 1));
+    if ((kb & (D - 1)) == D - 1 || kb + 1 == nkb) __syncthreads();
   }
 
   if (WRITE_S) {

@@ -105,22 +105,26 @@ static double widen_e4m3(uint8_t code)
     return sign ? -v : v;
 }
 
-static double elem_bf16(const void *base, int64_t i)
+/* Widens values [i0, i0 + n) of a bf16 (fp8 == 0) or E4M3 (fp8 != 0) array. */
+static void widen_run(const void *base, int64_t i0, int64_t n, int fp8, double *out)
 {
-    return widen_bf16(((const uint16_t *)base)[i]);
+    if (fp8) {
+        const uint8_t *v = (const uint8_t *)base + i0;
+        for (int64_t c = 0; c < n; ++c)
+            out[c] = widen_e4m3(v[c]);
+    } else {
+        const uint16_t *v = (const uint16_t *)base + i0;
+        for (int64_t c = 0; c < n; ++c)
+            out[c] = widen_bf16(v[c]);
+    }
 }
 
-static double elem_e4m3(const void *base, int64_t i)
-{
-    return widen_e4m3(((const uint8_t *)base)[i]);
-}
-
-/* Stages 1 and 2 for element format `elem`.  S[r, g, blk] for every listed
- * row r = (row_b[r], row_t[r]).  qI_rows: [nrows, G, d_I] (the q^I vectors
- * of the listed rows only), kI: [B, N, d_I]. */
+/* Stages 1 and 2.  S[r, g, blk] for every listed row r = (row_b[r], row_t[r]).
+ * qI_rows: [nrows, G, d_I] (the q^I vectors of the listed rows only),
+ * kI: [B, N, d_I]; bf16 bit patterns, or E4M3 codes when fp8 != 0. */
 static void block_scores(const msa_oracle_dims *d, int64_t nrows, const int64_t *row_b,
                          const int64_t *row_t, const void *qI_rows, const void *kI,
-                         double (*elem)(const void *, int64_t), double *S)
+                         int fp8, double *S)
 {
     const int64_t NB = block_count(d);
     const double root = sqrt((double)d->d_I);
@@ -132,20 +136,21 @@ static void block_scores(const msa_oracle_dims *d, int64_t nrows, const int64_t 
         const int64_t p = position_of(d, row_t[r]);
         double *out = S + (r * G + g) * NB;
         double *qd = (double *)malloc(sizeof(double) * dI);
-        for (int64_t c = 0; c < dI; ++c)
-            qd[c] = elem(qI_rows, (r * G + g) * dI + c);
+        double *kd = (double *)malloc(sizeof(double) * dI);
+        widen_run(qI_rows, (r * G + g) * dI, dI, fp8, qd);
         for (int64_t blk = 0; blk < NB; ++blk)
             out[blk] = -INFINITY;
         for (int64_t j = 0; j <= p; ++j) {
-            const int64_t kbase = (b * d->N + j) * dI;
+            widen_run(kI, (b * d->N + j) * dI, dI, fp8, kd);
             double dot = 0.0;
             for (int64_t c = 0; c < dI; ++c)
-                dot += qd[c] * elem(kI, kbase + c);
+                dot += qd[c] * kd[c];
             const double s = dot / root;
             const int64_t blk = j / d->Bk;
             if (s > out[blk])
                 out[blk] = s;
         }
+        free(kd);
         free(qd);
     }
 }
@@ -156,7 +161,7 @@ void msa_oracle_block_scores(const msa_oracle_dims *d, int64_t nrows,
                              const uint16_t *qI_rows, const uint16_t *kI,
                              double *S)
 {
-    block_scores(d, nrows, row_b, row_t, qI_rows, kI, elem_bf16, S);
+    block_scores(d, nrows, row_b, row_t, qI_rows, kI, 0, S);
 }
 
 /* Stages 1 and 2 on fp8 E4M3 inputs (one byte per value). */
@@ -164,7 +169,7 @@ void msa_oracle_block_scores_fp8(const msa_oracle_dims *d, int64_t nrows,
                                  const int64_t *row_b, const int64_t *row_t,
                                  const uint8_t *qI_rows, const uint8_t *kI, double *S)
 {
-    block_scores(d, nrows, row_b, row_t, qI_rows, kI, elem_e4m3, S);
+    block_scores(d, nrows, row_b, row_t, qI_rows, kI, 1, S);
 }
 
 /* The value of each of the 256 E4M3 codes (for the oracle's own checks). */

@@ -62,8 +62,8 @@ MUTATIONS = [
     ("e4m3_mantissa_halved", "v = ldexp(1.0 + m / 8.0, e - 7);",
      "v = ldexp(1.0 + m / 16.0, e - 7);"),
     ("e4m3_sign_dropped", "return sign ? -v : v;", "return v;"),
-    ("fp8_scores_use_bf16_decoder", "block_scores(d, nrows, row_b, row_t, qI_rows, kI, elem_e4m3, S);",
-     "block_scores(d, nrows, row_b, row_t, qI_rows, kI, elem_bf16, S);"),
+    ("fp8_scores_use_bf16_decoder", "block_scores(d, nrows, row_b, row_t, qI_rows, kI, 1, S);",
+     "block_scores(d, nrows, row_b, row_t, qI_rows, kI, 0, S);"),
 ]
 
 _RUNNER = r"""
