@@ -69,6 +69,28 @@ int check_ptr(const void* p, const char* name) {
   return MSA_OK;
 }
 
+const msa::PagedCache kContiguous = {nullptr, nullptr, 0, 0};
+
+// The page table and lengths of a paged call (device arrays; their contents
+// are the caller's, see msa.h).
+int check_paged(const msa_dims_t* d, int64_t num_pages, const int32_t* table,
+                const int64_t* lens, msa::PagedCache* pc) {
+  if (d->T != 1)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "paged calls are decode only (T == 1, got %lld)",
+                (long long)d->T);
+  if (num_pages < 1 || num_pages > (int64_t(1) << 31))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "num_pages %lld out of range", (long long)num_pages);
+  if (!table || (reinterpret_cast<uintptr_t>(table) & 3))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "block_table is NULL or not 4-byte aligned");
+  if (!lens || (reinterpret_cast<uintptr_t>(lens) & 7))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "seq_lens is NULL or not 8-byte aligned");
+  pc->table = table;
+  pc->lens = lens;
+  pc->pages = num_pages;
+  pc->nb = static_cast<int32_t>((d->N + d->Bk - 1) / d->Bk);
+  return MSA_OK;
+}
+
 #define MSA_TRY(x)               \
   do {                           \
     const int rc_ = (x);         \
@@ -143,7 +165,7 @@ static int index_scores_impl(const msa_dims_t* d, const void* qI, const void* kI
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d->T == 1)
-    e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, st);
+    e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, kContiguous, st);
   else
     e = msa::launch_index_tiles(true, fp8, qI, kI, S, nullptr, d->B, d->T, d->N, d->G, d->k,
                                 st);
@@ -167,8 +189,9 @@ static int select_blocks_impl(const msa_dims_t* d, const void* qI, const void* k
       return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "select needs %zu workspace bytes, got %zu",
                   need, ws_bytes);
     float* S = static_cast<float*>(ws);
-    e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, st);
-    if (e == hipSuccess) e = msa::launch_topk_rows(S, idx, d->B, 1, d->N, d->G, d->k, st);
+    e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, kContiguous, st);
+    if (e == hipSuccess)
+      e = msa::launch_topk_rows(S, idx, d->B, 1, d->N, d->G, d->k, kContiguous, st);
   } else {
     e = msa::launch_index_tiles(false, fp8, qI, kI, nullptr, idx, d->B, d->T, d->N, d->G, d->k,
                                 st);
@@ -203,7 +226,7 @@ int msa_select_blocks_from_scores(const msa_dims_t* d, const float* S, int32_t* 
   MSA_TRY(check_dims(d));
   MSA_TRY(check_ptr(S, "S"));
   MSA_TRY(check_ptr(idx, "idx"));
-  const hipError_t e = msa::launch_topk_rows(S, idx, d->B, d->T, d->N, d->G, d->k,
+  const hipError_t e = msa::launch_topk_rows(S, idx, d->B, d->T, d->N, d->G, d->k, kContiguous,
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_select_blocks_from_scores");
   return MSA_OK;
@@ -266,8 +289,76 @@ int msa_sparse_attn_decode(const msa_dims_t* d, const void* q, const void* K, co
   msa::AttnWorkspace w;
   msa::attn_workspace_carve(ws, d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true, &w);
   const hipError_t e = msa::launch_attn_decode(q, K, V, idx, O, lse, d->B, d->N, d->Hq, d->G,
-                                               d->k, w, static_cast<hipStream_t>(stream));
+                                               d->k, kContiguous, w,
+                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode");
+  return MSA_OK;
+}
+
+static int select_paged_impl(const msa_dims_t* d, const void* qI, const void* kI_pool,
+                             int64_t num_pages, const int32_t* block_table,
+                             const int64_t* seq_lens, int32_t* idx, void* ws, size_t ws_bytes,
+                             void* stream, bool fp8, const char* name) {
+  MSA_TRY(check_dims(d));
+  msa::PagedCache pc;
+  MSA_TRY(check_paged(d, num_pages, block_table, seq_lens, &pc));
+  MSA_TRY(check_ptr(qI, "qI"));
+  MSA_TRY(check_ptr(kI_pool, "kI_pool"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  MSA_TRY(check_ptr(ws, "ws"));
+  const size_t need = decode_select_ws(d);
+  if (ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "select needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* S = static_cast<float*>(ws);
+  hipError_t e = msa::launch_decode_scan(fp8, qI, kI_pool, S, d->B, d->N, d->G, pc, st);
+  if (e == hipSuccess) e = msa::launch_topk_rows(S, idx, d->B, 1, d->N, d->G, d->k, pc, st);
+  if (e != hipSuccess) return hip_fail(e, name);
+  return MSA_OK;
+}
+
+int msa_select_blocks_paged(const msa_dims_t* d, const void* qI, const void* kI_pool,
+                            int64_t num_pages, const int32_t* block_table,
+                            const int64_t* seq_lens, int32_t* idx, void* ws, size_t ws_bytes,
+                            void* stream) {
+  return select_paged_impl(d, qI, kI_pool, num_pages, block_table, seq_lens, idx, ws, ws_bytes,
+                           stream, false, "msa_select_blocks_paged");
+}
+
+int msa_select_blocks_paged_fp8(const msa_dims_t* d, const void* qI, const void* kI_pool,
+                                int64_t num_pages, const int32_t* block_table,
+                                const int64_t* seq_lens, int32_t* idx, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return select_paged_impl(d, qI, kI_pool, num_pages, block_table, seq_lens, idx, ws, ws_bytes,
+                           stream, true, "msa_select_blocks_paged_fp8");
+}
+
+int msa_sparse_attn_decode_paged(const msa_dims_t* d, const void* q, const void* K_pool,
+                                 const void* V_pool, int64_t num_pages,
+                                 const int32_t* block_table, const int64_t* seq_lens,
+                                 const int32_t* idx, void* O, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  MSA_TRY(check_dims(d));
+  msa::PagedCache pc;
+  MSA_TRY(check_paged(d, num_pages, block_table, seq_lens, &pc));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(K_pool, "K_pool"));
+  MSA_TRY(check_ptr(V_pool, "V_pool"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  MSA_TRY(check_ptr(O, "O"));
+  if (lse) MSA_TRY(check_ptr(lse, "lse"));
+  MSA_TRY(check_ptr(ws, "ws"));
+  const size_t need = decode_ws(d);
+  if (ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  msa::AttnWorkspace w;
+  msa::attn_workspace_carve(ws, d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true, &w);
+  const hipError_t e = msa::launch_attn_decode(q, K_pool, V_pool, idx, O, lse, d->B, d->N,
+                                               d->Hq, d->G, d->k, pc, w,
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode_paged");
   return MSA_OK;
 }
 

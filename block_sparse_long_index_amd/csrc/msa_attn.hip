@@ -805,13 +805,14 @@ hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
 // ---------------------------------------------------------------------------
 struct DecArgs {
   const u16* q;        // [B, Hq, 128]
-  const u16* K;        // [B, G, N, 128]
+  const u16* K;        // [B, G, N, 128], or the page pool [pages, G, 128, 128] when paged
   const u16* V;
   const int32_t* idx;  // [B, G, 1, k]
   u16* opart;          // [B, G, k, hg, 128]
   float2* lpart;       // [B, G, k, hg]
-  int64_t N;
+  int64_t N;           // cache capacity (tokens)
   int32_t Hq, G, k;
+  PagedCache pc;
 };
 
 // Key offset 0..31 within a wave's quarter -> its column in that wave's V^T
@@ -842,16 +843,19 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecArgs a) {
   const int g = static_cast<int>(bg % a.G);
   const int64_t b = bg / a.G;
   const int blk = a.idx[bg * a.k + slot];
-  if (blk < 0 || static_cast<int64_t>(blk) * kBlock >= a.N) return;  // unused slot
+  const int64_t len = paged_len(a.pc, b, a.N);  // this sequence's cache length
+  if (blk < 0 || static_cast<int64_t>(blk) * kBlock >= len) return;  // unused slot
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, qd = lane >> 4;
   const int64_t kblk = static_cast<int64_t>(blk) * kBlock;
   // keys of the block inside the sequence (>= 1); loads clamp to the last of
   // them, and this wave's quarter holds nvalid of them (<= 0: none)
-  const int nblk = static_cast<int>(a.N - kblk < kBlock ? a.N - kblk : kBlock);
+  const int nblk = static_cast<int>(len - kblk < kBlock ? len - kblk : kBlock);
   const int nvalid = nblk - 32 * wave < 32 ? nblk - 32 * wave : 32;
-  const u16* Kb = a.K + (bg * a.N + kblk) * kHeadDim;
-  const u16* Vb = a.V + (bg * a.N + kblk) * kHeadDim;
+  const int64_t row0 = a.pc.table ? (paged_page(a.pc, b, blk) * a.G + g) * kBlock
+                                  : bg * a.N + kblk;  // first key row of the block
+  const u16* Kb = a.K + row0 * kHeadDim;
+  const u16* Vb = a.V + row0 * kHeadDim;
   auto krow = [&](int kk) { return (32 * wave + kk < nblk ? 32 * wave + kk : nblk - 1) * kHeadDim; };
   unsigned char* vt = lds + wave * 8192;
 
@@ -999,9 +1003,11 @@ static hipError_t launch_decode_t(const DecArgs& da, const CombArgs& ca, int64_t
 
 hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse, int64_t B, int64_t N,
-                              int Hq, int G, int k, const AttnWorkspace& w, hipStream_t st) {
+                              int Hq, int G, int k, const PagedCache& pc,
+                              const AttnWorkspace& w, hipStream_t st) {
   const int hg = Hq / G;
   DecArgs da;
+  da.pc = pc;
   da.q = static_cast<const u16*>(q);
   da.K = static_cast<const u16*>(K);
   da.V = static_cast<const u16*>(V);

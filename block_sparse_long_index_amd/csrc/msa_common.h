@@ -1,6 +1,8 @@
 // msa_common.h -- device helpers shared by the MSA kernels (gfx950 only).
 #pragma once
 
+#include "msa_internal.h"
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -102,6 +104,20 @@ __device__ __forceinline__ f32x4 mfma16_f8(i32x8 a, i32x8 b, f32x4 c) {
 // positions, which covers all LDS banks once.
 __device__ __forceinline__ int swz(int r, int c) {
   return (r << 8) + ((c ^ (r & 15)) << 4);
+}
+
+// Paged decode caches (PagedCache, msa_internal.h): lengths are clamped to
+// [1, cap] and page ids to [0, pages - 1], so that bad table contents give
+// wrong results but never an access outside the pool.
+__device__ __forceinline__ int64_t paged_len(const PagedCache& pc, int64_t b, int64_t cap) {
+  if (!pc.table) return cap;
+  const int64_t n = pc.lens[b];
+  return n < 1 ? 1 : (n > cap ? cap : n);
+}
+
+__device__ __forceinline__ int64_t paged_page(const PagedCache& pc, int64_t b, int64_t j) {
+  const int64_t pg = pc.table[b * pc.nb + j];
+  return pg < 0 ? 0 : (pg >= pc.pages ? pc.pages - 1 : pg);
 }
 
 __device__ __forceinline__ float max3(float a, float b, float c) {

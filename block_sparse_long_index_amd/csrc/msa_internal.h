@@ -6,6 +6,17 @@
 
 namespace msa {
 
+// A paged cache for decode: 128-token pages in a pool of `pages`; sequence
+// b's logical block j lives in page table[b * nb + j] and the sequence holds
+// lens[b] tokens.  table == nullptr: the contiguous layout, every sequence as
+// long as the capacity.  Both arrays are device memory.
+struct PagedCache {
+  const int32_t* table;
+  const int64_t* lens;
+  int64_t pages;
+  int32_t nb;  // table row length (blocks of capacity)
+};
+
 // Stages 1+2 (write S) or stages 1-3 fused (write idx) for T > 1; fp8: q^I and
 // k^I are e4m3 bytes instead of bf16.
 hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const void* kI,
@@ -14,11 +25,12 @@ hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const
 
 // Stages 1+2 for T == 1: streams the index keys, S is [B, G, 1, NB].
 hipError_t launch_decode_scan(bool fp8, const void* qI, const void* kI, float* S,
-                              int64_t B, int64_t N, int G, hipStream_t st);
+                              int64_t B, int64_t N, int G, const PagedCache& pc,
+                              hipStream_t st);
 
 // Stage 3 from S [B, G, T, NB] (one wave per row).
 hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
-                            int64_t N, int G, int k, hipStream_t st);
+                            int64_t N, int G, int k, const PagedCache& pc, hipStream_t st);
 
 struct AttnWorkspace {
   int32_t* hist;       // [G * NB * nc]: unit block counts, then exclusive offsets
@@ -54,6 +66,6 @@ hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
 hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse,
                               int64_t B, int64_t N, int Hq, int G, int k,
-                              const AttnWorkspace& w, hipStream_t st);
+                              const PagedCache& pc, const AttnWorkspace& w, hipStream_t st);
 
 }  // namespace msa

@@ -408,10 +408,11 @@ hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const
 // ---------------------------------------------------------------------------
 struct ScanArgs {
   const u16* qI;
-  const u16* kI;
+  const u16* kI;  // [B, N, 128], or the page pool [pages, 128, 128] when paged
   float* S;
-  int64_t N;
+  int64_t N;      // cache capacity (tokens)
   int32_t NB, G;
+  PagedCache pc;
 };
 
 // F8: e4m3 inputs; one 16x16x128 MFMA covers 16 keys x all 128 dims (lane
@@ -435,17 +436,27 @@ __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(col < a.G ? ld16(qsrc + 64 * s + 16 * qd) : z);
   }
-  const unsigned char* kbase =
-      reinterpret_cast<const unsigned char*>(a.kI) + static_cast<int64_t>(b) * a.N * ROWB;
   {
     const int64_t kb = static_cast<int64_t>(blockIdx.x) * 4 + wave;
     if (kb >= a.NB) return;
+    // this sequence's length (paged: its own) and the block's keys inside it
+    const int64_t len = paged_len(a.pc, b, a.N);
+    float* srow = a.S + static_cast<int64_t>(b) * a.G * a.NB + kb;
+    if (kb * kBlock >= len) {  // past the end of this sequence: invisible
+      if (lane < a.G) srow[static_cast<int64_t>(lane) * a.NB] = -INFINITY;
+      return;
+    }
+    const int nvalid = static_cast<int>(len - kb * kBlock < kBlock ? len - kb * kBlock : kBlock);
+    const unsigned char* kblk = reinterpret_cast<const unsigned char*>(a.kI) +
+                                (a.pc.table ? paged_page(a.pc, b, kb) * kBlock
+                                            : static_cast<int64_t>(b) * a.N + kb * kBlock) *
+                                    ROWB;
     constexpr int LPK = F8 ? 2 : 4;  // 16-B loads per key row and lane
     uint4 d[8][LPK];
 #pragma unroll
     for (int kg = 0; kg < 8; ++kg) {
-      const int64_t key = kb * kBlock + kg * 16 + col;
-      const unsigned char* src = kbase + (key < a.N ? key : a.N - 1) * ROWB;
+      const int kk = kg * 16 + col;
+      const unsigned char* src = kblk + (kk < nvalid ? kk : nvalid - 1) * ROWB;
 #pragma unroll
       for (int s = 0; s < LPK; ++s)  // tail keys masked below
         d[kg][s] = F8 ? ld16(src + 32 * qd + 16 * s) : ld16(src + 64 * s + 16 * qd);
@@ -462,21 +473,23 @@ __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t key = kb * kBlock + kg * 16 + 4 * qd + r;
-        m = fmaxf(m, key < a.N ? acc[r] : -INFINITY);
+        const int kk = kg * 16 + 4 * qd + r;
+        m = fmaxf(m, kk < nvalid ? acc[r] : -INFINITY);
       }
     }
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
     if (lane < a.G)
-      a.S[(static_cast<int64_t>(b) * a.G + lane) * a.NB + kb] =
+      srow[static_cast<int64_t>(lane) * a.NB] =
           static_cast<float>(static_cast<double>(m) * kInvSqrt128);
   }
 }
 
 hipError_t launch_decode_scan(bool fp8, const void* qI, const void* kI, float* S,
-                              int64_t B, int64_t N, int G, hipStream_t st) {
+                              int64_t B, int64_t N, int G, const PagedCache& pc,
+                              hipStream_t st) {
   ScanArgs a;
+  a.pc = pc;
   a.qI = static_cast<const u16*>(qI);
   a.kI = static_cast<const u16*>(kI);
   a.S = S;
@@ -506,7 +519,8 @@ struct TopkArgs {
   const float* S;
   int32_t* idx;
   int64_t T, N, rows;
-  int32_t NB, k;
+  int32_t NB, k, G;
+  PagedCache pc;  // per-sequence lengths when paged (T == 1)
 };
 
 __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
@@ -672,7 +686,7 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (row >= a.rows) return;
   const int64_t t = row % a.T;
-  const int64_t L = (a.N - a.T + t) / kBlock;
+  const int64_t L = (paged_len(a.pc, row / (a.T * a.G), a.N) - a.T + t) / kBlock;
   const int m = static_cast<int>(L < a.k - 1 ? L : a.k - 1);
   int32_t* out = a.idx + row * a.k;
   if (m == 0) {
@@ -696,7 +710,7 @@ __global__ void __launch_bounds__(256) topk_wide_kernel(TopkArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.x;
   const int64_t t = row % a.T;
-  const int64_t L = (a.N - a.T + t) / kBlock;
+  const int64_t L = (paged_len(a.pc, row / (a.T * a.G), a.N) - a.T + t) / kBlock;
   const int m = static_cast<int>(L < a.k - 1 ? L : a.k - 1);
   int32_t* out = a.idx + row * a.k;
   if (m == 0) {
@@ -720,8 +734,10 @@ __global__ void __launch_bounds__(256) topk_wide_kernel(TopkArgs a) {
 }
 
 hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
-                            int64_t N, int G, int k, hipStream_t st) {
+                            int64_t N, int G, int k, const PagedCache& pc, hipStream_t st) {
   TopkArgs a;
+  a.G = G;
+  a.pc = pc;
   a.S = S;
   a.idx = idx;
   a.T = T;

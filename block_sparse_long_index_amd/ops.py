@@ -35,6 +35,12 @@ _SIGS = {
                                                ctypes.c_size_t, _P]),
     "msa_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
+    "msa_select_blocks_paged": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, _P, _P, _P, _P,
+                                               ctypes.c_size_t, _P]),
+    "msa_select_blocks_paged_fp8": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, _P, _P, _P, _P,
+                                                   ctypes.c_size_t, _P]),
+    "msa_sparse_attn_decode_paged": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, _P, _P,
+                                                    _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _P]),
     "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "msa_last_error": (ctypes.c_char_p, []),
@@ -225,3 +231,63 @@ def forward(qI, kI, q, K, V, k, return_lse=False):
     else:
         res = sparse_attn_prefill(q, K, V, idx, return_lse=return_lse)
     return idx, res
+
+
+# ------------------------------------------------------------- paged decode
+def _paged_args(block_table, seq_lens, B):
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int64, (B,))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, blocks], got %s" % (tuple(block_table.shape),))
+    return block_table.shape[1] * 128  # capacity in tokens
+
+
+def select_blocks_paged(qI, kI_pool, block_table, seq_lens, k, out=None, workspace=None):
+    """Decode block selection over a paged index-key pool.  qI [B, G, 128]
+    (bf16 or fp8 e4m3fn), kI_pool [pages, 128, 128] of the same dtype,
+    block_table int32 [B, nb], seq_lens int64 [B] -> idx [B, G, 1, k]."""
+    if qI.dtype not in _INDEX_DTYPES:
+        raise ValueError("qI must be bfloat16 or float8_e4m3fn, got %s" % qI.dtype)
+    B, G, dI = qI.shape
+    _need(qI, "qI", qI.dtype)
+    _need(kI_pool, "kI_pool", qI.dtype)
+    if kI_pool.dim() != 3 or tuple(kI_pool.shape[1:]) != (128, dI):
+        raise ValueError("kI_pool must be [pages, 128, %d], got %s" % (dI, tuple(kI_pool.shape)))
+    N = _paged_args(block_table, seq_lens, B)
+    d = dims(B, 1, N, G, G, k, d_I=dI)
+    idx = out if out is not None else torch.empty(B, G, 1, k, dtype=torch.int32, device=qI.device)
+    _need(idx, "idx", torch.int32, (B, G, 1, k))
+    ws, nbytes = _workspace(OP_SELECT_BLOCKS, d, workspace)
+    name = "msa_select_blocks_paged" + _INDEX_DTYPES[qI.dtype]
+    _check(getattr(lib(), name)(ctypes.byref(d), _ptr(qI), _ptr(kI_pool), kI_pool.shape[0],
+                                _ptr(block_table), _ptr(seq_lens), _ptr(idx), _ptr(ws), nbytes,
+                                _stream()), name)
+    return idx
+
+
+def sparse_attn_decode_paged(q, K_pool, V_pool, block_table, seq_lens, idx, out=None,
+                             lse=None, return_lse=False, workspace=None):
+    """Decode attention over paged K/V pools.  q [B, Hq, 128] bf16, K_pool /
+    V_pool [pages, G, 128, 128] bf16, block_table int32 [B, nb], seq_lens int64
+    [B], idx [B, G, 1, k] -> O [B, Hq, 128] (and lse [B, Hq])."""
+    B, Hq, dh = q.shape
+    P, G = K_pool.shape[0], K_pool.shape[1]
+    _need(q, "q", torch.bfloat16)
+    _need(K_pool, "K_pool", torch.bfloat16, (P, G, 128, dh))
+    _need(V_pool, "V_pool", torch.bfloat16, (P, G, 128, dh))
+    k = idx.shape[-1]
+    _need(idx, "idx", torch.int32, (B, G, 1, k))
+    N = _paged_args(block_table, seq_lens, B)
+    d = dims(B, 1, N, Hq, G, k, d_h=dh)
+    O = out if out is not None else torch.empty_like(q)
+    _need(O, "O", torch.bfloat16, (B, Hq, dh))
+    if return_lse and lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq))
+    ws, nbytes = _workspace(OP_ATTN_DECODE, d, workspace)
+    _check(lib().msa_sparse_attn_decode_paged(
+        ctypes.byref(d), _ptr(q), _ptr(K_pool), _ptr(V_pool), P, _ptr(block_table),
+        _ptr(seq_lens), _ptr(idx), _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()),
+        "msa_sparse_attn_decode_paged")
+    return (O, lse) if return_lse else O

@@ -176,6 +176,42 @@ int msa_sparse_attn_decode(const msa_dims_t *dims, const void *q,
                            void *O, float *lse, void *ws, size_t ws_bytes,
                            void *stream);
 
+/*
+ * Decode over paged caches: the explicit per-sequence position -> cell ->
+ * block map that the llama.cpp analysis page (section 4 on kv_unified and its
+ * dense fallback, section 5 on what to build) asks for, so that sequences of
+ * different lengths share one cache pool.  Token i of sequence b lives in
+ * row i % Bk of page block_table[b][i / Bk]; sequence b holds seq_lens[b]
+ * tokens, the last of which is the query's own (position seq_lens[b] - 1).
+ * Everything else is the contiguous calls' definition for that sequence.
+ *   dims          T == 1; N = the table's capacity in tokens (every
+ *                 seq_lens[b] <= N); the table has ceil(N / Bk) columns
+ *   num_pages     pages in each pool (1 .. 2^31)
+ *   block_table   int32 [B, ceil(N / Bk)], device; page ids in [0, num_pages)
+ *   seq_lens      int64 [B], device; in [1, N]
+ *   kI_pool       bf16 (fp8 e4m3 for _fp8) [num_pages, Bk, d_I]
+ *   K_pool/V_pool bf16 [num_pages, G, Bk, d_h]
+ *   qI, q, idx, O, lse, ws: as for msa_select_blocks / msa_sparse_attn_decode
+ *                 (the same workspace sizes)
+ * The table and lengths are device data and are not validated on the host:
+ * lengths are clamped to [1, N] and page ids to [0, num_pages) inside the
+ * kernels, so bad contents give wrong results but no access outside the
+ * pools.  Table columns at or past a sequence's last block are never read.
+ */
+int msa_select_blocks_paged(const msa_dims_t *dims, const void *qI, const void *kI_pool,
+                            int64_t num_pages, const int32_t *block_table,
+                            const int64_t *seq_lens, int32_t *idx, void *ws, size_t ws_bytes,
+                            void *stream);
+int msa_select_blocks_paged_fp8(const msa_dims_t *dims, const void *qI, const void *kI_pool,
+                                int64_t num_pages, const int32_t *block_table,
+                                const int64_t *seq_lens, int32_t *idx, void *ws,
+                                size_t ws_bytes, void *stream);
+int msa_sparse_attn_decode_paged(const msa_dims_t *dims, const void *q, const void *K_pool,
+                                 const void *V_pool, int64_t num_pages,
+                                 const int32_t *block_table, const int64_t *seq_lens,
+                                 const int32_t *idx, void *O, float *lse, void *ws,
+                                 size_t ws_bytes, void *stream);
+
 /* Scratch bytes an operation needs for these dims (0 if none); 0 also for
  * invalid dims.  Host only, no HIP call. */
 size_t msa_workspace_bytes(int op, const msa_dims_t *dims);

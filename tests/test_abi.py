@@ -22,7 +22,7 @@ def _declared():
 def test_header_functions_are_exported():
     L = ops.lib()
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(ops._SIGS)
@@ -121,3 +121,27 @@ def test_status_strings():
     for c in (0, -1, -2, -3, -4):
         assert L.msa_status_string(c)
     assert L.msa_status_string(12345) == b"unknown status"
+
+
+def test_paged_argument_checks():
+    L = ops.lib()
+    d = _good(T=1)
+    P = ctypes.c_int64
+    good = dict(lens=ctypes.c_void_p(0x1008))
+    # host-side rejections, before any HIP call (no call here may pass them:
+    # it would launch kernels)
+    dp = _good(T=2)
+    assert L.msa_select_blocks_paged(ctypes.byref(dp), FAKE, FAKE, P(4), FAKE, good["lens"],
+                                     FAKE, FAKE, 1 << 30, None) == -1
+    assert b"decode only" in L.msa_last_error()
+    assert L.msa_select_blocks_paged(ctypes.byref(d), FAKE, FAKE, P(0), FAKE, good["lens"],
+                                     FAKE, FAKE, 1 << 30, None) == -1
+    assert L.msa_select_blocks_paged(ctypes.byref(d), FAKE, FAKE, P(4), None, good["lens"],
+                                     FAKE, FAKE, 1 << 30, None) == -1
+    assert L.msa_select_blocks_paged_fp8(ctypes.byref(d), FAKE, FAKE, P(4), FAKE,
+                                         ctypes.c_void_p(0x1004), FAKE, FAKE, 1 << 30, None) == -1
+    assert b"seq_lens" in L.msa_last_error()
+    assert L.msa_sparse_attn_decode_paged(ctypes.byref(d), FAKE, FAKE, FAKE, P(4), FAKE,
+                                          good["lens"], FAKE, FAKE, None, FAKE, 16, None) == -3
+    assert L.msa_sparse_attn_decode_paged(ctypes.byref(dp), FAKE, FAKE, FAKE, P(4), FAKE,
+                                          good["lens"], FAKE, FAKE, None, FAKE, 1 << 30, None) == -1
