@@ -19,7 +19,8 @@
 
 namespace msa {
 
-constexpr int kChunkQueries = 64;  // queries per work chunk (rows = 64 * hg)
+constexpr int kChunkQueries = 64;  // queries per work chunk (rows = kChunkQueries * hg)
+static_assert(kChunkQueries % 64 == 0, "a chunk's entries fill whole wave registers");
 constexpr int kScanTile = 4096;    // elements per workgroup in the offset scan
 
 static inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -384,9 +385,13 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
     v1r[j] = k0 + 1 < nvalid ? x1 : make_uint4(0, 0, 0, 0);
   }
 
-  // The chunk's (at most 64) entries live in one register per lane; a row
-  // fetches its entry with a lane shuffle.
-  const int ent = lane < n ? a.entries[ch.y + lane] : 0;
+  // The chunk's entries live in kChunkQueries / 64 registers per lane; a row
+  // fetches its entry with lane shuffles.
+  constexpr int kEntRegs = kChunkQueries / 64;
+  int ent[kEntRegs];
+#pragma unroll
+  for (int r = 0; r < kEntRegs; ++r)
+    ent[r] = lane + 64 * r < n ? a.entries[ch.y + lane + 64 * r] : 0;
   const int rows = n * HG;
   // Window rows are rows t0 .. t0+W-1 of sequence b (r0 = b*T + t0), so a
   // row's query index is t0 + rl and everything fits 32-bit offsets except
@@ -397,7 +402,13 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
   auto row_of = [&](int pass, bool& valid, int& hh, int& slot, int& rl, int& p, const u16*& q) {
     const int rr = pass * 128 + wave * 32 + l32;
     valid = rr < rows;
-    const int e = __shfl(ent, valid ? rr / HG : 0);
+    const int qi = valid ? rr / HG : 0;
+    int e = __shfl(ent[0], qi & 63);
+#pragma unroll
+    for (int r = 1; r < kEntRegs; ++r) {
+      const int er = __shfl(ent[r], qi & 63);
+      if ((qi >> 6) == r) e = er;
+    }
     hh = rr % HG;
     rl = e >> 4;
     slot = e & 15;
@@ -617,7 +628,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
 #pragma unroll
     for (int q = 0; q < PPL; ++q) {
       const int pc = li * PPL + q, j = pc >> 1, hf = pc & 1;
-      raw[s][q] = ld16(src + j * 16 * HG + (hf * HG + hh) * 8);
+      raw[s][q] = ld16_once(src + j * 16 * HG + (hf * HG + hh) * 8);
     }
   }
   float acc[PPL][8];

@@ -23,6 +23,14 @@ constexpr int kRowBytes = kHeadDim * 2;  // one bf16 row of 128 values
 // score whenever the dot product itself is exact.
 constexpr double kInvSqrt128 = 0.088388347648318440550;
 
+// 16-byte load marked non-temporal: for data read exactly once (partial
+// results in the combine), so that it does not displace reused lines in L2.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_once(const void* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
