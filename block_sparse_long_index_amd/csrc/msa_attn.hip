@@ -19,7 +19,7 @@
 
 namespace msa {
 
-constexpr int kChunkQueries = 64;  // queries per work chunk (rows = kChunkQueries * hg)
+constexpr int kChunkQueries = 128;  // queries per work chunk (rows = kChunkQueries * hg)
 static_assert(kChunkQueries % 64 == 0, "a chunk's entries fill whole wave registers");
 constexpr int kScanTile = 4096;    // elements per workgroup in the offset scan
 
@@ -33,7 +33,7 @@ static int32_t unit_rows(int64_t NB) {
   return r;
 }
 
-// Chunks one stage can produce: its entries in chunks of 64 queries plus at
+// Chunks one stage can produce: its entries in chunks of kChunkQueries plus at
 // most one partial chunk per block.
 static int64_t stage_max_chunks(int64_t stage_rows, int64_t NB, int k) {
   const int64_t entries = stage_rows * k;
@@ -116,7 +116,7 @@ void attn_workspace_carve(void* ws, int64_t window, int64_t stage_rows, int64_t 
 //   2. exclusive scan of hist in that order: the entries of bin (g, blk) are
 //      contiguous, and inside a bin ordered by row unit
 //   3. scatter: each unit writes its entries from its offsets (LDS cursors)
-//   4. chunks: every bin is cut into chunks of at most 64 queries; chunk slots
+//   4. chunks: every bin is cut into chunks of at most kChunkQueries; chunk slots
 //      are allocated with one atomic per wave
 // LDS atomics keep hot blocks (block 0, the local block, needles) from
 // serialising on a global counter.
@@ -242,7 +242,7 @@ __global__ void __launch_bounds__(256) scan_apply_kernel(int32_t* x, int64_t n,
 
 // Stage chunk lists.  Stage (g, s) covers group g and the window rows of
 // sub-window s (units [s*U, (s+1)*U)); thread (g, s, blk) cuts the entries of
-// bin (g, blk) in those units into chunks of at most 64 queries.  A wave
+// bin (g, blk) in those units into chunks of at most kChunkQueries.  A wave
 // holds 64 blocks of one stage and takes its chunk slots with one atomic.
 __global__ void __launch_bounds__(256) stage_chunk_kernel(const int32_t* off, int32_t* totals,
                                                           int4* chunks, int32_t NB, int64_t nbins,
@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(256) stage_chunk_kernel(const int32_t* off, in
 }
 
 // ---------------------------------------------------------------------------
-// KV-outer attention.  One workgroup per chunk (b, g, block, <= 64 queries):
+// KV-outer attention.  One workgroup per chunk (b, g, block, <= 128 queries):
 // the block's K (row-major) and V (transposed) go to LDS once and every
 // gathered (query, head) row is processed against them: S^T = K Q^T with keys
 // on the MFMA M side (a lane holds 16 keys of one row, so the row max and sum
