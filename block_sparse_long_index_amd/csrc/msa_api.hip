@@ -24,10 +24,6 @@ int hip_fail(hipError_t e, const char* where) {
 }
 
 constexpr int64_t kDefaultWindow = int64_t(1) << 20;  // rows per inversion (one sequence)
-// Partial results of one KV-outer stage (rows x k slots x heads x 256 B) are
-// sized to the 256 MB last-level cache, so that the combine reads them back
-// from it; within that, more rows per stage fill the chunks better.
-constexpr int64_t kStagePartialBytes = int64_t(1) << 28;
 constexpr int64_t kMaxElems = int64_t(1) << 46;
 
 bool pow2_upto(int v, int hi) { return v >= 1 && v <= hi && (v & (v - 1)) == 0; }
@@ -107,10 +103,16 @@ int64_t default_window(const msa_dims_t* d) {
   return d->T < kDefaultWindow ? d->T : kDefaultWindow;
 }
 
+// Rows per attention stage: the largest power of two >= 1024 whose partials
+// fit a byte budget.  A bigger stage gathers more queries per KV block (fewer
+// block loads and fewer partly filled chunks) but writes more partials before
+// they are read back; 512 MB is best at 128K tokens, and from 4096 blocks on,
+// where a stage's queries are spread over many more blocks, 1 GB is.
 int64_t stage_rows_for(const msa_dims_t* d, int64_t window) {
   const int64_t per_row = int64_t(d->k) * (d->Hq / d->G) * 256;
+  const int64_t budget = nblocks(d) >= 4096 ? int64_t(1) << 30 : int64_t(1) << 29;
   int64_t rows = 1024;
-  while (rows * 2 * per_row <= kStagePartialBytes) rows *= 2;
+  while (rows * 2 * per_row <= budget) rows *= 2;
   return window < rows ? window : rows;
 }
 
