@@ -523,8 +523,10 @@ struct TopkArgs {
   PagedCache pc;  // per-sequence lengths when paged (T == 1)
 };
 
+// Non-short-circuit operators keep the comparisons branch-free (selects, not
+// exec-mask branches).
 __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+  return (av > bv) | ((av == bv) & (ai < bi));
 }
 
 // Bitonic sort of one (score, index) pair per lane; best_first puts the best
@@ -536,13 +538,13 @@ __device__ __forceinline__ void bitonic64(float& v, int& i, int lane, bool best_
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const float pv = __shfl_xor(v, stride);
       const int pi = __shfl_xor(i, stride);
-      const bool lower = (lane & stride) == 0;
-      const bool dir = (((lane & size) == 0) == best_first);
-      const bool swap = (lower == dir) ? beats(pv, pi, v, i) : beats(v, i, pv, pi);
-      if (swap) {
-        v = pv;
-        i = pi;
-      }
+      // keep: this lane ends with the better pair of the two.  One
+      // comparison decides both sides (for two equal pairs either choice
+      // leaves the same pair).
+      const bool keep = ((lane & stride) == 0) == (((lane & size) == 0) == best_first);
+      const bool take = beats(pv, pi, v, i) == keep;
+      v = take ? pv : v;
+      i = take ? pi : i;
     }
   }
 }
@@ -553,12 +555,9 @@ __device__ __forceinline__ void bitonic_merge64(float& v, int& i, int lane) {
   for (int stride = 32; stride > 0; stride >>= 1) {
     const float pv = __shfl_xor(v, stride);
     const int pi = __shfl_xor(i, stride);
-    const bool lower = (lane & stride) == 0;
-    const bool swap = lower ? beats(pv, pi, v, i) : beats(v, i, pv, pi);
-    if (swap) {
-      v = pv;
-      i = pi;
-    }
+    const bool take = beats(pv, pi, v, i) == ((lane & stride) == 0);
+    v = take ? pv : v;
+    i = take ? pi : i;
   }
 }
 
@@ -568,10 +567,8 @@ __device__ __forceinline__ float sort_desc_values64(float v, int lane) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const float pv = __shfl_xor(v, stride);
-      const bool lower = (lane & stride) == 0;
-      const bool desc = (lane & size) == 0;
-      const bool take = (lower == desc) ? (pv > v) : (pv < v);
-      v = take ? pv : v;
+      const bool keep = ((lane & stride) == 0) == ((lane & size) == 0);  // keep the larger
+      v = ((pv > v) == keep) ? pv : v;
     }
   }
   return v;
@@ -603,7 +600,7 @@ __device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int s
   const float tau = __shfl(sort_desc_values64(lm, lane), m - 1);
   int cnt = 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) cnt += (e0 + lane + step * r < n && x[r] >= tau) ? 1 : 0;
+  for (int r = 0; r < R; ++r) cnt += ((e0 + lane + step * r < n) & (x[r] >= tau)) ? 1 : 0;
   for (int e = rest + lane; e < n; e += step) cnt += src[e] >= tau ? 1 : 0;
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) cnt += __shfl_xor(cnt, s);
@@ -611,7 +608,7 @@ __device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int s
   vi = INT_MAX;
   auto chunk = [&](int c0, float xv, int& base) {
     const int e = c0 + lane;
-    const bool f = (e < n) && (xv >= tau);
+    const bool f = (e < n) & (xv >= tau);
     const unsigned long long bal = __ballot(f);
     if (f) {
       const int pos = base + lanes_below(bal);
@@ -622,7 +619,7 @@ __device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int s
   };
   auto merge = [&](int c0, float xv) {
     const int e = c0 + lane;
-    const bool f = (e < n) && (xv >= tau);
+    const bool f = (e < n) & (xv >= tau);
     if (!__ballot(f)) return;
     float cvv = f ? xv : -INFINITY;
     int cii = f ? e : INT_MAX;
@@ -670,10 +667,8 @@ __device__ __forceinline__ void write_selection(int32_t* out, int vi, int m, int
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const int pk = __shfl_xor(key, stride);
-      const bool lower = (lane & stride) == 0;
-      const bool asc = (lane & size) == 0 || size == 16;
-      const bool take = (lower == asc) ? (pk < key) : (pk > key);
-      key = take ? pk : key;
+      const bool keep = ((lane & stride) == 0) == (((lane & size) == 0) | (size == 16));
+      key = ((pk < key) == keep) ? pk : key;  // keep: the smaller of the two
     }
   }
   if (lane < k) out[lane] = lane < m ? key : (lane == m ? L : -1);
