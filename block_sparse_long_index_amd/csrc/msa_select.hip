@@ -529,49 +529,68 @@ __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
   return (av > bv) | ((av == bv) & (ai < bi));
 }
 
-// Bitonic sort of one (score, index) pair per lane; best_first puts the best
-// pair in lane 0.
+// The value of lane (lane ^ S), S a power of two below 64, by the cheapest
+// exchange for each distance: a DPP quad permutation for 1 and 2, a swizzle
+// (inside each half-wave) for 4 to 16, a permute for 32.
+template <int S>
+__device__ __forceinline__ int xlane(int x) {
+  if constexpr (S == 1) return __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);
+  else if constexpr (S == 2) return __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);
+  else if constexpr (S < 32) return __builtin_amdgcn_ds_swizzle(x, 0x1F | (S << 10));
+  else return __shfl_xor(x, 32);
+}
+
+template <int S>
+__device__ __forceinline__ float xlane(float x) {
+  return __int_as_float(xlane<S>(__float_as_int(x)));
+}
+
+// Bitonic sort of one (score, index) pair per lane, from the merge of SIZE
+// runs at distance STRIDE on; best_first puts the best pair in lane 0.  Each
+// compare-exchange takes one comparison: keep says whether this lane ends with
+// the better pair of the two (for two equal pairs either choice leaves the
+// same pair).
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_steps(float& v, int& i, int lane, bool best_first) {
+  const float pv = xlane<STRIDE>(v);
+  const int pi = xlane<STRIDE>(i);
+  const bool keep = ((lane & STRIDE) == 0) == (((lane & SIZE) == 0) == best_first);
+  const bool take = beats(pv, pi, v, i) == keep;
+  v = take ? pv : v;
+  i = take ? pi : i;
+  if constexpr (STRIDE > 1)
+    bitonic_steps<SIZE, STRIDE / 2>(v, i, lane, best_first);
+  else if constexpr (SIZE < 64)
+    bitonic_steps<SIZE * 2, SIZE>(v, i, lane, best_first);
+}
+
 __device__ __forceinline__ void bitonic64(float& v, int& i, int lane, bool best_first) {
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const float pv = __shfl_xor(v, stride);
-      const int pi = __shfl_xor(i, stride);
-      // keep: this lane ends with the better pair of the two.  One
-      // comparison decides both sides (for two equal pairs either choice
-      // leaves the same pair).
-      const bool keep = ((lane & stride) == 0) == (((lane & size) == 0) == best_first);
-      const bool take = beats(pv, pi, v, i) == keep;
-      v = take ? pv : v;
-      i = take ? pi : i;
-    }
-  }
+  bitonic_steps<2, 1>(v, i, lane, best_first);
 }
 
 // Merge of a best-first bitonic sequence into best-first order.
+template <int STRIDE = 32>
 __device__ __forceinline__ void bitonic_merge64(float& v, int& i, int lane) {
-#pragma unroll
-  for (int stride = 32; stride > 0; stride >>= 1) {
-    const float pv = __shfl_xor(v, stride);
-    const int pi = __shfl_xor(i, stride);
-    const bool take = beats(pv, pi, v, i) == ((lane & stride) == 0);
-    v = take ? pv : v;
-    i = take ? pi : i;
-  }
+  const float pv = xlane<STRIDE>(v);
+  const int pi = xlane<STRIDE>(i);
+  const bool take = beats(pv, pi, v, i) == ((lane & STRIDE) == 0);
+  v = take ? pv : v;
+  i = take ? pi : i;
+  if constexpr (STRIDE > 1) bitonic_merge64<STRIDE / 2>(v, i, lane);
 }
 
+// Values sorted descending across the wave (lane 0 the largest).
+template <int SIZE = 2, int STRIDE = 1>
 __device__ __forceinline__ float sort_desc_values64(float v, int lane) {
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const float pv = __shfl_xor(v, stride);
-      const bool keep = ((lane & stride) == 0) == ((lane & size) == 0);  // keep the larger
-      v = ((pv > v) == keep) ? pv : v;
-    }
-  }
-  return v;
+  const float pv = xlane<STRIDE>(v);
+  const bool keep = ((lane & STRIDE) == 0) == ((lane & SIZE) == 0);  // keep the larger
+  v = ((pv > v) == keep) ? pv : v;
+  if constexpr (STRIDE > 1)
+    return sort_desc_values64<SIZE, STRIDE / 2>(v, lane);
+  else if constexpr (SIZE < 64)
+    return sort_desc_values64<SIZE * 2, SIZE>(v, lane);
+  else
+    return v;
 }
 
 __device__ __forceinline__ int lanes_below(unsigned long long mask) {
@@ -598,12 +617,13 @@ __device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int s
   for (int r = 0; r < R; ++r) lm = fmaxf(lm, e0 + lane + step * r < n ? x[r] : -INFINITY);
   for (int e = rest + lane; e < n; e += step) lm = fmaxf(lm, src[e]);
   const float tau = __shfl(sort_desc_values64(lm, lane), m - 1);
-  int cnt = 0;
+  int cnt = 0;  // candidates >= tau, the same in every lane
 #pragma unroll
-  for (int r = 0; r < R; ++r) cnt += ((e0 + lane + step * r < n) & (x[r] >= tau)) ? 1 : 0;
-  for (int e = rest + lane; e < n; e += step) cnt += src[e] >= tau ? 1 : 0;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) cnt += __shfl_xor(cnt, s);
+  for (int r = 0; r < R; ++r) cnt += __popcll(__ballot((e0 + lane + step * r < n) & (x[r] >= tau)));
+  for (int c0 = rest; c0 < n; c0 += step) {
+    const int e = c0 + lane;
+    cnt += __popcll(__ballot((e < n) & (src[e < n ? e : n - 1] >= tau)));
+  }
   v = -INFINITY;
   vi = INT_MAX;
   auto chunk = [&](int c0, float xv, int& base) {
@@ -657,20 +677,26 @@ __device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int s
   }
 }
 
+// Ascending sort of the keys of each 16-lane row (bitonic, from the merge of
+// SIZE runs at distance STRIDE on).
+template <int SIZE = 2, int STRIDE = 1>
+__device__ __forceinline__ int sort_asc16(int key, int lane) {
+  const int pk = xlane<STRIDE>(key);
+  const bool keep = ((lane & STRIDE) == 0) == (((lane & SIZE) == 0) | (SIZE == 16));
+  key = ((pk < key) == keep) ? pk : key;  // keep: the smaller of the two
+  if constexpr (STRIDE > 1)
+    return sort_asc16<SIZE, STRIDE / 2>(key, lane);
+  else if constexpr (SIZE < 16)
+    return sort_asc16<SIZE * 2, SIZE>(key, lane);
+  else
+    return key;
+}
+
 // Lanes 0..m-1 hold block ids; write them ascending, then the local block L,
 // then -1 padding.
 __device__ __forceinline__ void write_selection(int32_t* out, int vi, int m, int L, int k,
                                                 int lane) {
-  int key = lane < m ? vi : INT_MAX;
-#pragma unroll
-  for (int size = 2; size <= 16; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int pk = __shfl_xor(key, stride);
-      const bool keep = ((lane & stride) == 0) == (((lane & size) == 0) | (size == 16));
-      key = ((pk < key) == keep) ? pk : key;  // keep: the smaller of the two
-    }
-  }
+  const int key = sort_asc16(lane < m ? vi : INT_MAX, lane);
   if (lane < k) out[lane] = lane < m ? key : (lane == m ? L : -1);
 }
 
