@@ -550,7 +550,7 @@ __device__ __forceinline__ float xlane(float x) {
 // compare-exchange takes one comparison: keep says whether this lane ends with
 // the better pair of the two (for two equal pairs either choice leaves the
 // same pair).
-template <int SIZE, int STRIDE>
+template <int SIZE, int STRIDE, int NMAX>
 __device__ __forceinline__ void bitonic_steps(float& v, int& i, int lane, bool best_first) {
   const float pv = xlane<STRIDE>(v);
   const int pi = xlane<STRIDE>(i);
@@ -559,13 +559,15 @@ __device__ __forceinline__ void bitonic_steps(float& v, int& i, int lane, bool b
   v = take ? pv : v;
   i = take ? pi : i;
   if constexpr (STRIDE > 1)
-    bitonic_steps<SIZE, STRIDE / 2>(v, i, lane, best_first);
-  else if constexpr (SIZE < 64)
-    bitonic_steps<SIZE * 2, SIZE>(v, i, lane, best_first);
+    bitonic_steps<SIZE, STRIDE / 2, NMAX>(v, i, lane, best_first);
+  else if constexpr (SIZE < NMAX)
+    bitonic_steps<SIZE * 2, SIZE, NMAX>(v, i, lane, best_first);
 }
 
+// Sorts each run of NMAX consecutive lanes (NMAX = 64: the whole wave).
+template <int NMAX = 64>
 __device__ __forceinline__ void bitonic64(float& v, int& i, int lane, bool best_first) {
-  bitonic_steps<2, 1>(v, i, lane, best_first);
+  bitonic_steps<2, 1, NMAX>(v, i, lane, best_first);
 }
 
 // Merge of a best-first bitonic sequence into best-first order.
@@ -602,9 +604,13 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 // step*i < n, left best-first in lanes 0..m-1 (m <= 15).  The first R strided
 // chunks are loaded once into registers, all loads in flight together; any
 // remainder is re-read from memory.  cv/ci: this wave's 64-entry LDS scratch.
+// Returns the number of candidates compacted into cv/ci in ascending index
+// order (all those >= the threshold, a superset of the best m), or -1 when
+// there were too many for the scratch (the best m then came from a running
+// merge).
 template <int R>
-__device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int step, int m,
-                                          int lane, float* cv, int* ci, float& v, int& vi) {
+__device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int step, int m,
+                                         int lane, float* cv, int* ci, float& v, int& vi) {
   float x[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -664,7 +670,14 @@ __device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int s
       v = cv[lane];
       vi = ci[lane];
     }
-    bitonic64(v, vi, lane, true);
+    // sort only as many lanes as hold candidates
+    if (cnt <= 16)
+      bitonic64<16>(v, vi, lane, true);
+    else if (cnt <= 32)
+      bitonic64<32>(v, vi, lane, true);
+    else
+      bitonic64(v, vi, lane, true);
+    return cnt;
   } else {
     // many equal scores at the threshold: merge 64 candidates at a time into
     // a running best-64 list
@@ -674,6 +687,7 @@ __device__ __forceinline__ void wave_topk(const float* src, int n, int e0, int s
       const int e = c0 + lane;
       merge(c0, e < n ? src[e] : -INFINITY);
     }
+    return -1;
   }
 }
 
@@ -716,8 +730,23 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
   }
   float v;
   int vi;
-  wave_topk<16>(a.S + row * a.NB, static_cast<int>(L), 0, 64, m, lane, cv[wave], ci[wave], v, vi);
-  write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
+  const int nc =
+      wave_topk<16>(a.S + row * a.NB, static_cast<int>(L), 0, 64, m, lane, cv[wave], ci[wave], v, vi);
+  if (nc < 0) {
+    write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
+    return;
+  }
+  // The compacted candidates are in ascending block order: those that are at
+  // least as good as the m-th best (lane m - 1 after the sort) are exactly the
+  // best m, and their ranks among themselves give their output slots.
+  const float vm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), m - 1));
+  const int im = __builtin_amdgcn_readlane(vi, m - 1);
+  const float c = lane < nc ? cv[wave][lane] : -INFINITY;
+  const int cidx = lane < nc ? ci[wave][lane] : INT_MAX;
+  const bool sel = (lane < nc) & !beats(vm, im, c, cidx);
+  const unsigned long long bm = __ballot(sel);
+  if (sel) out[lanes_below(bm)] = cidx;
+  if ((lane >= m) & (lane < a.k)) out[lane] = lane == m ? static_cast<int>(L) : -1;
 }
 
 // Long rows, few of them (decode): four waves per row, each takes every
