@@ -214,26 +214,31 @@ index_tile_kernel(TileArgs a) {
     const unsigned char* buf = kbuf[kb & (R - 1)];
     float m0 = -INFINITY, m1 = -INFINITY;
     const bool masked = WRITE_S && (kb == L);
-    // One 32-key tile: 8 K fragments from LDS, 16 MFMAs into two column tiles.
-    auto tile = [&](int kt, f32x16& c0, f32x16& c1) {
+    // One 32-key tile: its K fragments from LDS (8 for bf16: one per
+    // 16-dim step; 2 x 32 B for fp8), then 16 (bf16) or 4 (fp8) MFMAs into
+    // two column tiles.
+    typedef uint4 KFrag[8];
+    auto frags = [&](int kt, KFrag& av) {
       const int r = kt * 32 + l32;
       if constexpr (F8) {
-        // two 32x32x64 steps cover the 128 dims
         const unsigned char* rp = buf + r * PITCH + 32 * half;
-        i32x8 av[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          av[s] = as_i32x8(*reinterpret_cast<const uint4*>(rp + 64 * s),
-                           *reinterpret_cast<const uint4*>(rp + 64 * s + 16));
-        c0 = mfma32_f8(av[0], qf8[0][0], f32x16{});
-        c1 = mfma32_f8(av[0], qf8[1][0], f32x16{});
-        c0 = mfma32_f8(av[1], qf8[0][1], c0);
-        c1 = mfma32_f8(av[1], qf8[1][1], c1);
+        for (int s = 0; s < 4; ++s) av[s] = *reinterpret_cast<const uint4*>(rp + 64 * (s >> 1) + 16 * (s & 1));
       } else {
-        uint4 av[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s)
           av[s] = *reinterpret_cast<const uint4*>(&buf[swz(r, 2 * s + half)]);
+      }
+    };
+    auto tile = [&](const KFrag& av, f32x16& c0, f32x16& c1) {
+      if constexpr (F8) {
+        // two 32x32x64 steps cover the 128 dims
+        const i32x8 a0 = as_i32x8(av[0], av[1]), a1 = as_i32x8(av[2], av[3]);
+        c0 = mfma32_f8(a0, qf8[0][0], f32x16{});
+        c1 = mfma32_f8(a0, qf8[1][0], f32x16{});
+        c0 = mfma32_f8(a1, qf8[0][1], c0);
+        c1 = mfma32_f8(a1, qf8[1][1], c1);
+      } else {
         c0 = mfma32(as_bf16x8(av[0]), qf[0][0], f32x16{});
         c1 = mfma32(as_bf16x8(av[0]), qf[1][0], f32x16{});
 #pragma unroll
@@ -262,20 +267,47 @@ index_tile_kernel(TileArgs a) {
         m1 = max3(m1, c1[e], c1[e + 1]);
       }
     };
-    // Software pipeline: the MFMAs of tile kt run while tile kt-1 is reduced.
+    // Software pipeline: the MFMAs of tile kt run while tile kt-1 is reduced
+    // and (when S is not written: the score stores need those registers) the
+    // K fragments of tile kt+1 are read from LDS.
     f32x16 ta0, ta1, tb0, tb1;
-    tile(0, ta0, ta1);
-    sched_fence();
-    tile(1, tb0, tb1);
-    reduce(0, ta0, ta1);
-    sched_fence();
-    tile(2, ta0, ta1);
-    reduce(1, tb0, tb1);
-    sched_fence();
-    tile(3, tb0, tb1);
-    reduce(2, ta0, ta1);
-    sched_fence();
-    reduce(3, tb0, tb1);
+    KFrag fa, fb;
+    if constexpr (!WRITE_S) {
+      frags(0, fa);
+      sched_fence();
+      frags(1, fb);
+      tile(fa, ta0, ta1);
+      sched_fence();
+      frags(2, fa);
+      tile(fb, tb0, tb1);
+      reduce(0, ta0, ta1);
+      sched_fence();
+      frags(3, fb);
+      tile(fa, ta0, ta1);
+      reduce(1, tb0, tb1);
+      sched_fence();
+      tile(fb, tb0, tb1);
+      reduce(2, ta0, ta1);
+      sched_fence();
+      reduce(3, tb0, tb1);
+    } else {
+      frags(0, fa);
+      tile(fa, ta0, ta1);
+      sched_fence();
+      frags(1, fb);
+      tile(fb, tb0, tb1);
+      reduce(0, ta0, ta1);
+      sched_fence();
+      frags(2, fa);
+      tile(fa, ta0, ta1);
+      reduce(1, tb0, tb1);
+      sched_fence();
+      frags(3, fb);
+      tile(fb, tb0, tb1);
+      reduce(2, ta0, ta1);
+      sched_fence();
+      reduce(3, tb0, tb1);
+    }
     m0 = fmaxf(m0, __shfl_xor(m0, 32));
     m1 = fmaxf(m1, __shfl_xor(m1, 32));
     const float v = half ? m1 : m0;
