@@ -803,15 +803,19 @@ __global__ void __launch_bounds__(256) topk_wide_kernel(TopkArgs a) {
   int vi;
   wave_topk<8>(a.S + row * a.NB, static_cast<int>(L), 64 * wave, 256, m, lane, cv[wave], ci[wave],
             v, vi);
+  // Each wave's list is sorted best-first; odd waves store theirs reversed,
+  // so that every 32 entries form a bitonic sequence and two merge stages
+  // (instead of a whole sort) order the 64.
   if (lane < 16) {
-    mv[wave * 16 + lane] = lane < m ? v : -INFINITY;
-    mi[wave * 16 + lane] = lane < m ? vi : INT_MAX;
+    const int pos = wave * 16 + ((wave & 1) ? 15 - lane : lane);
+    mv[pos] = lane < m ? v : -INFINITY;
+    mi[pos] = lane < m ? vi : INT_MAX;
   }
   __syncthreads();
   if (wave != 0) return;
   v = mv[lane];
   vi = mi[lane];
-  bitonic64(v, vi, lane, true);
+  bitonic_steps<32, 16, 64>(v, vi, lane, true);
   write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
 }
 
