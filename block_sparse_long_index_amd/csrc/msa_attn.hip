@@ -999,6 +999,78 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecArgs a) {
   }
 }
 
+// Decode combine: one wave per (sequence, group, head), so that the batch's
+// few rows still spread over many waves.  Lane l takes piece l % 16 of the
+// head's partial (8 values, MFMA order as written by decode_attn_kernel) in
+// the slots s = l / 16 + 4i, i = 0..3; the four slot groups are then summed
+// across the wave.  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
+// row's valid slots, M = max m_s.
+template <int HG>
+__global__ void __launch_bounds__(256) decode_combine_kernel(CombArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (wid >= a.rows * a.G * HG) return;
+  const int h = static_cast<int>(wid % HG);
+  const int64_t bg = wid / HG;  // b * G + g
+  const int64_t b = bg / a.G;
+  const int g = static_cast<int>(bg % a.G);
+  const int32_t* ir = a.idx + bg * a.k;
+  const int nval = __popcll(__ballot(lane < a.k && ir[lane < a.k ? lane : 0] >= 0));
+  const int pc = lane & 15, sg = lane >> 4;
+  const int j = pc >> 1, hf = pc & 1;
+  float2 ml[4];
+  uint4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sl = sg + 4 * i;
+    const int64_t e = bg * a.k + (sl < nval ? sl : 0);  // entry (b, g, slot)
+    ml[i] = a.lpart[e * HG + h];
+    raw[i] = ld16_once(a.opart + e * HG * kHeadDim + j * 16 * HG + (hf * HG + h) * 8);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (sg + 4 * i < nval) mx = fmaxf(mx, ml[i].x);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float w = sg + 4 * i < nval ? fast_exp2(ml[i].x - mx) : 0.f;
+    den += w * ml[i].y;
+    const uint32_t wv[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[2 * u] += w * __uint_as_float(wv[u] << 16);
+      acc[2 * u + 1] += w * __uint_as_float(wv[u] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    acc[u] += __shfl_xor(acc[u], 16);
+    acc[u] += __shfl_xor(acc[u], 32);
+  }
+  den += __shfl_xor(den, 16);
+  den += __shfl_xor(den, 32);
+  const int hq = g * HG + h;
+  if (sg == 0) {
+    const float inv = 1.f / den;
+    // piece (j, hf): values 0-3 at d0, 4-7 at d0 + 8
+    const int d0 = 32 * (j >> 1) + 16 * (j & 1) + 4 * hf;
+    u16* dst = a.O + (b * a.Hq + hq) * kHeadDim + d0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      uint2 w;
+      w.x = pack_bf16x2(acc[4 * r + 0] * inv, acc[4 * r + 1] * inv);
+      w.y = pack_bf16x2(acc[4 * r + 2] * inv, acc[4 * r + 3] * inv);
+      *reinterpret_cast<uint2*>(dst + 8 * r) = w;
+    }
+  }
+  // lse in natural log: (max + log2(sum)) * ln 2, the max being log2-domain
+  if (a.lse && lane == 0) a.lse[b * a.Hq + hq] = (mx + __log2f(den)) * 0.6931471805599453f;
+}
+
 template <int HG>
 static hipError_t launch_decode_t(const DecArgs& da, const CombArgs& ca, int64_t n,
                                   hipStream_t st) {
@@ -1006,9 +1078,9 @@ static hipError_t launch_decode_t(const DecArgs& da, const CombArgs& ca, int64_t
                      da);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t waves = ca.rows * ca.G;
-  hipLaunchKernelGGL((combine_kernel<HG>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256),
-                     0, st, ca);
+  const int64_t waves = ca.rows * ca.G * HG;
+  hipLaunchKernelGGL((decode_combine_kernel<HG>), dim3(static_cast<unsigned>((waves + 3) / 4)),
+                     dim3(256), 0, st, ca);
   return hipGetLastError();
 }
 
