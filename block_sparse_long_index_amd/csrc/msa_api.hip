@@ -41,17 +41,22 @@ int check_dims(const msa_dims_t* d) {
                 d->Hq, d->G);
   if (d->k < 1 || d->Bk < 1 || d->d_h < 1 || d->d_I < 1)
     return fail(MSA_ERR_INVALID_ARGUMENT, "k, Bk, d_h, d_I must be >= 1");
-  if (d->d_h != 128 || d->d_I != 128 || d->Bk != 128)
-    return fail(MSA_ERR_UNSUPPORTED, "only d_h = d_I = Bk = 128 (got %d, %d, %d)", d->d_h,
-                d->d_I, d->Bk);
-  if (d->k > 16) return fail(MSA_ERR_UNSUPPORTED, "k > 16 (got %d)", d->k);
+  if (d->d_h != 128 || d->d_I != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "only d_h = d_I = 128 (got %d, %d)", d->d_h, d->d_I);
+  if (d->Bk != 128 && d->Bk != 64 && d->Bk != 32)
+    return fail(MSA_ERR_UNSUPPORTED, "Bk must be 32, 64 or 128 (got %d)", d->Bk);
+  // at most 2048 selected keys per query and group: k <= 16 / 32 / 64
+  if (d->k > 2048 / d->Bk)
+    return fail(MSA_ERR_UNSUPPORTED, "k * Bk > 2048 (k = %d, Bk = %d)", d->k, d->Bk);
   if (!pow2_upto(d->G, 16)) return fail(MSA_ERR_UNSUPPORTED, "G must be 1, 2, 4, 8 or 16");
   if (!pow2_upto(d->Hq / d->G, 16))
     return fail(MSA_ERR_UNSUPPORTED, "Hq / G must be 1, 2, 4, 8 or 16");
   if (d->B > 65535) return fail(MSA_ERR_UNSUPPORTED, "B > 65535");
   // block counts of one sequence live in LDS during the inversion (64 KB)
   if (d->N > (int64_t(1) << 21)) return fail(MSA_ERR_UNSUPPORTED, "N > 2^21");
-  const int64_t NB = (d->N + 127) / 128;
+  if ((d->N + d->Bk - 1) / d->Bk > 16384)
+    return fail(MSA_ERR_UNSUPPORTED, "more than 16384 blocks per sequence");
+  const int64_t NB = (d->N + d->Bk - 1) / d->Bk;
   if (d->B * d->T * d->Hq > kMaxElems / 128 || d->B * d->G * d->N > kMaxElems / 128 ||
       d->B * d->G * d->T * NB > kMaxElems || d->B * d->G * NB > (int64_t(1) << 30))
     return fail(MSA_ERR_UNSUPPORTED, "problem too large");
@@ -71,6 +76,8 @@ const msa::PagedCache kContiguous = {nullptr, nullptr, 0, 0};
 // are the caller's, see msa.h).
 int check_paged(const msa_dims_t* d, int64_t num_pages, const int32_t* table,
                 const int64_t* lens, msa::PagedCache* pc) {
+  if (d->Bk != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "paged caches have 128-token pages (Bk = %d)", d->Bk);
   if (d->T != 1)
     return fail(MSA_ERR_INVALID_ARGUMENT, "paged calls are decode only (T == 1, got %lld)",
                 (long long)d->T);
@@ -93,7 +100,31 @@ int check_paged(const msa_dims_t* d, int64_t num_pages, const int32_t* table,
     if (rc_ != MSA_OK) return rc_; \
   } while (0)
 
-int64_t nblocks(const msa_dims_t* d) { return (d->N + 127) / 128; }
+int64_t nblocks(const msa_dims_t* d) { return (d->N + d->Bk - 1) / d->Bk; }
+
+// Calls whose kernels only take 128-key blocks (the fused selection on fp8
+// inputs, paged caches).
+int need_bk128(const msa_dims_t* d, const char* what) {
+  if (d->Bk != 128) return fail(MSA_ERR_UNSUPPORTED, "%s needs Bk = 128 (got %d)", what, d->Bk);
+  return MSA_OK;
+}
+
+// Prefill selection with Bk < 128: the scores of a window of rows are
+// materialised, then ranked.  Rows per window for a workspace of ws bytes.
+int64_t select_window(const msa_dims_t* d, size_t ws) {
+  const int64_t per_row = d->B * d->G * nblocks(d) * int64_t(sizeof(float));
+  const int64_t w = static_cast<int64_t>(ws) / per_row;
+  return w < d->T ? w : d->T;
+}
+
+// Default: windows of up to 1 GB of scores.
+size_t select_window_ws(const msa_dims_t* d) {
+  const int64_t per_row = d->B * d->G * nblocks(d) * int64_t(sizeof(float));
+  int64_t w = (int64_t(1) << 30) / per_row;
+  if (w < 1) w = 1;
+  if (w > d->T) w = d->T;
+  return static_cast<size_t>(w * per_row);
+}
 
 size_t decode_select_ws(const msa_dims_t* d) {
   return static_cast<size_t>(d->B * d->G * nblocks(d)) * sizeof(float);
@@ -118,11 +149,11 @@ int64_t stage_rows_for(const msa_dims_t* d, int64_t window) {
 
 size_t prefill_ws(const msa_dims_t* d, int64_t window) {
   return msa::attn_workspace_bytes(window, stage_rows_for(d, window), d->N, d->G, d->Hq / d->G,
-                                   d->k, false);
+                                   d->k, d->Bk, false);
 }
 
 size_t decode_ws(const msa_dims_t* d) {
-  return msa::attn_workspace_bytes(d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true);
+  return msa::attn_workspace_bytes(d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, d->Bk, true);
 }
 
 }  // namespace
@@ -150,7 +181,8 @@ size_t msa_workspace_bytes(int op, const msa_dims_t* d) {
   if (rc != MSA_OK) return 0;
   switch (op) {
     case MSA_OP_INDEX_SCORES: return 0;
-    case MSA_OP_SELECT_BLOCKS: return d->T == 1 ? decode_select_ws(d) : 0;
+    case MSA_OP_SELECT_BLOCKS:
+      return d->T == 1 ? decode_select_ws(d) : (d->Bk == 128 ? 0 : select_window_ws(d));
     case MSA_OP_SELECT_FROM_SCORES: return 0;
     case MSA_OP_ATTN_PREFILL: return prefill_ws(d, default_window(d));
     case MSA_OP_ATTN_DECODE: return d->T == 1 ? decode_ws(d) : 0;
@@ -164,13 +196,14 @@ static int index_scores_impl(const msa_dims_t* d, const void* qI, const void* kI
   MSA_TRY(check_ptr(qI, "qI"));
   MSA_TRY(check_ptr(kI, "kI"));
   MSA_TRY(check_ptr(S, "S"));
+  if (fp8) MSA_TRY(need_bk128(d, name));
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d->T == 1)
-    e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, kContiguous, st);
+    e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, d->Bk, kContiguous, st);
   else
-    e = msa::launch_index_tiles(true, fp8, qI, kI, S, nullptr, d->B, d->T, d->N, d->G, d->k,
-                                st);
+    e = msa::launch_index_tiles(true, fp8, qI, kI, S, nullptr, d->B, d->T, 0, d->T, d->N, d->G,
+                                d->Bk, d->k, st);
   if (e != hipSuccess) return hip_fail(e, name);
   return MSA_OK;
 }
@@ -182,6 +215,7 @@ static int select_blocks_impl(const msa_dims_t* d, const void* qI, const void* k
   MSA_TRY(check_ptr(qI, "qI"));
   MSA_TRY(check_ptr(kI, "kI"));
   MSA_TRY(check_ptr(idx, "idx"));
+  if (fp8) MSA_TRY(need_bk128(d, name));
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d->T == 1) {
@@ -191,12 +225,30 @@ static int select_blocks_impl(const msa_dims_t* d, const void* qI, const void* k
       return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "select needs %zu workspace bytes, got %zu",
                   need, ws_bytes);
     float* S = static_cast<float*>(ws);
-    e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, kContiguous, st);
+    e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, d->Bk, kContiguous, st);
     if (e == hipSuccess)
-      e = msa::launch_topk_rows(S, idx, d->B, 1, d->N, d->G, d->k, kContiguous, st);
+      e = msa::launch_topk_rows(S, idx, d->B, 1, 0, 1, d->N, d->G, d->Bk, d->k, kContiguous, st);
+  } else if (d->Bk == 128) {
+    e = msa::launch_index_tiles(false, fp8, qI, kI, nullptr, idx, d->B, d->T, 0, d->T, d->N,
+                                d->G, 128, d->k, st);
   } else {
-    e = msa::launch_index_tiles(false, fp8, qI, kI, nullptr, idx, d->B, d->T, d->N, d->G, d->k,
-                                st);
+    // the scores of a window of rows at a time, then their top-k
+    MSA_TRY(check_ptr(ws, "ws"));
+    const int64_t W = select_window(d, ws_bytes);
+    if (W < 1)
+      return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                  "select needs at least %lld workspace bytes (one row of scores), got %zu",
+                  (long long)(d->B * d->G * nblocks(d) * 4), ws_bytes);
+    float* S = static_cast<float*>(ws);
+    e = hipSuccess;
+    for (int64_t t0 = 0; t0 < d->T && e == hipSuccess; t0 += W) {
+      const int64_t Tw = d->T - t0 < W ? d->T - t0 : W;
+      e = msa::launch_index_tiles(true, false, qI, kI, S, nullptr, d->B, d->T, t0, Tw, d->N,
+                                  d->G, d->Bk, d->k, st);
+      if (e == hipSuccess)
+        e = msa::launch_topk_rows(S, idx, d->B, d->T, t0, Tw, d->N, d->G, d->Bk, d->k,
+                                  kContiguous, st);
+    }
   }
   if (e != hipSuccess) return hip_fail(e, name);
   return MSA_OK;
@@ -228,7 +280,8 @@ int msa_select_blocks_from_scores(const msa_dims_t* d, const float* S, int32_t* 
   MSA_TRY(check_dims(d));
   MSA_TRY(check_ptr(S, "S"));
   MSA_TRY(check_ptr(idx, "idx"));
-  const hipError_t e = msa::launch_topk_rows(S, idx, d->B, d->T, d->N, d->G, d->k, kContiguous,
+  const hipError_t e = msa::launch_topk_rows(S, idx, d->B, d->T, 0, d->T, d->N, d->G, d->Bk,
+                                             d->k, kContiguous,
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_select_blocks_from_scores");
   return MSA_OK;
@@ -263,10 +316,11 @@ int msa_sparse_attn_prefill(const msa_dims_t* d, const void* q, const void* K, c
     hi = lo;
   }
   msa::AttnWorkspace w;
-  msa::attn_workspace_carve(ws, hi, stage_rows_for(d, hi), d->N, d->G, d->Hq / d->G, d->k, false,
-                            &w);
+  msa::attn_workspace_carve(ws, hi, stage_rows_for(d, hi), d->N, d->G, d->Hq / d->G, d->k, d->Bk,
+                            false, &w);
   const hipError_t e = msa::launch_attn_prefill(q, K, V, idx, O, lse, d->B, d->T, d->N, d->Hq,
-                                                d->G, d->k, w, static_cast<hipStream_t>(stream));
+                                                d->G, d->k, d->Bk, w,
+                                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_prefill");
   return MSA_OK;
 }
@@ -289,9 +343,9 @@ int msa_sparse_attn_decode(const msa_dims_t* d, const void* q, const void* K, co
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need,
                 ws_bytes);
   msa::AttnWorkspace w;
-  msa::attn_workspace_carve(ws, d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true, &w);
+  msa::attn_workspace_carve(ws, d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, d->Bk, true, &w);
   const hipError_t e = msa::launch_attn_decode(q, K, V, idx, O, lse, d->B, d->N, d->Hq, d->G,
-                                               d->k, kContiguous, w,
+                                               d->k, d->Bk, kContiguous, w,
                                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode");
   return MSA_OK;
@@ -314,8 +368,9 @@ static int select_paged_impl(const msa_dims_t* d, const void* qI, const void* kI
                 ws_bytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* S = static_cast<float*>(ws);
-  hipError_t e = msa::launch_decode_scan(fp8, qI, kI_pool, S, d->B, d->N, d->G, pc, st);
-  if (e == hipSuccess) e = msa::launch_topk_rows(S, idx, d->B, 1, d->N, d->G, d->k, pc, st);
+  hipError_t e = msa::launch_decode_scan(fp8, qI, kI_pool, S, d->B, d->N, d->G, 128, pc, st);
+  if (e == hipSuccess)
+    e = msa::launch_topk_rows(S, idx, d->B, 1, 0, 1, d->N, d->G, 128, d->k, pc, st);
   if (e != hipSuccess) return hip_fail(e, name);
   return MSA_OK;
 }
@@ -356,9 +411,9 @@ int msa_sparse_attn_decode_paged(const msa_dims_t* d, const void* q, const void*
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need,
                 ws_bytes);
   msa::AttnWorkspace w;
-  msa::attn_workspace_carve(ws, d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, true, &w);
+  msa::attn_workspace_carve(ws, d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, d->Bk, true, &w);
   const hipError_t e = msa::launch_attn_decode(q, K_pool, V_pool, idx, O, lse, d->B, d->N,
-                                               d->Hq, d->G, d->k, pc, w,
+                                               d->Hq, d->G, d->k, 128, pc, w,
                                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode_paged");
   return MSA_OK;

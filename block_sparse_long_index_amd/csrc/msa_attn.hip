@@ -40,9 +40,9 @@ static int64_t stage_max_chunks(int64_t stage_rows, int64_t NB, int k) {
   return entries / kChunkQueries + (NB < entries ? NB : entries) + 1;
 }
 
-static void layout(int64_t window, int64_t stage_rows, int64_t N, int G, int hg, int k,
+static void layout(int64_t window, int64_t stage_rows, int64_t N, int G, int hg, int k, int Bk,
                    bool decode, size_t* off, AttnWorkspace* w) {
-  const int64_t NB = (N + kBlock - 1) / kBlock;
+  const int64_t NB = (N + Bk - 1) / Bk;
   const int32_t rq = unit_rows(NB);
   int32_t nc = 0;
   int64_t nstages = 0, maxc = 0, prow_count = 0;
@@ -88,16 +88,16 @@ static void layout(int64_t window, int64_t stage_rows, int64_t N, int G, int hg,
 }
 
 size_t attn_workspace_bytes(int64_t window, int64_t stage_rows, int64_t N, int G, int hg, int k,
-                            bool decode) {
+                            int Bk, bool decode) {
   size_t off[8];
-  layout(window, stage_rows, N, G, hg, k, decode, off, nullptr);
+  layout(window, stage_rows, N, G, hg, k, Bk, decode, off, nullptr);
   return off[7];
 }
 
 void attn_workspace_carve(void* ws, int64_t window, int64_t stage_rows, int64_t N, int G, int hg,
-                          int k, bool decode, AttnWorkspace* w) {
+                          int k, int Bk, bool decode, AttnWorkspace* w) {
   size_t off[8];
-  layout(window, stage_rows, N, G, hg, k, decode, off, w);
+  layout(window, stage_rows, N, G, hg, k, Bk, decode, off, w);
   char* p = static_cast<char*>(ws);
   w->hist = reinterpret_cast<int32_t*>(p + off[0]);
   w->tile_sums = reinterpret_cast<int32_t*>(p + off[1]);
@@ -110,7 +110,7 @@ void attn_workspace_carve(void* ws, int64_t window, int64_t stage_rows, int64_t 
 
 // ---------------------------------------------------------------------------
 // Inversion of the selection for the query rows [t0, t0 + W) of sequence b: a
-// counting sort of the entries e = (t - t0) << 4 | slot by (group, block).
+// counting sort of the entries e = (t - t0) << 6 | slot by (group, block).
 //   1. unit histograms: workgroup (c, g) counts, in LDS, the blocks chosen by
 //      group g in rows [c*rq, (c+1)*rq) of the window; hist[(g*NB + blk)*nc + c]
 //   2. exclusive scan of hist in that order: the entries of bin (g, blk) are
@@ -166,8 +166,8 @@ __global__ void __launch_bounds__(256) scatter_kernel(InvArgs a) {
     const int32_t blk = src[i];
     if (blk >= 0 && blk < a.NB) {
       const int32_t pos = atomicAdd(&sh[blk], 1);
-      // entry = window row << 4 | slot (k <= 16), decoded with a shift
-      a.entries[pos] = static_cast<int32_t>(((r_lo + i / a.k) << 4) | (i % a.k));
+      // entry = window row << 6 | slot (k <= 64), decoded with a shift
+      a.entries[pos] = static_cast<int32_t>(((r_lo + i / a.k) << 6) | (i % a.k));
     }
   }
 }
@@ -334,8 +334,10 @@ __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~15) + ((o >> 2) & 1) * 8 + ((o >> 3) & 1) * 4 + (o & 3);
 }
 
-template <int HG>
+// NKT: 32-key tiles per block (Bk = 32 * NKT).
+template <int HG, int NKT>
 __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
+  constexpr int BK = 32 * NKT;
   __shared__ __align__(16) unsigned char ks[128 * kPitch];
   __shared__ __align__(16) unsigned char vt[128 * kPitch];
   // Workgroups are dealt to the 8 XCDs round-robin; give XCD x the x-th
@@ -358,26 +360,26 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
 
-  const int64_t key0 = blk * kBlock;
+  const int64_t key0 = blk * BK;
   const u16* Kb = a.K + (bg * a.N + key0) * kHeadDim;
   const u16* Vb = a.V + (bg * a.N + key0) * kHeadDim;
   // Issue the K/V block loads first; they are written to LDS after the first
   // pass's query rows are on their way.
-  uint4 kr[8], v0r[4], v1r[4];
+  uint4 kr[2 * NKT], v0r[NKT], v1r[NKT];
   // Branch-free loads (keys past N re-read the last key and are zeroed) keep
   // the number of outstanding loads fixed for the compiler's wait counting.
-  const int nvalid = static_cast<int>(a.N - key0 < kBlock ? a.N - key0 : kBlock);
+  const int nvalid = static_cast<int>(a.N - key0 < BK ? a.N - key0 : BK);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < 2 * NKT; ++j) {
     const int i = tid + j * 256;
     const int r = i >> 4, c = i & 15;
     const uint4 v = ld16(Kb + (r < nvalid ? r : nvalid - 1) * kHeadDim + c * 8);
     kr[j] = r < nvalid ? v : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NKT; ++j) {
     const int i = tid + j * 256;
-    const int kp = i & 63, c = i >> 6;
+    const int kp = i % (BK / 2), c = i / (BK / 2);  // key pair, 16-B chunk of d
     const int k0 = 2 * kp;
     const uint4 x0 = ld16(Vb + (k0 < nvalid ? k0 : nvalid - 1) * kHeadDim + c * 8);
     const uint4 x1 = ld16(Vb + (k0 + 1 < nvalid ? k0 + 1 : nvalid - 1) * kHeadDim + c * 8);
@@ -410,8 +412,8 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
       if ((qi >> 6) == r) e = er;
     }
     hh = rr % HG;
-    rl = e >> 4;
-    slot = e & 15;
+    rl = e >> 6;
+    slot = e & 63;
     const int64_t t = t0 + rl;
     p = static_cast<int>(a.N - a.T + t);
     q = a.q + ((b * a.T + t) * a.Hq + g * HG + hh) * kHeadDim;
@@ -432,14 +434,14 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
   load_q(qptr, qf);
 
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < 2 * NKT; ++j) {
     const int i = tid + j * 256;
     *reinterpret_cast<uint4*>(&ks[(i >> 4) * kPitch + (i & 15) * 16]) = kr[j];
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NKT; ++j) {
     const int i = tid + j * 256;
-    const int kp = i & 63, c = i >> 6;
+    const int kp = i % (BK / 2), c = i / (BK / 2);
     const int P = vt_pos(2 * kp);  // even; key 2*kp + 1 lands at P + 1
     const uint32_t w0[4] = {v0r[j].x, v0r[j].y, v0r[j].z, v0r[j].w};
     const uint32_t w1[4] = {v1r[j].x, v1r[j].y, v1r[j].z, v1r[j].w};
@@ -462,9 +464,9 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
   const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   for (int pass = 0; pass * 128 + wave * 32 < rows; ++pass) {
     // S^T = K Q^T, one 32-key tile at a time
-    f32x16 sacc[4];
+    f32x16 sacc[NKT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const uint4 ka = *reinterpret_cast<const uint4*>(kbase + kt * 32 * kPitch + s * 32);
@@ -486,9 +488,9 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
 
     // causal mask: only the local block of a row has keys after the row
     const int lim = p - static_cast<int>(key0);  // >= 0: block <= local(row)
-    if (__ballot(lim < kBlock - 1)) {
+    if (__ballot(lim < BK - 1)) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int off = kt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -497,7 +499,7 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
     }
     float m = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) m = max3(m, sacc[kt][i], sacc[kt][i + 1]);
     m = fmaxf(m, __shfl_xor(m, 32));
@@ -508,7 +510,7 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
     f32x16 oacc[4];
     float l = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < NKT; ++kt) {
       uint4 va[4][2];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -587,7 +589,9 @@ struct CombArgs {
   int32_t pgroups;   // groups held by the partial buffer
 };
 
-template <int HG>
+// WIDE: more than 16 slots (k <= 64): the row max first, then the partials
+// 16 slots at a time.
+template <int HG, bool WIDE>
 __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
   // A row's partial is 16 pieces of 8 values per head (MFMA order, see the
   // KV-outer kernel); a lane takes PPL consecutive pieces of one head.
@@ -610,26 +614,9 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
   const int li = lane % LPH;
   const int64_t pbase = (rl * a.pgroups + (a.pgroups > 1 ? g : 0)) * a.k;
 
-  // All 16 slots are loaded at once (slots past nval re-read slot 0 and get
-  // weight 0) so that every lane has its whole row in flight.
-  float2 ml[16];
   float mx = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int ss = s < nval ? s : 0;
-    ml[s] = a.lpart[(pbase + ss) * HG + hh];
-    if (s < nval) mx = fmaxf(mx, ml[s].x);
-  }
-  uint4 raw[16][PPL];
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int ss = s < nval ? s : 0;
-    const u16* src = a.opart + (pbase + ss) * HG * kHeadDim;
-#pragma unroll
-    for (int q = 0; q < PPL; ++q) {
-      const int pc = li * PPL + q, j = pc >> 1, hf = pc & 1;
-      raw[s][q] = ld16_once(src + j * 16 * HG + (hf * HG + hh) * 8);
-    }
+  if constexpr (WIDE) {
+    for (int s = 0; s < nval; ++s) mx = fmaxf(mx, a.lpart[(pbase + s) * HG + hh].x);
   }
   float acc[PPL][8];
 #pragma unroll
@@ -637,17 +624,40 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[q][u] = 0.f;
   float den = 0.f;
+  // One pass over 16 slots (WIDE: as many as the row has), all loaded at
+  // once (slots past nval re-read slot 0 and get weight 0) so that every lane
+  // has them in flight.
+  for (int s0 = 0; s0 < (WIDE ? nval : 1); s0 += 16) {
+    float2 ml[16];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const float w = s < nval ? fast_exp2(ml[s].x - mx) : 0.f;
-    den += w * ml[s].y;
+    for (int s = 0; s < 16; ++s) {
+      const int ss = s0 + s < nval ? s0 + s : 0;
+      ml[s] = a.lpart[(pbase + ss) * HG + hh];
+      if (!WIDE && s < nval) mx = fmaxf(mx, ml[s].x);
+    }
+    uint4 raw[16][PPL];
 #pragma unroll
-    for (int q = 0; q < PPL; ++q) {
-      const uint32_t wv[4] = {raw[s][q].x, raw[s][q].y, raw[s][q].z, raw[s][q].w};
+    for (int s = 0; s < 16; ++s) {
+      const int ss = s0 + s < nval ? s0 + s : 0;
+      const u16* src = a.opart + (pbase + ss) * HG * kHeadDim;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc[q][2 * u] += w * __uint_as_float(wv[u] << 16);
-        acc[q][2 * u + 1] += w * __uint_as_float(wv[u] & 0xffff0000u);
+      for (int q = 0; q < PPL; ++q) {
+        const int pc = li * PPL + q, j = pc >> 1, hf = pc & 1;
+        raw[s][q] = ld16_once(src + j * 16 * HG + (hf * HG + hh) * 8);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const float w = s0 + s < nval ? fast_exp2(ml[s].x - mx) : 0.f;
+      den += w * ml[s].y;
+#pragma unroll
+      for (int q = 0; q < PPL; ++q) {
+        const uint32_t wv[4] = {raw[s][q].x, raw[s][q].y, raw[s][q].z, raw[s][q].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc[q][2 * u] += w * __uint_as_float(wv[u] << 16);
+          acc[q][2 * u + 1] += w * __uint_as_float(wv[u] & 0xffff0000u);
+        }
       }
     }
   }
@@ -674,28 +684,43 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int HG>
+template <int HG, int NKT>
 static hipError_t launch_kv_combine(const AttnArgs& aa, const CombArgs& ca, int64_t grid_chunks,
                                     hipStream_t st) {
   const int64_t grid = (grid_chunks + 7) & ~static_cast<int64_t>(7);
-  hipLaunchKernelGGL((kv_outer_kernel<HG>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
-                     aa);
+  hipLaunchKernelGGL((kv_outer_kernel<HG, NKT>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                     st, aa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t waves = ca.rows * (ca.group >= 0 ? 1 : ca.G);
-  hipLaunchKernelGGL((combine_kernel<HG>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256),
-                     0, st, ca);
+  if (ca.k > 16)
+    hipLaunchKernelGGL((combine_kernel<HG, true>), dim3(static_cast<unsigned>((waves + 3) / 4)),
+                       dim3(256), 0, st, ca);
+  else
+    hipLaunchKernelGGL((combine_kernel<HG, false>), dim3(static_cast<unsigned>((waves + 3) / 4)),
+                       dim3(256), 0, st, ca);
   return hipGetLastError();
 }
 
-static hipError_t dispatch_hg(int hg, const AttnArgs& aa, const CombArgs& ca, int64_t grid,
-                              hipStream_t st) {
+template <int NKT>
+static hipError_t dispatch_hg_t(int hg, const AttnArgs& aa, const CombArgs& ca, int64_t grid,
+                                hipStream_t st) {
   switch (hg) {
-    case 8: return launch_kv_combine<8>(aa, ca, grid, st);
-    case 4: return launch_kv_combine<4>(aa, ca, grid, st);
-    case 16: return launch_kv_combine<16>(aa, ca, grid, st);
-    case 2: return launch_kv_combine<2>(aa, ca, grid, st);
-    case 1: return launch_kv_combine<1>(aa, ca, grid, st);
+    case 8: return launch_kv_combine<8, NKT>(aa, ca, grid, st);
+    case 4: return launch_kv_combine<4, NKT>(aa, ca, grid, st);
+    case 16: return launch_kv_combine<16, NKT>(aa, ca, grid, st);
+    case 2: return launch_kv_combine<2, NKT>(aa, ca, grid, st);
+    case 1: return launch_kv_combine<1, NKT>(aa, ca, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t dispatch_hg(int hg, int Bk, const AttnArgs& aa, const CombArgs& ca,
+                              int64_t grid, hipStream_t st) {
+  switch (Bk) {
+    case 128: return dispatch_hg_t<4>(hg, aa, ca, grid, st);
+    case 64: return dispatch_hg_t<2>(hg, aa, ca, grid, st);
+    case 32: return dispatch_hg_t<1>(hg, aa, ca, grid, st);
   }
   return hipErrorInvalidValue;
 }
@@ -712,10 +737,10 @@ static unsigned blocks_for(int64_t n, int per) {
 // launch right after reads them back.
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse, int64_t B,
-                               int64_t T, int64_t N, int Hq, int G, int k,
+                               int64_t T, int64_t N, int Hq, int G, int k, int Bk,
                                const AttnWorkspace& w, hipStream_t st) {
   const int hg = Hq / G;
-  const int32_t NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
+  const int32_t NB = static_cast<int32_t>((N + Bk - 1) / Bk);
   const size_t lds = sizeof(int32_t) * NB;
   for (int64_t b = 0; b < B; ++b) {
     for (int64_t t0 = 0; t0 < T; t0 += w.window) {
@@ -795,7 +820,7 @@ hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
           ca.rl_base = rl_base;
           ca.group = g;
           ca.pgroups = 1;
-          e = dispatch_hg(hg, aa, ca, w.max_chunks, st);
+          e = dispatch_hg(hg, Bk, aa, ca, w.max_chunks, st);
           if (e != hipSuccess) return e;
         }
       }
@@ -822,7 +847,7 @@ struct DecArgs {
   u16* opart;          // [B, G, k, hg, 128]
   float2* lpart;       // [B, G, k, hg]
   int64_t N;           // cache capacity (tokens)
-  int32_t Hq, G, k;
+  int32_t Hq, G, k, Bk;
   PagedCache pc;
 };
 
@@ -855,13 +880,13 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecArgs a) {
   const int64_t b = bg / a.G;
   const int blk = a.idx[bg * a.k + slot];
   const int64_t len = paged_len(a.pc, b, a.N);  // this sequence's cache length
-  if (blk < 0 || static_cast<int64_t>(blk) * kBlock >= len) return;  // unused slot
+  if (blk < 0 || static_cast<int64_t>(blk) * a.Bk >= len) return;  // unused slot
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, qd = lane >> 4;
-  const int64_t kblk = static_cast<int64_t>(blk) * kBlock;
+  const int64_t kblk = static_cast<int64_t>(blk) * a.Bk;
   // keys of the block inside the sequence (>= 1); loads clamp to the last of
   // them, and this wave's quarter holds nvalid of them (<= 0: none)
-  const int nblk = static_cast<int>(len - kblk < kBlock ? len - kblk : kBlock);
+  const int nblk = static_cast<int>(len - kblk < a.Bk ? len - kblk : a.Bk);
   const int nvalid = nblk - 32 * wave < 32 ? nblk - 32 * wave : 32;
   const int64_t row0 = a.pc.table ? (paged_page(a.pc, b, blk) * a.G + g) * kBlock
                                   : bg * a.N + kblk;  // first key row of the block
@@ -1002,10 +1027,10 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecArgs a) {
 // Decode combine: one wave per (sequence, group, head), so that the batch's
 // few rows still spread over many waves.  Lane l takes piece l % 16 of the
 // head's partial (8 values, MFMA order as written by decode_attn_kernel) in
-// the slots s = l / 16 + 4i, i = 0..3; the four slot groups are then summed
-// across the wave.  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
-// row's valid slots, M = max m_s.
-template <int HG>
+// the slots s = l / 16 + 4i, i = 0..NSL-1; the four slot groups are then
+// summed across the wave.  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// over the row's valid slots, M = max m_s.
+template <int HG, int NSL>
 __global__ void __launch_bounds__(256) decode_combine_kernel(CombArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -1018,10 +1043,10 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(CombArgs a) {
   const int nval = __popcll(__ballot(lane < a.k && ir[lane < a.k ? lane : 0] >= 0));
   const int pc = lane & 15, sg = lane >> 4;
   const int j = pc >> 1, hf = pc & 1;
-  float2 ml[4];
-  uint4 raw[4];
+  float2 ml[NSL];
+  uint4 raw[NSL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NSL; ++i) {
     const int sl = sg + 4 * i;
     const int64_t e = bg * a.k + (sl < nval ? sl : 0);  // entry (b, g, slot)
     ml[i] = a.lpart[e * HG + h];
@@ -1029,14 +1054,14 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(CombArgs a) {
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NSL; ++i)
     if (sg + 4 * i < nval) mx = fmaxf(mx, ml[i].x);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NSL; ++i) {
     const float w = sg + 4 * i < nval ? fast_exp2(ml[i].x - mx) : 0.f;
     den += w * ml[i].y;
     const uint32_t wv[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
@@ -1079,14 +1104,18 @@ static hipError_t launch_decode_t(const DecArgs& da, const CombArgs& ca, int64_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t waves = ca.rows * ca.G * HG;
-  hipLaunchKernelGGL((decode_combine_kernel<HG>), dim3(static_cast<unsigned>((waves + 3) / 4)),
-                     dim3(256), 0, st, ca);
+  if (ca.k > 16)
+    hipLaunchKernelGGL((decode_combine_kernel<HG, 16>), dim3(static_cast<unsigned>((waves + 3) / 4)),
+                       dim3(256), 0, st, ca);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<HG, 4>), dim3(static_cast<unsigned>((waves + 3) / 4)),
+                       dim3(256), 0, st, ca);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse, int64_t B, int64_t N,
-                              int Hq, int G, int k, const PagedCache& pc,
+                              int Hq, int G, int k, int Bk, const PagedCache& pc,
                               const AttnWorkspace& w, hipStream_t st) {
   const int hg = Hq / G;
   DecArgs da;
@@ -1101,6 +1130,7 @@ hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
   da.Hq = Hq;
   da.G = G;
   da.k = k;
+  da.Bk = Bk;
   CombArgs ca;
   ca.idx = idx;
   ca.opart = w.opart;

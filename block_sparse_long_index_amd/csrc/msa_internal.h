@@ -17,20 +17,25 @@ struct PagedCache {
   int32_t nb;  // table row length (blocks of capacity)
 };
 
-// Stages 1+2 (write S) or stages 1-3 fused (write idx) for T > 1; fp8: q^I and
-// k^I are e4m3 bytes instead of bf16.
+// Stages 1+2 (write S, blocks of Bk keys) or stages 1-3 fused (write idx,
+// Bk = 128) for the query rows t0 .. t0 + Tw - 1 of T; S holds those rows
+// only ([B, G, Tw, NB]).  fp8: q^I and k^I are e4m3 bytes instead of bf16
+// (Bk = 128).
 hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const void* kI,
-                              float* S, int32_t* idx, int64_t B, int64_t T,
-                              int64_t N, int G, int k, hipStream_t st);
+                              float* S, int32_t* idx, int64_t B, int64_t T, int64_t t0,
+                              int64_t Tw, int64_t N, int G, int Bk, int k, hipStream_t st);
 
-// Stages 1+2 for T == 1: streams the index keys, S is [B, G, 1, NB].
+// Stages 1+2 for T == 1: streams the index keys, S is [B, G, 1, NB] with NB
+// blocks of Bk keys (fp8 and paged caches: Bk = 128).
 hipError_t launch_decode_scan(bool fp8, const void* qI, const void* kI, float* S,
-                              int64_t B, int64_t N, int G, const PagedCache& pc,
+                              int64_t B, int64_t N, int G, int Bk, const PagedCache& pc,
                               hipStream_t st);
 
-// Stage 3 from S [B, G, T, NB] (one wave per row).
-hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
-                            int64_t N, int G, int k, const PagedCache& pc, hipStream_t st);
+// Stage 3 for the query rows t0 .. t0 + Tw - 1 of T from their scores
+// S [B, G, Tw, NB] (blocks of Bk keys) into idx [B, G, T, k], k <= 64.
+hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T, int64_t t0,
+                            int64_t Tw, int64_t N, int G, int Bk, int k, const PagedCache& pc,
+                            hipStream_t st);
 
 struct AttnWorkspace {
   int32_t* hist;       // [G * NB * nc]: unit block counts, then exclusive offsets
@@ -54,18 +59,18 @@ struct AttnWorkspace {
 // in stages of `stage_rows` rows of one group.  decode: one chunk per
 // (sequence, group, slot), window = B.
 size_t attn_workspace_bytes(int64_t window, int64_t stage_rows, int64_t N, int G, int hg, int k,
-                            bool decode);
+                            int Bk, bool decode);
 void attn_workspace_carve(void* ws, int64_t window, int64_t stage_rows, int64_t N, int G, int hg,
-                          int k, bool decode, AttnWorkspace* out);
+                          int k, int Bk, bool decode, AttnWorkspace* out);
 
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse,
                                int64_t B, int64_t T, int64_t N, int Hq, int G,
-                               int k, const AttnWorkspace& w, hipStream_t st);
+                               int k, int Bk, const AttnWorkspace& w, hipStream_t st);
 
 hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse,
-                              int64_t B, int64_t N, int Hq, int G, int k,
+                              int64_t B, int64_t N, int Hq, int G, int k, int Bk,
                               const PagedCache& pc, const AttnWorkspace& w, hipStream_t st);
 
 }  // namespace msa

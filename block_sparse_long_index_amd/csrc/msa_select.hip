@@ -42,9 +42,10 @@ struct TileShape {
 struct TileArgs {
   const u16* qI;
   const u16* kI;
-  float* S;
-  int32_t* idx;
+  float* S;         // scores of the window's rows: [B, G, Tw, NB]
+  int32_t* idx;     // [B, G, T, k]
   int64_t T, N;
+  int64_t t0, Tw;   // this launch's query rows: t0 .. t0 + Tw - 1
   int64_t tile_hi;  // last position tile; workgroups run heaviest first
   int32_t NB, k, B;
 };
@@ -89,9 +90,16 @@ __device__ __forceinline__ void sort_ascending(int (&v)[CAP]) {
 // F8: q^I and k^I are OCP e4m3 bytes instead of bf16.  A k^I row is then
 // 128 B; in LDS the rows sit 144 B apart (16 consecutive rows read at the
 // same column hit distinct banks) instead of the bf16 tile's chunk swizzle.
-template <int G, int CAP, bool WRITE_S, bool F8>
+// BK: the block size of the scores written (WRITE_S): each 128-key chunk
+// holds 128 / BK blocks, one per BK / 32 key tiles.  The fused selection
+// (!WRITE_S) takes BK = 128.
+template <int G, int CAP, bool WRITE_S, bool F8, int BK = 128>
 __global__ void __launch_bounds__(TileShape<G>::NT)
 index_tile_kernel(TileArgs a) {
+  static_assert(BK == 32 || BK == 64 || BK == 128, "block of 32, 64 or 128 keys");
+  static_assert(WRITE_S || BK == 128, "the fused selection takes 128-key blocks");
+  constexpr int TPB = BK / 32;   // key tiles per block
+  constexpr int BPC = 128 / BK;  // blocks per 128-key chunk
   using TS = TileShape<G>;
   constexpr int QT = TS::QT, NT = TS::NT;
   constexpr int ROWB = F8 ? 128 : 256;      // bytes per k^I / q^I row
@@ -132,7 +140,7 @@ index_tile_kernel(TileArgs a) {
     const int64_t p = P0 + qq;
     const int64_t t = p - row0;
     colp[j] = p;
-    const bool ok = (t >= 0) && (t < a.T);
+    const bool ok = (t >= a.t0) && (t < a.t0 + a.Tw);
     const unsigned char* src = reinterpret_cast<const unsigned char*>(a.qI) +
                                ((static_cast<int64_t>(b) * a.T + (ok ? t : 0)) * G + g) * ROWB;
     const uint4 z = make_uint4(0, 0, 0, 0);
@@ -156,7 +164,7 @@ index_tile_kernel(TileArgs a) {
   const int own = wave * 64 + lane;
   const int own_q = own / G, own_g = own % G;
   const int64_t own_t = P0 + own_q - row0;
-  const bool own_ok = (own_t >= 0) && (own_t < a.T);
+  const bool own_ok = (own_t >= a.t0) && (own_t < a.t0 + a.Tw);
 
   const int64_t nkb = WRITE_S ? (L + 1) : L;
   const unsigned char* kbase =
@@ -172,8 +180,29 @@ index_tile_kernel(TileArgs a) {
   float st[4] = {0.f, 0.f, 0.f, 0.f};
   float* srow = nullptr;
   if (WRITE_S && own_ok)
-    srow = a.S + ((static_cast<int64_t>(b) * G + own_g) * a.T + own_t) * a.NB;
+    srow = a.S + ((static_cast<int64_t>(b) * G + own_g) * a.Tw + (own_t - a.t0)) * a.NB;
   const bool s_vec = (a.NB & 3) == 0;
+  const int64_t nblocks = WRITE_S ? (L + 1) * BPC : 0;  // blocks this workgroup scores
+  // Score of block gb (the BK-key blocks in order): held in st[gb % 4] and
+  // stored four at a time, or at the last block.
+  auto emit = [&](int64_t gb, float v) {
+    const float sv = static_cast<float>(static_cast<double>(v) * kInvSqrt128);
+    const int slot = static_cast<int>(gb & 3);
+    st[0] = slot == 0 ? sv : st[0];
+    st[1] = slot == 1 ? sv : st[1];
+    st[2] = slot == 2 ? sv : st[2];
+    st[3] = slot == 3 ? sv : st[3];
+    if (srow && (slot == 3 || gb + 1 == nblocks)) {
+      const int64_t base = gb & ~static_cast<int64_t>(3);
+      if (slot == 3 && s_vec && base + 3 < a.NB) {
+        *reinterpret_cast<float4*>(srow + base) = make_float4(st[0], st[1], st[2], st[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e <= slot && base + e < a.NB) srow[base + e] = st[e];
+      }
+    }
+  };
 
   uint4 pf[PF];
   // Branch-free: keys past N re-read key N-1 and are zeroed, so that every
@@ -266,6 +295,16 @@ index_tile_kernel(TileArgs a) {
         m0 = max3(m0, c0[e], c0[e + 1]);
         m1 = max3(m1, c1[e], c1[e + 1]);
       }
+      if constexpr (WRITE_S && BK < 128) {
+        // the last tile of a block: its score, then start the next block
+        if ((kt + 1) % TPB == 0) {
+          const float bm0 = fmaxf(m0, __shfl_xor(m0, 32));
+          const float bm1 = fmaxf(m1, __shfl_xor(m1, 32));
+          emit(kb * BPC + kt / TPB, half ? bm1 : bm0);
+          m0 = -INFINITY;
+          m1 = -INFINITY;
+        }
+      }
     };
     // Software pipeline: the MFMAs of tile kt run while tile kt-1 is reduced
     // and (when S is not written: the score stores need those registers) the
@@ -313,22 +352,7 @@ index_tile_kernel(TileArgs a) {
     const float v = half ? m1 : m0;
 
     if (WRITE_S) {
-      const float sv = static_cast<float>(static_cast<double>(v) * kInvSqrt128);
-      const int slot = static_cast<int>(kb & 3);
-      st[0] = slot == 0 ? sv : st[0];
-      st[1] = slot == 1 ? sv : st[1];
-      st[2] = slot == 2 ? sv : st[2];
-      st[3] = slot == 3 ? sv : st[3];
-      if (srow && (slot == 3 || kb + 1 == nkb)) {
-        const int64_t base = kb & ~static_cast<int64_t>(3);
-        if (slot == 3 && s_vec) {
-          *reinterpret_cast<float4*>(srow + base) = make_float4(st[0], st[1], st[2], st[3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (e <= slot) srow[base + e] = st[e];
-        }
-      }
+      if constexpr (BK == 128) emit(kb, v);
     } else {
       const bool need = v > ts[CAP - 1];
       if (__ballot(need)) {
@@ -344,14 +368,14 @@ index_tile_kernel(TileArgs a) {
     // Blocks after the local block are invisible: -inf.  The workgroup fills
     // each row's tail together so that consecutive threads write consecutive
     // addresses.
-    const int64_t tail0 = L + 1;
+    const int64_t tail0 = nblocks;
     const int64_t len = a.NB - tail0;
     if (len > 0) {
       for (int c = 0; c < TS::NCOL; ++c) {
         const int q = c / G, g = c % G;
         const int64_t t = P0 + q - row0;
-        if (t < 0 || t >= a.T) continue;
-        float* row = a.S + ((static_cast<int64_t>(b) * G + g) * a.T + t) * a.NB + tail0;
+        if (t < a.t0 || t >= a.t0 + a.Tw) continue;
+        float* row = a.S + ((static_cast<int64_t>(b) * G + g) * a.Tw + (t - a.t0)) * a.NB + tail0;
         for (int64_t e = tid; e < len; e += NT) row[e] = -INFINITY;
       }
     }
@@ -374,29 +398,32 @@ index_tile_kernel(TileArgs a) {
   }
 }
 
-template <int G, bool WS, bool F8>
+template <int G, bool WS, bool F8, int BK>
 static hipError_t launch_tiles_cap(const TileArgs& a, int64_t ntiles, hipStream_t st) {
   using TS = TileShape<G>;
   const int64_t grid = ntiles * a.B;
   const dim3 gd(static_cast<unsigned>(grid)), bd(TS::NT);
   if (WS || a.k <= 4) {
-    hipLaunchKernelGGL((index_tile_kernel<G, 3, WS, F8>), gd, bd, 0, st, a);
-  } else if (a.k <= 8) {
-    hipLaunchKernelGGL((index_tile_kernel<G, 7, WS, F8>), gd, bd, 0, st, a);
+    hipLaunchKernelGGL((index_tile_kernel<G, 3, WS, F8, BK>), gd, bd, 0, st, a);
+  } else if constexpr (BK == 128) {
+    if (a.k <= 8)
+      hipLaunchKernelGGL((index_tile_kernel<G, 7, WS, F8>), gd, bd, 0, st, a);
+    else
+      hipLaunchKernelGGL((index_tile_kernel<G, 15, WS, F8>), gd, bd, 0, st, a);
   } else {
-    hipLaunchKernelGGL((index_tile_kernel<G, 15, WS, F8>), gd, bd, 0, st, a);
+    return hipErrorInvalidValue;  // the fused selection takes 128-key blocks
   }
   return hipGetLastError();
 }
 
-template <bool WS, bool F8>
+template <bool WS, bool F8, int BK>
 static hipError_t launch_tiles_g(const TileArgs& a, int G, int64_t ntiles, hipStream_t st) {
   switch (G) {
-    case 1: return launch_tiles_cap<1, WS, F8>(a, ntiles, st);
-    case 2: return launch_tiles_cap<2, WS, F8>(a, ntiles, st);
-    case 4: return launch_tiles_cap<4, WS, F8>(a, ntiles, st);
-    case 8: return launch_tiles_cap<8, WS, F8>(a, ntiles, st);
-    case 16: return launch_tiles_cap<16, WS, F8>(a, ntiles, st);
+    case 1: return launch_tiles_cap<1, WS, F8, BK>(a, ntiles, st);
+    case 2: return launch_tiles_cap<2, WS, F8, BK>(a, ntiles, st);
+    case 4: return launch_tiles_cap<4, WS, F8, BK>(a, ntiles, st);
+    case 8: return launch_tiles_cap<8, WS, F8, BK>(a, ntiles, st);
+    case 16: return launch_tiles_cap<16, WS, F8, BK>(a, ntiles, st);
   }
   return hipErrorInvalidValue;
 }
@@ -404,8 +431,8 @@ static hipError_t launch_tiles_g(const TileArgs& a, int G, int64_t ntiles, hipSt
 static int tile_queries(int G) { return (512 / G) < 128 ? (512 / G) : 128; }
 
 hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const void* kI,
-                              float* S, int32_t* idx, int64_t B, int64_t T,
-                              int64_t N, int G, int k, hipStream_t st) {
+                              float* S, int32_t* idx, int64_t B, int64_t T, int64_t t0,
+                              int64_t Tw, int64_t N, int G, int Bk, int k, hipStream_t st) {
   const int QT = tile_queries(G);
   TileArgs a;
   a.qI = static_cast<const u16*>(qI);
@@ -414,18 +441,26 @@ hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const
   a.idx = idx;
   a.T = T;
   a.N = N;
-  a.NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
+  a.t0 = t0;
+  a.Tw = Tw;
+  a.NB = static_cast<int32_t>((N + Bk - 1) / Bk);
   a.k = k;
   a.B = static_cast<int32_t>(B);
-  const int64_t tile_lo = (N - T) / QT;
-  a.tile_hi = (N - 1) / QT;
+  const int64_t tile_lo = (N - T + t0) / QT;
+  a.tile_hi = (N - T + t0 + Tw - 1) / QT;
   const int64_t ntiles = a.tile_hi - tile_lo + 1;
+  if (Bk != 128 && (fp8 || !write_scores)) return hipErrorInvalidValue;
   if (fp8) {
-    if (write_scores) return launch_tiles_g<true, true>(a, G, ntiles, st);
-    return launch_tiles_g<false, true>(a, G, ntiles, st);
+    if (write_scores) return launch_tiles_g<true, true, 128>(a, G, ntiles, st);
+    return launch_tiles_g<false, true, 128>(a, G, ntiles, st);
   }
-  if (write_scores) return launch_tiles_g<true, false>(a, G, ntiles, st);
-  return launch_tiles_g<false, false>(a, G, ntiles, st);
+  if (!write_scores) return launch_tiles_g<false, false, 128>(a, G, ntiles, st);
+  switch (Bk) {
+    case 128: return launch_tiles_g<true, false, 128>(a, G, ntiles, st);
+    case 64: return launch_tiles_g<true, false, 64>(a, G, ntiles, st);
+    case 32: return launch_tiles_g<true, false, 32>(a, G, ntiles, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------
@@ -441,16 +476,20 @@ hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const
 struct ScanArgs {
   const u16* qI;
   const u16* kI;  // [B, N, 128], or the page pool [pages, 128, 128] when paged
-  float* S;
+  float* S;       // [B, G, NB]
   int64_t N;      // cache capacity (tokens)
-  int32_t NB, G;
+  int32_t NB, G;  // NB: blocks of BK keys
+  int32_t NCH;    // 128-key chunks, one per wave
   PagedCache pc;
 };
 
 // F8: e4m3 inputs; one 16x16x128 MFMA covers 16 keys x all 128 dims (lane
 // quarter qd holds d = 32*qd .. +31), and a block is 16 KB.
-template <bool F8>
+// BK: block size of the scores; a wave's 128-key chunk holds 128 / BK blocks.
+template <bool F8, int BK>
 __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
+  constexpr int BPC = 128 / BK;  // blocks per chunk
+  constexpr int GPB = BK / 16;   // 16-key groups per block
   constexpr int ROWB = F8 ? 128 : 256;  // bytes per k^I / q^I row
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
@@ -469,13 +508,17 @@ __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
     for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(col < a.G ? ld16(qsrc + 64 * s + 16 * qd) : z);
   }
   {
-    const int64_t kb = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-    if (kb >= a.NB) return;
-    // this sequence's length (paged: its own) and the block's keys inside it
+    const int64_t kb = static_cast<int64_t>(blockIdx.x) * 4 + wave;  // the wave's chunk
+    if (kb >= a.NCH) return;
+    // this sequence's length (paged: its own) and the chunk's keys inside it
     const int64_t len = paged_len(a.pc, b, a.N);
-    float* srow = a.S + static_cast<int64_t>(b) * a.G * a.NB + kb;
+    float* srow = a.S + static_cast<int64_t>(b) * a.G * a.NB + kb * BPC;
     if (kb * kBlock >= len) {  // past the end of this sequence: invisible
-      if (lane < a.G) srow[static_cast<int64_t>(lane) * a.NB] = -INFINITY;
+      if (lane < a.G) {
+#pragma unroll
+        for (int j = 0; j < BPC; ++j)
+          if (kb * BPC + j < a.NB) srow[static_cast<int64_t>(lane) * a.NB + j] = -INFINITY;
+      }
       return;
     }
     const int nvalid = static_cast<int>(len - kb * kBlock < kBlock ? len - kb * kBlock : kBlock);
@@ -493,7 +536,9 @@ __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
       for (int s = 0; s < LPK; ++s)  // tail keys masked below
         d[kg][s] = F8 ? ld16(src + 32 * qd + 16 * s) : ld16(src + 64 * s + 16 * qd);
     }
-    float m = -INFINITY;
+    float m[BPC];
+#pragma unroll
+    for (int j = 0; j < BPC; ++j) m[j] = -INFINITY;
 #pragma unroll
     for (int kg = 0; kg < 8; ++kg) {
       f32x4 acc = {};
@@ -506,19 +551,26 @@ __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kk = kg * 16 + 4 * qd + r;
-        m = fmaxf(m, kk < nvalid ? acc[r] : -INFINITY);
+        m[kg / GPB] = fmaxf(m[kg / GPB], kk < nvalid ? acc[r] : -INFINITY);
       }
     }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    if (lane < a.G)
-      srow[static_cast<int64_t>(lane) * a.NB] =
-          static_cast<float>(static_cast<double>(m) * kInvSqrt128);
+#pragma unroll
+    for (int j = 0; j < BPC; ++j) {
+      m[j] = fmaxf(m[j], __shfl_xor(m[j], 16));
+      m[j] = fmaxf(m[j], __shfl_xor(m[j], 32));
+    }
+    if (lane < a.G) {
+#pragma unroll
+      for (int j = 0; j < BPC; ++j)
+        if (kb * BPC + j < a.NB)
+          srow[static_cast<int64_t>(lane) * a.NB + j] =
+              static_cast<float>(static_cast<double>(m[j]) * kInvSqrt128);
+    }
   }
 }
 
 hipError_t launch_decode_scan(bool fp8, const void* qI, const void* kI, float* S,
-                              int64_t B, int64_t N, int G, const PagedCache& pc,
+                              int64_t B, int64_t N, int G, int Bk, const PagedCache& pc,
                               hipStream_t st) {
   ScanArgs a;
   a.pc = pc;
@@ -526,13 +578,22 @@ hipError_t launch_decode_scan(bool fp8, const void* qI, const void* kI, float* S
   a.kI = static_cast<const u16*>(kI);
   a.S = S;
   a.N = N;
-  a.NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
+  a.NB = static_cast<int32_t>((N + Bk - 1) / Bk);
+  a.NCH = static_cast<int32_t>((N + kBlock - 1) / kBlock);
   a.G = G;
-  const dim3 grid(static_cast<unsigned>((a.NB + 3) / 4), static_cast<unsigned>(B));
-  if (fp8)
-    hipLaunchKernelGGL(decode_scan_kernel<true>, grid, dim3(256), 0, st, a);
+  const dim3 grid(static_cast<unsigned>((a.NCH + 3) / 4), static_cast<unsigned>(B));
+  if (fp8 && Bk == 128)
+    hipLaunchKernelGGL((decode_scan_kernel<true, 128>), grid, dim3(256), 0, st, a);
+  else if (fp8)
+    return hipErrorInvalidValue;
+  else if (Bk == 128)
+    hipLaunchKernelGGL((decode_scan_kernel<false, 128>), grid, dim3(256), 0, st, a);
+  else if (Bk == 64)
+    hipLaunchKernelGGL((decode_scan_kernel<false, 64>), grid, dim3(256), 0, st, a);
+  else if (Bk == 32)
+    hipLaunchKernelGGL((decode_scan_kernel<false, 32>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(decode_scan_kernel<false>, grid, dim3(256), 0, st, a);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -548,12 +609,29 @@ hipError_t launch_decode_scan(bool fp8, const void* qI, const void* kI, float* S
 //   3. the best m are sorted by block index and written with the local block.
 // ---------------------------------------------------------------------------
 struct TopkArgs {
-  const float* S;
-  int32_t* idx;
+  const float* S;   // scores of the window's rows: [B, G, Tw, NB]
+  int32_t* idx;     // [B, G, T, k]
   int64_t T, N, rows;
-  int32_t NB, k, G;
+  int64_t t0, Tw;   // this launch's query rows: t0 .. t0 + Tw - 1 (rows = B * G * Tw)
+  int32_t NB, k, G, Bk;
   PagedCache pc;  // per-sequence lengths when paged (T == 1)
 };
+
+// Row r of a top-k launch: its scores, its output and its local block.
+struct TopkRow {
+  const float* s;
+  int32_t* out;
+  int64_t L;
+};
+
+__device__ __forceinline__ TopkRow topk_row(const TopkArgs& a, int64_t r) {
+  const int64_t bg = r / a.Tw, t = a.t0 + r % a.Tw;
+  TopkRow x;
+  x.s = a.S + r * a.NB;
+  x.out = a.idx + (bg * a.T + t) * a.k;
+  x.L = (paged_len(a.pc, bg / a.G, a.N) - a.T + t) / a.Bk;
+  return x;
+}
 
 // Non-short-circuit operators keep the comparisons branch-free (selects, not
 // exec-mask branches).
@@ -633,7 +711,7 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 }
 
 // Best m candidates (score desc, index asc) among src[e] for e = e0 + lane +
-// step*i < n, left best-first in lanes 0..m-1 (m <= 15).  The first R strided
+// step*i < n, left best-first in lanes 0..m-1 (m <= 63).  The first R strided
 // chunks are loaded once into registers, all loads in flight together; any
 // remainder is re-read from memory.  cv/ci: this wave's 64-entry LDS scratch.
 // Returns the number of candidates compacted into cv/ci in ascending index
@@ -738,11 +816,26 @@ __device__ __forceinline__ int sort_asc16(int key, int lane) {
     return key;
 }
 
+// Ascending sort of the keys across the wave.
+template <int SIZE = 2, int STRIDE = 1>
+__device__ __forceinline__ int sort_asc64(int key, int lane) {
+  const int pk = xlane<STRIDE>(key);
+  const bool keep = ((lane & STRIDE) == 0) == ((lane & SIZE) == 0);
+  key = ((pk < key) == keep) ? pk : key;  // keep: the smaller of the two
+  if constexpr (STRIDE > 1)
+    return sort_asc64<SIZE, STRIDE / 2>(key, lane);
+  else if constexpr (SIZE < 64)
+    return sort_asc64<SIZE * 2, SIZE>(key, lane);
+  else
+    return key;
+}
+
 // Lanes 0..m-1 hold block ids; write them ascending, then the local block L,
-// then -1 padding.
+// then -1 padding (m < k <= 64).
 __device__ __forceinline__ void write_selection(int32_t* out, int vi, int m, int L, int k,
                                                 int lane) {
-  const int key = sort_asc16(lane < m ? vi : INT_MAX, lane);
+  const int key0 = lane < m ? vi : INT_MAX;
+  const int key = m <= 15 ? sort_asc16(key0, lane) : sort_asc64(key0, lane);
   if (lane < k) out[lane] = lane < m ? key : (lane == m ? L : -1);
 }
 
@@ -752,18 +845,17 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (row >= a.rows) return;
-  const int64_t t = row % a.T;
-  const int64_t L = (paged_len(a.pc, row / (a.T * a.G), a.N) - a.T + t) / kBlock;
+  const TopkRow x = topk_row(a, row);
+  const int64_t L = x.L;
   const int m = static_cast<int>(L < a.k - 1 ? L : a.k - 1);
-  int32_t* out = a.idx + row * a.k;
+  int32_t* out = x.out;
   if (m == 0) {
     if (lane < a.k) out[lane] = lane == 0 ? static_cast<int>(L) : -1;
     return;
   }
   float v;
   int vi;
-  const int nc =
-      wave_topk<16>(a.S + row * a.NB, static_cast<int>(L), 0, 64, m, lane, cv[wave], ci[wave], v, vi);
+  const int nc = wave_topk<16>(x.s, static_cast<int>(L), 0, 64, m, lane, cv[wave], ci[wave], v, vi);
   if (nc < 0) {
     write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
     return;
@@ -782,54 +874,76 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
 }
 
 // Long rows, few of them (decode): four waves per row, each takes every
-// fourth 64-candidate chunk; the four best-m lists meet in LDS and one wave
-// sorts the 64 entries and writes the selection.
+// fourth 64-candidate chunk; the four best-m lists meet in LDS and wave 0
+// orders them and writes the selection.
 __global__ void __launch_bounds__(256) topk_wide_kernel(TopkArgs a) {
   __shared__ float cv[4][64];
   __shared__ int ci[4][64];
-  __shared__ float mv[64];
-  __shared__ int mi[64];
+  __shared__ float mv[4][64];
+  __shared__ int mi[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t row = blockIdx.x;
-  const int64_t t = row % a.T;
-  const int64_t L = (paged_len(a.pc, row / (a.T * a.G), a.N) - a.T + t) / kBlock;
+  const TopkRow x = topk_row(a, blockIdx.x);
+  const int64_t L = x.L;
   const int m = static_cast<int>(L < a.k - 1 ? L : a.k - 1);
-  int32_t* out = a.idx + row * a.k;
+  int32_t* out = x.out;
   if (m == 0) {
     if (wave == 0 && lane < a.k) out[lane] = lane == 0 ? static_cast<int>(L) : -1;
     return;
   }
   float v;
   int vi;
-  wave_topk<8>(a.S + row * a.NB, static_cast<int>(L), 64 * wave, 256, m, lane, cv[wave], ci[wave],
-            v, vi);
-  // Each wave's list is sorted best-first; odd waves store theirs reversed,
-  // so that every 32 entries form a bitonic sequence and two merge stages
-  // (instead of a whole sort) order the 64.
-  if (lane < 16) {
-    const int pos = wave * 16 + ((wave & 1) ? 15 - lane : lane);
-    mv[pos] = lane < m ? v : -INFINITY;
-    mi[pos] = lane < m ? vi : INT_MAX;
+  wave_topk<8>(x.s, static_cast<int>(L), 64 * wave, 256, m, lane, cv[wave], ci[wave], v, vi);
+  if (m <= 15) {
+    // Each wave's list is sorted best-first; odd waves store theirs reversed,
+    // so that every 32 entries form a bitonic sequence and two merge stages
+    // (instead of a whole sort) order the 64.
+    if (lane < 16) {
+      const int pos = wave * 16 + ((wave & 1) ? 15 - lane : lane);
+      mv[0][pos] = lane < m ? v : -INFINITY;
+      mi[0][pos] = lane < m ? vi : INT_MAX;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    v = mv[0][lane];
+    vi = mi[0][lane];
+    bitonic_steps<32, 16, 64>(v, vi, lane, true);
+  } else {
+    // Up to 63 per wave: wave 0 merges the other lists into its own one at a
+    // time (its list best-first against the other reversed: the better of
+    // each pair is the best 64 of the two, a bitonic sequence).
+    mv[wave][lane] = lane < m ? v : -INFINITY;
+    mi[wave][lane] = lane < m ? vi : INT_MAX;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll 1
+    for (int w = 1; w < 4; ++w) {
+      const float u = mv[w][63 - lane];
+      const int ui = mi[w][63 - lane];
+      if (beats(u, ui, v, vi)) {
+        v = u;
+        vi = ui;
+      }
+      bitonic_merge64(v, vi, lane);
+    }
   }
-  __syncthreads();
-  if (wave != 0) return;
-  v = mv[lane];
-  vi = mi[lane];
-  bitonic_steps<32, 16, 64>(v, vi, lane, true);
   write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
 }
 
-hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T,
-                            int64_t N, int G, int k, const PagedCache& pc, hipStream_t st) {
+hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T, int64_t t0,
+                            int64_t Tw, int64_t N, int G, int Bk, int k, const PagedCache& pc,
+                            hipStream_t st) {
   TopkArgs a;
   a.G = G;
   a.pc = pc;
   a.S = S;
   a.idx = idx;
   a.T = T;
+  a.t0 = t0;
+  a.Tw = Tw;
   a.N = N;
-  a.rows = B * G * T;
-  a.NB = static_cast<int32_t>((N + kBlock - 1) / kBlock);
+  a.rows = B * G * Tw;
+  a.Bk = Bk;
+  a.NB = static_cast<int32_t>((N + Bk - 1) / Bk);
   a.k = k;
   if (a.rows <= 4096 && a.NB >= 1024) {
     // few long rows: spread each row over a workgroup

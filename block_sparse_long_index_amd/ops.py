@@ -139,11 +139,11 @@ def _index_inputs(qI, kI):
     return B, T, G, dI, N, _INDEX_DTYPES[qI.dtype]
 
 
-def index_scores(qI, kI, out=None):
+def index_scores(qI, kI, out=None, Bk=128):
     """Stages 1+2.  qI [B,T,G,128], kI [B,N,128] (both bf16 or both fp8
-    e4m3fn) -> S [B,G,T,NB] fp32."""
+    e4m3fn) -> S [B,G,T,NB] fp32, NB = ceil(N / Bk)."""
     B, T, G, dI, N, sfx = _index_inputs(qI, kI)
-    d = dims(B, T, N, G, G, 1, d_I=dI)
+    d = dims(B, T, N, G, G, 1, d_I=dI, Bk=Bk)
     NB = (N + d.Bk - 1) // d.Bk
     S = out if out is not None else torch.empty(B, G, T, NB, dtype=torch.float32, device=qI.device)
     _need(S, "S", torch.float32, (B, G, T, NB))
@@ -152,11 +152,11 @@ def index_scores(qI, kI, out=None):
     return S
 
 
-def select_blocks(qI, kI, k, out=None, workspace=None):
+def select_blocks(qI, kI, k, out=None, workspace=None, Bk=128):
     """Stages 1-3 fused (bf16 or fp8 e4m3fn inputs).  -> idx [B,G,T,k] int32
     (ascending, -1 padded)."""
     B, T, G, dI, N, sfx = _index_inputs(qI, kI)
-    d = dims(B, T, N, G, G, k, d_I=dI)
+    d = dims(B, T, N, G, G, k, d_I=dI, Bk=Bk)
     idx = out if out is not None else torch.empty(B, G, T, k, dtype=torch.int32, device=qI.device)
     _need(idx, "idx", torch.int32, (B, G, T, k))
     ws, nbytes = _workspace(OP_SELECT_BLOCKS, d, workspace)
@@ -166,11 +166,11 @@ def select_blocks(qI, kI, k, out=None, workspace=None):
     return idx
 
 
-def select_blocks_from_scores(S, k, N, out=None):
+def select_blocks_from_scores(S, k, N, out=None, Bk=128):
     """Stage 3 from S [B,G,T,NB] fp32 (query row t at position N - T + t)."""
     B, G, T, NB = S.shape
     _need(S, "S", torch.float32)
-    d = dims(B, T, N, G, G, k)
+    d = dims(B, T, N, G, G, k, Bk=Bk)
     if NB != (N + d.Bk - 1) // d.Bk:
         raise ValueError("S has %d blocks, N=%d needs %d" % (NB, N, (N + d.Bk - 1) // d.Bk))
     idx = out if out is not None else torch.empty(B, G, T, k, dtype=torch.int32, device=S.device)
@@ -180,7 +180,7 @@ def select_blocks_from_scores(S, k, N, out=None):
     return idx
 
 
-def sparse_attn_prefill(q, K, V, idx, return_lse=False, out=None, workspace=None):
+def sparse_attn_prefill(q, K, V, idx, return_lse=False, out=None, workspace=None, Bk=128):
     """Stage 4, KV-outer.  q [B,T,Hq,128], K/V [B,G,N,128] bf16, idx [B,G,T,k]
     -> O [B,T,Hq,128] bf16 (and lse [B,Hq,T] fp32)."""
     B, T, Hq, dh = q.shape
@@ -190,7 +190,7 @@ def sparse_attn_prefill(q, K, V, idx, return_lse=False, out=None, workspace=None
     _need(K, "K", torch.bfloat16, (B, G, N, dh))
     _need(V, "V", torch.bfloat16, (B, G, N, dh))
     _need(idx, "idx", torch.int32, (B, G, T, k))
-    d = dims(B, T, N, Hq, G, k, d_h=dh)
+    d = dims(B, T, N, Hq, G, k, d_h=dh, Bk=Bk)
     O = out if out is not None else torch.empty_like(q)
     _need(O, "O", torch.bfloat16, q.shape)
     lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device) if return_lse else None
@@ -201,7 +201,7 @@ def sparse_attn_prefill(q, K, V, idx, return_lse=False, out=None, workspace=None
     return (O, lse) if return_lse else O
 
 
-def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None):
+def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None, Bk=128):
     """Stage 4 for one new token per sequence.  q [B,Hq,128], K/V [B,G,N,128],
     idx [B,G,1,k] -> O [B,Hq,128] bf16 (and lse [B,Hq] fp32)."""
     B, Hq, dh = q.shape
@@ -211,7 +211,7 @@ def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None)
     _need(K, "K", torch.bfloat16, (B, G, N, dh))
     _need(V, "V", torch.bfloat16, (B, G, N, dh))
     _need(idx, "idx", torch.int32, (B, G, 1, k))
-    d = dims(B, 1, N, Hq, G, k, d_h=dh)
+    d = dims(B, 1, N, Hq, G, k, d_h=dh, Bk=Bk)
     O = out if out is not None else torch.empty_like(q)
     _need(O, "O", torch.bfloat16, q.shape)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
@@ -222,14 +222,14 @@ def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None)
     return (O, lse) if return_lse else O
 
 
-def forward(qI, kI, q, K, V, k, return_lse=False):
+def forward(qI, kI, q, K, V, k, return_lse=False, Bk=128):
     """The whole path for prefill (T > 1) or decode (T == 1)."""
-    idx = select_blocks(qI, kI, k)
+    idx = select_blocks(qI, kI, k, Bk=Bk)
     if qI.shape[1] == 1:
         res = sparse_attn_decode(q.reshape(q.shape[0], q.shape[2], q.shape[3]), K, V, idx,
-                                 return_lse=return_lse)
+                                 return_lse=return_lse, Bk=Bk)
     else:
-        res = sparse_attn_prefill(q, K, V, idx, return_lse=return_lse)
+        res = sparse_attn_prefill(q, K, V, idx, return_lse=return_lse, Bk=Bk)
     return idx, res
 
 

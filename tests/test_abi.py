@@ -58,7 +58,8 @@ MISALIGNED = ctypes.c_void_p(0x1004)
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), -1), (dict(T=0), -1), (dict(T=300), -1), (dict(N=0, T=0), -1),
     (dict(Hq=7), -1), (dict(k=0), -1), (dict(G=3, Hq=9), -2), (dict(k=17), -2),
-    (dict(d_h=64), -2), (dict(d_I=64), -2), (dict(Bk=64), -2),
+    (dict(d_h=64), -2), (dict(d_I=64), -2), (dict(Bk=96), -2), (dict(Bk=256), -2),
+    (dict(Bk=64, k=33), -2), (dict(Bk=32, k=65), -2), (dict(Bk=32, N=600000, T=300), -2),
     (dict(Hq=64, G=2), -2),
 ])
 def test_bad_dims(kw, code):
@@ -145,3 +146,26 @@ def test_paged_argument_checks():
                                           good["lens"], FAKE, FAKE, None, FAKE, 16, None) == -3
     assert L.msa_sparse_attn_decode_paged(ctypes.byref(dp), FAKE, FAKE, FAKE, P(4), FAKE,
                                           good["lens"], FAKE, FAKE, None, FAKE, 1 << 30, None) == -1
+
+
+def test_block_size_checks():
+    """Blocks of 64 and 32 keys (k up to 32 and 64): the selection of a
+    prefill materialises a window of block scores in the workspace; fp8 index
+    inputs and paged caches take 128-key blocks only."""
+    L = ops.lib()
+    d64 = _good(Bk=64, k=32, N=1024, T=1024)
+    need = L.msa_workspace_bytes(ops.OP_SELECT_BLOCKS, ctypes.byref(d64))
+    assert need == 1024 * 2 * 16 * 4  # all rows: B * G * NB floats per row
+    assert L.msa_select_blocks(ctypes.byref(d64), FAKE, FAKE, FAKE, FAKE, 2 * 16 * 4 - 4,
+                               None) == -3
+    assert L.msa_select_blocks_fp8(ctypes.byref(d64), FAKE, FAKE, FAKE, FAKE, need, None) == -2
+    assert L.msa_index_scores_fp8(ctypes.byref(d64), FAKE, FAKE, FAKE, None) == -2
+    d1 = _good(Bk=32, k=64, N=4096, T=1)
+    assert L.msa_workspace_bytes(ops.OP_SELECT_BLOCKS, ctypes.byref(d1)) == 2 * 128 * 4
+    P = ctypes.c_int64
+    assert L.msa_select_blocks_paged(ctypes.byref(d1), FAKE, FAKE, P(4), FAKE,
+                                     ctypes.c_void_p(0x1008), FAKE, FAKE, 1 << 30, None) == -2
+    assert b"128-token pages" in L.msa_last_error()
+    # decode and prefill attention workspaces grow with k
+    assert (L.msa_workspace_bytes(ops.OP_ATTN_DECODE, ctypes.byref(d1)) >
+            L.msa_workspace_bytes(ops.OP_ATTN_DECODE, ctypes.byref(_good(N=4096, T=1))))
