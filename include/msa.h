@@ -40,8 +40,12 @@
  * Errors.  Arguments are validated on the host before any HIP call; on an
  *   error nothing is launched and no output is touched.  A HIP launch error
  *   returns MSA_ERR_HIP (text from msa_last_error()).
- * Supported now: d_h == d_I == 128, Bk == 128, 1 <= k <= 16,
- *   G in {1,2,4,8,16}, Hq / G in {1,2,4,8,16,32}; others: MSA_ERR_UNSUPPORTED.
+ * Supported now: d_h == d_I == 128; Bk in {32, 64, 128} with 1 <= k and
+ *   k * Bk <= 2048 (the study notes' fixed budget of section 2-3, which its
+ *   block-size ablation in section 4-2 keeps: k <= 16, 32, 64) and at most
+ *   16384 blocks per sequence; G in {1,2,4,8,16}, Hq / G in {1,2,4,8,16};
+ *   N <= 2^21.  The fp8 index calls and the paged calls take Bk == 128.
+ *   Others: MSA_ERR_UNSUPPORTED.
  */
 #ifndef MSA_H
 #define MSA_H
@@ -99,8 +103,14 @@ int msa_index_scores(const msa_dims_t *dims, const void *qI, const void *kI,
  * attention, for top-k kept in registers while the keys stream).
  *   qI, kI as for msa_index_scores
  *   idx int32 [B, G, T, k]    out: selected blocks (see conventions)
- *   ws / ws_bytes             scratch, >= msa_workspace_bytes(MSA_OP_SELECT_BLOCKS)
- *                             (zero bytes for T > 1; decode uses a score row)
+ *   ws / ws_bytes             scratch, >= msa_workspace_bytes(MSA_OP_SELECT_BLOCKS):
+ *                             decode (T == 1) uses a row of block scores; a
+ *                             prefill with Bk == 128 needs none; with Bk < 128
+ *                             the block scores of a window of query rows are
+ *                             materialised and ranked, window after window (the
+ *                             default size holds up to 1 GB of scores; any
+ *                             workspace of at least one row's scores,
+ *                             B * G * ceil(N/Bk) floats, is accepted)
  */
 int msa_select_blocks(const msa_dims_t *dims, const void *qI, const void *kI,
                       int32_t *idx, void *ws, size_t ws_bytes, void *stream);
