@@ -42,7 +42,7 @@
  *   returns MSA_ERR_HIP (text from msa_last_error()).
  * Supported now: d_h == d_I == 128; Bk in {32, 64, 128} with 1 <= k and
  *   k * Bk <= 2048 (the study notes' fixed budget of section 2-3, which its
- *   block-size ablation in section 4-2 keeps: k <= 16, 32, 64) and at most
+ *   block-size comparison in section 4-6 keeps: k <= 16, 32, 64) and at most
  *   16384 blocks per sequence; G in {1,2,4,8,16}, Hq / G in {1,2,4,8,16};
  *   N <= 2^21.  The fp8 index calls and the paged calls take Bk == 128.
  *   Others: MSA_ERR_UNSUPPORTED.
