@@ -1,6 +1,6 @@
 """GPU parity for blocks of 64 and 32 keys at the 2048-token budget (k = 32
-and k = 64): the study notes' engineering notes (section 4-6) compare block sizes 32, 64 and 128 at a fixed k * Bk
-fixed.  Same bar as the 128-key path: block indices and scores bit-exact
+and k = 64): the study notes' engineering notes (section 4-6) compare block
+sizes 32, 64 and 128 with the number of selected tokens fixed.  Same bar as the 128-key path: block indices and scores bit-exact
 against the oracle on every row of small shapes, O within max-abs 2e-2 and
 mean-abs 2e-3, lse within 1e-3; the 32K workload with Bk = 64 on sampled rows
 plus structural invariants on every row."""
