@@ -199,20 +199,21 @@ def pin_select_exhaustive(orc):
 
 def pin_select_lexsort(orc):
     g = np.random.default_rng(6)
-    Bk, k, NB = 16, 16, 200
-    N = T = NB * Bk
-    d = dims_of(1, T, N, 3, 3, 128, 8, Bk, k)
-    rt = g.integers(0, T, size=300)
-    S = np.round(g.normal(size=(rt.size, 3, NB)) * 4)  # many ties
-    idx = orc.select(d, rt, S)
-    for r in range(rt.size):
-        L = rt[r] // Bk
-        m = min(k - 1, L)
-        for gg in range(3):
-            cand = np.arange(L)
-            order = np.lexsort((cand, -S[r, gg, :L]))[:m]
-            want = sorted(cand[order].tolist()) + [L] + [-1] * (k - m - 1)
-            assert idx[r, gg].tolist() == want
+    # (Bk, k, NB): 128-key-style k = 16, and the 2048-token budget at Bk = 32 (k = 64)
+    for Bk, k, NB in ((16, 16, 200), (32, 64, 90)):
+        N = T = NB * Bk
+        d = dims_of(1, T, N, 3, 3, 128, 8, Bk, k)
+        rt = g.integers(0, T, size=300)
+        S = np.round(g.normal(size=(rt.size, 3, NB)) * 4)  # many ties
+        idx = orc.select(d, rt, S)
+        for r in range(rt.size):
+            L = rt[r] // Bk
+            m = min(k - 1, L)
+            for gg in range(3):
+                cand = np.arange(L)
+                order = np.lexsort((cand, -S[r, gg, :L]))[:m]
+                want = sorted(cand[order].tolist()) + [L] + [-1] * (k - m - 1)
+                assert idx[r, gg].tolist() == want
 
 
 def pin_select_needle(orc):
@@ -330,19 +331,20 @@ def pin_attend_dense_equivalence(orc):
 
 def pin_attend_masked_sdpa(orc):
     """Any selection: attention over the support equals SDPA with the
-    support's boolean mask."""
-    B, T, N, Hq, G, dh, Bk, k = 1, 64, 64, 6, 3, 16, 4, 4
+    support's boolean mask (also with more than 16 slots)."""
+    for (B, T, N, Hq, G, dh, Bk, k) in ((1, 64, 64, 6, 3, 16, 4, 4),
+                                        (1, 200, 200, 4, 2, 8, 2, 40)):
 
-    def random_sel(d, rb, rt, g):
-        S = torch.randn(rb.size, d.G, -(-N // Bk), generator=g).double().numpy()
-        return orc.select(d, rt, S)
+        def random_sel(d, rb, rt, g):
+            S = torch.randn(rb.size, d.G, -(-N // Bk), generator=g).double().numpy()
+            return orc.select(d, rt, S)
 
-    q, K, V, idx, O, lse = _attend_case(orc, B, T, N, Hq, G, dh, Bk, k, 22,
-                                        random_sel)
-    mask = _mask_from_idx(idx, T, N, Bk, G)
-    refO, refL = _sdpa_reference(q[0], K[0], V[0], mask, Hq // G)
-    assert np.allclose(O[0], refO, rtol=1e-10, atol=1e-10)
-    assert np.allclose(lse[0], refL, rtol=1e-10, atol=1e-10)
+        q, K, V, idx, O, lse = _attend_case(orc, B, T, N, Hq, G, dh, Bk, k, 22,
+                                            random_sel)
+        mask = _mask_from_idx(idx, T, N, Bk, G)
+        refO, refL = _sdpa_reference(q[0], K[0], V[0], mask, Hq // G)
+        assert np.allclose(O[0], refO, rtol=1e-10, atol=1e-10)
+        assert np.allclose(lse[0], refL, rtol=1e-10, atol=1e-10)
 
 
 def pin_attend_k1_block_diagonal(orc):
