@@ -11,6 +11,7 @@ top-k leg on the materialised 128K scores (us), and the CPU oracle baseline
 on a bounded sample of rows.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu] [--only prefill]
+    python bench.py --block-size 64 --only prefill   # 64-key blocks, k = 32
 """
 from __future__ import annotations
 
@@ -67,25 +68,36 @@ def ev():
     return torch.cuda.Event(enable_timing=True)
 
 
+def with_block_size(w, args):
+    """The workload with --block-size / --k applied (the same token budget by
+    default: k = 2048 / Bk)."""
+    if args.block_size == w.Bk and args.k is None:
+        return w
+    k = args.k if args.k is not None else 2048 // args.block_size
+    return w.replace(Bk=args.block_size, k=k, name="%s_bk%d" % (w.name, args.block_size))
+
+
 def prefill_leg(args):
-    w = WORKLOADS[args.workload]
+    w = with_block_size(WORKLOADS[args.workload], args)
     log("[bench] generating", w.name)
     inp = make_inputs(w, device="cuda")
     qI, kI, q, K, V = inp["qI"], inp["kI"], inp["q"], inp["K"], inp["V"]
     idx = torch.empty(w.B, w.G, w.T, w.k, dtype=torch.int32, device="cuda")
     O = torch.empty_like(q)
-    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k)
+    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k, Bk=w.Bk)
     ws = torch.empty(max(1, ops.workspace_bytes(ops.OP_ATTN_PREFILL, d)), dtype=torch.uint8,
                      device="cuda")
+    nsel = ops.workspace_bytes(ops.OP_SELECT_BLOCKS, d)
+    ws_sel = torch.empty(nsel, dtype=torch.uint8, device="cuda") if nsel else None
     torch.cuda.synchronize()
 
     def step(evs=None):
         if evs is not None:
             evs[0].record()
-        ops.select_blocks(qI, kI, w.k, out=idx)
+        ops.select_blocks(qI, kI, w.k, out=idx, workspace=ws_sel, Bk=w.Bk)
         if evs is not None:
             evs[1].record()
-        ops.sparse_attn_prefill(q, K, V, idx, out=O, workspace=ws)
+        ops.sparse_attn_prefill(q, K, V, idx, out=O, workspace=ws, Bk=w.Bk)
         if evs is not None:
             evs[2].record()
 
@@ -179,6 +191,8 @@ def fp8_leg(args, pre):
 
 def decode_leg(args, fp8=False):
     w = WORKLOADS["decode_256k_b16"]
+    if not fp8:  # the fp8 index calls take 128-key blocks
+        w = with_block_size(w, args)
     log("[bench] generating", w.name, "(fp8 index keys)" if fp8 else "")
     inp = make_inputs(w, device="cuda")
     qI, kI, K, V = inp["qI"], inp["kI"], inp["K"], inp["V"]
@@ -189,7 +203,7 @@ def decode_leg(args, fp8=False):
     q = inp["q"][:, 0].contiguous()
     idx = torch.empty(w.B, w.G, 1, w.k, dtype=torch.int32, device="cuda")
     O = torch.empty_like(q)
-    d = ops.dims(w.B, 1, w.N, w.Hq, w.G, w.k)
+    d = ops.dims(w.B, 1, w.N, w.Hq, w.G, w.k, Bk=w.Bk)
     ws_s = torch.empty(ops.workspace_bytes(ops.OP_SELECT_BLOCKS, d), dtype=torch.uint8,
                        device="cuda")
     ws_a = torch.empty(ops.workspace_bytes(ops.OP_ATTN_DECODE, d), dtype=torch.uint8,
@@ -200,8 +214,8 @@ def decode_leg(args, fp8=False):
     sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def step():
-        ops.select_blocks(qI, kI, w.k, out=idx, workspace=ws_s)
-        ops.sparse_attn_decode(q, K, V, idx, out=O, workspace=ws_a)
+        ops.select_blocks(qI, kI, w.k, out=idx, workspace=ws_s, Bk=w.Bk)
+        ops.sparse_attn_decode(q, K, V, idx, out=O, workspace=ws_a, Bk=w.Bk)
 
     for _ in range(3):
         step()
@@ -281,6 +295,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-reps", type=int, default=30)
+    ap.add_argument("--block-size", type=int, default=128, choices=(32, 64, 128),
+                    help="Bk of the prefill and bf16 decode legs (default 128)")
+    ap.add_argument("--k", type=int, default=None,
+                    help="blocks per query and group (default: 2048 / block size)")
     ap.add_argument("--topk-reps", type=int, default=10)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy (counter calibration) and exit")
@@ -318,22 +336,27 @@ def main():
                          "G": w.G, "d_h": w.d_h, "d_I": w.d_I, "Bk": w.Bk, "k": w.k,
                          "needles": w.needles, "seed": w.seed}
         ach = fl["index"] / (sel * 1e-3) / 1e12
+        fused = w.Bk == 128
         out["roofline"] = {"kernel": "index_tile_kernel (fused select: scores, block max, "
-                                     "top-k)",
+                                     "top-k)" if fused else
+                                     "index_tile_kernel (block scores, written) + "
+                                     "topk_rows_kernel, window after window",
                            "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                           "traffic": select_traffic(),
+                           "traffic": select_traffic() if fused else None,
                            "flops_per_launch": fl["index"], "avg_launch_ms": sel}
         out["stages"] = {"select_ms": sel, "attention_ms": att,
                          "attention_TFLOPs": fl["main"] / (att * 1e-3) / 1e12,
                          "index_flops": fl["index"], "main_flops": fl["main"]}
-        if args.only in ("", "topk"):
+        if not fused:
+            log("[bench] Bk = %d: the top-k, fp8 and CPU legs run at Bk = 128 only" % w.Bk)
+        if args.only in ("", "topk") and fused:
             log("[bench] top-k leg")
             out["topk"] = topk_leg(args, pre)
-        if args.only in ("", "fp8"):
+        if args.only in ("", "fp8") and fused:
             log("[bench] fp8 index leg")
             out["fp8_index"] = fp8_leg(args, pre)
-        if not args.no_cpu and args.only == "":
+        if not args.no_cpu and args.only == "" and fused:
             log("[bench] cpu baseline")
             out["cpu_baseline"], out["parity_sample"] = cpu_leg(args, pre)
         del pre
