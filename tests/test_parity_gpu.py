@@ -301,3 +301,41 @@ def test_full_decode_256k():
 
 def test_full_prefill_1m():
     _full("prefill_1m", 24, scores=False)
+
+
+# ------------------------------------------------- the largest supported sizes
+def test_max_decode_2m():
+    """Decode over caches of 2^21 tokens (the largest N): 16384 blocks per
+    row, rows of the four-waves-per-row top-k with most candidates in memory."""
+    w = Workload("decode_2m", B=2, T=1, N=1 << 21, Hq=64, G=8, k=16, seed=31)
+    say("workload", w.name, "generating")
+    inp = make_inputs(w, device="cuda")
+    idx = ops.select_blocks(inp["qI"], inp["kI"], w.k)
+    S = ops.index_scores(inp["qI"], inp["kI"])
+    O, lse = ops.sparse_attn_decode(inp["q"][:, 0].contiguous(), inp["K"], inp["V"], idx,
+                                    return_lse=True)
+    torch.cuda.synchronize()
+    check_invariants(w, idx)
+    say("workload", w.name, "oracle")
+    compare_rows(w, inp, idx, O, lse, np.arange(2), np.zeros(2, dtype=np.int64), S=S,
+                 tag=w.name)
+
+
+def test_max_prefill_2m():
+    """Prefill of 2^21 tokens (the largest N) with one head per group, in the
+    benchmark's launch configuration; sampled rows against the oracle,
+    invariants on every row."""
+    w = Workload("prefill_2m", B=1, T=1 << 21, N=1 << 21, Hq=8, G=8, k=16,
+                 needles="per_64k", seed=32)
+    say("workload", w.name, "generating")
+    inp = make_inputs(w, device="cuda")
+    torch.cuda.synchronize()
+    say("workload", w.name, "select")
+    idx = ops.select_blocks(inp["qI"], inp["kI"], w.k)
+    say("workload", w.name, "attention")
+    O, lse = ops.sparse_attn_prefill(inp["q"], inp["K"], inp["V"], idx, return_lse=True)
+    torch.cuda.synchronize()
+    check_invariants(w, idx)
+    rb, rt = sample_rows(w, 14)
+    say("workload", w.name, "oracle on", len(rb), "rows")
+    compare_rows(w, inp, idx, O, lse, rb.numpy(), rt.numpy(), tag=w.name)
