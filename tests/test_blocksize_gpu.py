@@ -117,3 +117,45 @@ def test_full_prefill_32k_bk64():
     check_invariants(w, idx)
     rb, rt = sample_rows(w, 48)
     compare_rows(w, inp, idx, O, lse, rb.numpy(), rt.numpy(), tag="prefill_32k_bk64")
+
+
+def _random_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        Bk = int(g.choice([32, 64, 128]))
+        G = int(g.choice([1, 2, 4, 8, 16]))
+        hg = int(g.choice([1, 2, 4, 8, 16]))
+        if G * hg > 64:
+            continue
+        k = int(g.integers(1, 2048 // Bk + 1))
+        N = int(g.integers(1, 3000))
+        T = int(g.choice([1, N, int(g.integers(1, N + 1))]))
+        B = int(g.integers(1, 4))
+        cases.append((B, T, N, G * hg, G, k, Bk))
+    return cases
+
+
+@pytest.mark.parametrize("B,T,N,Hq,G,k,Bk", _random_cases(16, 2026))
+def test_random_shapes(B, T, N, Hq, G, k, Bk):
+    """Seeded random shapes over every supported block size, group layout,
+    k, chunked and decode rows: every row against the oracle."""
+    w = Workload("rand", B=B, T=T, N=N, Hq=Hq, G=G, k=k, Bk=Bk, seed=N * 7 + T)
+    say("case", w)
+    inp = make_inputs(w, device="cuda")
+    idx = ops.select_blocks(inp["qI"], inp["kI"], k, Bk=Bk)
+    S = ops.index_scores(inp["qI"], inp["kI"], Bk=Bk)
+    if T == 1:
+        O, lse = ops.sparse_attn_decode(inp["q"][:, 0].contiguous(), inp["K"], inp["V"], idx,
+                                        return_lse=True, Bk=Bk)
+    else:
+        O, lse = ops.sparse_attn_prefill(inp["q"], inp["K"], inp["V"], idx, return_lse=True,
+                                         Bk=Bk)
+    torch.cuda.synchronize()
+    check_invariants(w, idx)
+    rb = np.repeat(np.arange(B), T)
+    rt = np.tile(np.arange(T), B)
+    if rb.size > 600:  # every row of small cases, a sample of larger ones
+        keep = np.random.default_rng(N).choice(rb.size, 600, replace=False)
+        rb, rt = rb[keep], rt[keep]
+    compare_rows(w, inp, idx, O, lse, rb, rt, S=S, tag="rand")
