@@ -94,6 +94,8 @@ class OracleLib:
         lib.msa_oracle_e4m3_values.argtypes = [P]
         lib.msa_oracle_select.argtypes = [ctypes.POINTER(Dims), i64, P, P, P]
         lib.msa_oracle_attend.argtypes = [ctypes.POINTER(Dims), i64, P, P, P, P, P, P, P, P]
+        lib.msa_oracle_attend_backward.argtypes = [ctypes.POINTER(Dims), i64, P, P, P, P, P, P,
+                                                   P, i64, i64, P, P, P]
         for f in (lib.msa_oracle_block_scores, lib.msa_oracle_block_scores_fp8,
                   lib.msa_oracle_e4m3_values, lib.msa_oracle_select, lib.msa_oracle_attend):
             f.restype = None
@@ -172,6 +174,36 @@ class OracleLib:
                                    _ptr(Kb), _ptr(Vb), _ptr(ix), _ptr(O), _ptr(lse))
         return O, lse
 
+    def attend_backward(self, d: Dims, row_b, row_t, q_rows, dO_rows, K, V, idx, blk_lo=0,
+                        nblk=None):
+        """Stage 4 gradients for the listed rows, given their selection.
+        q_rows, dO_rows [n, Hq, d_h]; K/V [B, G, N, d_h]; idx [n, G, k] ->
+        (dq [n, Hq, d_h], dK, dV [B, G, nblk*Bk, d_h]) in fp64; dK and dV hold
+        the listed rows' contributions to the keys of blocks
+        blk_lo .. blk_lo+nblk-1 (all blocks by default)."""
+        rb, rt = _rows(row_b, row_t)
+        q = bits(q_rows)
+        g = bits(dO_rows)
+        Kb = bits(K)
+        Vb = bits(V)
+        ix = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+        n = rb.size
+        NB = (d.N + d.Bk - 1) // d.Bk
+        if nblk is None:
+            nblk = NB - blk_lo
+        assert 0 <= blk_lo and blk_lo + nblk <= NB and nblk >= 1
+        assert q.shape == (n, d.Hq, d.d_h) and g.shape == q.shape, (q.shape, g.shape)
+        assert Kb.shape == (d.B, d.G, d.N, d.d_h) and Vb.shape == Kb.shape
+        assert ix.shape == (n, d.G, d.k)
+        assert ((ix >= -1) & (ix < NB)).all()
+        dq = np.empty((n, d.Hq, d.d_h), dtype=np.float64)
+        dK = np.empty((d.B, d.G, nblk * d.Bk, d.d_h), dtype=np.float64)
+        dV = np.empty_like(dK)
+        self.lib.msa_oracle_attend_backward(ctypes.byref(d), n, _ptr(rb), _ptr(rt), _ptr(q),
+                                            _ptr(g), _ptr(Kb), _ptr(Vb), _ptr(ix), blk_lo, nblk,
+                                            _ptr(dq), _ptr(dK), _ptr(dV))
+        return dq, dK, dV
+
     def forward(self, d: Dims, row_b, row_t, qI_rows, kI, q_rows, K, V):
         """All four stages for the listed rows; returns S, idx, O, lse and
         the wall time of each part."""
@@ -210,6 +242,10 @@ def select(*a, **kw):
 
 def attend(*a, **kw):
     return default().attend(*a, **kw)
+
+
+def attend_backward(*a, **kw):
+    return default().attend_backward(*a, **kw)
 
 
 def forward(*a, **kw):

@@ -20,6 +20,8 @@
  *            keys j <= p of the selected blocks of h's group g = h / (Hq/G);
  *            lse = natural log of the softmax denominator (with the max added
  *            back)
+ *   stage 4 backward  dq, dK, dV of sum(dO . O) over the same support, the
+ *            selection held fixed (msa_oracle_attend_backward)
  *
  * Sources (the MSA study-notes page, dimensionstp.github.io/study-concept/msa):
  *   stages 1-3: section 2-3 "Fixed attention budget", the three displayed
@@ -296,4 +298,137 @@ void msa_oracle_attend(const msa_oracle_dims *d, int64_t nrows,
         free(z);
         free(key);
     }
+}
+
+/* Stage 4 backward.  The selection is a constant of the step (the discrete
+ * top-k has no gradient; the Flash-MSA training blog, "Backward pass", keeps
+ * the forward's block indices for it), so the gradients are those of exact
+ * softmax attention over each row's support.  With L = sum over rows and heads
+ * of dO . O, per (row, head), over the support keys j:
+ *   z_j  = q . K_j / sqrt(d_h)          P_j = softmax(z)_j
+ *   dP_j = dO . V_j                     dz_j = P_j (dP_j - sum_i P_i dP_i)
+ *   dq   = sum_j dz_j K_j / sqrt(d_h)
+ *   dK_j += dz_j q / sqrt(d_h)          dV_j += P_j dO
+ * (the softmax Jacobian dP_i/dz_j = P_i (delta_ij - P_j) applied to dL/dP).
+ * dq: [nrows, Hq, d_h] for the listed rows.  dK, dV: [B, G, nblk*Bk, d_h],
+ * the keys of blocks blk_lo .. blk_lo+nblk-1; they receive the contributions
+ * of the listed rows only (contributions to other keys are dropped), so a
+ * window of blocks is exact when every row that selects one of its blocks is
+ * listed.  Row-parallel over (sequence, head); a head's contributions are
+ * summed into the group in head order. */
+void msa_oracle_attend_backward(const msa_oracle_dims *d, int64_t nrows,
+                                const int64_t *row_b, const int64_t *row_t,
+                                const uint16_t *q_rows, const uint16_t *dO_rows,
+                                const uint16_t *K, const uint16_t *V,
+                                const int32_t *idx, int64_t blk_lo, int64_t nblk,
+                                double *dq, double *dK, double *dV)
+{
+    const int64_t Hq = d->Hq, G = d->G, dh = d->d_h, k = d->k, Bk = d->Bk;
+    const int64_t hg = Hq / G;
+    const int64_t wkeys = nblk * Bk, key_lo = blk_lo * Bk;
+    const double root = sqrt((double)dh);
+    const size_t per_head = (size_t)(wkeys * dh);
+    double *hk = (double *)calloc((size_t)(d->B * Hq) * per_head, sizeof(double));
+    double *hv = (double *)calloc((size_t)(d->B * Hq) * per_head, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < d->B * Hq; ++bh) {
+        const int64_t b = bh / Hq, h = bh % Hq, g = h / hg;
+        double *myk = hk + (size_t)bh * per_head;
+        double *myv = hv + (size_t)bh * per_head;
+        double *qd = (double *)malloc(sizeof(double) * dh);
+        double *go = (double *)malloc(sizeof(double) * dh);
+        double *z = (double *)malloc(sizeof(double) * (size_t)(k * Bk));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(k * Bk));
+        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)(k * Bk));
+        const uint16_t *Kg = K + (b * G + g) * d->N * dh;
+        const uint16_t *Vg = V + (b * G + g) * d->N * dh;
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (row_b[r] != b)
+                continue;
+            const int64_t p = position_of(d, row_t[r]);
+            const int32_t *sel = idx + (r * G + g) * k;
+            for (int64_t c = 0; c < dh; ++c) {
+                qd[c] = widen_bf16(q_rows[(r * Hq + h) * dh + c]);
+                go[c] = widen_bf16(dO_rows[(r * Hq + h) * dh + c]);
+            }
+            /* the support: visible keys of the distinct selected blocks */
+            int64_t n = 0;
+            for (int64_t s = 0; s < k; ++s) {
+                const int64_t blk = sel[s];
+                if (blk < 0)
+                    continue;
+                int dup = 0;
+                for (int64_t u = 0; u < s; ++u)
+                    if (sel[u] == blk)
+                        dup = 1;
+                if (dup)
+                    continue;
+                for (int64_t j = blk * Bk; j < (blk + 1) * Bk && j <= p; ++j)
+                    key[n++] = j;
+            }
+            double m = -INFINITY;
+            for (int64_t i = 0; i < n; ++i) {
+                double dot = 0.0, dv = 0.0;
+                for (int64_t c = 0; c < dh; ++c) {
+                    dot += qd[c] * widen_bf16(Kg[key[i] * dh + c]);
+                    dv += go[c] * widen_bf16(Vg[key[i] * dh + c]);
+                }
+                z[i] = dot / root;
+                dp[i] = dv;
+                if (z[i] > m)
+                    m = z[i];
+            }
+            double l = 0.0;
+            for (int64_t i = 0; i < n; ++i) {
+                z[i] = exp(z[i] - m); /* z now holds the unnormalised P */
+                l += z[i];
+            }
+            double pdp = 0.0;
+            for (int64_t i = 0; i < n; ++i) {
+                z[i] /= l;
+                pdp += z[i] * dp[i];
+            }
+            double *dqr = dq + (r * Hq + h) * dh;
+            for (int64_t c = 0; c < dh; ++c)
+                dqr[c] = 0.0;
+            for (int64_t i = 0; i < n; ++i) {
+                const double dz = z[i] * (dp[i] - pdp);
+                const uint16_t *kv = Kg + key[i] * dh;
+                for (int64_t c = 0; c < dh; ++c)
+                    dqr[c] += dz * widen_bf16(kv[c]) / root;
+                const int64_t kw = key[i] - key_lo;
+                if (kw < 0 || kw >= wkeys)
+                    continue;
+                for (int64_t c = 0; c < dh; ++c) {
+                    myk[kw * dh + c] += dz * qd[c] / root;
+                    myv[kw * dh + c] += z[i] * go[c];
+                }
+            }
+        }
+        free(qd);
+        free(go);
+        free(z);
+        free(dp);
+        free(key);
+    }
+    /* group sums, heads in order */
+    for (int64_t b = 0; b < d->B; ++b)
+        for (int64_t g = 0; g < G; ++g) {
+            double *ok = dK + (size_t)(b * G + g) * per_head;
+            double *ov = dV + (size_t)(b * G + g) * per_head;
+            for (size_t e = 0; e < per_head; ++e) {
+                ok[e] = 0.0;
+                ov[e] = 0.0;
+            }
+            for (int64_t h = g * hg; h < (g + 1) * hg; ++h) {
+                const double *sk = hk + (size_t)(b * Hq + h) * per_head;
+                const double *sv = hv + (size_t)(b * Hq + h) * per_head;
+                for (size_t e = 0; e < per_head; ++e) {
+                    ok[e] += sk[e];
+                    ov[e] += sv[e];
+                }
+            }
+        }
+    free(hk);
+    free(hv);
 }

@@ -449,6 +449,178 @@ def pin_fp8_scores_match_bf16_on_integers(orc):
     assert np.array_equal(S16, S8)
 
 
+
+# ------------------------------------------------------------ stage 4 backward
+def _bwd_case(orc, B, T, N, Hq, G, dh, Bk, k, seed, dense=False):
+    """Random q, K, V, dO and a selection made by the oracle's own ranking
+    of random block scores (or every visible block when dense)."""
+    g = _gen(seed)
+    q = _randn_bf16(g, (B, T, Hq, dh))
+    K = _randn_bf16(g, (B, G, N, dh))
+    V = _randn_bf16(g, (B, G, N, dh))
+    dO = _randn_bf16(g, (B, T, Hq, dh))
+    d = dims_of(B, T, N, Hq, G, dh, 8, Bk, k)
+    rb, rt = _all_rows(B, T)
+    NB = -(-N // Bk)
+    if dense:
+        idx = np.full((rb.size, G, k), -1, dtype=np.int32)
+        for r in range(rb.size):
+            L = (N - T + rt[r]) // Bk
+            idx[r, :, :L + 1] = np.arange(L + 1)
+    else:
+        S = torch.randn(rb.size, G, NB, generator=g).double().numpy()
+        idx = orc.select(d, rt, S)
+    return d, rb, rt, q, K, V, dO, idx
+
+
+def _autograd_reference(q, K, V, dO, mask, hg):
+    """Gradients of sum(dO * O) for softmax attention under a boolean mask,
+    by torch autograd in fp64.  q/dO [T,Hq,dh], K/V [G,N,dh], mask [G,T,N]."""
+    qq = q.double().permute(1, 0, 2).clone().requires_grad_(True)  # [Hq,T,dh]
+    kk = K.double().clone().requires_grad_(True)
+    vv = V.double().clone().requires_grad_(True)
+    ke = kk.repeat_interleave(hg, dim=0)
+    ve = vv.repeat_interleave(hg, dim=0)
+    mm = mask.repeat_interleave(hg, dim=0)
+    sc = (qq @ ke.transpose(1, 2)) / math.sqrt(qq.shape[-1])
+    sc = sc.masked_fill(~mm, -math.inf)
+    out = torch.softmax(sc, dim=-1) @ ve
+    (out * dO.double().permute(1, 0, 2)).sum().backward()
+    return qq.grad.permute(1, 0, 2).numpy(), kk.grad.numpy(), vv.grad.numpy()
+
+
+def pin_backward_autograd(orc):
+    """dq, dK, dV equal torch autograd through masked softmax attention (the
+    support's mask), GQA heads summed into their group; a window of blocks
+    equals the same slice of the full result."""
+    for (B, T, N, Hq, G, dh, Bk, k) in ((1, 60, 60, 6, 3, 16, 4, 4),
+                                        (2, 23, 41, 4, 2, 8, 4, 3),
+                                        (1, 150, 150, 4, 1, 8, 2, 40)):
+        d, rb, rt, q, K, V, dO, idx = _bwd_case(orc, B, T, N, Hq, G, dh, Bk, k, 31)
+        dq, dK, dV = orc.attend_backward(d, rb, rt, q.reshape(-1, Hq, dh),
+                                         dO.reshape(-1, Hq, dh), K, V, idx)
+        dq = dq.reshape(B, T, Hq, dh)
+        assert not dK[:, :, N:].any() and not dV[:, :, N:].any()  # keys past N
+        dK, dV = dK[:, :, :N], dV[:, :, :N]
+        ix = idx.reshape(B, T, G, k)
+        for b in range(B):
+            mask = _mask_from_idx(ix[b], T, N, Bk, G)
+            rq, rk, rv = _autograd_reference(q[b], K[b], V[b], dO[b], mask, Hq // G)
+            assert np.allclose(dq[b], rq, rtol=1e-10, atol=1e-10)
+            assert np.allclose(dK[b], rk, rtol=1e-10, atol=1e-10)
+            assert np.allclose(dV[b], rv, rtol=1e-10, atol=1e-10)
+        NB = -(-N // Bk)
+        lo, nb = NB // 3, 2
+        _, wK, wV = orc.attend_backward(d, rb, rt, q.reshape(-1, Hq, dh),
+                                        dO.reshape(-1, Hq, dh), K, V, idx, blk_lo=lo, nblk=nb)
+        keys = slice(lo * Bk, min((lo + nb) * Bk, N))
+        n_in = keys.stop - keys.start
+        assert np.array_equal(wK[:, :, :n_in], dK[:, :, keys])
+        assert np.array_equal(wV[:, :, :n_in], dV[:, :, keys])
+
+
+def pin_backward_dense_sdpa(orc):
+    """Every visible block selected: the gradients of dense causal GQA
+    attention, through torch's scaled_dot_product_attention."""
+    B, T, N, Hq, G, dh, Bk = 1, 37, 45, 4, 2, 8, 4
+    NB = -(-N // Bk)
+    d, rb, rt, q, K, V, dO, idx = _bwd_case(orc, B, T, N, Hq, G, dh, Bk, NB + 1, 32, dense=True)
+    dq, dK, dV = orc.attend_backward(d, rb, rt, q.reshape(-1, Hq, dh), dO.reshape(-1, Hq, dh),
+                                     K, V, idx)
+    hg = Hq // G
+    qq = q[0].double().permute(1, 0, 2).clone().requires_grad_(True)
+    kk = K[0].double().clone().requires_grad_(True)
+    vv = V[0].double().clone().requires_grad_(True)
+    pos = (N - T) + torch.arange(T)
+    causal = torch.arange(N)[None, :] <= pos[:, None]
+    out = F.scaled_dot_product_attention(qq.unsqueeze(0), kk.repeat_interleave(hg, 0).unsqueeze(0),
+                                         vv.repeat_interleave(hg, 0).unsqueeze(0),
+                                         attn_mask=causal)
+    (out[0] * dO[0].double().permute(1, 0, 2)).sum().backward()
+    assert np.allclose(dq.reshape(T, Hq, dh), qq.grad.permute(1, 0, 2).numpy(), atol=1e-10)
+    assert np.allclose(dK[0, :, :N], kk.grad.numpy(), atol=1e-10)
+    assert np.allclose(dV[0, :, :N], vv.grad.numpy(), atol=1e-10)
+
+
+def _bf16_value(x):
+    return torch.tensor([x], dtype=torch.bfloat16)[0]
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of L = sum(dO . O) through the oracle's forward:
+    a coordinate is set to 1.5 and moved to 1.5 +- 2^-7 (all exact in bf16),
+    for coordinates of q, of K and V in a selected block, and of K in a block
+    no row of the group selects (zero gradient)."""
+    B, T, N, Hq, G, dh, Bk, k = 1, 24, 24, 4, 2, 8, 4, 2
+    d, rb, rt, q, K, V, dO, idx = _bwd_case(orc, B, T, N, Hq, G, dh, Bk, k, 33)
+    hg = Hq // G
+    step = 2.0 ** -7
+
+    def loss(qx, Kx, Vx):
+        O, _ = orc.attend(d, rb, rt, qx.reshape(-1, Hq, dh), Kx, Vx, idx)
+        return float((O * dO.reshape(-1, Hq, dh).double().numpy()).sum())
+
+    def fd(tensor, where):
+        plus, minus = tensor.clone(), tensor.clone()
+        plus[where] = _bf16_value(1.5 + step)
+        minus[where] = _bf16_value(1.5 - step)
+        base = tensor.clone()
+        base[where] = _bf16_value(1.5)
+        return base, plus, minus
+
+    chosen = set(int(x) for x in idx[:, 0].ravel() if x >= 0)
+    unused = [blk for blk in range(-(-N // Bk)) if blk not in chosen]
+    sel_blk = sorted(chosen)[0]
+    cases = [("q", (0, 20, 1, 3)), ("q", (0, 7, 3, 0)),
+             ("K", (0, 0, sel_blk * Bk + 1, 5)), ("V", (0, 0, sel_blk * Bk + 2, 6)),
+             ("V", (0, 1, N - 1, 0))]
+    if unused:
+        cases.append(("K", (0, 0, unused[0] * Bk, 2)))
+    for name, where in cases:
+        src = {"q": q, "K": K, "V": V}[name]
+        base, plus, minus = fd(src, where)
+        def with_(t):
+            a = {"q": q, "K": K, "V": V}
+            a[name] = t
+            return loss(a["q"], a["K"], a["V"])
+        num = (with_(plus) - with_(minus)) / (2 * step)
+        a = {"q": q, "K": K, "V": V}
+        a[name] = base
+        dq, dK, dV = orc.attend_backward(d, rb, rt, a["q"].reshape(-1, Hq, dh),
+                                         dO.reshape(-1, Hq, dh), a["K"], a["V"], idx)
+        if name == "q":
+            ana = dq.reshape(B, T, Hq, dh)[where]
+        else:
+            ana = (dK if name == "K" else dV)[where]
+        assert abs(num - ana) <= 2e-3 * max(1.0, abs(ana)), (name, where, num, ana)
+        assert name == "K" and where[2] // Bk in unused or abs(ana) > 1e-3, (name, where, ana)
+        if name == "K" and where[2] // Bk in unused:
+            assert ana == 0.0 and num == 0.0
+
+
+def pin_backward_closed_forms(orc):
+    """Softmax weights sum to one, so over all keys of a group sum(dV) is the
+    sum of dO over the group's rows and heads and sum(dK) is zero; dO = 0
+    gives zero gradients; a constant V gives dq = 0 and dK = 0."""
+    B, T, N, Hq, G, dh, Bk, k = 2, 40, 52, 6, 2, 8, 4, 4
+    d, rb, rt, q, K, V, dO, idx = _bwd_case(orc, B, T, N, Hq, G, dh, Bk, k, 34)
+    hg = Hq // G
+    dq, dK, dV = orc.attend_backward(d, rb, rt, q.reshape(-1, Hq, dh), dO.reshape(-1, Hq, dh),
+                                     K, V, idx)
+    go = dO.double().numpy().reshape(B, T, G, hg, dh)
+    assert np.allclose(dV.sum(axis=2), go.sum(axis=(1, 3)), atol=1e-10)
+    assert np.allclose(dK.sum(axis=2), 0.0, atol=1e-10)
+    z = torch.zeros_like(dO)
+    dq0, dK0, dV0 = orc.attend_backward(d, rb, rt, q.reshape(-1, Hq, dh), z.reshape(-1, Hq, dh),
+                                        K, V, idx)
+    assert not dq0.any() and not dK0.any() and not dV0.any()
+    Vc = torch.full_like(V, -0.75)
+    dqc, dKc, dVc = orc.attend_backward(d, rb, rt, q.reshape(-1, Hq, dh),
+                                        dO.reshape(-1, Hq, dh), K, Vc, idx)
+    assert np.abs(dqc).max() < 1e-12 and np.abs(dKc).max() < 1e-12
+    assert np.allclose(dVc, dV, atol=1e-10)  # dV does not depend on V
+
+
 ALL_PINS = [
     pin_scores_brute_force,
     pin_scores_zero_keys,
@@ -465,4 +637,8 @@ ALL_PINS = [
     pin_decode_is_last_prefill_row,
     pin_e4m3_codes,
     pin_fp8_scores_match_bf16_on_integers,
+    pin_backward_autograd,
+    pin_backward_dense_sdpa,
+    pin_backward_finite_differences,
+    pin_backward_closed_forms,
 ]

@@ -62,6 +62,21 @@ MUTATIONS = [
     ("e4m3_mantissa_halved", "v = ldexp(1.0 + m / 8.0, e - 7);",
      "v = ldexp(1.0 + m / 16.0, e - 7);"),
     ("e4m3_sign_dropped", "return sign ? -v : v;", "return v;"),
+    ("bwd_no_softmax_jacobian_term", "const double dz = z[i] * (dp[i] - pdp);",
+     "const double dz = z[i] * dp[i];"),
+    ("bwd_dq_unscaled", "dqr[c] += dz * widen_bf16(kv[c]) / root;",
+     "dqr[c] += dz * widen_bf16(kv[c]);"),
+    ("bwd_dv_weighted_by_dz", "myv[kw * dh + c] += z[i] * go[c];",
+     "myv[kw * dh + c] += dz * go[c];"),
+    ("bwd_dk_sign", "myk[kw * dh + c] += dz * qd[c] / root;",
+     "myk[kw * dh + c] -= dz * qd[c] / root;"),
+    ("bwd_unnormalised_weights", "                z[i] /= l;\n", "                z[i] /= 1.0;\n"),
+    ("bwd_heads_interleaved", "const int64_t b = bh / Hq, h = bh % Hq, g = h / hg;",
+     "const int64_t b = bh / Hq, h = bh % Hq, g = h % G;"),
+    ("bwd_no_causal_mask", "j < (blk + 1) * Bk && j <= p; ++j)",
+     "j < (blk + 1) * Bk && j < d->N; ++j)"),
+    ("bwd_window_offset_dropped", "const int64_t kw = key[i] - key_lo;",
+     "const int64_t kw = key[i];"),
     ("fp8_scores_use_bf16_decoder", "block_scores(d, nrows, row_b, row_t, qI_rows, kI, 1, S);",
      "block_scores(d, nrows, row_b, row_t, qI_rows, kI, 0, S);"),
 ]
