@@ -152,6 +152,16 @@ size_t prefill_ws(const msa_dims_t* d, int64_t window) {
                                    d->k, d->Bk, false);
 }
 
+// Backward: the prefill's inversion and partial buffers (the dq partials take
+// the place of the partial O), then D = dO . O for every (row, head).
+size_t rowdot_bytes(const msa_dims_t* d) {
+  return ((static_cast<size_t>(d->B * d->T * d->Hq) * sizeof(float)) + 255) & ~size_t(255);
+}
+
+size_t backward_ws(const msa_dims_t* d, int64_t window) {
+  return rowdot_bytes(d) + prefill_ws(d, window);
+}
+
 size_t decode_ws(const msa_dims_t* d) {
   return msa::attn_workspace_bytes(d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, d->Bk, true);
 }
@@ -186,6 +196,7 @@ size_t msa_workspace_bytes(int op, const msa_dims_t* d) {
     case MSA_OP_SELECT_FROM_SCORES: return 0;
     case MSA_OP_ATTN_PREFILL: return prefill_ws(d, default_window(d));
     case MSA_OP_ATTN_DECODE: return d->T == 1 ? decode_ws(d) : 0;
+    case MSA_OP_ATTN_BACKWARD: return backward_ws(d, default_window(d));
   }
   return 0;
 }
@@ -322,6 +333,50 @@ int msa_sparse_attn_prefill(const msa_dims_t* d, const void* q, const void* K, c
                                                 d->G, d->k, d->Bk, w,
                                                 static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_prefill");
+  return MSA_OK;
+}
+
+int msa_sparse_attn_backward(const msa_dims_t* d, const void* q, const void* K, const void* V,
+                             const int32_t* idx, const void* O, const float* lse, const void* dO,
+                             float* dq, float* dK, float* dV, void* ws, size_t ws_bytes,
+                             void* stream) {
+  MSA_TRY(check_dims(d));
+  MSA_TRY(need_bk128(d, "msa_sparse_attn_backward"));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(K, "K"));
+  MSA_TRY(check_ptr(V, "V"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  MSA_TRY(check_ptr(O, "O"));
+  MSA_TRY(check_ptr(lse, "lse"));
+  MSA_TRY(check_ptr(dO, "dO"));
+  MSA_TRY(check_ptr(dq, "dq"));
+  MSA_TRY(check_ptr(dK, "dK"));
+  MSA_TRY(check_ptr(dV, "dV"));
+  MSA_TRY(check_ptr(ws, "ws"));
+  int64_t hi = default_window(d);
+  if (backward_ws(d, 1) > ws_bytes)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "backward needs at least %zu workspace bytes (%zu for the default window), got %zu",
+                backward_ws(d, 1), backward_ws(d, hi), ws_bytes);
+  if (backward_ws(d, hi) > ws_bytes) {
+    int64_t lo = 1;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo + 1) / 2;
+      if (backward_ws(d, mid) <= ws_bytes)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    hi = lo;
+  }
+  float* Dr = static_cast<float*>(ws);
+  msa::AttnWorkspace w;
+  msa::attn_workspace_carve(static_cast<char*>(ws) + rowdot_bytes(d), hi, stage_rows_for(d, hi),
+                            d->N, d->G, d->Hq / d->G, d->k, d->Bk, false, &w);
+  const hipError_t e = msa::launch_attn_backward(q, K, V, idx, O, lse, dO, dq, dK, dV, Dr, d->B,
+                                                 d->T, d->N, d->Hq, d->G, d->k, w,
+                                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_backward");
   return MSA_OK;
 }
 

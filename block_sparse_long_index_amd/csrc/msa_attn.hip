@@ -729,56 +729,67 @@ static unsigned blocks_for(int64_t n, int per) {
   return static_cast<unsigned>((n + per - 1) / per);
 }
 
-// Prefill: for every sequence and every window of its rows, one inversion
-// (unit histograms, scan, scatter, stage chunk lists); then the stages in
-// group-major order.  A stage is one group and stage_rows consecutive rows:
-// its KV-outer launch writes the stage's partials (a buffer small enough to
-// stay in the last-level cache next to the group's K/V) and the combine
-// launch right after reads them back.
+// Inversion of the query rows [t0, t0 + W) of sequence b (unit histograms,
+// scan, scatter, stage chunk lists); *nsub receives the number of row stages
+// per group.
+hipError_t launch_invert_window(const int32_t* idx, int64_t b, int64_t T, int64_t t0, int64_t W,
+                                int64_t N, int G, int k, int Bk, const AttnWorkspace& w,
+                                int32_t* nsub, hipStream_t st) {
+  const int32_t NB = static_cast<int32_t>((N + Bk - 1) / Bk);
+  const size_t lds = sizeof(int32_t) * NB;
+  InvArgs ia;
+  ia.idx = idx;
+  ia.hist = w.hist;
+  ia.entries = w.entries;
+  ia.T = T;
+  ia.t0 = t0;
+  ia.W = W;
+  ia.b = static_cast<int32_t>(b);
+  ia.G = G;
+  ia.k = k;
+  ia.NB = NB;
+  ia.rq = w.rq;
+  ia.nc = static_cast<int32_t>((W + w.rq - 1) / w.rq);
+  const int64_t nhist = static_cast<int64_t>(G) * NB * ia.nc;
+  const int64_t ntiles = (nhist + kScanTile - 1) / kScanTile;
+  const int32_t S = static_cast<int32_t>((W + w.stage_rows - 1) / w.stage_rows);
+  const int32_t U = static_cast<int32_t>(w.stage_rows / w.rq);
+  const int64_t nst = static_cast<int64_t>(G) * S;
+  const dim3 ugrid(static_cast<unsigned>(ia.nc), static_cast<unsigned>(G));
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks_for(nst, 256)), dim3(256), 0, st,
+                     w.totals + 4, nst, 0);
+  hipLaunchKernelGGL(hist_kernel, ugrid, dim3(256), lds, st, ia);
+  hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, st,
+                     w.hist, nhist, w.tile_sums);
+  hipLaunchKernelGGL(scan_sums_kernel, dim3(1), dim3(256), 0, st, w.tile_sums, ntiles,
+                     w.totals);
+  hipLaunchKernelGGL(scan_apply_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, st,
+                     w.hist, nhist, w.tile_sums);
+  hipLaunchKernelGGL(scatter_kernel, ugrid, dim3(256), lds, st, ia);
+  const int64_t per_stage = ((NB + 63) / 64) * 64;
+  hipLaunchKernelGGL(stage_chunk_kernel, dim3(blocks_for(nst * per_stage, 256)), dim3(256), 0,
+                     st, w.hist, w.totals, w.chunks, NB, static_cast<int64_t>(G) * NB, ia.nc,
+                     U, S, w.max_chunks, static_cast<int32_t>(b * G));
+  *nsub = S;
+  return hipGetLastError();
+}
+
+// Prefill: for every sequence and every window of its rows, one inversion;
+// then the stages in group-major order.  A stage is one group and
+// stage_rows consecutive rows: its KV-outer launch writes the stage's
+// partials (a buffer small enough to stay in the last-level cache next to
+// the group's K/V) and the combine launch right after reads them back.
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse, int64_t B,
                                int64_t T, int64_t N, int Hq, int G, int k, int Bk,
                                const AttnWorkspace& w, hipStream_t st) {
   const int hg = Hq / G;
   const int32_t NB = static_cast<int32_t>((N + Bk - 1) / Bk);
-  const size_t lds = sizeof(int32_t) * NB;
   for (int64_t b = 0; b < B; ++b) {
     for (int64_t t0 = 0; t0 < T; t0 += w.window) {
       const int64_t W = (T - t0) < w.window ? (T - t0) : w.window;
-      InvArgs ia;
-      ia.idx = idx;
-      ia.hist = w.hist;
-      ia.entries = w.entries;
-      ia.T = T;
-      ia.t0 = t0;
-      ia.W = W;
-      ia.b = static_cast<int32_t>(b);
-      ia.G = G;
-      ia.k = k;
-      ia.NB = NB;
-      ia.rq = w.rq;
-      ia.nc = static_cast<int32_t>((W + w.rq - 1) / w.rq);
-      const int64_t nhist = static_cast<int64_t>(G) * NB * ia.nc;
-      const int64_t ntiles = (nhist + kScanTile - 1) / kScanTile;
-      const int32_t S = static_cast<int32_t>((W + w.stage_rows - 1) / w.stage_rows);
-      const int32_t U = static_cast<int32_t>(w.stage_rows / w.rq);
-      const int64_t nst = static_cast<int64_t>(G) * S;
-      const dim3 ugrid(static_cast<unsigned>(ia.nc), static_cast<unsigned>(G));
-      hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks_for(nst, 256)), dim3(256), 0, st,
-                         w.totals + 4, nst, 0);
-      hipLaunchKernelGGL(hist_kernel, ugrid, dim3(256), lds, st, ia);
-      hipLaunchKernelGGL(scan_tiles_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, st,
-                         w.hist, nhist, w.tile_sums);
-      hipLaunchKernelGGL(scan_sums_kernel, dim3(1), dim3(256), 0, st, w.tile_sums, ntiles,
-                         w.totals);
-      hipLaunchKernelGGL(scan_apply_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, st,
-                         w.hist, nhist, w.tile_sums);
-      hipLaunchKernelGGL(scatter_kernel, ugrid, dim3(256), lds, st, ia);
-      const int64_t per_stage = ((NB + 63) / 64) * 64;
-      hipLaunchKernelGGL(stage_chunk_kernel, dim3(blocks_for(nst * per_stage, 256)), dim3(256), 0,
-                         st, w.hist, w.totals, w.chunks, NB, static_cast<int64_t>(G) * NB, ia.nc,
-                         U, S, w.max_chunks, static_cast<int32_t>(b * G));
-      hipError_t e = hipGetLastError();
+      int32_t S = 0;
+      hipError_t e = launch_invert_window(idx, b, T, t0, W, N, G, k, Bk, w, &S, st);
       if (e != hipSuccess) return e;
       const int64_t r0 = b * T + t0;
       for (int g = 0; g < G; ++g) {

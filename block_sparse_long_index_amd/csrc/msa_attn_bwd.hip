@@ -1,0 +1,438 @@
+// msa_attn_bwd.hip -- backward of the main branch of MSA (stage 4) on gfx950:
+// dq, dK and dV of exact softmax attention over each row's selected blocks,
+// scheduled KV-outer like the forward.
+//
+// Method: the selection is fixed by the forward (the top-k has no gradient);
+// the Flash-MSA training blog (hackernews.jp, "Backward pass") keeps the
+// forward's block indices and the main branch's lse for the backward, inverts
+// the [batch, group, query, slot] -> block map into block -> queries and
+// schedules the sparse KV blocks shared by many queries from that inverse.
+// Per (row, head), over the row's support keys j (scale c = 1/sqrt(128)):
+//   P_j = exp(c q.K_j - lse),  dP_j = dO.V_j,  D = dO.O = sum_j P_j dP_j,
+//   dS_j = P_j (dP_j - D),  dq = c sum_j dS_j K_j,
+//   dK_j += c dS_j q,  dV_j += P_j dO.
+//
+// One workgroup per chunk (b, g, block, <= 128 queries, all heads of the
+// group): K (row-major and transposed) and V of the block stay in LDS while
+// the chunk's (query, head) rows stream through in passes of 32.  Wave w owns
+// keys 32w..32w+31 for S, dP, dS and its dK/dV accumulators (registers for the
+// whole chunk), and dims 32w..32w+31 of the pass's dq.  The dq of a (row,
+// slot) pair is written as a bf16 partial and the partials of a row are summed
+// in slot order by dq_combine_kernel; dK and dV of a chunk are added to the
+// fp32 outputs with one atomic add per element (a block's queries may span
+// several chunks and stages).
+#include "msa_common.h"
+#include "msa_internal.h"
+
+#include <math.h>
+
+namespace msa {
+
+constexpr int kBP = 272;  // LDS row pitch (bytes) of every 128-column bf16 tile
+
+struct BwdArgs {
+  const u16* q;
+  const u16* K;
+  const u16* V;
+  const u16* dO;
+  const float* lse;       // [B, Hq, T], natural log
+  const float* Dr;        // [B, T, Hq]: dO . O
+  const int4* chunks;     // this stage's chunk list
+  const int32_t* entries;
+  const int32_t* count;
+  u16* dqpart;            // [stage rows, k, hg, 128] bf16
+  float* dK;              // [B, G, N, 128]
+  float* dV;
+  int64_t T, N, r0;       // r0: global row (b*T + t) of window row 0
+  int32_t Hq, G, k;
+  int32_t rl_base;        // first window row of this stage
+  int32_t sink;           // spare partial row (hg rows) for rows past a chunk's end
+};
+
+template <int HG>
+__global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
+  __shared__ __align__(16) unsigned char ks[128 * kBP];  // K [key][d]
+  __shared__ __align__(16) unsigned char vs[128 * kBP];  // V [key][d]
+  __shared__ __align__(16) unsigned char kt[128 * kBP];  // K^T [d][key]
+  __shared__ __align__(16) unsigned char qs[32 * kBP];   // the pass's q rows [row][d]
+  __shared__ __align__(16) unsigned char gs[32 * kBP];   // the pass's dO rows [row][d]
+  __shared__ __align__(16) unsigned char dss[32 * kBP];  // dS [row][key], bf16, scaled by c
+  __shared__ float r_l2[32], r_D[32];
+  __shared__ int r_lim[32];
+
+  // the chunk list is dealt to the 8 XCDs in contiguous eighths (as forward)
+  const int nchunks = *a.count;
+  const int per_xcd = (nchunks + 7) >> 3;
+  const int xj = static_cast<int>(blockIdx.x >> 3);
+  const int ci = static_cast<int>(blockIdx.x & 7) * per_xcd + xj;
+  if (xj >= per_xcd || ci >= nchunks) return;
+  const int4 ch = a.chunks[ci];
+  const int n = ch.z;
+  if (n <= 0) return;
+  const int64_t blk = ch.w;
+  const int64_t bg = ch.x;
+  const int g = static_cast<int>(bg) & (a.G - 1);  // G is a power of two
+  const int64_t b = bg >> __builtin_ctz(a.G);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  const int64_t key0 = blk * 128;
+  const int nvalid = static_cast<int>(a.N - key0 < 128 ? a.N - key0 : 128);  // >= 1
+  const u16* Kb = a.K + (bg * a.N + key0) * kHeadDim;
+  const u16* Vb = a.V + (bg * a.N + key0) * kHeadDim;
+
+  // K: 64 key pairs x 16 chunks of 8 dims; each pair goes to ks row-major and
+  // to kt as 32-bit (key, key + 1) words.  Keys past N are zero.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + 256 * j;
+    const int kp = i & 63, c = i >> 6;
+    const int k0 = 2 * kp;
+    const uint4 y0 = ld16(Kb + (k0 < nvalid ? k0 : nvalid - 1) * kHeadDim + 8 * c);
+    const uint4 y1 = ld16(Kb + (k0 + 1 < nvalid ? k0 + 1 : nvalid - 1) * kHeadDim + 8 * c);
+    const uint4 x0 = k0 < nvalid ? y0 : make_uint4(0, 0, 0, 0);
+    const uint4 x1 = k0 + 1 < nvalid ? y1 : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&ks[k0 * kBP + 16 * c]) = x0;
+    *reinterpret_cast<uint4*>(&ks[(k0 + 1) * kBP + 16 * c]) = x1;
+    const uint32_t w0[4] = {x0.x, x0.y, x0.z, x0.w};
+    const uint32_t w1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t lo = (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      const uint32_t hi = (w1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      *reinterpret_cast<uint32_t*>(&kt[(8 * c + e) * kBP + 2 * k0]) = lo | (hi << 16);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = tid + 256 * j;
+    const int r = i >> 4, c = i & 15;
+    const uint4 y = ld16(Vb + (r < nvalid ? r : nvalid - 1) * kHeadDim + 8 * c);
+    *reinterpret_cast<uint4*>(&vs[r * kBP + 16 * c]) = r < nvalid ? y : make_uint4(0, 0, 0, 0);
+  }
+
+  const int rows = n * HG;
+  const int64_t t0 = a.r0 - b * a.T;
+  const int key_w = 32 * wave + l32;  // this lane's key in S, dP, dS
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kScale = 0.08838834764831845f;  // 1/sqrt(128)
+  const float qscale = kLog2e * kScale;
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+
+  for (int pass = 0; pass * 32 < rows; ++pass) {
+    // Gather the pass's 32 (query, head) rows: thread -> row tid/8, dims
+    // 16*(tid%8) .. +15.  Rows past the chunk's end are zero with lse = +inf
+    // and an empty causal range, so they add nothing to dK and dV.
+    {
+      const int rw = tid >> 3, c8 = tid & 7;
+      const int rr = pass * 32 + rw;
+      const bool valid = rr < rows;
+      const int qi = valid ? rr / HG : 0;
+      const int hh = valid ? rr % HG : 0;
+      const int e = a.entries[ch.y + qi];
+      const int64_t t = t0 + (e >> 6);
+      const int64_t hq = static_cast<int64_t>(g) * HG + hh;
+      const int64_t off = ((b * a.T + t) * a.Hq + hq) * kHeadDim + 16 * c8;
+      uint4 q0 = ld16(a.q + off), q1 = ld16(a.q + off + 8);
+      uint4 g0 = ld16(a.dO + off), g1 = ld16(a.dO + off + 8);
+      if (!valid) {
+        q0 = q1 = g0 = g1 = make_uint4(0, 0, 0, 0);
+      }
+      *reinterpret_cast<uint4*>(&qs[rw * kBP + 32 * c8]) = q0;
+      *reinterpret_cast<uint4*>(&qs[rw * kBP + 32 * c8 + 16]) = q1;
+      *reinterpret_cast<uint4*>(&gs[rw * kBP + 32 * c8]) = g0;
+      *reinterpret_cast<uint4*>(&gs[rw * kBP + 32 * c8 + 16]) = g1;
+      if (c8 == 0) {
+        r_l2[rw] = valid ? a.lse[(b * a.Hq + hq) * a.T + t] * kLog2e : INFINITY;
+        r_D[rw] = valid ? a.Dr[(b * a.T + t) * a.Hq + hq] : 0.f;
+        r_lim[rw] = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
+      }
+    }
+    __syncthreads();
+
+    // S = Q K^T and dP = dO V^T: rows on M, this wave's 32 keys on N
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    {
+      const unsigned char* qa = qs + l32 * kBP + half * 16;
+      const unsigned char* ga = gs + l32 * kBP + half * 16;
+      const unsigned char* kb = ks + key_w * kBP + half * 16;
+      const unsigned char* vb = vs + key_w * kBP + half * 16;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(qa + 32 * s)),
+                      as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s)), sacc);
+        pacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ga + 32 * s)),
+                      as_bf16x8(*reinterpret_cast<const uint4*>(vb + 32 * s)), pacc);
+      }
+    }
+    // P and c*dS; lane: key key_w, rows m(i) = 8(i/4) + 4 half + i%4
+    float pr[16], dsr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = 8 * (i >> 2) + 4 * half + (i & 3);
+      const float p = key_w <= r_lim[m] ? fast_exp2(fmaf(sacc[i], qscale, -r_l2[m])) : 0.f;
+      pr[i] = p;
+      dsr[i] = p * (pacc[i] - r_D[m]) * kScale;
+      *reinterpret_cast<u16*>(&dss[m * kBP + 2 * key_w]) = f32_to_bf16(dsr[i]);
+    }
+    // dV += P^T dO and dK += dS^T q over the pass's rows: keys on M, dims on
+    // N.  A lane's P values for k-step s are rows 16s + 8(j/4) + 4 half + j%4
+    // (j = 0..7), so the B operand takes dO / q at exactly those rows.
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint4 pa = make_uint4(pack_bf16x2(pr[8 * s + 0], pr[8 * s + 1]),
+                                  pack_bf16x2(pr[8 * s + 2], pr[8 * s + 3]),
+                                  pack_bf16x2(pr[8 * s + 4], pr[8 * s + 5]),
+                                  pack_bf16x2(pr[8 * s + 6], pr[8 * s + 7]));
+      const uint4 da = make_uint4(pack_bf16x2(dsr[8 * s + 0], dsr[8 * s + 1]),
+                                  pack_bf16x2(dsr[8 * s + 2], dsr[8 * s + 3]),
+                                  pack_bf16x2(dsr[8 * s + 4], dsr[8 * s + 5]),
+                                  pack_bf16x2(dsr[8 * s + 6], dsr[8 * s + 7]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int col = 2 * (32 * dt + l32);
+        uint32_t wg[4], wq[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r0 = 16 * s + 8 * (jj >> 1) + 4 * half + 2 * (jj & 1);
+          wg[jj] = static_cast<uint32_t>(*reinterpret_cast<const u16*>(&gs[r0 * kBP + col])) |
+                   (static_cast<uint32_t>(*reinterpret_cast<const u16*>(&gs[(r0 + 1) * kBP + col]))
+                    << 16);
+          wq[jj] = static_cast<uint32_t>(*reinterpret_cast<const u16*>(&qs[r0 * kBP + col])) |
+                   (static_cast<uint32_t>(*reinterpret_cast<const u16*>(&qs[(r0 + 1) * kBP + col]))
+                    << 16);
+        }
+        dv[dt] = mfma32(as_bf16x8(pa), as_bf16x8(make_uint4(wg[0], wg[1], wg[2], wg[3])), dv[dt]);
+        dk[dt] = mfma32(as_bf16x8(da), as_bf16x8(make_uint4(wq[0], wq[1], wq[2], wq[3])), dk[dt]);
+      }
+    }
+    __syncthreads();  // dss complete; every wave is done with qs, gs and the row data
+
+    // dq^T of this wave's 32 dims x the pass's 32 rows = K^T dS^T over 128 keys
+    f32x16 qacc = f32x16{};
+    {
+      const unsigned char* ka = kt + (32 * wave + l32) * kBP + half * 16;
+      const unsigned char* db = dss + l32 * kBP + half * 16;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        qacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
+                      as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), qacc);
+    }
+    // partial of (row, slot): lane = row l32, dims 32 wave + 8(i/4) + 4 half + i%4
+    {
+      const int rr = pass * 32 + l32;
+      const bool valid = rr < rows;
+      const int qi = valid ? rr / HG : 0;
+      const int hh = rr % HG;
+      const int e = a.entries[ch.y + qi];
+      const int prow = valid ? (((e >> 6) - a.rl_base) * a.k + (e & 63)) * HG + hh : a.sink + hh;
+      u16* dst = a.dqpart + static_cast<int64_t>(prow) * kHeadDim + 32 * wave + 4 * half;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        uint2 w;
+        w.x = pack_bf16x2(qacc[4 * a4 + 0], qacc[4 * a4 + 1]);
+        w.y = pack_bf16x2(qacc[4 * a4 + 2], qacc[4 * a4 + 3]);
+        *reinterpret_cast<uint2*>(dst + 8 * a4) = w;
+      }
+    }
+  }
+
+  // dK, dV of this wave's keys: lane = dim 32 dt + l32, keys m(i)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t key = key0 + 32 * wave + 8 * (i >> 2) + 4 * half + (i & 3);
+    if (key < a.N) {
+      float* pk = a.dK + (bg * a.N + key) * kHeadDim + l32;
+      float* pv = a.dV + (bg * a.N + key) * kHeadDim + l32;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        unsafeAtomicAdd(pk + 32 * dt, dk[dt][i]);
+        unsafeAtomicAdd(pv + 32 * dt, dv[dt][i]);
+      }
+    }
+  }
+}
+
+// D = dO . O per (row, head): 16 lanes per row, fp32.
+__global__ void __launch_bounds__(256) bwd_rowdot_kernel(const u16* O, const u16* dO, float* Dr,
+                                                         int64_t nrows) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = i >> 4;
+  const int part = static_cast<int>(i & 15);
+  float s = 0.f;
+  if (row < nrows) {
+    const uint4 o = ld16(O + row * kHeadDim + 8 * part);
+    const uint4 d = ld16(dO + row * kHeadDim + 8 * part);
+    const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s = fmaf(__uint_as_float(ow[u] << 16), __uint_as_float(dw[u] << 16), s);
+      s = fmaf(__uint_as_float(ow[u] & 0xffff0000u), __uint_as_float(dw[u] & 0xffff0000u), s);
+    }
+  }
+  s += __shfl_xor(s, 8);
+  s += __shfl_xor(s, 4);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 1);
+  if (row < nrows && part == 0) Dr[row] = s;
+}
+
+__global__ void __launch_bounds__(256) bwd_zero_kernel(float4* p, int64_t n4) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+struct DqArgs {
+  const int32_t* idx;
+  const u16* dqpart;
+  float* dq;
+  int64_t T, r0, rows;  // rows: window rows rl_base .. rl_base + rows - 1
+  int32_t Hq, G, k, rl_base, group;
+};
+
+// dq of a row = the sum of its valid slots' partials, in slot order.  One wave
+// per (row, stage group); 16 lanes per head, 8 dims per lane.
+template <int HG>
+__global__ void __launch_bounds__(256) dq_combine_kernel(DqArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (wid >= a.rows) return;  // uniform per wave
+  const int64_t grow = a.r0 + a.rl_base + wid;  // b * T + t
+  const int64_t b = grow / a.T, t = grow % a.T;
+  const int32_t* ir = a.idx + ((b * a.G + a.group) * a.T + t) * a.k;
+  const int nval = __popcll(__ballot(lane < a.k && ir[lane < a.k ? lane : 0] >= 0));
+  const int piece = lane & 15;
+#pragma unroll
+  for (int h0 = 0; h0 < HG; h0 += 4) {
+    const int h = h0 + (lane >> 4);
+    if (h < HG) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < nval; ++s) {
+        const int64_t prow = (wid * a.k + s) * HG + h;
+        const uint4 v = ld16_once(a.dqpart + prow * kHeadDim + 8 * piece);
+        const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc[2 * u] += __uint_as_float(vw[u] << 16);
+          acc[2 * u + 1] += __uint_as_float(vw[u] & 0xffff0000u);
+        }
+      }
+      float4* dst = reinterpret_cast<float4*>(
+          a.dq + (grow * a.Hq + static_cast<int64_t>(a.group) * HG + h) * kHeadDim + 8 * piece);
+      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+template <int HG>
+static hipError_t launch_bwd_stage(const BwdArgs& ba, const DqArgs& da, int64_t grid_chunks,
+                                   hipStream_t st) {
+  const int64_t grid = (grid_chunks + 7) & ~static_cast<int64_t>(7);
+  hipLaunchKernelGGL((kv_outer_bwd_kernel<HG>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                     st, ba);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dq_combine_kernel<HG>), dim3(static_cast<unsigned>((da.rows + 3) / 4)),
+                     dim3(256), 0, st, da);
+  return hipGetLastError();
+}
+
+static hipError_t dispatch_bwd(int hg, const BwdArgs& ba, const DqArgs& da, int64_t grid,
+                               hipStream_t st) {
+  switch (hg) {
+    case 8: return launch_bwd_stage<8>(ba, da, grid, st);
+    case 4: return launch_bwd_stage<4>(ba, da, grid, st);
+    case 16: return launch_bwd_stage<16>(ba, da, grid, st);
+    case 2: return launch_bwd_stage<2>(ba, da, grid, st);
+    case 1: return launch_bwd_stage<1>(ba, da, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+static unsigned nblocks_of(int64_t n, int per) {
+  return static_cast<unsigned>((n + per - 1) / per);
+}
+
+// Zero dK and dV, D = dO . O for every row; then, per sequence and window of
+// rows, the inversion and the stages in group-major order: a stage's KV-outer
+// launch writes its rows' dq partials and adds its chunks' dK / dV, and the
+// dq combine right after sums the partials.
+hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
+                                const int32_t* idx, const void* O, const float* lse,
+                                const void* dO, float* dq, float* dK, float* dV, float* Dr,
+                                int64_t B, int64_t T, int64_t N, int Hq, int G, int k,
+                                const AttnWorkspace& w, hipStream_t st) {
+  const int hg = Hq / G;
+  const int64_t n4 = B * G * N * kHeadDim / 4;
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3(nblocks_of(n4, 256)), dim3(256), 0, st,
+                     reinterpret_cast<float4*>(dK), n4);
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3(nblocks_of(n4, 256)), dim3(256), 0, st,
+                     reinterpret_cast<float4*>(dV), n4);
+  const int64_t nrows = B * T * Hq;
+  hipLaunchKernelGGL(bwd_rowdot_kernel, dim3(nblocks_of(nrows * 16, 256)), dim3(256), 0, st,
+                     static_cast<const u16*>(O), static_cast<const u16*>(dO), Dr, nrows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t t0 = 0; t0 < T; t0 += w.window) {
+      const int64_t W = (T - t0) < w.window ? (T - t0) : w.window;
+      int32_t S = 0;
+      e = launch_invert_window(idx, b, T, t0, W, N, G, k, 128, w, &S, st);
+      if (e != hipSuccess) return e;
+      const int64_t r0 = b * T + t0;
+      for (int g = 0; g < G; ++g) {
+        for (int32_t sub = 0; sub < S; ++sub) {
+          const int64_t si = static_cast<int64_t>(g) * S + sub;
+          const int32_t rl_base = sub * static_cast<int32_t>(w.stage_rows);
+          BwdArgs ba;
+          ba.q = static_cast<const u16*>(q);
+          ba.K = static_cast<const u16*>(K);
+          ba.V = static_cast<const u16*>(V);
+          ba.dO = static_cast<const u16*>(dO);
+          ba.lse = lse;
+          ba.Dr = Dr;
+          ba.chunks = w.chunks + si * w.max_chunks;
+          ba.entries = w.entries;
+          ba.count = w.totals + 4 + si;
+          ba.dqpart = w.opart;
+          ba.dK = dK;
+          ba.dV = dV;
+          ba.T = T;
+          ba.N = N;
+          ba.r0 = r0;
+          ba.Hq = Hq;
+          ba.G = G;
+          ba.k = k;
+          ba.rl_base = rl_base;
+          ba.sink = static_cast<int32_t>(w.sink);
+          DqArgs da;
+          da.idx = idx;
+          da.dqpart = w.opart;
+          da.dq = dq;
+          da.T = T;
+          da.r0 = r0;
+          da.rows = (W - rl_base) < w.stage_rows ? (W - rl_base) : w.stage_rows;
+          da.Hq = Hq;
+          da.G = G;
+          da.k = k;
+          da.rl_base = rl_base;
+          da.group = g;
+          e = dispatch_bwd(hg, ba, da, w.max_chunks, st);
+          if (e != hipSuccess) return e;
+        }
+      }
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace msa

@@ -63,6 +63,19 @@ size_t attn_workspace_bytes(int64_t window, int64_t stage_rows, int64_t N, int G
 void attn_workspace_carve(void* ws, int64_t window, int64_t stage_rows, int64_t N, int G, int hg,
                           int k, int Bk, bool decode, AttnWorkspace* out);
 
+// Inversion of the selection for the query rows [t0, t0 + W) of sequence b
+// into per-stage chunk lists in w; *nsub = row stages per group.
+hipError_t launch_invert_window(const int32_t* idx, int64_t b, int64_t T, int64_t t0, int64_t W,
+                                int64_t N, int G, int k, int Bk, const AttnWorkspace& w,
+                                int32_t* nsub, hipStream_t st);
+// Stage 4 backward: dq [B, T, Hq, 128], dK, dV [B, G, N, 128] (fp32, all
+// overwritten) from q, O, dO [B, T, Hq, 128], K, V, idx and the forward's lse
+// [B, Hq, T]; Dr: B*T*Hq floats of scratch.  Bk = 128.
+hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
+                                const int32_t* idx, const void* O, const float* lse,
+                                const void* dO, float* dq, float* dK, float* dV, float* Dr,
+                                int64_t B, int64_t T, int64_t N, int Hq, int G, int k,
+                                const AttnWorkspace& w, hipStream_t st);
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse,
                                int64_t B, int64_t T, int64_t N, int Hq, int G,

@@ -22,6 +22,7 @@ OP_SELECT_BLOCKS = 1
 OP_SELECT_FROM_SCORES = 2
 OP_ATTN_PREFILL = 3
 OP_ATTN_DECODE = 4
+OP_ATTN_BACKWARD = 5
 
 # Every function the C header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -35,6 +36,8 @@ _SIGS = {
                                                ctypes.c_size_t, _P]),
     "msa_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
+    "msa_sparse_attn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                _P, ctypes.c_size_t, _P]),
     "msa_select_blocks_paged": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, _P, _P, _P, _P,
                                                ctypes.c_size_t, _P]),
     "msa_select_blocks_paged_fp8": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, _P, _P, _P, _P,
@@ -199,6 +202,38 @@ def sparse_attn_prefill(q, K, V, idx, return_lse=False, out=None, workspace=None
                                          _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()),
            "msa_sparse_attn_prefill")
     return (O, lse) if return_lse else O
+
+
+def sparse_attn_backward(q, K, V, idx, O, lse, dO, out=None, workspace=None):
+    """Stage 4 gradients (Bk = 128).  q, O, dO [B,T,Hq,128] bf16, K/V
+    [B,G,N,128] bf16, idx [B,G,T,k], lse [B,Hq,T] fp32 from the prefill ->
+    (dq [B,T,Hq,128], dK, dV [B,G,N,128]), all fp32.  out: optional
+    (dq, dK, dV) tensors to write."""
+    B, T, Hq, dh = q.shape
+    _, G, N, _ = K.shape
+    k = idx.shape[-1]
+    _need(q, "q", torch.bfloat16)
+    _need(K, "K", torch.bfloat16, (B, G, N, dh))
+    _need(V, "V", torch.bfloat16, (B, G, N, dh))
+    _need(idx, "idx", torch.int32, (B, G, T, k))
+    _need(O, "O", torch.bfloat16, q.shape)
+    _need(dO, "dO", torch.bfloat16, q.shape)
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    d = dims(B, T, N, Hq, G, k, d_h=dh)
+    if out is None:
+        out = (torch.empty(q.shape, dtype=torch.float32, device=q.device),
+               torch.empty(K.shape, dtype=torch.float32, device=q.device),
+               torch.empty(K.shape, dtype=torch.float32, device=q.device))
+    dq, dK, dV = out
+    _need(dq, "dq", torch.float32, q.shape)
+    _need(dK, "dK", torch.float32, K.shape)
+    _need(dV, "dV", torch.float32, K.shape)
+    ws, nbytes = _workspace(OP_ATTN_BACKWARD, d, workspace)
+    _check(lib().msa_sparse_attn_backward(ctypes.byref(d), _ptr(q), _ptr(K), _ptr(V), _ptr(idx),
+                                          _ptr(O), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dK),
+                                          _ptr(dV), _ptr(ws), nbytes, _stream()),
+           "msa_sparse_attn_backward")
+    return dq, dK, dV
 
 
 def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None, Bk=128):

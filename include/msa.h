@@ -83,7 +83,8 @@ enum {
     MSA_OP_SELECT_BLOCKS = 1,
     MSA_OP_SELECT_FROM_SCORES = 2,
     MSA_OP_ATTN_PREFILL = 3,
-    MSA_OP_ATTN_DECODE = 4
+    MSA_OP_ATTN_DECODE = 4,
+    MSA_OP_ATTN_BACKWARD = 5
 };
 
 /*
@@ -167,6 +168,32 @@ int msa_sparse_attn_prefill(const msa_dims_t *dims, const void *q,
                             const void *K, const void *V, const int32_t *idx,
                             void *O, float *lse, void *ws, size_t ws_bytes,
                             void *stream);
+
+/*
+ * Backward of stage 4 for training: the gradients of exact softmax attention
+ * over each row's selected blocks, the selection held fixed (the Flash-MSA
+ * blog's backward pass keeps the forward's block indices and the main
+ * branch's lse, inverts the selection into block -> queries and schedules
+ * the shared KV blocks from it; the study notes, section 3-3, define the
+ * forward being differentiated).  With P = softmax over the support,
+ * dS = P (dO.V - dO.O):  dq = dS K / sqrt(d_h), dK = dS^T q / sqrt(d_h),
+ * dV = P^T dO, dK and dV summed over the heads of each group.
+ *   q, O, dO  bf16 [B, T, Hq, d_h]   O and lse as written by the prefill call
+ *   K, V      bf16 [B, G, N, d_h]
+ *   idx       int32 [B, G, T, k]     the forward's selection
+ *   lse       fp32 [B, Hq, T]        natural log (required)
+ *   dq        fp32 [B, T, Hq, d_h]   out, overwritten
+ *   dK, dV    fp32 [B, G, N, d_h]    out, overwritten (keys no row selects get 0)
+ *   ws / ws_bytes  >= msa_workspace_bytes(MSA_OP_ATTN_BACKWARD) for the
+ *                  default query window; a smaller one (down to one row per
+ *                  window plus B*T*Hq floats) runs more windows.
+ * Needs Bk = 128.  dK and dV are accumulated with fp32 atomic adds, so their
+ * last bits can differ between runs; dq is summed in slot order.
+ */
+int msa_sparse_attn_backward(const msa_dims_t *dims, const void *q, const void *K,
+                             const void *V, const int32_t *idx, const void *O,
+                             const float *lse, const void *dO, float *dq, float *dK,
+                             float *dV, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Stage 4 for decode (T must be 1): split over the B * G * k selected KV

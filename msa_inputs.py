@@ -23,6 +23,7 @@ Value distributions follow the workloads the MSA pages describe:
 Layouts (all contiguous, row-major):
   qI [B, T, G, d_I]   kI [B, N, d_I]
   q  [B, T, Hq, d_h]  K, V [B, G, N, d_h]
+  dO [B, T, Hq, d_h]  (the backward's upstream gradient, ~N(0,1) bf16)
 Query row t of sequence b sits at absolute position p = N - T + t.
 """
 from __future__ import annotations
@@ -164,6 +165,14 @@ def make_main_inputs(w: Workload, device="cpu", gen=None):
     K = _randn_bf16(gen, (w.B, w.G, w.N, w.d_h), device)
     V = _randn_bf16(gen, (w.B, w.G, w.N, w.d_h), device)
     return q, K, V
+
+
+def make_grad_output(w: Workload, device="cpu"):
+    """dO [B,T,Hq,d_h] (bf16, ~N(0,1)): the upstream gradient of the
+    attention output for the backward."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed + 200000)
+    return _randn_bf16(gen, (w.B, w.T, w.Hq, w.d_h), device)
 
 
 def make_inputs(w: Workload, device="cpu"):

@@ -22,7 +22,7 @@ def _declared():
 def test_header_functions_are_exported():
     L = ops.lib()
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(ops._SIGS)
@@ -169,3 +169,26 @@ def test_block_size_checks():
     # decode and prefill attention workspaces grow with k
     assert (L.msa_workspace_bytes(ops.OP_ATTN_DECODE, ctypes.byref(d1)) >
             L.msa_workspace_bytes(ops.OP_ATTN_DECODE, ctypes.byref(_good(N=4096, T=1))))
+
+
+def test_backward_argument_checks():
+    """The backward validates before any HIP call: every pointer (lse is
+    required), Bk = 128, the workspace floor; its workspace is the prefill's
+    plus one float per (row, head)."""
+    L = ops.lib()
+    d = _good()
+    need = L.msa_workspace_bytes(ops.OP_ATTN_BACKWARD, ctypes.byref(d))
+    assert need >= L.msa_workspace_bytes(ops.OP_ATTN_PREFILL, ctypes.byref(d)) + 256 * 8 * 4
+    args = [FAKE] * 10
+    for i in range(10):  # q K V idx O lse dO dq dK dV
+        bad = list(args)
+        bad[i] = None
+        assert L.msa_sparse_attn_backward(ctypes.byref(d), *bad, FAKE, need, None) == -1
+        bad[i] = MISALIGNED
+        assert L.msa_sparse_attn_backward(ctypes.byref(d), *bad, FAKE, need, None) == -1
+        assert b"aligned" in L.msa_last_error()
+    assert L.msa_sparse_attn_backward(ctypes.byref(d), *args, None, need, None) == -1
+    assert L.msa_sparse_attn_backward(ctypes.byref(d), *args, FAKE, 64, None) == -3
+    d64 = _good(Bk=64, k=4)
+    assert L.msa_sparse_attn_backward(ctypes.byref(d64), *args, FAKE, 1 << 40, None) == -2
+    assert b"Bk" in L.msa_last_error()
