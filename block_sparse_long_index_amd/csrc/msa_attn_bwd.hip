@@ -29,6 +29,18 @@
 namespace msa {
 
 constexpr int kBP = 272;  // LDS row pitch (bytes) of every 128-column bf16 tile
+constexpr int kTP = 80;   // LDS row pitch of the transposed 32-row q and dO tiles
+
+// Column of pass row r (0..31) in the transposed q / dO tiles.  The dK / dV
+// products take a lane's P (or dS) values of k-step s in the order
+// rows 16s + 8(j/4) + 4 half + j%4, j = 0..7; storing row 16s + o at column
+// 16s + 8 ((o >> 2) & 1) + 4 (o >> 3) + o % 4 puts exactly those rows side by
+// side, so each B operand is one 16-byte LDS read.  Rows 2i and 2i + 1 stay
+// adjacent.
+__device__ __forceinline__ int tpos(int r) {
+  const int o = r & 15;
+  return (r & 16) + 8 * ((o >> 2) & 1) + 4 * (o >> 3) + (o & 3);
+}
 
 struct BwdArgs {
   const u16* q;
@@ -56,9 +68,11 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) unsigned char kt[128 * kBP];  // K^T [d][key]
   __shared__ __align__(16) unsigned char qs[32 * kBP];   // the pass's q rows [row][d]
   __shared__ __align__(16) unsigned char gs[32 * kBP];   // the pass's dO rows [row][d]
+  __shared__ __align__(16) unsigned char qT[128 * kTP];  // q^T [d][tpos(row)]
+  __shared__ __align__(16) unsigned char gT[128 * kTP];  // dO^T [d][tpos(row)]
   __shared__ __align__(16) unsigned char dss[32 * kBP];  // dS [row][key], bf16, scaled by c
   __shared__ float r_l2[32], r_D[32];
-  __shared__ int r_lim[32];
+  __shared__ int r_lim[32], r_prow[2][32];
 
   // the chunk list is dealt to the 8 XCDs in contiguous eighths (as forward)
   const int nchunks = *a.count;
@@ -126,37 +140,77 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
     dv[dt] = f32x16{};
   }
 
-  for (int pass = 0; pass * 32 < rows; ++pass) {
-    // Gather the pass's 32 (query, head) rows: thread -> row tid/8, dims
-    // 16*(tid%8) .. +15.  Rows past the chunk's end are zero with lse = +inf
-    // and an empty causal range, so they add nothing to dK and dV.
-    {
-      const int rw = tid >> 3, c8 = tid & 7;
-      const int rr = pass * 32 + rw;
+  // A pass's gather, one thread's share: rows 2 rp and 2 rp + 1, dims
+  // 8 cc .. 8 cc + 7 of q and dO, plus (for cc == 0) the rows' lse, D, causal
+  // limit and partial row.  Rows past the chunk's end are zero with lse = +inf
+  // and an empty causal range, so they add nothing to dK and dV; their dq
+  // goes to the sink row.  The next pass's loads are issued before the
+  // current pass's products and written to LDS after them.
+  const int rp = tid >> 4, cc = tid & 15;
+  uint4 fq[2], fg[2];
+  float fl[2], fD[2];
+  int flim[2], fprow[2];
+  auto fetch = [&](int pass) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int rr = pass * 32 + 2 * rp + u;
       const bool valid = rr < rows;
       const int qi = valid ? rr / HG : 0;
-      const int hh = valid ? rr % HG : 0;
+      const int hh = rr % HG;
       const int e = a.entries[ch.y + qi];
       const int64_t t = t0 + (e >> 6);
       const int64_t hq = static_cast<int64_t>(g) * HG + hh;
-      const int64_t off = ((b * a.T + t) * a.Hq + hq) * kHeadDim + 16 * c8;
-      uint4 q0 = ld16(a.q + off), q1 = ld16(a.q + off + 8);
-      uint4 g0 = ld16(a.dO + off), g1 = ld16(a.dO + off + 8);
-      if (!valid) {
-        q0 = q1 = g0 = g1 = make_uint4(0, 0, 0, 0);
+      const int64_t off = ((b * a.T + t) * a.Hq + hq) * kHeadDim + 8 * cc;
+      const uint4 x = ld16(a.q + off), y = ld16(a.dO + off);
+      fq[u] = valid ? x : make_uint4(0, 0, 0, 0);
+      fg[u] = valid ? y : make_uint4(0, 0, 0, 0);
+      fl[u] = INFINITY;
+      fD[u] = 0.f;
+      if (cc == 0 && valid) {
+        fl[u] = a.lse[(b * a.Hq + hq) * a.T + t] * kLog2e;
+        fD[u] = a.Dr[(b * a.T + t) * a.Hq + hq];
       }
-      *reinterpret_cast<uint4*>(&qs[rw * kBP + 32 * c8]) = q0;
-      *reinterpret_cast<uint4*>(&qs[rw * kBP + 32 * c8 + 16]) = q1;
-      *reinterpret_cast<uint4*>(&gs[rw * kBP + 32 * c8]) = g0;
-      *reinterpret_cast<uint4*>(&gs[rw * kBP + 32 * c8 + 16]) = g1;
-      if (c8 == 0) {
-        r_l2[rw] = valid ? a.lse[(b * a.Hq + hq) * a.T + t] * kLog2e : INFINITY;
-        r_D[rw] = valid ? a.Dr[(b * a.T + t) * a.Hq + hq] : 0.f;
-        r_lim[rw] = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
+      flim[u] = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
+      fprow[u] = valid ? (((e >> 6) - a.rl_base) * a.k + (e & 63)) * HG + hh : a.sink + hh;
+    }
+  };
+  auto stash = [&](int pass) {
+    const int r0 = 2 * rp;
+    *reinterpret_cast<uint4*>(&qs[r0 * kBP + 16 * cc]) = fq[0];
+    *reinterpret_cast<uint4*>(&qs[(r0 + 1) * kBP + 16 * cc]) = fq[1];
+    *reinterpret_cast<uint4*>(&gs[r0 * kBP + 16 * cc]) = fg[0];
+    *reinterpret_cast<uint4*>(&gs[(r0 + 1) * kBP + 16 * cc]) = fg[1];
+    const int P = tpos(r0);  // even; row r0 + 1 sits at P + 1
+    const uint32_t q0[4] = {fq[0].x, fq[0].y, fq[0].z, fq[0].w};
+    const uint32_t q1[4] = {fq[1].x, fq[1].y, fq[1].z, fq[1].w};
+    const uint32_t g0[4] = {fg[0].x, fg[0].y, fg[0].z, fg[0].w};
+    const uint32_t g1[4] = {fg[1].x, fg[1].y, fg[1].z, fg[1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = 16 * (e & 1);
+      const int o = (8 * cc + e) * kTP + 2 * P;
+      *reinterpret_cast<uint32_t*>(&qT[o]) =
+          ((q0[e >> 1] >> sh) & 0xffffu) | (((q1[e >> 1] >> sh) & 0xffffu) << 16);
+      *reinterpret_cast<uint32_t*>(&gT[o]) =
+          ((g0[e >> 1] >> sh) & 0xffffu) | (((g1[e >> 1] >> sh) & 0xffffu) << 16);
+    }
+    if (cc == 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        r_l2[r0 + u] = fl[u];
+        r_D[r0 + u] = fD[u];
+        r_lim[r0 + u] = flim[u];
+        r_prow[pass & 1][r0 + u] = fprow[u];
       }
     }
-    __syncthreads();
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
 
+  for (int pass = 0; pass * 32 < rows; ++pass) {
+    const bool more = (pass + 1) * 32 < rows;
+    if (more) fetch(pass + 1);
     // S = Q K^T and dP = dO V^T: rows on M, this wave's 32 keys on N
     f32x16 sacc = f32x16{}, pacc = f32x16{};
     {
@@ -183,8 +237,7 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
       *reinterpret_cast<u16*>(&dss[m * kBP + 2 * key_w]) = f32_to_bf16(dsr[i]);
     }
     // dV += P^T dO and dK += dS^T q over the pass's rows: keys on M, dims on
-    // N.  A lane's P values for k-step s are rows 16s + 8(j/4) + 4 half + j%4
-    // (j = 0..7), so the B operand takes dO / q at exactly those rows.
+    // N; the B operands are the transposed tiles (see tpos).
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const uint4 pa = make_uint4(pack_bf16x2(pr[8 * s + 0], pr[8 * s + 1]),
@@ -197,23 +250,13 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
                                   pack_bf16x2(dsr[8 * s + 6], dsr[8 * s + 7]));
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int col = 2 * (32 * dt + l32);
-        uint32_t wg[4], wq[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r0 = 16 * s + 8 * (jj >> 1) + 4 * half + 2 * (jj & 1);
-          wg[jj] = static_cast<uint32_t>(*reinterpret_cast<const u16*>(&gs[r0 * kBP + col])) |
-                   (static_cast<uint32_t>(*reinterpret_cast<const u16*>(&gs[(r0 + 1) * kBP + col]))
-                    << 16);
-          wq[jj] = static_cast<uint32_t>(*reinterpret_cast<const u16*>(&qs[r0 * kBP + col])) |
-                   (static_cast<uint32_t>(*reinterpret_cast<const u16*>(&qs[(r0 + 1) * kBP + col]))
-                    << 16);
-        }
-        dv[dt] = mfma32(as_bf16x8(pa), as_bf16x8(make_uint4(wg[0], wg[1], wg[2], wg[3])), dv[dt]);
-        dk[dt] = mfma32(as_bf16x8(da), as_bf16x8(make_uint4(wq[0], wq[1], wq[2], wq[3])), dk[dt]);
+        const int o = (32 * dt + l32) * kTP + 2 * (16 * s + 8 * half);
+        dv[dt] = mfma32(as_bf16x8(pa), as_bf16x8(*reinterpret_cast<const uint4*>(&gT[o])), dv[dt]);
+        dk[dt] = mfma32(as_bf16x8(da), as_bf16x8(*reinterpret_cast<const uint4*>(&qT[o])), dk[dt]);
       }
     }
-    __syncthreads();  // dss complete; every wave is done with qs, gs and the row data
+    __syncthreads();  // dss complete; q, dO and the row data of this pass are consumed
+    if (more) stash(pass + 1);
 
     // dq^T of this wave's 32 dims x the pass's 32 rows = K^T dS^T over 128 keys
     f32x16 qacc = f32x16{};
@@ -227,12 +270,7 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
     }
     // partial of (row, slot): lane = row l32, dims 32 wave + 8(i/4) + 4 half + i%4
     {
-      const int rr = pass * 32 + l32;
-      const bool valid = rr < rows;
-      const int qi = valid ? rr / HG : 0;
-      const int hh = rr % HG;
-      const int e = a.entries[ch.y + qi];
-      const int prow = valid ? (((e >> 6) - a.rl_base) * a.k + (e & 63)) * HG + hh : a.sink + hh;
+      const int prow = r_prow[pass & 1][l32];
       u16* dst = a.dqpart + static_cast<int64_t>(prow) * kHeadDim + 32 * wave + 4 * half;
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
@@ -242,6 +280,7 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
         *reinterpret_cast<uint2*>(dst + 8 * a4) = w;
       }
     }
+    __syncthreads();  // dss is read; the next pass's rows are in LDS
   }
 
   // dK, dV of this wave's keys: lane = dim 32 dt + l32, keys m(i)
