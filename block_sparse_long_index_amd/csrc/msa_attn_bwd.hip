@@ -146,7 +146,9 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
   // and an empty causal range, so they add nothing to dK and dV; their dq
   // goes to the sink row.  The next pass's loads are issued before the
   // current pass's products and written to LDS after them.
-  const int rp = tid >> 4, cc = tid & 15;
+  // (rp varies fastest across lanes: one wave's stores to a transposed tile
+  // row then hit 16 consecutive words instead of one bank 16 times)
+  const int rp = tid & 15, cc = tid >> 4;
   uint4 fq[2], fg[2];
   float fl[2], fD[2];
   int flim[2], fprow[2];
@@ -268,17 +270,23 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
         qacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
                       as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), qacc);
     }
-    // partial of (row, slot): lane = row l32, dims 32 wave + 8(i/4) + 4 half + i%4
+    // partial of (row, slot), lane = row l32: the lane's 16 values (dims
+    // 32 wave + 8(i/4) + 4 half + i%4) are stored contiguously at element
+    // 32 wave + 16 half of the partial row (see dq_combine_kernel)
     {
       const int prow = r_prow[pass & 1][l32];
-      u16* dst = a.dqpart + static_cast<int64_t>(prow) * kHeadDim + 32 * wave + 4 * half;
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        uint2 w;
-        w.x = pack_bf16x2(qacc[4 * a4 + 0], qacc[4 * a4 + 1]);
-        w.y = pack_bf16x2(qacc[4 * a4 + 2], qacc[4 * a4 + 3]);
-        *reinterpret_cast<uint2*>(dst + 8 * a4) = w;
-      }
+      u16* dst = a.dqpart + static_cast<int64_t>(prow) * kHeadDim + 32 * wave + 16 * half;
+      uint4 w0, w1;
+      w0.x = pack_bf16x2(qacc[0], qacc[1]);
+      w0.y = pack_bf16x2(qacc[2], qacc[3]);
+      w0.z = pack_bf16x2(qacc[4], qacc[5]);
+      w0.w = pack_bf16x2(qacc[6], qacc[7]);
+      w1.x = pack_bf16x2(qacc[8], qacc[9]);
+      w1.y = pack_bf16x2(qacc[10], qacc[11]);
+      w1.z = pack_bf16x2(qacc[12], qacc[13]);
+      w1.w = pack_bf16x2(qacc[14], qacc[15]);
+      *reinterpret_cast<uint4*>(dst) = w0;
+      *reinterpret_cast<uint4*>(dst + 8) = w1;
     }
     __syncthreads();  // dss is read; the next pass's rows are in LDS
   }
@@ -338,7 +346,10 @@ struct DqArgs {
 };
 
 // dq of a row = the sum of its valid slots' partials, in slot order.  One wave
-// per (row, stage group); 16 lanes per head, 8 dims per lane.
+// per (row, stage group); 16 lanes per head, one 8-value piece per lane.  A
+// partial row holds its 128 dims in the KV-outer kernel's register order:
+// piece p (elements 8p .. 8p + 7) is wave w = p / 4, half h = (p / 2) % 2,
+// groups a = 2 (p % 2) + {0, 1}, i.e. dims 32 w + 8 a + 4 h + {0, 1, 2, 3}.
 template <int HG>
 __global__ void __launch_bounds__(256) dq_combine_kernel(DqArgs a) {
   const int lane = threadIdx.x & 63;
@@ -364,10 +375,11 @@ __global__ void __launch_bounds__(256) dq_combine_kernel(DqArgs a) {
           acc[2 * u + 1] += __uint_as_float(vw[u] & 0xffff0000u);
         }
       }
-      float4* dst = reinterpret_cast<float4*>(
-          a.dq + (grow * a.Hq + static_cast<int64_t>(a.group) * HG + h) * kHeadDim + 8 * piece);
-      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      const int d0 = 32 * (piece >> 2) + 16 * (piece & 1) + 4 * ((piece >> 1) & 1);
+      float* dst =
+          a.dq + (grow * a.Hq + static_cast<int64_t>(a.group) * HG + h) * kHeadDim + d0;
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(dst + 8) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
   }
 }
