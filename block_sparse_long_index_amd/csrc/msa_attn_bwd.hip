@@ -233,7 +233,8 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int m = 8 * (i >> 2) + 4 * half + (i & 3);
-      const float p = key_w <= r_lim[m] ? fast_exp2(fmaf(sacc[i], qscale, -r_l2[m])) : 0.f;
+      const float ex = fast_exp2(fmaf(sacc[i], qscale, -r_l2[m]));
+      const float p = key_w <= r_lim[m] ? ex : 0.f;
       pr[i] = p;
       dsr[i] = p * (pacc[i] - r_D[m]) * kScale;
       *reinterpret_cast<u16*>(&dss[m * kBP + 2 * key_w]) = f32_to_bf16(dsr[i]);
@@ -261,14 +262,21 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
     if (more) stash(pass + 1);
 
     // dq^T of this wave's 32 dims x the pass's 32 rows = K^T dS^T over 128 keys
-    f32x16 qacc = f32x16{};
+    f32x16 qacc;
     {
+      // two accumulator chains (even and odd k-steps) to halve the
+      // dependent-MFMA latency
       const unsigned char* ka = kt + (32 * wave + l32) * kBP + half * 16;
       const unsigned char* db = dss + l32 * kBP + half * 16;
+      f32x16 q0 = f32x16{}, q1 = f32x16{};
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        qacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
-                      as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), qacc);
+      for (int s = 0; s < 8; s += 2) {
+        q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
+                    as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
+        q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s + 32)),
+                    as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s + 32)), q1);
+      }
+      qacc = q0 + q1;
     }
     // partial of (row, slot), lane = row l32: the lane's 16 values (dims
     // 32 wave + 8(i/4) + 4 half + i%4) are stored contiguously at element
