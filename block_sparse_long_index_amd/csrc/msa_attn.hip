@@ -19,7 +19,6 @@
 
 namespace msa {
 
-constexpr int kChunkQueries = 128;  // queries per work chunk (rows = kChunkQueries * hg)
 static_assert(kChunkQueries % 64 == 0, "a chunk's entries fill whole wave registers");
 constexpr int kScanTile = 4096;    // elements per workgroup in the offset scan
 

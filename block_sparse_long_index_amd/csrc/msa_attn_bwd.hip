@@ -73,6 +73,7 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) unsigned char dss[32 * kBP];  // dS [row][key], bf16, scaled by c
   __shared__ float r_l2[32], r_D[32];
   __shared__ int r_lim[32], r_prow[2][32];
+  __shared__ int ents[kChunkQueries];  // the chunk's (row << 6 | slot) entries
 
   // the chunk list is dealt to the 8 XCDs in contiguous eighths (as forward)
   const int nchunks = *a.count;
@@ -127,6 +128,8 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
     *reinterpret_cast<uint4*>(&vs[r * kBP + 16 * c]) = r < nvalid ? y : make_uint4(0, 0, 0, 0);
   }
 
+  for (int i = tid; i < n; i += 256) ents[i] = a.entries[ch.y + i];
+  __syncthreads();
   const int rows = n * HG;
   const int64_t t0 = a.r0 - b * a.T;
   const int key_w = 32 * wave + l32;  // this lane's key in S, dP, dS
@@ -159,7 +162,7 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
       const bool valid = rr < rows;
       const int qi = valid ? rr / HG : 0;
       const int hh = rr % HG;
-      const int e = a.entries[ch.y + qi];
+      const int e = ents[qi];
       const int64_t t = t0 + (e >> 6);
       const int64_t hq = static_cast<int64_t>(g) * HG + hh;
       const int64_t off = ((b * a.T + t) * a.Hq + hq) * kHeadDim + 8 * cc;

@@ -37,6 +37,8 @@ hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T, 
                             int64_t Tw, int64_t N, int G, int Bk, int k, const PagedCache& pc,
                             hipStream_t st);
 
+// Queries per KV-outer work chunk (a chunk's rows = kChunkQueries * hg).
+constexpr int kChunkQueries = 128;
 struct AttnWorkspace {
   int32_t* hist;       // [G * NB * nc]: unit block counts, then exclusive offsets
   int32_t* tile_sums;  // [ntiles]
