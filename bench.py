@@ -122,6 +122,39 @@ def prefill_leg(args):
     return res
 
 
+def backward_leg(args, pre):
+    """Stage-4 backward (msa_sparse_attn_backward) on the prefill leg's
+    inputs and selection, with O and lse from the forward and a seeded dO;
+    timed with events on the launch stream."""
+    from msa_inputs import make_grad_output
+    w, inp, idx = pre["w"], pre["inp"], pre["idx"]
+    q, K, V = inp["q"], inp["K"], inp["V"]
+    O, lse = ops.sparse_attn_prefill(q, K, V, idx, return_lse=True)
+    dO = make_grad_output(w, device="cuda")
+    outs = (torch.empty(q.shape, dtype=torch.float32, device="cuda"),
+            torch.empty(K.shape, dtype=torch.float32, device="cuda"),
+            torch.empty(K.shape, dtype=torch.float32, device="cuda"))
+    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k)
+    ws = torch.empty(ops.workspace_bytes(ops.OP_ATTN_BACKWARD, d), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(max(1, args.warmup)):
+        ops.sparse_attn_backward(q, K, V, idx, O, lse, dO, out=outs, workspace=ws)
+    torch.cuda.synchronize()
+    events = [(ev(), ev()) for _ in range(args.steps)]
+    for e0, e1 in events:
+        e0.record()
+        ops.sparse_attn_backward(q, K, V, idx, O, lse, dO, out=outs, workspace=ws)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in events])
+    fl = acc.backward_flops(w.N, w.T, w.Hq, w.d_h, w.Bk, w.k, w.B)
+    tf = fl / (ms.mean() * 1e-3) / 1e12
+    log("[bench] backward %.3f ms (%.1f TFLOP/s)" % (ms.mean(), tf))
+    return {"workload": w.name, "ms": float(ms.mean()), "ms_min": float(ms.min()),
+            "flops": fl, "TFLOPs": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+            "outputs": "dq, dK, dV fp32"}
+
+
 def topk_leg(args, pre):
     """Stage 3 alone on materialised scores of the same workload."""
     w, inp = pre["w"], pre["inp"]
@@ -291,7 +324,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--only", default="",
-                    help="prefill | decode | topk | fp8 (skip the other legs)")
+                    help="prefill | decode | topk | fp8 | backward (skip the other legs)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-reps", type=int, default=30)
@@ -324,7 +357,7 @@ def main():
     out = {"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
-    if args.only in ("", "prefill", "topk", "fp8"):
+    if args.only in ("", "prefill", "topk", "fp8", "backward"):
         pre = prefill_leg(args)
         w = pre["w"]
         fl = pre["flops"]
@@ -356,6 +389,9 @@ def main():
         if args.only in ("", "fp8") and fused:
             log("[bench] fp8 index leg")
             out["fp8_index"] = fp8_leg(args, pre)
+        if args.only in ("", "backward") and fused:
+            log("[bench] backward leg")
+            out["backward"] = backward_leg(args, pre)
         if not args.no_cpu and args.only == "" and fused:
             log("[bench] cpu baseline")
             out["cpu_baseline"], out["parity_sample"] = cpu_leg(args, pre)

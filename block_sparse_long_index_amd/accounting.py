@@ -56,6 +56,13 @@ def main_flops(N, T, Hq, d_h, Bk, k, B=1) -> int:
     return 4 * Hq * d_h * support_tokens(N, T, Bk, k, B)
 
 
+def backward_flops(N, T, Hq, d_h, Bk, k, B=1) -> int:
+    """Stage-4 backward over the same supports: five products of the
+    forward's per-product size (S = q K^T recomputed, dP = dO V^T,
+    dV += P^T dO, dK += dS^T q, dq = dS K), against the forward's two."""
+    return 10 * Hq * d_h * support_tokens(N, T, Bk, k, B)
+
+
 def prefill_flops(w) -> dict:
     idx = index_flops(w.N, w.T, w.G, w.d_I, w.B)
     main = main_flops(w.N, w.T, w.Hq, w.d_h, w.Bk, w.k, w.B)

@@ -80,6 +80,9 @@ def test_workload_totals():
     assert abs(d["kv"] / 1e6 - 134.2) < 0.1
     tk = acc.topk_bytes(w)
     assert abs(tk["read"] / 1e9 - 2.145) < 0.01
+    # backward: five products of the forward's per-product size
+    assert acc.backward_flops(w.N, w.T, w.Hq, w.d_h, w.Bk, w.k) * 2 == fl["main"] * 5
+    assert abs(acc.backward_flops(w.N, w.T, w.Hq, w.d_h, w.Bk, w.k) / 1e12 - 21.15) < 0.01
     w0 = WORKLOADS["prefill_2k"]
     assert acc.support_tokens(w0.N, w0.T, w0.Bk, w0.k) == 820224
     assert np.isclose(acc.prefill_flops(w0)["index"], 1.074e9, rtol=1e-3)
