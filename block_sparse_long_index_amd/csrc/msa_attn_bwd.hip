@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) unsigned char gs[32 * kBP];   // the pass's dO rows [row][d]
   __shared__ __align__(16) unsigned char qT[128 * kTP];  // q^T [d][tpos(row)]
   __shared__ __align__(16) unsigned char gT[128 * kTP];  // dO^T [d][tpos(row)]
-  __shared__ __align__(16) unsigned char dss[32 * kBP];  // dS [row][key], bf16, scaled by c
+  __shared__ __align__(16) unsigned char dss[2][32 * kBP];  // dS [row][key], bf16, scaled by c
   __shared__ float r_l2[32], r_D[32];
   __shared__ int r_lim[32], r_prow[2][32];
   __shared__ int ents[kChunkQueries];  // the chunk's (row << 6 | slot) entries
@@ -213,25 +213,61 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
   stash(0);
   __syncthreads();
 
-  for (int pass = 0; pass * 32 < rows; ++pass) {
-    const bool more = (pass + 1) * 32 < rows;
+  // dq^T of this wave's 32 dims x pass p's 32 rows = K^T dS^T over the 128
+  // keys, from dss[p & 1]; stored as the (row, slot) partial, lane = row l32:
+  // the lane's 16 values (dims 32 wave + 8(i/4) + 4 half + i%4) go
+  // contiguously to element 32 wave + 16 half of the partial row (see
+  // dq_combine_kernel).
+  const unsigned char* ka = kt + (32 * wave + l32) * kBP + half * 16;
+  auto store_dq = [&](int p, const f32x16& qacc) {
+    const int prow = r_prow[p & 1][l32];
+    u16* dst = a.dqpart + static_cast<int64_t>(prow) * kHeadDim + 32 * wave + 16 * half;
+    uint4 w0, w1;
+    w0.x = pack_bf16x2(qacc[0], qacc[1]);
+    w0.y = pack_bf16x2(qacc[2], qacc[3]);
+    w0.z = pack_bf16x2(qacc[4], qacc[5]);
+    w0.w = pack_bf16x2(qacc[6], qacc[7]);
+    w1.x = pack_bf16x2(qacc[8], qacc[9]);
+    w1.y = pack_bf16x2(qacc[10], qacc[11]);
+    w1.z = pack_bf16x2(qacc[12], qacc[13]);
+    w1.w = pack_bf16x2(qacc[14], qacc[15]);
+    *reinterpret_cast<uint4*>(dst) = w0;
+    *reinterpret_cast<uint4*>(dst + 8) = w1;
+  };
+
+  // Pass p: the S / dP products of pass p run beside the dq product of pass
+  // p - 1 (two independent MFMA streams), then P, dS (into dss[p & 1]) and
+  // dK / dV; a barrier; the next pass's rows go to LDS; a barrier.
+  const int npass = (rows + 31) / 32;
+  for (int pass = 0; pass < npass; ++pass) {
+    const bool more = pass + 1 < npass;
     if (more) fetch(pass + 1);
-    // S = Q K^T and dP = dO V^T: rows on M, this wave's 32 keys on N
     f32x16 sacc = f32x16{}, pacc = f32x16{};
+    f32x16 q0 = f32x16{}, q1 = f32x16{};
     {
       const unsigned char* qa = qs + l32 * kBP + half * 16;
       const unsigned char* ga = gs + l32 * kBP + half * 16;
       const unsigned char* kb = ks + key_w * kBP + half * 16;
       const unsigned char* vb = vs + key_w * kBP + half * 16;
+      // dS of pass p - 1 (for pass 0 this reads the other buffer's stale
+      // contents, and the result is not stored)
+      const unsigned char* db = dss[(pass + 1) & 1] + l32 * kBP + half * 16;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(qa + 32 * s)),
                       as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s)), sacc);
         pacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ga + 32 * s)),
                       as_bf16x8(*reinterpret_cast<const uint4*>(vb + 32 * s)), pacc);
+        if (s & 1)
+          q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
+                      as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q1);
+        else
+          q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
+                      as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
       }
     }
     // P and c*dS; lane: key key_w, rows m(i) = 8(i/4) + 4 half + i%4
+    unsigned char* dsw = dss[pass & 1];
     float pr[16], dsr[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -240,8 +276,9 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
       const float p = key_w <= r_lim[m] ? ex : 0.f;
       pr[i] = p;
       dsr[i] = p * (pacc[i] - r_D[m]) * kScale;
-      *reinterpret_cast<u16*>(&dss[m * kBP + 2 * key_w]) = f32_to_bf16(dsr[i]);
+      *reinterpret_cast<u16*>(&dsw[m * kBP + 2 * key_w]) = f32_to_bf16(dsr[i]);
     }
+    if (pass > 0) store_dq(pass - 1, q0 + q1);
     // dV += P^T dO and dK += dS^T q over the pass's rows: keys on M, dims on
     // N; the B operands are the transposed tiles (see tpos).
 #pragma unroll
@@ -261,45 +298,25 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
         dk[dt] = mfma32(as_bf16x8(da), as_bf16x8(*reinterpret_cast<const uint4*>(&qT[o])), dk[dt]);
       }
     }
-    __syncthreads();  // dss complete; q, dO and the row data of this pass are consumed
-    if (more) stash(pass + 1);
-
-    // dq^T of this wave's 32 dims x the pass's 32 rows = K^T dS^T over 128 keys
-    f32x16 qacc;
-    {
-      // two accumulator chains (even and odd k-steps) to halve the
-      // dependent-MFMA latency
-      const unsigned char* ka = kt + (32 * wave + l32) * kBP + half * 16;
-      const unsigned char* db = dss + l32 * kBP + half * 16;
-      f32x16 q0 = f32x16{}, q1 = f32x16{};
+    // every wave is done with this pass's rows and with dss[(pass + 1) & 1];
+    // dss[pass & 1] is complete
+    __syncthreads();
+    if (more) {
+      stash(pass + 1);
+      __syncthreads();
+    }
+  }
+  {  // dq of the last pass
+    const unsigned char* db = dss[(npass - 1) & 1] + l32 * kBP + half * 16;
+    f32x16 q0 = f32x16{}, q1 = f32x16{};
 #pragma unroll
-      for (int s = 0; s < 8; s += 2) {
-        q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
-                    as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
-        q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s + 32)),
-                    as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s + 32)), q1);
-      }
-      qacc = q0 + q1;
+    for (int s = 0; s < 8; s += 2) {
+      q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
+                  as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
+      q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s + 32)),
+                  as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s + 32)), q1);
     }
-    // partial of (row, slot), lane = row l32: the lane's 16 values (dims
-    // 32 wave + 8(i/4) + 4 half + i%4) are stored contiguously at element
-    // 32 wave + 16 half of the partial row (see dq_combine_kernel)
-    {
-      const int prow = r_prow[pass & 1][l32];
-      u16* dst = a.dqpart + static_cast<int64_t>(prow) * kHeadDim + 32 * wave + 16 * half;
-      uint4 w0, w1;
-      w0.x = pack_bf16x2(qacc[0], qacc[1]);
-      w0.y = pack_bf16x2(qacc[2], qacc[3]);
-      w0.z = pack_bf16x2(qacc[4], qacc[5]);
-      w0.w = pack_bf16x2(qacc[6], qacc[7]);
-      w1.x = pack_bf16x2(qacc[8], qacc[9]);
-      w1.y = pack_bf16x2(qacc[10], qacc[11]);
-      w1.z = pack_bf16x2(qacc[12], qacc[13]);
-      w1.w = pack_bf16x2(qacc[14], qacc[15]);
-      *reinterpret_cast<uint4*>(dst) = w0;
-      *reinterpret_cast<uint4*>(dst + 8) = w1;
-    }
-    __syncthreads();  // dss is read; the next pass's rows are in LDS
+    store_dq(npass - 1, q0 + q1);
   }
 
   // dK, dV of this wave's keys: lane = dim 32 dt + l32, keys m(i)
