@@ -96,6 +96,8 @@ class OracleLib:
         lib.msa_oracle_attend.argtypes = [ctypes.POINTER(Dims), i64, P, P, P, P, P, P, P, P]
         lib.msa_oracle_attend_backward.argtypes = [ctypes.POINTER(Dims), i64, P, P, P, P, P, P,
                                                    P, i64, i64, P, P, P]
+        lib.msa_oracle_index_kl_backward.argtypes = [ctypes.POINTER(Dims), i64, P, P, P, P, P,
+                                                     P, P, i64, i64, P, P, P]
         for f in (lib.msa_oracle_block_scores, lib.msa_oracle_block_scores_fp8,
                   lib.msa_oracle_e4m3_values, lib.msa_oracle_select, lib.msa_oracle_attend):
             f.restype = None
@@ -204,6 +206,35 @@ class OracleLib:
                                             _ptr(dq), _ptr(dK), _ptr(dV))
         return dq, dK, dV
 
+    def index_kl_backward(self, d: Dims, row_b, row_t, qI_rows, kI, q_rows, K, idx, blk_lo=0,
+                          nblk=None):
+        """Index-branch KL alignment for the listed rows, given their
+        selection.  qI_rows [n, G, d_I], kI [B, N, d_I], q_rows [n, Hq, d_h],
+        K [B, G, N, d_h], idx [n, G, k] -> (dqI [n, G, d_I], dkI
+        [B, nblk*Bk, d_I], kl [n, G]) in fp64; dkI holds the listed rows'
+        contributions to the keys of blocks blk_lo .. blk_lo+nblk-1."""
+        rb, rt = _rows(row_b, row_t)
+        qi = bits(qI_rows)
+        ki = bits(kI)
+        q = bits(q_rows)
+        Kb = bits(K)
+        ix = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+        n = rb.size
+        NB = (d.N + d.Bk - 1) // d.Bk
+        if nblk is None:
+            nblk = NB - blk_lo
+        assert 0 <= blk_lo and blk_lo + nblk <= NB and nblk >= 1
+        assert qi.shape == (n, d.G, d.d_I) and ki.shape == (d.B, d.N, d.d_I)
+        assert q.shape == (n, d.Hq, d.d_h) and Kb.shape == (d.B, d.G, d.N, d.d_h)
+        assert ix.shape == (n, d.G, d.k) and ((ix >= -1) & (ix < NB)).all()
+        dqI = np.empty((n, d.G, d.d_I), dtype=np.float64)
+        dkI = np.empty((d.B, nblk * d.Bk, d.d_I), dtype=np.float64)
+        kl = np.empty((n, d.G), dtype=np.float64)
+        self.lib.msa_oracle_index_kl_backward(ctypes.byref(d), n, _ptr(rb), _ptr(rt), _ptr(qi),
+                                              _ptr(ki), _ptr(q), _ptr(Kb), _ptr(ix), blk_lo, nblk,
+                                              _ptr(dqI), _ptr(dkI), _ptr(kl))
+        return dqI, dkI, kl
+
     def forward(self, d: Dims, row_b, row_t, qI_rows, kI, q_rows, K, V):
         """All four stages for the listed rows; returns S, idx, O, lse and
         the wall time of each part."""
@@ -246,6 +277,10 @@ def attend(*a, **kw):
 
 def attend_backward(*a, **kw):
     return default().attend_backward(*a, **kw)
+
+
+def index_kl_backward(*a, **kw):
+    return default().index_kl_backward(*a, **kw)
 
 
 def forward(*a, **kw):

@@ -22,6 +22,9 @@
  *            back)
  *   stage 4 backward  dq, dK, dV of sum(dO . O) over the same support, the
  *            selection held fixed (msa_oracle_attend_backward)
+ *   index KL  the index branch's alignment loss KL(teacher || proxy) over
+ *            each row's support and its gradients dq^I, dk^I
+ *            (msa_oracle_index_kl_backward)
  *
  * Sources (the MSA study-notes page, dimensionstp.github.io/study-concept/msa):
  *   stages 1-3: section 2-3 "Fixed attention budget", the three displayed
@@ -431,4 +434,144 @@ void msa_oracle_attend_backward(const msa_oracle_dims *d, int64_t nrows,
         }
     free(hk);
     free(hv);
+}
+
+/* Index-branch KL alignment, backward.  Per row and group, over the row's
+ * support J (the visible keys of its selected blocks):
+ *   teacher  p_t(j)  = mean over the group's heads h of the main attention
+ *            weights softmax_J(q_h . K_j / sqrt(d_h)) (detached: no gradient
+ *            flows into q, K; study notes section 4-2 and 4-3);
+ *   proxy    p_x(j)  = softmax_J(s_j), s_j = q^I . k^I_j / sqrt(d_I) (the index
+ *            scores of stage 1, renormalised over the support, as the
+ *            Flash-MSA blog recomputes the proxy lse on the sparse support);
+ *   loss     KL(p_t || p_x) = sum_j p_t(j) (log p_t(j) - log p_x(j));
+ *   dL/ds_j  = p_x(j) - p_t(j)  (the blog's "KL divergence loss" section);
+ *   dq^I     = sum_j (p_x(j) - p_t(j)) k^I_j / sqrt(d_I);
+ *   dk^I_j  += (p_x(j) - p_t(j)) q^I / sqrt(d_I), summed over rows and groups.
+ * qI_rows [nrows, G, d_I], q_rows [nrows, Hq, d_h], kI [B, N, d_I],
+ * K [B, G, N, d_h], idx [nrows, G, k].  Out: dqI [nrows, G, d_I];
+ * dkI [B, nblk*Bk, d_I] for the keys of blocks blk_lo .. blk_lo+nblk-1
+ * (contributions of the listed rows only); kl [nrows, G]. */
+void msa_oracle_index_kl_backward(const msa_oracle_dims *d, int64_t nrows,
+                                  const int64_t *row_b, const int64_t *row_t,
+                                  const uint16_t *qI_rows, const uint16_t *kI,
+                                  const uint16_t *q_rows, const uint16_t *K,
+                                  const int32_t *idx, int64_t blk_lo, int64_t nblk,
+                                  double *dqI, double *dkI, double *kl)
+{
+    const int64_t Hq = d->Hq, G = d->G, dh = d->d_h, dI = d->d_I, k = d->k, Bk = d->Bk;
+    const int64_t hg = Hq / G;
+    const int64_t wkeys = nblk * Bk, key_lo = blk_lo * Bk;
+    const double root_h = sqrt((double)dh), root_i = sqrt((double)dI);
+    const size_t per_bg = (size_t)(wkeys * dI);
+    double *gk = (double *)calloc((size_t)(d->B * G) * per_bg, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bgi = 0; bgi < d->B * G; ++bgi) {
+        const int64_t b = bgi / G, g = bgi % G;
+        double *myk = gk + (size_t)bgi * per_bg;
+        double *qi = (double *)malloc(sizeof(double) * dI);
+        double *qh = (double *)malloc(sizeof(double) * dh);
+        double *pt = (double *)malloc(sizeof(double) * (size_t)(k * Bk));
+        double *z = (double *)malloc(sizeof(double) * (size_t)(k * Bk));
+        double *px = (double *)malloc(sizeof(double) * (size_t)(k * Bk));
+        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)(k * Bk));
+        const uint16_t *Kg = K + (b * G + g) * d->N * dh;
+        const uint16_t *kIb = kI + b * d->N * dI;
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (row_b[r] != b)
+                continue;
+            const int64_t p = position_of(d, row_t[r]);
+            const int32_t *sel = idx + (r * G + g) * k;
+            int64_t n = 0;
+            for (int64_t s = 0; s < k; ++s) {
+                const int64_t blk = sel[s];
+                if (blk < 0)
+                    continue;
+                int dup = 0;
+                for (int64_t u = 0; u < s; ++u)
+                    if (sel[u] == blk)
+                        dup = 1;
+                if (dup)
+                    continue;
+                for (int64_t j = blk * Bk; j < (blk + 1) * Bk && j <= p; ++j)
+                    key[n++] = j;
+            }
+            /* teacher: mean over the group's heads of the main weights */
+            for (int64_t i = 0; i < n; ++i)
+                pt[i] = 0.0;
+            for (int64_t h = g * hg; h < (g + 1) * hg; ++h) {
+                for (int64_t c = 0; c < dh; ++c)
+                    qh[c] = widen_bf16(q_rows[(r * Hq + h) * dh + c]);
+                double m = -INFINITY;
+                for (int64_t i = 0; i < n; ++i) {
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < dh; ++c)
+                        dot += qh[c] * widen_bf16(Kg[key[i] * dh + c]);
+                    z[i] = dot / root_h;
+                    if (z[i] > m)
+                        m = z[i];
+                }
+                double l = 0.0;
+                for (int64_t i = 0; i < n; ++i) {
+                    z[i] = exp(z[i] - m);
+                    l += z[i];
+                }
+                for (int64_t i = 0; i < n; ++i)
+                    pt[i] += z[i] / l / (double)hg;
+            }
+            /* proxy: softmax of the index scores over the same support */
+            for (int64_t c = 0; c < dI; ++c)
+                qi[c] = widen_bf16(qI_rows[(r * G + g) * dI + c]);
+            double m = -INFINITY;
+            for (int64_t i = 0; i < n; ++i) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < dI; ++c)
+                    dot += qi[c] * widen_bf16(kIb[key[i] * dI + c]);
+                px[i] = dot / root_i;
+                if (px[i] > m)
+                    m = px[i];
+            }
+            double l = 0.0;
+            for (int64_t i = 0; i < n; ++i)
+                l += exp(px[i] - m);
+            const double lse = m + log(l);
+            double loss = 0.0;
+            double *dq = dqI + (r * G + g) * dI;
+            for (int64_t c = 0; c < dI; ++c)
+                dq[c] = 0.0;
+            for (int64_t i = 0; i < n; ++i) {
+                const double logx = px[i] - lse;
+                if (pt[i] > 0.0)
+                    loss += pt[i] * (log(pt[i]) - logx);
+                const double dz = exp(logx) - pt[i];
+                const uint16_t *kv = kIb + key[i] * dI;
+                for (int64_t c = 0; c < dI; ++c)
+                    dq[c] += dz * widen_bf16(kv[c]) / root_i;
+                const int64_t kw = key[i] - key_lo;
+                if (kw < 0 || kw >= wkeys)
+                    continue;
+                for (int64_t c = 0; c < dI; ++c)
+                    myk[kw * dI + c] += dz * qi[c] / root_i;
+            }
+            kl[r * G + g] = loss;
+        }
+        free(qi);
+        free(qh);
+        free(pt);
+        free(z);
+        free(px);
+        free(key);
+    }
+    /* the shared index keys: sum over groups, in group order */
+    for (int64_t b = 0; b < d->B; ++b) {
+        double *o = dkI + (size_t)b * per_bg;
+        for (size_t e = 0; e < per_bg; ++e)
+            o[e] = 0.0;
+        for (int64_t g = 0; g < G; ++g) {
+            const double *sg = gk + (size_t)(b * G + g) * per_bg;
+            for (size_t e = 0; e < per_bg; ++e)
+                o[e] += sg[e];
+        }
+    }
+    free(gk);
 }

@@ -621,6 +621,101 @@ def pin_backward_closed_forms(orc):
     assert np.allclose(dVc, dV, atol=1e-10)  # dV does not depend on V
 
 
+
+# ------------------------------------------------- index-branch KL alignment
+def _kl_case(orc, B, T, N, Hq, G, dh, dI, Bk, k, seed, zero_q=False, zero_qI=False):
+    g = _gen(seed)
+    q = _randn_bf16(g, (B, T, Hq, dh))
+    K = _randn_bf16(g, (B, G, N, dh))
+    qI = _randn_bf16(g, (B, T, G, dI))
+    kI = _randn_bf16(g, (B, N, dI))
+    if zero_q:
+        q = torch.zeros_like(q)
+    if zero_qI:
+        qI = torch.zeros_like(qI)
+    d = dims_of(B, T, N, Hq, G, dh, dI, Bk, k)
+    rb, rt = _all_rows(B, T)
+    S = torch.randn(rb.size, G, -(-N // Bk), generator=g).double().numpy()
+    idx = orc.select(d, rt, S)
+    return d, rb, rt, q, K, qI, kI, idx
+
+
+def _kl_call(orc, d, rb, rt, q, K, qI, kI, idx):
+    B, T, Hq, dh = q.shape
+    return orc.index_kl_backward(d, rb, rt, qI.reshape(B * T, d.G, -1), kI,
+                                 q.reshape(B * T, Hq, dh), K, idx)
+
+
+def pin_index_kl_autograd(orc):
+    """dq^I, dk^I and the loss equal torch autograd of
+    sum KL(teacher || softmax(s)) over masked dense scores in fp64, with the
+    teacher (mean of the group's heads' attention weights) detached."""
+    for (B, T, N, Hq, G, dh, dI, Bk, k) in ((1, 50, 50, 6, 3, 8, 16, 4, 4),
+                                            (2, 19, 33, 4, 2, 8, 8, 4, 3)):
+        d, rb, rt, q, K, qI, kI, idx = _kl_case(orc, B, T, N, Hq, G, dh, dI, Bk, k, 51)
+        dqI, dkI, kl = _kl_call(orc, d, rb, rt, q, K, qI, kI, idx)
+        assert not dkI[:, N:].any()
+        hg = Hq // G
+        ix = idx.reshape(B, T, G, k)
+        for b in range(B):
+            mask = _mask_from_idx(ix[b], T, N, Bk, G)                  # [G, T, N]
+            qq = q[b].double().permute(1, 0, 2)                          # [Hq, T, dh]
+            sc = (qq @ K[b].double().repeat_interleave(hg, 0).transpose(1, 2)) / math.sqrt(dh)
+            sc = sc.masked_fill(~mask.repeat_interleave(hg, 0), -math.inf)
+            teacher = torch.softmax(sc, -1).view(G, hg, T, N).mean(1)    # [G, T, N]
+            qi = qI[b].double().permute(1, 0, 2).clone().requires_grad_(True)  # [G, T, dI]
+            ki = kI[b].double().clone().requires_grad_(True)
+            s = (qi @ ki.T) / math.sqrt(dI)
+            logp = torch.log_softmax(s.masked_fill(~mask, -math.inf), -1)
+            logp = logp.masked_fill(~mask, 0.0)
+            per_row = (torch.xlogy(teacher, teacher) - teacher * logp).sum(-1)  # [G, T]
+            per_row.sum().backward()
+            assert np.allclose(kl.reshape(B, T, G)[b], per_row.detach().T.numpy(), atol=1e-10)
+            assert np.allclose(dqI.reshape(B, T, G, dI)[b], qi.grad.permute(1, 0, 2).numpy(),
+                               atol=1e-10)
+            assert np.allclose(dkI[b, :N], ki.grad.numpy(), atol=1e-10)
+
+
+def pin_index_kl_finite_differences(orc):
+    """Central differences of sum KL (the oracle's own loss values) in a
+    q^I and a k^I coordinate set to 1.5 and moved by +-2^-7 (exact in
+    bf16) match dq^I and dk^I."""
+    B, T, N, Hq, G, dh, dI, Bk, k = 1, 24, 24, 4, 2, 8, 8, 4, 3
+    d, rb, rt, q, K, qI, kI, idx = _kl_case(orc, B, T, N, Hq, G, dh, dI, Bk, k, 52)
+    step = 2.0 ** -7
+    for name, where in (("qI", (0, 21, 1, 2)), ("qI", (0, 9, 0, 5)), ("kI", (0, 3, 4)),
+                        ("kI", (0, 17, 0))):
+        src = qI if name == "qI" else kI
+        vals = []
+        for v in (1.5 + step, 1.5 - step, 1.5):
+            t = src.clone()
+            t[where] = _bf16_value(v)
+            a = (t, kI) if name == "qI" else (qI, t)
+            vals.append(_kl_call(orc, d, rb, rt, q, K, a[0], a[1], idx))
+        num = (vals[0][2].sum() - vals[1][2].sum()) / (2 * step)
+        dqI, dkI, _ = vals[2]
+        ana = dqI.reshape(B, T, G, dI)[where] if name == "qI" else dkI[where]
+        assert abs(num - ana) <= 2e-3 * max(1.0, abs(ana)), (name, where, num, ana)
+        assert abs(ana) > 1e-4, (name, where, ana)
+
+
+def pin_index_kl_closed_forms(orc):
+    """Zero q and zero q^I make teacher and proxy both uniform on the
+    support: zero loss and zero gradients.  Equal index keys give dq^I = 0
+    (the weights' differences sum to zero).  The loss is never negative."""
+    B, T, N, Hq, G, dh, dI, Bk, k = 1, 40, 40, 4, 2, 8, 8, 4, 3
+    d, rb, rt, q, K, qI, kI, idx = _kl_case(orc, B, T, N, Hq, G, dh, dI, Bk, k, 53,
+                                            zero_q=True, zero_qI=True)
+    dqI, dkI, kl = _kl_call(orc, d, rb, rt, q, K, qI, kI, idx)
+    assert np.abs(kl).max() < 1e-12 and np.abs(dqI).max() < 1e-12 and np.abs(dkI).max() < 1e-12
+    d, rb, rt, q, K, qI, kI, idx = _kl_case(orc, B, T, N, Hq, G, dh, dI, Bk, k, 54)
+    kI_eq = kI[:, :1].expand_as(kI).contiguous()
+    dqI, _, kl = _kl_call(orc, d, rb, rt, q, K, qI, kI_eq, idx)
+    assert np.abs(dqI).max() < 1e-12
+    _, _, kl = _kl_call(orc, d, rb, rt, q, K, qI, kI, idx)
+    assert kl.min() >= -1e-12 and kl.max() > 1e-3
+
+
 ALL_PINS = [
     pin_scores_brute_force,
     pin_scores_zero_keys,
@@ -641,4 +736,7 @@ ALL_PINS = [
     pin_backward_dense_sdpa,
     pin_backward_finite_differences,
     pin_backward_closed_forms,
+    pin_index_kl_autograd,
+    pin_index_kl_finite_differences,
+    pin_index_kl_closed_forms,
 ]

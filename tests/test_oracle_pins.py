@@ -77,6 +77,15 @@ MUTATIONS = [
      "j < (blk + 1) * Bk && j < d->N; ++j)"),
     ("bwd_window_offset_dropped", "const int64_t kw = key[i] - key_lo;",
      "const int64_t kw = key[i];"),
+    ("kl_teacher_summed_not_averaged", "pt[i] += z[i] / l / (double)hg;", "pt[i] += z[i] / l;"),
+    ("kl_teacher_first_head_only", "for (int64_t h = g * hg; h < (g + 1) * hg; ++h) {\n                for (int64_t c = 0; c < dh; ++c)\n                    qh[c]",
+     "for (int64_t h = g * hg; h < g * hg + 1; ++h) {\n                for (int64_t c = 0; c < dh; ++c)\n                    qh[c]"),
+    ("kl_gradient_sign", "const double dz = exp(logx) - pt[i];", "const double dz = pt[i] - exp(logx);"),
+    ("kl_dqI_unscaled", "dq[c] += dz * widen_bf16(kv[c]) / root_i;", "dq[c] += dz * widen_bf16(kv[c]);"),
+    ("kl_dkI_first_group_only", "        for (int64_t g = 0; g < G; ++g) {\n            const double *sg",
+     "        for (int64_t g = 0; g < 1; ++g) {\n            const double *sg"),
+    ("kl_proxy_unnormalised", "const double lse = m + log(l);", "const double lse = m;"),
+    ("kl_loss_direction", "loss += pt[i] * (log(pt[i]) - logx);", "loss += exp(logx) * (logx - log(pt[i]));"),
     ("fp8_scores_use_bf16_decoder", "block_scores(d, nrows, row_b, row_t, qI_rows, kI, 1, S);",
      "block_scores(d, nrows, row_b, row_t, qI_rows, kI, 0, S);"),
 ]
