@@ -162,6 +162,16 @@ size_t backward_ws(const msa_dims_t* d, int64_t window) {
   return rowdot_bytes(d) + prefill_ws(d, window);
 }
 
+// Index-branch KL backward: the prefill's inversion and partial buffers,
+// then the proxy lse of every (row, group).
+size_t lpx_bytes(const msa_dims_t* d) {
+  return ((static_cast<size_t>(d->B * d->T * d->G) * sizeof(float)) + 255) & ~size_t(255);
+}
+
+size_t index_kl_ws(const msa_dims_t* d, int64_t window) {
+  return lpx_bytes(d) + prefill_ws(d, window);
+}
+
 size_t decode_ws(const msa_dims_t* d) {
   return msa::attn_workspace_bytes(d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, d->Bk, true);
 }
@@ -197,6 +207,7 @@ size_t msa_workspace_bytes(int op, const msa_dims_t* d) {
     case MSA_OP_ATTN_PREFILL: return prefill_ws(d, default_window(d));
     case MSA_OP_ATTN_DECODE: return d->T == 1 ? decode_ws(d) : 0;
     case MSA_OP_ATTN_BACKWARD: return backward_ws(d, default_window(d));
+    case MSA_OP_INDEX_KL_BACKWARD: return index_kl_ws(d, default_window(d));
   }
   return 0;
 }
@@ -377,6 +388,49 @@ int msa_sparse_attn_backward(const msa_dims_t* d, const void* q, const void* K, 
                                                  d->T, d->N, d->Hq, d->G, d->k, w,
                                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_backward");
+  return MSA_OK;
+}
+
+int msa_index_kl_backward(const msa_dims_t* d, const void* qI, const void* kI, const void* q,
+                          const void* K, const int32_t* idx, const float* lse, float* dqI,
+                          float* dkI, float* kl, void* ws, size_t ws_bytes, void* stream) {
+  MSA_TRY(check_dims(d));
+  MSA_TRY(need_bk128(d, "msa_index_kl_backward"));
+  MSA_TRY(check_ptr(qI, "qI"));
+  MSA_TRY(check_ptr(kI, "kI"));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(K, "K"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  MSA_TRY(check_ptr(lse, "lse"));
+  MSA_TRY(check_ptr(dqI, "dqI"));
+  MSA_TRY(check_ptr(dkI, "dkI"));
+  if (kl) MSA_TRY(check_ptr(kl, "kl"));
+  MSA_TRY(check_ptr(ws, "ws"));
+  int64_t hi = default_window(d);
+  if (index_kl_ws(d, 1) > ws_bytes)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "index KL backward needs at least %zu workspace bytes (%zu for the default "
+                "window), got %zu",
+                index_kl_ws(d, 1), index_kl_ws(d, hi), ws_bytes);
+  if (index_kl_ws(d, hi) > ws_bytes) {
+    int64_t lo = 1;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo + 1) / 2;
+      if (index_kl_ws(d, mid) <= ws_bytes)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    hi = lo;
+  }
+  float* lpx = static_cast<float*>(ws);
+  msa::AttnWorkspace w;
+  msa::attn_workspace_carve(static_cast<char*>(ws) + lpx_bytes(d), hi, stage_rows_for(d, hi),
+                            d->N, d->G, d->Hq / d->G, d->k, d->Bk, false, &w);
+  const hipError_t e = msa::launch_index_kl_backward(qI, kI, q, K, idx, lse, dqI, dkI, kl, lpx,
+                                                     d->B, d->T, d->N, d->Hq, d->G, d->k, w,
+                                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_index_kl_backward");
   return MSA_OK;
 }
 

@@ -437,6 +437,28 @@ static hipError_t dispatch_bwd(int hg, const BwdArgs& ba, const DqArgs& da, int6
   return hipErrorInvalidValue;
 }
 
+// The slot-ordered partial sum on its own (one value set per (row, group):
+// hg = 1, out [rows, outer, 128] with outer = groups).
+hipError_t launch_dq_combine(const int32_t* idx, const uint16_t* part, float* out, int64_t T,
+                             int64_t r0, int64_t rows, int outer, int G, int k, int rl_base,
+                             int group, hipStream_t st) {
+  DqArgs da;
+  da.idx = idx;
+  da.dqpart = part;
+  da.dq = out;
+  da.T = T;
+  da.r0 = r0;
+  da.rows = rows;
+  da.Hq = outer;
+  da.G = G;
+  da.k = k;
+  da.rl_base = rl_base;
+  da.group = group;
+  hipLaunchKernelGGL((dq_combine_kernel<1>), dim3(static_cast<unsigned>((rows + 3) / 4)),
+                     dim3(256), 0, st, da);
+  return hipGetLastError();
+}
+
 static unsigned nblocks_of(int64_t n, int per) {
   return static_cast<unsigned>((n + per - 1) / per);
 }

@@ -1,0 +1,540 @@
+// msa_index_kl.hip -- backward of the index branch's KL alignment on gfx950:
+// dq^I, dk^I (and the loss) of sum over rows and groups of KL(teacher ||
+// proxy), each row's selection held fixed, scheduled KV-outer from the
+// forward's inversion.
+//
+// Method: the study notes (sections 4-2 and 4-3) train the index branch by a
+// KL loss against the mean of the group's main-branch head weights, that
+// teacher detached; the Flash-MSA training blog (hackernews.jp, "KL
+// divergence loss") shows that the loss's gradient on the proxy logits is
+// the proxy weight minus the main weight, and recomputes the proxy lse over
+// the selected sparse activations.  Per (row, group), over the row's support
+// J (visible keys of its selected blocks), with c_I = 1/sqrt(128):
+//   s_j = c_I q^I . k^I_j,      p_x = softmax_J(s)          (proxy)
+//   p_t(j) = mean over the group's heads h of exp(q_h . K_j / sqrt(128) - lse_h)
+//   KL = sum_j p_t (log p_t - log p_x),  dz_j = p_x(j) - p_t(j),
+//   dq^I = c_I sum_j dz_j k^I_j,         dk^I_j += c_I dz_j q^I.
+// Two KV-outer passes per stage: index_px_kernel writes (max, sum) of the
+// proxy exponentials per (row, slot), px_combine_kernel makes the proxy lse
+// per row; index_kl_kernel then forms p_x, p_t and dz per (row, key), adds
+// dk^I (fp32 atomics: the index keys are shared by all groups) and writes
+// per-(row, slot) partials of dq^I and of the loss, summed in slot order.
+#include "msa_common.h"
+#include "msa_internal.h"
+
+#include <math.h>
+
+namespace msa {
+
+namespace {
+
+constexpr int kP = 272;   // LDS row pitch of a 128-column bf16 tile
+constexpr int kTq = 80;   // LDS row pitch of the transposed 32-query q^I tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kScale = 0.08838834764831845f;  // 1/sqrt(128)
+
+// Column of pass query r (0..31) in the transposed q^I tile: the k-slot order
+// of the dk^I product's A operand (see the backward kernel's transposed tiles).
+__device__ __forceinline__ int tcol(int r) {
+  const int o = r & 15;
+  return (r & 16) + 8 * ((o >> 2) & 1) + 4 * (o >> 3) + (o & 3);
+}
+
+struct IkArgs {
+  const u16* qI;          // [B, T, G, 128]
+  const u16* kI;          // [B, N, 128]
+  const u16* q;           // [B, T, Hq, 128]
+  const u16* K;           // [B, G, N, 128]
+  const float* lse;       // main lse [B, Hq, T], natural log
+  const float* lpx;       // proxy lse [B, G, T], log2 domain (index_kl_kernel)
+  const int4* chunks;
+  const int32_t* entries;
+  const int32_t* count;
+  float2* part;           // per (row, slot): (max, sum) or (loss, -)
+  u16* dqpart;            // per (row, slot): 128 bf16
+  float* dkI;             // [B, N, 128]
+  int64_t T, N, r0;
+  int32_t Hq, G, k, rl_base, sink;
+};
+
+// Proxy lse partials.  One workgroup per chunk; wave w takes queries
+// 32w..32w+31 of the chunk against the block's 128 index keys: s^T = k^I q^I^T
+// with keys on M, so a lane holds 16 keys of its query per 32-key tile and the
+// row max / sum stay in-register plus one half-wave exchange.
+static_assert(kChunkQueries == 128, "index_px_kernel: four waves of 32 queries cover a chunk");
+__global__ void __launch_bounds__(256) index_px_kernel(IkArgs a) {
+  __shared__ __align__(16) unsigned char kis[128 * kP];
+  const int nchunks = *a.count;
+  const int per_xcd = (nchunks + 7) >> 3;
+  const int xj = static_cast<int>(blockIdx.x >> 3);
+  const int ci = static_cast<int>(blockIdx.x & 7) * per_xcd + xj;
+  if (xj >= per_xcd || ci >= nchunks) return;
+  const int4 ch = a.chunks[ci];
+  const int n = ch.z;
+  if (n <= 0) return;
+  const int64_t blk = ch.w, bg = ch.x;
+  const int g = static_cast<int>(bg) & (a.G - 1);
+  const int64_t b = bg >> __builtin_ctz(a.G);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t key0 = blk * 128;
+  const int nvalid = static_cast<int>(a.N - key0 < 128 ? a.N - key0 : 128);
+  const u16* kb = a.kI + (b * a.N + key0) * kHeadDim;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = tid + 256 * j;
+    const int r = i >> 4, c = i & 15;
+    const uint4 y = ld16(kb + (r < nvalid ? r : nvalid - 1) * kHeadDim + 8 * c);
+    *reinterpret_cast<uint4*>(&kis[r * kP + 16 * c]) = r < nvalid ? y : make_uint4(0, 0, 0, 0);
+  }
+  // this lane's query
+  const int qi = 32 * wave + l32;
+  const bool valid = qi < n;
+  const int e = a.entries[ch.y + (valid ? qi : 0)];
+  const int64_t t = (a.r0 - b * a.T) + (e >> 6);
+  const int lim = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
+  const u16* qr = a.qI + ((b * a.T + t) * a.G + g) * kHeadDim + 8 * half;
+  bf16x8 qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(ld16(qr + 16 * s));
+  __syncthreads();
+  const float c2 = kScale * kLog2e;
+  float v[4][16];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    f32x16 acc = f32x16{};
+    const unsigned char* ka = kis + (32 * kt + l32) * kP + half * 16;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      acc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)), qf[s], acc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
+      v[kt][i] = key <= lim ? acc[i] * c2 : -INFINITY;
+    }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, v[kt][i]);
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float l = 0.f;
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) l += fast_exp2(v[kt][i] - m);
+  }
+  l += __shfl_xor(l, 32);
+  if (valid && half == 0) {
+    const int prow = ((e >> 6) - a.rl_base) * a.k + (e & 63);
+    a.part[prow] = make_float2(m, l);
+  }
+}
+
+struct PxArgs {
+  const int32_t* idx;
+  const float2* part;
+  float* lpx;  // [B, G, T], log2 domain
+  int64_t T, r0, rows;
+  int32_t G, k, rl_base, group;
+};
+
+// proxy lse of a row = log2 of the sum over its valid slots of l 2^m
+__global__ void __launch_bounds__(256) px_combine_kernel(PxArgs a) {
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (wid >= a.rows) return;
+  const int64_t grow = a.r0 + a.rl_base + wid;
+  const int64_t b = grow / a.T, t = grow % a.T;
+  const int32_t* ir = a.idx + ((b * a.G + a.group) * a.T + t) * a.k;
+  float M = -INFINITY;
+  int nval = 0;
+  for (int s = 0; s < a.k && ir[s] >= 0; ++s) {
+    M = fmaxf(M, a.part[wid * a.k + s].x);
+    nval = s + 1;
+  }
+  float L = 0.f;
+  for (int s = 0; s < nval; ++s) {
+    const float2 p = a.part[wid * a.k + s];
+    L += p.y * fast_exp2(p.x - M);
+  }
+  a.lpx[(b * a.G + a.group) * a.T + t] = M + __log2f(L);
+}
+
+// The gradient pass.  One workgroup per chunk, queries in passes of 32; wave w
+// owns keys 32w..32w+31 (their dk^I in registers for the whole chunk).  Per
+// pass: the index scores s (queries on M, keys on N) and, head by head, the
+// main scores with the head's q rows read straight from memory as the A
+// operand; the teacher is the mean of the heads' weights.  dz goes to LDS for
+// dq^I^T = k^I^T dz^T (wave w: dims 32w..32w+31).
+template <int HG>
+__global__ void __launch_bounds__(256, 1) index_kl_kernel(IkArgs a) {
+  __shared__ __align__(16) unsigned char kis[128 * kP];   // k^I [key][d]
+  __shared__ __align__(16) unsigned char kit[128 * kP];   // k^I^T [d][key]
+  __shared__ __align__(16) unsigned char ks[128 * kP];    // K [key][d]
+  __shared__ __align__(16) unsigned char qis[32 * kP];    // the pass's q^I [query][d]
+  __shared__ __align__(16) unsigned char qit[128 * kTq];  // q^I^T [d][tcol(query)]
+  __shared__ __align__(16) unsigned char dzs[32 * kP];    // dz [query][key], bf16
+  __shared__ float r_px[32], r_l2[HG][32], r_kl[4][32];  // r_kl: per wave, summed in order
+  __shared__ int r_lim[32], r_prow[32];
+  __shared__ int ents[kChunkQueries];
+
+  const int nchunks = *a.count;
+  const int per_xcd = (nchunks + 7) >> 3;
+  const int xj = static_cast<int>(blockIdx.x >> 3);
+  const int ci = static_cast<int>(blockIdx.x & 7) * per_xcd + xj;
+  if (xj >= per_xcd || ci >= nchunks) return;
+  const int4 ch = a.chunks[ci];
+  const int n = ch.z;
+  if (n <= 0) return;
+  const int64_t blk = ch.w, bg = ch.x;
+  const int g = static_cast<int>(bg) & (a.G - 1);
+  const int64_t b = bg >> __builtin_ctz(a.G);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t key0 = blk * 128;
+  const int nvalid = static_cast<int>(a.N - key0 < 128 ? a.N - key0 : 128);
+
+  // k^I (row-major and transposed) and K of the block; keys past N are zero
+  const u16* kib = a.kI + (b * a.N + key0) * kHeadDim;
+  const u16* Kb = a.K + (bg * a.N + key0) * kHeadDim;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + 256 * j;
+    const int kp = i & 63, c = i >> 6;
+    const int k0 = 2 * kp;
+    const uint4 y0 = ld16(kib + (k0 < nvalid ? k0 : nvalid - 1) * kHeadDim + 8 * c);
+    const uint4 y1 = ld16(kib + (k0 + 1 < nvalid ? k0 + 1 : nvalid - 1) * kHeadDim + 8 * c);
+    const uint4 x0 = k0 < nvalid ? y0 : make_uint4(0, 0, 0, 0);
+    const uint4 x1 = k0 + 1 < nvalid ? y1 : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&kis[k0 * kP + 16 * c]) = x0;
+    *reinterpret_cast<uint4*>(&kis[(k0 + 1) * kP + 16 * c]) = x1;
+    const uint32_t w0[4] = {x0.x, x0.y, x0.z, x0.w};
+    const uint32_t w1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t lo = (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      const uint32_t hi = (w1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      *reinterpret_cast<uint32_t*>(&kit[(8 * c + e) * kP + 2 * k0]) = lo | (hi << 16);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = tid + 256 * j;
+    const int r = i >> 4, c = i & 15;
+    const uint4 y = ld16(Kb + (r < nvalid ? r : nvalid - 1) * kHeadDim + 8 * c);
+    *reinterpret_cast<uint4*>(&ks[r * kP + 16 * c]) = r < nvalid ? y : make_uint4(0, 0, 0, 0);
+  }
+  if (tid < n) ents[tid] = a.entries[ch.y + tid];
+  __syncthreads();
+
+  const int64_t t0 = a.r0 - b * a.T;
+  const int key_w = 32 * wave + l32;
+  const float qscale = kLog2e * kScale;
+  f32x16 dk[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) dk[dt] = f32x16{};
+
+  const int npass = (n + 31) / 32;
+  for (int pass = 0; pass < npass; ++pass) {
+    // gather: thread -> query pair rp (queries 2rp, 2rp + 1), dims 8cc..8cc+7
+    {
+      const int rp = tid & 15, cc = tid >> 4;
+      uint4 x[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qq = pass * 32 + 2 * rp + u;
+        const bool valid = qq < n;
+        const int e = ents[valid ? qq : 0];
+        const int64_t t = t0 + (e >> 6);
+        const uint4 y = ld16(a.qI + ((b * a.T + t) * a.G + g) * kHeadDim + 8 * cc);
+        x[u] = valid ? y : make_uint4(0, 0, 0, 0);
+        if (cc == 0) {
+          const int r = 2 * rp + u;
+          r_lim[r] = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
+          r_px[r] = valid ? a.lpx[(b * a.G + g) * a.T + t] : INFINITY;
+          r_prow[r] = valid ? ((e >> 6) - a.rl_base) * a.k + (e & 63) : a.sink;
+        }
+        if (cc < HG) {
+          const int r = 2 * rp + u;
+          r_l2[cc][r] = valid ? a.lse[(b * a.Hq + static_cast<int64_t>(g) * HG + cc) * a.T + t] *
+                                    kLog2e
+                              : INFINITY;
+        }
+      }
+      const int r0 = 2 * rp;
+      *reinterpret_cast<uint4*>(&qis[r0 * kP + 16 * cc]) = x[0];
+      *reinterpret_cast<uint4*>(&qis[(r0 + 1) * kP + 16 * cc]) = x[1];
+      const int P = tcol(r0);
+      const uint32_t w0[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
+      const uint32_t w1[4] = {x[1].x, x[1].y, x[1].z, x[1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = 16 * (e & 1);
+        *reinterpret_cast<uint32_t*>(&qit[(8 * cc + e) * kTq + 2 * P]) =
+            ((w0[e >> 1] >> sh) & 0xffffu) | (((w1[e >> 1] >> sh) & 0xffffu) << 16);
+      }
+    }
+    __syncthreads();
+
+    // index scores s: queries on M (A = q^I rows), this wave's keys on N
+    f32x16 sacc = f32x16{};
+    {
+      const unsigned char* qa = qis + l32 * kP + half * 16;
+      const unsigned char* kb = kis + key_w * kP + half * 16;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(qa + 32 * s)),
+                      as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s)), sacc);
+    }
+    // teacher: the heads' weights, q rows of head h as the A operand straight
+    // from memory (lane = query l32, dims 16s + 8 half)
+    float tw[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tw[i] = 0.f;
+    {
+      const int qq = pass * 32 + l32;
+      const int e = ents[qq < n ? qq : 0];
+      const int64_t t = t0 + (e >> 6);
+      const u16* qb = a.q + ((b * a.T + t) * a.Hq + static_cast<int64_t>(g) * HG) * kHeadDim +
+                      8 * half;
+      const unsigned char* kb = ks + key_w * kP + half * 16;
+      uint4 qf[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf[s] = ld16(qb + 16 * s);
+      for (int h = 0; h < HG; ++h) {
+        uint4 qn[8];
+        if (h + 1 < HG) {
+#pragma unroll
+          for (int s = 0; s < 8; ++s) qn[s] = ld16(qb + (h + 1) * kHeadDim + 16 * s);
+        }
+        f32x16 m0 = f32x16{}, m1 = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; s += 2) {
+          m0 = mfma32(as_bf16x8(qf[s]), as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s)),
+                      m0);
+          m1 = mfma32(as_bf16x8(qf[s + 1]),
+                      as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s + 32)), m1);
+        }
+        const f32x16 sc = m0 + m1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = 8 * (i >> 2) + 4 * half + (i & 3);
+          const float ex = fast_exp2(fmaf(sc[i], qscale, -r_l2[h][m]));
+          tw[i] += key_w <= r_lim[m] ? ex : 0.f;
+        }
+        if (h + 1 < HG) {
+#pragma unroll
+          for (int s = 0; s < 8; ++s) qf[s] = qn[s];
+        }
+      }
+    }
+    // dz = p_x - p_t, the loss terms p_t (log p_t - log p_x); dz to LDS
+    const float c2 = kScale * kLog2e;
+    float dz[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = 8 * (i >> 2) + 4 * half + (i & 3);
+      const bool vis = key_w <= r_lim[m];
+      const float lx2 = fmaf(sacc[i], c2, -r_px[m]);  // log2 p_x
+      const float px = vis ? fast_exp2(lx2) : 0.f;
+      const float pt = tw[i] * (1.f / HG);
+      dz[i] = px - pt;
+      float term = (vis && pt > 0.f) ? pt * (__log2f(pt) - lx2) * kLn2 : 0.f;
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) term += __shfl_xor(term, o);  // over the half's keys
+      if (l32 == 0) r_kl[wave][m] = term;
+      *reinterpret_cast<u16*>(&dzs[m * kP + 2 * key_w]) = f32_to_bf16(dz[i] * kScale);
+    }
+    // dk^I += c_I dz^T q^I (keys on M, dims on N; B from the transposed tile)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint4 da = make_uint4(pack_bf16x2(dz[8 * s + 0] * kScale, dz[8 * s + 1] * kScale),
+                                  pack_bf16x2(dz[8 * s + 2] * kScale, dz[8 * s + 3] * kScale),
+                                  pack_bf16x2(dz[8 * s + 4] * kScale, dz[8 * s + 5] * kScale),
+                                  pack_bf16x2(dz[8 * s + 6] * kScale, dz[8 * s + 7] * kScale));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int o = (32 * dt + l32) * kTq + 2 * (16 * s + 8 * half);
+        dk[dt] = mfma32(as_bf16x8(da), as_bf16x8(*reinterpret_cast<const uint4*>(&qit[o])), dk[dt]);
+      }
+    }
+    __syncthreads();  // dzs and r_kl complete
+
+    // dq^I^T of this wave's 32 dims x the pass's queries = k^I^T (c_I dz)^T
+    {
+      const unsigned char* ka = kit + (32 * wave + l32) * kP + half * 16;
+      const unsigned char* db = dzs + l32 * kP + half * 16;
+      f32x16 q0 = f32x16{}, q1 = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; s += 2) {
+        q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
+                    as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
+        q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s + 32)),
+                    as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s + 32)), q1);
+      }
+      const f32x16 qacc = q0 + q1;
+      // lane = query l32: its 16 values at element 32 wave + 16 half of the
+      // partial row (the layout the dq combine reads)
+      u16* dst = a.dqpart + static_cast<int64_t>(r_prow[l32]) * kHeadDim + 32 * wave + 16 * half;
+      uint4 w0, w1;
+      w0.x = pack_bf16x2(qacc[0], qacc[1]);
+      w0.y = pack_bf16x2(qacc[2], qacc[3]);
+      w0.z = pack_bf16x2(qacc[4], qacc[5]);
+      w0.w = pack_bf16x2(qacc[6], qacc[7]);
+      w1.x = pack_bf16x2(qacc[8], qacc[9]);
+      w1.y = pack_bf16x2(qacc[10], qacc[11]);
+      w1.z = pack_bf16x2(qacc[12], qacc[13]);
+      w1.w = pack_bf16x2(qacc[14], qacc[15]);
+      *reinterpret_cast<uint4*>(dst) = w0;
+      *reinterpret_cast<uint4*>(dst + 8) = w1;
+    }
+    if (tid < 32)
+      a.part[r_prow[tid]] =
+          make_float2(((r_kl[0][tid] + r_kl[1][tid]) + r_kl[2][tid]) + r_kl[3][tid], 0.f);
+    __syncthreads();  // before the next pass's gather overwrites the tiles
+  }
+
+  // dk^I of this wave's keys (shared by every group): lane = dim 32 dt + l32
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t key = key0 + 32 * wave + 8 * (i >> 2) + 4 * half + (i & 3);
+    if (key < a.N) {
+      float* pk = a.dkI + (b * a.N + key) * kHeadDim + l32;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) unsafeAtomicAdd(pk + 32 * dt, dk[dt][i]);
+    }
+  }
+}
+
+struct KlArgs {
+  const int32_t* idx;
+  const float2* part;
+  float* kl;  // [B, G, T]
+  int64_t T, r0, rows;
+  int32_t G, k, rl_base, group;
+};
+
+// loss of a row = the sum of its valid slots' partials, in slot order
+__global__ void __launch_bounds__(256) kl_combine_kernel(KlArgs a) {
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (wid >= a.rows) return;
+  const int64_t grow = a.r0 + a.rl_base + wid;
+  const int64_t b = grow / a.T, t = grow % a.T;
+  const int32_t* ir = a.idx + ((b * a.G + a.group) * a.T + t) * a.k;
+  float sum = 0.f;
+  for (int s = 0; s < a.k && ir[s] >= 0; ++s) sum += a.part[wid * a.k + s].x;
+  a.kl[(b * a.G + a.group) * a.T + t] = sum;
+}
+
+__global__ void __launch_bounds__(256) ik_zero_kernel(float4* p, int64_t n4) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+unsigned nblk_of(int64_t n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
+
+hipError_t launch_kl(int hg, const IkArgs& ia, int64_t grid, hipStream_t st) {
+  const dim3 gd(static_cast<unsigned>(grid)), bd(256);
+  switch (hg) {
+    case 8: hipLaunchKernelGGL((index_kl_kernel<8>), gd, bd, 0, st, ia); break;
+    case 4: hipLaunchKernelGGL((index_kl_kernel<4>), gd, bd, 0, st, ia); break;
+    case 16: hipLaunchKernelGGL((index_kl_kernel<16>), gd, bd, 0, st, ia); break;
+    case 2: hipLaunchKernelGGL((index_kl_kernel<2>), gd, bd, 0, st, ia); break;
+    case 1: hipLaunchKernelGGL((index_kl_kernel<1>), gd, bd, 0, st, ia); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index_kl_backward(const void* qI, const void* kI, const void* q, const void* K,
+                                    const int32_t* idx, const float* lse, float* dqI, float* dkI,
+                                    float* kl, float* lpx, int64_t B, int64_t T, int64_t N,
+                                    int Hq, int G, int k, const AttnWorkspace& w,
+                                    hipStream_t st) {
+  const int hg = Hq / G;
+  const int64_t n4 = B * N * kHeadDim / 4;
+  hipLaunchKernelGGL(ik_zero_kernel, dim3(nblk_of(n4, 256)), dim3(256), 0, st,
+                     reinterpret_cast<float4*>(dkI), n4);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t t0 = 0; t0 < T; t0 += w.window) {
+      const int64_t W = (T - t0) < w.window ? (T - t0) : w.window;
+      int32_t S = 0;
+      e = launch_invert_window(idx, b, T, t0, W, N, G, k, 128, w, &S, st);
+      if (e != hipSuccess) return e;
+      const int64_t r0 = b * T + t0;
+      for (int g = 0; g < G; ++g) {
+        for (int32_t sub = 0; sub < S; ++sub) {
+          const int64_t si = static_cast<int64_t>(g) * S + sub;
+          const int32_t rl_base = sub * static_cast<int32_t>(w.stage_rows);
+          const int64_t rows = (W - rl_base) < w.stage_rows ? (W - rl_base) : w.stage_rows;
+          IkArgs ia;
+          ia.qI = static_cast<const u16*>(qI);
+          ia.kI = static_cast<const u16*>(kI);
+          ia.q = static_cast<const u16*>(q);
+          ia.K = static_cast<const u16*>(K);
+          ia.lse = lse;
+          ia.lpx = lpx;
+          ia.chunks = w.chunks + si * w.max_chunks;
+          ia.entries = w.entries;
+          ia.count = w.totals + 4 + si;
+          ia.part = w.lpart;
+          ia.dqpart = w.opart;
+          ia.dkI = dkI;
+          ia.T = T;
+          ia.N = N;
+          ia.r0 = r0;
+          ia.Hq = Hq;
+          ia.G = G;
+          ia.k = k;
+          ia.rl_base = rl_base;
+          ia.sink = static_cast<int32_t>(w.sink);
+          const int64_t grid = (w.max_chunks + 7) & ~static_cast<int64_t>(7);
+          hipLaunchKernelGGL(index_px_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+                             ia);
+          PxArgs pa;
+          pa.idx = idx;
+          pa.part = w.lpart;
+          pa.lpx = lpx;
+          pa.T = T;
+          pa.r0 = r0;
+          pa.rows = rows;
+          pa.G = G;
+          pa.k = k;
+          pa.rl_base = rl_base;
+          pa.group = g;
+          hipLaunchKernelGGL(px_combine_kernel, dim3(nblk_of(rows, 256)), dim3(256), 0, st, pa);
+          e = launch_kl(hg, ia, grid, st);
+          if (e != hipSuccess) return e;
+          e = launch_dq_combine(idx, w.opart, dqI, T, r0, rows, G, G, k, rl_base, g, st);
+          if (e != hipSuccess) return e;
+          if (kl) {
+            KlArgs ka;
+            ka.idx = idx;
+            ka.part = w.lpart;
+            ka.kl = kl;
+            ka.T = T;
+            ka.r0 = r0;
+            ka.rows = rows;
+            ka.G = G;
+            ka.k = k;
+            ka.rl_base = rl_base;
+            ka.group = g;
+            hipLaunchKernelGGL(kl_combine_kernel, dim3(nblk_of(rows, 256)), dim3(256), 0, st, ka);
+          }
+          e = hipGetLastError();
+          if (e != hipSuccess) return e;
+        }
+      }
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace msa

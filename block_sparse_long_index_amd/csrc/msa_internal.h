@@ -78,6 +78,20 @@ hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
                                 const void* dO, float* dq, float* dK, float* dV, float* Dr,
                                 int64_t B, int64_t T, int64_t N, int Hq, int G, int k,
                                 const AttnWorkspace& w, hipStream_t st);
+// Sum in slot order of per-(row, slot) bf16 partials (the backward's layout)
+// for the rows of one stage and group: out [.., outer, 128] fp32 at
+// (b*T + t) * outer + group.
+hipError_t launch_dq_combine(const int32_t* idx, const uint16_t* part, float* out, int64_t T,
+                             int64_t r0, int64_t rows, int outer, int G, int k, int rl_base,
+                             int group, hipStream_t st);
+// Index-branch KL alignment backward: dqI [B, T, G, 128], dkI [B, N, 128]
+// (fp32, overwritten), kl [B, G, T] (nullable) from q^I, k^I, q, K, idx and
+// the main lse [B, Hq, T]; lpx: B*G*T floats of scratch.  Bk = 128.
+hipError_t launch_index_kl_backward(const void* qI, const void* kI, const void* q, const void* K,
+                                    const int32_t* idx, const float* lse, float* dqI, float* dkI,
+                                    float* kl, float* lpx, int64_t B, int64_t T, int64_t N,
+                                    int Hq, int G, int k, const AttnWorkspace& w,
+                                    hipStream_t st);
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse,
                                int64_t B, int64_t T, int64_t N, int Hq, int G,

@@ -23,6 +23,7 @@ OP_SELECT_FROM_SCORES = 2
 OP_ATTN_PREFILL = 3
 OP_ATTN_DECODE = 4
 OP_ATTN_BACKWARD = 5
+OP_INDEX_KL_BACKWARD = 6
 
 # Every function the C header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -38,6 +39,8 @@ _SIGS = {
                                               ctypes.c_size_t, _P]),
     "msa_sparse_attn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                 _P, ctypes.c_size_t, _P]),
+    "msa_index_kl_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             ctypes.c_size_t, _P]),
     "msa_select_blocks_paged": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, _P, _P, _P, _P,
                                                ctypes.c_size_t, _P]),
     "msa_select_blocks_paged_fp8": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, _P, _P, _P, _P,
@@ -234,6 +237,37 @@ def sparse_attn_backward(q, K, V, idx, O, lse, dO, out=None, workspace=None):
                                           _ptr(dV), _ptr(ws), nbytes, _stream()),
            "msa_sparse_attn_backward")
     return dq, dK, dV
+
+
+def index_kl_backward(qI, kI, q, K, idx, lse, return_loss=False, out=None, workspace=None):
+    """Index-branch KL alignment gradients (Bk = 128).  qI [B,T,G,128],
+    kI [B,N,128], q [B,T,Hq,128], K [B,G,N,128] bf16, idx [B,G,T,k], lse
+    [B,Hq,T] fp32 (the prefill's) -> (dqI [B,T,G,128], dkI [B,N,128]) fp32,
+    plus the loss kl [B,G,T] when return_loss."""
+    B, T, G, dI = qI.shape
+    _, N, _ = kI.shape
+    Hq = q.shape[2]
+    k = idx.shape[-1]
+    _need(qI, "qI", torch.bfloat16)
+    _need(kI, "kI", torch.bfloat16, (B, N, dI))
+    _need(q, "q", torch.bfloat16, (B, T, Hq, q.shape[3]))
+    _need(K, "K", torch.bfloat16, (B, G, N, q.shape[3]))
+    _need(idx, "idx", torch.int32, (B, G, T, k))
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    d = dims(B, T, N, Hq, G, k, d_h=q.shape[3], d_I=dI)
+    if out is None:
+        out = (torch.empty(qI.shape, dtype=torch.float32, device=qI.device),
+               torch.empty(kI.shape, dtype=torch.float32, device=qI.device))
+    dqI, dkI = out
+    _need(dqI, "dqI", torch.float32, qI.shape)
+    _need(dkI, "dkI", torch.float32, kI.shape)
+    kl = torch.empty(B, G, T, dtype=torch.float32, device=qI.device) if return_loss else None
+    ws, nbytes = _workspace(OP_INDEX_KL_BACKWARD, d, workspace)
+    _check(lib().msa_index_kl_backward(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(q), _ptr(K),
+                                       _ptr(idx), _ptr(lse), _ptr(dqI), _ptr(dkI), _ptr(kl),
+                                       _ptr(ws), nbytes, _stream()),
+           "msa_index_kl_backward")
+    return (dqI, dkI, kl) if return_loss else (dqI, dkI)
 
 
 def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None, Bk=128):

@@ -84,7 +84,8 @@ enum {
     MSA_OP_SELECT_FROM_SCORES = 2,
     MSA_OP_ATTN_PREFILL = 3,
     MSA_OP_ATTN_DECODE = 4,
-    MSA_OP_ATTN_BACKWARD = 5
+    MSA_OP_ATTN_BACKWARD = 5,
+    MSA_OP_INDEX_KL_BACKWARD = 6
 };
 
 /*
@@ -194,6 +195,34 @@ int msa_sparse_attn_backward(const msa_dims_t *dims, const void *q, const void *
                              const void *V, const int32_t *idx, const void *O,
                              const float *lse, const void *dO, float *dq, float *dK,
                              float *dV, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of the index branch's KL alignment for training: per row and
+ * group, over the row's support (the visible keys of its selected blocks),
+ * teacher p_t = mean over the group's heads of the main attention weights
+ * (detached), proxy p_x = softmax of the index scores s over the same support,
+ * loss KL(p_t || p_x); its gradient on s is p_x - p_t, giving
+ * dq^I = (p_x - p_t) k^I / sqrt(d_I) and dk^I += (p_x - p_t) q^I / sqrt(d_I)
+ * summed over rows and groups (study notes sections 4-2 and 4-3 on the teacher
+ * and the detach; the Flash-MSA blog's "KL divergence loss" section on the
+ * gradient and the proxy lse recomputed over the sparse support).
+ *   qI, kI    bf16 [B, T, G, d_I], [B, N, d_I]   the index branch's inputs
+ *   q, K      bf16 [B, T, Hq, d_h], [B, G, N, d_h]
+ *   idx       int32 [B, G, T, k]     the forward's selection
+ *   lse       fp32 [B, Hq, T]        the main branch's lse from the prefill
+ *   dqI       fp32 [B, T, G, d_I]    out, overwritten
+ *   dkI       fp32 [B, N, d_I]       out, overwritten (keys no row selects get 0)
+ *   kl        fp32 [B, G, T]         out, the loss per row and group; may be NULL
+ *   ws / ws_bytes  >= msa_workspace_bytes(MSA_OP_INDEX_KL_BACKWARD) for the
+ *                  default window; smaller (down to one row per window plus
+ *                  B*G*T floats) runs more windows.
+ * Needs Bk = 128.  dkI is accumulated with fp32 atomic adds; dqI and kl are
+ * summed in slot order.  Scaling by a loss weight is the caller's.
+ */
+int msa_index_kl_backward(const msa_dims_t *dims, const void *qI, const void *kI,
+                          const void *q, const void *K, const int32_t *idx, const float *lse,
+                          float *dqI, float *dkI, float *kl, void *ws, size_t ws_bytes,
+                          void *stream);
 
 /*
  * Stage 4 for decode (T must be 1): split over the B * G * k selected KV

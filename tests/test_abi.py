@@ -22,7 +22,7 @@ def _declared():
 def test_header_functions_are_exported():
     L = ops.lib()
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(ops._SIGS)
@@ -192,3 +192,26 @@ def test_backward_argument_checks():
     d64 = _good(Bk=64, k=4)
     assert L.msa_sparse_attn_backward(ctypes.byref(d64), *args, FAKE, 1 << 40, None) == -2
     assert b"Bk" in L.msa_last_error()
+
+
+def test_index_kl_argument_checks():
+    """Validation before any HIP call: every required pointer (kl may be
+    NULL), Bk = 128, the workspace floor."""
+    L = ops.lib()
+    d = _good()
+    need = L.msa_workspace_bytes(ops.OP_INDEX_KL_BACKWARD, ctypes.byref(d))
+    assert need >= L.msa_workspace_bytes(ops.OP_ATTN_PREFILL, ctypes.byref(d)) + 256 * 2 * 4
+    args = [FAKE] * 9  # qI kI q K idx lse dqI dkI kl
+    for i in range(8):
+        bad = list(args)
+        bad[i] = None
+        assert L.msa_index_kl_backward(ctypes.byref(d), *bad, FAKE, need, None) == -1
+        bad[i] = MISALIGNED
+        assert L.msa_index_kl_backward(ctypes.byref(d), *bad, FAKE, need, None) == -1
+    bad = list(args)
+    bad[8] = MISALIGNED
+    assert L.msa_index_kl_backward(ctypes.byref(d), *bad, FAKE, need, None) == -1
+    assert L.msa_index_kl_backward(ctypes.byref(d), *args, None, need, None) == -1
+    assert L.msa_index_kl_backward(ctypes.byref(d), *args, FAKE, 64, None) == -3
+    d64 = _good(Bk=64, k=4)
+    assert L.msa_index_kl_backward(ctypes.byref(d64), *args, FAKE, 1 << 40, None) == -2
