@@ -155,6 +155,40 @@ def backward_leg(args, pre):
             "outputs": "dq, dK, dV fp32"}
 
 
+def index_kl_leg(args, pre):
+    """Index-branch KL alignment backward (msa_index_kl_backward) on the
+    prefill leg's inputs, selection and main lse; events on the launch
+    stream.  Work: the teacher's main scores for every head (2 d_h FLOP per
+    (row, head, support key)) plus the index scores twice (proxy lse, then
+    the gradient pass) and the two gradient products (2 d_I FLOP each per
+    (row, group, support key))."""
+    w, inp, idx = pre["w"], pre["inp"], pre["idx"]
+    _, lse = ops.sparse_attn_prefill(inp["q"], inp["K"], inp["V"], idx, return_lse=True)
+    outs = (torch.empty(inp["qI"].shape, dtype=torch.float32, device="cuda"),
+            torch.empty(inp["kI"].shape, dtype=torch.float32, device="cuda"))
+    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k)
+    ws = torch.empty(ops.workspace_bytes(ops.OP_INDEX_KL_BACKWARD, d), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda: ops.index_kl_backward(inp["qI"], inp["kI"], inp["q"], inp["K"], idx, lse,
+                                         out=outs, workspace=ws)
+    for _ in range(max(1, args.warmup)):
+        call()
+    torch.cuda.synchronize()
+    events = [(ev(), ev()) for _ in range(args.steps)]
+    for e0, e1 in events:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in events])
+    fl = acc.index_kl_flops(w.N, w.T, w.Hq, w.G, w.d_h, w.d_I, w.Bk, w.k, w.B)
+    tf = fl / (ms.mean() * 1e-3) / 1e12
+    log("[bench] index KL backward %.3f ms (%.1f TFLOP/s)" % (ms.mean(), tf))
+    return {"workload": w.name, "ms": float(ms.mean()), "ms_min": float(ms.min()), "flops": fl,
+            "TFLOPs": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+            "outputs": "dqI, dkI fp32"}
+
+
 def topk_leg(args, pre):
     """Stage 3 alone on materialised scores of the same workload."""
     w, inp = pre["w"], pre["inp"]
@@ -392,6 +426,8 @@ def main():
         if args.only in ("", "backward") and fused:
             log("[bench] backward leg")
             out["backward"] = backward_leg(args, pre)
+            log("[bench] index KL backward leg")
+            out["index_kl_backward"] = index_kl_leg(args, pre)
         if not args.no_cpu and args.only == "" and fused:
             log("[bench] cpu baseline")
             out["cpu_baseline"], out["parity_sample"] = cpu_leg(args, pre)

@@ -63,6 +63,15 @@ def backward_flops(N, T, Hq, d_h, Bk, k, B=1) -> int:
     return 10 * Hq * d_h * support_tokens(N, T, Bk, k, B)
 
 
+def index_kl_flops(N, T, Hq, G, d_h, d_I, Bk, k, B=1) -> int:
+    """Index-branch KL backward over the same supports: the teacher's main
+    scores for every head (2 d_h per (row, head, key)), the index scores twice
+    (proxy lse pass, gradient pass) and the two gradient products dq^I, dk^I
+    (2 d_I each per (row, group, key))."""
+    n = support_tokens(N, T, Bk, k, B)
+    return 2 * Hq * d_h * n + 8 * G * d_I * n
+
+
 def prefill_flops(w) -> dict:
     idx = index_flops(w.N, w.T, w.G, w.d_I, w.B)
     main = main_flops(w.N, w.T, w.Hq, w.d_h, w.Bk, w.k, w.B)

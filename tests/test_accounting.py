@@ -83,6 +83,10 @@ def test_workload_totals():
     # backward: five products of the forward's per-product size
     assert acc.backward_flops(w.N, w.T, w.Hq, w.d_h, w.Bk, w.k) * 2 == fl["main"] * 5
     assert abs(acc.backward_flops(w.N, w.T, w.Hq, w.d_h, w.Bk, w.k) / 1e12 - 21.15) < 0.01
+    # index KL backward: the teacher's scores (half a forward) + 4 index products
+    kl = acc.index_kl_flops(w.N, w.T, w.Hq, w.G, w.d_h, w.d_I, w.Bk, w.k)
+    assert kl * 2 == fl["main"] + 8 * w.G * w.d_I * acc.support_tokens(w.N, w.T, w.Bk, w.k) * 2
+    assert abs(kl / 1e12 - 6.344) < 0.01
     w0 = WORKLOADS["prefill_2k"]
     assert acc.support_tokens(w0.N, w0.T, w0.Bk, w0.k) == 820224
     assert np.isclose(acc.prefill_flops(w0)["index"], 1.074e9, rtol=1e-3)
