@@ -177,6 +177,7 @@ __global__ void __launch_bounds__(256, 1) index_kl_kernel(IkArgs a) {
   __shared__ __align__(16) unsigned char qis[32 * kP];    // the pass's q^I [query][d]
   __shared__ __align__(16) unsigned char qit[128 * kTq];  // q^I^T [d][tcol(query)]
   __shared__ __align__(16) unsigned char dzs[32 * kP];    // dz [query][key], bf16
+  __shared__ __align__(16) unsigned char qbuf[2][32 * kP];  // one head's q rows, double-buffered
   __shared__ float r_px[32], r_l2[HG][32], r_kl[4][32];  // r_kl: per wave, summed in order
   __shared__ int r_lim[32], r_prow[32];
   __shared__ int ents[kChunkQueries];
@@ -237,8 +238,25 @@ __global__ void __launch_bounds__(256, 1) index_kl_kernel(IkArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) dk[dt] = f32x16{};
 
+  // the teacher's q rows: thread -> query tid / 8, dims 16 (tid % 8) .. +15;
+  // the loads of up to four heads are issued together (at the start of a pass)
+  constexpr int HB = HG < 4 ? HG : 4;
+  const int gq = tid >> 3, g8 = tid & 7;
   const int npass = (n + 31) / 32;
   for (int pass = 0; pass < npass; ++pass) {
+    const bool gvalid = pass * 32 + gq < n;
+    const u16* gqb;
+    {
+      const int ge = ents[gvalid ? pass * 32 + gq : 0];
+      gqb = a.q + ((b * a.T + t0 + (ge >> 6)) * a.Hq + static_cast<int64_t>(g) * HG) * kHeadDim +
+            16 * g8;
+    }
+    uint4 qh[HB][2];
+#pragma unroll
+    for (int j = 0; j < HB; ++j) {
+      qh[j][0] = ld16(gqb + j * kHeadDim);
+      qh[j][1] = ld16(gqb + j * kHeadDim + 8);
+    }
     // gather: thread -> query pair rp (queries 2rp, 2rp + 1), dims 8cc..8cc+7
     {
       const int rp = tid & 15, cc = tid >> 4;
@@ -289,45 +307,48 @@ __global__ void __launch_bounds__(256, 1) index_kl_kernel(IkArgs a) {
         sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(qa + 32 * s)),
                       as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s)), sacc);
     }
-    // teacher: the heads' weights, q rows of head h as the A operand straight
-    // from memory (lane = query l32, dims 16s + 8 half)
+    // teacher: the heads' weights.  Head h's q rows go through qbuf[h & 1]
+    // (one barrier per head) as the A operand (lane = query l32, dims
+    // 16s + 8 half); rows past the chunk's end are zero.
     float tw[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) tw[i] = 0.f;
     {
-      const int qq = pass * 32 + l32;
-      const int e = ents[qq < n ? qq : 0];
-      const int64_t t = t0 + (e >> 6);
-      const u16* qb = a.q + ((b * a.T + t) * a.Hq + static_cast<int64_t>(g) * HG) * kHeadDim +
-                      8 * half;
       const unsigned char* kb = ks + key_w * kP + half * 16;
-      uint4 qf[8];
+#pragma unroll 1
+      for (int hb = 0; hb < HG; hb += HB) {
+        if (hb > 0) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) qf[s] = ld16(qb + 16 * s);
-      for (int h = 0; h < HG; ++h) {
-        uint4 qn[8];
-        if (h + 1 < HG) {
-#pragma unroll
-          for (int s = 0; s < 8; ++s) qn[s] = ld16(qb + (h + 1) * kHeadDim + 16 * s);
+          for (int j = 0; j < HB; ++j) {
+            qh[j][0] = ld16(gqb + (hb + j) * kHeadDim);
+            qh[j][1] = ld16(gqb + (hb + j) * kHeadDim + 8);
+          }
         }
-        f32x16 m0 = f32x16{}, m1 = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 8; s += 2) {
-          m0 = mfma32(as_bf16x8(qf[s]), as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s)),
-                      m0);
-          m1 = mfma32(as_bf16x8(qf[s + 1]),
-                      as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s + 32)), m1);
-        }
-        const f32x16 sc = m0 + m1;
+        for (int j = 0; j < HB; ++j) {
+          const int h = hb + j;
+          unsigned char* qt = qbuf[h & 1];
+          *reinterpret_cast<uint4*>(&qt[gq * kP + 32 * g8]) =
+              gvalid ? qh[j][0] : make_uint4(0, 0, 0, 0);
+          *reinterpret_cast<uint4*>(&qt[gq * kP + 32 * g8 + 16]) =
+              gvalid ? qh[j][1] : make_uint4(0, 0, 0, 0);
+          __syncthreads();
+          const unsigned char* qa = qt + l32 * kP + half * 16;
+          f32x16 m0 = f32x16{}, m1 = f32x16{};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = 8 * (i >> 2) + 4 * half + (i & 3);
-          const float ex = fast_exp2(fmaf(sc[i], qscale, -r_l2[h][m]));
-          tw[i] += key_w <= r_lim[m] ? ex : 0.f;
-        }
-        if (h + 1 < HG) {
+          for (int s = 0; s < 8; s += 2) {
+            m0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(qa + 32 * s)),
+                        as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s)), m0);
+            m1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(qa + 32 * s + 32)),
+                        as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s + 32)), m1);
+          }
+          const f32x16 sc = m0 + m1;
 #pragma unroll
-          for (int s = 0; s < 8; ++s) qf[s] = qn[s];
+          for (int i = 0; i < 16; ++i) {
+            const int m = 8 * (i >> 2) + 4 * half + (i & 3);
+            const float ex = fast_exp2(fmaf(sc[i], qscale, -r_l2[h][m]));
+            tw[i] += key_w <= r_lim[m] ? ex : 0.f;
+          }
         }
       }
     }
