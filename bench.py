@@ -371,7 +371,7 @@ def main():
                     help="run one 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if "RANK" in os.environ and int(os.environ.get("WORLD_SIZE", "1")) > 1:
