@@ -351,6 +351,52 @@ def cpu_leg(args, pre):
                       "uniform rows; fp64 plain C, OpenMP over rows" % (n, w.G, w.Hq, w.name)}, parity
 
 
+def cpu_train_leg(args, pre):
+    """The oracle's two backward functions, as they stand, on host cores, on
+    a bounded sample of rows of the prefill workload (their selection from
+    the oracle's own stages 1-3, outside the timed region); scaled to
+    TFLOP/s by the sample's algorithmic FLOPs (the accounting of the GPU
+    legs).  dK / dV and dk^I are accumulated for an 8-block window."""
+    import oracle
+    from msa_inputs import make_grad_output
+    w, inp = pre["w"], pre["inp"]
+    d = oracle.dims_of(w.B, w.T, w.N, w.Hq, w.G, w.d_h, w.d_I, w.Bk, w.k)
+    kI, K, V = inp["kI"].cpu(), inp["K"].cpu(), inp["V"].cpu()
+    dO = make_grad_output(w, device="cuda")
+    out = {}
+    for leg in ("backward", "index_kl_backward"):
+        n = 16
+        while True:
+            rb, rt = sample_rows(w, n, seed=5)
+            rbd, rtd = rb.cuda(), rt.cuda()
+            S = oracle.block_scores(d, rb.numpy(), rt.numpy(), inp["qI"][rbd, rtd].cpu(), kI)
+            idx = oracle.select(d, rt.numpy(), S)
+            q_rows = inp["q"][rbd, rtd].cpu()
+            t0 = time.perf_counter()
+            if leg == "backward":
+                oracle.attend_backward(d, rb.numpy(), rt.numpy(), q_rows, dO[rbd, rtd].cpu(), K,
+                                       V, idx, blk_lo=w.NB - 8, nblk=8)
+            else:
+                oracle.index_kl_backward(d, rb.numpy(), rt.numpy(), inp["qI"][rbd, rtd].cpu(), kI,
+                                         q_rows, K, idx, blk_lo=w.NB - 8, nblk=8)
+            sec = time.perf_counter() - t0
+            if sec * 2 > args.cpu_seconds / 3 or n >= 4096:
+                break
+            n = int(min(4096, max(2 * n, n * (args.cpu_seconds / 3) / max(sec, 1e-3))))
+        p = (w.N - w.T) + rt.numpy()
+        nsel = np.minimum(p // w.Bk, w.k - 1) * w.Bk + p % w.Bk + 1
+        if leg == "backward":
+            fl = float(10 * w.Hq * w.d_h * nsel.sum())
+        else:
+            fl = float((2 * w.Hq * w.d_h + 8 * w.G * w.d_I) * nsel.sum())
+        log("[bench] cpu oracle %s: %d rows, %.2fs" % (leg, len(rb), sec))
+        out[leg] = {"value": fl / sec / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+                    "kind": "oracle", "seconds": sec,
+                    "sample": "%d query rows (all %d groups, %d heads) of %s; fp64 plain C, "
+                              "OpenMP" % (len(rb), w.G, w.Hq, w.name)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -431,6 +477,10 @@ def main():
         if not args.no_cpu and args.only == "" and fused:
             log("[bench] cpu baseline")
             out["cpu_baseline"], out["parity_sample"] = cpu_leg(args, pre)
+            log("[bench] cpu baseline of the backward calls")
+            cb = cpu_train_leg(args, pre)
+            out["backward"]["cpu_baseline"] = cb["backward"]
+            out["index_kl_backward"]["cpu_baseline"] = cb["index_kl_backward"]
         del pre
         torch.cuda.empty_cache()
     if args.only in ("", "decode"):
