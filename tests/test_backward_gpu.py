@@ -210,3 +210,38 @@ def test_backward_full_32k():
 
 def test_backward_full_128k():
     _full("prefill_128k", 24)
+
+
+def _random_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        G = int(g.choice([1, 2, 4, 8, 16]))
+        hg = int(g.choice([1, 2, 4, 8, 16]))
+        if G * hg > 64:
+            continue
+        k = int(g.integers(1, 17))
+        N = int(g.integers(1, 2600))
+        T = int(g.choice([N, int(g.integers(1, N + 1))]))
+        B = int(g.integers(1, 4))
+        cases.append((B, T, N, G * hg, G, k))
+    return cases
+
+
+@pytest.mark.parametrize("B,T,N,Hq,G,k", _random_cases(10, 77))
+def test_backward_random_shapes(B, T, N, Hq, G, k):
+    """Seeded random shapes (chunked rows, group layouts, k): every row's dq
+    and every key's dK / dV against the oracle."""
+    w = Workload("rand", B=B, T=T, N=N, Hq=Hq, G=G, k=k, seed=N * 3 + T)
+    say("case", w)
+    inp = make_inputs(w, device="cuda")
+    dO = make_grad_output(w, device="cuda")
+    idx, dq, dK, dV = run_gpu(w, inp, dO)
+    rb = np.repeat(np.arange(B), T)
+    rt = np.tile(np.arange(T), B)
+    ref_idx = oracle_selection(w, inp, rb, rt)
+    assert np.array_equal(gpu_rows(idx, rb, rt), ref_idx), "selection"
+    rdq, rdK, rdV = oracle_backward(w, inp, dO, rb, rt, ref_idx)
+    close("rand dq", dq.cpu().reshape(B * T, Hq, -1), rdq)
+    close("rand dK", dK.cpu(), rdK[:, :, :N])
+    close("rand dV", dV.cpu(), rdV[:, :, :N])

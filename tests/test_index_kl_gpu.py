@@ -196,3 +196,37 @@ def test_index_kl_full_32k():
 
 def test_index_kl_full_128k():
     _full("prefill_128k", 24)
+
+
+def _random_cases(n, seed):
+    g = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        G = int(g.choice([1, 2, 4, 8, 16]))
+        hg = int(g.choice([1, 2, 4, 8, 16]))
+        if G * hg > 64:
+            continue
+        k = int(g.integers(1, 17))
+        N = int(g.integers(1, 2600))
+        T = int(g.choice([N, int(g.integers(1, N + 1))]))
+        B = int(g.integers(1, 4))
+        cases.append((B, T, N, G * hg, G, k))
+    return cases
+
+
+@pytest.mark.parametrize("B,T,N,Hq,G,k", _random_cases(10, 78))
+def test_index_kl_random_shapes(B, T, N, Hq, G, k):
+    """Seeded random shapes: every row's dq^I and loss and every key's dk^I
+    against the oracle."""
+    w = Workload("rand", B=B, T=T, N=N, Hq=Hq, G=G, k=k, seed=N * 5 + T)
+    say("case", w)
+    inp = make_inputs(w, device="cuda")
+    idx, dqI, dkI, kl = run_gpu(w, inp)
+    rb = np.repeat(np.arange(B), T)
+    rt = np.tile(np.arange(T), B)
+    ref_idx = oracle_selection(w, inp, rb, rt)
+    assert np.array_equal(gpu_rows(idx, rb, rt), ref_idx), "selection"
+    rdq, rdk, rkl = oracle_kl(w, inp, rb, rt, ref_idx)
+    close("rand dqI", dqI.cpu().reshape(B * T, G, -1), rdq)
+    close("rand dkI", dkI.cpu(), rdk[:, :N])
+    close_kl("rand", kl.permute(0, 2, 1).reshape(B * T, G).cpu(), rkl)
