@@ -205,25 +205,28 @@ index_tile_kernel(TileArgs a) {
   };
 
   uint4 pf[PF];
-  // Branch-free: keys past N re-read key N-1 and are zeroed, so that every
-  // iteration issues the same number of loads and the compiler's wait
-  // counting does not fall back to waiting for the whole prefetch.
+  // Keys past N re-read key N-1 and are zeroed when stored.  The loads are
+  // issued on every iteration (a block already loaded when there is no next
+  // one) and nothing uses them before store_block: a use right after a load
+  // under a branch, such as the zeroing select, makes the compiler wait for
+  // the load at the branch's end, before the block's products.
   auto load_block = [&](int64_t kb) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int i = tid + j * NT;
       const int r = i / CPR, c = i % CPR;
       const int64_t key = kb * kBlock + r;
-      const uint4 v = ld16(kbase + (key < a.N ? key : a.N - 1) * ROWB + c * 16);
-      pf[j] = key < a.N ? v : make_uint4(0, 0, 0, 0);
+      pf[j] = ld16(kbase + (key < a.N ? key : a.N - 1) * ROWB + c * 16);
     }
   };
-  auto store_block = [&](int buf) {
+  auto store_block = [&](int buf, int64_t kb) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int i = tid + j * NT;
       const int r = i / CPR, c = i % CPR;
-      *reinterpret_cast<uint4*>(&kbuf[buf][F8 ? r * PITCH + c * 16 : swz(r, c)]) = pf[j];
+      const int64_t key = kb * kBlock + r;
+      *reinterpret_cast<uint4*>(&kbuf[buf][F8 ? r * PITCH + c * 16 : swz(r, c)]) =
+          key < a.N ? pf[j] : make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -231,7 +234,7 @@ index_tile_kernel(TileArgs a) {
   for (int j = 0; j < D; ++j) {
     if (j < nkb) {
       load_block(j);
-      store_block(j);
+      store_block(j, j);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // q^I fragments and blocks 0 .. D-1 have landed
@@ -239,7 +242,7 @@ index_tile_kernel(TileArgs a) {
 
   for (int64_t kb = 0; kb < nkb; ++kb) {
     const bool more = kb + D < nkb;
-    if (more) load_block(kb + D);
+    load_block(more ? kb + D : kb);
     const unsigned char* buf = kbuf[kb & (R - 1)];
     float m0 = -INFINITY, m1 = -INFINITY;
     const bool masked = WRITE_S && (kb == L);
@@ -360,7 +363,7 @@ index_tile_kernel(TileArgs a) {
       }
     }
 
-    if (more) store_block((kb + D) & (R - 1));
+    if (more) store_block((kb + D) & (R - 1), kb + D);
     if ((kb & (D - 1)) == D - 1 || kb + 1 == nkb) __syncthreads();
   }
 
