@@ -155,6 +155,10 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
   uint4 fq[2], fg[2];
   float fl[2], fD[2];
   int flim[2], fprow[2];
+  bool fvalid[2];
+  // fetch only issues loads (every lane, valid addresses; nothing uses them
+  // before stash: a use under a branch would make the compiler wait for the
+  // loads there, ahead of the pass's products)
   auto fetch = [&](int pass) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -166,20 +170,23 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
       const int64_t t = t0 + (e >> 6);
       const int64_t hq = static_cast<int64_t>(g) * HG + hh;
       const int64_t off = ((b * a.T + t) * a.Hq + hq) * kHeadDim + 8 * cc;
-      const uint4 x = ld16(a.q + off), y = ld16(a.dO + off);
-      fq[u] = valid ? x : make_uint4(0, 0, 0, 0);
-      fg[u] = valid ? y : make_uint4(0, 0, 0, 0);
-      fl[u] = INFINITY;
-      fD[u] = 0.f;
-      if (cc == 0 && valid) {
-        fl[u] = a.lse[(b * a.Hq + hq) * a.T + t] * kLog2e;
-        fD[u] = a.Dr[(b * a.T + t) * a.Hq + hq];
-      }
+      fq[u] = ld16(a.q + off);
+      fg[u] = ld16(a.dO + off);
+      fl[u] = a.lse[(b * a.Hq + hq) * a.T + t];
+      fD[u] = a.Dr[(b * a.T + t) * a.Hq + hq];
+      fvalid[u] = valid;
       flim[u] = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
       fprow[u] = valid ? (((e >> 6) - a.rl_base) * a.k + (e & 63)) * HG + hh : a.sink + hh;
     }
   };
   auto stash = [&](int pass) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!fvalid[u]) {
+        fq[u] = make_uint4(0, 0, 0, 0);
+        fg[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
     const int r0 = 2 * rp;
     *reinterpret_cast<uint4*>(&qs[r0 * kBP + 16 * cc]) = fq[0];
     *reinterpret_cast<uint4*>(&qs[(r0 + 1) * kBP + 16 * cc]) = fq[1];
@@ -202,8 +209,8 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
     if (cc == 0) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        r_l2[r0 + u] = fl[u];
-        r_D[r0 + u] = fD[u];
+        r_l2[r0 + u] = fvalid[u] ? fl[u] * kLog2e : INFINITY;
+        r_D[r0 + u] = fvalid[u] ? fD[u] : 0.f;
         r_lim[r0 + u] = flim[u];
         r_prow[pass & 1][r0 + u] = fprow[u];
       }
@@ -241,7 +248,7 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
   const int npass = (rows + 31) / 32;
   for (int pass = 0; pass < npass; ++pass) {
     const bool more = pass + 1 < npass;
-    if (more) fetch(pass + 1);
+    fetch(more ? pass + 1 : pass);
     f32x16 sacc = f32x16{}, pacc = f32x16{};
     f32x16 q0 = f32x16{}, q1 = f32x16{};
     {
