@@ -243,7 +243,66 @@ __global__ void __launch_bounds__(256, 1) index_kl_kernel(IkArgs a) {
   constexpr int HB = HG < 4 ? HG : 4;
   const int gq = tid >> 3, g8 = tid & 7;
   const int npass = (n + 31) / 32;
+  // A pass's gather, one thread's share: q^I of queries 2rp, 2rp + 1 (dims
+  // 8cc..8cc+7), their row data, and the first heads' q rows for the teacher.
+  // fetch(p) only issues loads (every lane, valid addresses) and runs during
+  // the previous pass; stash(p) masks and writes to LDS at the pass's start.
+  const int rp = tid & 15, cc = tid >> 4;
+  uint4 xq[2], qh[HB][2];
+  float fpx[2], fl2[2];
+  int flim[2], fprow[2];
+  bool fval[2];
+  auto fetch = [&](int p) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int qq = p * 32 + 2 * rp + u;
+      const bool valid = qq < n;
+      const int e = ents[valid ? qq : 0];
+      const int64_t t = t0 + (e >> 6);
+      xq[u] = ld16(a.qI + ((b * a.T + t) * a.G + g) * kHeadDim + 8 * cc);
+      fpx[u] = a.lpx[(b * a.G + g) * a.T + t];
+      fl2[u] = a.lse[(b * a.Hq + static_cast<int64_t>(g) * HG + (cc < HG ? cc : HG - 1)) * a.T + t];
+      fval[u] = valid;
+      flim[u] = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
+      fprow[u] = valid ? ((e >> 6) - a.rl_base) * a.k + (e & 63) : a.sink;
+    }
+    const int ge = ents[p * 32 + gq < n ? p * 32 + gq : 0];
+    const u16* qb = a.q + ((b * a.T + t0 + (ge >> 6)) * a.Hq + static_cast<int64_t>(g) * HG) *
+                              kHeadDim + 16 * g8;
+#pragma unroll
+    for (int j = 0; j < HB; ++j) {
+      qh[j][0] = ld16(qb + j * kHeadDim);
+      qh[j][1] = ld16(qb + j * kHeadDim + 8);
+    }
+  };
+  auto stash = [&]() {
+    const uint4 x0 = fval[0] ? xq[0] : make_uint4(0, 0, 0, 0);
+    const uint4 x1 = fval[1] ? xq[1] : make_uint4(0, 0, 0, 0);
+    const int r0 = 2 * rp;
+    *reinterpret_cast<uint4*>(&qis[r0 * kP + 16 * cc]) = x0;
+    *reinterpret_cast<uint4*>(&qis[(r0 + 1) * kP + 16 * cc]) = x1;
+    const int P = tcol(r0);
+    const uint32_t w0[4] = {x0.x, x0.y, x0.z, x0.w};
+    const uint32_t w1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = 16 * (e & 1);
+      *reinterpret_cast<uint32_t*>(&qit[(8 * cc + e) * kTq + 2 * P]) =
+          ((w0[e >> 1] >> sh) & 0xffffu) | (((w1[e >> 1] >> sh) & 0xffffu) << 16);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (cc == 0) {
+        r_lim[r0 + u] = flim[u];
+        r_px[r0 + u] = fval[u] ? fpx[u] : INFINITY;
+        r_prow[r0 + u] = fprow[u];
+      }
+      if (cc < HG) r_l2[cc][r0 + u] = fval[u] ? fl2[u] * kLog2e : INFINITY;
+    }
+  };
+  fetch(0);
   for (int pass = 0; pass < npass; ++pass) {
+    const bool more = pass + 1 < npass;
     const bool gvalid = pass * 32 + gq < n;
     const u16* gqb;
     {
@@ -251,50 +310,7 @@ __global__ void __launch_bounds__(256, 1) index_kl_kernel(IkArgs a) {
       gqb = a.q + ((b * a.T + t0 + (ge >> 6)) * a.Hq + static_cast<int64_t>(g) * HG) * kHeadDim +
             16 * g8;
     }
-    uint4 qh[HB][2];
-#pragma unroll
-    for (int j = 0; j < HB; ++j) {
-      qh[j][0] = ld16(gqb + j * kHeadDim);
-      qh[j][1] = ld16(gqb + j * kHeadDim + 8);
-    }
-    // gather: thread -> query pair rp (queries 2rp, 2rp + 1), dims 8cc..8cc+7
-    {
-      const int rp = tid & 15, cc = tid >> 4;
-      uint4 x[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int qq = pass * 32 + 2 * rp + u;
-        const bool valid = qq < n;
-        const int e = ents[valid ? qq : 0];
-        const int64_t t = t0 + (e >> 6);
-        const uint4 y = ld16(a.qI + ((b * a.T + t) * a.G + g) * kHeadDim + 8 * cc);
-        x[u] = valid ? y : make_uint4(0, 0, 0, 0);
-        if (cc == 0) {
-          const int r = 2 * rp + u;
-          r_lim[r] = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
-          r_px[r] = valid ? a.lpx[(b * a.G + g) * a.T + t] : INFINITY;
-          r_prow[r] = valid ? ((e >> 6) - a.rl_base) * a.k + (e & 63) : a.sink;
-        }
-        if (cc < HG) {
-          const int r = 2 * rp + u;
-          r_l2[cc][r] = valid ? a.lse[(b * a.Hq + static_cast<int64_t>(g) * HG + cc) * a.T + t] *
-                                    kLog2e
-                              : INFINITY;
-        }
-      }
-      const int r0 = 2 * rp;
-      *reinterpret_cast<uint4*>(&qis[r0 * kP + 16 * cc]) = x[0];
-      *reinterpret_cast<uint4*>(&qis[(r0 + 1) * kP + 16 * cc]) = x[1];
-      const int P = tcol(r0);
-      const uint32_t w0[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
-      const uint32_t w1[4] = {x[1].x, x[1].y, x[1].z, x[1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = 16 * (e & 1);
-        *reinterpret_cast<uint32_t*>(&qit[(8 * cc + e) * kTq + 2 * P]) =
-            ((w0[e >> 1] >> sh) & 0xffffu) | (((w1[e >> 1] >> sh) & 0xffffu) << 16);
-      }
-    }
+    stash();
     __syncthreads();
 
     // index scores s: queries on M (A = q^I rows), this wave's keys on N
@@ -352,6 +368,7 @@ __global__ void __launch_bounds__(256, 1) index_kl_kernel(IkArgs a) {
         }
       }
     }
+    fetch(more ? pass + 1 : pass);  // lands during this pass's dz, dk^I and dq^I
     // dz = p_x - p_t, the loss terms p_t (log p_t - log p_x); dz to LDS
     const float c2 = kScale * kLog2e;
     float dz[16];
