@@ -627,12 +627,13 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
   // once (slots past nval re-read slot 0 and get weight 0) so that every lane
   // has them in flight.
   for (int s0 = 0; s0 < (WIDE ? nval : 1); s0 += 16) {
+    // every load is issued before any is used (a use right after a load
+    // makes the compiler wait for it there)
     float2 ml[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       const int ss = s0 + s < nval ? s0 + s : 0;
       ml[s] = a.lpart[(pbase + ss) * HG + hh];
-      if (!WIDE && s < nval) mx = fmaxf(mx, ml[s].x);
     }
     uint4 raw[16][PPL];
 #pragma unroll
@@ -644,6 +645,12 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
         const int pc = li * PPL + q, j = pc >> 1, hf = pc & 1;
         raw[s][q] = ld16_once(src + j * 16 * HG + (hf * HG + hh) * 8);
       }
+    }
+    sched_fence();  // keep the uses below the loads
+    if constexpr (!WIDE) {
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (s < nval) mx = fmaxf(mx, ml[s].x);
     }
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
