@@ -352,7 +352,6 @@ int msa_sparse_attn_backward(const msa_dims_t* d, const void* q, const void* K, 
                              float* dq, float* dK, float* dV, void* ws, size_t ws_bytes,
                              void* stream) {
   MSA_TRY(check_dims(d));
-  MSA_TRY(need_bk128(d, "msa_sparse_attn_backward"));
   MSA_TRY(check_ptr(q, "q"));
   MSA_TRY(check_ptr(K, "K"));
   MSA_TRY(check_ptr(V, "V"));
@@ -385,7 +384,7 @@ int msa_sparse_attn_backward(const msa_dims_t* d, const void* q, const void* K, 
   msa::attn_workspace_carve(static_cast<char*>(ws) + rowdot_bytes(d), hi, stage_rows_for(d, hi),
                             d->N, d->G, d->Hq / d->G, d->k, d->Bk, false, &w);
   const hipError_t e = msa::launch_attn_backward(q, K, V, idx, O, lse, dO, dq, dK, dV, Dr, d->B,
-                                                 d->T, d->N, d->Hq, d->G, d->k, w,
+                                                 d->T, d->N, d->Hq, d->G, d->k, d->Bk, w,
                                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_backward");
   return MSA_OK;
@@ -395,7 +394,6 @@ int msa_index_kl_backward(const msa_dims_t* d, const void* qI, const void* kI, c
                           const void* K, const int32_t* idx, const float* lse, float* dqI,
                           float* dkI, float* kl, void* ws, size_t ws_bytes, void* stream) {
   MSA_TRY(check_dims(d));
-  MSA_TRY(need_bk128(d, "msa_index_kl_backward"));
   MSA_TRY(check_ptr(qI, "qI"));
   MSA_TRY(check_ptr(kI, "kI"));
   MSA_TRY(check_ptr(q, "q"));
@@ -428,7 +426,7 @@ int msa_index_kl_backward(const msa_dims_t* d, const void* qI, const void* kI, c
   msa::attn_workspace_carve(static_cast<char*>(ws) + lpx_bytes(d), hi, stage_rows_for(d, hi),
                             d->N, d->G, d->Hq / d->G, d->k, d->Bk, false, &w);
   const hipError_t e = msa::launch_index_kl_backward(qI, kI, q, K, idx, lse, dqI, dkI, kl, lpx,
-                                                     d->B, d->T, d->N, d->Hq, d->G, d->k, w,
+                                                     d->B, d->T, d->N, d->Hq, d->G, d->k, d->Bk, w,
                                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_index_kl_backward");
   return MSA_OK;

@@ -56,7 +56,7 @@ struct BwdArgs {
   float* dK;              // [B, G, N, 128]
   float* dV;
   int64_t T, N, r0;       // r0: global row (b*T + t) of window row 0
-  int32_t Hq, G, k;
+  int32_t Hq, G, k, Bk;
   int32_t rl_base;        // first window row of this stage
   int32_t sink;           // spare partial row (hg rows) for rows past a chunk's end
 };
@@ -93,8 +93,9 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
 
-  const int64_t key0 = blk * 128;
-  const int nvalid = static_cast<int>(a.N - key0 < 128 ? a.N - key0 : 128);  // >= 1
+  const int64_t key0 = blk * a.Bk;
+  // the block's keys (>= 1); LDS rows past them are zero and masked
+  const int nvalid = static_cast<int>(a.N - key0 < a.Bk ? a.N - key0 : a.Bk);
   const u16* Kb = a.K + (bg * a.N + key0) * kHeadDim;
   const u16* Vb = a.V + (bg * a.N + key0) * kHeadDim;
 
@@ -175,7 +176,8 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
       fl[u] = a.lse[(b * a.Hq + hq) * a.T + t];
       fD[u] = a.Dr[(b * a.T + t) * a.Hq + hq];
       fvalid[u] = valid;
-      flim[u] = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
+      flim[u] = valid ? static_cast<int>(min(a.N - a.T + t - key0, static_cast<int64_t>(nvalid - 1)))
+                       : -1;  // last key of the block the row sees
       fprow[u] = valid ? (((e >> 6) - a.rl_base) * a.k + (e & 63)) * HG + hh : a.sink + hh;
     }
   };
@@ -330,7 +332,7 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t key = key0 + 32 * wave + 8 * (i >> 2) + 4 * half + (i & 3);
-    if (key < a.N) {
+    if (key < key0 + nvalid) {
       float* pk = a.dK + (bg * a.N + key) * kHeadDim + l32;
       float* pv = a.dV + (bg * a.N + key) * kHeadDim + l32;
 #pragma unroll
@@ -477,7 +479,7 @@ static unsigned nblocks_of(int64_t n, int per) {
 hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
                                 const int32_t* idx, const void* O, const float* lse,
                                 const void* dO, float* dq, float* dK, float* dV, float* Dr,
-                                int64_t B, int64_t T, int64_t N, int Hq, int G, int k,
+                                int64_t B, int64_t T, int64_t N, int Hq, int G, int k, int Bk,
                                 const AttnWorkspace& w, hipStream_t st) {
   const int hg = Hq / G;
   const int64_t n4 = B * G * N * kHeadDim / 4;
@@ -494,7 +496,7 @@ hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
     for (int64_t t0 = 0; t0 < T; t0 += w.window) {
       const int64_t W = (T - t0) < w.window ? (T - t0) : w.window;
       int32_t S = 0;
-      e = launch_invert_window(idx, b, T, t0, W, N, G, k, 128, w, &S, st);
+      e = launch_invert_window(idx, b, T, t0, W, N, G, k, Bk, w, &S, st);
       if (e != hipSuccess) return e;
       const int64_t r0 = b * T + t0;
       for (int g = 0; g < G; ++g) {
@@ -520,6 +522,7 @@ hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
           ba.Hq = Hq;
           ba.G = G;
           ba.k = k;
+          ba.Bk = Bk;
           ba.rl_base = rl_base;
           ba.sink = static_cast<int32_t>(w.sink);
           DqArgs da;

@@ -55,7 +55,7 @@ struct IkArgs {
   u16* dqpart;            // per (row, slot): 128 bf16
   float* dkI;             // [B, N, 128]
   int64_t T, N, r0;
-  int32_t Hq, G, k, rl_base, sink;
+  int32_t Hq, G, k, Bk, rl_base, sink;
 };
 
 // Proxy lse partials.  One workgroup per chunk; wave w takes queries
@@ -78,8 +78,9 @@ __global__ void __launch_bounds__(256) index_px_kernel(IkArgs a) {
   const int64_t b = bg >> __builtin_ctz(a.G);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int64_t key0 = blk * 128;
-  const int nvalid = static_cast<int>(a.N - key0 < 128 ? a.N - key0 : 128);
+  const int64_t key0 = blk * a.Bk;
+  // the block's keys (>= 1); LDS rows past them are zero and masked
+  const int nvalid = static_cast<int>(a.N - key0 < a.Bk ? a.N - key0 : a.Bk);
   const u16* kb = a.kI + (b * a.N + key0) * kHeadDim;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -93,7 +94,8 @@ __global__ void __launch_bounds__(256) index_px_kernel(IkArgs a) {
   const bool valid = qi < n;
   const int e = a.entries[ch.y + (valid ? qi : 0)];
   const int64_t t = (a.r0 - b * a.T) + (e >> 6);
-  const int lim = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
+  const int lim =
+      valid ? static_cast<int>(min(a.N - a.T + t - key0, static_cast<int64_t>(nvalid - 1))) : -1;
   const u16* qr = a.qI + ((b * a.T + t) * a.G + g) * kHeadDim + 8 * half;
   bf16x8 qf[8];
 #pragma unroll
@@ -195,8 +197,9 @@ __global__ void __launch_bounds__(256, 1) index_kl_kernel(IkArgs a) {
   const int64_t b = bg >> __builtin_ctz(a.G);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int64_t key0 = blk * 128;
-  const int nvalid = static_cast<int>(a.N - key0 < 128 ? a.N - key0 : 128);
+  const int64_t key0 = blk * a.Bk;
+  // the block's keys (>= 1); LDS rows past them are zero and masked
+  const int nvalid = static_cast<int>(a.N - key0 < a.Bk ? a.N - key0 : a.Bk);
 
   // k^I (row-major and transposed) and K of the block; keys past N are zero
   const u16* kib = a.kI + (b * a.N + key0) * kHeadDim;
@@ -263,7 +266,8 @@ __global__ void __launch_bounds__(256, 1) index_kl_kernel(IkArgs a) {
       fpx[u] = a.lpx[(b * a.G + g) * a.T + t];
       fl2[u] = a.lse[(b * a.Hq + static_cast<int64_t>(g) * HG + (cc < HG ? cc : HG - 1)) * a.T + t];
       fval[u] = valid;
-      flim[u] = valid ? static_cast<int>(a.N - a.T + t - key0) : -1;
+      flim[u] = valid ? static_cast<int>(min(a.N - a.T + t - key0, static_cast<int64_t>(nvalid - 1)))
+                       : -1;  // last key of the block the row sees
       fprow[u] = valid ? ((e >> 6) - a.rl_base) * a.k + (e & 63) : a.sink;
     }
     const int ge = ents[p * 32 + gq < n ? p * 32 + gq : 0];
@@ -439,7 +443,7 @@ __global__ void __launch_bounds__(256, 1) index_kl_kernel(IkArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t key = key0 + 32 * wave + 8 * (i >> 2) + 4 * half + (i & 3);
-    if (key < a.N) {
+    if (key < key0 + nvalid) {
       float* pk = a.dkI + (b * a.N + key) * kHeadDim + l32;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) unsafeAtomicAdd(pk + 32 * dt, dk[dt][i]);
@@ -492,7 +496,7 @@ hipError_t launch_kl(int hg, const IkArgs& ia, int64_t grid, hipStream_t st) {
 hipError_t launch_index_kl_backward(const void* qI, const void* kI, const void* q, const void* K,
                                     const int32_t* idx, const float* lse, float* dqI, float* dkI,
                                     float* kl, float* lpx, int64_t B, int64_t T, int64_t N,
-                                    int Hq, int G, int k, const AttnWorkspace& w,
+                                    int Hq, int G, int k, int Bk, const AttnWorkspace& w,
                                     hipStream_t st) {
   const int hg = Hq / G;
   const int64_t n4 = B * N * kHeadDim / 4;
@@ -504,7 +508,7 @@ hipError_t launch_index_kl_backward(const void* qI, const void* kI, const void* 
     for (int64_t t0 = 0; t0 < T; t0 += w.window) {
       const int64_t W = (T - t0) < w.window ? (T - t0) : w.window;
       int32_t S = 0;
-      e = launch_invert_window(idx, b, T, t0, W, N, G, k, 128, w, &S, st);
+      e = launch_invert_window(idx, b, T, t0, W, N, G, k, Bk, w, &S, st);
       if (e != hipSuccess) return e;
       const int64_t r0 = b * T + t0;
       for (int g = 0; g < G; ++g) {
@@ -531,6 +535,7 @@ hipError_t launch_index_kl_backward(const void* qI, const void* kI, const void* 
           ia.Hq = Hq;
           ia.G = G;
           ia.k = k;
+          ia.Bk = Bk;
           ia.rl_base = rl_base;
           ia.sink = static_cast<int32_t>(w.sink);
           const int64_t grid = (w.max_chunks + 7) & ~static_cast<int64_t>(7);

@@ -72,11 +72,11 @@ hipError_t launch_invert_window(const int32_t* idx, int64_t b, int64_t T, int64_
                                 int32_t* nsub, hipStream_t st);
 // Stage 4 backward: dq [B, T, Hq, 128], dK, dV [B, G, N, 128] (fp32, all
 // overwritten) from q, O, dO [B, T, Hq, 128], K, V, idx and the forward's lse
-// [B, Hq, T]; Dr: B*T*Hq floats of scratch.  Bk = 128.
+// [B, Hq, T]; Dr: B*T*Hq floats of scratch.  Blocks of Bk keys (32, 64, 128).
 hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
                                 const int32_t* idx, const void* O, const float* lse,
                                 const void* dO, float* dq, float* dK, float* dV, float* Dr,
-                                int64_t B, int64_t T, int64_t N, int Hq, int G, int k,
+                                int64_t B, int64_t T, int64_t N, int Hq, int G, int k, int Bk,
                                 const AttnWorkspace& w, hipStream_t st);
 // Sum in slot order of per-(row, slot) bf16 partials (the backward's layout)
 // for the rows of one stage and group: out [.., outer, 128] fp32 at
@@ -86,11 +86,11 @@ hipError_t launch_dq_combine(const int32_t* idx, const uint16_t* part, float* ou
                              int group, hipStream_t st);
 // Index-branch KL alignment backward: dqI [B, T, G, 128], dkI [B, N, 128]
 // (fp32, overwritten), kl [B, G, T] (nullable) from q^I, k^I, q, K, idx and
-// the main lse [B, Hq, T]; lpx: B*G*T floats of scratch.  Bk = 128.
+// the main lse [B, Hq, T]; lpx: B*G*T floats of scratch.  Blocks of Bk keys.
 hipError_t launch_index_kl_backward(const void* qI, const void* kI, const void* q, const void* K,
                                     const int32_t* idx, const float* lse, float* dqI, float* dkI,
                                     float* kl, float* lpx, int64_t B, int64_t T, int64_t N,
-                                    int Hq, int G, int k, const AttnWorkspace& w,
+                                    int Hq, int G, int k, int Bk, const AttnWorkspace& w,
                                     hipStream_t st);
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse,

@@ -207,8 +207,8 @@ def sparse_attn_prefill(q, K, V, idx, return_lse=False, out=None, workspace=None
     return (O, lse) if return_lse else O
 
 
-def sparse_attn_backward(q, K, V, idx, O, lse, dO, out=None, workspace=None):
-    """Stage 4 gradients (Bk = 128).  q, O, dO [B,T,Hq,128] bf16, K/V
+def sparse_attn_backward(q, K, V, idx, O, lse, dO, out=None, workspace=None, Bk=128):
+    """Stage 4 gradients (blocks of Bk keys).  q, O, dO [B,T,Hq,128] bf16, K/V
     [B,G,N,128] bf16, idx [B,G,T,k], lse [B,Hq,T] fp32 from the prefill ->
     (dq [B,T,Hq,128], dK, dV [B,G,N,128]), all fp32.  out: optional
     (dq, dK, dV) tensors to write."""
@@ -222,7 +222,7 @@ def sparse_attn_backward(q, K, V, idx, O, lse, dO, out=None, workspace=None):
     _need(O, "O", torch.bfloat16, q.shape)
     _need(dO, "dO", torch.bfloat16, q.shape)
     _need(lse, "lse", torch.float32, (B, Hq, T))
-    d = dims(B, T, N, Hq, G, k, d_h=dh)
+    d = dims(B, T, N, Hq, G, k, d_h=dh, Bk=Bk)
     if out is None:
         out = (torch.empty(q.shape, dtype=torch.float32, device=q.device),
                torch.empty(K.shape, dtype=torch.float32, device=q.device),
@@ -239,8 +239,9 @@ def sparse_attn_backward(q, K, V, idx, O, lse, dO, out=None, workspace=None):
     return dq, dK, dV
 
 
-def index_kl_backward(qI, kI, q, K, idx, lse, return_loss=False, out=None, workspace=None):
-    """Index-branch KL alignment gradients (Bk = 128).  qI [B,T,G,128],
+def index_kl_backward(qI, kI, q, K, idx, lse, return_loss=False, out=None, workspace=None,
+                      Bk=128):
+    """Index-branch KL alignment gradients (blocks of Bk keys).  qI [B,T,G,128],
     kI [B,N,128], q [B,T,Hq,128], K [B,G,N,128] bf16, idx [B,G,T,k], lse
     [B,Hq,T] fp32 (the prefill's) -> (dqI [B,T,G,128], dkI [B,N,128]) fp32,
     plus the loss kl [B,G,T] when return_loss."""
@@ -254,7 +255,7 @@ def index_kl_backward(qI, kI, q, K, idx, lse, return_loss=False, out=None, works
     _need(K, "K", torch.bfloat16, (B, G, N, q.shape[3]))
     _need(idx, "idx", torch.int32, (B, G, T, k))
     _need(lse, "lse", torch.float32, (B, Hq, T))
-    d = dims(B, T, N, Hq, G, k, d_h=q.shape[3], d_I=dI)
+    d = dims(B, T, N, Hq, G, k, d_h=q.shape[3], d_I=dI, Bk=Bk)
     if out is None:
         out = (torch.empty(qI.shape, dtype=torch.float32, device=qI.device),
                torch.empty(kI.shape, dtype=torch.float32, device=qI.device))

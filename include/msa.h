@@ -188,8 +188,9 @@ int msa_sparse_attn_prefill(const msa_dims_t *dims, const void *q,
  *   ws / ws_bytes  >= msa_workspace_bytes(MSA_OP_ATTN_BACKWARD) for the
  *                  default query window; a smaller one (down to one row per
  *                  window plus B*T*Hq floats) runs more windows.
- * Needs Bk = 128.  dK and dV are accumulated with fp32 atomic adds, so their
- * last bits can differ between runs; dq is summed in slot order.
+ * Any supported block size (Bk = 32, 64, 128).  dK and dV are accumulated with
+ * fp32 atomic adds, so their last bits can differ between runs; dq is summed
+ * in slot order.
  */
 int msa_sparse_attn_backward(const msa_dims_t *dims, const void *q, const void *K,
                              const void *V, const int32_t *idx, const void *O,
@@ -216,8 +217,9 @@ int msa_sparse_attn_backward(const msa_dims_t *dims, const void *q, const void *
  *   ws / ws_bytes  >= msa_workspace_bytes(MSA_OP_INDEX_KL_BACKWARD) for the
  *                  default window; smaller (down to one row per window plus
  *                  B*G*T floats) runs more windows.
- * Needs Bk = 128.  dkI is accumulated with fp32 atomic adds; dqI and kl are
- * summed in slot order.  Scaling by a loss weight is the caller's.
+ * Any supported block size (Bk = 32, 64, 128).  dkI is accumulated with fp32
+ * atomic adds; dqI and kl are summed in slot order.  Scaling by a loss weight
+ * is the caller's.
  */
 int msa_index_kl_backward(const msa_dims_t *dims, const void *qI, const void *kI,
                           const void *q, const void *K, const int32_t *idx, const float *lse,

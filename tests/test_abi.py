@@ -173,8 +173,8 @@ def test_block_size_checks():
 
 def test_backward_argument_checks():
     """The backward validates before any HIP call: every pointer (lse is
-    required), Bk = 128, the workspace floor; its workspace is the prefill's
-    plus one float per (row, head)."""
+    required), the block size, the workspace floor; its workspace is the
+    prefill's plus one float per (row, head)."""
     L = ops.lib()
     d = _good()
     need = L.msa_workspace_bytes(ops.OP_ATTN_BACKWARD, ctypes.byref(d))
@@ -189,14 +189,16 @@ def test_backward_argument_checks():
         assert b"aligned" in L.msa_last_error()
     assert L.msa_sparse_attn_backward(ctypes.byref(d), *args, None, need, None) == -1
     assert L.msa_sparse_attn_backward(ctypes.byref(d), *args, FAKE, 64, None) == -3
-    d64 = _good(Bk=64, k=4)
-    assert L.msa_sparse_attn_backward(ctypes.byref(d64), *args, FAKE, 1 << 40, None) == -2
-    assert b"Bk" in L.msa_last_error()
+    # every supported block size has a workspace size; unsupported ones are refused
+    for bk, k in ((64, 4), (32, 8)):
+        assert L.msa_workspace_bytes(ops.OP_ATTN_BACKWARD, ctypes.byref(_good(Bk=bk, k=k))) > 0
+    assert L.msa_sparse_attn_backward(ctypes.byref(_good(Bk=96)), *args, FAKE, 1 << 40,
+                                      None) == -2
 
 
 def test_index_kl_argument_checks():
     """Validation before any HIP call: every required pointer (kl may be
-    NULL), Bk = 128, the workspace floor."""
+    NULL), the block size, the workspace floor."""
     L = ops.lib()
     d = _good()
     need = L.msa_workspace_bytes(ops.OP_INDEX_KL_BACKWARD, ctypes.byref(d))
@@ -213,5 +215,6 @@ def test_index_kl_argument_checks():
     assert L.msa_index_kl_backward(ctypes.byref(d), *bad, FAKE, need, None) == -1
     assert L.msa_index_kl_backward(ctypes.byref(d), *args, None, need, None) == -1
     assert L.msa_index_kl_backward(ctypes.byref(d), *args, FAKE, 64, None) == -3
-    d64 = _good(Bk=64, k=4)
-    assert L.msa_index_kl_backward(ctypes.byref(d64), *args, FAKE, 1 << 40, None) == -2
+    for bk, k in ((64, 4), (32, 8)):
+        assert L.msa_workspace_bytes(ops.OP_INDEX_KL_BACKWARD, ctypes.byref(_good(Bk=bk, k=k))) > 0
+    assert L.msa_index_kl_backward(ctypes.byref(_good(Bk=96)), *args, FAKE, 1 << 40, None) == -2

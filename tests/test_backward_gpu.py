@@ -65,9 +65,9 @@ def close(tag, got, ref):
 
 
 def run_gpu(w, inp, dO):
-    idx = ops.select_blocks(inp["qI"], inp["kI"], w.k)
-    O, lse = ops.sparse_attn_prefill(inp["q"], inp["K"], inp["V"], idx, return_lse=True)
-    dq, dK, dV = ops.sparse_attn_backward(inp["q"], inp["K"], inp["V"], idx, O, lse, dO)
+    idx = ops.select_blocks(inp["qI"], inp["kI"], w.k, Bk=w.Bk)
+    O, lse = ops.sparse_attn_prefill(inp["q"], inp["K"], inp["V"], idx, return_lse=True, Bk=w.Bk)
+    dq, dK, dV = ops.sparse_attn_backward(inp["q"], inp["K"], inp["V"], idx, O, lse, dO, Bk=w.Bk)
     torch.cuda.synchronize()
     return idx, dq, dK, dV
 
@@ -220,19 +220,20 @@ def _random_cases(n, seed):
         hg = int(g.choice([1, 2, 4, 8, 16]))
         if G * hg > 64:
             continue
-        k = int(g.integers(1, 17))
+        Bk = int(g.choice([32, 64, 128]))
+        k = int(g.integers(1, 2048 // Bk + 1))
         N = int(g.integers(1, 2600))
         T = int(g.choice([N, int(g.integers(1, N + 1))]))
         B = int(g.integers(1, 4))
-        cases.append((B, T, N, G * hg, G, k))
+        cases.append((B, T, N, G * hg, G, k, Bk))
     return cases
 
 
-@pytest.mark.parametrize("B,T,N,Hq,G,k", _random_cases(10, 77))
-def test_backward_random_shapes(B, T, N, Hq, G, k):
-    """Seeded random shapes (chunked rows, group layouts, k): every row's dq
-    and every key's dK / dV against the oracle."""
-    w = Workload("rand", B=B, T=T, N=N, Hq=Hq, G=G, k=k, seed=N * 3 + T)
+@pytest.mark.parametrize("B,T,N,Hq,G,k,Bk", _random_cases(12, 77))
+def test_backward_random_shapes(B, T, N, Hq, G, k, Bk):
+    """Seeded random shapes (block sizes, chunked rows, group layouts, k):
+    every row's dq and every key's dK / dV against the oracle."""
+    w = Workload("rand", B=B, T=T, N=N, Hq=Hq, G=G, k=k, Bk=Bk, seed=N * 3 + T)
     say("case", w)
     inp = make_inputs(w, device="cuda")
     dO = make_grad_output(w, device="cuda")
@@ -245,3 +246,32 @@ def test_backward_random_shapes(B, T, N, Hq, G, k):
     close("rand dq", dq.cpu().reshape(B * T, Hq, -1), rdq)
     close("rand dK", dK.cpu(), rdK[:, :, :N])
     close("rand dV", dV.cpu(), rdV[:, :, :N])
+
+
+BK_CASES = [
+    # name, B, T, N, Hq, G, k, Bk  (k * Bk <= 2048)
+    ("bk64_k32", 1, 2100, 2100, 64, 8, 32, 64),
+    ("bk32_k64", 1, 2500, 2500, 64, 8, 64, 32),
+    ("bk64_chunked", 2, 300, 900, 32, 8, 20, 64),
+    ("bk32_g16", 1, 700, 700, 32, 16, 12, 32),
+    ("bk32_tiny", 1, 5, 5, 8, 2, 4, 32),
+]
+
+
+@pytest.mark.parametrize("name,B,T,N,Hq,G,k,Bk", BK_CASES, ids=[c[0] for c in BK_CASES])
+def test_backward_block_sizes(name, B, T, N, Hq, G, k, Bk):
+    """Blocks of 64 and 32 keys: every row's dq and every key's dK / dV."""
+    w = Workload(name, B=B, T=T, N=N, Hq=Hq, G=G, k=k, Bk=Bk, seed=91 + N)
+    say("case", w)
+    inp = make_inputs(w, device="cuda")
+    dO = make_grad_output(w, device="cuda")
+    idx, dq, dK, dV = run_gpu(w, inp, dO)
+    rb = np.repeat(np.arange(B), T)
+    rt = np.tile(np.arange(T), B)
+    ref_idx = oracle_selection(w, inp, rb, rt)
+    assert np.array_equal(gpu_rows(idx, rb, rt), ref_idx), "selection"
+    rdq, rdK, rdV = oracle_backward(w, inp, dO, rb, rt, ref_idx)
+    close(name + " dq", dq.cpu().reshape(B * T, Hq, -1), rdq)
+    close(name + " dK", dK.cpu(), rdK[:, :, :N])
+    close(name + " dV", dV.cpu(), rdV[:, :, :N])
+    check_sums(w, inp, dO, dK, dV)

@@ -67,10 +67,10 @@ def close_kl(tag, got, ref):
 
 
 def run_gpu(w, inp):
-    idx = ops.select_blocks(inp["qI"], inp["kI"], w.k)
-    _, lse = ops.sparse_attn_prefill(inp["q"], inp["K"], inp["V"], idx, return_lse=True)
+    idx = ops.select_blocks(inp["qI"], inp["kI"], w.k, Bk=w.Bk)
+    _, lse = ops.sparse_attn_prefill(inp["q"], inp["K"], inp["V"], idx, return_lse=True, Bk=w.Bk)
     dqI, dkI, kl = ops.index_kl_backward(inp["qI"], inp["kI"], inp["q"], inp["K"], idx, lse,
-                                         return_loss=True)
+                                         return_loss=True, Bk=w.Bk)
     torch.cuda.synchronize()
     return idx, dqI, dkI, kl
 
@@ -206,19 +206,20 @@ def _random_cases(n, seed):
         hg = int(g.choice([1, 2, 4, 8, 16]))
         if G * hg > 64:
             continue
-        k = int(g.integers(1, 17))
+        Bk = int(g.choice([32, 64, 128]))
+        k = int(g.integers(1, 2048 // Bk + 1))
         N = int(g.integers(1, 2600))
         T = int(g.choice([N, int(g.integers(1, N + 1))]))
         B = int(g.integers(1, 4))
-        cases.append((B, T, N, G * hg, G, k))
+        cases.append((B, T, N, G * hg, G, k, Bk))
     return cases
 
 
-@pytest.mark.parametrize("B,T,N,Hq,G,k", _random_cases(10, 78))
-def test_index_kl_random_shapes(B, T, N, Hq, G, k):
-    """Seeded random shapes: every row's dq^I and loss and every key's dk^I
-    against the oracle."""
-    w = Workload("rand", B=B, T=T, N=N, Hq=Hq, G=G, k=k, seed=N * 5 + T)
+@pytest.mark.parametrize("B,T,N,Hq,G,k,Bk", _random_cases(12, 78))
+def test_index_kl_random_shapes(B, T, N, Hq, G, k, Bk):
+    """Seeded random shapes (block sizes too): every row's dq^I and loss and
+    every key's dk^I against the oracle."""
+    w = Workload("rand", B=B, T=T, N=N, Hq=Hq, G=G, k=k, Bk=Bk, seed=N * 5 + T)
     say("case", w)
     inp = make_inputs(w, device="cuda")
     idx, dqI, dkI, kl = run_gpu(w, inp)
@@ -230,3 +231,30 @@ def test_index_kl_random_shapes(B, T, N, Hq, G, k):
     close("rand dqI", dqI.cpu().reshape(B * T, G, -1), rdq)
     close("rand dkI", dkI.cpu(), rdk[:, :N])
     close_kl("rand", kl.permute(0, 2, 1).reshape(B * T, G).cpu(), rkl)
+
+
+BK_CASES = [
+    ("bk64_k32", 1, 2100, 2100, 64, 8, 32, 64),
+    ("bk32_k64", 1, 2500, 2500, 64, 8, 64, 32),
+    ("bk64_chunked", 2, 300, 900, 32, 8, 20, 64),
+    ("bk32_g16", 1, 700, 700, 32, 16, 12, 32),
+    ("bk32_tiny", 1, 5, 5, 8, 2, 4, 32),
+]
+
+
+@pytest.mark.parametrize("name,B,T,N,Hq,G,k,Bk", BK_CASES, ids=[c[0] for c in BK_CASES])
+def test_index_kl_block_sizes(name, B, T, N, Hq, G, k, Bk):
+    """Blocks of 64 and 32 keys: every row's dq^I and loss, every key's dk^I."""
+    w = Workload(name, B=B, T=T, N=N, Hq=Hq, G=G, k=k, Bk=Bk, seed=93 + N)
+    say("case", w)
+    inp = make_inputs(w, device="cuda")
+    idx, dqI, dkI, kl = run_gpu(w, inp)
+    rb = np.repeat(np.arange(B), T)
+    rt = np.tile(np.arange(T), B)
+    ref_idx = oracle_selection(w, inp, rb, rt)
+    assert np.array_equal(gpu_rows(idx, rb, rt), ref_idx), "selection"
+    rdq, rdk, rkl = oracle_kl(w, inp, rb, rt, ref_idx)
+    close(name + " dqI", dqI.cpu().reshape(B * T, G, -1), rdq)
+    close(name + " dkI", dkI.cpu(), rdk[:, :N])
+    close_kl(name, kl.permute(0, 2, 1).reshape(B * T, G).cpu(), rkl)
+    check_sum(w, inp, dkI)
