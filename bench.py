@@ -129,30 +129,30 @@ def backward_leg(args, pre):
     from msa_inputs import make_grad_output
     w, inp, idx = pre["w"], pre["inp"], pre["idx"]
     q, K, V = inp["q"], inp["K"], inp["V"]
-    O, lse = ops.sparse_attn_prefill(q, K, V, idx, return_lse=True)
+    O, lse = ops.sparse_attn_prefill(q, K, V, idx, return_lse=True, Bk=w.Bk)
     dO = make_grad_output(w, device="cuda")
     outs = (torch.empty(q.shape, dtype=torch.float32, device="cuda"),
             torch.empty(K.shape, dtype=torch.float32, device="cuda"),
             torch.empty(K.shape, dtype=torch.float32, device="cuda"))
-    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k)
+    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k, Bk=w.Bk)
     ws = torch.empty(ops.workspace_bytes(ops.OP_ATTN_BACKWARD, d), dtype=torch.uint8,
                      device="cuda")
     for _ in range(max(1, args.warmup)):
-        ops.sparse_attn_backward(q, K, V, idx, O, lse, dO, out=outs, workspace=ws)
+        ops.sparse_attn_backward(q, K, V, idx, O, lse, dO, out=outs, workspace=ws, Bk=w.Bk)
     torch.cuda.synchronize()
     events = [(ev(), ev()) for _ in range(args.steps)]
     for e0, e1 in events:
         e0.record()
-        ops.sparse_attn_backward(q, K, V, idx, O, lse, dO, out=outs, workspace=ws)
+        ops.sparse_attn_backward(q, K, V, idx, O, lse, dO, out=outs, workspace=ws, Bk=w.Bk)
         e1.record()
     torch.cuda.synchronize()
     ms = np.array([e0.elapsed_time(e1) for e0, e1 in events])
     fl = acc.backward_flops(w.N, w.T, w.Hq, w.d_h, w.Bk, w.k, w.B)
     tf = fl / (ms.mean() * 1e-3) / 1e12
     log("[bench] backward %.3f ms (%.1f TFLOP/s)" % (ms.mean(), tf))
-    return {"workload": w.name, "ms": float(ms.mean()), "ms_min": float(ms.min()),
-            "flops": fl, "TFLOPs": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
-            "outputs": "dq, dK, dV fp32"}
+    return {"workload": w.name, "Bk": w.Bk, "k": w.k, "ms": float(ms.mean()),
+            "ms_min": float(ms.min()), "flops": fl, "TFLOPs": tf,
+            "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, "outputs": "dq, dK, dV fp32"}
 
 
 def index_kl_leg(args, pre):
@@ -163,14 +163,14 @@ def index_kl_leg(args, pre):
     the gradient pass) and the two gradient products (2 d_I FLOP each per
     (row, group, support key))."""
     w, inp, idx = pre["w"], pre["inp"], pre["idx"]
-    _, lse = ops.sparse_attn_prefill(inp["q"], inp["K"], inp["V"], idx, return_lse=True)
+    _, lse = ops.sparse_attn_prefill(inp["q"], inp["K"], inp["V"], idx, return_lse=True, Bk=w.Bk)
     outs = (torch.empty(inp["qI"].shape, dtype=torch.float32, device="cuda"),
             torch.empty(inp["kI"].shape, dtype=torch.float32, device="cuda"))
-    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k)
+    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k, Bk=w.Bk)
     ws = torch.empty(ops.workspace_bytes(ops.OP_INDEX_KL_BACKWARD, d), dtype=torch.uint8,
                      device="cuda")
     call = lambda: ops.index_kl_backward(inp["qI"], inp["kI"], inp["q"], inp["K"], idx, lse,
-                                         out=outs, workspace=ws)
+                                         out=outs, workspace=ws, Bk=w.Bk)
     for _ in range(max(1, args.warmup)):
         call()
     torch.cuda.synchronize()
@@ -184,9 +184,9 @@ def index_kl_leg(args, pre):
     fl = acc.index_kl_flops(w.N, w.T, w.Hq, w.G, w.d_h, w.d_I, w.Bk, w.k, w.B)
     tf = fl / (ms.mean() * 1e-3) / 1e12
     log("[bench] index KL backward %.3f ms (%.1f TFLOP/s)" % (ms.mean(), tf))
-    return {"workload": w.name, "ms": float(ms.mean()), "ms_min": float(ms.min()), "flops": fl,
-            "TFLOPs": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
-            "outputs": "dqI, dkI fp32"}
+    return {"workload": w.name, "Bk": w.Bk, "k": w.k, "ms": float(ms.mean()),
+            "ms_min": float(ms.min()), "flops": fl, "TFLOPs": tf,
+            "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, "outputs": "dqI, dkI fp32"}
 
 
 def topk_leg(args, pre):
@@ -469,7 +469,7 @@ def main():
         if args.only in ("", "fp8") and fused:
             log("[bench] fp8 index leg")
             out["fp8_index"] = fp8_leg(args, pre)
-        if args.only in ("", "backward") and fused:
+        if args.only in ("", "backward"):
             log("[bench] backward leg")
             out["backward"] = backward_leg(args, pre)
             log("[bench] index KL backward leg")
