@@ -1,6 +1,7 @@
 /*
- * msa.h -- C ABI of the MiniMax Sparse Attention (MSA) forward path for AMD
- * MI355X (gfx950).  Implemented by libmsa.so (hand-written HIP kernels).
+ * msa.h -- C ABI of the MiniMax Sparse Attention (MSA) hot path for AMD MI355X
+ * (gfx950): the forward, and the two backward calls of a training step.
+ * Implemented by libmsa.so (hand-written HIP kernels).
  *
  * The method (MSA study notes, dimensionstp.github.io/study-concept/msa,
  * section 2-3 "Fixed attention budget", its three displayed equations and the
@@ -12,6 +13,9 @@
  *                     plus the best min(k-1, local(t)) earlier blocks by S
  *   (4) main branch   O[t,h] = softmax(q[t,h] K_g^T / sqrt(d_h)) V_g over the
  *                     keys j <= p(t) of the selected blocks of h's group g
+ *   training          the gradients of (4) with the selection held fixed, and
+ *                     the index branch's KL alignment against the group's
+ *                     mean main-branch weights (study notes sections 4-2, 4-3)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -21,7 +25,8 @@
  * Groups.  Query head h belongs to group g = h / (Hq / G).  Every head of a
  *   group reads the group's selection (study notes, section 3-3).
  * Budget.  k counts the local block: at most k * Bk keys per query and group
- *   (study notes, section 2-3: "including the local block, at most 2048").
+ *   (study notes, section 2-3: a budget of 2048 tokens with the local block
+ *   counted in it).
  * Ties.  Among equal block scores the lower block index wins.
  * Slot order.  idx rows list the selected blocks in ascending order; the
  *   local block is the last valid slot; unused slots hold -1.
@@ -44,7 +49,8 @@
  *   k * Bk <= 2048 (the study notes' fixed budget of section 2-3, which its
  *   block-size comparison in section 4-6 keeps: k <= 16, 32, 64) and at most
  *   16384 blocks per sequence; G in {1,2,4,8,16}, Hq / G in {1,2,4,8,16};
- *   N <= 2^21.  The fp8 index calls and the paged calls take Bk == 128.
+ *   N <= 2^21.  The fp8 index calls and the paged calls take Bk == 128; the
+ *   training calls take every supported Bk.
  *   Others: MSA_ERR_UNSUPPORTED.
  */
 #ifndef MSA_H
