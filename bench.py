@@ -189,6 +189,45 @@ def index_kl_leg(args, pre):
             "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, "outputs": "dqI, dkI fp32"}
 
 
+def train_leg(args, pre):
+    """Both training backwards in one call (msa_train_backward) on the same
+    inputs as the two legs above; events on the launch stream.  Work: the
+    stage-4 backward's five products plus the index branch's four (the
+    teacher is the backward's own weights)."""
+    from msa_inputs import make_grad_output
+    w, inp, idx = pre["w"], pre["inp"], pre["idx"]
+    q, K, V = inp["q"], inp["K"], inp["V"]
+    O, lse = ops.sparse_attn_prefill(q, K, V, idx, return_lse=True, Bk=w.Bk)
+    dO = make_grad_output(w, device="cuda")
+    outs = (torch.empty(q.shape, dtype=torch.float32, device="cuda"),
+            torch.empty(K.shape, dtype=torch.float32, device="cuda"),
+            torch.empty(K.shape, dtype=torch.float32, device="cuda"),
+            torch.empty(inp["qI"].shape, dtype=torch.float32, device="cuda"),
+            torch.empty(inp["kI"].shape, dtype=torch.float32, device="cuda"))
+    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k, Bk=w.Bk)
+    ws = torch.empty(ops.workspace_bytes(ops.OP_TRAIN_BACKWARD, d), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda: ops.train_backward(q, K, V, inp["qI"], inp["kI"], idx, O, lse, dO, out=outs,
+                                      workspace=ws, Bk=w.Bk)
+    for _ in range(max(1, args.warmup)):
+        call()
+    torch.cuda.synchronize()
+    events = [(ev(), ev()) for _ in range(args.steps)]
+    for e0, e1 in events:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in events])
+    fl = acc.train_flops(w.N, w.T, w.Hq, w.G, w.d_h, w.d_I, w.Bk, w.k, w.B)
+    tf = fl / (ms.mean() * 1e-3) / 1e12
+    log("[bench] fused training backward %.3f ms (%.1f TFLOP/s)" % (ms.mean(), tf))
+    return {"workload": w.name, "Bk": w.Bk, "k": w.k, "ms": float(ms.mean()),
+            "ms_min": float(ms.min()), "flops": fl, "TFLOPs": tf,
+            "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+            "outputs": "dq, dK, dV, dqI, dkI fp32"}
+
+
 def topk_leg(args, pre):
     """Stage 3 alone on materialised scores of the same workload."""
     w, inp = pre["w"], pre["inp"]
@@ -474,6 +513,8 @@ def main():
             out["backward"] = backward_leg(args, pre)
             log("[bench] index KL backward leg")
             out["index_kl_backward"] = index_kl_leg(args, pre)
+            log("[bench] fused training backward leg")
+            out["train_backward"] = train_leg(args, pre)
         if not args.no_cpu and args.only == "" and fused:
             log("[bench] cpu baseline")
             out["cpu_baseline"], out["parity_sample"] = cpu_leg(args, pre)

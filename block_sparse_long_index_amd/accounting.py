@@ -72,6 +72,15 @@ def index_kl_flops(N, T, Hq, G, d_h, d_I, Bk, k, B=1) -> int:
     return 2 * Hq * d_h * n + 8 * G * d_I * n
 
 
+def train_flops(N, T, Hq, G, d_h, d_I, Bk, k, B=1) -> int:
+    """Fused training backward: the stage-4 backward's five products plus the
+    index branch's four (index scores for the proxy lse and for the gradient
+    pass, dq^I, dk^I); the teacher comes from the backward's own weights, so
+    the main scores are not counted twice."""
+    n = support_tokens(N, T, Bk, k, B)
+    return 10 * Hq * d_h * n + 8 * G * d_I * n
+
+
 def prefill_flops(w) -> dict:
     idx = index_flops(w.N, w.T, w.G, w.d_I, w.B)
     main = main_flops(w.N, w.T, w.Hq, w.d_h, w.Bk, w.k, w.B)

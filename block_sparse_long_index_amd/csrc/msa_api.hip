@@ -172,6 +172,17 @@ size_t index_kl_ws(const msa_dims_t* d, int64_t window) {
   return lpx_bytes(d) + prefill_ws(d, window);
 }
 
+// Fused training backward: D = dO . O, the proxy lse, one stage's teacher
+// (fp32 per (row, slot, key)), then the prefill's inversion and partials.
+size_t teach_bytes(const msa_dims_t* d, int64_t window) {
+  return ((static_cast<size_t>(stage_rows_for(d, window) * d->k * d->Bk) * sizeof(float)) + 255) &
+         ~size_t(255);
+}
+
+size_t train_ws(const msa_dims_t* d, int64_t window) {
+  return rowdot_bytes(d) + lpx_bytes(d) + teach_bytes(d, window) + prefill_ws(d, window);
+}
+
 size_t decode_ws(const msa_dims_t* d) {
   return msa::attn_workspace_bytes(d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, d->Bk, true);
 }
@@ -208,6 +219,7 @@ size_t msa_workspace_bytes(int op, const msa_dims_t* d) {
     case MSA_OP_ATTN_DECODE: return d->T == 1 ? decode_ws(d) : 0;
     case MSA_OP_ATTN_BACKWARD: return backward_ws(d, default_window(d));
     case MSA_OP_INDEX_KL_BACKWARD: return index_kl_ws(d, default_window(d));
+    case MSA_OP_TRAIN_BACKWARD: return train_ws(d, default_window(d));
   }
   return 0;
 }
@@ -429,6 +441,62 @@ int msa_index_kl_backward(const msa_dims_t* d, const void* qI, const void* kI, c
                                                      d->B, d->T, d->N, d->Hq, d->G, d->k, d->Bk, w,
                                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_index_kl_backward");
+  return MSA_OK;
+}
+
+int msa_train_backward(const msa_dims_t* d, const void* q, const void* K, const void* V,
+                       const void* qI, const void* kI, const int32_t* idx, const void* O,
+                       const float* lse, const void* dO, float* dq, float* dK, float* dV,
+                       float* dqI, float* dkI, float* kl, void* ws, size_t ws_bytes,
+                       void* stream) {
+  MSA_TRY(check_dims(d));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(K, "K"));
+  MSA_TRY(check_ptr(V, "V"));
+  MSA_TRY(check_ptr(qI, "qI"));
+  MSA_TRY(check_ptr(kI, "kI"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  MSA_TRY(check_ptr(O, "O"));
+  MSA_TRY(check_ptr(lse, "lse"));
+  MSA_TRY(check_ptr(dO, "dO"));
+  MSA_TRY(check_ptr(dq, "dq"));
+  MSA_TRY(check_ptr(dK, "dK"));
+  MSA_TRY(check_ptr(dV, "dV"));
+  MSA_TRY(check_ptr(dqI, "dqI"));
+  MSA_TRY(check_ptr(dkI, "dkI"));
+  if (kl) MSA_TRY(check_ptr(kl, "kl"));
+  MSA_TRY(check_ptr(ws, "ws"));
+  int64_t hi = default_window(d);
+  if (train_ws(d, 1) > ws_bytes)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "training backward needs at least %zu workspace bytes (%zu for the default "
+                "window), got %zu",
+                train_ws(d, 1), train_ws(d, hi), ws_bytes);
+  if (train_ws(d, hi) > ws_bytes) {
+    int64_t lo = 1;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo + 1) / 2;
+      if (train_ws(d, mid) <= ws_bytes)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    hi = lo;
+  }
+  char* p = static_cast<char*>(ws);
+  float* Dr = reinterpret_cast<float*>(p);
+  p += rowdot_bytes(d);
+  float* lpx = reinterpret_cast<float*>(p);
+  p += lpx_bytes(d);
+  float* teach = reinterpret_cast<float*>(p);
+  p += teach_bytes(d, hi);
+  msa::AttnWorkspace w;
+  msa::attn_workspace_carve(p, hi, stage_rows_for(d, hi), d->N, d->G, d->Hq / d->G, d->k, d->Bk,
+                            false, &w);
+  const hipError_t e = msa::launch_train_backward(
+      q, K, V, qI, kI, idx, O, lse, dO, dq, dK, dV, dqI, dkI, kl, Dr, lpx, teach, d->B, d->T,
+      d->N, d->Hq, d->G, d->k, d->Bk, w, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_train_backward");
   return MSA_OK;
 }
 

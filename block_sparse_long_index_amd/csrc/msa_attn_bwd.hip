@@ -55,13 +55,16 @@ struct BwdArgs {
   u16* dqpart;            // [stage rows, k, hg, 128] bf16
   float* dK;              // [B, G, N, 128]
   float* dV;
+  float* teach;           // [stage rows, k, Bk] fp32: the teacher of each (row, slot), or null
   int64_t T, N, r0;       // r0: global row (b*T + t) of window row 0
   int32_t Hq, G, k, Bk;
   int32_t rl_base;        // first window row of this stage
   int32_t sink;           // spare partial row (hg rows) for rows past a chunk's end
 };
 
-template <int HG>
+// TW: also write the teacher of the index branch's KL alignment, the mean over
+// the group's heads of P, per (row, slot, key).
+template <int HG, bool TW>
 __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) unsigned char ks[128 * kBP];  // K [key][d]
   __shared__ __align__(16) unsigned char vs[128 * kBP];  // V [key][d]
@@ -244,6 +247,51 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
     *reinterpret_cast<uint4*>(dst + 8) = w1;
   };
 
+  // The teacher of the pass's queries at this lane's key: the lane's P values
+  // are rows m(i) = 8(i/4) + 4 half + i%4, a query's HG head rows are
+  // consecutive, so the head sum is in-lane (HG <= 4), in-lane plus the other
+  // half-wave (HG = 8, HG = 16).  Rows past the chunk's end (partial row >=
+  // sink) write nothing; keys past Bk belong to no block (wave-uniform test).
+  auto write_teacher = [&](int pass, const float* pr) {
+    if (32 * wave >= a.Bk) return;
+    const int* rpw = r_prow[pass & 1];
+    auto put = [&](int m, float sum) {
+      const int pw = rpw[m];  // (row, slot) entry * HG for the query's first head
+      if (pw < a.sink)
+        a.teach[static_cast<int64_t>(pw / HG) * a.Bk + key_w] = sum * (1.f / HG);
+    };
+    if constexpr (HG <= 4) {
+#pragma unroll
+      for (int i = 0; i < 16; i += HG) {
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < HG; ++j) sum += pr[i + j];
+        put(8 * (i >> 2) + 4 * half + (i & 3), sum);
+      }
+    } else if constexpr (HG == 8) {
+      float sum[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sum[j] = (pr[4 * j] + pr[4 * j + 1]) + (pr[4 * j + 2] + pr[4 * j + 3]);
+        sum[j] += __shfl_xor(sum[j], 32);
+      }
+      // half h writes queries 2h and 2h + 1 (rows 16h and 16h + 8)
+      put(16 * half, half ? sum[2] : sum[0]);
+      put(16 * half + 8, half ? sum[3] : sum[1]);
+    } else {
+      static_assert(HG == 16, "heads per group");
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        s0 += pr[j];
+        s1 += pr[8 + j];
+      }
+      s0 += __shfl_xor(s0, 32);
+      s1 += __shfl_xor(s1, 32);
+      put(16 * half, half ? s1 : s0);  // half h writes query h
+    }
+  };
+
   // Pass p: the S / dP products of pass p run beside the dq product of pass
   // p - 1 (two independent MFMA streams), then P, dS (into dss[p & 1]) and
   // dK / dV; a barrier; the next pass's rows go to LDS; a barrier.
@@ -287,6 +335,7 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
       dsr[i] = p * (pacc[i] - r_D[m]) * kScale;
       *reinterpret_cast<u16*>(&dsw[m * kBP + 2 * key_w]) = f32_to_bf16(dsr[i]);
     }
+    if constexpr (TW) write_teacher(pass, pr);
     if (pass > 0) store_dq(pass - 1, q0 + q1);
     // dV += P^T dO and dK += dS^T q over the pass's rows: keys on M, dims on
     // N; the B operands are the transposed tiles (see tpos).
@@ -425,8 +474,12 @@ template <int HG>
 static hipError_t launch_bwd_stage(const BwdArgs& ba, const DqArgs& da, int64_t grid_chunks,
                                    hipStream_t st) {
   const int64_t grid = (grid_chunks + 7) & ~static_cast<int64_t>(7);
-  hipLaunchKernelGGL((kv_outer_bwd_kernel<HG>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                     st, ba);
+  if (ba.teach)
+    hipLaunchKernelGGL((kv_outer_bwd_kernel<HG, true>), dim3(static_cast<unsigned>(grid)),
+                       dim3(256), 0, st, ba);
+  else
+    hipLaunchKernelGGL((kv_outer_bwd_kernel<HG, false>), dim3(static_cast<unsigned>(grid)),
+                       dim3(256), 0, st, ba);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dq_combine_kernel<HG>), dim3(static_cast<unsigned>((da.rows + 3) / 4)),
@@ -472,16 +525,9 @@ static unsigned nblocks_of(int64_t n, int per) {
   return static_cast<unsigned>((n + per - 1) / per);
 }
 
-// Zero dK and dV, D = dO . O for every row; then, per sequence and window of
-// rows, the inversion and the stages in group-major order: a stage's KV-outer
-// launch writes its rows' dq partials and adds its chunks' dK / dV, and the
-// dq combine right after sums the partials.
-hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
-                                const int32_t* idx, const void* O, const float* lse,
-                                const void* dO, float* dq, float* dK, float* dV, float* Dr,
-                                int64_t B, int64_t T, int64_t N, int Hq, int G, int k, int Bk,
-                                const AttnWorkspace& w, hipStream_t st) {
-  const int hg = Hq / G;
+// Zero dK and dV; D = dO . O for every (row, head).
+hipError_t attn_bwd_prepare(const void* O, const void* dO, float* dK, float* dV, float* Dr,
+                            int64_t B, int64_t T, int64_t N, int Hq, int G, hipStream_t st) {
   const int64_t n4 = B * G * N * kHeadDim / 4;
   hipLaunchKernelGGL(bwd_zero_kernel, dim3(nblocks_of(n4, 256)), dim3(256), 0, st,
                      reinterpret_cast<float4*>(dK), n4);
@@ -490,7 +536,66 @@ hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
   const int64_t nrows = B * T * Hq;
   hipLaunchKernelGGL(bwd_rowdot_kernel, dim3(nblocks_of(nrows * 16, 256)), dim3(256), 0, st,
                      static_cast<const u16*>(O), static_cast<const u16*>(dO), Dr, nrows);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+// One stage (group g, row stage sub) of a window inverted by
+// launch_invert_window: the KV-outer launch writes the stage's dq partials
+// (and the teacher when teach is set) and adds its chunks' dK / dV; the dq
+// combine right after sums the partials.
+hipError_t attn_bwd_stage(const void* q, const void* K, const void* V, const int32_t* idx,
+                          const float* lse, const void* dO, const float* Dr, float* dq,
+                          float* dK, float* dV, float* teach, int64_t T, int64_t N, int Hq,
+                          int G, int k, int Bk, const AttnWorkspace& w, int64_t r0, int64_t W,
+                          int32_t S, int g, int32_t sub, hipStream_t st) {
+  const int64_t si = static_cast<int64_t>(g) * S + sub;
+  const int32_t rl_base = sub * static_cast<int32_t>(w.stage_rows);
+  BwdArgs ba;
+  ba.q = static_cast<const u16*>(q);
+  ba.K = static_cast<const u16*>(K);
+  ba.V = static_cast<const u16*>(V);
+  ba.dO = static_cast<const u16*>(dO);
+  ba.lse = lse;
+  ba.Dr = Dr;
+  ba.chunks = w.chunks + si * w.max_chunks;
+  ba.entries = w.entries;
+  ba.count = w.totals + 4 + si;
+  ba.dqpart = w.opart;
+  ba.dK = dK;
+  ba.dV = dV;
+  ba.teach = teach;
+  ba.T = T;
+  ba.N = N;
+  ba.r0 = r0;
+  ba.Hq = Hq;
+  ba.G = G;
+  ba.k = k;
+  ba.Bk = Bk;
+  ba.rl_base = rl_base;
+  ba.sink = static_cast<int32_t>(w.sink);
+  DqArgs da;
+  da.idx = idx;
+  da.dqpart = w.opart;
+  da.dq = dq;
+  da.T = T;
+  da.r0 = r0;
+  da.rows = (W - rl_base) < w.stage_rows ? (W - rl_base) : w.stage_rows;
+  da.Hq = Hq;
+  da.G = G;
+  da.k = k;
+  da.rl_base = rl_base;
+  da.group = g;
+  return dispatch_bwd(Hq / G, ba, da, w.max_chunks, st);
+}
+
+// Per sequence and window of rows: the inversion, then the stages in
+// group-major order.
+hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
+                                const int32_t* idx, const void* O, const float* lse,
+                                const void* dO, float* dq, float* dK, float* dV, float* Dr,
+                                int64_t B, int64_t T, int64_t N, int Hq, int G, int k, int Bk,
+                                const AttnWorkspace& w, hipStream_t st) {
+  hipError_t e = attn_bwd_prepare(O, dO, dK, dV, Dr, B, T, N, Hq, G, st);
   if (e != hipSuccess) return e;
   for (int64_t b = 0; b < B; ++b) {
     for (int64_t t0 = 0; t0 < T; t0 += w.window) {
@@ -498,46 +603,10 @@ hipError_t launch_attn_backward(const void* q, const void* K, const void* V,
       int32_t S = 0;
       e = launch_invert_window(idx, b, T, t0, W, N, G, k, Bk, w, &S, st);
       if (e != hipSuccess) return e;
-      const int64_t r0 = b * T + t0;
       for (int g = 0; g < G; ++g) {
         for (int32_t sub = 0; sub < S; ++sub) {
-          const int64_t si = static_cast<int64_t>(g) * S + sub;
-          const int32_t rl_base = sub * static_cast<int32_t>(w.stage_rows);
-          BwdArgs ba;
-          ba.q = static_cast<const u16*>(q);
-          ba.K = static_cast<const u16*>(K);
-          ba.V = static_cast<const u16*>(V);
-          ba.dO = static_cast<const u16*>(dO);
-          ba.lse = lse;
-          ba.Dr = Dr;
-          ba.chunks = w.chunks + si * w.max_chunks;
-          ba.entries = w.entries;
-          ba.count = w.totals + 4 + si;
-          ba.dqpart = w.opart;
-          ba.dK = dK;
-          ba.dV = dV;
-          ba.T = T;
-          ba.N = N;
-          ba.r0 = r0;
-          ba.Hq = Hq;
-          ba.G = G;
-          ba.k = k;
-          ba.Bk = Bk;
-          ba.rl_base = rl_base;
-          ba.sink = static_cast<int32_t>(w.sink);
-          DqArgs da;
-          da.idx = idx;
-          da.dqpart = w.opart;
-          da.dq = dq;
-          da.T = T;
-          da.r0 = r0;
-          da.rows = (W - rl_base) < w.stage_rows ? (W - rl_base) : w.stage_rows;
-          da.Hq = Hq;
-          da.G = G;
-          da.k = k;
-          da.rl_base = rl_base;
-          da.group = g;
-          e = dispatch_bwd(hg, ba, da, w.max_chunks, st);
+          e = attn_bwd_stage(q, K, V, idx, lse, dO, Dr, dq, dK, dV, nullptr, T, N, Hq, G, k, Bk,
+                             w, b * T + t0, W, S, g, sub, st);
           if (e != hipSuccess) return e;
         }
       }

@@ -92,6 +92,34 @@ hipError_t launch_index_kl_backward(const void* qI, const void* kI, const void* 
                                     float* kl, float* lpx, int64_t B, int64_t T, int64_t N,
                                     int Hq, int G, int k, int Bk, const AttnWorkspace& w,
                                     hipStream_t st);
+// Pieces of the two backward launchers, for the fused training backward:
+// zeroing / D = dO . O, and one stage (group g, row stage sub of the window
+// of W rows at global row r0, S row stages per group) after
+// launch_invert_window.  teach: [stage rows, k, Bk] fp32, written by the
+// main stage and read by the KL stage (null: each stands alone).
+hipError_t attn_bwd_prepare(const void* O, const void* dO, float* dK, float* dV, float* Dr,
+                            int64_t B, int64_t T, int64_t N, int Hq, int G, hipStream_t st);
+hipError_t attn_bwd_stage(const void* q, const void* K, const void* V, const int32_t* idx,
+                          const float* lse, const void* dO, const float* Dr, float* dq,
+                          float* dK, float* dV, float* teach, int64_t T, int64_t N, int Hq,
+                          int G, int k, int Bk, const AttnWorkspace& w, int64_t r0, int64_t W,
+                          int32_t S, int g, int32_t sub, hipStream_t st);
+hipError_t index_kl_prepare(float* dkI, int64_t B, int64_t N, hipStream_t st);
+hipError_t index_kl_stage(const void* qI, const void* kI, const void* q, const void* K,
+                          const int32_t* idx, const float* lse, const float* teach, float* dqI,
+                          float* dkI, float* kl, float* lpx, int64_t T, int64_t N, int Hq, int G,
+                          int k, int Bk, const AttnWorkspace& w, int64_t r0, int64_t W, int32_t S,
+                          int g, int32_t sub, hipStream_t st);
+// Both training backwards in one pass over the stages (the outputs of
+// launch_attn_backward and launch_index_kl_backward); teach: w.stage_rows *
+// k * Bk floats of scratch.
+hipError_t launch_train_backward(const void* q, const void* K, const void* V, const void* qI,
+                                 const void* kI, const int32_t* idx, const void* O,
+                                 const float* lse, const void* dO, float* dq, float* dK,
+                                 float* dV, float* dqI, float* dkI, float* kl, float* Dr,
+                                 float* lpx, float* teach, int64_t B, int64_t T, int64_t N,
+                                 int Hq, int G, int k, int Bk, const AttnWorkspace& w,
+                                 hipStream_t st);
 hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse,
                                int64_t B, int64_t T, int64_t N, int Hq, int G,

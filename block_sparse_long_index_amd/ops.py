@@ -24,6 +24,7 @@ OP_ATTN_PREFILL = 3
 OP_ATTN_DECODE = 4
 OP_ATTN_BACKWARD = 5
 OP_INDEX_KL_BACKWARD = 6
+OP_TRAIN_BACKWARD = 7
 
 # Every function the C header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -39,6 +40,7 @@ _SIGS = {
                                               ctypes.c_size_t, _P]),
     "msa_sparse_attn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                 _P, ctypes.c_size_t, _P]),
+    "msa_train_backward": (ctypes.c_int, [_P] * 17 + [ctypes.c_size_t, _P]),
     "msa_index_kl_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              ctypes.c_size_t, _P]),
     "msa_select_blocks_paged": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, _P, _P, _P, _P,
@@ -269,6 +271,49 @@ def index_kl_backward(qI, kI, q, K, idx, lse, return_loss=False, out=None, works
                                        _ptr(ws), nbytes, _stream()),
            "msa_index_kl_backward")
     return (dqI, dkI, kl) if return_loss else (dqI, dkI)
+
+
+def train_backward(q, K, V, qI, kI, idx, O, lse, dO, return_loss=False, out=None,
+                   workspace=None, Bk=128):
+    """Both training backwards in one call (msa_train_backward): the inputs
+    of sparse_attn_backward and index_kl_backward together -> (dq, dK, dV,
+    dqI, dkI), plus the loss kl [B,G,T] when return_loss.  out: optional
+    (dq, dK, dV, dqI, dkI) tensors to write."""
+    B, T, Hq, dh = q.shape
+    _, G, N, _ = K.shape
+    dI = qI.shape[3]
+    k = idx.shape[-1]
+    _need(q, "q", torch.bfloat16)
+    _need(K, "K", torch.bfloat16, (B, G, N, dh))
+    _need(V, "V", torch.bfloat16, (B, G, N, dh))
+    _need(qI, "qI", torch.bfloat16, (B, T, G, dI))
+    _need(kI, "kI", torch.bfloat16, (B, N, dI))
+    _need(idx, "idx", torch.int32, (B, G, T, k))
+    _need(O, "O", torch.bfloat16, q.shape)
+    _need(dO, "dO", torch.bfloat16, q.shape)
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    d = dims(B, T, N, Hq, G, k, d_h=dh, d_I=dI, Bk=Bk)
+    if out is None:
+        dev = q.device
+        out = (torch.empty(q.shape, dtype=torch.float32, device=dev),
+               torch.empty(K.shape, dtype=torch.float32, device=dev),
+               torch.empty(K.shape, dtype=torch.float32, device=dev),
+               torch.empty(qI.shape, dtype=torch.float32, device=dev),
+               torch.empty(kI.shape, dtype=torch.float32, device=dev))
+    dq, dK, dV, dqI, dkI = out
+    _need(dq, "dq", torch.float32, q.shape)
+    _need(dK, "dK", torch.float32, K.shape)
+    _need(dV, "dV", torch.float32, K.shape)
+    _need(dqI, "dqI", torch.float32, qI.shape)
+    _need(dkI, "dkI", torch.float32, kI.shape)
+    kl = torch.empty(B, G, T, dtype=torch.float32, device=q.device) if return_loss else None
+    ws, nbytes = _workspace(OP_TRAIN_BACKWARD, d, workspace)
+    _check(lib().msa_train_backward(ctypes.byref(d), _ptr(q), _ptr(K), _ptr(V), _ptr(qI),
+                                    _ptr(kI), _ptr(idx), _ptr(O), _ptr(lse), _ptr(dO), _ptr(dq),
+                                    _ptr(dK), _ptr(dV), _ptr(dqI), _ptr(dkI), _ptr(kl), _ptr(ws),
+                                    nbytes, _stream()),
+           "msa_train_backward")
+    return (dq, dK, dV, dqI, dkI, kl) if return_loss else (dq, dK, dV, dqI, dkI)
 
 
 def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None, Bk=128):

@@ -91,7 +91,8 @@ enum {
     MSA_OP_ATTN_PREFILL = 3,
     MSA_OP_ATTN_DECODE = 4,
     MSA_OP_ATTN_BACKWARD = 5,
-    MSA_OP_INDEX_KL_BACKWARD = 6
+    MSA_OP_INDEX_KL_BACKWARD = 6,
+    MSA_OP_TRAIN_BACKWARD = 7
 };
 
 /*
@@ -231,6 +232,30 @@ int msa_index_kl_backward(const msa_dims_t *dims, const void *qI, const void *kI
                           const void *q, const void *K, const int32_t *idx, const float *lse,
                           float *dqI, float *dkI, float *kl, void *ws, size_t ws_bytes,
                           void *stream);
+
+/*
+ * Both training backwards in one call, the fused proxy + main backward of
+ * the Flash-MSA blog's backward pass: one inversion of the selection drives
+ * both branches stage by stage, and the main branch's weights are formed
+ * once.  Each stage's main backward writes the teacher of its rows (the mean
+ * over the group's heads of the main weights, fp32, in the workspace); the
+ * index branch's pass right after reads it instead of recomputing the main
+ * scores.  Outputs and their meaning are those of msa_sparse_attn_backward
+ * (dq, dK, dV) and msa_index_kl_backward (dqI, dkI, kl); the arguments are
+ * the union of theirs, with the same shapes and layouts.
+ *   ws / ws_bytes  >= msa_workspace_bytes(MSA_OP_TRAIN_BACKWARD) for the
+ *                  default window; smaller (down to one row per window plus
+ *                  B*T*(Hq+G) floats plus one stage's teacher) runs more
+ *                  windows.
+ * Any supported block size.  Results equal those of the two separate calls
+ * up to rounding (the teacher's head sum is taken in another order) and the
+ * atomic-add order of dK, dV and dkI.
+ */
+int msa_train_backward(const msa_dims_t *dims, const void *q, const void *K, const void *V,
+                       const void *qI, const void *kI, const int32_t *idx, const void *O,
+                       const float *lse, const void *dO, float *dq, float *dK, float *dV,
+                       float *dqI, float *dkI, float *kl, void *ws, size_t ws_bytes,
+                       void *stream);
 
 /*
  * Stage 4 for decode (T must be 1): split over the B * G * k selected KV

@@ -22,7 +22,7 @@ def _declared():
 def test_header_functions_are_exported():
     L = ops.lib()
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(ops._SIGS)
@@ -218,3 +218,30 @@ def test_index_kl_argument_checks():
     for bk, k in ((64, 4), (32, 8)):
         assert L.msa_workspace_bytes(ops.OP_INDEX_KL_BACKWARD, ctypes.byref(_good(Bk=bk, k=k))) > 0
     assert L.msa_index_kl_backward(ctypes.byref(_good(Bk=96)), *args, FAKE, 1 << 40, None) == -2
+
+
+def test_train_backward_argument_checks():
+    """The fused training backward validates before any HIP call: every
+    required pointer (kl may be NULL), the block size, the workspace floor;
+    its workspace covers both separate calls' scratch plus one stage's
+    teacher (fp32 per (row, slot, key))."""
+    L = ops.lib()
+    d = _good()
+    need = L.msa_workspace_bytes(ops.OP_TRAIN_BACKWARD, ctypes.byref(d))
+    prefill = L.msa_workspace_bytes(ops.OP_ATTN_PREFILL, ctypes.byref(d))
+    assert need >= prefill + 256 * (8 + 2) * 4 + 256 * d.k * d.Bk * 4
+    args = [FAKE] * 15  # q K V qI kI idx O lse dO dq dK dV dqI dkI kl
+    for i in range(14):
+        bad = list(args)
+        bad[i] = None
+        assert L.msa_train_backward(ctypes.byref(d), *bad, FAKE, need, None) == -1
+        bad[i] = MISALIGNED
+        assert L.msa_train_backward(ctypes.byref(d), *bad, FAKE, need, None) == -1
+    bad = list(args)
+    bad[14] = MISALIGNED
+    assert L.msa_train_backward(ctypes.byref(d), *bad, FAKE, need, None) == -1
+    assert L.msa_train_backward(ctypes.byref(d), *args, None, need, None) == -1
+    assert L.msa_train_backward(ctypes.byref(d), *args, FAKE, 64, None) == -3
+    for bk, k in ((64, 4), (32, 8)):
+        assert L.msa_workspace_bytes(ops.OP_TRAIN_BACKWARD, ctypes.byref(_good(Bk=bk, k=k))) > 0
+    assert L.msa_train_backward(ctypes.byref(_good(Bk=96)), *args, FAKE, 1 << 40, None) == -2

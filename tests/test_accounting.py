@@ -87,6 +87,10 @@ def test_workload_totals():
     kl = acc.index_kl_flops(w.N, w.T, w.Hq, w.G, w.d_h, w.d_I, w.Bk, w.k)
     assert kl * 2 == fl["main"] + 8 * w.G * w.d_I * acc.support_tokens(w.N, w.T, w.Bk, w.k) * 2
     assert abs(kl / 1e12 - 6.344) < 0.01
+    # fused training backward: the backward's five products + the 4 index products
+    tr = acc.train_flops(w.N, w.T, w.Hq, w.G, w.d_h, w.d_I, w.Bk, w.k)
+    assert tr * 2 == fl["main"] * 5 + 8 * w.G * w.d_I * acc.support_tokens(w.N, w.T, w.Bk, w.k) * 2
+    assert abs(tr / 1e12 - 23.26) < 0.01
     w0 = WORKLOADS["prefill_2k"]
     assert acc.support_tokens(w0.N, w0.T, w0.Bk, w0.k) == 820224
     assert np.isclose(acc.prefill_flops(w0)["index"], 1.074e9, rtol=1e-3)
