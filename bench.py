@@ -433,6 +433,15 @@ def cpu_train_leg(args, pre):
                     "kind": "oracle", "seconds": sec,
                     "sample": "%d query rows (all %d groups, %d heads) of %s; fp64 plain C, "
                               "OpenMP" % (len(rb), w.G, w.Hq, w.name)}
+    # the fused call's work done by the oracle's two functions: per support
+    # key, its FLOPs over the sum of the two functions' times for theirs
+    fb, fk = 10 * w.Hq * w.d_h, 2 * w.Hq * w.d_h + 8 * w.G * w.d_I
+    ft = 10 * w.Hq * w.d_h + 8 * w.G * w.d_I
+    rate = ft / (fb / out["backward"]["value"] + fk / out["index_kl_backward"]["value"])
+    out["train_backward"] = {"value": rate, "unit": "TFLOP/s", "cores": oracle.threads(),
+                             "kind": "oracle",
+                             "sample": "the two samples above: the oracle's backward and "
+                                       "index KL functions' times per support key, added"}
     return out
 
 
@@ -522,6 +531,7 @@ def main():
             cb = cpu_train_leg(args, pre)
             out["backward"]["cpu_baseline"] = cb["backward"]
             out["index_kl_backward"]["cpu_baseline"] = cb["index_kl_backward"]
+            out["train_backward"]["cpu_baseline"] = cb["train_backward"]
         del pre
         torch.cuda.empty_cache()
     if args.only in ("", "decode"):

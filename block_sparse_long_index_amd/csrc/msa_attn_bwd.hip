@@ -257,8 +257,9 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
     const int* rpw = r_prow[pass & 1];
     auto put = [&](int m, float sum) {
       const int pw = rpw[m];  // (row, slot) entry * HG for the query's first head
-      if (pw < a.sink)
-        a.teach[static_cast<int64_t>(pw / HG) * a.Bk + key_w] = sum * (1.f / HG);
+      if (pw < a.sink)  // read once, by the KL pass: kept out of the caches
+        __builtin_nontemporal_store(sum * (1.f / HG),
+                                    a.teach + static_cast<int64_t>(pw / HG) * a.Bk + key_w);
     };
     if constexpr (HG <= 4) {
 #pragma unroll

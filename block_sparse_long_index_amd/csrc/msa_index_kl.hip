@@ -552,7 +552,7 @@ __global__ void __launch_bounds__(256, 2) index_kl_teach_kernel(IkArgs a) {
       const int qq = p * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
       const int e = ents[qq < n ? qq : 0];
       const int64_t tp = ((e >> 6) - a.rl_base) * a.k + (e & 63);
-      tv[i] = a.teach[tp * a.Bk + tkey];
+      tv[i] = __builtin_nontemporal_load(a.teach + tp * a.Bk + tkey);
     }
   };
   auto stash = [&]() {
