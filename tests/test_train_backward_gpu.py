@@ -116,6 +116,34 @@ def test_train_backward_small_all(name, B, T, N, Hq, G, k, Bk):
     against_separate(w, inp, idx, O, lse, dO, out)
 
 
+@pytest.mark.parametrize("B,T,N,Hq,G,k,Bk", tb._random_cases(12, 2027))
+def test_train_backward_random_shapes(B, T, N, Hq, G, k, Bk):
+    """Seeded random shapes (block sizes, chunked rows, group layouts, k):
+    every row and key of all six outputs against the oracle, and the
+    separate calls on the same inputs."""
+    w = Workload("rand", B=B, T=T, N=N, Hq=Hq, G=G, k=k, Bk=Bk, seed=N * 5 + T)
+    say("case", w)
+    inp = make_inputs(w, device="cuda")
+    dO = make_grad_output(w, device="cuda")
+    idx, O, lse = forward(w, inp)
+    out = fused(w, inp, idx, O, lse, dO)
+    torch.cuda.synchronize()
+    dq, dK, dV, dqI, dkI, kl = out
+    rb = np.repeat(np.arange(B), T)
+    rt = np.tile(np.arange(T), B)
+    ref_idx = tb.oracle_selection(w, inp, rb, rt)
+    assert np.array_equal(tb.gpu_rows(idx, rb, rt), ref_idx), "selection"
+    rdq, rdK, rdV = tb.oracle_backward(w, inp, dO, rb, rt, ref_idx)
+    tb.close("rand dq", dq.cpu().reshape(B * T, Hq, -1), rdq)
+    tb.close("rand dK", dK.cpu(), rdK[:, :, :N])
+    tb.close("rand dV", dV.cpu(), rdV[:, :, :N])
+    rdqI, rdkI, rkl = tk.oracle_kl(w, inp, rb, rt, ref_idx)
+    tk.close("rand dqI", dqI.cpu().reshape(B * T, G, -1), rdqI)
+    tk.close("rand dkI", dkI.cpu(), rdkI[:, :N])
+    tk.close_kl("rand", kl.permute(0, 2, 1).reshape(B * T, G).cpu(), rkl)
+    against_separate(w, inp, idx, O, lse, dO, out)
+
+
 def test_train_backward_windows_and_repeat():
     """A workspace of a few rows per window (several inversions, and stages
     of fewer rows) and a repeat: dq, dq^I and the loss bit for bit, dK, dV
