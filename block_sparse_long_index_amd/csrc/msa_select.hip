@@ -724,37 +724,34 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 template <int R>
 __device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int step, int m,
                                          int lane, float* cv, int* ci, float& v, int& vi) {
-  float x[R];
+  float x[R];  // -inf past the row's end
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int e = e0 + lane + step * r;
-    x[r] = src[e < n ? e : n - 1];
+    const float y = src[e < n ? e : n - 1];
+    x[r] = e < n ? y : -INFINITY;
   }
   const int rest = e0 + step * R;
   float lm = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < R; ++r) lm = fmaxf(lm, e0 + lane + step * r < n ? x[r] : -INFINITY);
+  for (int r = 0; r < R; ++r) lm = fmaxf(lm, x[r]);
   for (int e = rest + lane; e < n; e += step) lm = fmaxf(lm, src[e]);
   const float tau = __shfl(sort_desc_values64(lm, lane), m - 1);
-  int cnt = 0;  // candidates >= tau, the same in every lane
-#pragma unroll
-  for (int r = 0; r < R; ++r) cnt += __popcll(__ballot((e0 + lane + step * r < n) & (x[r] >= tau)));
-  for (int c0 = rest; c0 < n; c0 += step) {
-    const int e = c0 + lane;
-    cnt += __popcll(__ballot((e < n) & (src[e < n ? e : n - 1] >= tau)));
-  }
   v = -INFINITY;
   vi = INT_MAX;
-  auto chunk = [&](int c0, float xv, int& base) {
+  // candidates >= tau, compacted in index order while they fit the scratch;
+  // cnt counts them all (the same in every lane)
+  int cnt = 0;
+  auto chunk = [&](int c0, float xv) {
     const int e = c0 + lane;
     const bool f = (e < n) & (xv >= tau);
     const unsigned long long bal = __ballot(f);
-    if (f) {
-      const int pos = base + lanes_below(bal);
+    const int pos = cnt + lanes_below(bal);
+    if (f & (pos < 64)) {
       cv[pos] = xv;
       ci[pos] = e;
     }
-    base += __popcll(bal);
+    cnt += __popcll(bal);
   };
   auto merge = [&](int c0, float xv) {
     const int e = c0 + lane;
@@ -769,14 +766,13 @@ __device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int st
     }
     bitonic_merge64(v, vi, lane);
   };
-  if (cnt <= 64) {
-    int base = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) chunk(e0 + step * r, x[r], base);
-    for (int c0 = rest; c0 < n; c0 += step) {
-      const int e = c0 + lane;
-      chunk(c0, e < n ? src[e] : -INFINITY, base);
-    }
+  for (int r = 0; r < R; ++r) chunk(e0 + step * r, x[r]);
+  for (int c0 = rest; c0 < n; c0 += step) {
+    const int e = c0 + lane;
+    chunk(c0, e < n ? src[e] : -INFINITY);
+  }
+  if (cnt <= 64) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     if (lane < cnt) {
