@@ -336,7 +336,6 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
       dsr[i] = p * (pacc[i] - r_D[m]) * kScale;
       *reinterpret_cast<u16*>(&dsw[m * kBP + 2 * key_w]) = f32_to_bf16(dsr[i]);
     }
-    if constexpr (TW) write_teacher(pass, pr);
     if (pass > 0) store_dq(pass - 1, q0 + q1);
     // dV += P^T dO and dK += dS^T q over the pass's rows: keys on M, dims on
     // N; the B operands are the transposed tiles (see tpos).
@@ -357,6 +356,8 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
         dk[dt] = mfma32(as_bf16x8(da), as_bf16x8(*reinterpret_cast<const uint4*>(&qT[o])), dk[dt]);
       }
     }
+    // the teacher's stores go out after the pass's products, not among them
+    if constexpr (TW) write_teacher(pass, pr);
     // every wave is done with this pass's rows and with dss[(pass + 1) & 1];
     // dss[pass & 1] is complete
     __syncthreads();
