@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -523,6 +525,88 @@ int msa_sparse_attn_decode(const msa_dims_t* d, const void* q, const void* K, co
                                                d->k, d->Bk, kContiguous, w,
                                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode");
+  return MSA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode attention for callers that cannot allocate device memory: the
+// partial results of the selected blocks (bf16 O, fp32 (max, sum)) live in a
+// device array of this file instead of a caller workspace.  Each GPU holds its
+// own copy for the life of the process; its device address is looked up once
+// per device and kept.  The decode kernels write every partial they read, so
+// nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kScratchRows = 32768;  // partial rows: B * Hq * k
+constexpr size_t kScratchOpart = static_cast<size_t>(kScratchRows) * 128 * sizeof(uint16_t);
+constexpr size_t kScratchBytes = kScratchOpart + static_cast<size_t>(kScratchRows) * 8;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// The current device's copy of the scratch array (its device address).
+int scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attn_decode_noalloc: device %d >= %d", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "msa_sparse_attn_decode_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_sparse_attn_decode_noalloc(const msa_dims_t* d, const void* q, const void* K,
+                                   const void* V, const int32_t* idx, void* O, float* lse,
+                                   void* stream) {
+  MSA_TRY(check_dims(d));
+  if (d->T != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "decode needs T == 1 (got %lld)",
+                             (long long)d->T);
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(K, "K"));
+  MSA_TRY(check_ptr(V, "V"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  MSA_TRY(check_ptr(O, "O"));
+  if (lse) MSA_TRY(check_ptr(lse, "lse"));
+  const int64_t rows = d->B * d->Hq * d->k;
+  if (rows > kScratchRows)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "msa_sparse_attn_decode_noalloc: B * Hq * k = %lld partial rows exceed the "
+                "static scratch (%lld rows)", (long long)rows, (long long)kScratchRows);
+  void* base = nullptr;
+  MSA_TRY(scratch_ptr(&base));
+  msa::AttnWorkspace w = {};
+  w.opart = static_cast<uint16_t*>(base);
+  w.lpart = reinterpret_cast<float2*>(static_cast<char*>(base) + kScratchOpart);
+  w.window = d->B;
+  w.stage_rows = d->B;
+  const hipError_t e = msa::launch_attn_decode(q, K, V, idx, O, lse, d->B, d->N, d->Hq, d->G,
+                                               d->k, d->Bk, kContiguous, w,
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode_noalloc");
   return MSA_OK;
 }
 

@@ -38,6 +38,7 @@ _SIGS = {
                                                ctypes.c_size_t, _P]),
     "msa_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
+    "msa_sparse_attn_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "msa_sparse_attn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                 _P, ctypes.c_size_t, _P]),
     "msa_train_backward": (ctypes.c_int, [_P] * 17 + [ctypes.c_size_t, _P]),
@@ -335,6 +336,32 @@ def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None,
                                         _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()),
            "msa_sparse_attn_decode")
     return (O, lse) if return_lse else O
+
+
+def sparse_attn_decode_noalloc(q, K, V, idx, return_lse=False, out=None, lse_out=None,
+                               Bk=128):
+    """msa_sparse_attn_decode_noalloc: the decode attention with the library's
+    static scratch instead of a workspace (no device allocation by the
+    library; pass out / lse_out to allocate nothing here either)."""
+    B, Hq, dh = q.shape
+    _, G, N, _ = K.shape
+    k = idx.shape[-1]
+    _need(q, "q", torch.bfloat16)
+    _need(K, "K", torch.bfloat16, (B, G, N, dh))
+    _need(V, "V", torch.bfloat16, (B, G, N, dh))
+    _need(idx, "idx", torch.int32, (B, G, 1, k))
+    d = dims(B, 1, N, Hq, G, k, d_h=dh, Bk=Bk)
+    O = out if out is not None else torch.empty_like(q)
+    _need(O, "O", torch.bfloat16, q.shape)
+    lse = lse_out
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq))
+    _check(lib().msa_sparse_attn_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(K), _ptr(V),
+                                                _ptr(idx), _ptr(O), _ptr(lse), _stream()),
+           "msa_sparse_attn_decode_noalloc")
+    return (O, lse) if (return_lse or lse_out is not None) else O
 
 
 def forward(qI, kI, q, K, V, k, return_lse=False, Bk=128):

@@ -38,7 +38,9 @@
  *   natural log.
  * Memory.  Every pointer is a device pointer the caller owns, 16-byte aligned,
  *   to a contiguous row-major tensor of the layout given.  The library never
- *   allocates or frees device memory and keeps no pointer after returning.
+ *   allocates or frees device memory and keeps no pointer after returning;
+ *   its only device memory of its own is the static scratch array of
+ *   msa_sparse_attn_decode_noalloc.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *   enqueue work on it; nothing synchronises.  Results are ready when the
  *   stream reaches them.
@@ -274,6 +276,25 @@ int msa_sparse_attn_decode(const msa_dims_t *dims, const void *q,
                            const void *K, const void *V, const int32_t *idx,
                            void *O, float *lse, void *ws, size_t ws_bytes,
                            void *stream);
+
+/*
+ * msa_sparse_attn_decode without a workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  It allocates nothing.  The partial
+ * results of the selected blocks live in a static device array of the library
+ * instead (8.25 MB on each GPU the library runs on, held until the process
+ * ends), which bounds the call to B * Hq * k <= 32768 partial rows (the
+ * 256K x 16 decode step uses 16384); larger calls return
+ * MSA_ERR_WORKSPACE_TOO_SMALL before anything is launched.  The array used is
+ * the one of the current device, so `stream` must belong to it.  Every call on
+ * a GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  Arguments,
+ * results and errors are those of msa_sparse_attn_decode; the kernels are
+ * the same, so the outputs are bitwise equal to its outputs.
+ */
+int msa_sparse_attn_decode_noalloc(const msa_dims_t *dims, const void *q, const void *K,
+                                   const void *V, const int32_t *idx, void *O, float *lse,
+                                   void *stream);
 
 /*
  * Decode over paged caches: the explicit per-sequence position -> cell ->

@@ -22,7 +22,7 @@ def _declared():
 def test_header_functions_are_exported():
     L = ops.lib()
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(ops._SIGS)
@@ -245,3 +245,22 @@ def test_train_backward_argument_checks():
     for bk, k in ((64, 4), (32, 8)):
         assert L.msa_workspace_bytes(ops.OP_TRAIN_BACKWARD, ctypes.byref(_good(Bk=bk, k=k))) > 0
     assert L.msa_train_backward(ctypes.byref(_good(Bk=96)), *args, FAKE, 1 << 40, None) == -2
+
+
+def test_noalloc_decode_rejects_on_host():
+    """The no-allocation decode call validates like the workspace one and
+    rejects a batch whose partials exceed its static scratch, all before any
+    HIP call (fake pointers, no GPU)."""
+    L = ops.lib()
+    d = _good(T=1, N=4096, Hq=64, G=8, k=16, B=33)  # 33 * 64 * 16 > 32768 rows
+    rc = L.msa_sparse_attn_decode_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                          None)
+    assert rc == -3 and b"scratch" in L.msa_last_error()
+    d = _good(T=2, N=4096)
+    assert L.msa_sparse_attn_decode_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                            None) == -1
+    d = _good(T=1, N=4096)
+    assert L.msa_sparse_attn_decode_noalloc(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, None,
+                                            None) == -1
+    assert L.msa_sparse_attn_decode_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, MISALIGNED,
+                                            None, None) == -1
