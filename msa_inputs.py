@@ -128,12 +128,16 @@ def make_index_inputs(w: Workload, device="cpu", gen=None):
     if w.needles is not None:
         blocks = _needle_blocks(w, gen, device)
         meta["needle_blocks"] = [b.cpu() for b in blocks]
+        # per group: the query rows that copied a needle and that needle's block
+        meta["needle_rows"] = []
         pos = torch.arange(w.T, device=device) + (w.N - w.T)
         local = torch.div(pos, w.Bk, rounding_mode="floor")
         for g in range(w.G):
             nb = blocks[g]
             n = nb.numel()
             if n == 0:
+                meta["needle_rows"].append((torch.zeros(0, dtype=torch.int64),
+                                            torch.zeros(0, dtype=torch.int64)))
                 continue
             signs = torch.randint(0, 2, (n, w.d_I), generator=gen, device=device)
             u = (signs * 8 - 4).to(torch.bfloat16)  # {-4, +4}
@@ -152,6 +156,8 @@ def make_index_inputs(w: Workload, device="cpu", gen=None):
             for b in range(w.B):
                 row = qI[b, :, g, :]
                 row[assign] = planted[assign]
+            rows = torch.nonzero(assign).view(-1)
+            meta["needle_rows"].append((rows.cpu(), nb[which[rows]].cpu()))
         meta["needle_rows_fraction"] = 0.25
     return qI, kI, meta
 

@@ -119,6 +119,23 @@ def test_full_prefill_32k_bk64():
     compare_rows(w, inp, idx, O, lse, rb.numpy(), rt.numpy(), tag="prefill_32k_bk64")
 
 
+def test_full_prefill_32k_bk32():
+    """The 32K workload with 32-key blocks and k = 64 (the same 2048-token
+    budget): the windowed score path (1024 blocks per row) at full size,
+    sampled rows against the oracle with S bit-exact, invariants on every
+    row."""
+    w = WORKLOADS["prefill_32k"].replace(Bk=32, k=64)
+    say("workload", w.name, "Bk 32 generating")
+    inp = make_inputs(w, device="cuda")
+    idx = ops.select_blocks(inp["qI"], inp["kI"], w.k, Bk=32)
+    O, lse = ops.sparse_attn_prefill(inp["q"], inp["K"], inp["V"], idx, return_lse=True, Bk=32)
+    S = ops.index_scores(inp["qI"], inp["kI"], Bk=32)
+    torch.cuda.synchronize()
+    check_invariants(w, idx)
+    rb, rt = sample_rows(w, 64)
+    compare_rows(w, inp, idx, O, lse, rb.numpy(), rt.numpy(), S=S, tag="prefill_32k_bk32")
+
+
 def _random_cases(n, seed):
     g = np.random.default_rng(seed)
     cases = []

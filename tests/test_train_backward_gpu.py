@@ -104,8 +104,9 @@ def test_train_backward_small_all(name, B, T, N, Hq, G, k, Bk):
     ref_idx = tb.oracle_selection(w, inp, rb, rt)
     assert np.array_equal(tb.gpu_rows(idx, rb, rt), ref_idx), "selection"
     rdq, rdK, rdV = tb.oracle_backward(w, inp, dO, rb, rt, ref_idx)
-    tb.close(name + " dq", dq.cpu().reshape(B * T, Hq, -1), rdq)
-    tb.close(name + " dK", dK.cpu(), rdK[:, :, :N])
+    ex_dq, ex_dk = tb.bound_extras(w, inp, dO, rb, rt, ref_idx)
+    tb.close(name + " dq", dq.cpu().reshape(B * T, Hq, -1), rdq, ex_dq)
+    tb.close(name + " dK", dK.cpu(), rdK[:, :, :N], ex_dk[:, :, :N])
     tb.close(name + " dV", dV.cpu(), rdV[:, :, :N])
     rdqI, rdkI, rkl = tk.oracle_kl(w, inp, rb, rt, ref_idx)
     tk.close(name + " dqI", dqI.cpu().reshape(B * T, G, -1), rdqI)
@@ -134,8 +135,9 @@ def test_train_backward_random_shapes(B, T, N, Hq, G, k, Bk):
     ref_idx = tb.oracle_selection(w, inp, rb, rt)
     assert np.array_equal(tb.gpu_rows(idx, rb, rt), ref_idx), "selection"
     rdq, rdK, rdV = tb.oracle_backward(w, inp, dO, rb, rt, ref_idx)
-    tb.close("rand dq", dq.cpu().reshape(B * T, Hq, -1), rdq)
-    tb.close("rand dK", dK.cpu(), rdK[:, :, :N])
+    ex_dq, ex_dk = tb.bound_extras(w, inp, dO, rb, rt, ref_idx)
+    tb.close("rand dq", dq.cpu().reshape(B * T, Hq, -1), rdq, ex_dq)
+    tb.close("rand dK", dK.cpu(), rdK[:, :, :N], ex_dk[:, :, :N])
     tb.close("rand dV", dV.cpu(), rdV[:, :, :N])
     rdqI, rdkI, rkl = tk.oracle_kl(w, inp, rb, rt, ref_idx)
     tk.close("rand dqI", dqI.cpu().reshape(B * T, G, -1), rdqI)
@@ -186,7 +188,8 @@ def _full(name, n_rows, oracle_rows):
         assert np.array_equal(tb.gpu_rows(idx, rb, rt), ref_idx), "selection"
         rdq, _, _ = tb.oracle_backward(w, inp, dO, rb, rt, ref_idx, blk_lo=w.NB - 1, nblk=1)
         sel = (torch.as_tensor(rb, device="cuda"), torch.as_tensor(rt, device="cuda"))
-        tb.close(name + " dq rows", dq[sel].cpu(), rdq)
+        tb.close(name + " dq rows", dq[sel].cpu(), rdq,
+                 tb.dq_bound_extra(w, inp, dO, rb, rt, ref_idx))
         rdqI, _, rkl = tk.oracle_kl(w, inp, rb, rt, ref_idx, blk_lo=w.NB - 1, nblk=1)
         tk.close(name + " dqI rows", dqI[sel].cpu(), rdqI)
         tk.close_kl(name, kl.permute(0, 2, 1)[sel].cpu(), rkl)
