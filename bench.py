@@ -2,8 +2,10 @@
 
 One step = the whole prefill hot path on the 128K-token workload (B=1,
 N=T=131072, Hq=64, G=8, d=128, Bk=128, k=16, needles planted): fused index
-scoring + block max + top-k (msa_select_blocks), then KV-outer sparse
-attention with inversion and combine (msa_sparse_attn_prefill).  Inputs are
+scoring + block max + top-k, then KV-outer sparse attention with inversion and
+combine, as one msa_prefill call (the two halves of successive row windows
+overlapped on two streams); the same step as the two calls msa_select_blocks
++ msa_sparse_attn_prefill is timed with events for the stage breakdown.  Inputs are
 generated on the device before timing.  Printed: one JSON line with the
 prefill throughput (algorithmic TFLOP/s), the roofline of the dominant kernel
 (the fused select), the decode leg (B=16 x 256K cache, GB/s), the standalone
@@ -68,6 +70,103 @@ def ev():
     return torch.cuda.Event(enable_timing=True)
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo) and the threads this
+    process may run on."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return name, len(os.sched_getaffinity(0))
+
+
+def config_leg(name, steps, warmup, cpu=False):
+    """One more prefill workload (select + attention per step), timed like the
+    headline leg: per-step wall time between synchronisations, and the two
+    calls' times from events on the launch stream."""
+    w = WORKLOADS[name]
+    log("[bench] config leg", name, "generating")
+    inp = make_inputs(w, device="cuda")
+    qI, kI, q, K, V = inp["qI"], inp["kI"], inp["q"], inp["K"], inp["V"]
+    idx = torch.empty(w.B, w.G, w.T, w.k, dtype=torch.int32, device="cuda")
+    O = torch.empty_like(q)
+    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k, Bk=w.Bk)
+    ws = torch.empty(max(1, ops.workspace_bytes(ops.OP_ATTN_PREFILL, d)), dtype=torch.uint8,
+                     device="cuda")
+    nsel = ops.workspace_bytes(ops.OP_SELECT_BLOCKS, d)
+    ws_sel = torch.empty(nsel, dtype=torch.uint8, device="cuda") if nsel else None
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        ops.select_blocks(qI, kI, w.k, out=idx, workspace=ws_sel, Bk=w.Bk)
+        if evs is not None:
+            evs[1].record()
+        ops.sparse_attn_prefill(q, K, V, idx, out=O, workspace=ws, Bk=w.Bk)
+        if evs is not None:
+            evs[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[ev(), ev(), ev()] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    sel = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    att = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    del ws, ws_sel
+    wall1, equal = time_one_call(w, inp, idx, O, steps, warmup)
+    fl = acc.prefill_flops(w)
+    tf = fl["total"] / wall1 / 1e12
+    log("[bench] %s %.3f ms/step in one call, %.1f TFLOP/s (two calls %.3f ms: select %.3f, "
+        "attention %.3f)" % (name, wall1 * 1e3, tf, wall * 1e3, sel, att))
+    extra = {"cpu_baseline": cpu_full(w, inp)} if cpu else {}
+    del inp, qI, kI, q, K, V, idx, O
+    torch.cuda.empty_cache()
+    return {"workload": name, "steps": steps, "ms_per_step": wall1 * 1e3, "flops": fl["total"],
+            "TFLOPs": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+            "one_call_equal_two_calls": equal,
+            "two_calls": {"ms_per_step": wall * 1e3, "select_ms": sel, "attention_ms": att,
+                          "index_flops": fl["index"], "main_flops": fl["main"],
+                          "select_TFLOPs": fl["index"] / (sel * 1e-3) / 1e12,
+                          "attention_TFLOPs": fl["main"] / (att * 1e-3) / 1e12}, **extra}
+
+
+def time_one_call(w, inp, idx_ref, O_ref, steps, warmup):
+    """The whole prefill as one msa_prefill call per step (selection and
+    attention of successive row windows overlapped on two streams): wall time
+    per step between synchronisations, and whether its outputs equal the two
+    separate calls' (idx_ref, O_ref)."""
+    d = ops.dims(w.B, w.T, w.N, w.Hq, w.G, w.k, Bk=w.Bk)
+    ws1 = torch.empty(max(1, ops.workspace_bytes(ops.OP_PREFILL, d)), dtype=torch.uint8,
+                      device="cuda")
+    idx1, O1 = torch.empty_like(idx_ref), torch.empty_like(O_ref)
+
+    def one_call():
+        ops.prefill(inp["qI"], inp["kI"], inp["q"], inp["K"], inp["V"], w.k, out=(idx1, O1),
+                    workspace=ws1, Bk=w.Bk)
+
+    for _ in range(max(1, warmup)):
+        one_call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_call()
+    torch.cuda.synchronize()
+    wall1 = (time.perf_counter() - t0) / steps
+    equal = bool(torch.equal(idx1, idx_ref) and torch.equal(O1, O_ref))
+    del ws1, idx1, O1
+    return wall1, equal
+
+
 def with_block_size(w, args):
     """The workload with --block-size / --k applied (the same token budget by
     default: k = 2048 / Bk)."""
@@ -119,6 +218,12 @@ def prefill_leg(args):
     res = dict(w=w, inp=inp, idx=idx, O=O, wall=wall, sel_ms=sel_ms, att_ms=att_ms, flops=fl)
     log("[bench] prefill %.3f ms/step (select %.3f, attention %.3f)"
         % (1e3 * wall / args.steps, sel_ms.mean(), att_ms.mean()))
+    # the headline step: the same work as one call (msa_prefill)
+    del ws, ws_sel
+    wall1, res["one_call_equal"] = time_one_call(w, inp, idx, O, args.steps, args.warmup)
+    res["wall1"] = wall1 * args.steps
+    log("[bench] prefill, one call: %.3f ms/step (outputs equal to the two calls: %s)"
+        % (1e3 * wall1, res["one_call_equal"]))
     return res
 
 
@@ -295,7 +400,7 @@ def fp8_leg(args, pre):
             "note": "step = fp8 select + the bf16 attention of the same run"}
 
 
-def decode_leg(args, fp8=False):
+def decode_leg(args, fp8=False, cpu=False):
     w = WORKLOADS["decode_256k_b16"]
     if not fp8:  # the fp8 index calls take 128-key blocks
         w = with_block_size(w, args)
@@ -341,6 +446,8 @@ def decode_leg(args, fp8=False):
            "bytes": by["total"], "GBps": by["total"] / med / 1e3,
            "frac_hbm": by["total"] / med / 1e3 / PEAK_HBM_GBS,
            "note": "last-level cache flushed before each step"}
+    if cpu and not fp8:
+        out["cpu_baseline"] = cpu_full(w, inp)
     del inp, flush
     torch.cuda.empty_cache()
     return out
@@ -384,10 +491,34 @@ def cpu_leg(args, pre):
     parity = {"rows": int(n), "idx_exact": bool(np.array_equal(got, ref["idx"])),
               "O_max_abs": float(err.max()), "O_mean_abs": float(err.mean())}
     del rate
+    model, _ = cpu_model()
     return {"value": fl / sec / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle", "seconds": sec,
+            "cpu_model": model, "kind": "oracle", "seconds": sec,
             "sample": "%d query rows (all %d groups, %d heads) of %s: edge positions plus "
                       "uniform rows; fp64 plain C, OpenMP over rows" % (n, w.G, w.Hq, w.name)}, parity
+
+
+def cpu_full(w, inp):
+    """The oracle on every row of a small workload (the 2K prefill, the 256K x
+    16 decode step) from host copies of its inputs."""
+    import oracle
+    model, _ = cpu_model()
+    d = oracle.dims_of(w.B, w.T, w.N, w.Hq, w.G, w.d_h, w.d_I, w.Bk, w.k)
+    rb = np.repeat(np.arange(w.B), w.T)
+    rt = np.tile(np.arange(w.T), w.B)
+    host = {k: inp[k].cpu() for k in ("qI", "kI", "q", "K", "V")}
+    t0 = time.perf_counter()
+    oracle.forward(d, rb, rt, host["qI"][rb, rt], host["kI"], host["q"][rb, rt], host["K"],
+                   host["V"])
+    sec = time.perf_counter() - t0
+    if w.T == 1:
+        val, unit = acc.decode_bytes(w)["total"] / sec / 1e9, "GB/s"
+    else:
+        val, unit = acc.prefill_flops(w)["total"] / sec / 1e12, "TFLOP/s"
+    log("[bench] cpu oracle, every row of %s: %.2f s" % (w.name, sec))
+    return {"value": val, "unit": unit, "seconds": sec, "cores": oracle.threads(),
+            "cpu_model": model, "kind": "oracle",
+            "sample": "every row (%d) of %s; fp64 plain C, OpenMP over rows" % (rb.size, w.name)}
 
 
 def cpu_train_leg(args, pre):
@@ -452,7 +583,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--only", default="",
-                    help="prefill | decode | topk | fp8 | backward (skip the other legs)")
+                    help="prefill | decode | topk | fp8 | backward | configs (skip the other legs)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-reps", type=int, default=30)
@@ -461,6 +592,8 @@ def main():
     ap.add_argument("--k", type=int, default=None,
                     help="blocks per query and group (default: 2048 / block size)")
     ap.add_argument("--topk-reps", type=int, default=10)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 2K, 32K and 1M prefill legs")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -489,7 +622,8 @@ def main():
         pre = prefill_leg(args)
         w = pre["w"]
         fl = pre["flops"]
-        ms = 1e3 * pre["wall"] / args.steps
+        ms2 = 1e3 * pre["wall"] / args.steps
+        ms = 1e3 * pre["wall1"] / args.steps
         sel = float(pre["sel_ms"].mean())
         att = float(pre["att_ms"].mean())
         out.update({"value": fl["total"] / (ms * 1e-3) / 1e12, "ms_per_step": ms})
@@ -506,6 +640,11 @@ def main():
                            "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
                            "traffic": select_traffic() if fused else None,
                            "flops_per_launch": fl["index"], "avg_launch_ms": sel}
+        out["step"] = ("one msa_prefill call: fused select and KV-outer attention of "
+                       "successive row windows overlapped on two streams")
+        out["two_calls"] = {"ms_per_step": ms2, "TFLOPs": fl["total"] / (ms2 * 1e-3) / 1e12,
+                            "one_call_outputs_equal": pre["one_call_equal"],
+                            "calls": "msa_select_blocks, then msa_sparse_attn_prefill"}
         out["stages"] = {"select_ms": sel, "attention_ms": att,
                          "attention_TFLOPs": fl["main"] / (att * 1e-3) / 1e12,
                          "index_flops": fl["index"], "main_flops": fl["main"]}
@@ -534,9 +673,15 @@ def main():
             out["train_backward"]["cpu_baseline"] = cb["train_backward"]
         del pre
         torch.cuda.empty_cache()
+    if args.only in ("", "configs") and not args.no_configs and args.block_size == 128 \
+            and args.k is None:
+        out["prefill_configs"] = [config_leg("prefill_2k", max(args.steps, 20), args.warmup,
+                                             cpu=not args.no_cpu),
+                                  config_leg("prefill_32k", args.steps, args.warmup),
+                                  config_leg("prefill_1m", 3, 1)]
     if args.only in ("", "decode"):
         log("[bench] decode leg")
-        out["decode"] = decode_leg(args)
+        out["decode"] = decode_leg(args, cpu=not args.no_cpu and args.only == "")
         out["decode_fp8_index"] = decode_leg(args, fp8=True)
         if args.only == "decode":
             out.update({"value": out["decode"]["GBps"], "unit": "GB/s",

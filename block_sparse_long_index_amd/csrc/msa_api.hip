@@ -185,6 +185,47 @@ size_t train_ws(const msa_dims_t* d, int64_t window) {
   return rowdot_bytes(d) + lpx_bytes(d) + teach_bytes(d, window) + prefill_ws(d, window);
 }
 
+// The one-call prefill (msa_prefill): windows of about T / 8 query rows, at
+// least 16384 (smaller windows fill the attention's chunks too thinly to
+// gain from the overlap), a multiple of 4096, at most 64 windows; the
+// selection of a window overlaps the attention of the one before.
+constexpr int kMaxPipeWindows = 64;
+
+#ifndef MSA_PIPE_SPLIT
+#define MSA_PIPE_SPLIT 8
+#endif
+int64_t pipe_window(const msa_dims_t* d) {
+  int64_t w = (d->T + MSA_PIPE_SPLIT - 1) / MSA_PIPE_SPLIT;
+  if (w < 16384) w = 16384;
+  w = ((w + 4095) / 4096) * 4096;
+  if ((d->T + w - 1) / w > kMaxPipeWindows) w = (d->T + kMaxPipeWindows - 1) / kMaxPipeWindows;
+  return w < d->T ? w : d->T;
+}
+
+// Rows of block scores the one-call prefill materialises at a time (Bk < 128).
+int64_t pipe_score_rows(const msa_dims_t* d) {
+  const int64_t per_row = d->B * d->G * nblocks(d) * int64_t(sizeof(float));
+  int64_t r = (int64_t(1) << 30) / per_row;
+  if (r < 1) r = 1;
+  const int64_t w = pipe_window(d);
+  return r < w ? r : w;
+}
+
+size_t pipe_score_bytes(const msa_dims_t* d) {
+  if (d->Bk == 128) return 0;
+  const size_t b = static_cast<size_t>(pipe_score_rows(d) * d->B * d->G * nblocks(d)) * 4;
+  return (b + 255) & ~size_t(255);
+}
+
+// Workspace of the one-call prefill: the selection's item counters (one per
+// window), the score rows (Bk < 128), then the attention's.
+constexpr size_t kPipeCounterBytes = 512;
+static_assert(kPipeCounterBytes >= sizeof(int32_t) * msa::kMaxPrefillWindows, "counters");
+
+size_t pipe_ws(const msa_dims_t* d) {
+  return kPipeCounterBytes + pipe_score_bytes(d) + prefill_ws(d, pipe_window(d));
+}
+
 size_t decode_ws(const msa_dims_t* d) {
   return msa::attn_workspace_bytes(d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, d->Bk, true);
 }
@@ -222,6 +263,7 @@ size_t msa_workspace_bytes(int op, const msa_dims_t* d) {
     case MSA_OP_ATTN_BACKWARD: return backward_ws(d, default_window(d));
     case MSA_OP_INDEX_KL_BACKWARD: return index_kl_ws(d, default_window(d));
     case MSA_OP_TRAIN_BACKWARD: return train_ws(d, default_window(d));
+    case MSA_OP_PREFILL: return d->T > 1 ? pipe_ws(d) : 0;
   }
   return 0;
 }
@@ -358,6 +400,84 @@ int msa_sparse_attn_prefill(const msa_dims_t* d, const void* q, const void* K, c
                                                 d->G, d->k, d->Bk, w,
                                                 static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_prefill");
+  return MSA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Events of the one-call prefill's stream hand-offs: a pool per thread and
+// device, created on first use and reused by every later call of that thread
+// (a call enqueues all its records and waits before it returns, so a later
+// call's records cannot be confused with them).
+constexpr int kPoolDevices = 64;
+constexpr int kPoolEvents = kMaxPipeWindows + 2;  // windows (the last one may be cut) + 1
+struct EventPool {
+  bool ready;
+  hipEvent_t ev[kPoolEvents];
+};
+thread_local EventPool t_events[kPoolDevices];
+
+int pipe_events(hipEvent_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "msa_prefill: hipGetDevice");
+  if (dev < 0 || dev >= kPoolDevices)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_prefill: device %d >= %d", dev, kPoolDevices);
+  EventPool& p = t_events[dev];
+  if (!p.ready) {
+    for (int i = 0; i < kPoolEvents; ++i) {
+      e = hipEventCreateWithFlags(&p.ev[i], hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "msa_prefill: hipEventCreateWithFlags");
+    }
+    p.ready = true;
+  }
+  *out = p.ev;
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_prefill(const msa_dims_t* d, const void* qI, const void* kI, const void* q,
+                const void* K, const void* V, int32_t* idx, void* O, float* lse, void* ws,
+                size_t ws_bytes, void* stream, void* stream2) {
+  MSA_TRY(check_dims(d));
+  if (d->T < 2)
+    return fail(MSA_ERR_INVALID_ARGUMENT,
+                "msa_prefill needs T >= 2 (got %lld); one row is a decode step",
+                (long long)d->T);
+  MSA_TRY(check_ptr(qI, "qI"));
+  MSA_TRY(check_ptr(kI, "kI"));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(K, "K"));
+  MSA_TRY(check_ptr(V, "V"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  MSA_TRY(check_ptr(O, "O"));
+  if (lse) MSA_TRY(check_ptr(lse, "lse"));
+  MSA_TRY(check_ptr(ws, "ws"));
+  const size_t need = pipe_ws(d);
+  if (ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "msa_prefill needs %zu workspace bytes, got %zu",
+                need, ws_bytes);
+  const int64_t win = pipe_window(d);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStream_t st2 = stream2 ? static_cast<hipStream_t>(stream2) : st;
+  hipEvent_t* ev = nullptr;
+  if (st2 != st) MSA_TRY(pipe_events(&ev));
+  char* p = static_cast<char*>(ws);
+  int32_t* counters = reinterpret_cast<int32_t*>(p);
+  float* S = d->Bk == 128 ? nullptr : reinterpret_cast<float*>(p + kPipeCounterBytes);
+  msa::AttnWorkspace w;
+  msa::attn_workspace_carve(p + kPipeCounterBytes + pipe_score_bytes(d), win,
+                            stage_rows_for(d, win), d->N, d->G, d->Hq / d->G, d->k, d->Bk, false,
+                            &w);
+  const hipError_t e = msa::launch_prefill_pipelined(
+      qI, kI, q, K, V, idx, O, lse, d->B, d->T, d->N, d->Hq, d->G, d->k, d->Bk, win, S,
+      pipe_score_rows(d), counters, w, st, st2, ev, kPoolEvents);
+  if (e != hipSuccess) return hip_fail(e, "msa_prefill");
   return MSA_OK;
 }
 

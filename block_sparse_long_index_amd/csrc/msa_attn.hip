@@ -789,61 +789,179 @@ hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse, int64_t B,
                                int64_t T, int64_t N, int Hq, int G, int k, int Bk,
                                const AttnWorkspace& w, hipStream_t st) {
-  const int hg = Hq / G;
-  const int32_t NB = static_cast<int32_t>((N + Bk - 1) / Bk);
   for (int64_t b = 0; b < B; ++b) {
     for (int64_t t0 = 0; t0 < T; t0 += w.window) {
       const int64_t W = (T - t0) < w.window ? (T - t0) : w.window;
-      int32_t S = 0;
-      hipError_t e = launch_invert_window(idx, b, T, t0, W, N, G, k, Bk, w, &S, st);
+      const hipError_t e =
+          launch_attn_prefill_rows(q, K, V, idx, O, lse, b, T, t0, W, N, Hq, G, k, Bk, w, st);
       if (e != hipSuccess) return e;
-      const int64_t r0 = b * T + t0;
-      for (int g = 0; g < G; ++g) {
-        for (int32_t sub = 0; sub < S; ++sub) {
-          const int64_t si = static_cast<int64_t>(g) * S + sub;
-          const int32_t rl_base = sub * static_cast<int32_t>(w.stage_rows);
-          const int64_t rows = (W - rl_base) < w.stage_rows ? (W - rl_base) : w.stage_rows;
-          AttnArgs aa;
-          aa.q = static_cast<const u16*>(q);
-          aa.K = static_cast<const u16*>(K);
-          aa.V = static_cast<const u16*>(V);
-          aa.chunks = w.chunks + si * w.max_chunks;
-          aa.entries = w.entries;
-          aa.count = w.totals + 4 + si;
-          aa.opart = w.opart;
-          aa.lpart = w.lpart;
-          aa.T = T;
-          aa.N = N;
-          aa.r0 = r0;
-          aa.Hq = Hq;
-          aa.G = G;
-          aa.NB = NB;
-          aa.k = k;
-          aa.rl_base = rl_base;
-          aa.pgroups = 1;
-          aa.sink = static_cast<int32_t>(w.sink);
-          CombArgs ca;
-          ca.idx = idx;
-          ca.opart = w.opart;
-          ca.lpart = w.lpart;
-          ca.O = static_cast<u16*>(O);
-          ca.lse = lse;
-          ca.T = T;
-          ca.r0 = r0;
-          ca.rows = rows;
-          ca.Hq = Hq;
-          ca.G = G;
-          ca.k = k;
-          ca.rl_base = rl_base;
-          ca.group = g;
-          ca.pgroups = 1;
-          e = dispatch_hg(hg, Bk, aa, ca, w.max_chunks, st);
-          if (e != hipSuccess) return e;
-        }
-      }
     }
   }
   return hipSuccess;
+}
+
+hipError_t launch_attn_prefill_rows(const void* q, const void* K, const void* V,
+                                    const int32_t* idx, void* O, float* lse, int64_t b,
+                                    int64_t T, int64_t t0, int64_t W, int64_t N, int Hq, int G,
+                                    int k, int Bk, const AttnWorkspace& w, hipStream_t st) {
+  const int hg = Hq / G;
+  const int32_t NB = static_cast<int32_t>((N + Bk - 1) / Bk);
+  int32_t S = 0;
+  hipError_t e = launch_invert_window(idx, b, T, t0, W, N, G, k, Bk, w, &S, st);
+  if (e != hipSuccess) return e;
+  const int64_t r0 = b * T + t0;
+  for (int g = 0; g < G; ++g) {
+    for (int32_t sub = 0; sub < S; ++sub) {
+      const int64_t si = static_cast<int64_t>(g) * S + sub;
+      const int32_t rl_base = sub * static_cast<int32_t>(w.stage_rows);
+      const int64_t rows = (W - rl_base) < w.stage_rows ? (W - rl_base) : w.stage_rows;
+      AttnArgs aa;
+      aa.q = static_cast<const u16*>(q);
+      aa.K = static_cast<const u16*>(K);
+      aa.V = static_cast<const u16*>(V);
+      aa.chunks = w.chunks + si * w.max_chunks;
+      aa.entries = w.entries;
+      aa.count = w.totals + 4 + si;
+      aa.opart = w.opart;
+      aa.lpart = w.lpart;
+      aa.T = T;
+      aa.N = N;
+      aa.r0 = r0;
+      aa.Hq = Hq;
+      aa.G = G;
+      aa.NB = NB;
+      aa.k = k;
+      aa.rl_base = rl_base;
+      aa.pgroups = 1;
+      aa.sink = static_cast<int32_t>(w.sink);
+      CombArgs ca;
+      ca.idx = idx;
+      ca.opart = w.opart;
+      ca.lpart = w.lpart;
+      ca.O = static_cast<u16*>(O);
+      ca.lse = lse;
+      ca.T = T;
+      ca.r0 = r0;
+      ca.rows = rows;
+      ca.Hq = Hq;
+      ca.G = G;
+      ca.k = k;
+      ca.rl_base = rl_base;
+      ca.group = g;
+      ca.pgroups = 1;
+      e = dispatch_hg(hg, Bk, aa, ca, w.max_chunks, st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+// Stages 1-4 of a prefill, one window of query rows after another.  The
+// selection of window i runs on st; an event hands its rows to st2, where
+// their attention (inversion, KV-outer stages, combines) runs while st goes on
+// with the selection of window i + 1.  The selection is MFMA-bound and moves
+// little memory; the attention is bound by the memory traffic of its gathers
+// and partial results, so the two overlap on the chip.  st2 == st runs the
+// same launches in order on one stream.  ev: nwin + 1 events.
+// Workgroups (one per CU: 128 KB of LDS, 8 waves of 256 registers) of the
+// fused select's own launches while an attention window runs beside them.
+#ifndef MSA_PIPE_SELECT_WGS
+#define MSA_PIPE_SELECT_WGS 128
+#endif
+constexpr int kPipeSelectWGs = MSA_PIPE_SELECT_WGS;
+
+// Window boundaries of the pipelined prefill: windows of `win` rows, the
+// last one cut in two halves (its attention runs alone, after the last
+// selection, so a shorter one costs less).  Returns the number of windows.
+int prefill_windows(int64_t T, int64_t win, int64_t* bounds, int max_windows) {
+  int n = 0;
+  bounds[0] = 0;
+  for (int64_t t0 = 0; t0 < T && n < max_windows; t0 += win) {
+    const int64_t t1 = t0 + win < T ? t0 + win : T;
+    if (t1 == T && t1 - t0 >= 8192 && n + 2 <= max_windows) bounds[++n] = t0 + (t1 - t0) / 2;
+    bounds[++n] = t1;
+  }
+  return n;
+}
+
+// Stages 1-4 of a prefill, one window of query rows after another.  The
+// selection is MFMA-bound and moves little memory; the attention is bound by
+// the memory traffic of its gathers and partial results, so the two are run
+// side by side: window i's attention (inversion, KV-outer stages, combines)
+// on st2 while st selects the windows after it.  A fused-select workgroup
+// fills a CU by itself, so left alone its workgroups would take every CU an
+// attention launch frees and the two would merely alternate; instead each
+// window's selection is launched twice over one item counter: on st with at
+// most kPipeSelectWGs workgroups (the first window: no cap), and on st2 right
+// after the attention of the window before, uncapped, to take whatever items
+// are left once that attention is done.  Either launch may find the counter
+// exhausted.  With Bk < 128 (scores materialised window by window, then
+// ranked) and with st2 == st every launch runs in order on one stream.
+hipError_t launch_prefill_pipelined(const void* qI, const void* kI, const void* q, const void* K,
+                                    const void* V, int32_t* idx, void* O, float* lse, int64_t B,
+                                    int64_t T, int64_t N, int Hq, int G, int k, int Bk,
+                                    int64_t win, float* S, int64_t srows, int32_t* counters,
+                                    const AttnWorkspace& w, hipStream_t st, hipStream_t st2,
+                                    hipEvent_t* ev, int nev) {
+  int64_t bounds[kMaxPrefillWindows + 1];
+  const int maxw = nev - 1 < kMaxPrefillWindows ? nev - 1 : kMaxPrefillWindows;
+  const int nwin = prefill_windows(T, win, bounds, maxw);
+  if (bounds[nwin] != T) return hipErrorInvalidValue;
+  if (nwin == 1) st2 = st;  // nothing to overlap
+  hipError_t e = hipSuccess;
+  auto attend = [&](int i, hipStream_t s) {
+    hipError_t r = hipSuccess;
+    for (int64_t b = 0; b < B && r == hipSuccess; ++b)
+      r = launch_attn_prefill_rows(q, K, V, idx, O, lse, b, T, bounds[i],
+                                   bounds[i + 1] - bounds[i], N, Hq, G, k, Bk, w, s);
+    return r;
+  };
+  if (Bk != 128 || st2 == st) {
+    for (int i = 0; i < nwin && e == hipSuccess; ++i) {
+      const int64_t t0 = bounds[i], Tw = bounds[i + 1] - bounds[i];
+      if (Bk == 128) {
+        e = launch_index_tiles(false, false, qI, kI, nullptr, idx, B, T, t0, Tw, N, G, 128, k,
+                               st);
+      } else {
+        for (int64_t s0 = t0; s0 < t0 + Tw && e == hipSuccess; s0 += srows) {
+          const int64_t n = (t0 + Tw - s0) < srows ? (t0 + Tw - s0) : srows;
+          e = launch_index_tiles(true, false, qI, kI, S, nullptr, B, T, s0, n, N, G, Bk, k, st);
+          if (e == hipSuccess) {
+            const PagedCache none = {nullptr, nullptr, 0, 0};
+            e = launch_topk_rows(S, idx, B, T, s0, n, N, G, Bk, k, none, st);
+          }
+        }
+      }
+      if (e == hipSuccess && st2 != st) {
+        e = hipEventRecord(ev[i], st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(st2, ev[i], 0);
+      }
+      if (e == hipSuccess) e = attend(i, st2);
+    }
+  } else {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, counters,
+                       static_cast<int64_t>(nwin), 0);
+    e = hipGetLastError();
+    for (int i = 0; i < nwin && e == hipSuccess; ++i) {
+      e = launch_index_tiles(false, false, qI, kI, nullptr, idx, B, T, bounds[i],
+                             bounds[i + 1] - bounds[i], N, G, 128, k, st,
+                             i == 0 ? 0 : kPipeSelectWGs, counters + i);
+      if (e == hipSuccess) e = hipEventRecord(ev[i], st);
+    }
+    for (int i = 0; i < nwin && e == hipSuccess; ++i) {
+      e = hipStreamWaitEvent(st2, ev[i], 0);
+      if (e == hipSuccess) e = attend(i, st2);
+      if (e == hipSuccess && i + 1 < nwin)
+        e = launch_index_tiles(false, false, qI, kI, nullptr, idx, B, T, bounds[i + 1],
+                               bounds[i + 2] - bounds[i + 1], N, G, 128, k, st2, 0,
+                               counters + i + 1);
+    }
+  }
+  if (e == hipSuccess && st2 != st) {
+    e = hipEventRecord(ev[nwin], st2);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, ev[nwin], 0);
+  }
+  return e;
 }
 
 // ---------------------------------------------------------------------------

@@ -20,10 +20,14 @@ struct PagedCache {
 // Stages 1+2 (write S, blocks of Bk keys) or stages 1-3 fused (write idx,
 // Bk = 128) for the query rows t0 .. t0 + Tw - 1 of T; S holds those rows
 // only ([B, G, Tw, NB]).  fp8: q^I and k^I are e4m3 bytes instead of bf16
-// (Bk = 128).
+// (Bk = 128).  wgs > 0: at most that many workgroups, each looping over the
+// work items (the selection then occupies at most wgs CUs).  counter
+// (non-null, zero before the first of them): the workgroups take items from
+// it, so several launches over the same rows share the items.
 hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const void* kI,
                               float* S, int32_t* idx, int64_t B, int64_t T, int64_t t0,
-                              int64_t Tw, int64_t N, int G, int Bk, int k, hipStream_t st);
+                              int64_t Tw, int64_t N, int G, int Bk, int k, hipStream_t st,
+                              int wgs = 0, int32_t* counter = nullptr);
 
 // Stages 1+2 for T == 1: streams the index keys, S is [B, G, 1, NB] with NB
 // blocks of Bk keys (fp8 and paged caches: Bk = 128).
@@ -124,6 +128,26 @@ hipError_t launch_attn_prefill(const void* q, const void* K, const void* V,
                                const int32_t* idx, void* O, float* lse,
                                int64_t B, int64_t T, int64_t N, int Hq, int G,
                                int k, int Bk, const AttnWorkspace& w, hipStream_t st);
+// Stage 4 for the query rows [t0, t0 + W) of sequence b only (W <= w.window):
+// their inversion, then their stages.  Reads only those rows' idx.
+hipError_t launch_attn_prefill_rows(const void* q, const void* K, const void* V,
+                                    const int32_t* idx, void* O, float* lse, int64_t b,
+                                    int64_t T, int64_t t0, int64_t W, int64_t N, int Hq, int G,
+                                    int k, int Bk, const AttnWorkspace& w, hipStream_t st);
+
+// Stages 1-4 of a prefill in windows of about `win` query rows (all
+// sequences): selection of window i on st, then its attention on st2 after an
+// event, so that window i's attention overlaps the later windows' selection.
+// Bk < 128: S holds the scores of `srows` rows of every sequence.  counters:
+// kMaxPrefillWindows ints of scratch.  w: an attention workspace whose window
+// is >= win.  ev: nev >= ceil(T / win) + 2 events (unused when st2 == st).
+constexpr int kMaxPrefillWindows = 72;
+hipError_t launch_prefill_pipelined(const void* qI, const void* kI, const void* q, const void* K,
+                                    const void* V, int32_t* idx, void* O, float* lse, int64_t B,
+                                    int64_t T, int64_t N, int Hq, int G, int k, int Bk,
+                                    int64_t win, float* S, int64_t srows, int32_t* counters,
+                                    const AttnWorkspace& w, hipStream_t st, hipStream_t st2,
+                                    hipEvent_t* ev, int nev);
 
 hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse,

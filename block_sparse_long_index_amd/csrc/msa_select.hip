@@ -31,9 +31,12 @@ namespace msa {
 // its q^I fragments stay in registers for the whole kernel.  k^I blocks
 // (32 KB) stream through double-buffered LDS, shared by all waves.
 // ---------------------------------------------------------------------------
+#ifndef MSA_TILE_COLS
+#define MSA_TILE_COLS 512
+#endif
 template <int G>
 struct TileShape {
-  static constexpr int QT = (512 / G) < 128 ? (512 / G) : 128;
+  static constexpr int QT = (MSA_TILE_COLS / G) < 128 ? (MSA_TILE_COLS / G) : 128;
   static constexpr int NCOL = QT * G;
   static constexpr int NW = NCOL / 64;
   static constexpr int NT = NW * 64;
@@ -47,7 +50,10 @@ struct TileArgs {
   int64_t T, N;
   int64_t t0, Tw;   // this launch's query rows: t0 .. t0 + Tw - 1
   int64_t tile_hi;  // last position tile; workgroups run heaviest first
+  int64_t nitems;   // (sequence, position tile) work items
+  int32_t* counter; // non-null: workgroups take items from this counter
   int32_t NB, k, B;
+  int32_t wgs;      // workgroups to launch (0: one per item)
 };
 
 // Insert (x, xi) into a list sorted by score descending, equal scores kept in
@@ -93,9 +99,19 @@ __device__ __forceinline__ void sort_ascending(int (&v)[CAP]) {
 // BK: the block size of the scores written (WRITE_S): each 128-key chunk
 // holds 128 / BK blocks, one per BK / 32 key tiles.  The fused selection
 // (!WRITE_S) takes BK = 128.
-template <int G, int CAP, bool WRITE_S, bool F8, int BK = 128>
-__global__ void __launch_bounds__(TileShape<G>::NT)
-index_tile_kernel(TileArgs a) {
+template <int G, bool F8>
+struct TileRing {
+  // The LDS ring of k^I blocks of the tile body (described there).
+  static constexpr int D = TileShape<G>::NT < 512 ? 1 : (F8 ? 4 : 2);
+  static constexpr int R = 2 * D;
+  static constexpr int PITCH = F8 ? 144 : 256;  // LDS row pitch
+};
+
+// One work item (sequence b = item % B, position tile tile_hi - item / B).
+template <int G, int CAP, bool WRITE_S, bool F8, int BK>
+__device__ __forceinline__ void index_tile(
+    const TileArgs& a, int64_t item,
+    unsigned char (*kbuf)[128 * TileRing<G, F8>::PITCH]) {
   static_assert(BK == 32 || BK == 64 || BK == 128, "block of 32, 64 or 128 keys");
   static_assert(WRITE_S || BK == 128, "the fused selection takes 128-key blocks");
   constexpr int TPB = BK / 32;   // key tiles per block
@@ -116,15 +132,15 @@ index_tile_kernel(TileArgs a) {
   // every wave after it read the block D back before that buffer is reused.
   // D = 2 for bf16 (4 x 32 KB of LDS), 4 for fp8 (8 x 18 KB); workgroups of
   // fewer than 8 waves (G < 4) keep D = 1 so that several fit on a CU.
-  constexpr int D = NT < 512 ? 1 : (F8 ? 4 : 2);
-  constexpr int R = 2 * D;
-  __shared__ __align__(16) unsigned char kbuf[R][128 * PITCH];
+  constexpr int D = TileRing<G, F8>::D;
+  constexpr int R = TileRing<G, F8>::R;
+  static_assert(PITCH == TileRing<G, F8>::PITCH, "LDS pitch");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int b = blockIdx.x % a.B;
-  const int64_t tile = a.tile_hi - blockIdx.x / a.B;
+  const int b = static_cast<int>(item % a.B);
+  const int64_t tile = a.tile_hi - item / a.B;
   const int64_t P0 = tile * QT;
   const int64_t L = P0 / kBlock;
   const int64_t row0 = a.N - a.T;
@@ -401,10 +417,38 @@ index_tile_kernel(TileArgs a) {
   }
 }
 
+// Workgroups take work items (sequence, position tile) heaviest first; with
+// fewer workgroups than items (a.wgs > 0) each loops over every wgs-th item,
+// so that the selection keeps to that many CUs and leaves the others to work
+// on another stream.
+template <int G, int CAP, bool WRITE_S, bool F8, int BK = 128>
+__global__ void __launch_bounds__(TileShape<G>::NT)
+index_tile_kernel(TileArgs a) {
+  __shared__ __align__(16) unsigned char kbuf[TileRing<G, F8>::R][128 * TileRing<G, F8>::PITCH];
+  if (a.counter) {
+    // items are taken from a counter shared with other launches of the same
+    // rows (see launch_index_tiles)
+    __shared__ int item_s;
+    for (;;) {
+      if (threadIdx.x == 0) item_s = atomicAdd(a.counter, 1);
+      __syncthreads();
+      const int64_t item = item_s;
+      if (item >= a.nitems) break;  // uniform: every thread read the same value
+      index_tile<G, CAP, WRITE_S, F8, BK>(a, item, kbuf);
+      __syncthreads();  // item_s is read; the next item refills the ring buffers
+    }
+    return;
+  }
+  for (int64_t item = blockIdx.x; item < a.nitems; item += gridDim.x) {
+    index_tile<G, CAP, WRITE_S, F8, BK>(a, item, kbuf);
+    __syncthreads();  // the next item refills the ring buffers
+  }
+}
+
 template <int G, bool WS, bool F8, int BK>
 static hipError_t launch_tiles_cap(const TileArgs& a, int64_t ntiles, hipStream_t st) {
   using TS = TileShape<G>;
-  const int64_t grid = ntiles * a.B;
+  const int64_t grid = a.wgs > 0 && a.wgs < a.nitems ? a.wgs : a.nitems;
   const dim3 gd(static_cast<unsigned>(grid)), bd(TS::NT);
   if (WS || a.k <= 4) {
     hipLaunchKernelGGL((index_tile_kernel<G, 3, WS, F8, BK>), gd, bd, 0, st, a);
@@ -431,11 +475,12 @@ static hipError_t launch_tiles_g(const TileArgs& a, int G, int64_t ntiles, hipSt
   return hipErrorInvalidValue;
 }
 
-static int tile_queries(int G) { return (512 / G) < 128 ? (512 / G) : 128; }
+static int tile_queries(int G) { return (MSA_TILE_COLS / G) < 128 ? (MSA_TILE_COLS / G) : 128; }
 
 hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const void* kI,
                               float* S, int32_t* idx, int64_t B, int64_t T, int64_t t0,
-                              int64_t Tw, int64_t N, int G, int Bk, int k, hipStream_t st) {
+                              int64_t Tw, int64_t N, int G, int Bk, int k, hipStream_t st,
+                              int wgs, int32_t* counter) {
   const int QT = tile_queries(G);
   TileArgs a;
   a.qI = static_cast<const u16*>(qI);
@@ -452,6 +497,9 @@ hipError_t launch_index_tiles(bool write_scores, bool fp8, const void* qI, const
   const int64_t tile_lo = (N - T + t0) / QT;
   a.tile_hi = (N - T + t0 + Tw - 1) / QT;
   const int64_t ntiles = a.tile_hi - tile_lo + 1;
+  a.nitems = ntiles * B;
+  a.wgs = wgs;
+  a.counter = counter;
   if (Bk != 128 && (fp8 || !write_scores)) return hipErrorInvalidValue;
   if (fp8) {
     if (write_scores) return launch_tiles_g<true, true, 128>(a, G, ntiles, st);

@@ -25,6 +25,7 @@ OP_ATTN_DECODE = 4
 OP_ATTN_BACKWARD = 5
 OP_INDEX_KL_BACKWARD = 6
 OP_TRAIN_BACKWARD = 7
+OP_PREFILL = 8
 
 # Every function the C header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -39,6 +40,7 @@ _SIGS = {
     "msa_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
     "msa_sparse_attn_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
+    "msa_prefill": (ctypes.c_int, [_P] * 10 + [ctypes.c_size_t, _P, _P]),
     "msa_sparse_attn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                 _P, ctypes.c_size_t, _P]),
     "msa_train_backward": (ctypes.c_int, [_P] * 17 + [ctypes.c_size_t, _P]),
@@ -187,6 +189,58 @@ def select_blocks_from_scores(S, k, N, out=None, Bk=128):
     _check(lib().msa_select_blocks_from_scores(ctypes.byref(d), _ptr(S), _ptr(idx), _stream()),
            "msa_select_blocks_from_scores")
     return idx
+
+
+_side_streams = {}
+
+
+def side_stream(device=None):
+    """A second stream of the device (created once, default priority) for
+    the attention windows of prefill()."""
+    dev = torch.cuda.current_device() if device is None else device
+    if dev not in _side_streams:
+        _side_streams[dev] = torch.cuda.Stream(device=dev)
+    return _side_streams[dev]
+
+
+def prefill(qI, kI, q, K, V, k, return_lse=False, out=None, workspace=None, Bk=128,
+            overlap=True):
+    """Stages 1-4 in one call (msa_prefill): selection and attention of
+    successive row windows overlapped on the current stream and a second
+    one (overlap=False: all on the current stream).  Returns (idx, O) or
+    (idx, O, lse); out = (idx, O) or (idx, O, lse) to write into."""
+    B, T, G, dI = qI.shape
+    _, _, Hq, dh = q.shape
+    N = kI.shape[1]
+    _index_inputs(qI, kI)
+    if qI.dtype != torch.bfloat16:
+        raise ValueError("prefill takes bf16 index inputs")
+    _need(q, "q", torch.bfloat16, (B, T, Hq, dh))
+    _need(K, "K", torch.bfloat16, (B, G, N, dh))
+    _need(V, "V", torch.bfloat16, (B, G, N, dh))
+    d = dims(B, T, N, Hq, G, k, d_h=dh, d_I=dI, Bk=Bk)
+    if out is not None:
+        idx, O = out[0], out[1]
+        lse = out[2] if len(out) > 2 else None
+    else:
+        idx = torch.empty(B, G, T, k, dtype=torch.int32, device=q.device)
+        O = torch.empty_like(q)
+        lse = None
+    if return_lse and lse is None:
+        lse = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    _need(idx, "idx", torch.int32, (B, G, T, k))
+    _need(O, "O", torch.bfloat16, q.shape)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq, T))
+    ws, nbytes = _workspace(OP_PREFILL, d, workspace)
+    s2 = ctypes.c_void_p(side_stream(q.device.index).cuda_stream) if overlap else None
+    _check(lib().msa_prefill(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(q), _ptr(K), _ptr(V),
+                             _ptr(idx), _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream(), s2),
+           "msa_prefill")
+    if ws is not None and workspace is None and overlap:
+        # the side stream still reads the temporary workspace after this returns
+        ws.record_stream(side_stream(q.device.index))
+    return (idx, O, lse) if return_lse else (idx, O)
 
 
 def sparse_attn_prefill(q, K, V, idx, return_lse=False, out=None, workspace=None, Bk=128):

@@ -94,7 +94,8 @@ enum {
     MSA_OP_ATTN_DECODE = 4,
     MSA_OP_ATTN_BACKWARD = 5,
     MSA_OP_INDEX_KL_BACKWARD = 6,
-    MSA_OP_TRAIN_BACKWARD = 7
+    MSA_OP_TRAIN_BACKWARD = 7,
+    MSA_OP_PREFILL = 8
 };
 
 /*
@@ -178,6 +179,33 @@ int msa_sparse_attn_prefill(const msa_dims_t *dims, const void *q,
                             const void *K, const void *V, const int32_t *idx,
                             void *O, float *lse, void *ws, size_t ws_bytes,
                             void *stream);
+
+/*
+ * Stages 1 to 4 of a prefill in one call: msa_select_blocks, then
+ * msa_sparse_attn_prefill, on the same arguments and with the same results
+ * (idx bit for bit, O and lse as the prefill call computes them), scheduled
+ * window by window of query rows so that the two halves overlap.  The study
+ * notes (section 5-3 on efficiency) name the selection and the gather and
+ * combine of the sparse attention as the overheads of a prefill; here the
+ * fused selection of window i + 1 (bound by the matrix cores) runs on
+ * `stream` while the attention of window i (bound by the memory traffic of
+ * its gathers and partial results) runs on `stream2`.
+ *   qI, kI, q, K, V, idx, O, lse   as for msa_select_blocks and
+ *                                  msa_sparse_attn_prefill (idx is written)
+ *   ws / ws_bytes  >= msa_workspace_bytes(MSA_OP_PREFILL)
+ *   stream         the caller's stream: everything is ordered after the work
+ *                  already on it, and the results are ready when it reaches
+ *                  the point where the call returned
+ *   stream2        a second stream of the same device for the attention
+ *                  windows (it waits for each window's selection; `stream`
+ *                  waits for its last window), or NULL: every launch in
+ *                  order on `stream`
+ * Needs T >= 2.  Any supported Bk (with Bk < 128 the selection materialises
+ * the scores of up to 1 GB of rows at a time in the workspace).
+ */
+int msa_prefill(const msa_dims_t *dims, const void *qI, const void *kI, const void *q,
+                const void *K, const void *V, int32_t *idx, void *O, float *lse, void *ws,
+                size_t ws_bytes, void *stream, void *stream2);
 
 /*
  * Backward of stage 4 for training: the gradients of exact softmax attention
