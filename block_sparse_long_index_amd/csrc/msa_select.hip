@@ -56,27 +56,34 @@ struct TileArgs {
   int32_t wgs;      // workgroups to launch (0: one per item)
 };
 
+// max(m, the 16 values of an accumulator tile) as a tree of three-input maxima
+// (v_max3_f32), depth three.
+__device__ __forceinline__ float max16(float m, const f32x16& c) {
+  const float a = max3(c[0], c[1], c[2]), b = max3(c[3], c[4], c[5]);
+  const float d = max3(c[6], c[7], c[8]), e = max3(c[9], c[10], c[11]);
+  const float f = max3(c[12], c[13], c[14]);
+  return max3(m, max3(a, b, d), max3(e, f, c[15]));
+}
+
 // Insert (x, xi) into a list sorted by score descending, equal scores kept in
-// arrival order; the caller guarantees x > ts[CAP-1].
+// arrival order (an entry already in the list stays ahead of an equal x; x
+// below the last entry leaves the list unchanged).  The new score at position
+// i is the median of (ts[i], ts[i-1], x), one v_med3 per entry; an index moves
+// with its score: position i takes x's index where x beats ts[i] but not
+// ts[i-1], and ts[i-1]'s where it beats both.
 template <int CAP>
 __device__ __forceinline__ void topk_insert(float (&ts)[CAP], int (&ti)[CAP],
                                             float x, int xi) {
+  bool c[CAP];
 #pragma unroll
-  for (int i = CAP - 1; i >= 0; --i) {
-    const bool stay = ts[i] >= x;
-    float ns;
-    int ni;
-    if (i > 0) {
-      const bool shift = !(ts[i - 1] >= x);
-      ns = stay ? ts[i] : (shift ? ts[i - 1] : x);
-      ni = stay ? ti[i] : (shift ? ti[i - 1] : xi);
-    } else {
-      ns = stay ? ts[i] : x;
-      ni = stay ? ti[i] : xi;
-    }
-    ts[i] = ns;
-    ti[i] = ni;
+  for (int i = 0; i < CAP; ++i) c[i] = x > ts[i];
+#pragma unroll
+  for (int i = CAP - 1; i > 0; --i) {
+    ti[i] = c[i] ? (c[i - 1] ? ti[i - 1] : xi) : ti[i];
+    ts[i] = __builtin_amdgcn_fmed3f(ts[i], ts[i - 1], x);
   }
+  ti[0] = c[0] ? xi : ti[0];
+  ts[0] = fmaxf(ts[0], x);
 }
 
 template <int CAP>
@@ -226,23 +233,43 @@ __device__ __forceinline__ void index_tile(
   // one) and nothing uses them before store_block: a use right after a load
   // under a branch, such as the zeroing select, makes the compiler wait for
   // the load at the branch's end, before the block's products.
+  // Thread chunk j of a block is row kr0 + j * NT / CPR, 16-B chunk kc0: its
+  // offsets are per-thread constants plus the block's base; only the block
+  // holding key N - 1 (the last one) needs its rows clamped (loads) and
+  // zeroed (stores), which is one uniform branch per block.
+  const int kr0 = tid / CPR, kc0 = tid % CPR;
+  constexpr int RS = NT / CPR;  // rows between a thread's chunks
   auto load_block = [&](int64_t kb) {
+    const unsigned char* src = kbase + kb * (kBlock * ROWB);
+    const int64_t last = a.N - 1 - kb * kBlock;  // last row of the block inside N
+    // unsigned 32-bit offsets from a uniform base: scalar-base loads
+    if (last >= kBlock - 1) {
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int i = tid + j * NT;
-      const int r = i / CPR, c = i % CPR;
-      const int64_t key = kb * kBlock + r;
-      pf[j] = ld16(kbase + (key < a.N ? key : a.N - 1) * ROWB + c * 16);
+      for (int j = 0; j < PF; ++j)
+        pf[j] = ld16(src + static_cast<uint32_t>((kr0 + RS * j) * ROWB + kc0 * 16));
+    } else {
+      const int lr = static_cast<int>(last);
+#pragma unroll
+      for (int j = 0; j < PF; ++j)
+        pf[j] = ld16(src + static_cast<uint32_t>(min(kr0 + RS * j, lr) * ROWB + kc0 * 16));
     }
   };
   auto store_block = [&](int buf, int64_t kb) {
+    unsigned char* dst = kbuf[buf];
+    const int64_t last = a.N - 1 - kb * kBlock;
+    if (last >= kBlock - 1) {
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int i = tid + j * NT;
-      const int r = i / CPR, c = i % CPR;
-      const int64_t key = kb * kBlock + r;
-      *reinterpret_cast<uint4*>(&kbuf[buf][F8 ? r * PITCH + c * 16 : swz(r, c)]) =
-          key < a.N ? pf[j] : make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < PF; ++j) {
+        const int r = kr0 + RS * j;
+        *reinterpret_cast<uint4*>(&dst[F8 ? r * PITCH + kc0 * 16 : swz(r, kc0)]) = pf[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int r = kr0 + RS * j;
+        *reinterpret_cast<uint4*>(&dst[F8 ? r * PITCH + kc0 * 16 : swz(r, kc0)]) =
+            r <= last ? pf[j] : make_uint4(0, 0, 0, 0);
+      }
     }
   };
 
@@ -267,15 +294,16 @@ __device__ __forceinline__ void index_tile(
     // two column tiles.
     typedef uint4 KFrag[8];
     auto frags = [&](int kt, KFrag& av) {
-      const int r = kt * 32 + l32;
       if constexpr (F8) {
-        const unsigned char* rp = buf + r * PITCH + 32 * half;
+        const unsigned char* rp = buf + (kt * 32 + l32) * PITCH + 32 * half;
 #pragma unroll
         for (int s = 0; s < 4; ++s) av[s] = *reinterpret_cast<const uint4*>(rp + 64 * (s >> 1) + 16 * (s & 1));
       } else {
+        // rows kt * 32 + l32 share l32's swizzle (32 is a multiple of 16):
+        // the lane's offsets plus kt * 32 rows
 #pragma unroll
         for (int s = 0; s < 8; ++s)
-          av[s] = *reinterpret_cast<const uint4*>(&buf[swz(r, 2 * s + half)]);
+          av[s] = *reinterpret_cast<const uint4*>(&buf[kt * 32 * 256 + swz(l32, 2 * s + half)]);
       }
     };
     auto tile = [&](const KFrag& av, f32x16& c0, f32x16& c1) {
@@ -309,11 +337,8 @@ __device__ __forceinline__ void index_tile(
           if (off > lim1) c1[e] = -INFINITY;
         }
       }
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        m0 = max3(m0, c0[e], c0[e + 1]);
-        m1 = max3(m1, c1[e], c1[e + 1]);
-      }
+      m0 = max16(m0, c0);
+      m1 = max16(m1, c1);
       if constexpr (WRITE_S && BK < 128) {
         // the last tile of a block: its score, then start the next block
         if ((kt + 1) % TPB == 0) {
@@ -432,7 +457,8 @@ index_tile_kernel(TileArgs a) {
     for (;;) {
       if (threadIdx.x == 0) item_s = atomicAdd(a.counter, 1);
       __syncthreads();
-      const int64_t item = item_s;
+      // the same value in every lane: keep it (and all that derives from it) scalar
+      const int64_t item = __builtin_amdgcn_readfirstlane(item_s);
       if (item >= a.nitems) break;  // uniform: every thread read the same value
       index_tile<G, CAP, WRITE_S, F8, BK>(a, item, kbuf);
       __syncthreads();  // item_s is read; the next item refills the ring buffers

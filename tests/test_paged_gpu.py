@@ -76,6 +76,9 @@ CASES = [
     ("mixed", [1000, 129, 3000, 1], 64, 8, 16),
     ("block_edges", [128, 256, 127, 255, 2048], 16, 4, 4),
     ("hg16_g1", [700, 5], 16, 1, 8),
+    # 32 sequences x 4 groups: enough (sequence, group) pairs for the one-pass
+    # decode attention (one workgroup per pair)
+    ("many_seqs", [1 + (i * 977) % 3100 for i in range(32)], 32, 4, 16),
 ]
 
 

@@ -157,6 +157,31 @@ def test_decode_small(N, Hq, G):
                  tag="decode_small")
 
 
+@pytest.mark.parametrize("B,N,Hq,G,k,Bk", [
+    (16, 5000, 64, 8, 16, 128),   # ragged last block (8 keys)
+    (64, 300, 16, 2, 16, 128),    # 3 blocks: most slots unused
+    (32, 1000, 32, 4, 7, 128),    # odd k: the two slot parities differ in count
+    (128, 129, 8, 1, 4, 128),     # G = 1, one key in the last block
+    (16, 3000, 128, 8, 16, 128),  # 16 heads per group
+    (64, 2500, 16, 2, 32, 64),    # 64-key blocks: two key quarters past each block
+    (32, 2100, 32, 4, 64, 32),    # 32-key blocks
+    (128, 1, 8, 1, 4, 128),       # one token
+])
+def test_decode_one_pass(B, N, Hq, G, k, Bk):
+    """Batches with at least 128 (sequence, group) pairs take the one-pass
+    decode attention (a workgroup per pair walks its selected blocks and
+    writes the normalised output): every sequence against the oracle."""
+    w = Workload("decode_rows", B=B, T=1, N=N, Hq=Hq, G=G, k=k, Bk=Bk, seed=7 + N + B)
+    inp = make_inputs(w, device="cuda")
+    idx = ops.select_blocks(inp["qI"], inp["kI"], w.k, Bk=Bk)
+    O, lse = ops.sparse_attn_decode(inp["q"][:, 0].contiguous(), inp["K"], inp["V"], idx,
+                                    return_lse=True, Bk=Bk)
+    torch.cuda.synchronize()
+    check_invariants(w, idx)
+    compare_rows(w, inp, idx, O, lse, np.arange(B), np.zeros(B, dtype=np.int64),
+                 tag="decode_rows")
+
+
 def test_decode_equals_prefill_last_row():
     """decode over a cache of length L == the last row of a prefill over L."""
     N = 1337
