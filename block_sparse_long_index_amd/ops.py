@@ -14,7 +14,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmsa.so")
+# MSA_LIB_PATH: another build of the same library (the sanitizer test loads a
+# host-sanitized copy); there is no other implementation to fall back to.
+LIB_PATH = os.environ.get("MSA_LIB_PATH") or os.path.join(_PKG, "libmsa.so")
 
 MSA_OK = 0
 OP_INDEX_SCORES = 0

@@ -287,15 +287,16 @@ def forward(*a, **kw):
     return default().forward(*a, **kw)
 
 
-def build_variant(source_text: str, out_dir: str, name: str) -> str:
-    """Compile a modified copy of the oracle source (used by the tests that
-    check that the pins catch planted mistakes).  Returns the .so path."""
+def build_variant(source_text: str, out_dir: str, name: str, extra_flags=()) -> str:
+    """Compile a copy of the oracle source, possibly modified (the tests that
+    check that the pins catch planted mistakes) or with extra flags (the
+    sanitizer build).  Returns the .so path."""
     src = os.path.join(out_dir, name + ".c")
     so = os.path.join(out_dir, name + ".so")
     with open(src, "w") as f:
         f.write(source_text)
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC",
-                           "-shared", src, "-o", so, "-lm"])
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC"] + list(extra_flags) +
+                          ["-shared", src, "-o", so, "-lm"])
     return so
 
 

@@ -167,10 +167,10 @@ def test_decode_small(N, Hq, G):
     (32, 2100, 32, 4, 64, 32),    # 32-key blocks
     (128, 1, 8, 1, 4, 128),       # one token
 ])
-def test_decode_one_pass(B, N, Hq, G, k, Bk):
-    """Batches with at least 128 (sequence, group) pairs take the one-pass
-    decode attention (a workgroup per pair walks its selected blocks and
-    writes the normalised output): every sequence against the oracle."""
+def test_decode_many_pairs(B, N, Hq, G, k, Bk):
+    """Batches of many (sequence, group) pairs with short and ragged caches,
+    unused slots, odd k and every block size: every sequence against the
+    oracle."""
     w = Workload("decode_rows", B=B, T=1, N=N, Hq=Hq, G=G, k=k, Bk=Bk, seed=7 + N + B)
     inp = make_inputs(w, device="cuda")
     idx = ops.select_blocks(inp["qI"], inp["kI"], w.k, Bk=Bk)
