@@ -498,9 +498,7 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
     }
     float m = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) m = max3(m, sacc[kt][i], sacc[kt][i + 1]);
+    for (int kt = 0; kt < NKT; ++kt) m = max16(m, sacc[kt]);
     m = fmaxf(m, __shfl_xor(m, 32));
     const float mc = m * qscale;
 

@@ -12,6 +12,7 @@ typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kHeadDim = 128;   // d_h and d_I supported by these kernels
@@ -49,8 +50,7 @@ __device__ __forceinline__ u16 f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -130,6 +130,15 @@ __device__ __forceinline__ int64_t paged_page(const PagedCache& pc, int64_t b, i
 
 __device__ __forceinline__ float max3(float a, float b, float c) {
   return fmaxf(a, fmaxf(b, c));
+}
+
+// max(m, the 16 values of an accumulator tile) as a tree of three-input maxima
+// (v_max3_f32), depth three.
+__device__ __forceinline__ float max16(float m, const f32x16& c) {
+  const float a = max3(c[0], c[1], c[2]), b = max3(c[3], c[4], c[5]);
+  const float d = max3(c[6], c[7], c[8]), e = max3(c[9], c[10], c[11]);
+  const float f = max3(c[12], c[13], c[14]);
+  return max3(m, max3(a, b, d), max3(e, f, c[15]));
 }
 
 }  // namespace msa

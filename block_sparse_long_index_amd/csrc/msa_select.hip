@@ -56,15 +56,6 @@ struct TileArgs {
   int32_t wgs;      // workgroups to launch (0: one per item)
 };
 
-// max(m, the 16 values of an accumulator tile) as a tree of three-input maxima
-// (v_max3_f32), depth three.
-__device__ __forceinline__ float max16(float m, const f32x16& c) {
-  const float a = max3(c[0], c[1], c[2]), b = max3(c[3], c[4], c[5]);
-  const float d = max3(c[6], c[7], c[8]), e = max3(c[9], c[10], c[11]);
-  const float f = max3(c[12], c[13], c[14]);
-  return max3(m, max3(a, b, d), max3(e, f, c[15]));
-}
-
 // Insert (x, xi) into a list sorted by score descending, equal scores kept in
 // arrival order (an entry already in the list stays ahead of an equal x; x
 // below the last entry leaves the list unchanged).  The new score at position
