@@ -7,8 +7,9 @@ combine, as one msa_prefill call (the two halves of successive row windows
 overlapped on two streams); the same step as the two calls msa_select_blocks
 + msa_sparse_attn_prefill is timed with events for the stage breakdown.  Inputs are
 generated on the device before timing.  Printed: one JSON line with the
-prefill throughput (algorithmic TFLOP/s), the roofline of the dominant kernel
-(the fused select), the decode leg (B=16 x 256K cache, GB/s), the standalone
+prefill throughput (algorithmic TFLOP/s), the roofline of the kernel that takes
+the most time per step (and of the other stage kernels; per-kernel times from
+the library's own HIP events on each launch stream), the decode leg (B=16 x 256K cache, GB/s), the standalone
 top-k leg on the materialised 128K scores (us), and the CPU oracle baseline
 on a bounded sample of rows.
 
@@ -44,26 +45,58 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def select_traffic():
-    """Bytes per launch of the fused select kernel from the committed counter
-    summary (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None if
-    the kernel source changed since the counters were taken."""
+def counter_traffic(kernel):
+    """Bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE from rocprofv3,
+    copy-calibrated) from the committed counter summaries under profiles/:
+    a line `traffic: <kernel> | sources: <files> | sha256: <hex> | fetch_bytes:
+    <n> | write_bytes: <n>`.  None when no summary names the kernel or when
+    its source files changed since the counters were taken."""
+    import glob
     import hashlib
-    import re
-    path = os.path.join(ROOT, "profiles", "fused_select_prefill_128k_traffic.md")
-    try:
-        text = open(path).read()
-    except OSError:
-        return None
-    m = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
-    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
-    if not (m and t):
-        return None
-    h = hashlib.sha256()
-    for f in ("msa_select.hip", "msa_common.h"):
-        with open(os.path.join(ROOT, "block_sparse_long_index_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return int(t.group(1)) if h.hexdigest() == m.group(1) else None
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        for line in open(path):
+            if not line.startswith("traffic: "):
+                continue
+            f = dict(x.strip().split(": ", 1) for x in line.strip().split(" | "))
+            if f.get("traffic") != kernel:
+                continue
+            h = hashlib.sha256()
+            for src in f["sources"].split(","):
+                with open(os.path.join(ROOT, "block_sparse_long_index_amd", "csrc",
+                                       src.strip()), "rb") as fh:
+                    h.update(fh.read())
+            if h.hexdigest() != f["sha256"]:
+                return None
+            return int(f["fetch_bytes"]) + int(f["write_bytes"])
+    return None
+
+
+def kernel_times(fn, steps, between=None):
+    """fn() run `steps` times with the library's per-kernel timing on (HIP
+    events recorded by the library on each kernel's own launch stream):
+    {kind: {avg_launch_ms, launches_per_step, ms_per_step}}.  between(): work
+    run before each step, outside the library (not timed)."""
+    torch.cuda.synchronize()
+    ops.timing_begin(1 << 18)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if between is not None:
+            between()
+        fn()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    t = ops.timing_end()
+    out = {k: {"avg_launch_ms": ms / n, "launches_per_step": n / steps, "ms_per_step": ms / steps}
+           for k, (ms, n) in t.items()}
+    out["wall_ms_per_step"] = wall * 1e3
+    return out
+
+
+def roof(kernel, bound, achieved, peak, unit, traffic=None, **extra):
+    r = {"kernel": kernel, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+         "frac": achieved / peak, "traffic": traffic}
+    r.update(extra)
+    return r
 
 
 def ev():
@@ -218,6 +251,10 @@ def prefill_leg(args):
     res = dict(w=w, inp=inp, idx=idx, O=O, wall=wall, sel_ms=sel_ms, att_ms=att_ms, flops=fl)
     log("[bench] prefill %.3f ms/step (select %.3f, attention %.3f)"
         % (1e3 * wall / args.steps, sel_ms.mean(), att_ms.mean()))
+    # the same steps again with the library timing each kernel launch
+    res["kernels"] = kernel_times(step, args.steps)
+    log("[bench] per kernel:", {k: round(v["ms_per_step"], 3) for k, v in res["kernels"].items()
+                                if isinstance(v, dict)})
     # the headline step: the same work as one call (msa_prefill)
     del ws, ws_sel
     wall1, res["one_call_equal"] = time_one_call(w, inp, idx, O, args.steps, args.warmup)
@@ -349,6 +386,8 @@ def topk_leg(args, pre):
     torch.cuda.synchronize()
     us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
     same = bool(torch.equal(idx, pre["idx"]))
+    kt = kernel_times(lambda: ops.select_blocks_from_scores(S, w.k, w.N, out=idx),
+                      args.topk_reps)
     # torch.topk over the same rows, as context only (full rows, no local rule)
     tk = []
     for _ in range(3):
@@ -365,7 +404,12 @@ def topk_leg(args, pre):
     return {"workload": w.name, "rows": w.B * w.G * w.T, "us_p50": med,
             "us_p95": float(np.percentile(us, 95)), "bytes": by["total"],
             "GBps": by["total"] / med / 1e3, "frac_hbm": by["total"] / med / 1e3 / PEAK_HBM_GBS,
-            "matches_fused_select": same, "torch_topk_us": float(np.median(tk))}
+            "matches_fused_select": same, "torch_topk_us": float(np.median(tk)),
+            "roofline": roof("topk_rows_kernel", "hbm",
+                             by["total"] / (kt["topk"]["avg_launch_ms"] * 1e-3) / 1e9,
+                             PEAK_HBM_GBS, "GB/s", counter_traffic("topk_rows_kernel"),
+                             bytes_per_launch=by["total"],
+                             avg_launch_ms=kt["topk"]["avg_launch_ms"])}
 
 
 def fp8_leg(args, pre):
@@ -446,6 +490,25 @@ def decode_leg(args, fp8=False, cpu=False):
            "bytes": by["total"], "GBps": by["total"] / med / 1e3,
            "frac_hbm": by["total"] / med / 1e3 / PEAK_HBM_GBS,
            "note": "last-level cache flushed before each step"}
+    kt = kernel_times(step, args.decode_reps,
+                      between=lambda: torch.sum(flush, dim=0, out=sink))
+    out["kernel_us_per_step"] = {k: v["ms_per_step"] * 1e3 for k, v in kt.items()
+                                 if isinstance(v, dict)}
+    if "decode_scan" in kt:
+        sc = kt["decode_scan"]["avg_launch_ms"]
+        ach = by["index_keys"] / (sc * 1e-3) / 1e9
+        out["roofline"] = roof("decode_scan_kernel<%s, %d> (stages 1-2: index-key scan)"
+                               % ("true" if fp8 else "false", w.Bk), "hbm", ach, PEAK_HBM_GBS,
+                               "GB/s", counter_traffic("decode_scan_kernel<%s, %d>"
+                                                       % ("true" if fp8 else "false", w.Bk)),
+                               bytes_per_launch=by["index_keys"], avg_launch_ms=sc)
+    if "decode_attn" in kt:
+        da = kt["decode_attn"]["avg_launch_ms"]
+        ach = by["kv"] / (da * 1e-3) / 1e9
+        out["roofline_attention"] = roof(
+            "decode_attn_kernel<%d> (stage 4: selected K/V blocks)" % (w.Hq // w.G), "hbm", ach,
+            PEAK_HBM_GBS, "GB/s", counter_traffic("decode_attn_kernel<%d>" % (w.Hq // w.G)),
+            bytes_per_launch=by["kv"], avg_launch_ms=da)
     if cpu and not fp8:
         out["cpu_baseline"] = cpu_full(w, inp)
     del inp, flush
@@ -630,16 +693,54 @@ def main():
         out["config"] = {"workload": w.name, "B": w.B, "N": w.N, "T": w.T, "Hq": w.Hq,
                          "G": w.G, "d_h": w.d_h, "d_I": w.d_I, "Bk": w.Bk, "k": w.k,
                          "needles": w.needles, "seed": w.seed}
-        ach = fl["index"] / (sel * 1e-3) / 1e12
         fused = w.Bk == 128
-        out["roofline"] = {"kernel": "index_tile_kernel (fused select: scores, block max, "
-                                     "top-k)" if fused else
-                                     "index_tile_kernel (block scores, written) + "
-                                     "topk_rows_kernel, window after window",
-                           "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                           "traffic": select_traffic() if fused else None,
-                           "flops_per_launch": fl["index"], "avg_launch_ms": sel}
+        kt = pre["kernels"]
+        s4 = acc.stage4_bytes(w)
+        pb = acc.partial_bytes(w)
+        rl = []
+        if "kv_outer" in kt:
+            ko = kt["kv_outer"]
+            n = ko["launches_per_step"]
+            ach = fl["main"] / (ko["ms_per_step"] * 1e-3) / 1e12
+            rl.append(roof("kv_outer_kernel<%d, %d> (stage 4 KV-outer attention, one launch per "
+                           "stage of rows and group)" % (w.Hq // w.G, w.Bk // 32), "mfma", ach,
+                           PEAK_BF16_TFLOPS, "TFLOP/s",
+                           counter_traffic("kv_outer_kernel<%d, %d>" % (w.Hq // w.G, w.Bk // 32)),
+                           flops_per_launch=fl["main"] / n, avg_launch_ms=ko["avg_launch_ms"],
+                           launches_per_step=n, ms_per_step=ko["ms_per_step"],
+                           algorithmic_stage4_bytes=s4["total"],
+                           partial_bytes_written=pb["partials"] / n))
+        sel_k = kt.get("select")
+        sel_avg = sel_k["avg_launch_ms"] if sel_k else sel
+        ach_s = fl["index"] / (sel_k["ms_per_step"] if sel_k else sel) / 1e9
+        rl.append(roof("index_tile_kernel (fused select: scores, block max, top-k)" if fused else
+                       "index_tile_kernel (block scores, written) + topk_rows_kernel, window "
+                       "after window", "mfma", ach_s, PEAK_BF16_TFLOPS, "TFLOP/s",
+                       counter_traffic("index_tile_kernel<8, 15, false, false, 128>")
+                       if fused and w.G == 8 else None,
+                       flops_per_launch=fl["index"], avg_launch_ms=sel_avg,
+                       ms_per_step=sel_k["ms_per_step"] if sel_k else sel))
+        if "combine" in kt:
+            co = kt["combine"]
+            ach_c = pb["combine"] / (co["ms_per_step"] * 1e-3) / 1e9
+            rl.append(roof("combine_kernel<%d, false> (stage 4 partial combine)" % (w.Hq // w.G),
+                           "hbm", ach_c, PEAK_HBM_GBS, "GB/s",
+                           counter_traffic("combine_kernel<%d, false>" % (w.Hq // w.G)),
+                           bytes_per_launch=pb["combine"] / co["launches_per_step"],
+                           bytes_note="the KV-outer schedule's partials read once, idx read, "
+                                      "O and lse written",
+                           avg_launch_ms=co["avg_launch_ms"],
+                           launches_per_step=co["launches_per_step"],
+                           ms_per_step=co["ms_per_step"]))
+        # the kernel that takes the most time per step
+        out["roofline"] = max(rl, key=lambda r: r["ms_per_step"])
+        out["rooflines"] = rl
+        out["kernel_ms_per_step"] = {k: v["ms_per_step"] for k, v in kt.items()
+                                     if isinstance(v, dict)}
+        out["kernel_timing_note"] = ("per-kernel times: HIP events the library records on each "
+                                     "launch's stream over %d more steps of the two calls "
+                                     "(%.3f ms per step with the events)"
+                                     % (args.steps, kt["wall_ms_per_step"]))
         out["step"] = ("one msa_prefill call: fused select and KV-outer attention of "
                        "successive row windows overlapped on two streams")
         out["two_calls"] = {"ms_per_step": ms2, "TFLOPs": fl["total"] / (ms2 * 1e-3) / 1e12,

@@ -100,6 +100,30 @@ def decode_bytes(w, index_bytes: int = 2) -> dict:
     return dict(index_keys=kI, kv=kv, small=small, total=kI + kv + small)
 
 
+def stage4_bytes(w) -> dict:
+    """Bytes stage 4 must move at least: q, K, V and idx read once, O (bf16)
+    and lse (fp32) written once."""
+    q = w.B * w.T * w.Hq * w.d_h * 2
+    kv = 2 * w.B * w.G * w.N * w.d_h * 2
+    idx = w.B * w.G * w.T * w.k * 4
+    out = q + w.B * w.T * w.Hq * 4
+    return dict(q=q, kv=kv, idx=idx, out=out, total=q + kv + idx + out)
+
+
+def partial_bytes(w) -> dict:
+    """Bytes of the per-(row, slot) partial results a split over key blocks
+    produces for every query head: the bf16 unnormalised output (2 d_h B) and
+    its (max, sum) pair (8 B), for the support slots of every row.  A KV-outer
+    schedule writes them once and its combine reads them once; the combine
+    also reads idx and writes O and lse."""
+    p = positions(w.N, w.T)
+    slots = np.minimum(p // w.Bk + 1, w.k)
+    entries = int(w.B * w.Hq * slots.sum())
+    part = entries * (2 * w.d_h + 8)
+    comb = part + w.B * w.G * w.T * w.k * 4 + w.B * w.T * w.Hq * (2 * w.d_h + 4)
+    return dict(entries=entries, partials=part, combine=comb)
+
+
 def decode_flops(w) -> int:
     return (2 * w.G * w.d_I * w.B * w.N
             + 4 * w.Hq * w.d_h * support_tokens(w.N, 1, w.Bk, w.k, w.B))

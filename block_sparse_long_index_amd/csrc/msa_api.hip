@@ -247,6 +247,30 @@ const char* msa_status_string(int status) {
 
 const char* msa_last_error(void) { return g_err; }
 
+int msa_timing_begin(int64_t max_launches) {
+  if (max_launches < 1 || max_launches > (int64_t(1) << 20))
+    return fail(MSA_ERR_INVALID_ARGUMENT, "max_launches %lld outside [1, 2^20]",
+                (long long)max_launches);
+  if (msa::timing_enabled())
+    return fail(MSA_ERR_INVALID_ARGUMENT, "a timing session is already open");
+  const hipError_t e = msa::timing_start(max_launches);
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_timing_begin");
+}
+
+int msa_timing_end(double* total_ms, int64_t* launches, int nkinds) {
+  if (!total_ms || !launches || nkinds < 1 || nkinds > MSA_KERNEL_KINDS)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "total_ms, launches NULL or nkinds %d outside [1, %d]",
+                nkinds, MSA_KERNEL_KINDS);
+  if (!msa::timing_enabled()) return fail(MSA_ERR_INVALID_ARGUMENT, "no timing session is open");
+  int64_t dropped = 0;
+  const hipError_t e = msa::timing_stop(total_ms, launches, nkinds, &dropped);
+  if (e != hipSuccess) return hip_fail(e, "msa_timing_end");
+  if (dropped > 0)
+    return fail(MSA_ERR_INVALID_ARGUMENT, "%lld launches were not timed (max_launches too small)",
+                (long long)dropped);
+  return MSA_OK;
+}
+
 size_t msa_workspace_bytes(int op, const msa_dims_t* d) {
   char saved[sizeof g_err];
   memcpy(saved, g_err, sizeof g_err);

@@ -692,11 +692,15 @@ template <int HG, int NKT>
 static hipError_t launch_kv_combine(const AttnArgs& aa, const CombArgs& ca, int64_t grid_chunks,
                                     hipStream_t st) {
   const int64_t grid = (grid_chunks + 7) & ~static_cast<int64_t>(7);
-  hipLaunchKernelGGL((kv_outer_kernel<HG, NKT>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                     st, aa);
+  {
+    TimedLaunch tl(MSA_KERNEL_KV_OUTER, st);
+    hipLaunchKernelGGL((kv_outer_kernel<HG, NKT>), dim3(static_cast<unsigned>(grid)), dim3(256),
+                       0, st, aa);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t waves = ca.rows * (ca.group >= 0 ? 1 : ca.G);
+  TimedLaunch tl(MSA_KERNEL_COMBINE, st);
   if (ca.k > 16)
     hipLaunchKernelGGL((combine_kernel<HG, true>), dim3(static_cast<unsigned>((waves + 3) / 4)),
                        dim3(256), 0, st, ca);
@@ -760,6 +764,7 @@ hipError_t launch_invert_window(const int32_t* idx, int64_t b, int64_t T, int64_
   const int32_t U = static_cast<int32_t>(w.stage_rows / w.rq);
   const int64_t nst = static_cast<int64_t>(G) * S;
   const dim3 ugrid(static_cast<unsigned>(ia.nc), static_cast<unsigned>(G));
+  TimedLaunch tl(MSA_KERNEL_INVERT, st);
   hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks_for(nst, 256)), dim3(256), 0, st,
                      w.totals + 4, nst, 0);
   hipLaunchKernelGGL(hist_kernel, ugrid, dim3(256), lds, st, ia);
@@ -1232,11 +1237,15 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(CombArgs a) {
 template <int HG>
 static hipError_t launch_decode_t(const DecArgs& da, const CombArgs& ca, int64_t n,
                                   hipStream_t st) {
-  hipLaunchKernelGGL((decode_attn_kernel<HG>), dim3(static_cast<unsigned>(n)), dim3(256), 0, st,
-                     da);
+  {
+    TimedLaunch tl(MSA_KERNEL_DECODE_ATTN, st);
+    hipLaunchKernelGGL((decode_attn_kernel<HG>), dim3(static_cast<unsigned>(n)), dim3(256), 0,
+                       st, da);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t waves = ca.rows * ca.G * HG;
+  TimedLaunch tl(MSA_KERNEL_DECODE_COMBINE, st);
   if (ca.k > 16)
     hipLaunchKernelGGL((decode_combine_kernel<HG, 16>), dim3(static_cast<unsigned>((waves + 3) / 4)),
                        dim3(256), 0, st, ca);

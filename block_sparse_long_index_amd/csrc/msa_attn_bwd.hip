@@ -476,12 +476,15 @@ template <int HG>
 static hipError_t launch_bwd_stage(const BwdArgs& ba, const DqArgs& da, int64_t grid_chunks,
                                    hipStream_t st) {
   const int64_t grid = (grid_chunks + 7) & ~static_cast<int64_t>(7);
-  if (ba.teach)
-    hipLaunchKernelGGL((kv_outer_bwd_kernel<HG, true>), dim3(static_cast<unsigned>(grid)),
-                       dim3(256), 0, st, ba);
-  else
-    hipLaunchKernelGGL((kv_outer_bwd_kernel<HG, false>), dim3(static_cast<unsigned>(grid)),
-                       dim3(256), 0, st, ba);
+  {
+    TimedLaunch tl(MSA_KERNEL_ATTN_BACKWARD, st);
+    if (ba.teach)
+      hipLaunchKernelGGL((kv_outer_bwd_kernel<HG, true>), dim3(static_cast<unsigned>(grid)),
+                         dim3(256), 0, st, ba);
+    else
+      hipLaunchKernelGGL((kv_outer_bwd_kernel<HG, false>), dim3(static_cast<unsigned>(grid)),
+                         dim3(256), 0, st, ba);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dq_combine_kernel<HG>), dim3(static_cast<unsigned>((da.rows + 3) / 4)),

@@ -721,6 +721,7 @@ unsigned nblk_of(int64_t n, int per) { return static_cast<unsigned>((n + per - 1
 
 hipError_t launch_kl(int hg, const IkArgs& ia, int64_t grid, hipStream_t st) {
   const dim3 gd(static_cast<unsigned>(grid)), bd(256);
+  TimedLaunch tl(MSA_KERNEL_INDEX_KL, st);
   if (ia.teach) {
     hipLaunchKernelGGL(index_kl_teach_kernel, gd, bd, 0, st, ia);
     return hipGetLastError();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "msa.h"
+
 namespace msa {
 
 // A paged cache for decode: 128-token pages in a pool of `pages`; sequence
@@ -153,5 +155,22 @@ hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse,
                               int64_t B, int64_t N, int Hq, int G, int k, int Bk,
                               const PagedCache& pc, const AttnWorkspace& w, hipStream_t st);
+
+// Per-kernel timing (msa_timing.hip).  Kinds are the MSA_KERNEL_* ids of
+// msa.h.  TimedLaunch brackets the launches made during its lifetime with
+// two events on `st` when timing is on.
+bool timing_enabled();
+int timing_open(int kind, hipStream_t st);
+void timing_close(int slot, hipStream_t st);
+hipError_t timing_start(int64_t max_launches);
+hipError_t timing_stop(double* ms, int64_t* launches, int nkinds, int64_t* dropped);
+struct TimedLaunch {
+  int slot;
+  hipStream_t st;
+  TimedLaunch(int kind, hipStream_t s) : slot(timing_enabled() ? timing_open(kind, s) : -1), st(s) {}
+  ~TimedLaunch() { timing_close(slot, st); }
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+};
 
 }  // namespace msa

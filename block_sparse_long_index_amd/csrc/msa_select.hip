@@ -467,6 +467,7 @@ static hipError_t launch_tiles_cap(const TileArgs& a, int64_t ntiles, hipStream_
   using TS = TileShape<G>;
   const int64_t grid = a.wgs > 0 && a.wgs < a.nitems ? a.wgs : a.nitems;
   const dim3 gd(static_cast<unsigned>(grid)), bd(TS::NT);
+  TimedLaunch tl(MSA_KERNEL_SELECT, st);
   if (WS || a.k <= 4) {
     hipLaunchKernelGGL((index_tile_kernel<G, 3, WS, F8, BK>), gd, bd, 0, st, a);
   } else if constexpr (BK == 128) {
@@ -650,6 +651,7 @@ hipError_t launch_decode_scan(bool fp8, const void* qI, const void* kI, float* S
   a.NCH = static_cast<int32_t>((N + kBlock - 1) / kBlock);
   a.G = G;
   const dim3 grid(static_cast<unsigned>((a.NCH + 3) / 4), static_cast<unsigned>(B));
+  TimedLaunch tl(MSA_KERNEL_DECODE_SCAN, st);
   if (fp8 && Bk == 128)
     hipLaunchKernelGGL((decode_scan_kernel<true, 128>), grid, dim3(256), 0, st, a);
   else if (fp8)
@@ -1009,6 +1011,7 @@ hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T, 
   a.Bk = Bk;
   a.NB = static_cast<int32_t>((N + Bk - 1) / Bk);
   a.k = k;
+  TimedLaunch tl(MSA_KERNEL_TOPK, st);
   if (a.rows <= 4096 && a.NB >= 1024) {
     // few long rows: spread each row over a workgroup
     hipLaunchKernelGGL(topk_wide_kernel, dim3(static_cast<unsigned>(a.rows)), dim3(256), 0, st, a);

@@ -54,6 +54,8 @@ _SIGS = {
                                                    ctypes.c_size_t, _P]),
     "msa_sparse_attn_decode_paged": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, _P, _P,
                                                     _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_timing_begin": (ctypes.c_int, [ctypes.c_int64]),
+    "msa_timing_end": (ctypes.c_int, [_P, _P, ctypes.c_int]),
     "msa_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _P]),
     "msa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "msa_last_error": (ctypes.c_char_p, []),
@@ -191,6 +193,26 @@ def select_blocks_from_scores(S, k, N, out=None, Bk=128):
     _check(lib().msa_select_blocks_from_scores(ctypes.byref(d), _ptr(S), _ptr(idx), _stream()),
            "msa_select_blocks_from_scores")
     return idx
+
+
+# Kernel kinds of msa_timing_begin / msa_timing_end, in id order.
+KERNEL_KINDS = ("select", "kv_outer", "combine", "invert", "decode_scan", "topk",
+                "decode_attn", "decode_combine", "attn_backward", "index_kl")
+
+
+def timing_begin(max_launches=65536):
+    """Start timing every launch of the library's timed kernel kinds with HIP
+    events on its own stream (msa_timing_begin)."""
+    _check(lib().msa_timing_begin(int(max_launches)), "msa_timing_begin")
+
+
+def timing_end():
+    """Stop timing; {kind: (total ms, launches)} for the kinds that ran."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib().msa_timing_end(ms, cnt, n), "msa_timing_end")
+    return {KERNEL_KINDS[i]: (ms[i], cnt[i]) for i in range(n) if cnt[i] > 0}
 
 
 _side_streams = {}

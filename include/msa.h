@@ -360,6 +360,36 @@ int msa_sparse_attn_decode_paged(const msa_dims_t *dims, const void *q, const vo
                                  const int32_t *idx, void *O, float *lse, void *ws,
                                  size_t ws_bytes, void *stream);
 
+/*
+ * Per-kernel timing, for measurement harnesses.  Between msa_timing_begin and
+ * msa_timing_end every launch of the kernel kinds below, by any call on any
+ * stream, is bracketed by two HIP events recorded on the stream the kernel is
+ * launched on; msa_timing_end waits for those events and returns, per kind,
+ * the summed elapsed milliseconds and the number of launches timed.  The
+ * events are created on the current device by msa_timing_begin (room for
+ * max_launches launches, 1 <= max_launches <= 2^20) and destroyed by
+ * msa_timing_end.  A launch past that room is not timed, and msa_timing_end
+ * then returns MSA_ERR_INVALID_ARGUMENT after filling the arrays.  Timing adds
+ * two event records per timed launch; calls made with it off are unchanged.
+ * Not for use under HIP graph capture.  One timing session per process.
+ *   total_ms, launches  out: arrays of nkinds (<= MSA_KERNEL_KINDS) entries
+ */
+enum {
+    MSA_KERNEL_SELECT = 0,        /* index-score tiles (fused select or score writing) */
+    MSA_KERNEL_KV_OUTER = 1,      /* prefill KV-outer attention */
+    MSA_KERNEL_COMBINE = 2,       /* prefill partial combine */
+    MSA_KERNEL_INVERT = 3,        /* block->queries inversion (all of its kernels) */
+    MSA_KERNEL_DECODE_SCAN = 4,   /* decode index-key scan */
+    MSA_KERNEL_TOPK = 5,          /* top-k from materialised scores */
+    MSA_KERNEL_DECODE_ATTN = 6,   /* decode split-KV attention */
+    MSA_KERNEL_DECODE_COMBINE = 7,
+    MSA_KERNEL_ATTN_BACKWARD = 8, /* KV-outer backward */
+    MSA_KERNEL_INDEX_KL = 9,      /* index-branch KL backward passes */
+    MSA_KERNEL_KINDS = 10
+};
+int msa_timing_begin(int64_t max_launches);
+int msa_timing_end(double *total_ms, int64_t *launches, int nkinds);
+
 /* Scratch bytes an operation needs for these dims (0 if none); 0 also for
  * invalid dims.  Host only, no HIP call. */
 size_t msa_workspace_bytes(int op, const msa_dims_t *dims);

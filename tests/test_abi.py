@@ -22,7 +22,7 @@ def _declared():
 def test_header_functions_are_exported():
     L = ops.lib()
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(ops._SIGS)
@@ -264,3 +264,19 @@ def test_noalloc_decode_rejects_on_host():
                                             None) == -1
     assert L.msa_sparse_attn_decode_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, MISALIGNED,
                                             None, None) == -1
+
+
+def test_timing_rejects_on_host():
+    """The timing calls reject a bad pool size, a read without an open
+    session and bad output arrays before any HIP call."""
+    L = ops.lib()
+    assert L.msa_timing_begin(0) == -1
+    assert L.msa_timing_begin((1 << 20) + 1) == -1
+    n = len(ops.KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    assert L.msa_timing_end(ms, cnt, n) == -1
+    assert b"no timing session" in L.msa_last_error()
+    assert L.msa_timing_end(None, cnt, n) == -1
+    assert L.msa_timing_end(ms, cnt, n + 1) == -1
+    assert n == 10  # MSA_KERNEL_KINDS
