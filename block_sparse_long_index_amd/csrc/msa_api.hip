@@ -185,21 +185,28 @@ size_t train_ws(const msa_dims_t* d, int64_t window) {
   return rowdot_bytes(d) + lpx_bytes(d) + teach_bytes(d, window) + prefill_ws(d, window);
 }
 
-// The one-call prefill (msa_prefill): windows of about T / 8 query rows, at
+// The one-call prefill (msa_prefill): windows of about T / 4 query rows, at
 // least 16384 (smaller windows fill the attention's chunks too thinly to
 // gain from the overlap), a multiple of 4096, at most 64 windows; the
-// selection of a window overlaps the attention of the one before.
+// selection of a window overlaps the attention of the one before.  When that
+// makes fewer than four windows the whole prefill is one window: the overlap
+// does not pay there, and the windows' smaller launches cost more than one
+// selection and one attention over all rows (32K rows: 6.33 ms in three
+// windows in order, 5.62 ms as one).
 constexpr int kMaxPipeWindows = 64;
 
 #ifndef MSA_PIPE_SPLIT
-#define MSA_PIPE_SPLIT 8
+#define MSA_PIPE_SPLIT 4
 #endif
 int64_t pipe_window(const msa_dims_t* d) {
   int64_t w = (d->T + MSA_PIPE_SPLIT - 1) / MSA_PIPE_SPLIT;
   if (w < 16384) w = 16384;
   w = ((w + 4095) / 4096) * 4096;
   if ((d->T + w - 1) / w > kMaxPipeWindows) w = (d->T + kMaxPipeWindows - 1) / kMaxPipeWindows;
-  return w < d->T ? w : d->T;
+  if (w >= d->T) return d->T;
+  int64_t bounds[msa::kMaxPrefillWindows + 1];
+  if (msa::prefill_windows(d->T, w, bounds, msa::kMaxPrefillWindows) < 4) return d->T;
+  return w;
 }
 
 // Rows of block scores the one-call prefill materialises at a time (Bk < 128).

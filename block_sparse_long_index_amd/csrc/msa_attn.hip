@@ -874,14 +874,16 @@ hipError_t launch_attn_prefill_rows(const void* q, const void* K, const void* V,
 constexpr int kPipeSelectWGs = MSA_PIPE_SELECT_WGS;
 
 // Window boundaries of the pipelined prefill: windows of `win` rows, the
-// last one cut in two halves (its attention runs alone, after the last
-// selection, so a shorter one costs less).  Returns the number of windows.
+// last one (unless it is the only one) cut in two halves: its attention runs
+// alone, after the last selection, so a shorter one costs less.  Returns the
+// number of windows.
 int prefill_windows(int64_t T, int64_t win, int64_t* bounds, int max_windows) {
   int n = 0;
   bounds[0] = 0;
   for (int64_t t0 = 0; t0 < T && n < max_windows; t0 += win) {
     const int64_t t1 = t0 + win < T ? t0 + win : T;
-    if (t1 == T && t1 - t0 >= 8192 && n + 2 <= max_windows) bounds[++n] = t0 + (t1 - t0) / 2;
+    if (t1 == T && t0 > 0 && t1 - t0 >= 8192 && n + 2 <= max_windows)
+      bounds[++n] = t0 + (t1 - t0) / 2;
     bounds[++n] = t1;
   }
   return n;

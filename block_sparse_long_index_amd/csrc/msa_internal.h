@@ -144,6 +144,9 @@ hipError_t launch_attn_prefill_rows(const void* q, const void* K, const void* V,
 // kMaxPrefillWindows ints of scratch.  w: an attention workspace whose window
 // is >= win.  ev: nev >= ceil(T / win) + 2 events (unused when st2 == st).
 constexpr int kMaxPrefillWindows = 72;
+// Window boundaries [bounds[i], bounds[i + 1]) of the pipelined prefill for
+// windows of `win` rows; returns their number.
+int prefill_windows(int64_t T, int64_t win, int64_t* bounds, int max_windows);
 hipError_t launch_prefill_pipelined(const void* qI, const void* kI, const void* q, const void* K,
                                     const void* V, int32_t* idx, void* O, float* lse, int64_t B,
                                     int64_t T, int64_t N, int Hq, int G, int k, int Bk,

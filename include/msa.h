@@ -199,7 +199,8 @@ int msa_sparse_attn_prefill(const msa_dims_t *dims, const void *q,
  *   stream2        a second stream of the same device for the attention
  *                  windows (it waits for each window's selection; `stream`
  *                  waits for its last window), or NULL: every launch in
- *                  order on `stream`
+ *                  order on `stream`.  Prefills of fewer than four windows
+ *                  (T up to about 49152 rows) also run in order on `stream`.
  * Needs T >= 2.  Any supported Bk (with Bk < 128 the selection materialises
  * the scores of up to 1 GB of rows at a time in the workspace).
  */

@@ -46,9 +46,10 @@ CASES = [
     ("c2k", 1, 2048, 2048, 8, 2, 4, 128),
     ("ragged_b2", 2, 9000, 9000, 16, 4, 8, 128),
     ("chunked", 1, 5000, 12000, 64, 8, 16, 128),
-    ("windows", 1, 40000, 40000, 64, 8, 16, 128),
+    ("one_window", 1, 40000, 40000, 64, 8, 16, 128),   # < 4 windows: one window
+    ("windows", 1, 70000, 70000, 16, 4, 8, 128),       # 5 windows, the last one halved
     ("bk64", 1, 10000, 10000, 32, 8, 32, 64),
-    ("bk64_windows", 1, 34000, 34000, 16, 4, 32, 64),
+    ("bk64_windows", 1, 66000, 66000, 16, 4, 32, 64),  # 4 windows of 64-key blocks
     ("bk32_b2", 2, 6000, 6500, 16, 2, 64, 32),
     ("hg16", 1, 3333, 3333, 64, 4, 3, 128),
     ("two_rows", 3, 2, 130, 8, 2, 4, 128),
@@ -76,13 +77,13 @@ def test_prefill_equals_two_calls(name, B, T, N, Hq, G, k, Bk, overlap):
 def test_prefill_repeat_and_stream_order():
     """Two calls in a row on the same outputs, and a consumer on the caller's
     stream right after: it must see the finished results."""
-    w = Workload("rep", B=1, T=20000, N=20000, Hq=64, G=8, k=16, seed=5)
+    w = Workload("rep", B=1, T=70000, N=70000, Hq=16, G=4, k=8, seed=5)  # 5 windows
     inp = make_inputs(w, device="cuda")
-    out = (torch.empty(1, 8, w.T, 16, dtype=torch.int32, device="cuda"),
+    out = (torch.empty(1, w.G, w.T, w.k, dtype=torch.int32, device="cuda"),
            torch.empty_like(inp["q"]))
-    ops.prefill(inp["qI"], inp["kI"], inp["q"], inp["K"], inp["V"], 16, out=out)
+    ops.prefill(inp["qI"], inp["kI"], inp["q"], inp["K"], inp["V"], w.k, out=out)
     a = out[1].float().sum()  # enqueued on the caller's stream after the call
-    ops.prefill(inp["qI"], inp["kI"], inp["q"], inp["K"], inp["V"], 16, out=out)
+    ops.prefill(inp["qI"], inp["kI"], inp["q"], inp["K"], inp["V"], w.k, out=out)
     b = out[1].float().sum()
     idx2, O2, _ = two_calls(w, inp)
     torch.cuda.synchronize()
