@@ -468,28 +468,52 @@ def decode_leg(args, fp8=False, cpu=False):
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
 
-    def step():
+    def two_calls():
         ops.select_blocks(qI, kI, w.k, out=idx, workspace=ws_s, Bk=w.Bk)
         ops.sparse_attn_decode(q, K, V, idx, out=O, workspace=ws_a, Bk=w.Bk)
 
-    for _ in range(3):
-        step()
-    times = []
-    for _ in range(args.decode_reps):
-        torch.sum(flush, dim=0, out=sink)
-        a, b = ev(), ev()
-        a.record()
-        step()
-        b.record()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) * 1e3)
-    us = np.array(times)
+    # the bf16 step as one msa_decode call (fp8 index keys: the two calls)
+    idx1, O1 = torch.empty_like(idx), torch.empty_like(O)
+    ws_1 = None
+    if not fp8:
+        ws_1 = torch.empty(ops.workspace_bytes(ops.OP_DECODE, d), dtype=torch.uint8,
+                           device="cuda")
+
+    def one_call():
+        ops.decode(qI, kI, q, K, V, w.k, out=(idx1, O1), workspace=ws_1, Bk=w.Bk)
+
+    def timed(step):
+        for _ in range(3):
+            step()
+        times = []
+        for _ in range(args.decode_reps):
+            torch.sum(flush, dim=0, out=sink)
+            a, b = ev(), ev()
+            a.record()
+            step()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        return np.array(times)
+
+    step = two_calls if fp8 else one_call
+    us2 = timed(two_calls)
+    us = us2 if fp8 else timed(one_call)
     by = acc.decode_bytes(w, index_bytes=1 if fp8 else 2)
     med = float(np.median(us))
     out = {"workload": w.name, "us_p50": med, "us_p95": float(np.percentile(us, 95)),
            "bytes": by["total"], "GBps": by["total"] / med / 1e3,
            "frac_hbm": by["total"] / med / 1e3 / PEAK_HBM_GBS,
+           "step": ("msa_select_blocks_fp8, then msa_sparse_attn_decode" if fp8 else
+                    "one msa_decode call: index-key scan, then one workgroup per (sequence, "
+                    "group) selecting, attending and merging its blocks"),
            "note": "last-level cache flushed before each step"}
+    if not fp8:
+        out["two_calls"] = {"us_p50": float(np.median(us2)),
+                            "GBps": by["total"] / float(np.median(us2)) / 1e3,
+                            "calls": "msa_select_blocks, then msa_sparse_attn_decode",
+                            "idx_equal": bool(torch.equal(idx1, idx)),
+                            "O_max_abs_diff": float((O1.float() - O.float()).abs().max())}
     kt = kernel_times(step, args.decode_reps,
                       between=lambda: torch.sum(flush, dim=0, out=sink))
     out["kernel_us_per_step"] = {k: v["ms_per_step"] * 1e3 for k, v in kt.items()
@@ -508,6 +532,14 @@ def decode_leg(args, fp8=False, cpu=False):
         out["roofline_attention"] = roof(
             "decode_attn_kernel<%d> (stage 4: selected K/V blocks)" % (w.Hq // w.G), "hbm", ach,
             PEAK_HBM_GBS, "GB/s", counter_traffic("decode_attn_kernel<%d>" % (w.Hq // w.G)),
+            bytes_per_launch=by["kv"], avg_launch_ms=da)
+    if "decode_step" in kt:
+        da = kt["decode_step"]["avg_launch_ms"]
+        ach = by["kv"] / (da * 1e-3) / 1e9
+        out["roofline_attention"] = roof(
+            "decode_step_kernel<%d> (stages 3-4: selection, selected K/V blocks, merge)"
+            % (w.Hq // w.G), "hbm", ach, PEAK_HBM_GBS, "GB/s",
+            counter_traffic("decode_step_kernel<%d>" % (w.Hq // w.G)),
             bytes_per_launch=by["kv"], avg_launch_ms=da)
     if cpu and not fp8:
         out["cpu_baseline"] = cpu_full(w, inp)

@@ -237,6 +237,26 @@ size_t decode_ws(const msa_dims_t* d) {
   return msa::attn_workspace_bytes(d->B, d->B, d->N, d->G, d->Hq / d->G, d->k, d->Bk, true);
 }
 
+// One-call decode (msa_decode): the block scores of the scan, then either the
+// fused step (one workgroup per (sequence, group): selection, attention and
+// merge) or, for batches of fewer rows than that needs to fill the chip, the
+// separate top-k, attention and combine launches (whose partials follow the
+// scores in the workspace).
+#ifndef MSA_STEP_MIN_ROWS
+#define MSA_STEP_MIN_ROWS 128
+#endif
+constexpr int64_t kStepMinRows = MSA_STEP_MIN_ROWS;
+
+size_t decode_scores_bytes(const msa_dims_t* d) {
+  return (decode_select_ws(d) + 255) & ~size_t(255);
+}
+
+size_t decode1_ws(const msa_dims_t* d) {
+  return decode_scores_bytes(d) + (d->B * d->G >= kStepMinRows
+                                       ? msa::decode_step_scratch_bytes(d->B, d->G, d->Hq)
+                                       : decode_ws(d));
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +315,7 @@ size_t msa_workspace_bytes(int op, const msa_dims_t* d) {
     case MSA_OP_INDEX_KL_BACKWARD: return index_kl_ws(d, default_window(d));
     case MSA_OP_TRAIN_BACKWARD: return train_ws(d, default_window(d));
     case MSA_OP_PREFILL: return d->T > 1 ? pipe_ws(d) : 0;
+    case MSA_OP_DECODE: return d->T == 1 ? decode1_ws(d) : 0;
   }
   return 0;
 }
@@ -676,6 +697,49 @@ int msa_sparse_attn_decode(const msa_dims_t* d, const void* q, const void* K, co
                                                d->k, d->Bk, kContiguous, w,
                                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_decode");
+  return MSA_OK;
+}
+
+int msa_decode(const msa_dims_t* d, const void* qI, const void* kI, const void* q, const void* K,
+               const void* V, int32_t* idx, void* O, float* lse, void* ws, size_t ws_bytes,
+               void* stream) {
+  MSA_TRY(check_dims(d));
+  if (d->T != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "decode needs T == 1 (got %lld)",
+                             (long long)d->T);
+  MSA_TRY(check_ptr(qI, "qI"));
+  MSA_TRY(check_ptr(kI, "kI"));
+  MSA_TRY(check_ptr(q, "q"));
+  MSA_TRY(check_ptr(K, "K"));
+  MSA_TRY(check_ptr(V, "V"));
+  MSA_TRY(check_ptr(idx, "idx"));
+  MSA_TRY(check_ptr(O, "O"));
+  if (lse) MSA_TRY(check_ptr(lse, "lse"));
+  MSA_TRY(check_ptr(ws, "ws"));
+  const size_t need = decode1_ws(d);
+  if (ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "msa_decode needs %zu workspace bytes, got %zu",
+                need, ws_bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* S = static_cast<float*>(ws);
+  hipError_t e = msa::launch_decode_scan(false, qI, kI, S, d->B, d->N, d->G, d->Bk, kContiguous,
+                                         st);
+  if (e == hipSuccess) {
+    if (d->B * d->G >= kStepMinRows) {
+      e = msa::launch_decode_step(S, q, K, V, idx, O, lse,
+                                  static_cast<unsigned char*>(ws) + decode_scores_bytes(d), d->B,
+                                  d->N, d->Hq, d->G, d->k, d->Bk, kContiguous, st);
+    } else {
+      e = msa::launch_topk_rows(S, idx, d->B, 1, 0, 1, d->N, d->G, d->Bk, d->k, kContiguous, st);
+      if (e == hipSuccess) {
+        msa::AttnWorkspace w;
+        msa::attn_workspace_carve(static_cast<unsigned char*>(ws) + decode_scores_bytes(d), d->B,
+                                  d->B, d->N, d->G, d->Hq / d->G, d->k, d->Bk, true, &w);
+        e = msa::launch_attn_decode(q, K, V, idx, O, lse, d->B, d->N, d->Hq, d->G, d->k, d->Bk,
+                                    kContiguous, w, st);
+      }
+    }
+  }
+  if (e != hipSuccess) return hip_fail(e, "msa_decode");
   return MSA_OK;
 }
 

@@ -14,6 +14,7 @@
 // queries that chose it.
 #include "msa_common.h"
 #include "msa_internal.h"
+#include "msa_topk.h"
 
 #include <math.h>
 
@@ -1234,6 +1235,347 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(CombArgs a) {
   }
   // lse in natural log: (max + log2(sum)) * ln 2, the max being log2-domain
   if (a.lse && lane == 0) a.lse[b * a.Hq + hq] = (mx + __log2f(den)) * 0.6931471805599453f;
+}
+
+// ---------------------------------------------------------------------------
+// One-call decode step, after the index-key scan.  Each (sequence, group) row
+// is split over SPLIT workgroups of eight waves (SPLIT = 2 while the batch has
+// fewer than 256 rows, so that every CU streams K / V).  In each workgroup,
+// waves 0-3 select the row's blocks from its block scores (the four-wave
+// top-k of the decode selection; the first workgroup of the row writes idx).
+// Then wave w takes the slots h + SPLIT (w + 8i) of the row (h: the
+// workgroup's part) and each of their 32-key quarters in turn: K rows
+// straight from HBM as the A operand of 16x16x32 MFMAs (keys x the group's
+// heads), V^T of the quarter through the wave's 8 KB of LDS (the layout of
+// decode_attn_kernel), and an online softmax per head: a running log2-domain
+// max and sum, the O accumulators rescaled before each PV product.  The next
+// quarter's K and V load while the current one is computed.  The waves'
+// (max, sum, O) meet in LDS; with SPLIT = 1 the workgroup writes O and lse,
+// with SPLIT = 2 each part writes its fp32 (max, sum, O) and a small combine
+// merges the two.  No bf16 partials leave the chip.
+// ---------------------------------------------------------------------------
+struct StepArgs {
+  const float* S;  // [B, G, NB] block scores
+  const u16* q;    // [B, Hq, 128]
+  const u16* K;    // [B, G, N, 128], or the page pool [pages, G, 128, 128] when paged
+  const u16* V;
+  int32_t* idx;    // [B, G, 1, k], written
+  u16* O;          // [B, Hq, 128]
+  float* lse;      // [B, Hq], natural log, or null
+  float* part;     // SPLIT > 1: [B * G, SPLIT, hg, 128] fp32 unnormalised O of each part
+  float2* ml;      // SPLIT > 1: [B * G, SPLIT, hg] (log2-domain max, sum)
+  int64_t N;       // cache capacity (tokens)
+  int32_t Hq, G, k, Bk, NB;
+  PagedCache pc;
+};
+
+// One quarter's operands: K as MFMA A fragments (2 tiles of 16 keys x 4
+// k-steps) and V as key pairs x 8 dims (4 tasks per lane).
+struct StepQuarter {
+  uint4 kf[2][4];
+  uint4 v0[4], v1[4];
+};
+
+template <int HG, int SPLIT>
+__global__ void __launch_bounds__(512, 1) decode_step_kernel(StepArgs a) {
+  constexpr int NW = 8;
+  __shared__ WideTopkLds tk;
+  __shared__ int sel[64];
+  __shared__ __align__(16) unsigned char lds[NW * 8192];  // V^T per wave, then the O merge
+  __shared__ __align__(16) uint4 qs[4][64];                // the heads' q fragments
+  __shared__ float wm[NW][16], wl[NW][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, qd = lane >> 4;
+  const int64_t bg = blockIdx.x / SPLIT;
+  const int h = static_cast<int>(blockIdx.x % SPLIT);
+  const int g = static_cast<int>(bg % a.G);
+  const int64_t b = bg / a.G;
+  const int64_t len = paged_len(a.pc, b, a.N);  // this sequence's cache length (>= 1)
+  const int L = static_cast<int>((len - 1) / a.Bk);  // the local block
+  const int m = L < a.k - 1 ? L : a.k - 1;          // blocks chosen besides it
+
+  // selection: the best m of blocks 0..L-1, then L, then -1 padding; waves
+  // 4-7 fetch the q fragments meanwhile
+  if (m == 0) {
+    if (threadIdx.x < a.k) sel[threadIdx.x] = threadIdx.x == 0 ? L : -1;
+  } else if (wave < 4) {
+    wide_topk_part1(a.S + bg * a.NB, L, m, lane, wave, tk);
+  } else {
+    const int s = wave - 4;
+    const u16* qr = a.q + (b * a.Hq + g * HG + (col < HG ? col : 0)) * kHeadDim + 8 * qd;
+    qs[s][lane] = col < HG ? ld16(qr + 32 * s) : make_uint4(0, 0, 0, 0);
+  }
+  if (m == 0 && wave >= 4) {
+    const int s = wave - 4;
+    const u16* qr = a.q + (b * a.Hq + g * HG + (col < HG ? col : 0)) * kHeadDim + 8 * qd;
+    qs[s][lane] = col < HG ? ld16(qr + 32 * s) : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  if (m > 0 && wave == 0) {
+    const int v = wide_topk_part2(L, m, lane, tk);
+    if (lane < a.k) sel[lane] = v;
+  }
+  __syncthreads();
+  if (h == 0 && threadIdx.x < a.k) a.idx[bg * a.k + threadIdx.x] = sel[threadIdx.x];
+
+  // this wave's items: slots h + SPLIT (wave + NW i) <= m (the valid ones),
+  // Bk / 32 quarters each
+  const int nq = a.Bk >> 5;
+  const int first_slot = h + SPLIT * wave;
+  const int ns = first_slot <= m ? (m - first_slot) / (SPLIT * NW) + 1 : 0;
+  const int nitems = ns * nq;
+  unsigned char* vt = lds + wave * 8192;
+  // V^T store bases of this lane (see the store loop)
+  const int Pv = dec_pos(2 * col);
+  const int vb0 = 8 * qd * 64 + (((Pv >> 3) ^ (2 * qd)) & 3) * 16 + 2 * (Pv & 7);
+  const int vb1 = 8 * qd * 64 + (((Pv >> 3) ^ (2 * qd + 1)) & 3) * 16 + 2 * (Pv & 7);
+  // loads of item j: K as the A fragments, V as key pairs; keys past the
+  // block's end re-read its last key (masked below)
+  auto load = [&](int j, StepQuarter& x, int& nvalid) {
+    const int s = first_slot + SPLIT * NW * (j / nq);
+    const int qq = j % nq;
+    const int blk = sel[s];
+    const int64_t kblk = static_cast<int64_t>(blk) * a.Bk;
+    const int nblk = static_cast<int>(len - kblk < a.Bk ? len - kblk : a.Bk);
+    const int64_t row0 = a.pc.table ? (paged_page(a.pc, b, blk) * a.G + g) * kBlock
+                                    : bg * a.N + kblk;
+    nvalid = nblk - 32 * qq < 32 ? nblk - 32 * qq : 32;
+    const int first = 32 * qq < nblk ? 32 * qq : nblk - 1;
+    const u16* Kq = a.K + (row0 + first) * kHeadDim;
+    const u16* Vq = a.V + (row0 + first) * kHeadDim;
+    const int lim = nvalid > 0 ? nvalid - 1 : 0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int key = 16 * t + col;
+      const u16* kr = Kq + (key < lim ? key : lim) * kHeadDim + 8 * qd;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) x.kf[t][s4] = ld16(kr + 32 * s4);
+    }
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int k0 = 2 * col, c = qd + 4 * j4;
+      x.v0[j4] = ld16(Vq + (k0 < lim ? k0 : lim) * kHeadDim + c * 8);
+      x.v1[j4] = ld16(Vq + (k0 + 1 < lim ? k0 + 1 : lim) * kHeadDim + c * 8);
+    }
+  };
+
+  constexpr float qscale = 1.4426950408889634f * 0.08838834764831845f;
+  float M = -INFINITY, Ls = 0.f;  // running log2-domain max and sum of this lane's head
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{};
+  StepQuarter cur;
+  int nv_cur = 0;
+  if (nitems > 0) load(0, cur, nv_cur);
+  for (int j = 0; j < nitems; ++j) {
+    // the next quarter's loads first (the last item re-reads itself)
+    StepQuarter nxt;
+    int nv_nxt;
+    load(j + 1 < nitems ? j + 1 : j, nxt, nv_nxt);
+    const int nv = nv_cur;
+    if (nv > 0) {
+      // V -> V^T: task j4 of a lane holds keys 2 col, 2 col + 1 and d = 8 qd +
+      // 32 j4 + e; dec_vt's swizzle depends on e >> 2 only, so two base
+      // addresses plus immediate offsets cover all 32 stores
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int k0 = 2 * col;
+        const uint32_t w0[4] = {cur.v0[j4].x, cur.v0[j4].y, cur.v0[j4].z, cur.v0[j4].w};
+        const uint32_t w1[4] = {cur.v1[j4].x, cur.v1[j4].y, cur.v1[j4].z, cur.v1[j4].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t lo = k0 < nv ? (w0[e >> 1] >> (16 * (e & 1))) & 0xffffu : 0u;
+          const uint32_t hi = k0 + 1 < nv ? (w1[e >> 1] >> (16 * (e & 1))) & 0xffffu : 0u;
+          *reinterpret_cast<uint32_t*>(&vt[(e < 4 ? vb0 : vb1) + (32 * j4 + e) * 64]) =
+              lo | (hi << 16);
+        }
+      }
+      // S^T tiles: lane holds head col, keys 16t + 4qd + r
+      f32x4 sc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          sc[t] = mfma16(as_bf16x8(cur.kf[t][s4]), as_bf16x8(qs[s4][lane]), sc[t]);
+      float mq = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (16 * t + 4 * qd + r >= nv) sc[t][r] = -INFINITY;
+          mq = fmaxf(mq, sc[t][r]);
+        }
+      mq = fmaxf(mq, __shfl_xor(mq, 16));
+      mq = fmaxf(mq, __shfl_xor(mq, 32));
+      const float Mn = fmaxf(M, mq * qscale);  // finite: the quarter has a valid key
+      const float alpha = fast_exp2(M - Mn);    // 0 while M is -inf
+      float pv[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = fast_exp2(fmaf(sc[0][r], qscale, -Mn));
+        pv[4 + r] = fast_exp2(fmaf(sc[1][r], qscale, -Mn));
+      }
+      float l = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) l += pv[e];
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      Ls = Ls * alpha + l;
+      M = Mn;
+      const uint4 pf = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                  pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // O^T tiles: lane holds head col, d = 16dt + 4qd + r
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint4 av = *reinterpret_cast<const uint4*>(&vt[dec_vt(16 * dt + col, qd)]);
+        o[dt] = mfma16(as_bf16x8(av), as_bf16x8(pf), o[dt] * alpha);
+      }
+    }
+    cur = nxt;
+    nv_cur = nv_nxt;
+  }
+
+  // the waves' (max, sum, O) meet in LDS
+  if (qd == 0) {
+    wm[wave][col] = M;
+    wl[wave][col] = Ls;
+  }
+  __syncthreads();  // every wave is done with its V^T; the merge reuses the LDS
+  float* red = reinterpret_cast<float*>(lds);  // [NW][HG][128]
+  if (col < HG) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<f32x4*>(&red[(wave * HG + col) * kHeadDim + 16 * dt + 4 * qd]) = o[dt];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < HG * 32; e += 64 * NW) {
+    const int hh = e >> 5, d0 = 4 * (e & 31);
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, wm[w][hh]);
+    f32x4 acc = f32x4{};
+    float den = 0.f;
+    if (Mh > -INFINITY) {  // a part without items keeps zeros and -inf
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float sw = fast_exp2(wm[w][hh] - Mh);  // 0 for a wave without items
+        acc += *reinterpret_cast<const f32x4*>(&red[(w * HG + hh) * kHeadDim + d0]) * sw;
+        den += wl[w][hh] * sw;
+      }
+    }
+    if constexpr (SPLIT == 1) {
+      const float inv = 1.f / den;
+      uint2 st;
+      st.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+      st.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+      *reinterpret_cast<uint2*>(a.O + (b * a.Hq + g * HG + hh) * kHeadDim + d0) = st;
+      if (a.lse && d0 == 0)
+        a.lse[b * a.Hq + g * HG + hh] = (Mh + __log2f(den)) * 0.6931471805599453f;
+    } else {
+      const int64_t pr = (bg * SPLIT + h) * HG + hh;
+      *reinterpret_cast<f32x4*>(a.part + pr * kHeadDim + d0) = acc;
+      if (d0 == 0) a.ml[pr] = make_float2(Mh, den);
+    }
+  }
+}
+
+// Merge of the SPLIT parts of each (sequence, head): one wave per (sequence,
+// head), two values per lane.
+template <int SPLIT>
+__global__ void __launch_bounds__(256) decode_step_merge_kernel(StepArgs a, int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (wid >= rows) return;  // rows = B * Hq
+  const int hg = a.Hq / a.G;
+  const int64_t b = wid / a.Hq;
+  const int hq = static_cast<int>(wid % a.Hq);
+  const int64_t bg = b * a.G + hq / hg;
+  const int hh = hq % hg;
+  float2 ml[SPLIT];
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < SPLIT; ++p) {
+    ml[p] = a.ml[(bg * SPLIT + p) * hg + hh];
+    M = fmaxf(M, ml[p].x);
+  }
+  float o0 = 0.f, o1 = 0.f, den = 0.f;
+#pragma unroll
+  for (int p = 0; p < SPLIT; ++p) {
+    const float sw = ml[p].x > -INFINITY ? fast_exp2(ml[p].x - M) : 0.f;
+    const float2 v =
+        *reinterpret_cast<const float2*>(a.part + ((bg * SPLIT + p) * hg + hh) * kHeadDim + 2 * lane);
+    o0 += v.x * sw;
+    o1 += v.y * sw;
+    den += ml[p].y * sw;
+  }
+  const float inv = 1.f / den;
+  *reinterpret_cast<uint32_t*>(a.O + wid * kHeadDim + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
+  if (a.lse && lane == 0) a.lse[wid] = (M + __log2f(den)) * 0.6931471805599453f;
+}
+
+// Rows below which the step splits each row over two workgroups.
+constexpr int64_t kStepSplitRows = 256;
+
+size_t decode_step_scratch_bytes(int64_t B, int G, int Hq) {
+  if (B * G >= kStepSplitRows) return 0;
+  const int64_t pr = B * G * 2 * (Hq / G);
+  return static_cast<size_t>(pr) * (kHeadDim * sizeof(float) + sizeof(float2));
+}
+
+template <int HG>
+static hipError_t launch_step_t(const StepArgs& sa, int64_t rows, hipStream_t st) {
+  if (rows >= kStepSplitRows) {
+    hipLaunchKernelGGL((decode_step_kernel<HG, 1>), dim3(static_cast<unsigned>(rows)), dim3(512),
+                       0, st, sa);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_step_kernel<HG, 2>), dim3(static_cast<unsigned>(2 * rows)),
+                     dim3(512), 0, st, sa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t heads = rows * HG;
+  hipLaunchKernelGGL((decode_step_merge_kernel<2>), dim3(static_cast<unsigned>((heads + 3) / 4)),
+                     dim3(256), 0, st, sa, heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const float* S, const void* q, const void* K, const void* V,
+                              int32_t* idx, void* O, float* lse, void* scratch, int64_t B,
+                              int64_t N, int Hq, int G, int k, int Bk, const PagedCache& pc,
+                              hipStream_t st) {
+  StepArgs sa;
+  sa.S = S;
+  sa.q = static_cast<const u16*>(q);
+  sa.K = static_cast<const u16*>(K);
+  sa.V = static_cast<const u16*>(V);
+  sa.idx = idx;
+  sa.O = static_cast<u16*>(O);
+  sa.lse = lse;
+  const int64_t rows = B * G;
+  sa.part = static_cast<float*>(scratch);
+  sa.ml = reinterpret_cast<float2*>(static_cast<float*>(scratch) + rows * 2 * (Hq / G) * kHeadDim);
+  sa.N = N;
+  sa.Hq = Hq;
+  sa.G = G;
+  sa.k = k;
+  sa.Bk = Bk;
+  sa.NB = static_cast<int32_t>((N + Bk - 1) / Bk);
+  sa.pc = pc;
+  TimedLaunch tl(MSA_KERNEL_DECODE_STEP, st);
+  switch (Hq / G) {
+    case 8: return launch_step_t<8>(sa, rows, st);
+    case 4: return launch_step_t<4>(sa, rows, st);
+    case 16: return launch_step_t<16>(sa, rows, st);
+    case 2: return launch_step_t<2>(sa, rows, st);
+    case 1: return launch_step_t<1>(sa, rows, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int HG>

@@ -154,6 +154,17 @@ hipError_t launch_prefill_pipelined(const void* qI, const void* kI, const void* 
                                     const AttnWorkspace& w, hipStream_t st, hipStream_t st2,
                                     hipEvent_t* ev, int nev);
 
+// One-call decode after the scan: per (sequence, group) one workgroup selects
+// the blocks from S [B, G, NB] (writing idx) and attends them, writing O and
+// lse (nullable) directly.
+// scratch: decode_step_scratch_bytes(B, G, Hq) bytes (fp32 results of the
+// row parts when a row is split over two workgroups; 0 bytes otherwise).
+size_t decode_step_scratch_bytes(int64_t B, int G, int Hq);
+hipError_t launch_decode_step(const float* S, const void* q, const void* K, const void* V,
+                              int32_t* idx, void* O, float* lse, void* scratch, int64_t B,
+                              int64_t N, int Hq, int G, int k, int Bk, const PagedCache& pc,
+                              hipStream_t st);
+
 hipError_t launch_attn_decode(const void* q, const void* K, const void* V,
                               const int32_t* idx, void* O, float* lse,
                               int64_t B, int64_t N, int Hq, int G, int k, int Bk,

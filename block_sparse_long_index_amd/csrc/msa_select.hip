@@ -12,6 +12,7 @@
 // same selection.
 #include "msa_common.h"
 #include "msa_internal.h"
+#include "msa_topk.h"
 
 #include <limits.h>
 #include <math.h>
@@ -703,208 +704,6 @@ __device__ __forceinline__ TopkRow topk_row(const TopkArgs& a, int64_t r) {
   return x;
 }
 
-// Non-short-circuit operators keep the comparisons branch-free (selects, not
-// exec-mask branches).
-__device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
-  return (av > bv) | ((av == bv) & (ai < bi));
-}
-
-// The value of lane (lane ^ S), S a power of two below 64, by the cheapest
-// exchange for each distance: a DPP quad permutation for 1 and 2, a swizzle
-// (inside each half-wave) for 4 to 16, a permute for 32.
-template <int S>
-__device__ __forceinline__ int xlane(int x) {
-  if constexpr (S == 1) return __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);
-  else if constexpr (S == 2) return __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);
-  else if constexpr (S < 32) return __builtin_amdgcn_ds_swizzle(x, 0x1F | (S << 10));
-  else return __shfl_xor(x, 32);
-}
-
-template <int S>
-__device__ __forceinline__ float xlane(float x) {
-  return __int_as_float(xlane<S>(__float_as_int(x)));
-}
-
-// Bitonic sort of one (score, index) pair per lane, from the merge of SIZE
-// runs at distance STRIDE on; best_first puts the best pair in lane 0.  Each
-// compare-exchange takes one comparison: keep says whether this lane ends with
-// the better pair of the two (for two equal pairs either choice leaves the
-// same pair).
-template <int SIZE, int STRIDE, int NMAX>
-__device__ __forceinline__ void bitonic_steps(float& v, int& i, int lane, bool best_first) {
-  const float pv = xlane<STRIDE>(v);
-  const int pi = xlane<STRIDE>(i);
-  const bool keep = ((lane & STRIDE) == 0) == (((lane & SIZE) == 0) == best_first);
-  const bool take = beats(pv, pi, v, i) == keep;
-  v = take ? pv : v;
-  i = take ? pi : i;
-  if constexpr (STRIDE > 1)
-    bitonic_steps<SIZE, STRIDE / 2, NMAX>(v, i, lane, best_first);
-  else if constexpr (SIZE < NMAX)
-    bitonic_steps<SIZE * 2, SIZE, NMAX>(v, i, lane, best_first);
-}
-
-// Sorts each run of NMAX consecutive lanes (NMAX = 64: the whole wave).
-template <int NMAX = 64>
-__device__ __forceinline__ void bitonic64(float& v, int& i, int lane, bool best_first) {
-  bitonic_steps<2, 1, NMAX>(v, i, lane, best_first);
-}
-
-// Merge of a best-first bitonic sequence into best-first order.
-template <int STRIDE = 32>
-__device__ __forceinline__ void bitonic_merge64(float& v, int& i, int lane) {
-  const float pv = xlane<STRIDE>(v);
-  const int pi = xlane<STRIDE>(i);
-  const bool take = beats(pv, pi, v, i) == ((lane & STRIDE) == 0);
-  v = take ? pv : v;
-  i = take ? pi : i;
-  if constexpr (STRIDE > 1) bitonic_merge64<STRIDE / 2>(v, i, lane);
-}
-
-// Values sorted descending across the wave (lane 0 the largest).
-template <int SIZE = 2, int STRIDE = 1>
-__device__ __forceinline__ float sort_desc_values64(float v, int lane) {
-  const float pv = xlane<STRIDE>(v);
-  const bool keep = ((lane & STRIDE) == 0) == ((lane & SIZE) == 0);  // keep the larger
-  v = ((pv > v) == keep) ? pv : v;
-  if constexpr (STRIDE > 1)
-    return sort_desc_values64<SIZE, STRIDE / 2>(v, lane);
-  else if constexpr (SIZE < 64)
-    return sort_desc_values64<SIZE * 2, SIZE>(v, lane);
-  else
-    return v;
-}
-
-__device__ __forceinline__ int lanes_below(unsigned long long mask) {
-  return __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0));
-}
-
-// Best m candidates (score desc, index asc) among src[e] for e = e0 + lane +
-// step*i < n, left best-first in lanes 0..m-1 (m <= 63).  The first R strided
-// chunks are loaded once into registers, all loads in flight together; any
-// remainder is re-read from memory.  cv/ci: this wave's 64-entry LDS scratch.
-// Returns the number of candidates compacted into cv/ci in ascending index
-// order (all those >= the threshold, a superset of the best m), or -1 when
-// there were too many for the scratch (the best m then came from a running
-// merge).
-template <int R>
-__device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int step, int m,
-                                         int lane, float* cv, int* ci, float& v, int& vi) {
-  float x[R];  // -inf past the row's end
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = e0 + lane + step * r;
-    const float y = src[e < n ? e : n - 1];
-    x[r] = e < n ? y : -INFINITY;
-  }
-  const int rest = e0 + step * R;
-  float lm = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < R; ++r) lm = fmaxf(lm, x[r]);
-  for (int e = rest + lane; e < n; e += step) lm = fmaxf(lm, src[e]);
-  const float tau = __shfl(sort_desc_values64(lm, lane), m - 1);
-  v = -INFINITY;
-  vi = INT_MAX;
-  // candidates >= tau, compacted in index order while they fit the scratch;
-  // cnt counts them all (the same in every lane)
-  int cnt = 0;
-  auto chunk = [&](int c0, float xv) {
-    const int e = c0 + lane;
-    const bool f = (e < n) & (xv >= tau);
-    const unsigned long long bal = __ballot(f);
-    const int pos = cnt + lanes_below(bal);
-    if (f & (pos < 64)) {
-      cv[pos] = xv;
-      ci[pos] = e;
-    }
-    cnt += __popcll(bal);
-  };
-  auto merge = [&](int c0, float xv) {
-    const int e = c0 + lane;
-    const bool f = (e < n) & (xv >= tau);
-    if (!__ballot(f)) return;
-    float cvv = f ? xv : -INFINITY;
-    int cii = f ? e : INT_MAX;
-    bitonic64(cvv, cii, lane, false);
-    if (beats(cvv, cii, v, vi)) {
-      v = cvv;
-      vi = cii;
-    }
-    bitonic_merge64(v, vi, lane);
-  };
-#pragma unroll
-  for (int r = 0; r < R; ++r) chunk(e0 + step * r, x[r]);
-  for (int c0 = rest; c0 < n; c0 += step) {
-    const int e = c0 + lane;
-    chunk(c0, e < n ? src[e] : -INFINITY);
-  }
-  if (cnt <= 64) {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (lane < cnt) {
-      v = cv[lane];
-      vi = ci[lane];
-    }
-    // sort only as many lanes as hold candidates
-    if (cnt <= 16)
-      bitonic64<16>(v, vi, lane, true);
-    else if (cnt <= 32)
-      bitonic64<32>(v, vi, lane, true);
-    else
-      bitonic64(v, vi, lane, true);
-    return cnt;
-  } else {
-    // many equal scores at the threshold: merge 64 candidates at a time into
-    // a running best-64 list
-#pragma unroll
-    for (int r = 0; r < R; ++r) merge(e0 + step * r, x[r]);
-    for (int c0 = rest; c0 < n; c0 += step) {
-      const int e = c0 + lane;
-      merge(c0, e < n ? src[e] : -INFINITY);
-    }
-    return -1;
-  }
-}
-
-// Ascending sort of the keys of each 16-lane row (bitonic, from the merge of
-// SIZE runs at distance STRIDE on).
-template <int SIZE = 2, int STRIDE = 1>
-__device__ __forceinline__ int sort_asc16(int key, int lane) {
-  const int pk = xlane<STRIDE>(key);
-  const bool keep = ((lane & STRIDE) == 0) == (((lane & SIZE) == 0) | (SIZE == 16));
-  key = ((pk < key) == keep) ? pk : key;  // keep: the smaller of the two
-  if constexpr (STRIDE > 1)
-    return sort_asc16<SIZE, STRIDE / 2>(key, lane);
-  else if constexpr (SIZE < 16)
-    return sort_asc16<SIZE * 2, SIZE>(key, lane);
-  else
-    return key;
-}
-
-// Ascending sort of the keys across the wave.
-template <int SIZE = 2, int STRIDE = 1>
-__device__ __forceinline__ int sort_asc64(int key, int lane) {
-  const int pk = xlane<STRIDE>(key);
-  const bool keep = ((lane & STRIDE) == 0) == ((lane & SIZE) == 0);
-  key = ((pk < key) == keep) ? pk : key;  // keep: the smaller of the two
-  if constexpr (STRIDE > 1)
-    return sort_asc64<SIZE, STRIDE / 2>(key, lane);
-  else if constexpr (SIZE < 64)
-    return sort_asc64<SIZE * 2, SIZE>(key, lane);
-  else
-    return key;
-}
-
-// Lanes 0..m-1 hold block ids; write them ascending, then the local block L,
-// then -1 padding (m < k <= 64).
-__device__ __forceinline__ void write_selection(int32_t* out, int vi, int m, int L, int k,
-                                                int lane) {
-  const int key0 = lane < m ? vi : INT_MAX;
-  const int key = m <= 15 ? sort_asc16(key0, lane) : sort_asc64(key0, lane);
-  if (lane < k) out[lane] = lane < m ? key : (lane == m ? L : -1);
-}
-
 __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
   __shared__ float cv[4][64];
   __shared__ int ci[4][64];
@@ -943,10 +742,7 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
 // fourth 64-candidate chunk; the four best-m lists meet in LDS and wave 0
 // orders them and writes the selection.
 __global__ void __launch_bounds__(256) topk_wide_kernel(TopkArgs a) {
-  __shared__ float cv[4][64];
-  __shared__ int ci[4][64];
-  __shared__ float mv[4][64];
-  __shared__ int mi[4][64];
+  __shared__ WideTopkLds t;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const TopkRow x = topk_row(a, blockIdx.x);
   const int64_t L = x.L;
@@ -956,43 +752,11 @@ __global__ void __launch_bounds__(256) topk_wide_kernel(TopkArgs a) {
     if (wave == 0 && lane < a.k) out[lane] = lane == 0 ? static_cast<int>(L) : -1;
     return;
   }
-  float v;
-  int vi;
-  wave_topk<8>(x.s, static_cast<int>(L), 64 * wave, 256, m, lane, cv[wave], ci[wave], v, vi);
-  if (m <= 15) {
-    // Each wave's list is sorted best-first; odd waves store theirs reversed,
-    // so that every 32 entries form a bitonic sequence and two merge stages
-    // (instead of a whole sort) order the 64.
-    if (lane < 16) {
-      const int pos = wave * 16 + ((wave & 1) ? 15 - lane : lane);
-      mv[0][pos] = lane < m ? v : -INFINITY;
-      mi[0][pos] = lane < m ? vi : INT_MAX;
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    v = mv[0][lane];
-    vi = mi[0][lane];
-    bitonic_steps<32, 16, 64>(v, vi, lane, true);
-  } else {
-    // Up to 63 per wave: wave 0 merges the other lists into its own one at a
-    // time (its list best-first against the other reversed: the better of
-    // each pair is the best 64 of the two, a bitonic sequence).
-    mv[wave][lane] = lane < m ? v : -INFINITY;
-    mi[wave][lane] = lane < m ? vi : INT_MAX;
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll 1
-    for (int w = 1; w < 4; ++w) {
-      const float u = mv[w][63 - lane];
-      const int ui = mi[w][63 - lane];
-      if (beats(u, ui, v, vi)) {
-        v = u;
-        vi = ui;
-      }
-      bitonic_merge64(v, vi, lane);
-    }
-  }
-  write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
+  wide_topk_part1(x.s, static_cast<int>(L), m, lane, wave, t);
+  __syncthreads();
+  if (wave != 0) return;
+  const int v = wide_topk_part2(static_cast<int>(L), m, lane, t);
+  if (lane < a.k) out[lane] = v;
 }
 
 hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T, int64_t t0,

@@ -28,6 +28,7 @@ OP_ATTN_BACKWARD = 5
 OP_INDEX_KL_BACKWARD = 6
 OP_TRAIN_BACKWARD = 7
 OP_PREFILL = 8
+OP_DECODE = 9
 
 # Every function the C header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -43,6 +44,7 @@ _SIGS = {
                                               ctypes.c_size_t, _P]),
     "msa_sparse_attn_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "msa_prefill": (ctypes.c_int, [_P] * 10 + [ctypes.c_size_t, _P, _P]),
+    "msa_decode": (ctypes.c_int, [_P] * 10 + [ctypes.c_size_t, _P]),
     "msa_sparse_attn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                 _P, ctypes.c_size_t, _P]),
     "msa_train_backward": (ctypes.c_int, [_P] * 17 + [ctypes.c_size_t, _P]),
@@ -197,7 +199,7 @@ def select_blocks_from_scores(S, k, N, out=None, Bk=128):
 
 # Kernel kinds of msa_timing_begin / msa_timing_end, in id order.
 KERNEL_KINDS = ("select", "kv_outer", "combine", "invert", "decode_scan", "topk",
-                "decode_attn", "decode_combine", "attn_backward", "index_kl")
+                "decode_attn", "decode_combine", "attn_backward", "index_kl", "decode_step")
 
 
 def timing_begin(max_launches=65536):
@@ -414,6 +416,34 @@ def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None,
                                         _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()),
            "msa_sparse_attn_decode")
     return (O, lse) if return_lse else O
+
+
+def decode(qI, kI, q, K, V, k, return_lse=False, out=None, workspace=None, Bk=128):
+    """Stages 1-4 of a decode step in one call (msa_decode).  qI [B,1,G,128],
+    kI [B,N,128], q [B,Hq,128], K/V [B,G,N,128] -> (idx [B,G,1,k] int32,
+    O [B,Hq,128] bf16) and lse [B,Hq] fp32 when return_lse.  out: optional
+    (idx, O)."""
+    B, Hq, dh = q.shape
+    _, G, N, _ = K.shape
+    _need(qI, "qI", torch.bfloat16, (B, 1, G, 128))
+    _need(kI, "kI", torch.bfloat16, (B, N, 128))
+    _need(q, "q", torch.bfloat16)
+    _need(K, "K", torch.bfloat16, (B, G, N, dh))
+    _need(V, "V", torch.bfloat16, (B, G, N, dh))
+    d = dims(B, 1, N, Hq, G, k, d_h=dh, Bk=Bk)
+    if out is None:
+        idx = torch.empty(B, G, 1, k, dtype=torch.int32, device=q.device)
+        O = torch.empty_like(q)
+    else:
+        idx, O = out
+    _need(idx, "idx", torch.int32, (B, G, 1, k))
+    _need(O, "O", torch.bfloat16, q.shape)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
+    ws, nbytes = _workspace(OP_DECODE, d, workspace)
+    _check(lib().msa_decode(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(q), _ptr(K), _ptr(V),
+                            _ptr(idx), _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()),
+           "msa_decode")
+    return (idx, O, lse) if return_lse else (idx, O)
 
 
 def sparse_attn_decode_noalloc(q, K, V, idx, return_lse=False, out=None, lse_out=None,

@@ -95,7 +95,8 @@ enum {
     MSA_OP_ATTN_BACKWARD = 5,
     MSA_OP_INDEX_KL_BACKWARD = 6,
     MSA_OP_TRAIN_BACKWARD = 7,
-    MSA_OP_PREFILL = 8
+    MSA_OP_PREFILL = 8,
+    MSA_OP_DECODE = 9
 };
 
 /*
@@ -362,6 +363,28 @@ int msa_sparse_attn_decode_paged(const msa_dims_t *dims, const void *q, const vo
                                  size_t ws_bytes, void *stream);
 
 /*
+ * A decode step in one call (T == 1): stages 1 to 4 with the results of
+ * msa_select_blocks followed by msa_sparse_attn_decode (idx bit for bit; O
+ * and lse within the decode tolerance: the slot results are merged in fp32
+ * inside the chip instead of through bf16 partials).  The llama.cpp analysis
+ * page (section 2) reads per step the whole index-key cache plus only the
+ * selected K/V blocks; the study notes (section 3-5) scan, select, then
+ * attend.  After the scan of the index keys, each (sequence, group) row is
+ * one workgroup that selects its blocks, attends them with an online softmax
+ * and merges its waves' results, so the selected K/V are the only other bytes
+ * read and nothing is written but idx, O and lse.  Batches of fewer than 128
+ * (sequence, group) rows run the separate top-k, attention and combine
+ * launches instead (one workgroup per row would leave most of the chip idle).
+ *   qI, kI, q, K, V, idx, O, lse   as for msa_select_blocks and
+ *                                  msa_sparse_attn_decode (idx is written)
+ *   ws / ws_bytes  >= msa_workspace_bytes(MSA_OP_DECODE)
+ * bf16 index inputs, contiguous caches, every supported Bk.
+ */
+int msa_decode(const msa_dims_t *dims, const void *qI, const void *kI, const void *q,
+               const void *K, const void *V, int32_t *idx, void *O, float *lse, void *ws,
+               size_t ws_bytes, void *stream);
+
+/*
  * Per-kernel timing, for measurement harnesses.  Between msa_timing_begin and
  * msa_timing_end every launch of the kernel kinds below, by any call on any
  * stream, is bracketed by two HIP events recorded on the stream the kernel is
@@ -386,7 +409,8 @@ enum {
     MSA_KERNEL_DECODE_COMBINE = 7,
     MSA_KERNEL_ATTN_BACKWARD = 8, /* KV-outer backward */
     MSA_KERNEL_INDEX_KL = 9,      /* index-branch KL backward passes */
-    MSA_KERNEL_KINDS = 10
+    MSA_KERNEL_DECODE_STEP = 10,  /* one-call decode: selection + attention per row */
+    MSA_KERNEL_KINDS = 11
 };
 int msa_timing_begin(int64_t max_launches);
 int msa_timing_end(double *total_ms, int64_t *launches, int nkinds);

@@ -22,7 +22,7 @@ def _declared():
 def test_header_functions_are_exported():
     L = ops.lib()
     names = _declared()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(ops._SIGS)
@@ -279,4 +279,21 @@ def test_timing_rejects_on_host():
     assert b"no timing session" in L.msa_last_error()
     assert L.msa_timing_end(None, cnt, n) == -1
     assert L.msa_timing_end(ms, cnt, n + 1) == -1
-    assert n == 10  # MSA_KERNEL_KINDS
+    assert n == 11  # MSA_KERNEL_KINDS
+
+
+def test_decode_one_call_rejects_on_host():
+    """msa_decode validates like the two decode calls, before any HIP call."""
+    L = ops.lib()
+    d = _good(T=2, N=4096)
+    args = [FAKE] * 8
+    assert L.msa_decode(ctypes.byref(d), *args, FAKE, 1 << 40, None) == -1  # T != 1
+    d = _good(T=1, N=4096)
+    assert L.msa_decode(ctypes.byref(d), FAKE, None, *([FAKE] * 6), FAKE, 1 << 40, None) == -1
+    assert L.msa_decode(ctypes.byref(d), *([FAKE] * 6), MISALIGNED, None, FAKE, 1 << 40,
+                        None) == -1  # O misaligned
+    need = L.msa_workspace_bytes(ops.OP_DECODE, ctypes.byref(d))
+    assert need > 0
+    rc = L.msa_decode(ctypes.byref(d), *([FAKE] * 7), None, FAKE, need - 1, None)
+    assert rc == -3
+    assert L.msa_workspace_bytes(ops.OP_DECODE, ctypes.byref(_good(T=3, N=4096))) == 0
