@@ -1276,9 +1276,24 @@ struct StepQuarter {
   uint4 v0[4], v1[4];
 };
 
+// Waves per workgroup of the step kernel; a part's (slot, quarter) items are
+// dealt to them round-robin (four per wave for 16 slots in two parts).
+// Measured per decode step at 256K x 16: 8 waves 216.8 us, 16 waves (two
+// items each, 128 VGPRs) 218.1 us; 4 parts of 8 or 16 waves 227.0 / 230.1 us;
+// one workgroup per row 223.7 us.
+#ifndef MSA_STEP_WAVES
+#define MSA_STEP_WAVES 8
+#endif
+constexpr int kStepWaves = MSA_STEP_WAVES;
+// Parts per row below kStepSplitRows rows.
+#ifndef MSA_STEP_PARTS
+#define MSA_STEP_PARTS 2
+#endif
+constexpr int kStepParts = MSA_STEP_PARTS;
+
 template <int HG, int SPLIT>
-__global__ void __launch_bounds__(512, 1) decode_step_kernel(StepArgs a) {
-  constexpr int NW = 8;
+__global__ void __launch_bounds__(64 * kStepWaves) decode_step_kernel(StepArgs a) {
+  constexpr int NW = kStepWaves;
   __shared__ WideTopkLds tk;
   __shared__ int sel[64];
   __shared__ __align__(16) unsigned char lds[NW * 8192];  // V^T per wave, then the O merge
@@ -1300,12 +1315,8 @@ __global__ void __launch_bounds__(512, 1) decode_step_kernel(StepArgs a) {
     if (threadIdx.x < a.k) sel[threadIdx.x] = threadIdx.x == 0 ? L : -1;
   } else if (wave < 4) {
     wide_topk_part1(a.S + bg * a.NB, L, m, lane, wave, tk);
-  } else {
-    const int s = wave - 4;
-    const u16* qr = a.q + (b * a.Hq + g * HG + (col < HG ? col : 0)) * kHeadDim + 8 * qd;
-    qs[s][lane] = col < HG ? ld16(qr + 32 * s) : make_uint4(0, 0, 0, 0);
   }
-  if (m == 0 && wave >= 4) {
+  if (wave >= 4 && wave < 8) {
     const int s = wave - 4;
     const u16* qr = a.q + (b * a.Hq + g * HG + (col < HG ? col : 0)) * kHeadDim + 8 * qd;
     qs[s][lane] = col < HG ? ld16(qr + 32 * s) : make_uint4(0, 0, 0, 0);
@@ -1318,32 +1329,35 @@ __global__ void __launch_bounds__(512, 1) decode_step_kernel(StepArgs a) {
   __syncthreads();
   if (h == 0 && threadIdx.x < a.k) a.idx[bg * a.k + threadIdx.x] = sel[threadIdx.x];
 
-  // this wave's items: slots h + SPLIT (wave + NW i) <= m (the valid ones),
-  // Bk / 32 quarters each
+  // this part's items: its valid slots h, h + SPLIT, ... <= m times Bk / 32
+  // quarters; wave w takes items w, w + NW, ...
   const int nq = a.Bk >> 5;
-  const int first_slot = h + SPLIT * wave;
-  const int ns = first_slot <= m ? (m - first_slot) / (SPLIT * NW) + 1 : 0;
+  const int ns = h <= m ? (m - h) / SPLIT + 1 : 0;
   const int nitems = ns * nq;
+  const int mine = wave < nitems ? (nitems - wave + NW - 1) / NW : 0;
   unsigned char* vt = lds + wave * 8192;
   // V^T store bases of this lane (see the store loop)
   const int Pv = dec_pos(2 * col);
   const int vb0 = 8 * qd * 64 + (((Pv >> 3) ^ (2 * qd)) & 3) * 16 + 2 * (Pv & 7);
   const int vb1 = 8 * qd * 64 + (((Pv >> 3) ^ (2 * qd + 1)) & 3) * 16 + 2 * (Pv & 7);
-  // loads of item j: K as the A fragments, V as key pairs; keys past the
-  // block's end re-read its last key (masked below)
-  auto load = [&](int j, StepQuarter& x, int& nvalid) {
-    const int s = first_slot + SPLIT * NW * (j / nq);
-    const int qq = j % nq;
+  // geometry of this wave's j-th item: its quarter's first K / V rows and its
+  // valid keys (keys past the block's end re-read its last key, masked below)
+  auto item = [&](int j, const u16*& Kq, const u16*& Vq, int& nv) {
+    const int it = wave + NW * j;
+    const int s = h + SPLIT * (it / nq);
+    const int qq = it % nq;
     const int blk = sel[s];
     const int64_t kblk = static_cast<int64_t>(blk) * a.Bk;
     const int nblk = static_cast<int>(len - kblk < a.Bk ? len - kblk : a.Bk);
     const int64_t row0 = a.pc.table ? (paged_page(a.pc, b, blk) * a.G + g) * kBlock
                                     : bg * a.N + kblk;
-    nvalid = nblk - 32 * qq < 32 ? nblk - 32 * qq : 32;
+    nv = nblk - 32 * qq < 32 ? nblk - 32 * qq : 32;
     const int first = 32 * qq < nblk ? 32 * qq : nblk - 1;
-    const u16* Kq = a.K + (row0 + first) * kHeadDim;
-    const u16* Vq = a.V + (row0 + first) * kHeadDim;
-    const int lim = nvalid > 0 ? nvalid - 1 : 0;
+    Kq = a.K + (row0 + first) * kHeadDim;
+    Vq = a.V + (row0 + first) * kHeadDim;
+  };
+  auto load_k = [&](StepQuarter& x, const u16* Kq, int nv) {
+    const int lim = nv > 0 ? nv - 1 : 0;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int key = 16 * t + col;
@@ -1351,6 +1365,9 @@ __global__ void __launch_bounds__(512, 1) decode_step_kernel(StepArgs a) {
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) x.kf[t][s4] = ld16(kr + 32 * s4);
     }
+  };
+  auto load_v = [&](StepQuarter& x, const u16* Vq, int nv) {
+    const int lim = nv > 0 ? nv - 1 : 0;
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int k0 = 2 * col, c = qd + 4 * j4;
@@ -1364,15 +1381,22 @@ __global__ void __launch_bounds__(512, 1) decode_step_kernel(StepArgs a) {
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{};
+  // One buffer: item j's V goes to LDS and its K into the S product, then
+  // item j + 1's V loads go out (landing during item j's softmax and PV) and
+  // its K loads after them.  Loads past the last item re-read it.  (Two
+  // buffers, item j + 2 in flight beside j + 1, measured slower: 220.6
+  // against 217.4 us per decode step.)
   StepQuarter cur;
-  int nv_cur = 0;
-  if (nitems > 0) load(0, cur, nv_cur);
-  for (int j = 0; j < nitems; ++j) {
-    // the next quarter's loads first (the last item re-reads itself)
-    StepQuarter nxt;
-    int nv_nxt;
-    load(j + 1 < nitems ? j + 1 : j, nxt, nv_nxt);
-    const int nv = nv_cur;
+  int nvalid = 0;
+  if (mine > 0) {
+    const u16 *Kq, *Vq;
+    item(0, Kq, Vq, nvalid);
+    load_k(cur, Kq, nvalid);
+    load_v(cur, Vq, nvalid);
+  }
+  for (int j = 0; j < mine; ++j) {
+    const int nv = nvalid;
+    f32x4 sc[2] = {f32x4{}, f32x4{}};
     if (nv > 0) {
       // V -> V^T: task j4 of a lane holds keys 2 col, 2 col + 1 and d = 8 qd +
       // 32 j4 + e; dec_vt's swizzle depends on e >> 2 only, so two base
@@ -1394,12 +1418,16 @@ __global__ void __launch_bounds__(512, 1) decode_step_kernel(StepArgs a) {
         }
       }
       // S^T tiles: lane holds head col, keys 16t + 4qd + r
-      f32x4 sc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
           sc[t] = mfma16(as_bf16x8(cur.kf[t][s4]), as_bf16x8(qs[s4][lane]), sc[t]);
+    }
+    const u16 *Kq, *Vq;
+    item(j + 1 < mine ? j + 1 : j, Kq, Vq, nvalid);
+    load_v(cur, Vq, nvalid);
+    if (nv > 0) {
       float mq = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -1437,8 +1465,7 @@ __global__ void __launch_bounds__(512, 1) decode_step_kernel(StepArgs a) {
         o[dt] = mfma16(as_bf16x8(av), as_bf16x8(pf), o[dt] * alpha);
       }
     }
-    cur = nxt;
-    nv_cur = nv_nxt;
+    load_k(cur, Kq, nvalid);
   }
 
   // the waves' (max, sum, O) meet in LDS
@@ -1520,27 +1547,32 @@ __global__ void __launch_bounds__(256) decode_step_merge_kernel(StepArgs a, int6
 }
 
 // Rows below which the step splits each row over two workgroups.
-constexpr int64_t kStepSplitRows = 256;
+#ifndef MSA_STEP_SPLIT_ROWS
+#define MSA_STEP_SPLIT_ROWS 256
+#endif
+constexpr int64_t kStepSplitRows = MSA_STEP_SPLIT_ROWS;
 
 size_t decode_step_scratch_bytes(int64_t B, int G, int Hq) {
   if (B * G >= kStepSplitRows) return 0;
-  const int64_t pr = B * G * 2 * (Hq / G);
+  const int64_t pr = B * G * kStepParts * (Hq / G);
   return static_cast<size_t>(pr) * (kHeadDim * sizeof(float) + sizeof(float2));
 }
 
 template <int HG>
 static hipError_t launch_step_t(const StepArgs& sa, int64_t rows, hipStream_t st) {
   if (rows >= kStepSplitRows) {
-    hipLaunchKernelGGL((decode_step_kernel<HG, 1>), dim3(static_cast<unsigned>(rows)), dim3(512),
-                       0, st, sa);
+    hipLaunchKernelGGL((decode_step_kernel<HG, 1>), dim3(static_cast<unsigned>(rows)),
+                       dim3(64 * kStepWaves), 0, st, sa);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_step_kernel<HG, 2>), dim3(static_cast<unsigned>(2 * rows)),
-                     dim3(512), 0, st, sa);
+  hipLaunchKernelGGL((decode_step_kernel<HG, kStepParts>),
+                     dim3(static_cast<unsigned>(kStepParts * rows)), dim3(64 * kStepWaves), 0, st,
+                     sa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t heads = rows * HG;
-  hipLaunchKernelGGL((decode_step_merge_kernel<2>), dim3(static_cast<unsigned>((heads + 3) / 4)),
+  hipLaunchKernelGGL((decode_step_merge_kernel<kStepParts>),
+                     dim3(static_cast<unsigned>((heads + 3) / 4)),
                      dim3(256), 0, st, sa, heads);
   return hipGetLastError();
 }
@@ -1559,7 +1591,8 @@ hipError_t launch_decode_step(const float* S, const void* q, const void* K, cons
   sa.lse = lse;
   const int64_t rows = B * G;
   sa.part = static_cast<float*>(scratch);
-  sa.ml = reinterpret_cast<float2*>(static_cast<float*>(scratch) + rows * 2 * (Hq / G) * kHeadDim);
+  sa.ml = reinterpret_cast<float2*>(static_cast<float*>(scratch) +
+                                    rows * kStepParts * (Hq / G) * kHeadDim);
   sa.N = N;
   sa.Hq = Hq;
   sa.G = G;
