@@ -536,10 +536,11 @@ def decode_leg(args, fp8=False, cpu=False):
     if "decode_step" in kt:
         da = kt["decode_step"]["avg_launch_ms"]
         ach = by["kv"] / (da * 1e-3) / 1e9
+        parts = 2 if w.B * w.G < 256 else 1  # workgroups per (sequence, group) row
+        name = "decode_step_kernel<%d, %d>" % (w.Hq // w.G, parts)
         out["roofline_attention"] = roof(
-            "decode_step_kernel<%d> (stages 3-4: selection, selected K/V blocks, merge)"
-            % (w.Hq // w.G), "hbm", ach, PEAK_HBM_GBS, "GB/s",
-            counter_traffic("decode_step_kernel<%d>" % (w.Hq // w.G)),
+            name + " (stages 3-4: selection, selected K/V blocks, merge; with its merge kernel)",
+            "hbm", ach, PEAK_HBM_GBS, "GB/s", counter_traffic(name),
             bytes_per_launch=by["kv"], avg_launch_ms=da)
     if cpu and not fp8:
         out["cpu_baseline"] = cpu_full(w, inp)
