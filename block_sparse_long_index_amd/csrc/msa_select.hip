@@ -705,8 +705,8 @@ __device__ __forceinline__ TopkRow topk_row(const TopkArgs& a, int64_t r) {
 }
 
 __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
-  __shared__ float cv[4][64];
-  __shared__ int ci[4][64];
+  __shared__ float cv[4][128];
+  __shared__ int ci[4][128];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (row >= a.rows) return;

@@ -92,7 +92,8 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
 // Best m candidates (score desc, index asc) among src[e] for e = e0 + lane +
 // step*i < n, left best-first in lanes 0..m-1 (m <= 63).  The first R strided
 // chunks are loaded once into registers, all loads in flight together; any
-// remainder is re-read from memory.  cv/ci: this wave's 64-entry LDS scratch.
+// remainder is re-read from memory.  cv/ci: this wave's 128-entry LDS scratch
+// (64 compacted candidates, then one spare entry per lane).
 // Returns the number of candidates compacted into cv/ci in ascending index
 // order (all those >= the threshold, a superset of the best m), or -1 when
 // there were too many for the scratch (the best m then came from a running
@@ -118,15 +119,17 @@ __device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int st
   // candidates >= tau, compacted in index order while they fit the scratch;
   // cnt counts them all (the same in every lane)
   int cnt = 0;
+  // every lane stores: a kept candidate at its compacted position, any
+  // other value in the lane's own spare entry 64 + lane (never read), so
+  // the loop has no exec-mask branches
   auto chunk = [&](int c0, float xv) {
     const int e = c0 + lane;
     const bool f = (e < n) & (xv >= tau);
     const unsigned long long bal = __ballot(f);
     const int pos = cnt + lanes_below(bal);
-    if (f & (pos < 64)) {
-      cv[pos] = xv;
-      ci[pos] = e;
-    }
+    const int slot = (f & (pos < 64)) ? pos : 64 + lane;
+    cv[slot] = xv;
+    ci[slot] = e;
     cnt += __popcll(bal);
   };
   auto merge = [&](int c0, float xv) {
@@ -224,8 +227,8 @@ __device__ __forceinline__ void write_selection(int32_t* out, int vi, int m, int
 // 64-candidate chunk of s[0..L) and leaves its best m in LDS.  Part 2 (wave 0
 // only): orders the four lists and returns lane's selection entry (lanes < k).
 struct WideTopkLds {
-  float cv[4][64];
-  int ci[4][64];
+  float cv[4][128];
+  int ci[4][128];
   float mv[4][64];
   int mi[4][64];
 };
