@@ -13,14 +13,15 @@
 //   dK_j += c dS_j q,  dV_j += P_j dO.
 //
 // One workgroup per chunk (b, g, block, <= 128 queries, all heads of the
-// group): K (row-major and transposed) and V of the block stay in LDS while
-// the chunk's (query, head) rows stream through in passes of 32.  Wave w owns
-// keys 32w..32w+31 for S, dP, dS and its dK/dV accumulators (registers for the
-// whole chunk), and dims 32w..32w+31 of the pass's dq.  The dq of a (row,
-// slot) pair is written as a bf16 partial and the partials of a row are summed
-// in slot order by dq_combine_kernel; dK and dV of a chunk are added to the
-// fp32 outputs with one atomic add per element (a block's queries may span
-// several chunks and stages).
+// group): the block's K and V stay on the chip (K and V rows in registers,
+// K^T in LDS) while the chunk's (query, head) rows stream through in passes of
+// 32.  Score waves 0-3 own keys 32w..32w+31 for S, dP and dS and dims
+// 32w..32w+31 of the pass's dq; key-gradient waves 4-7 hold the dK / dV
+// accumulators of the same keys for the whole chunk and gather the rows.  The
+// dq of a (row, slot) pair is written as a bf16 partial and the partials of a
+// row are summed in slot order by dq_combine_kernel; dK and dV of a chunk are
+// added to the fp32 outputs with one atomic add per element (a block's queries
+// may span several chunks and stages).
 #include "msa_common.h"
 #include "msa_internal.h"
 
@@ -30,6 +31,9 @@ namespace msa {
 
 constexpr int kBP = 272;  // LDS row pitch (bytes) of every 128-column bf16 tile
 constexpr int kTP = 80;   // LDS row pitch of the transposed 32-row q and dO tiles
+// One pass's P and dS operands for the dK / dV products: [score wave][j][lane]
+// 16-byte slots, j = 0, 1: P of k-steps 0, 1; j = 2, 3: dS of k-steps 0, 1.
+constexpr int kPdBytes = 4 * 4 * 64 * 16;
 
 // Column of pass row r (0..31) in the transposed q / dO tiles.  The dK / dV
 // products take a lane's P (or dS) values of k-step s in the order
@@ -64,16 +68,29 @@ struct BwdArgs {
 
 // TW: also write the teacher of the index branch's KL alignment, the mean over
 // the group's heads of P, per (row, slot, key).
+//
+// Eight waves, two per SIMD, in two roles that run side by side:
+//  * score waves 0-3: wave w keeps the K and V rows of keys 32w..32w+31 in
+//    registers; per pass it forms S and dP (rows x its keys), P and dS, and
+//    the dq of the previous pass for dims 32w..32w+31 (from the dS tile of all
+//    keys in LDS);
+//  * key-gradient waves 4-7: wave 4 + w holds the dK and dV accumulators of
+//    the same 32 keys and adds pass p - 1's P^T dO and dS^T q while the score
+//    waves work on pass p; they also gather every pass's q / dO rows.
+// The score waves hand P and dS over through LDS in their own register order
+// (a 16-byte slot per lane and k-step), which is exactly the A operand layout
+// of the key-gradient products, so neither side rearranges them.  Each pass
+// ends with two workgroup barriers that both roles reach the same number of
+// times: after the first, the key-gradient waves store the next pass's rows.
 template <int HG, bool TW>
-__global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
-  __shared__ __align__(16) unsigned char ks[128 * kBP];  // K [key][d]
-  __shared__ __align__(16) unsigned char vs[128 * kBP];  // V [key][d]
-  __shared__ __align__(16) unsigned char kt[128 * kBP];  // K^T [d][key]
-  __shared__ __align__(16) unsigned char qs[32 * kBP];   // the pass's q rows [row][d]
-  __shared__ __align__(16) unsigned char gs[32 * kBP];   // the pass's dO rows [row][d]
-  __shared__ __align__(16) unsigned char qT[128 * kTP];  // q^T [d][tpos(row)]
-  __shared__ __align__(16) unsigned char gT[128 * kTP];  // dO^T [d][tpos(row)]
+__global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
+  __shared__ __align__(16) unsigned char kt[128 * kBP];     // K^T [d][key]
+  __shared__ __align__(16) unsigned char qs[32 * kBP];      // the pass's q rows [row][d]
+  __shared__ __align__(16) unsigned char gs[32 * kBP];      // the pass's dO rows [row][d]
+  __shared__ __align__(16) unsigned char qT[2][128 * kTP];  // q^T [d][tpos(row)], by pass parity
+  __shared__ __align__(16) unsigned char gT[2][128 * kTP];  // dO^T [d][tpos(row)]
   __shared__ __align__(16) unsigned char dss[2][32 * kBP];  // dS [row][key], bf16, scaled by c
+  __shared__ __align__(16) unsigned char pd[2][kPdBytes];   // P, dS operands [wave][j][lane]
   __shared__ float r_l2[32], r_D[32];
   __shared__ int r_lim[32], r_prow[2][32];
   __shared__ int ents[kChunkQueries];  // the chunk's (row << 6 | slot) entries
@@ -97,24 +114,22 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
   const int half = lane >> 5, l32 = lane & 31;
 
   const int64_t key0 = blk * a.Bk;
-  // the block's keys (>= 1); LDS rows past them are zero and masked
+  // the block's keys (>= 1); K^T columns past them are zero
   const int nvalid = static_cast<int>(a.N - key0 < a.Bk ? a.N - key0 : a.Bk);
   const u16* Kb = a.K + (bg * a.N + key0) * kHeadDim;
   const u16* Vb = a.V + (bg * a.N + key0) * kHeadDim;
 
-  // K: 64 key pairs x 16 chunks of 8 dims; each pair goes to ks row-major and
-  // to kt as 32-bit (key, key + 1) words.  Keys past N are zero.
+  // K^T: 64 key pairs x 16 chunks of 8 dims, stored as 32-bit (key, key + 1)
+  // words.  Keys past N are zero.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = tid + 256 * j;
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + 512 * j;
     const int kp = i & 63, c = i >> 6;
     const int k0 = 2 * kp;
     const uint4 y0 = ld16(Kb + (k0 < nvalid ? k0 : nvalid - 1) * kHeadDim + 8 * c);
     const uint4 y1 = ld16(Kb + (k0 + 1 < nvalid ? k0 + 1 : nvalid - 1) * kHeadDim + 8 * c);
     const uint4 x0 = k0 < nvalid ? y0 : make_uint4(0, 0, 0, 0);
     const uint4 x1 = k0 + 1 < nvalid ? y1 : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(&ks[k0 * kBP + 16 * c]) = x0;
-    *reinterpret_cast<uint4*>(&ks[(k0 + 1) * kBP + 16 * c]) = x1;
     const uint32_t w0[4] = {x0.x, x0.y, x0.z, x0.w};
     const uint32_t w1[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
@@ -124,273 +139,308 @@ __global__ void __launch_bounds__(256, 1) kv_outer_bwd_kernel(BwdArgs a) {
       *reinterpret_cast<uint32_t*>(&kt[(8 * c + e) * kBP + 2 * k0]) = lo | (hi << 16);
     }
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = tid + 256 * j;
-    const int r = i >> 4, c = i & 15;
-    const uint4 y = ld16(Vb + (r < nvalid ? r : nvalid - 1) * kHeadDim + 8 * c);
-    *reinterpret_cast<uint4*>(&vs[r * kBP + 16 * c]) = r < nvalid ? y : make_uint4(0, 0, 0, 0);
-  }
-
-  for (int i = tid; i < n; i += 256) ents[i] = a.entries[ch.y + i];
+  for (int i = tid; i < n; i += 512) ents[i] = a.entries[ch.y + i];
   __syncthreads();
   const int rows = n * HG;
+  const int npass = (rows + 31) / 32;
   const int64_t t0 = a.r0 - b * a.T;
-  const int key_w = 32 * wave + l32;  // this lane's key in S, dP, dS
   constexpr float kLog2e = 1.4426950408889634f;
   constexpr float kScale = 0.08838834764831845f;  // 1/sqrt(128)
-  const float qscale = kLog2e * kScale;
-  f32x16 dk[4], dv[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    dk[dt] = f32x16{};
-    dv[dt] = f32x16{};
-  }
 
-  // A pass's gather, one thread's share: rows 2 rp and 2 rp + 1, dims
-  // 8 cc .. 8 cc + 7 of q and dO, plus (for cc == 0) the rows' lse, D, causal
-  // limit and partial row.  Rows past the chunk's end are zero with lse = +inf
-  // and an empty causal range, so they add nothing to dK and dV; their dq
-  // goes to the sink row.  The next pass's loads are issued before the
-  // current pass's products and written to LDS after them.
-  // (rp varies fastest across lanes: one wave's stores to a transposed tile
-  // row then hit 16 consecutive words instead of one bank 16 times)
-  const int rp = tid & 15, cc = tid >> 4;
-  uint4 fq[2], fg[2];
-  float fl[2], fD[2];
-  int flim[2], fprow[2];
-  bool fvalid[2];
-  // fetch only issues loads (every lane, valid addresses; nothing uses them
-  // before stash: a use under a branch would make the compiler wait for the
-  // loads there, ahead of the pass's products)
-  auto fetch = [&](int pass) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int rr = pass * 32 + 2 * rp + u;
-      const bool valid = rr < rows;
-      const int qi = valid ? rr / HG : 0;
-      const int hh = rr % HG;
-      const int e = ents[qi];
-      const int64_t t = t0 + (e >> 6);
-      const int64_t hq = static_cast<int64_t>(g) * HG + hh;
-      const int64_t off = ((b * a.T + t) * a.Hq + hq) * kHeadDim + 8 * cc;
-      fq[u] = ld16(a.q + off);
-      fg[u] = ld16(a.dO + off);
-      fl[u] = a.lse[(b * a.Hq + hq) * a.T + t];
-      fD[u] = a.Dr[(b * a.T + t) * a.Hq + hq];
-      fvalid[u] = valid;
-      flim[u] = valid ? static_cast<int>(min(a.N - a.T + t - key0, static_cast<int64_t>(nvalid - 1)))
-                       : -1;  // last key of the block the row sees
-      fprow[u] = valid ? (((e >> 6) - a.rl_base) * a.k + (e & 63)) * HG + hh : a.sink + hh;
-    }
-  };
-  auto stash = [&](int pass) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (!fvalid[u]) {
-        fq[u] = make_uint4(0, 0, 0, 0);
-        fg[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    const int r0 = 2 * rp;
-    *reinterpret_cast<uint4*>(&qs[r0 * kBP + 16 * cc]) = fq[0];
-    *reinterpret_cast<uint4*>(&qs[(r0 + 1) * kBP + 16 * cc]) = fq[1];
-    *reinterpret_cast<uint4*>(&gs[r0 * kBP + 16 * cc]) = fg[0];
-    *reinterpret_cast<uint4*>(&gs[(r0 + 1) * kBP + 16 * cc]) = fg[1];
-    const int P = tpos(r0);  // even; row r0 + 1 sits at P + 1
-    const uint32_t q0[4] = {fq[0].x, fq[0].y, fq[0].z, fq[0].w};
-    const uint32_t q1[4] = {fq[1].x, fq[1].y, fq[1].z, fq[1].w};
-    const uint32_t g0[4] = {fg[0].x, fg[0].y, fg[0].z, fg[0].w};
-    const uint32_t g1[4] = {fg[1].x, fg[1].y, fg[1].z, fg[1].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = 16 * (e & 1);
-      const int o = (8 * cc + e) * kTP + 2 * P;
-      *reinterpret_cast<uint32_t*>(&qT[o]) =
-          ((q0[e >> 1] >> sh) & 0xffffu) | (((q1[e >> 1] >> sh) & 0xffffu) << 16);
-      *reinterpret_cast<uint32_t*>(&gT[o]) =
-          ((g0[e >> 1] >> sh) & 0xffffu) | (((g1[e >> 1] >> sh) & 0xffffu) << 16);
-    }
-    if (cc == 0) {
+  if (wave >= 4) {
+    // ---- key-gradient waves ----
+    const int gw = wave - 4;
+    // A pass's gather, one thread's share: rows 2 rp and 2 rp + 1, dims
+    // 8 cc .. 8 cc + 7 of q and dO, plus (for cc == 0) the rows' lse, D,
+    // causal limit and partial row.  Rows past the chunk's end are zero with
+    // lse = +inf and an empty causal range, so they add nothing to dK and dV;
+    // their dq goes to the sink row.  (rp varies fastest across lanes: one
+    // wave's stores to a transposed tile row then hit 16 consecutive words
+    // instead of one bank 16 times.)
+    const int t = tid - 256;
+    const int rp = t & 15, cc = t >> 4;
+    uint4 fq[2], fg[2];
+    float fl[2], fD[2];
+    int flim[2], fprow[2];
+    bool fvalid[2];
+    // fetch only issues loads (every lane, valid addresses; nothing uses them
+    // before stash: a use under a branch would make the compiler wait for the
+    // loads there)
+    auto fetch = [&](int pass) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        r_l2[r0 + u] = fvalid[u] ? fl[u] * kLog2e : INFINITY;
-        r_D[r0 + u] = fvalid[u] ? fD[u] : 0.f;
-        r_lim[r0 + u] = flim[u];
-        r_prow[pass & 1][r0 + u] = fprow[u];
+        const int rr = pass * 32 + 2 * rp + u;
+        const bool valid = rr < rows;
+        const int qi = valid ? rr / HG : 0;
+        const int hh = rr % HG;
+        const int e = ents[qi];
+        const int64_t tt = t0 + (e >> 6);
+        const int64_t hq = static_cast<int64_t>(g) * HG + hh;
+        const int64_t off = ((b * a.T + tt) * a.Hq + hq) * kHeadDim + 8 * cc;
+        fq[u] = ld16(a.q + off);
+        fg[u] = ld16(a.dO + off);
+        fl[u] = a.lse[(b * a.Hq + hq) * a.T + tt];
+        fD[u] = a.Dr[(b * a.T + tt) * a.Hq + hq];
+        fvalid[u] = valid;
+        flim[u] = valid ? static_cast<int>(min(a.N - a.T + tt - key0,
+                                               static_cast<int64_t>(nvalid - 1)))
+                        : -1;  // last key of the block the row sees
+        fprow[u] = valid ? (((e >> 6) - a.rl_base) * a.k + (e & 63)) * HG + hh : a.sink + hh;
       }
-    }
-  };
-  fetch(0);
-  stash(0);
-  __syncthreads();
-
-  // dq^T of this wave's 32 dims x pass p's 32 rows = K^T dS^T over the 128
-  // keys, from dss[p & 1]; stored as the (row, slot) partial, lane = row l32:
-  // the lane's 16 values (dims 32 wave + 8(i/4) + 4 half + i%4) go
-  // contiguously to element 32 wave + 16 half of the partial row (see
-  // dq_combine_kernel).
-  const unsigned char* ka = kt + (32 * wave + l32) * kBP + half * 16;
-  auto store_dq = [&](int p, const f32x16& qacc) {
-    const int prow = r_prow[p & 1][l32];
-    u16* dst = a.dqpart + static_cast<int64_t>(prow) * kHeadDim + 32 * wave + 16 * half;
-    uint4 w0, w1;
-    w0.x = pack_bf16x2(qacc[0], qacc[1]);
-    w0.y = pack_bf16x2(qacc[2], qacc[3]);
-    w0.z = pack_bf16x2(qacc[4], qacc[5]);
-    w0.w = pack_bf16x2(qacc[6], qacc[7]);
-    w1.x = pack_bf16x2(qacc[8], qacc[9]);
-    w1.y = pack_bf16x2(qacc[10], qacc[11]);
-    w1.z = pack_bf16x2(qacc[12], qacc[13]);
-    w1.w = pack_bf16x2(qacc[14], qacc[15]);
-    *reinterpret_cast<uint4*>(dst) = w0;
-    *reinterpret_cast<uint4*>(dst + 8) = w1;
-  };
-
-  // The teacher of the pass's queries at this lane's key: the lane's P values
-  // are rows m(i) = 8(i/4) + 4 half + i%4, a query's HG head rows are
-  // consecutive, so the head sum is in-lane (HG <= 4), in-lane plus the other
-  // half-wave (HG = 8, HG = 16).  Rows past the chunk's end (partial row >=
-  // sink) write nothing; keys past Bk belong to no block (wave-uniform test).
-  auto write_teacher = [&](int pass, const float* pr) {
-    if (32 * wave >= a.Bk) return;
-    const int* rpw = r_prow[pass & 1];
-    auto put = [&](int m, float sum) {
-      const int pw = rpw[m];  // (row, slot) entry * HG for the query's first head
-      if (pw < a.sink)  // read once, by the KL pass: kept out of the caches
-        __builtin_nontemporal_store(sum * (1.f / HG),
-                                    a.teach + static_cast<int64_t>(pw / HG) * a.Bk + key_w);
     };
-    if constexpr (HG <= 4) {
+    auto stash = [&](int pass) {
 #pragma unroll
-      for (int i = 0; i < 16; i += HG) {
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < HG; ++j) sum += pr[i + j];
-        put(8 * (i >> 2) + 4 * half + (i & 3), sum);
+      for (int u = 0; u < 2; ++u) {
+        if (!fvalid[u]) {
+          fq[u] = make_uint4(0, 0, 0, 0);
+          fg[u] = make_uint4(0, 0, 0, 0);
+        }
       }
-    } else if constexpr (HG == 8) {
-      float sum[4];
+      const int r0 = 2 * rp;
+      *reinterpret_cast<uint4*>(&qs[r0 * kBP + 16 * cc]) = fq[0];
+      *reinterpret_cast<uint4*>(&qs[(r0 + 1) * kBP + 16 * cc]) = fq[1];
+      *reinterpret_cast<uint4*>(&gs[r0 * kBP + 16 * cc]) = fg[0];
+      *reinterpret_cast<uint4*>(&gs[(r0 + 1) * kBP + 16 * cc]) = fg[1];
+      const int P = tpos(r0);  // even; row r0 + 1 sits at P + 1
+      const uint32_t q0[4] = {fq[0].x, fq[0].y, fq[0].z, fq[0].w};
+      const uint32_t q1[4] = {fq[1].x, fq[1].y, fq[1].z, fq[1].w};
+      const uint32_t g0[4] = {fg[0].x, fg[0].y, fg[0].z, fg[0].w};
+      const uint32_t g1[4] = {fg[1].x, fg[1].y, fg[1].z, fg[1].w};
+      unsigned char* qTw = qT[pass & 1];
+      unsigned char* gTw = gT[pass & 1];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sum[j] = (pr[4 * j] + pr[4 * j + 1]) + (pr[4 * j + 2] + pr[4 * j + 3]);
-        sum[j] += __shfl_xor(sum[j], 32);
+      for (int e = 0; e < 8; ++e) {
+        const int sh = 16 * (e & 1);
+        const int o = (8 * cc + e) * kTP + 2 * P;
+        *reinterpret_cast<uint32_t*>(&qTw[o]) =
+            ((q0[e >> 1] >> sh) & 0xffffu) | (((q1[e >> 1] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<uint32_t*>(&gTw[o]) =
+            ((g0[e >> 1] >> sh) & 0xffffu) | (((g1[e >> 1] >> sh) & 0xffffu) << 16);
       }
-      // half h writes queries 2h and 2h + 1 (rows 16h and 16h + 8)
-      put(16 * half, half ? sum[2] : sum[0]);
-      put(16 * half + 8, half ? sum[3] : sum[1]);
-    } else {
-      static_assert(HG == 16, "heads per group");
-      float s0 = 0.f, s1 = 0.f;
+      if (cc == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        s0 += pr[j];
-        s1 += pr[8 + j];
+        for (int u = 0; u < 2; ++u) {
+          r_l2[r0 + u] = fvalid[u] ? fl[u] * kLog2e : INFINITY;
+          r_D[r0 + u] = fvalid[u] ? fD[u] : 0.f;
+          r_lim[r0 + u] = flim[u];
+          r_prow[pass & 1][r0 + u] = fprow[u];
+        }
       }
-      s0 += __shfl_xor(s0, 32);
-      s1 += __shfl_xor(s1, 32);
-      put(16 * half, half ? s1 : s0);  // half h writes query h
+    };
+    // dV += P^T dO and dK += dS^T q over pass p's rows: keys on M, dims on N;
+    // A = the score wave's P / dS slots, B = the transposed tiles (see tpos).
+    f32x16 dk[4], dv[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      dk[dt] = f32x16{};
+      dv[dt] = f32x16{};
     }
-  };
+    auto key_grads = [&](int p) {
+      const unsigned char* pdr = pd[p & 1] + (gw * 256 + lane) * 16;
+      const unsigned char* gTr = gT[p & 1];
+      const unsigned char* qTr = qT[p & 1];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint4 pa = *reinterpret_cast<const uint4*>(pdr + 1024 * s);
+        const uint4 da = *reinterpret_cast<const uint4*>(pdr + 1024 * (2 + s));
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int o = (32 * dt + l32) * kTP + 2 * (16 * s + 8 * half);
+          dv[dt] = mfma32(as_bf16x8(pa), as_bf16x8(*reinterpret_cast<const uint4*>(&gTr[o])),
+                          dv[dt]);
+          dk[dt] = mfma32(as_bf16x8(da), as_bf16x8(*reinterpret_cast<const uint4*>(&qTr[o])),
+                          dk[dt]);
+        }
+      }
+    };
+    fetch(0);
+    stash(0);
+    __syncthreads();  // pass 0's rows are in LDS
+    for (int pass = 0; pass < npass; ++pass) {
+      const bool more = pass + 1 < npass;
+      fetch(more ? pass + 1 : pass);
+      if (pass > 0) key_grads(pass - 1);
+      // the score waves are done with pass's rows (qs, gs, r_*) and have
+      // stored pass's P / dS; this wave is done with pass - 1's tiles
+      __syncthreads();
+      if (more) {
+        stash(pass + 1);
+        __syncthreads();
+      }
+    }
+    key_grads(npass - 1);
 
-  // Pass p: the S / dP products of pass p run beside the dq product of pass
-  // p - 1 (two independent MFMA streams), then P, dS (into dss[p & 1]) and
-  // dK / dV; a barrier; the next pass's rows go to LDS; a barrier.
-  const int npass = (rows + 31) / 32;
-  for (int pass = 0; pass < npass; ++pass) {
-    const bool more = pass + 1 < npass;
-    fetch(more ? pass + 1 : pass);
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-    f32x16 q0 = f32x16{}, q1 = f32x16{};
-    {
-      const unsigned char* qa = qs + l32 * kBP + half * 16;
-      const unsigned char* ga = gs + l32 * kBP + half * 16;
-      const unsigned char* kb = ks + key_w * kBP + half * 16;
-      const unsigned char* vb = vs + key_w * kBP + half * 16;
-      // dS of pass p - 1 (for pass 0 this reads the other buffer's stale
-      // contents, and the result is not stored)
-      const unsigned char* db = dss[(pass + 1) & 1] + l32 * kBP + half * 16;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(qa + 32 * s)),
-                      as_bf16x8(*reinterpret_cast<const uint4*>(kb + 32 * s)), sacc);
-        pacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ga + 32 * s)),
-                      as_bf16x8(*reinterpret_cast<const uint4*>(vb + 32 * s)), pacc);
-        if (s & 1)
-          q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
-                      as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q1);
-        else
-          q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
-                      as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
-      }
-    }
-    // P and c*dS; lane: key key_w, rows m(i) = 8(i/4) + 4 half + i%4
-    unsigned char* dsw = dss[pass & 1];
-    float pr[16], dsr[16];
+    // dK, dV of this wave's keys: lane = dim 32 dt + l32, keys m(i)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int m = 8 * (i >> 2) + 4 * half + (i & 3);
-      const float ex = fast_exp2(fmaf(sacc[i], qscale, -r_l2[m]));
-      const float p = key_w <= r_lim[m] ? ex : 0.f;
-      pr[i] = p;
-      dsr[i] = p * (pacc[i] - r_D[m]) * kScale;
-      *reinterpret_cast<u16*>(&dsw[m * kBP + 2 * key_w]) = f32_to_bf16(dsr[i]);
-    }
-    if (pass > 0) store_dq(pass - 1, q0 + q1);
-    // dV += P^T dO and dK += dS^T q over the pass's rows: keys on M, dims on
-    // N; the B operands are the transposed tiles (see tpos).
+      const int64_t key = key0 + 32 * gw + 8 * (i >> 2) + 4 * half + (i & 3);
+      if (key < key0 + nvalid) {
+        float* pk = a.dK + (bg * a.N + key) * kHeadDim + l32;
+        float* pv = a.dV + (bg * a.N + key) * kHeadDim + l32;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint4 pa = make_uint4(pack_bf16x2(pr[8 * s + 0], pr[8 * s + 1]),
-                                  pack_bf16x2(pr[8 * s + 2], pr[8 * s + 3]),
-                                  pack_bf16x2(pr[8 * s + 4], pr[8 * s + 5]),
-                                  pack_bf16x2(pr[8 * s + 6], pr[8 * s + 7]));
-      const uint4 da = make_uint4(pack_bf16x2(dsr[8 * s + 0], dsr[8 * s + 1]),
-                                  pack_bf16x2(dsr[8 * s + 2], dsr[8 * s + 3]),
-                                  pack_bf16x2(dsr[8 * s + 4], dsr[8 * s + 5]),
-                                  pack_bf16x2(dsr[8 * s + 6], dsr[8 * s + 7]));
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int o = (32 * dt + l32) * kTP + 2 * (16 * s + 8 * half);
-        dv[dt] = mfma32(as_bf16x8(pa), as_bf16x8(*reinterpret_cast<const uint4*>(&gT[o])), dv[dt]);
-        dk[dt] = mfma32(as_bf16x8(da), as_bf16x8(*reinterpret_cast<const uint4*>(&qT[o])), dk[dt]);
+        for (int dt = 0; dt < 4; ++dt) {
+          unsafeAtomicAdd(pk + 32 * dt, dk[dt][i]);
+          unsafeAtomicAdd(pv + 32 * dt, dv[dt][i]);
+        }
       }
     }
-    // the teacher's stores go out after the pass's products, not among them
-    if constexpr (TW) write_teacher(pass, pr);
-    // every wave is done with this pass's rows and with dss[(pass + 1) & 1];
-    // dss[pass & 1] is complete
-    __syncthreads();
-    if (more) {
-      stash(pass + 1);
-      __syncthreads();
-    }
-  }
-  {  // dq of the last pass
-    const unsigned char* db = dss[(npass - 1) & 1] + l32 * kBP + half * 16;
-    f32x16 q0 = f32x16{}, q1 = f32x16{};
+  } else {
+    // ---- score waves ----
+    const int key_w = 32 * wave + l32;  // this lane's key in S, dP, dS
+    const float qscale = kLog2e * kScale;
+    // this wave's keys' K and V rows (the B operands of S and dP, 8 k-steps
+    // each) stay in registers for the whole chunk; rows past the block's end
+    // repeat its last key (their P is masked to 0)
+    uint4 kf[8], vf[8];
+    {
+      const int kr = key_w < nvalid ? key_w : nvalid - 1;
+      const u16* kp = Kb + static_cast<int64_t>(kr) * kHeadDim + 8 * half;
+      const u16* vp = Vb + static_cast<int64_t>(kr) * kHeadDim + 8 * half;
 #pragma unroll
-    for (int s = 0; s < 8; s += 2) {
-      q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
-                  as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
-      q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s + 32)),
-                  as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s + 32)), q1);
+      for (int s = 0; s < 8; ++s) {
+        kf[s] = ld16(kp + 16 * s);
+        vf[s] = ld16(vp + 16 * s);
+      }
     }
-    store_dq(npass - 1, q0 + q1);
-  }
+    // dq^T of this wave's 32 dims x pass p's 32 rows = K^T dS^T over the 128
+    // keys, from dss[p & 1]; stored as the (row, slot) partial, lane = row
+    // l32: the lane's 16 values (dims 32 wave + 8(i/4) + 4 half + i%4) go
+    // contiguously to element 32 wave + 16 half of the partial row (see
+    // dq_combine_kernel).
+    const unsigned char* ka = kt + (32 * wave + l32) * kBP + half * 16;
+    auto store_dq = [&](int p, const f32x16& qacc) {
+      const int prow = r_prow[p & 1][l32];
+      u16* dst = a.dqpart + static_cast<int64_t>(prow) * kHeadDim + 32 * wave + 16 * half;
+      uint4 w0, w1;
+      w0.x = pack_bf16x2(qacc[0], qacc[1]);
+      w0.y = pack_bf16x2(qacc[2], qacc[3]);
+      w0.z = pack_bf16x2(qacc[4], qacc[5]);
+      w0.w = pack_bf16x2(qacc[6], qacc[7]);
+      w1.x = pack_bf16x2(qacc[8], qacc[9]);
+      w1.y = pack_bf16x2(qacc[10], qacc[11]);
+      w1.z = pack_bf16x2(qacc[12], qacc[13]);
+      w1.w = pack_bf16x2(qacc[14], qacc[15]);
+      *reinterpret_cast<uint4*>(dst) = w0;
+      *reinterpret_cast<uint4*>(dst + 8) = w1;
+    };
 
-  // dK, dV of this wave's keys: lane = dim 32 dt + l32, keys m(i)
+    // The teacher of the pass's queries at this lane's key: the lane's P
+    // values are rows m(i) = 8(i/4) + 4 half + i%4, a query's HG head rows are
+    // consecutive, so the head sum is in-lane (HG <= 4), in-lane plus the
+    // other half-wave (HG = 8, HG = 16).  Rows past the chunk's end (partial
+    // row >= sink) write nothing; keys past Bk belong to no block
+    // (wave-uniform test).
+    auto write_teacher = [&](int pass, const float* pr) {
+      if (32 * wave >= a.Bk) return;
+      const int* rpw = r_prow[pass & 1];
+      auto put = [&](int m, float sum) {
+        const int pw = rpw[m];  // (row, slot) entry * HG for the query's first head
+        if (pw < a.sink)  // read once, by the KL pass: kept out of the caches
+          __builtin_nontemporal_store(sum * (1.f / HG),
+                                      a.teach + static_cast<int64_t>(pw / HG) * a.Bk + key_w);
+      };
+      if constexpr (HG <= 4) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t key = key0 + 32 * wave + 8 * (i >> 2) + 4 * half + (i & 3);
-    if (key < key0 + nvalid) {
-      float* pk = a.dK + (bg * a.N + key) * kHeadDim + l32;
-      float* pv = a.dV + (bg * a.N + key) * kHeadDim + l32;
+        for (int i = 0; i < 16; i += HG) {
+          float sum = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        unsafeAtomicAdd(pk + 32 * dt, dk[dt][i]);
-        unsafeAtomicAdd(pv + 32 * dt, dv[dt][i]);
+          for (int j = 0; j < HG; ++j) sum += pr[i + j];
+          put(8 * (i >> 2) + 4 * half + (i & 3), sum);
+        }
+      } else if constexpr (HG == 8) {
+        float sum[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sum[j] = (pr[4 * j] + pr[4 * j + 1]) + (pr[4 * j + 2] + pr[4 * j + 3]);
+          sum[j] += __shfl_xor(sum[j], 32);
+        }
+        // half h writes queries 2h and 2h + 1 (rows 16h and 16h + 8)
+        put(16 * half, half ? sum[2] : sum[0]);
+        put(16 * half + 8, half ? sum[3] : sum[1]);
+      } else {
+        static_assert(HG == 16, "heads per group");
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          s0 += pr[j];
+          s1 += pr[8 + j];
+        }
+        s0 += __shfl_xor(s0, 32);
+        s1 += __shfl_xor(s1, 32);
+        put(16 * half, half ? s1 : s0);  // half h writes query h
       }
+    };
+
+    __syncthreads();  // pass 0's rows are in LDS
+    // Pass p: the S / dP products of pass p run beside the dq product of pass
+    // p - 1 (two independent MFMA streams), then P and dS: into dss[p & 1]
+    // (row-major, for the next pass's dq) and into pd[p & 1] (the key-gradient
+    // waves' operands).
+    for (int pass = 0; pass < npass; ++pass) {
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      f32x16 q0 = f32x16{}, q1 = f32x16{};
+      {
+        const unsigned char* qa = qs + l32 * kBP + half * 16;
+        const unsigned char* ga = gs + l32 * kBP + half * 16;
+        // dS of pass p - 1 (for pass 0 this reads the other buffer's stale
+        // contents, and the result is not stored)
+        const unsigned char* db = dss[(pass + 1) & 1] + l32 * kBP + half * 16;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(qa + 32 * s)), as_bf16x8(kf[s]),
+                        sacc);
+          pacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ga + 32 * s)), as_bf16x8(vf[s]),
+                        pacc);
+          if (s & 1)
+            q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
+                        as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q1);
+          else
+            q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
+                        as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
+        }
+      }
+      // P and c*dS; lane: key key_w, rows m(i) = 8(i/4) + 4 half + i%4
+      unsigned char* dsw = dss[pass & 1];
+      float pr[16], dsr[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = 8 * (i >> 2) + 4 * half + (i & 3);
+        const float ex = fast_exp2(fmaf(sacc[i], qscale, -r_l2[m]));
+        const float p = key_w <= r_lim[m] ? ex : 0.f;
+        pr[i] = p;
+        dsr[i] = p * (pacc[i] - r_D[m]) * kScale;
+        *reinterpret_cast<u16*>(&dsw[m * kBP + 2 * key_w]) = f32_to_bf16(dsr[i]);
+      }
+      if (pass > 0) store_dq(pass - 1, q0 + q1);
+      unsigned char* pdw = pd[pass & 1] + (wave * 256 + lane) * 16;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        *reinterpret_cast<uint4*>(pdw + 1024 * s) =
+            make_uint4(pack_bf16x2(pr[8 * s + 0], pr[8 * s + 1]),
+                       pack_bf16x2(pr[8 * s + 2], pr[8 * s + 3]),
+                       pack_bf16x2(pr[8 * s + 4], pr[8 * s + 5]),
+                       pack_bf16x2(pr[8 * s + 6], pr[8 * s + 7]));
+        *reinterpret_cast<uint4*>(pdw + 1024 * (2 + s)) =
+            make_uint4(pack_bf16x2(dsr[8 * s + 0], dsr[8 * s + 1]),
+                       pack_bf16x2(dsr[8 * s + 2], dsr[8 * s + 3]),
+                       pack_bf16x2(dsr[8 * s + 4], dsr[8 * s + 5]),
+                       pack_bf16x2(dsr[8 * s + 6], dsr[8 * s + 7]));
+      }
+      if constexpr (TW) write_teacher(pass, pr);
+      __syncthreads();  // pass's P / dS are stored; its rows may be replaced
+      if (pass + 1 < npass) __syncthreads();  // the next pass's rows are in LDS
+    }
+    {  // dq of the last pass
+      const unsigned char* db = dss[(npass - 1) & 1] + l32 * kBP + half * 16;
+      f32x16 q0 = f32x16{}, q1 = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; s += 2) {
+        q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
+                    as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
+        q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s + 32)),
+                    as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s + 32)), q1);
+      }
+      store_dq(npass - 1, q0 + q1);
     }
   }
 }
@@ -480,10 +530,10 @@ static hipError_t launch_bwd_stage(const BwdArgs& ba, const DqArgs& da, int64_t 
     TimedLaunch tl(MSA_KERNEL_ATTN_BACKWARD, st);
     if (ba.teach)
       hipLaunchKernelGGL((kv_outer_bwd_kernel<HG, true>), dim3(static_cast<unsigned>(grid)),
-                         dim3(256), 0, st, ba);
+                         dim3(512), 0, st, ba);
     else
       hipLaunchKernelGGL((kv_outer_bwd_kernel<HG, false>), dim3(static_cast<unsigned>(grid)),
-                         dim3(256), 0, st, ba);
+                         dim3(512), 0, st, ba);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
