@@ -13,9 +13,8 @@
 //   dK_j += c dS_j q,  dV_j += P_j dO.
 //
 // One workgroup per chunk (b, g, block, <= 128 queries, all heads of the
-// group): the block's K and V stay on the chip (K and V rows in registers,
-// K^T in LDS) while the chunk's (query, head) rows stream through in passes of
-// 32.  Score waves 0-3 own keys 32w..32w+31 for S, dP and dS and dims
+// group): the block's K, V and K^T stay in registers while the chunk's
+// (query, head) rows stream through in passes of 32.  Score waves 0-3 own keys 32w..32w+31 for S, dP and dS and dims
 // 32w..32w+31 of the pass's dq; key-gradient waves 4-7 hold the dK / dV
 // accumulators of the same keys for the whole chunk and gather the rows.  The
 // dq of a (row, slot) pair is written as a bf16 partial and the partials of a
@@ -70,30 +69,36 @@ struct BwdArgs {
 // the group's heads of P, per (row, slot, key).
 //
 // Eight waves, two per SIMD, in two roles that run side by side:
-//  * score waves 0-3: wave w keeps the K and V rows of keys 32w..32w+31 in
-//    registers; per pass it forms S and dP (rows x its keys), P and dS, and
-//    the dq of the previous pass for dims 32w..32w+31 (from the dS tile of all
-//    keys in LDS);
+//  * score waves 0-3: wave w keeps the K and V rows of keys 32w..32w+31 and
+//    the K^T rows of dims 32w..32w+31 in registers; per pass it forms S and
+//    dP (rows x its keys), P and dS, and the dq of the previous pass for its
+//    dims (from the dS tile of all keys in LDS);
 //  * key-gradient waves 4-7: wave 4 + w holds the dK and dV accumulators of
 //    the same 32 keys and adds pass p - 1's P^T dO and dS^T q while the score
-//    waves work on pass p; they also gather every pass's q / dO rows.
+//    waves work on pass p; they also store pass p + 1's q / dO rows (loaded a
+//    pass earlier) and issue the loads of pass p + 2.
 // The score waves hand P and dS over through LDS in their own register order
 // (a 16-byte slot per lane and k-step), which is exactly the A operand layout
-// of the key-gradient products, so neither side rearranges them.  Each pass
-// ends with two workgroup barriers that both roles reach the same number of
-// times: after the first, the key-gradient waves store the next pass's rows.
+// of the key-gradient products, so neither side rearranges them.  Every
+// buffer a pass writes is distinct from those the other role reads in the
+// same pass (two row tiles, three transposed tiles, two P / dS and dS tiles,
+// three partial-row lists), so a pass ends with a single workgroup barrier,
+// reached by both roles the same number of times.
 template <int HG, bool TW>
 __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
-  __shared__ __align__(16) unsigned char kt[128 * kBP];     // K^T [d][key]
-  __shared__ __align__(16) unsigned char qs[32 * kBP];      // the pass's q rows [row][d]
-  __shared__ __align__(16) unsigned char gs[32 * kBP];      // the pass's dO rows [row][d]
-  __shared__ __align__(16) unsigned char qT[2][128 * kTP];  // q^T [d][tpos(row)], by pass parity
-  __shared__ __align__(16) unsigned char gT[2][128 * kTP];  // dO^T [d][tpos(row)]
-  __shared__ __align__(16) unsigned char dss[2][32 * kBP];  // dS [row][key], bf16, scaled by c
-  __shared__ __align__(16) unsigned char pd[2][kPdBytes];   // P, dS operands [wave][j][lane]
-  __shared__ float r_l2[32], r_D[32];
-  __shared__ int r_lim[32], r_prow[2][32];
+  constexpr int kRowTile = 32 * kBP;   // 32 rows x 128 dims, row-major
+  constexpr int kTTile = 128 * kTP;    // 128 dims x 32 rows, transposed
+  __shared__ __align__(16) unsigned char qs[2][kRowTile];    // the pass's q rows, by parity
+  __shared__ __align__(16) unsigned char gs[2][kRowTile];    // the pass's dO rows
+  // q^T and dO^T tiles [d][tpos(row)] of passes p mod 3; before the first
+  // pass the same bytes stage the block's K^T [d][key]
+  __shared__ __align__(16) unsigned char tt[6 * kTTile];
+  __shared__ __align__(16) unsigned char dss[2][kRowTile];   // dS [row][key], bf16, scaled by c
+  __shared__ __align__(16) unsigned char pd[2][kPdBytes];    // P, dS operands [wave][j][lane]
+  __shared__ float r_l2[2][32], r_D[2][32];
+  __shared__ int r_lim[2][32], r_prow[3][32];
   __shared__ int ents[kChunkQueries];  // the chunk's (row << 6 | slot) entries
+  static_assert(6 * kTTile >= 128 * kBP, "K^T staging fits the transposed tiles");
 
   // the chunk list is dealt to the 8 XCDs in contiguous eighths (as forward)
   const int nchunks = *a.count;
@@ -119,8 +124,9 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
   const u16* Kb = a.K + (bg * a.N + key0) * kHeadDim;
   const u16* Vb = a.V + (bg * a.N + key0) * kHeadDim;
 
-  // K^T: 64 key pairs x 16 chunks of 8 dims, stored as 32-bit (key, key + 1)
+  // K^T: 64 key pairs x 16 chunks of 8 dims, staged as 32-bit (key, key + 1)
   // words.  Keys past N are zero.
+  unsigned char* kt = tt;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int i = tid + 512 * j;
@@ -152,62 +158,67 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
     const int gw = wave - 4;
     // A pass's gather, one thread's share: rows 2 rp and 2 rp + 1, dims
     // 8 cc .. 8 cc + 7 of q and dO, plus (for cc == 0) the rows' lse, D,
-    // causal limit and partial row.  Rows past the chunk's end are zero with
-    // lse = +inf and an empty causal range, so they add nothing to dK and dV;
-    // their dq goes to the sink row.  (rp varies fastest across lanes: one
-    // wave's stores to a transposed tile row then hit 16 consecutive words
-    // instead of one bank 16 times.)
+    // causal limit and partial row.  Rows past the chunk's end repeat the
+    // chunk's first row with lse = +inf and an empty causal range, so their P
+    // and dS are 0 and they add nothing to dK and dV; their dq goes to the
+    // sink row.  (rp varies fastest across lanes: one wave's stores to a
+    // transposed tile row then hit 16 consecutive words instead of one bank 16
+    // times.)
     const int t = tid - 256;
     const int rp = t & 15, cc = t >> 4;
+    const int r0 = 2 * rp;
     uint4 fq[2], fg[2];
     float fl[2], fD[2];
     int flim[2], fprow[2];
     bool fvalid[2];
-    // fetch only issues loads (every lane, valid addresses; nothing uses them
-    // before stash: a use under a branch would make the compiler wait for the
-    // loads there)
+    // fetch only issues loads (every lane, valid addresses); they are used a
+    // pass later, by stash
     auto fetch = [&](int pass) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int rr = pass * 32 + 2 * rp + u;
+        const int rr = pass * 32 + r0 + u;
         const bool valid = rr < rows;
         const int qi = valid ? rr / HG : 0;
         const int hh = rr % HG;
         const int e = ents[qi];
-        const int64_t tt = t0 + (e >> 6);
+        const int64_t tt_ = t0 + (e >> 6);
         const int64_t hq = static_cast<int64_t>(g) * HG + hh;
-        const int64_t off = ((b * a.T + tt) * a.Hq + hq) * kHeadDim + 8 * cc;
+        const int64_t off = ((b * a.T + tt_) * a.Hq + hq) * kHeadDim + 8 * cc;
         fq[u] = ld16(a.q + off);
         fg[u] = ld16(a.dO + off);
-        fl[u] = a.lse[(b * a.Hq + hq) * a.T + tt];
-        fD[u] = a.Dr[(b * a.T + tt) * a.Hq + hq];
+        fl[u] = a.lse[(b * a.Hq + hq) * a.T + tt_];
+        fD[u] = a.Dr[(b * a.T + tt_) * a.Hq + hq];
         fvalid[u] = valid;
-        flim[u] = valid ? static_cast<int>(min(a.N - a.T + tt - key0,
+        flim[u] = valid ? static_cast<int>(min(a.N - a.T + tt_ - key0,
                                                static_cast<int64_t>(nvalid - 1)))
                         : -1;  // last key of the block the row sees
         fprow[u] = valid ? (((e >> 6) - a.rl_base) * a.k + (e & 63)) * HG + hh : a.sink + hh;
       }
     };
+    // the row-major tiles and the rows' scalars (read by the score waves) and
+    // the transposed tiles (read by this role), all for pass `pass`
     auto stash = [&](int pass) {
+      const int pb = pass & 1;
+      *reinterpret_cast<uint4*>(&qs[pb][r0 * kBP + 16 * cc]) = fq[0];
+      *reinterpret_cast<uint4*>(&qs[pb][(r0 + 1) * kBP + 16 * cc]) = fq[1];
+      *reinterpret_cast<uint4*>(&gs[pb][r0 * kBP + 16 * cc]) = fg[0];
+      *reinterpret_cast<uint4*>(&gs[pb][(r0 + 1) * kBP + 16 * cc]) = fg[1];
+      if (cc == 0) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (!fvalid[u]) {
-          fq[u] = make_uint4(0, 0, 0, 0);
-          fg[u] = make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+          r_l2[pb][r0 + u] = fvalid[u] ? fl[u] * kLog2e : INFINITY;
+          r_D[pb][r0 + u] = fvalid[u] ? fD[u] : 0.f;
+          r_lim[pb][r0 + u] = flim[u];
+          r_prow[pass % 3][r0 + u] = fprow[u];
         }
       }
-      const int r0 = 2 * rp;
-      *reinterpret_cast<uint4*>(&qs[r0 * kBP + 16 * cc]) = fq[0];
-      *reinterpret_cast<uint4*>(&qs[(r0 + 1) * kBP + 16 * cc]) = fq[1];
-      *reinterpret_cast<uint4*>(&gs[r0 * kBP + 16 * cc]) = fg[0];
-      *reinterpret_cast<uint4*>(&gs[(r0 + 1) * kBP + 16 * cc]) = fg[1];
       const int P = tpos(r0);  // even; row r0 + 1 sits at P + 1
       const uint32_t q0[4] = {fq[0].x, fq[0].y, fq[0].z, fq[0].w};
       const uint32_t q1[4] = {fq[1].x, fq[1].y, fq[1].z, fq[1].w};
       const uint32_t g0[4] = {fg[0].x, fg[0].y, fg[0].z, fg[0].w};
       const uint32_t g1[4] = {fg[1].x, fg[1].y, fg[1].z, fg[1].w};
-      unsigned char* qTw = qT[pass & 1];
-      unsigned char* gTw = gT[pass & 1];
+      unsigned char* qTw = tt + (2 * (pass % 3)) * kTTile;
+      unsigned char* gTw = qTw + kTTile;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int sh = 16 * (e & 1);
@@ -216,15 +227,6 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
             ((q0[e >> 1] >> sh) & 0xffffu) | (((q1[e >> 1] >> sh) & 0xffffu) << 16);
         *reinterpret_cast<uint32_t*>(&gTw[o]) =
             ((g0[e >> 1] >> sh) & 0xffffu) | (((g1[e >> 1] >> sh) & 0xffffu) << 16);
-      }
-      if (cc == 0) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          r_l2[r0 + u] = fvalid[u] ? fl[u] * kLog2e : INFINITY;
-          r_D[r0 + u] = fvalid[u] ? fD[u] : 0.f;
-          r_lim[r0 + u] = flim[u];
-          r_prow[pass & 1][r0 + u] = fprow[u];
-        }
       }
     };
     // dV += P^T dO and dK += dS^T q over pass p's rows: keys on M, dims on N;
@@ -237,8 +239,8 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
     }
     auto key_grads = [&](int p) {
       const unsigned char* pdr = pd[p & 1] + (gw * 256 + lane) * 16;
-      const unsigned char* gTr = gT[p & 1];
-      const unsigned char* qTr = qT[p & 1];
+      const unsigned char* qTr = tt + (2 * (p % 3)) * kTTile;
+      const unsigned char* gTr = qTr + kTTile;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const uint4 pa = *reinterpret_cast<const uint4*>(pdr + 1024 * s);
@@ -254,19 +256,17 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
       }
     };
     fetch(0);
+    __syncthreads();  // the score waves have their K^T rows: the staging may be replaced
     stash(0);
+    fetch(npass > 1 ? 1 : 0);
     __syncthreads();  // pass 0's rows are in LDS
     for (int pass = 0; pass < npass; ++pass) {
-      const bool more = pass + 1 < npass;
-      fetch(more ? pass + 1 : pass);
       if (pass > 0) key_grads(pass - 1);
-      // the score waves are done with pass's rows (qs, gs, r_*) and have
-      // stored pass's P / dS; this wave is done with pass - 1's tiles
-      __syncthreads();
-      if (more) {
+      if (pass + 1 < npass) {
         stash(pass + 1);
-        __syncthreads();
+        fetch(pass + 2 < npass ? pass + 2 : pass + 1);
       }
+      __syncthreads();
     }
     key_grads(npass - 1);
 
@@ -288,18 +288,21 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
     // ---- score waves ----
     const int key_w = 32 * wave + l32;  // this lane's key in S, dP, dS
     const float qscale = kLog2e * kScale;
-    // this wave's keys' K and V rows (the B operands of S and dP, 8 k-steps
-    // each) stay in registers for the whole chunk; rows past the block's end
-    // repeat its last key (their P is masked to 0)
-    uint4 kf[8], vf[8];
+    // this wave's operands that stay fixed for the whole chunk, kept in
+    // registers: its keys' K and V rows (B of S and dP) and its dims' K^T
+    // rows (A of dq), 8 k-steps each.  K / V rows past the block's end repeat
+    // its last key (their P is masked to 0).
+    uint4 kf[8], vf[8], tf[8];
     {
       const int kr = key_w < nvalid ? key_w : nvalid - 1;
       const u16* kp = Kb + static_cast<int64_t>(kr) * kHeadDim + 8 * half;
       const u16* vp = Vb + static_cast<int64_t>(kr) * kHeadDim + 8 * half;
+      const unsigned char* ka = kt + (32 * wave + l32) * kBP + half * 16;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         kf[s] = ld16(kp + 16 * s);
         vf[s] = ld16(vp + 16 * s);
+        tf[s] = *reinterpret_cast<const uint4*>(ka + 32 * s);
       }
     }
     // dq^T of this wave's 32 dims x pass p's 32 rows = K^T dS^T over the 128
@@ -307,9 +310,8 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
     // l32: the lane's 16 values (dims 32 wave + 8(i/4) + 4 half + i%4) go
     // contiguously to element 32 wave + 16 half of the partial row (see
     // dq_combine_kernel).
-    const unsigned char* ka = kt + (32 * wave + l32) * kBP + half * 16;
     auto store_dq = [&](int p, const f32x16& qacc) {
-      const int prow = r_prow[p & 1][l32];
+      const int prow = r_prow[p % 3][l32];
       u16* dst = a.dqpart + static_cast<int64_t>(prow) * kHeadDim + 32 * wave + 16 * half;
       uint4 w0, w1;
       w0.x = pack_bf16x2(qacc[0], qacc[1]);
@@ -332,7 +334,7 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
     // (wave-uniform test).
     auto write_teacher = [&](int pass, const float* pr) {
       if (32 * wave >= a.Bk) return;
-      const int* rpw = r_prow[pass & 1];
+      const int* rpw = r_prow[pass % 3];
       auto put = [&](int m, float sum) {
         const int pw = rpw[m];  // (row, slot) entry * HG for the query's first head
         if (pw < a.sink)  // read once, by the KL pass: kept out of the caches
@@ -371,20 +373,22 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
       }
     };
 
+    __syncthreads();  // this role's K^T rows are read: the staging may be replaced
     __syncthreads();  // pass 0's rows are in LDS
     // Pass p: the S / dP products of pass p run beside the dq product of pass
     // p - 1 (two independent MFMA streams), then P and dS: into dss[p & 1]
     // (row-major, for the next pass's dq) and into pd[p & 1] (the key-gradient
     // waves' operands).
     for (int pass = 0; pass < npass; ++pass) {
+      const int pb = pass & 1;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       f32x16 q0 = f32x16{}, q1 = f32x16{};
       {
-        const unsigned char* qa = qs + l32 * kBP + half * 16;
-        const unsigned char* ga = gs + l32 * kBP + half * 16;
+        const unsigned char* qa = qs[pb] + l32 * kBP + half * 16;
+        const unsigned char* ga = gs[pb] + l32 * kBP + half * 16;
         // dS of pass p - 1 (for pass 0 this reads the other buffer's stale
         // contents, and the result is not stored)
-        const unsigned char* db = dss[(pass + 1) & 1] + l32 * kBP + half * 16;
+        const unsigned char* db = dss[pb ^ 1] + l32 * kBP + half * 16;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(qa + 32 * s)), as_bf16x8(kf[s]),
@@ -392,27 +396,27 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
           pacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ga + 32 * s)), as_bf16x8(vf[s]),
                         pacc);
           if (s & 1)
-            q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
-                        as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q1);
+            q1 = mfma32(as_bf16x8(tf[s]), as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)),
+                        q1);
           else
-            q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
-                        as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
+            q0 = mfma32(as_bf16x8(tf[s]), as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)),
+                        q0);
         }
       }
       // P and c*dS; lane: key key_w, rows m(i) = 8(i/4) + 4 half + i%4
-      unsigned char* dsw = dss[pass & 1];
+      unsigned char* dsw = dss[pb];
       float pr[16], dsr[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int m = 8 * (i >> 2) + 4 * half + (i & 3);
-        const float ex = fast_exp2(fmaf(sacc[i], qscale, -r_l2[m]));
-        const float p = key_w <= r_lim[m] ? ex : 0.f;
+        const float ex = fast_exp2(fmaf(sacc[i], qscale, -r_l2[pb][m]));
+        const float p = key_w <= r_lim[pb][m] ? ex : 0.f;
         pr[i] = p;
-        dsr[i] = p * (pacc[i] - r_D[m]) * kScale;
+        dsr[i] = p * (pacc[i] - r_D[pb][m]) * kScale;
         *reinterpret_cast<u16*>(&dsw[m * kBP + 2 * key_w]) = f32_to_bf16(dsr[i]);
       }
       if (pass > 0) store_dq(pass - 1, q0 + q1);
-      unsigned char* pdw = pd[pass & 1] + (wave * 256 + lane) * 16;
+      unsigned char* pdw = pd[pb] + (wave * 256 + lane) * 16;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         *reinterpret_cast<uint4*>(pdw + 1024 * s) =
@@ -427,17 +431,15 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
                        pack_bf16x2(dsr[8 * s + 6], dsr[8 * s + 7]));
       }
       if constexpr (TW) write_teacher(pass, pr);
-      __syncthreads();  // pass's P / dS are stored; its rows may be replaced
-      if (pass + 1 < npass) __syncthreads();  // the next pass's rows are in LDS
+      __syncthreads();
     }
     {  // dq of the last pass
       const unsigned char* db = dss[(npass - 1) & 1] + l32 * kBP + half * 16;
       f32x16 q0 = f32x16{}, q1 = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; s += 2) {
-        q0 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s)),
-                    as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
-        q1 = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * s + 32)),
+        q0 = mfma32(as_bf16x8(tf[s]), as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s)), q0);
+        q1 = mfma32(as_bf16x8(tf[s + 1]),
                     as_bf16x8(*reinterpret_cast<const uint4*>(db + 32 * s + 32)), q1);
       }
       store_dq(npass - 1, q0 + q1);
