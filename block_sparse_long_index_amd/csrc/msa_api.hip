@@ -164,22 +164,24 @@ size_t backward_ws(const msa_dims_t* d, int64_t window) {
   return rowdot_bytes(d) + prefill_ws(d, window);
 }
 
-// Index-branch KL backward: the prefill's inversion and partial buffers,
-// then the proxy lse of every (row, group).
+// Index-branch KL backward: the proxy lse of every (row, group), one stage's
+// teacher (fp32 per (row, slot, key)), then the prefill's inversion and
+// partial buffers.
 size_t lpx_bytes(const msa_dims_t* d) {
   return ((static_cast<size_t>(d->B * d->T * d->G) * sizeof(float)) + 255) & ~size_t(255);
 }
 
-size_t index_kl_ws(const msa_dims_t* d, int64_t window) {
-  return lpx_bytes(d) + prefill_ws(d, window);
-}
-
-// Fused training backward: D = dO . O, the proxy lse, one stage's teacher
-// (fp32 per (row, slot, key)), then the prefill's inversion and partials.
 size_t teach_bytes(const msa_dims_t* d, int64_t window) {
   return ((static_cast<size_t>(stage_rows_for(d, window) * d->k * d->Bk) * sizeof(float)) + 255) &
          ~size_t(255);
 }
+
+size_t index_kl_ws(const msa_dims_t* d, int64_t window) {
+  return lpx_bytes(d) + teach_bytes(d, window) + prefill_ws(d, window);
+}
+
+// Fused training backward: D = dO . O, the proxy lse, one stage's teacher,
+// then the prefill's inversion and partials.
 
 size_t train_ws(const msa_dims_t* d, int64_t window) {
   return rowdot_bytes(d) + lpx_bytes(d) + teach_bytes(d, window) + prefill_ws(d, window);
@@ -607,13 +609,17 @@ int msa_index_kl_backward(const msa_dims_t* d, const void* qI, const void* kI, c
     }
     hi = lo;
   }
-  float* lpx = static_cast<float*>(ws);
+  char* p = static_cast<char*>(ws);
+  float* lpx = reinterpret_cast<float*>(p);
+  p += lpx_bytes(d);
+  float* teach = reinterpret_cast<float*>(p);
+  p += teach_bytes(d, hi);
   msa::AttnWorkspace w;
-  msa::attn_workspace_carve(static_cast<char*>(ws) + lpx_bytes(d), hi, stage_rows_for(d, hi),
-                            d->N, d->G, d->Hq / d->G, d->k, d->Bk, false, &w);
-  const hipError_t e = msa::launch_index_kl_backward(qI, kI, q, K, idx, lse, dqI, dkI, kl, lpx,
-                                                     d->B, d->T, d->N, d->Hq, d->G, d->k, d->Bk, w,
-                                                     static_cast<hipStream_t>(stream));
+  msa::attn_workspace_carve(p, hi, stage_rows_for(d, hi), d->N, d->G, d->Hq / d->G, d->k, d->Bk,
+                            false, &w);
+  const hipError_t e = msa::launch_index_kl_backward(
+      qI, kI, q, K, idx, lse, dqI, dkI, kl, lpx, teach, d->B, d->T, d->N, d->Hq, d->G, d->k,
+      d->Bk, w, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "msa_index_kl_backward");
   return MSA_OK;
 }

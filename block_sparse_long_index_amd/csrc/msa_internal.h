@@ -92,17 +92,19 @@ hipError_t launch_dq_combine(const int32_t* idx, const uint16_t* part, float* ou
                              int group, hipStream_t st);
 // Index-branch KL alignment backward: dqI [B, T, G, 128], dkI [B, N, 128]
 // (fp32, overwritten), kl [B, G, T] (nullable) from q^I, k^I, q, K, idx and
-// the main lse [B, Hq, T]; lpx: B*G*T floats of scratch.  Blocks of Bk keys.
+// the main lse [B, Hq, T]; lpx: B*G*T floats of scratch; teach: w.stage_rows
+// * k * Bk floats of scratch (one stage's teacher).  Blocks of Bk keys.
 hipError_t launch_index_kl_backward(const void* qI, const void* kI, const void* q, const void* K,
                                     const int32_t* idx, const float* lse, float* dqI, float* dkI,
-                                    float* kl, float* lpx, int64_t B, int64_t T, int64_t N,
-                                    int Hq, int G, int k, int Bk, const AttnWorkspace& w,
-                                    hipStream_t st);
+                                    float* kl, float* lpx, float* teach, int64_t B, int64_t T,
+                                    int64_t N, int Hq, int G, int k, int Bk,
+                                    const AttnWorkspace& w, hipStream_t st);
 // Pieces of the two backward launchers, for the fused training backward:
 // zeroing / D = dO . O, and one stage (group g, row stage sub of the window
 // of W rows at global row r0, S row stages per group) after
 // launch_invert_window.  teach: [stage rows, k, Bk] fp32, written by the
-// main stage and read by the KL stage (null: each stands alone).
+// main stage (null: no teacher) or by the KL stage itself (make_teacher) and
+// read by the KL stage.
 hipError_t attn_bwd_prepare(const void* O, const void* dO, float* dK, float* dV, float* Dr,
                             int64_t B, int64_t T, int64_t N, int Hq, int G, hipStream_t st);
 hipError_t attn_bwd_stage(const void* q, const void* K, const void* V, const int32_t* idx,
@@ -112,7 +114,8 @@ hipError_t attn_bwd_stage(const void* q, const void* K, const void* V, const int
                           int32_t S, int g, int32_t sub, hipStream_t st);
 hipError_t index_kl_prepare(float* dkI, int64_t B, int64_t N, hipStream_t st);
 hipError_t index_kl_stage(const void* qI, const void* kI, const void* q, const void* K,
-                          const int32_t* idx, const float* lse, const float* teach, float* dqI,
+                          const int32_t* idx, const float* lse, float* teach, bool make_teacher,
+                          float* dqI,
                           float* dkI, float* kl, float* lpx, int64_t T, int64_t N, int Hq, int G,
                           int k, int Bk, const AttnWorkspace& w, int64_t r0, int64_t W, int32_t S,
                           int g, int32_t sub, hipStream_t st);
