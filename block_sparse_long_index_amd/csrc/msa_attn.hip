@@ -500,7 +500,7 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
     float m = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) m = max16(m, sacc[kt]);
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = halves_max(m);
     const float mc = m * qscale;
 
     // P = exp2(s * log2e/sqrt(d) - max) rounded to bf16, O^T += V^T P^T.  The
@@ -534,7 +534,7 @@ __global__ void __launch_bounds__(256, 2) kv_outer_kernel(AttnArgs a) {
         oacc[dt] = mfma32(as_bf16x8(va[dt][1]), as_bf16x8(pb[1]), oacc[dt]);
       }
     }
-    l += __shfl_xor(l, 32);
+    l = halves_sum(l);
     // Unnormalised partial O (bf16, MFMA order) and its (log2-domain max,
     // sum).  Rows past the chunk's end write to the buffer's sink entry;
     // stores are unconditional so that no branch hides them from the wait

@@ -354,11 +354,11 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           sum[j] = (pr[4 * j] + pr[4 * j + 1]) + (pr[4 * j + 2] + pr[4 * j + 3]);
-          sum[j] += __shfl_xor(sum[j], 32);
         }
-        // half h writes queries 2h and 2h + 1 (rows 16h and 16h + 8)
-        put(16 * half, half ? sum[2] : sum[0]);
-        put(16 * half + 8, half ? sum[3] : sum[1]);
+        // half h writes queries 2h and 2h + 1 (rows 16h and 16h + 8), each
+        // summed over both half-waves
+        put(16 * half, halves_sum2(sum[0], sum[2]));
+        put(16 * half + 8, halves_sum2(sum[1], sum[3]));
       } else {
         static_assert(HG == 16, "heads per group");
         float s0 = 0.f, s1 = 0.f;
@@ -367,9 +367,7 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
           s0 += pr[j];
           s1 += pr[8 + j];
         }
-        s0 += __shfl_xor(s0, 32);
-        s1 += __shfl_xor(s1, 32);
-        put(16 * half, half ? s1 : s0);  // half h writes query h
+        put(16 * half, halves_sum2(s0, s1));  // half h writes query h
       }
     };
 

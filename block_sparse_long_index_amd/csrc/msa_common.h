@@ -128,6 +128,34 @@ __device__ __forceinline__ int64_t paged_page(const PagedCache& pc, int64_t b, i
   return pg < 0 ? 0 : (pg >= pc.pages ? pc.pages - 1 : pg);
 }
 
+// Exchanges between the two half-waves (lane l and lane l ^ 32) with
+// v_permlane32_swap, a VALU lane swap that needs no LDS round trip.  The
+// swap of (a, b) leaves lanes 0-31 holding a's two halves and lanes 32-63
+// holding b's, one per returned register.
+__device__ __forceinline__ float halves_max2(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// max(x[l], x[l ^ 32]) in lane l (the same value in both lanes).
+__device__ __forceinline__ float halves_max(float x) { return halves_max2(x, x); }
+
+// x[l] + x[l ^ 32] in lane l; equal to x + __shfl_xor(x, 32) bit for bit
+// (the sum of two values does not depend on their order).
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Lanes 0-31: a[l] + a[l + 32]; lanes 32-63: b[l - 32] + b[l].
+__device__ __forceinline__ float halves_sum2(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float max3(float a, float b, float c) {
   return fmaxf(a, fmaxf(b, c));
 }

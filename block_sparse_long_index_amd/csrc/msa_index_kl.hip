@@ -124,7 +124,7 @@ __global__ void __launch_bounds__(256) index_px_kernel(IkArgs a) {
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, v[kt][i]);
-  m = fmaxf(m, __shfl_xor(m, 32));
+  m = halves_max(m);
   float l = 0.f;
   if (m > -INFINITY) {
 #pragma unroll
@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256) index_px_kernel(IkArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) l += fast_exp2(v[kt][i] - m);
   }
-  l += __shfl_xor(l, 32);
+  l = halves_sum(l);
   if (valid && half == 0) {
     const int prow = ((e >> 6) - a.rl_base) * a.k + (e & 63);
     a.part[prow] = make_float2(m, l);
@@ -575,11 +575,11 @@ __global__ void __launch_bounds__(256, 2) teacher_kernel(IkArgs a, float* teach)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           sum[j] = (pr[4 * j] + pr[4 * j + 1]) + (pr[4 * j + 2] + pr[4 * j + 3]);
-          sum[j] += __shfl_xor(sum[j], 32);
         }
-        // half h writes queries 2h and 2h + 1 (rows 16h and 16h + 8)
-        put(rpw, 16 * half, half ? sum[2] : sum[0]);
-        put(rpw, 16 * half + 8, half ? sum[3] : sum[1]);
+        // half h writes queries 2h and 2h + 1 (rows 16h and 16h + 8), each
+        // summed over both half-waves
+        put(rpw, 16 * half, halves_sum2(sum[0], sum[2]));
+        put(rpw, 16 * half + 8, halves_sum2(sum[1], sum[3]));
       } else {
         static_assert(HG == 16, "heads per group");
         float a0 = 0.f, a1 = 0.f;
@@ -588,9 +588,7 @@ __global__ void __launch_bounds__(256, 2) teacher_kernel(IkArgs a, float* teach)
           a0 += pr[j];
           a1 += pr[8 + j];
         }
-        a0 += __shfl_xor(a0, 32);
-        a1 += __shfl_xor(a1, 32);
-        put(rpw, 16 * half, half ? a1 : a0);  // half h writes query h
+        put(rpw, 16 * half, halves_sum2(a0, a1));  // half h writes query h
       }
     }
     __syncthreads();  // pass's tile and row data may be replaced

@@ -334,9 +334,7 @@ __device__ __forceinline__ void index_tile(
       if constexpr (WRITE_S && BK < 128) {
         // the last tile of a block: its score, then start the next block
         if ((kt + 1) % TPB == 0) {
-          const float bm0 = fmaxf(m0, __shfl_xor(m0, 32));
-          const float bm1 = fmaxf(m1, __shfl_xor(m1, 32));
-          emit(kb * BPC + kt / TPB, half ? bm1 : bm0);
+          emit(kb * BPC + kt / TPB, halves_max2(m0, m1));
           m0 = -INFINITY;
           m1 = -INFINITY;
         }
@@ -383,9 +381,8 @@ __device__ __forceinline__ void index_tile(
       sched_fence();
       reduce(3, tb0, tb1);
     }
-    m0 = fmaxf(m0, __shfl_xor(m0, 32));
-    m1 = fmaxf(m1, __shfl_xor(m1, 32));
-    const float v = half ? m1 : m0;
+    // the block max of the lane's own column (lanes 0-31: tile 0's columns)
+    const float v = halves_max2(m0, m1);
 
     if (WRITE_S) {
       if constexpr (BK == 128) emit(kb, v);
