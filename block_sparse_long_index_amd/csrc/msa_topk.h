@@ -145,8 +145,13 @@ __device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int st
     }
     bitonic_merge64(v, vi, lane);
   };
+  // chunks from nch on hold no candidate (all -inf): no compaction work
+  // (a uniform branch; the loads above stay unconditional so that none of
+  // them waits before the next is issued)
+  const int nch = n > e0 ? (n - e0 + step - 1) / step : 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) chunk(e0 + step * r, x[r]);
+  for (int r = 0; r < R; ++r)
+    if (r < nch) chunk(e0 + step * r, x[r]);
   for (int c0 = rest; c0 < n; c0 += step) {
     const int e = c0 + lane;
     chunk(c0, e < n ? src[e] : -INFINITY);
