@@ -1094,8 +1094,7 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecArgs a) {
       if (16 * t + 4 * qd + r >= nvalid) sc[t][r] = -INFINITY;
       m = fmaxf(m, sc[t][r]);
     }
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
+  m = quads_max(m);
   const float mc = m == -INFINITY ? 0.f : m * qscale;  // all-masked quarter: p = 0
   float pv[8];
 #pragma unroll
@@ -1106,8 +1105,7 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecArgs a) {
   float l = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) l += pv[e];
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = quads_sum(l);
   const uint4 pf = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                               pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
 
@@ -1197,8 +1195,7 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(CombArgs a) {
 #pragma unroll
   for (int i = 0; i < NSL; ++i)
     if (sg + 4 * i < nval) mx = fmaxf(mx, ml[i].x);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = quads_max(mx);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
 #pragma unroll
@@ -1214,11 +1211,9 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(CombArgs a) {
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    acc[u] += __shfl_xor(acc[u], 16);
-    acc[u] += __shfl_xor(acc[u], 32);
+    acc[u] = quads_sum(acc[u]);
   }
-  den += __shfl_xor(den, 16);
-  den += __shfl_xor(den, 32);
+  den = quads_sum(den);
   const int hq = g * HG + h;
   if (sg == 0) {
     const float inv = 1.f / den;
@@ -1436,8 +1431,7 @@ __global__ void __launch_bounds__(64 * kStepWaves) decode_step_kernel(StepArgs a
           if (16 * t + 4 * qd + r >= nv) sc[t][r] = -INFINITY;
           mq = fmaxf(mq, sc[t][r]);
         }
-      mq = fmaxf(mq, __shfl_xor(mq, 16));
-      mq = fmaxf(mq, __shfl_xor(mq, 32));
+      mq = quads_max(mq);
       const float Mn = fmaxf(M, mq * qscale);  // finite: the quarter has a valid key
       const float alpha = fast_exp2(M - Mn);    // 0 while M is -inf
       float pv[8];
@@ -1449,8 +1443,7 @@ __global__ void __launch_bounds__(64 * kStepWaves) decode_step_kernel(StepArgs a
       float l = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) l += pv[e];
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
+      l = quads_sum(l);
       Ls = Ls * alpha + l;
       M = Mn;
       const uint4 pf = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),

@@ -156,6 +156,19 @@ __device__ __forceinline__ float halves_sum2(float a, float b) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// max / sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (v_permlane16_swap, then
+// the half-wave swap); the sum equals the two __shfl_xor steps bit for bit.
+__device__ __forceinline__ float quads_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return halves_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quads_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return halves_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float max3(float a, float b, float c) {
   return fmaxf(a, fmaxf(b, c));
 }

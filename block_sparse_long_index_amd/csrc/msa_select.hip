@@ -623,8 +623,7 @@ __global__ void __launch_bounds__(256) decode_scan_kernel(ScanArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < BPC; ++j) {
-      m[j] = fmaxf(m[j], __shfl_xor(m[j], 16));
-      m[j] = fmaxf(m[j], __shfl_xor(m[j], 32));
+      m[j] = quads_max(m[j]);
     }
     if (lane < a.G) {
 #pragma unroll
