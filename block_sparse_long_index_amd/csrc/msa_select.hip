@@ -701,9 +701,10 @@ __device__ __forceinline__ TopkRow topk_row(const TopkArgs& a, int64_t r) {
 }
 
 __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
-  __shared__ float cv[4][128];
-  __shared__ int ci[4][128];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ TopkScratch sc[4];
+  // the wave index read as a scalar: the row's bookkeeping (divisions for
+  // its position and local block, its pointers) runs on the scalar unit
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (row >= a.rows) return;
   const TopkRow x = topk_row(a, row);
@@ -716,19 +717,25 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
   }
   float v;
   int vi;
-  const int nc = wave_topk<16>(x.s, static_cast<int>(L), 0, 64, m, lane, cv[wave], ci[wave], v, vi);
+  const int nc = wave_topk<16, false>(x.s, static_cast<int>(L), 0, 64, m, lane, sc[wave], v, vi);
   if (nc < 0) {
     write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
     return;
   }
-  // The compacted candidates are in ascending block order: those that are at
-  // least as good as the m-th best (lane m - 1 after the sort) are exactly the
-  // best m, and their ranks among themselves give their output slots.
-  const float vm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), m - 1));
-  const int im = __builtin_amdgcn_readlane(vi, m - 1);
-  const float c = lane < nc ? cv[wave][lane] : -INFINITY;
-  const int cidx = lane < nc ? ci[wave][lane] : INT_MAX;
-  const bool sel = (lane < nc) & !beats(vm, im, c, cidx);
+  // The nc >= m compacted candidates are in ascending block order.  Sorting
+  // their scores alone gives the m-th best score vm (finite); the best m are
+  // the candidates scoring above vm and, of those equal to it, the first ones
+  // in block order, as many as are still missing.  Their order in the list is
+  // their output slot.
+  const float c = lane < nc ? sc[wave].v[lane] : -INFINITY;
+  const int cidx = lane < nc ? sc[wave].i[lane] : INT_MAX;
+  const float sv = nc <= 16   ? sort_desc_values<16>(c, lane)
+                   : nc <= 32 ? sort_desc_values<32>(c, lane)
+                              : sort_desc_values<64>(c, lane);
+  const float vm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), m - 1));
+  const unsigned long long above = __ballot(c > vm);
+  const unsigned long long equal = __ballot(c == vm);
+  const bool sel = (c > vm) | ((c == vm) & (lanes_below(equal) < m - __popcll(above)));
   const unsigned long long bm = __ballot(sel);
   if (sel) out[lanes_below(bm)] = cidx;
   if ((lane >= m) & (lane < a.k)) out[lane] = lane == m ? static_cast<int>(L) : -1;

@@ -5,12 +5,19 @@
 // decode kernel.
 #pragma once
 
+#include <float.h>
 #include <limits.h>
 #include <math.h>
 
 #include "msa_common.h"
 
 namespace msa {
+
+// Word 3 of a raw (stride 0) buffer resource for untyped dword loads on this
+// architecture family: DATA_FORMAT (bits 15-18) = 4, 32-bit elements; the
+// other fields 0.  A load whose byte offset is at or past the resource's
+// byte count returns 0 and reads nothing.
+constexpr int kBufferFormat32 = 4 << 15;
 
 // Non-short-circuit operators keep the comparisons branch-free (selects, not
 // exec-mask branches).
@@ -70,16 +77,17 @@ __device__ __forceinline__ void bitonic_merge64(float& v, int& i, int lane) {
   if constexpr (STRIDE > 1) bitonic_merge64<STRIDE / 2>(v, i, lane);
 }
 
-// Values sorted descending across the wave (lane 0 the largest).
-template <int SIZE = 2, int STRIDE = 1>
-__device__ __forceinline__ float sort_desc_values64(float v, int lane) {
+// Values sorted descending within each run of NMAX consecutive lanes (lane 0
+// the largest; NMAX = 64: the whole wave).
+template <int NMAX = 64, int SIZE = 2, int STRIDE = 1>
+__device__ __forceinline__ float sort_desc_values(float v, int lane) {
   const float pv = xlane<STRIDE>(v);
-  const bool keep = ((lane & STRIDE) == 0) == ((lane & SIZE) == 0);  // keep the larger
-  v = ((pv > v) == keep) ? pv : v;
+  const bool keep = ((lane & STRIDE) == 0) == (((lane & SIZE) == 0) | (SIZE == NMAX));
+  v = ((pv > v) == keep) ? pv : v;  // keep: the larger of the two
   if constexpr (STRIDE > 1)
-    return sort_desc_values64<SIZE, STRIDE / 2>(v, lane);
-  else if constexpr (SIZE < 64)
-    return sort_desc_values64<SIZE * 2, SIZE>(v, lane);
+    return sort_desc_values<NMAX, SIZE, STRIDE / 2>(v, lane);
+  else if constexpr (SIZE < NMAX)
+    return sort_desc_values<NMAX, SIZE * 2, SIZE>(v, lane);
   else
     return v;
 }
@@ -89,48 +97,64 @@ __device__ __forceinline__ int lanes_below(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0));
 }
 
+// Per-wave LDS scratch of the threshold-and-compact selection: the compacted
+// candidates (at most 64 are ever read), the spare entries 64 + lane, and
+// room for compacted positions up to 191, so that every lane stores every
+// chunk without a bounds test or an exec-mask branch.
+constexpr int kTopkScratch = 192;
+struct TopkScratch {
+  float v[kTopkScratch];
+  int i[kTopkScratch];
+};
+
 // Best m candidates (score desc, index asc) among src[e] for e = e0 + lane +
 // step*i < n, left best-first in lanes 0..m-1 (m <= 63).  The first R strided
 // chunks are loaded once into registers, all loads in flight together; any
-// remainder is re-read from memory.  cv/ci: this wave's 128-entry LDS scratch
-// (64 compacted candidates, then one spare entry per lane).
-// Returns the number of candidates compacted into cv/ci in ascending index
+// remainder is re-read from memory.
+// Returns the number of candidates compacted into sc in ascending index
 // order (all those >= the threshold, a superset of the best m), or -1 when
-// there were too many for the scratch (the best m then came from a running
-// merge).
-template <int R>
+// there were more than 64 (the best m then came from a running merge).  With
+// SORT false the compacted candidates are left unsorted and v / vi are set
+// only on the merge path.
+template <int R, bool SORT = true>
 __device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int step, int m,
-                                         int lane, float* cv, int* ci, float& v, int& vi) {
-  float x[R];  // -inf past the row's end
+                                         int lane, TopkScratch& sc, float& v, int& vi) {
+  // The first R chunks through a raw buffer of n floats: a load at or past
+  // the row's end returns 0 without a memory access, and needs no address
+  // clamp (the chunk offsets become immediate offsets of one lane offset).
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), 0, n * 4,
+                                                    kBufferFormat32);
+  float x[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = e0 + lane + step * r;
-    const float y = src[e < n ? e : n - 1];
-    x[r] = e < n ? y : -INFINITY;
-  }
+  for (int r = 0; r < R; ++r)
+    x[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (e0 + lane + step * r), 0, 0));
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = lane < n - e0 - step * r ? x[r] : -INFINITY;
   const int rest = e0 + step * R;
   float lm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < R; ++r) lm = fmaxf(lm, x[r]);
   for (int e = rest + lane; e < n; e += step) lm = fmaxf(lm, src[e]);
-  const float tau = __shfl(sort_desc_values64(lm, lane), m - 1);
+  // The m-th largest lane max: at least m candidates reach it.  Kept above
+  // -inf (a wave whose part of the row holds fewer than m candidates), so
+  // that the -inf fill past the row's end never passes the test.
+  const float tau = fmaxf(__shfl(sort_desc_values(lm, lane), m - 1), -FLT_MAX);
   v = -INFINITY;
   vi = INT_MAX;
-  // candidates >= tau, compacted in index order while they fit the scratch;
-  // cnt counts them all (the same in every lane)
+  // candidates >= tau, compacted in index order; cnt counts them (the same in
+  // every lane), saturating at 128 so that positions stay below 192
   int cnt = 0;
   // every lane stores: a kept candidate at its compacted position, any
-  // other value in the lane's own spare entry 64 + lane (never read), so
-  // the loop has no exec-mask branches
+  // other value in the lane's own spare entry 64 + lane (never read)
   auto chunk = [&](int c0, float xv) {
-    const int e = c0 + lane;
-    const bool f = (e < n) & (xv >= tau);
+    const bool f = xv >= tau;
     const unsigned long long bal = __ballot(f);
-    const int pos = cnt + lanes_below(bal);
-    const int slot = (f & (pos < 64)) ? pos : 64 + lane;
-    cv[slot] = xv;
-    ci[slot] = e;
-    cnt += __popcll(bal);
+    const int pos = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bal >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bal), cnt));
+    const int slot = f ? pos : 64 + lane;
+    sc.v[slot] = xv;
+    sc.i[slot] = c0 + lane;
+    cnt = min(cnt + static_cast<int>(__popcll(bal)), 128);
   };
   auto merge = [&](int c0, float xv) {
     const int e = c0 + lane;
@@ -145,9 +169,9 @@ __device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int st
     }
     bitonic_merge64(v, vi, lane);
   };
-  // chunks from nch on hold no candidate (all -inf): no compaction work
-  // (a uniform branch; the loads above stay unconditional so that none of
-  // them waits before the next is issued)
+  // chunks from nch on hold no candidate: no compaction work (a uniform
+  // branch; the loads above stay unconditional so that none of them waits
+  // before the next is issued)
   const int nch = n > e0 ? (n - e0 + step - 1) / step : 0;
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -159,9 +183,10 @@ __device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int st
   if (cnt <= 64) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    if constexpr (!SORT) return cnt;
     if (lane < cnt) {
-      v = cv[lane];
-      vi = ci[lane];
+      v = sc.v[lane];
+      vi = sc.i[lane];
     }
     // sort only as many lanes as hold candidates
     if (cnt <= 16)
@@ -232,8 +257,7 @@ __device__ __forceinline__ void write_selection(int32_t* out, int vi, int m, int
 // 64-candidate chunk of s[0..L) and leaves its best m in LDS.  Part 2 (wave 0
 // only): orders the four lists and returns lane's selection entry (lanes < k).
 struct WideTopkLds {
-  float cv[4][128];
-  int ci[4][128];
+  TopkScratch sc[4];
   float mv[4][64];
   int mi[4][64];
 };
@@ -242,7 +266,7 @@ __device__ __forceinline__ void wide_topk_part1(const float* s, int L, int m, in
                                                 WideTopkLds& t) {
   float v;
   int vi;
-  wave_topk<8>(s, L, 64 * wave, 256, m, lane, t.cv[wave], t.ci[wave], v, vi);
+  wave_topk<8>(s, L, 64 * wave, 256, m, lane, t.sc[wave], v, vi);
   if (m <= 15) {
     // Each wave's list is sorted best-first; odd waves store theirs reversed,
     // so that every 32 entries form a bitonic sequence and two merge stages

@@ -236,6 +236,33 @@ def test_topk_random_scores():
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("G,T,N,k,Bk,scale", [
+    (8, 600, 131072, 16, 128, None),  # 1018-1023 candidates, no ties
+    (8, 600, 131072, 16, 128, 3.0),   # the same with frequent ties
+    (8, 600, 32768, 64, 32, 1.0),     # 63 picks: up to and past 64 survivors
+    (1, 5000, 17500, 40, 32, 0.25),   # nearly all scores equal: the merge path
+    (8, 600, 200000, 16, 128, 3.0),   # 1563 candidates: chunks past the registers
+    (8, 700, 700, 7, 128, 2.0),       # short rows, m < 16
+    (8, 600, 65536, 32, 64, 2.0),     # 31 picks
+])
+def test_topk_long_rows(G, T, N, k, Bk, scale):
+    """Standalone top-k over many long rows (one wave per row), against the
+    oracle's selection on every row: exact scores, rounded scores with ties
+    at the m-th place, and rows where more than 64 candidates reach the
+    threshold."""
+    NB = (N + Bk - 1) // Bk
+    g = torch.Generator(device="cuda").manual_seed(T + k)
+    S = torch.randn(1, G, T, NB, device="cuda", generator=g)
+    if scale is not None:
+        S = torch.round(S * scale)
+    idx = ops.select_blocks_from_scores(S, k, N, Bk=Bk)
+    torch.cuda.synchronize()
+    d = oracle.dims_of(1, T, N, G, G, 128, 128, Bk, k)
+    ref = oracle.select(d, np.arange(T), S[0].permute(1, 0, 2).double().cpu().numpy())
+    got = idx[0].permute(1, 0, 2).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
 @pytest.mark.parametrize("scale", [3.0, 0.0])
 def test_topk_wide_rows(scale):
     """Few long rows (the decode shape) take the four-waves-per-row top-k:
