@@ -700,14 +700,9 @@ __device__ __forceinline__ TopkRow topk_row(const TopkArgs& a, int64_t r) {
   return x;
 }
 
-__global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
-  __shared__ TopkScratch sc[4];
-  // the wave index read as a scalar: the row's bookkeeping (divisions for
-  // its position and local block, its pointers) runs on the scalar unit
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  if (row >= a.rows) return;
-  const TopkRow x = topk_row(a, row);
+// The selection of one row by one wave.
+__device__ __forceinline__ void topk_one_row(const TopkArgs& a, const TopkRow& x, int lane,
+                                             TopkScratch& sc) {
   const int64_t L = x.L;
   const int m = static_cast<int>(L < a.k - 1 ? L : a.k - 1);
   int32_t* out = x.out;
@@ -717,7 +712,15 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
   }
   float v;
   int vi;
-  const int nc = wave_topk<16, false>(x.s, static_cast<int>(L), 0, 64, m, lane, sc[wave], v, vi);
+  // the row's pointer and length read as scalars: the buffer resource built
+  // from them must be uniform (the pair kernel's fallback otherwise sees
+  // them through per-lane copies)
+  const uint64_t sp = reinterpret_cast<uint64_t>(x.s);
+  const float* src = reinterpret_cast<const float*>(
+      (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sp >> 32))) << 32) |
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sp))));
+  const int nc = wave_topk<16, false>(src, __builtin_amdgcn_readfirstlane(static_cast<int>(L)), 0, 64,
+                                      m, lane, sc, v, vi);
   if (nc < 0) {
     write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
     return;
@@ -727,8 +730,8 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
   // the candidates scoring above vm and, of those equal to it, the first ones
   // in block order, as many as are still missing.  Their order in the list is
   // their output slot.
-  const float c = lane < nc ? sc[wave].v[lane] : -INFINITY;
-  const int cidx = lane < nc ? sc[wave].i[lane] : INT_MAX;
+  const float c = lane < nc ? sc.v[lane] : -INFINITY;
+  const int cidx = lane < nc ? sc.i[lane] : INT_MAX;
   const float sv = nc <= 16   ? sort_desc_values<16>(c, lane)
                    : nc <= 32 ? sort_desc_values<32>(c, lane)
                               : sort_desc_values<64>(c, lane);
@@ -739,6 +742,154 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
   const unsigned long long bm = __ballot(sel);
   if (sel) out[lanes_below(bm)] = cidx;
   if ((lane >= m) & (lane < a.k)) out[lane] = lane == m ? static_cast<int>(L) : -1;
+}
+
+__global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
+  __shared__ TopkScratch sc[4];
+  // the wave index read as a scalar: the row's bookkeeping (divisions for
+  // its position and local block, its pointers) runs on the scalar unit
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (row >= a.rows) return;
+  topk_one_row(a, topk_row(a, row), lane, sc[wave]);
+}
+
+// Lanes below this one inside its half-wave that are set in `mask`, plus
+// base: mbcnt over the whole wave counts, for an upper-half lane, every set
+// lane of the lower half, so those are taken off the base there.
+__device__ __forceinline__ int half_rank(unsigned long long mask, bool upper, int base) {
+  const unsigned lo = static_cast<unsigned>(mask), hi = static_cast<unsigned>(mask >> 32);
+  return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, upper ? base - __popc(lo) : base));
+}
+
+// Two rows per wave, one in each half-wave (rows of at most 32 x 32
+// candidates, k <= 32, fewer than 2^31 rows).  Half-lane h holds its row's
+// candidates h + 32 r in registers, and the threshold and ranking steps of
+// topk_one_row run on both halves at once, so that every sorting network
+// serves two rows.  The candidates reaching either half's threshold are
+// compacted into one list in wave order (each row's in block order), then
+// split into the two halves.  If more than 32 of one row (or 64 of both)
+// reach the threshold, both rows go to topk_one_row instead.
+constexpr int kPairChunks = 32;
+
+__global__ void __launch_bounds__(256) topk_pair_kernel(TopkArgs a) {
+  __shared__ TopkScratch sc[4];
+  const int lane = threadIdx.x & 63, h = lane & 31;
+  const bool upper = lane >= 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t r0 = (blockIdx.x * 4u + static_cast<uint32_t>(wave)) * 2u;
+  if (r0 >= static_cast<uint64_t>(a.rows)) return;
+  const bool two = r0 + 1u < static_cast<uint64_t>(a.rows);
+  // scalar bookkeeping: one 32-bit division for both rows; Bk is a power of
+  // two and the position N' - T + t of a query row is never negative
+  const uint32_t Tw = static_cast<uint32_t>(a.Tw);
+  const uint32_t bg0 = r0 / Tw, tw0 = r0 - bg0 * Tw;
+  const uint32_t bg1 = tw0 + 1u == Tw ? bg0 + 1u : bg0, tw1 = tw0 + 1u == Tw ? 0u : tw0 + 1u;
+  const int bks = __builtin_ctz(static_cast<unsigned>(a.Bk));
+  auto row_L = [&](uint32_t bg, uint32_t tw) {
+    const int64_t len = a.pc.table ? paged_len(a.pc, bg / static_cast<uint32_t>(a.G), a.N) : a.N;
+    return static_cast<int>((len - a.T + a.t0 + tw) >> bks);
+  };
+  TopkRow x0, x1;
+  x0.s = a.S + static_cast<int64_t>(r0) * a.NB;
+  x0.out = a.idx + (static_cast<int64_t>(bg0) * a.T + a.t0 + tw0) * a.k;
+  x0.L = row_L(bg0, tw0);
+  x1.s = x0.s + a.NB;
+  x1.out = a.idx + (static_cast<int64_t>(bg1) * a.T + a.t0 + tw1) * a.k;
+  x1.L = two ? row_L(bg1, tw1) : 0;
+  const int L0 = static_cast<int>(x0.L), L1 = static_cast<int>(x1.L);
+  const int m0 = min(L0, a.k - 1), m1 = min(L1, a.k - 1);
+  const int n = upper ? L1 : L0;  // this lane's row: candidates, picks
+  const int m = upper ? m1 : m0;
+  TopkScratch& s = sc[wave];
+
+  // Each row through a raw buffer of its own candidates (a load past the
+  // row's end returns 0 and reads nothing), one half-wave's loads at a time.
+  // The upper half's loads carry the sc0 cache bit (its reads skip the
+  // per-CU cache; the scores are read once): the two groups differ in an
+  // immediate, so they stay two groups under a uniform resource each
+  // instead of being merged into one load on a per-lane resource.
+  const auto rs0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(x0.s), 0, L0 * 4,
+                                                     kBufferFormat32);
+  const auto rs1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(x1.s), 0, L1 * 4,
+                                                     kBufferFormat32);
+  float x[kPairChunks];
+  if (upper) {
+#pragma unroll
+    for (int r = 0; r < kPairChunks; ++r)
+      x[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs1, 4 * h + 128 * r, 0, 1));
+  } else {
+#pragma unroll
+    for (int r = 0; r < kPairChunks; ++r)
+      x[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs0, 4 * h + 128 * r, 0, 0));
+  }
+  const int lim = n - h;
+#pragma unroll
+  for (int r = 0; r < kPairChunks; ++r) x[r] = 32 * r < lim ? x[r] : -INFINITY;
+  float lm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < kPairChunks; ++r) lm = fmaxf(lm, x[r]);
+  // the m-th largest lane max of each half (kept above -inf, see wave_topk)
+  const int msel = 4 * ((upper ? 32 : 0) + (m > 0 ? m : 1) - 1);
+  const float tau = fmaxf(__int_as_float(__builtin_amdgcn_ds_bpermute(
+                              msel, __float_as_int(sort_desc_values<32>(lm, lane)))),
+                          -FLT_MAX);
+  // compaction of both rows' candidates >= their tau into one list (every
+  // lane stores; a non-candidate to its spare entry 64 + lane); entries
+  // carry the block index and, in bit 16, the row
+  const int nch = (max(L0, L1) + 31) >> 5;  // chunks holding a candidate of either row
+  const int tag = h | (upper ? 1 << 16 : 0);
+  int cnt = 0;  // saturates at 128: positions stay below 192
+#pragma unroll
+  for (int r = 0; r < kPairChunks; ++r) {
+    if (r < nch) {
+      const bool f = x[r] >= tau;
+      const unsigned long long bal = __ballot(f);
+      const int pos = __builtin_amdgcn_mbcnt_hi(
+          static_cast<unsigned>(bal >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bal), cnt));
+      const int slot = f ? pos : 64 + lane;
+      s.v[slot] = x[r];
+      s.i[slot] = tag + 32 * r;
+      cnt = min(cnt + static_cast<int>(__popcll(bal)), 128);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // the list's entry of this lane, its row, and its place in that row's list
+  const bool live = lane < cnt;
+  const float ev = s.v[lane];
+  const int ei = s.i[lane];
+  const bool eup = (ei >> 16) != 0;
+  const unsigned long long in1 = __ballot(live & eup), in0 = __ballot(live & !eup);
+  const int c0 = static_cast<int>(__popcll(in0)), c1 = static_cast<int>(__popcll(in1));
+  if ((cnt > 64) | (max(c0, c1) > 32)) {
+    topk_one_row(a, x0, lane, s);
+    if (two) topk_one_row(a, x1, lane, s);
+    return;
+  }
+  // split: row r0's entries to lanes 0.., row r0 + 1's to lanes 32.., each
+  // in list order (block order)
+  if (live) {
+    const int dst = eup ? 32 + lanes_below(in1) : lanes_below(in0);
+    s.v[dst] = ev;
+    s.i[dst] = ei & 0xFFFF;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // ranking as in topk_one_row, per half
+  const int cn = upper ? c1 : c0;
+  const float c = h < cn ? s.v[lane] : -INFINITY;
+  const int cidx = h < cn ? s.i[lane] : INT_MAX;
+  const float sv = max(c0, c1) <= 16 ? sort_desc_values<16>(c, lane) : sort_desc_values<32>(c, lane);
+  const float vm = __int_as_float(__builtin_amdgcn_ds_bpermute(msel, __float_as_int(sv)));
+  const unsigned long long above = __ballot(c > vm);
+  const int n_above = __popc(upper ? static_cast<unsigned>(above >> 32) : static_cast<unsigned>(above));
+  const bool sel = (c > vm) | ((c == vm) & (half_rank(__ballot(c == vm), upper, 0) < m - n_above));
+  const unsigned long long bm = __ballot(sel);
+  if (upper & !two) return;
+  int32_t* out = upper ? x1.out : x0.out;
+  if (sel) out[half_rank(bm, upper, 0)] = cidx;
+  if ((h >= m) & (h < a.k)) out[h] = h == m ? n : -1;
 }
 
 // Long rows, few of them (decode): four waves per row, each takes every
@@ -782,6 +933,9 @@ hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T, 
   if (a.rows <= 4096 && a.NB >= 1024) {
     // few long rows: spread each row over a workgroup
     hipLaunchKernelGGL(topk_wide_kernel, dim3(static_cast<unsigned>(a.rows)), dim3(256), 0, st, a);
+  } else if (a.k <= 32 && a.NB <= 32 * kPairChunks && a.rows < (int64_t{1} << 31)) {
+    const int64_t grid = (a.rows + 7) / 8;
+    hipLaunchKernelGGL(topk_pair_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a);
   } else {
     const int64_t grid = (a.rows + 3) / 4;
     hipLaunchKernelGGL(topk_rows_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a);

@@ -26,14 +26,42 @@ __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
 }
 
 // The value of lane (lane ^ S), S a power of two below 64, by the cheapest
-// exchange for each distance: a DPP quad permutation for 1 and 2, a swizzle
-// (inside each half-wave) for 4 to 16, a permute for 32.
+// exchange for each distance: a DPP quad permutation for 1 and 2 (every lane
+// has a source, so no old value is kept), a swizzle (inside each half-wave)
+// for 4 to 16, a permute for 32.
 template <int S>
 __device__ __forceinline__ int xlane(int x) {
-  if constexpr (S == 1) return __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);
-  else if constexpr (S == 2) return __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);
+  if constexpr (S == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);
+  else if constexpr (S == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);
   else if constexpr (S < 32) return __builtin_amdgcn_ds_swizzle(x, 0x1F | (S << 10));
-  else return __shfl_xor(x, 32);
+  else
+    return __builtin_amdgcn_ds_bpermute(
+        (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) ^ 32) << 2, x);
+}
+
+// Compare-exchange directions as wave masks.  Lane l keeps the first-ranked
+// of its pair at stage (size, stride) of a bitonic sort when bit `stride` of
+// l is clear exactly in runs whose direction is `first`: the run of size
+// `size` holding l goes first-ranked-first when bit `size` of l is clear or
+// size == nmax (the last merge of runs of nmax lanes).  Used through
+// __builtin_amdgcn_inverse_ballot_w64, the per-lane condition is a constant
+// in scalar registers: no vector instruction per stage.
+constexpr unsigned long long keep_lanes(int size, int stride, int nmax, bool first) {
+  unsigned long long m = 0;
+  for (int l = 0; l < 64; ++l) {
+    const bool run_first = (((l & size) == 0) || size == nmax) == first;
+    if (((l & stride) == 0) == run_first) m |= 1ull << l;
+  }
+  return m;
+}
+
+static_assert(keep_lanes(2, 1, 64, true) == 0x9999999999999999ull, "pairs (0,1) up, (2,3) down");
+static_assert(keep_lanes(64, 32, 64, true) == 0x00000000FFFFFFFFull, "last stage: low half first");
+static_assert(keep_lanes(16, 8, 16, true) == 0x00FF00FF00FF00FFull, "runs of 16 all first");
+
+template <unsigned long long K>
+__device__ __forceinline__ bool lane_in() {
+  return __builtin_amdgcn_inverse_ballot_w64(K);
 }
 
 template <int S>
@@ -50,7 +78,8 @@ template <int SIZE, int STRIDE, int NMAX>
 __device__ __forceinline__ void bitonic_steps(float& v, int& i, int lane, bool best_first) {
   const float pv = xlane<STRIDE>(v);
   const int pi = xlane<STRIDE>(i);
-  const bool keep = ((lane & STRIDE) == 0) == (((lane & SIZE) == 0) == best_first);
+  const bool keep = best_first ? lane_in<keep_lanes(SIZE, STRIDE, 0, true)>()
+                               : lane_in<keep_lanes(SIZE, STRIDE, 0, false)>();
   const bool take = beats(pv, pi, v, i) == keep;
   v = take ? pv : v;
   i = take ? pi : i;
@@ -71,7 +100,7 @@ template <int STRIDE = 32>
 __device__ __forceinline__ void bitonic_merge64(float& v, int& i, int lane) {
   const float pv = xlane<STRIDE>(v);
   const int pi = xlane<STRIDE>(i);
-  const bool take = beats(pv, pi, v, i) == ((lane & STRIDE) == 0);
+  const bool take = beats(pv, pi, v, i) == lane_in<keep_lanes(64, STRIDE, 64, true)>();
   v = take ? pv : v;
   i = take ? pi : i;
   if constexpr (STRIDE > 1) bitonic_merge64<STRIDE / 2>(v, i, lane);
@@ -82,7 +111,7 @@ __device__ __forceinline__ void bitonic_merge64(float& v, int& i, int lane) {
 template <int NMAX = 64, int SIZE = 2, int STRIDE = 1>
 __device__ __forceinline__ float sort_desc_values(float v, int lane) {
   const float pv = xlane<STRIDE>(v);
-  const bool keep = ((lane & STRIDE) == 0) == (((lane & SIZE) == 0) | (SIZE == NMAX));
+  const bool keep = lane_in<keep_lanes(SIZE, STRIDE, NMAX, true)>();
   v = ((pv > v) == keep) ? pv : v;  // keep: the larger of the two
   if constexpr (STRIDE > 1)
     return sort_desc_values<NMAX, SIZE, STRIDE / 2>(v, lane);
@@ -214,7 +243,7 @@ __device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int st
 template <int SIZE = 2, int STRIDE = 1>
 __device__ __forceinline__ int sort_asc16(int key, int lane) {
   const int pk = xlane<STRIDE>(key);
-  const bool keep = ((lane & STRIDE) == 0) == (((lane & SIZE) == 0) | (SIZE == 16));
+  const bool keep = lane_in<keep_lanes(SIZE, STRIDE, 16, true)>();
   key = ((pk < key) == keep) ? pk : key;  // keep: the smaller of the two
   if constexpr (STRIDE > 1)
     return sort_asc16<SIZE, STRIDE / 2>(key, lane);
@@ -228,7 +257,7 @@ __device__ __forceinline__ int sort_asc16(int key, int lane) {
 template <int SIZE = 2, int STRIDE = 1>
 __device__ __forceinline__ int sort_asc64(int key, int lane) {
   const int pk = xlane<STRIDE>(key);
-  const bool keep = ((lane & STRIDE) == 0) == ((lane & SIZE) == 0);
+  const bool keep = lane_in<keep_lanes(SIZE, STRIDE, 64, true)>();
   key = ((pk < key) == keep) ? pk : key;  // keep: the smaller of the two
   if constexpr (STRIDE > 1)
     return sort_asc64<SIZE, STRIDE / 2>(key, lane);
