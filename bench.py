@@ -401,13 +401,17 @@ def topk_leg(args, pre):
     torch.cuda.empty_cache()
     by = acc.topk_bytes(w)
     med = float(np.median(us))
+    # the launch's kernel: two rows per wave for rows of at most 1024 blocks
+    # and k <= 32, else one row per wave
+    nb = (w.N + w.Bk - 1) // w.Bk
+    kname = "topk_pair_kernel" if (w.k <= 32 and nb <= 1024) else "topk_rows_kernel"
     return {"workload": w.name, "rows": w.B * w.G * w.T, "us_p50": med,
             "us_p95": float(np.percentile(us, 95)), "bytes": by["total"],
             "GBps": by["total"] / med / 1e3, "frac_hbm": by["total"] / med / 1e3 / PEAK_HBM_GBS,
             "matches_fused_select": same, "torch_topk_us": float(np.median(tk)),
-            "roofline": roof("topk_rows_kernel", "hbm",
+            "roofline": roof(kname, "hbm",
                              by["total"] / (kt["topk"]["avg_launch_ms"] * 1e-3) / 1e9,
-                             PEAK_HBM_GBS, "GB/s", counter_traffic("topk_rows_kernel"),
+                             PEAK_HBM_GBS, "GB/s", counter_traffic(kname),
                              bytes_per_launch=by["total"],
                              avg_launch_ms=kt["topk"]["avg_launch_ms"])}
 
@@ -747,7 +751,7 @@ def main():
         sel_avg = sel_k["avg_launch_ms"] if sel_k else sel
         ach_s = fl["index"] / (sel_k["ms_per_step"] if sel_k else sel) / 1e9
         rl.append(roof("index_tile_kernel (fused select: scores, block max, top-k)" if fused else
-                       "index_tile_kernel (block scores, written) + topk_rows_kernel, window "
+                       "index_tile_kernel (block scores, written) + top-k kernel, window "
                        "after window", "mfma", ach_s, PEAK_BF16_TFLOPS, "TFLOP/s",
                        counter_traffic("index_tile_kernel<8, 15, false, false, 128>")
                        if fused and w.G == 8 else None,
