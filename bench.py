@@ -402,9 +402,9 @@ def topk_leg(args, pre):
     by = acc.topk_bytes(w)
     med = float(np.median(us))
     # the launch's kernel: two rows per wave for rows of at most 1024 blocks
-    # and k <= 32, else one row per wave
+    # and k <= 16, else one row per wave
     nb = (w.N + w.Bk - 1) // w.Bk
-    kname = "topk_pair_kernel" if (w.k <= 32 and nb <= 1024) else "topk_rows_kernel"
+    kname = "topk_pair_kernel" if (w.k <= 16 and nb <= 1024) else "topk_rows_kernel"
     return {"workload": w.name, "rows": w.B * w.G * w.T, "us_p50": med,
             "us_p95": float(np.percentile(us, 95)), "bytes": by["total"],
             "GBps": by["total"] / med / 1e3, "frac_hbm": by["total"] / med / 1e3 / PEAK_HBM_GBS,

@@ -763,7 +763,8 @@ __device__ __forceinline__ int half_rank(unsigned long long mask, bool upper, in
 }
 
 // Two rows per wave, one in each half-wave (rows of at most 32 x 32
-// candidates, k <= 32, fewer than 2^31 rows).  Half-lane h holds its row's
+// candidates, k <= 16, fewer than 2^31 rows; with more picks the m-th
+// largest of only 32 lane maxima lets most of a row through).  Half-lane h holds its row's
 // candidates h + 32 r in registers, and the threshold and ranking steps of
 // topk_one_row run on both halves at once, so that every sorting network
 // serves two rows.  The candidates reaching either half's threshold are
@@ -933,7 +934,7 @@ hipError_t launch_topk_rows(const float* S, int32_t* idx, int64_t B, int64_t T, 
   if (a.rows <= 4096 && a.NB >= 1024) {
     // few long rows: spread each row over a workgroup
     hipLaunchKernelGGL(topk_wide_kernel, dim3(static_cast<unsigned>(a.rows)), dim3(256), 0, st, a);
-  } else if (a.k <= 32 && a.NB <= 32 * kPairChunks && a.rows < (int64_t{1} << 31)) {
+  } else if (a.k <= 16 && a.NB <= 32 * kPairChunks && a.rows < (int64_t{1} << 31)) {
     const int64_t grid = (a.rows + 7) / 8;
     hipLaunchKernelGGL(topk_pair_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a);
   } else {

@@ -244,7 +244,7 @@ def test_topk_random_scores():
     (8, 600, 200000, 16, 128, 3.0),   # 1563 candidates: chunks past the registers
     (8, 700, 700, 7, 128, 2.0),       # short rows, m < 16
     (8, 600, 65536, 32, 64, 2.0),     # 31 picks
-    (8, 600, 32768, 32, 32, 0.25),    # two rows per wave, > 32 survivors: one-row path
+    (8, 600, 131072, 16, 128, 0.25),  # two rows per wave, > 32 survivors: one-row path
     (1, 701, 90000, 16, 128, 3.0),    # an odd number of rows: the last wave holds one
 ])
 def test_topk_long_rows(G, T, N, k, Bk, scale):
