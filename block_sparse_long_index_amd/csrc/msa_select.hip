@@ -265,11 +265,39 @@ __device__ __forceinline__ void index_tile(
     }
   };
 
+  // The fused bf16 selection reads only blocks before the local block (all
+  // keys inside N): there each wave's loads go straight from memory into LDS
+  // (global_load_lds: lane l of an instruction fills 16 B at the
+  // instruction's base + 16 l), no registers hold the block in between.
+  // Wave w's instruction j fills the 1 KB segment j * NW + w of the buffer;
+  // its lanes read the chunks that the swizzled layout puts there.
+  constexpr bool kDirect = !WRITE_S && !F8;
+  constexpr int NW = NT / 64;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the LDS base is scalar (M0)
+  auto direct_block = [&](int buf, int64_t kb) {
+    const unsigned char* src = kbase + kb * (kBlock * ROWB);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int seg = j * NW + wave_s;
+      const int r = seg * 4 + (lane >> 4);        // (seg * 1024 + lane * 16) >> 8
+      const int c = (lane & 15) ^ (r & 15);       // swz(r, c) = seg * 1024 + lane * 16
+      __builtin_amdgcn_global_load_lds(
+          src + static_cast<uint32_t>(r * ROWB + c * 16),
+          reinterpret_cast<__attribute__((address_space(3))) void*>(
+              reinterpret_cast<uintptr_t>(kbuf[buf] + seg * 1024)),
+          16, 0, 0);
+    }
+  };
+
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     if (j < nkb) {
-      load_block(j);
-      store_block(j, j);
+      if constexpr (kDirect) {
+        direct_block(j, j);
+      } else {
+        load_block(j);
+        store_block(j, j);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // q^I fragments and blocks 0 .. D-1 have landed
@@ -277,7 +305,13 @@ __device__ __forceinline__ void index_tile(
 
   for (int64_t kb = 0; kb < nkb; ++kb) {
     const bool more = kb + D < nkb;
-    load_block(more ? kb + D : kb);
+    // the buffer of block kb + D held block kb - D, which every wave has
+    // left: a barrier followed the iteration of block kb - D
+    if constexpr (kDirect) {
+      if (more) direct_block((kb + D) & (R - 1), kb + D);
+    } else {
+      load_block(more ? kb + D : kb);
+    }
     const unsigned char* buf = kbuf[kb & (R - 1)];
     float m0 = -INFINITY, m1 = -INFINITY;
     const bool masked = WRITE_S && (kb == L);
@@ -393,8 +427,15 @@ __device__ __forceinline__ void index_tile(
       }
     }
 
-    if (more) store_block((kb + D) & (R - 1), kb + D);
-    if ((kb & (D - 1)) == D - 1 || kb + 1 == nkb) __syncthreads();
+    if constexpr (!kDirect) {
+      if (more) store_block((kb + D) & (R - 1), kb + D);
+    }
+    if ((kb & (D - 1)) == D - 1 || kb + 1 == nkb) {
+      // direct loads land in LDS asynchronously: this wave's must be done
+      // before the barrier publishes their blocks
+      if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   if (WRITE_S) {
