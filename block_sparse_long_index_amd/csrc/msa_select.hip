@@ -265,24 +265,28 @@ __device__ __forceinline__ void index_tile(
     }
   };
 
-  // The fused bf16 selection reads only blocks before the local block (all
-  // keys inside N): there each wave's loads go straight from memory into LDS
-  // (global_load_lds: lane l of an instruction fills 16 B at the
-  // instruction's base + 16 l), no registers hold the block in between.
-  // Wave w's instruction j fills the 1 KB segment j * NW + w of the buffer;
-  // its lanes read the chunks that the swizzled layout puts there.
-  constexpr bool kDirect = !WRITE_S && !F8;
+  // bf16 blocks go straight from memory into LDS (global_load_lds: lane l
+  // of an instruction fills 16 B at the instruction's base + 16 l), no
+  // registers hold a block in between.  Wave w's instruction j fills the 1 KB
+  // segment j * NW + w of the buffer; its lanes read the chunks that the
+  // swizzled layout puts there.  Only the local block can hold keys past N
+  // (the scores-writing tiles score it): their rows re-read key N - 1, and
+  // the causal mask of the local block drops them.
+  constexpr bool kDirect = !F8;
   constexpr int NW = NT / 64;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the LDS base is scalar (M0)
   auto direct_block = [&](int buf, int64_t kb) {
     const unsigned char* src = kbase + kb * (kBlock * ROWB);
+    const int64_t last = a.N - 1 - kb * kBlock;  // last row of the block inside N
+    // (the selection reads only blocks before the local one: no clamp)
+    const int lr = WRITE_S && last < kBlock - 1 ? static_cast<int>(last) : kBlock - 1;
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int seg = j * NW + wave_s;
       const int r = seg * 4 + (lane >> 4);        // (seg * 1024 + lane * 16) >> 8
       const int c = (lane & 15) ^ (r & 15);       // swz(r, c) = seg * 1024 + lane * 16
       __builtin_amdgcn_global_load_lds(
-          src + static_cast<uint32_t>(r * ROWB + c * 16),
+          src + static_cast<uint32_t>((WRITE_S ? min(r, lr) : r) * ROWB + c * 16),
           reinterpret_cast<__attribute__((address_space(3))) void*>(
               reinterpret_cast<uintptr_t>(kbuf[buf] + seg * 1024)),
           16, 0, 0);
