@@ -103,7 +103,7 @@ struct TileRing {
   // The LDS ring of k^I blocks of the tile body (described there).
   static constexpr int D = TileShape<G>::NT < 512 ? 1 : (F8 ? 4 : 2);
   static constexpr int R = 2 * D;
-  static constexpr int PITCH = F8 ? 144 : 256;  // LDS row pitch
+  static constexpr int PITCH = F8 ? 128 : 256;  // bytes per key row in LDS
 };
 
 // One work item (sequence b = item % B, position tile tile_hi - item / B).
@@ -119,18 +119,18 @@ __device__ __forceinline__ void index_tile(
   constexpr int QT = TS::QT, NT = TS::NT;
   constexpr int ROWB = F8 ? 128 : 256;      // bytes per k^I / q^I row
   constexpr int CPR = ROWB / 16;            // 16-B chunks per row
-  constexpr int PITCH = F8 ? 144 : 256;     // LDS row pitch
+  constexpr int PITCH = F8 ? 128 : 256;     // bytes per key row in LDS
   constexpr int PF = 128 * CPR / NT;        // 16-B chunks per thread per block
   static_assert(PF * NT == 128 * CPR, "block chunks must split evenly over the threads");
   // A ring of R = 2D block buffers with a prefetch distance of D: block kb+D
-  // is loaded into registers while block kb is scored and stored into buffer
-  // (kb+D) % R afterwards; that buffer was last read for block kb-D.  The
-  // workgroup then needs a barrier only after every D-th block (and after the
-  // last): any D consecutive blocks contain one barrier, which both publishes
-  // each stored block before its use (stored D blocks ahead) and is passed by
-  // every wave after it read the block D back before that buffer is reused.
-  // D = 2 for bf16 (4 x 32 KB of LDS), 4 for fp8 (8 x 18 KB); workgroups of
-  // fewer than 8 waves (G < 4) keep D = 1 so that several fit on a CU.
+  // is loaded into buffer (kb+D) % R while block kb is scored; that buffer
+  // was last read for block kb-D.  The workgroup then needs a barrier only
+  // after every D-th block (and after the last): any D consecutive blocks
+  // contain one barrier, which both publishes each loaded block before its
+  // use (loaded D blocks ahead) and is passed by every wave after it read the
+  // block D back before that buffer is reused.  D = 2 for bf16 (4 x 32 KB of
+  // LDS), 4 for fp8 (8 x 16 KB); workgroups of fewer than 8 waves (G < 4)
+  // keep D = 1 so that several fit on a CU.
   constexpr int D = TileRing<G, F8>::D;
   constexpr int R = TileRing<G, F8>::R;
   static_assert(PITCH == TileRing<G, F8>::PITCH, "LDS pitch");
@@ -219,61 +219,17 @@ __device__ __forceinline__ void index_tile(
     }
   };
 
-  uint4 pf[PF];
-  // Keys past N re-read key N-1 and are zeroed when stored.  The loads are
-  // issued on every iteration (a block already loaded when there is no next
-  // one) and nothing uses them before store_block: a use right after a load
-  // under a branch, such as the zeroing select, makes the compiler wait for
-  // the load at the branch's end, before the block's products.
-  // Thread chunk j of a block is row kr0 + j * NT / CPR, 16-B chunk kc0: its
-  // offsets are per-thread constants plus the block's base; only the block
-  // holding key N - 1 (the last one) needs its rows clamped (loads) and
-  // zeroed (stores), which is one uniform branch per block.
-  const int kr0 = tid / CPR, kc0 = tid % CPR;
-  constexpr int RS = NT / CPR;  // rows between a thread's chunks
-  auto load_block = [&](int64_t kb) {
-    const unsigned char* src = kbase + kb * (kBlock * ROWB);
-    const int64_t last = a.N - 1 - kb * kBlock;  // last row of the block inside N
-    // unsigned 32-bit offsets from a uniform base: scalar-base loads
-    if (last >= kBlock - 1) {
-#pragma unroll
-      for (int j = 0; j < PF; ++j)
-        pf[j] = ld16(src + static_cast<uint32_t>((kr0 + RS * j) * ROWB + kc0 * 16));
-    } else {
-      const int lr = static_cast<int>(last);
-#pragma unroll
-      for (int j = 0; j < PF; ++j)
-        pf[j] = ld16(src + static_cast<uint32_t>(min(kr0 + RS * j, lr) * ROWB + kc0 * 16));
-    }
-  };
-  auto store_block = [&](int buf, int64_t kb) {
-    unsigned char* dst = kbuf[buf];
-    const int64_t last = a.N - 1 - kb * kBlock;
-    if (last >= kBlock - 1) {
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int r = kr0 + RS * j;
-        *reinterpret_cast<uint4*>(&dst[F8 ? r * PITCH + kc0 * 16 : swz(r, kc0)]) = pf[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int r = kr0 + RS * j;
-        *reinterpret_cast<uint4*>(&dst[F8 ? r * PITCH + kc0 * 16 : swz(r, kc0)]) =
-            r <= last ? pf[j] : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  // bf16 blocks go straight from memory into LDS (global_load_lds: lane l
-  // of an instruction fills 16 B at the instruction's base + 16 l), no
-  // registers hold a block in between.  Wave w's instruction j fills the 1 KB
-  // segment j * NW + w of the buffer; its lanes read the chunks that the
-  // swizzled layout puts there.  Only the local block can hold keys past N
-  // (the scores-writing tiles score it): their rows re-read key N - 1, and
-  // the causal mask of the local block drops them.
-  constexpr bool kDirect = !F8;
+  // Blocks go straight from memory into LDS (global_load_lds: lane l of an
+  // instruction fills 16 B at the instruction's base + 16 l), no registers
+  // hold a block in between.  The LDS block is 256-B lines in the swizzled
+  // layout swz (a line is one bf16 key row, or two fp8 rows, which are also
+  // contiguous in memory), so wave w's instruction j fills the 1 KB segment
+  // j * NW + w of the buffer and its lanes read the chunks that the layout
+  // puts there.  Only the local block can hold keys past N (the
+  // scores-writing tiles score it): their rows re-read key N - 1, and the
+  // causal mask of the local block drops them.
   constexpr int NW = NT / 64;
+  static_assert(PF * NW * 1024 == 128 * ROWB, "1 KB segments cover the block");
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the LDS base is scalar (M0)
   auto direct_block = [&](int buf, int64_t kb) {
     const unsigned char* src = kbase + kb * (kBlock * ROWB);
@@ -283,10 +239,13 @@ __device__ __forceinline__ void index_tile(
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int seg = j * NW + wave_s;
-      const int r = seg * 4 + (lane >> 4);        // (seg * 1024 + lane * 16) >> 8
-      const int c = (lane & 15) ^ (r & 15);       // swz(r, c) = seg * 1024 + lane * 16
+      const int ln = seg * 4 + (lane >> 4);       // (seg * 1024 + lane * 16) >> 8
+      const int c = (lane & 15) ^ (ln & 15);      // swz(ln, c) = seg * 1024 + lane * 16
+      // the chunk's key row and its offset in that row
+      const int r = F8 ? 2 * ln + (c >> 3) : ln;
+      const int co = F8 ? (c & 7) * 16 : c * 16;
       __builtin_amdgcn_global_load_lds(
-          src + static_cast<uint32_t>((WRITE_S ? min(r, lr) : r) * ROWB + c * 16),
+          src + static_cast<uint32_t>((WRITE_S ? min(r, lr) : r) * ROWB + co),
           reinterpret_cast<__attribute__((address_space(3))) void*>(
               reinterpret_cast<uintptr_t>(kbuf[buf] + seg * 1024)),
           16, 0, 0);
@@ -296,12 +255,7 @@ __device__ __forceinline__ void index_tile(
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     if (j < nkb) {
-      if constexpr (kDirect) {
-        direct_block(j, j);
-      } else {
-        load_block(j);
-        store_block(j, j);
-      }
+      direct_block(j, j);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // q^I fragments and blocks 0 .. D-1 have landed
@@ -311,11 +265,7 @@ __device__ __forceinline__ void index_tile(
     const bool more = kb + D < nkb;
     // the buffer of block kb + D held block kb - D, which every wave has
     // left: a barrier followed the iteration of block kb - D
-    if constexpr (kDirect) {
-      if (more) direct_block((kb + D) & (R - 1), kb + D);
-    } else {
-      load_block(more ? kb + D : kb);
-    }
+    if (more) direct_block((kb + D) & (R - 1), kb + D);
     const unsigned char* buf = kbuf[kb & (R - 1)];
     float m0 = -INFINITY, m1 = -INFINITY;
     const bool masked = WRITE_S && (kb == L);
@@ -325,9 +275,13 @@ __device__ __forceinline__ void index_tile(
     typedef uint4 KFrag[8];
     auto frags = [&](int kt, KFrag& av) {
       if constexpr (F8) {
-        const unsigned char* rp = buf + (kt * 32 + l32) * PITCH + 32 * half;
+        // key row r = kt * 32 + l32 is half of line r / 2 (chunks 8 (r & 1) ..
+        // +7); k-step s reads its 16-B chunks 4 (s >> 1) + 2 half + (s & 1)
+        const int r = kt * 32 + l32;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) av[s] = *reinterpret_cast<const uint4*>(rp + 64 * (s >> 1) + 16 * (s & 1));
+        for (int s = 0; s < 4; ++s)
+          av[s] = *reinterpret_cast<const uint4*>(
+              &buf[swz(r >> 1, ((r & 1) << 3) | (4 * (s >> 1) + 2 * half + (s & 1)))]);
       } else {
         // rows kt * 32 + l32 share l32's swizzle (32 is a multiple of 16):
         // the lane's offsets plus kt * 32 rows
@@ -431,13 +385,10 @@ __device__ __forceinline__ void index_tile(
       }
     }
 
-    if constexpr (!kDirect) {
-      if (more) store_block((kb + D) & (R - 1), kb + D);
-    }
     if ((kb & (D - 1)) == D - 1 || kb + 1 == nkb) {
-      // direct loads land in LDS asynchronously: this wave's must be done
+      // the loads land in LDS asynchronously: this wave's must be done
       // before the barrier publishes their blocks
-      if constexpr (kDirect) __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
