@@ -712,11 +712,11 @@ __device__ __forceinline__ void topk_one_row(const TopkArgs& a, const TopkRow& x
   // from them must be uniform (the pair kernel's fallback otherwise sees
   // them through per-lane copies)
   const uint64_t sp = reinterpret_cast<uint64_t>(x.s);
-  const float* src = reinterpret_cast<const float*>(
-      (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sp >> 32))) << 32) |
-      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sp))));
-  const int nc = wave_topk<16, false>(src, __builtin_amdgcn_readfirstlane(static_cast<int>(L)), 0, 64,
-                                      m, lane, sc, v, vi);
+  const uint32_t sp_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sp >> 32));
+  const uint32_t sp_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sp));
+  const float* src = reinterpret_cast<const float*>((static_cast<uint64_t>(sp_hi) << 32) | sp_lo);
+  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(L));
+  const int nc = wave_topk<16, false>(src, n, 0, 64, m, lane, sc, v, vi);
   if (nc < 0) {
     write_selection(out, vi, m, static_cast<int>(L), a.k, lane);
     return;
@@ -755,18 +755,19 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(TopkArgs a) {
 // lane of the lower half, so those are taken off the base there.
 __device__ __forceinline__ int half_rank(unsigned long long mask, bool upper, int base) {
   const unsigned lo = static_cast<unsigned>(mask), hi = static_cast<unsigned>(mask >> 32);
-  return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, upper ? base - __popc(lo) : base));
+  const int b = upper ? base - static_cast<int>(__popc(lo)) : base;
+  return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, b));
 }
 
 // Two rows per wave, one in each half-wave (rows of at most 32 x 32
 // candidates, k <= 16, fewer than 2^31 rows; with more picks the m-th
-// largest of only 32 lane maxima lets most of a row through).  Half-lane h holds its row's
-// candidates h + 32 r in registers, and the threshold and ranking steps of
-// topk_one_row run on both halves at once, so that every sorting network
-// serves two rows.  The candidates reaching either half's threshold are
-// compacted into one list in wave order (each row's in block order), then
-// split into the two halves.  If more than 32 of one row (or 64 of both)
-// reach the threshold, both rows go to topk_one_row instead.
+// largest of only 32 lane maxima lets most of a row through).  Half-lane h
+// holds its row's candidates h + 32 r in registers, and the threshold and
+// ranking steps of topk_one_row run on both halves at once, so that every
+// sorting network serves two rows.  The candidates reaching either half's
+// threshold are compacted into one list in wave order (each row's in block
+// order), then split into the two halves.  If more than 32 of one row (or
+// 64 of both) reach the threshold, both rows go to topk_one_row instead.
 constexpr int kPairChunks = 32;
 
 __global__ void __launch_bounds__(256) topk_pair_kernel(TopkArgs a) {
@@ -842,8 +843,8 @@ __global__ void __launch_bounds__(256) topk_pair_kernel(TopkArgs a) {
     if (r < nch) {
       const bool f = x[r] >= tau;
       const unsigned long long bal = __ballot(f);
-      const int pos = __builtin_amdgcn_mbcnt_hi(
-          static_cast<unsigned>(bal >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bal), cnt));
+      const unsigned bal_lo = static_cast<unsigned>(bal), bal_hi = static_cast<unsigned>(bal >> 32);
+      const int pos = __builtin_amdgcn_mbcnt_hi(bal_hi, __builtin_amdgcn_mbcnt_lo(bal_lo, cnt));
       const int slot = f ? pos : 64 + lane;
       s.v[slot] = x[r];
       s.i[slot] = tag + 32 * r;
@@ -877,10 +878,12 @@ __global__ void __launch_bounds__(256) topk_pair_kernel(TopkArgs a) {
   const int cn = upper ? c1 : c0;
   const float c = h < cn ? s.v[lane] : -INFINITY;
   const int cidx = h < cn ? s.i[lane] : INT_MAX;
-  const float sv = max(c0, c1) <= 16 ? sort_desc_values<16>(c, lane) : sort_desc_values<32>(c, lane);
+  const float sv =
+      max(c0, c1) <= 16 ? sort_desc_values<16>(c, lane) : sort_desc_values<32>(c, lane);
   const float vm = __int_as_float(__builtin_amdgcn_ds_bpermute(msel, __float_as_int(sv)));
   const unsigned long long above = __ballot(c > vm);
-  const int n_above = __popc(upper ? static_cast<unsigned>(above >> 32) : static_cast<unsigned>(above));
+  const int n_above =
+      __popc(upper ? static_cast<unsigned>(above >> 32) : static_cast<unsigned>(above));
   const bool sel = (c > vm) | ((c == vm) & (half_rank(__ballot(c == vm), upper, 0) < m - n_above));
   const unsigned long long bm = __ballot(sel);
   if (upper & !two) return;

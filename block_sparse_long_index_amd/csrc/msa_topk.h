@@ -156,7 +156,8 @@ __device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int st
   float x[R];
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    x[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (e0 + lane + step * r), 0, 0));
+    x[r] = __int_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (e0 + lane + step * r), 0, 0));
 #pragma unroll
   for (int r = 0; r < R; ++r) x[r] = lane < n - e0 - step * r ? x[r] : -INFINITY;
   const int rest = e0 + step * R;
@@ -178,8 +179,8 @@ __device__ __forceinline__ int wave_topk(const float* src, int n, int e0, int st
   auto chunk = [&](int c0, float xv) {
     const bool f = xv >= tau;
     const unsigned long long bal = __ballot(f);
-    const int pos = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bal >> 32),
-                                              __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bal), cnt));
+    const unsigned bal_lo = static_cast<unsigned>(bal), bal_hi = static_cast<unsigned>(bal >> 32);
+    const int pos = __builtin_amdgcn_mbcnt_hi(bal_hi, __builtin_amdgcn_mbcnt_lo(bal_lo, cnt));
     const int slot = f ? pos : 64 + lane;
     sc.v[slot] = xv;
     sc.i[slot] = c0 + lane;
