@@ -10,7 +10,7 @@ import torch
 
 from block_sparse_long_index_amd import ops
 from msa_inputs import WORKLOADS, Workload, make_inputs, sample_rows
-from test_parity_gpu import check_invariants, compare_rows, say
+from test_parity_gpu import check_invariants, compare_rows, gather_bgt, oracle_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -59,10 +59,13 @@ def test_prefill_small_all_rows(name, B, T, N, Hq, G, k, Bk):
     compare_rows(w, inp, idx, O, lse, rb, rt, S=S, tag=name)
 
 
-def test_select_windows():
+@pytest.mark.parametrize("k", [32, 8])
+def test_select_windows(k):
     """A workspace of a few rows of scores makes the selection run in many
-    windows; the result must not change."""
-    w = Workload("win", B=2, T=1200, N=1300, Hq=16, G=4, k=32, Bk=64, seed=9)
+    windows; the result must not change.  k = 8 ranks with two rows per wave,
+    whose row pairs then straddle (sequence, group) rows inside each window
+    of 37 query rows."""
+    w = Workload("win", B=2, T=1200, N=1300, Hq=16, G=4, k=k, Bk=64, seed=9)
     inp = make_inputs(w, device="cuda")
     idx1 = ops.select_blocks(inp["qI"], inp["kI"], w.k, Bk=64)
     row_bytes = w.B * w.G * ((w.N + 63) // 64) * 4
@@ -70,6 +73,11 @@ def test_select_windows():
     idx2 = ops.select_blocks(inp["qI"], inp["kI"], w.k, workspace=ws, Bk=64)
     torch.cuda.synchronize()
     assert torch.equal(idx1, idx2)
+    rows = np.arange(0, w.T, 7)
+    rb = np.repeat(np.arange(w.B), rows.size)
+    rt = np.tile(rows, w.B)
+    ref = oracle_rows(w, inp, rb, rt)
+    assert np.array_equal(gather_bgt(idx2, rb, rt).numpy(), ref["idx"])
 
 
 @pytest.mark.parametrize("N,Bk,k", [(1000, 64, 32), (5000, 32, 64), (70000, 64, 32),
