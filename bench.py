@@ -476,12 +476,9 @@ def decode_leg(args, fp8=False, cpu=False):
         ops.select_blocks(qI, kI, w.k, out=idx, workspace=ws_s, Bk=w.Bk)
         ops.sparse_attn_decode(q, K, V, idx, out=O, workspace=ws_a, Bk=w.Bk)
 
-    # the bf16 step as one msa_decode call (fp8 index keys: the two calls)
+    # the step as one msa_decode (msa_decode_fp8) call
     idx1, O1 = torch.empty_like(idx), torch.empty_like(O)
-    ws_1 = None
-    if not fp8:
-        ws_1 = torch.empty(ops.workspace_bytes(ops.OP_DECODE, d), dtype=torch.uint8,
-                           device="cuda")
+    ws_1 = torch.empty(ops.workspace_bytes(ops.OP_DECODE, d), dtype=torch.uint8, device="cuda")
 
     def one_call():
         ops.decode(qI, kI, q, K, V, w.k, out=(idx1, O1), workspace=ws_1, Bk=w.Bk)
@@ -500,25 +497,23 @@ def decode_leg(args, fp8=False, cpu=False):
             times.append(a.elapsed_time(b) * 1e3)
         return np.array(times)
 
-    step = two_calls if fp8 else one_call
     us2 = timed(two_calls)
-    us = us2 if fp8 else timed(one_call)
+    us = timed(one_call)
     by = acc.decode_bytes(w, index_bytes=1 if fp8 else 2)
     med = float(np.median(us))
     out = {"workload": w.name, "us_p50": med, "us_p95": float(np.percentile(us, 95)),
            "bytes": by["total"], "GBps": by["total"] / med / 1e3,
            "frac_hbm": by["total"] / med / 1e3 / PEAK_HBM_GBS,
-           "step": ("msa_select_blocks_fp8, then msa_sparse_attn_decode" if fp8 else
-                    "one msa_decode call: index-key scan, then one workgroup per (sequence, "
-                    "group) selecting, attending and merging its blocks"),
+           "step": ("one msa_decode%s call: index-key scan, then one workgroup per (sequence, "
+                    "group) selecting, attending and merging its blocks" % ("_fp8" if fp8 else "")),
            "note": "last-level cache flushed before each step"}
-    if not fp8:
-        out["two_calls"] = {"us_p50": float(np.median(us2)),
-                            "GBps": by["total"] / float(np.median(us2)) / 1e3,
-                            "calls": "msa_select_blocks, then msa_sparse_attn_decode",
-                            "idx_equal": bool(torch.equal(idx1, idx)),
-                            "O_max_abs_diff": float((O1.float() - O.float()).abs().max())}
-    kt = kernel_times(step, args.decode_reps,
+    out["two_calls"] = {"us_p50": float(np.median(us2)),
+                        "GBps": by["total"] / float(np.median(us2)) / 1e3,
+                        "calls": "msa_select_blocks%s, then msa_sparse_attn_decode"
+                                 % ("_fp8" if fp8 else ""),
+                        "idx_equal": bool(torch.equal(idx1, idx)),
+                        "O_max_abs_diff": float((O1.float() - O.float()).abs().max())}
+    kt = kernel_times(one_call, args.decode_reps,
                       between=lambda: torch.sum(flush, dim=0, out=sink))
     out["kernel_us_per_step"] = {k: v["ms_per_step"] * 1e3 for k, v in kt.items()
                                  if isinstance(v, dict)}

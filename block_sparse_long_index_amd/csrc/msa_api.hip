@@ -706,12 +706,15 @@ int msa_sparse_attn_decode(const msa_dims_t* d, const void* q, const void* K, co
   return MSA_OK;
 }
 
-int msa_decode(const msa_dims_t* d, const void* qI, const void* kI, const void* q, const void* K,
-               const void* V, int32_t* idx, void* O, float* lse, void* ws, size_t ws_bytes,
-               void* stream) {
+}  // extern "C"
+
+static int decode_impl(const msa_dims_t* d, const void* qI, const void* kI, const void* q,
+                       const void* K, const void* V, int32_t* idx, void* O, float* lse, void* ws,
+                       size_t ws_bytes, void* stream, bool fp8, const char* name) {
   MSA_TRY(check_dims(d));
-  if (d->T != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "decode needs T == 1 (got %lld)",
+  if (d->T != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "%s needs T == 1 (got %lld)", name,
                              (long long)d->T);
+  if (fp8) MSA_TRY(need_bk128(d, name));
   MSA_TRY(check_ptr(qI, "qI"));
   MSA_TRY(check_ptr(kI, "kI"));
   MSA_TRY(check_ptr(q, "q"));
@@ -723,11 +726,11 @@ int msa_decode(const msa_dims_t* d, const void* qI, const void* kI, const void* 
   MSA_TRY(check_ptr(ws, "ws"));
   const size_t need = decode1_ws(d);
   if (ws_bytes < need)
-    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "msa_decode needs %zu workspace bytes, got %zu",
-                need, ws_bytes);
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "%s needs %zu workspace bytes, got %zu", name, need,
+                ws_bytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* S = static_cast<float*>(ws);
-  hipError_t e = msa::launch_decode_scan(false, qI, kI, S, d->B, d->N, d->G, d->Bk, kContiguous,
+  hipError_t e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, d->Bk, kContiguous,
                                          st);
   if (e == hipSuccess) {
     if (d->B * d->G >= kStepMinRows) {
@@ -745,8 +748,23 @@ int msa_decode(const msa_dims_t* d, const void* qI, const void* kI, const void* 
       }
     }
   }
-  if (e != hipSuccess) return hip_fail(e, "msa_decode");
+  if (e != hipSuccess) return hip_fail(e, name);
   return MSA_OK;
+}
+
+extern "C" {
+
+int msa_decode(const msa_dims_t* d, const void* qI, const void* kI, const void* q, const void* K,
+               const void* V, int32_t* idx, void* O, float* lse, void* ws, size_t ws_bytes,
+               void* stream) {
+  return decode_impl(d, qI, kI, q, K, V, idx, O, lse, ws, ws_bytes, stream, false, "msa_decode");
+}
+
+int msa_decode_fp8(const msa_dims_t* d, const void* qI, const void* kI, const void* q,
+                   const void* K, const void* V, int32_t* idx, void* O, float* lse, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return decode_impl(d, qI, kI, q, K, V, idx, O, lse, ws, ws_bytes, stream, true,
+                     "msa_decode_fp8");
 }
 
 }  // extern "C"

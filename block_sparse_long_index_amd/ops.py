@@ -45,6 +45,7 @@ _SIGS = {
     "msa_sparse_attn_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "msa_prefill": (ctypes.c_int, [_P] * 10 + [ctypes.c_size_t, _P, _P]),
     "msa_decode": (ctypes.c_int, [_P] * 10 + [ctypes.c_size_t, _P]),
+    "msa_decode_fp8": (ctypes.c_int, [_P] * 10 + [ctypes.c_size_t, _P]),
     "msa_sparse_attn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                 _P, ctypes.c_size_t, _P]),
     "msa_train_backward": (ctypes.c_int, [_P] * 17 + [ctypes.c_size_t, _P]),
@@ -419,14 +420,18 @@ def sparse_attn_decode(q, K, V, idx, return_lse=False, out=None, workspace=None,
 
 
 def decode(qI, kI, q, K, V, k, return_lse=False, out=None, workspace=None, Bk=128):
-    """Stages 1-4 of a decode step in one call (msa_decode).  qI [B,1,G,128],
-    kI [B,N,128], q [B,Hq,128], K/V [B,G,N,128] -> (idx [B,G,1,k] int32,
+    """Stages 1-4 of a decode step in one call (msa_decode, or msa_decode_fp8
+    for float8_e4m3fn index inputs).  qI [B,1,G,128], kI [B,N,128] (both bf16
+    or both fp8), q [B,Hq,128], K/V [B,G,N,128] -> (idx [B,G,1,k] int32,
     O [B,Hq,128] bf16) and lse [B,Hq] fp32 when return_lse.  out: optional
     (idx, O)."""
     B, Hq, dh = q.shape
     _, G, N, _ = K.shape
-    _need(qI, "qI", torch.bfloat16, (B, 1, G, 128))
-    _need(kI, "kI", torch.bfloat16, (B, N, 128))
+    if qI.dtype not in _INDEX_DTYPES:
+        raise ValueError("qI must be bfloat16 or float8_e4m3fn, got %s" % qI.dtype)
+    sfx = _INDEX_DTYPES[qI.dtype]
+    _need(qI, "qI", qI.dtype, (B, 1, G, 128))
+    _need(kI, "kI", qI.dtype, (B, N, 128))
     _need(q, "q", torch.bfloat16)
     _need(K, "K", torch.bfloat16, (B, G, N, dh))
     _need(V, "V", torch.bfloat16, (B, G, N, dh))
@@ -440,9 +445,10 @@ def decode(qI, kI, q, K, V, k, return_lse=False, out=None, workspace=None, Bk=12
     _need(O, "O", torch.bfloat16, q.shape)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
     ws, nbytes = _workspace(OP_DECODE, d, workspace)
-    _check(lib().msa_decode(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(q), _ptr(K), _ptr(V),
-                            _ptr(idx), _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()),
-           "msa_decode")
+    name = "msa_decode" + sfx
+    _check(getattr(lib(), name)(ctypes.byref(d), _ptr(qI), _ptr(kI), _ptr(q), _ptr(K), _ptr(V),
+                                _ptr(idx), _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()),
+           name)
     return (idx, O, lse) if return_lse else (idx, O)
 
 

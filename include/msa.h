@@ -385,6 +385,19 @@ int msa_decode(const msa_dims_t *dims, const void *qI, const void *kI, const voi
                size_t ws_bytes, void *stream);
 
 /*
+ * msa_decode on 8-bit (E4M3) index inputs (the kernel co-design section of
+ * the Italian news page on MSA lists FP8 among the kernel's precisions; the
+ * definitions are those of msa_select_blocks_fp8): qI fp8 e4m3 [B, 1, G, d_I]
+ * and kI fp8 e4m3 [B, N, d_I], one byte per value, Bk = 128 (otherwise
+ * MSA_ERR_UNSUPPORTED).  idx equals msa_select_blocks_fp8's bit for bit;
+ * everything else (q, K, V, O, lse, the workspace of MSA_OP_DECODE, errors)
+ * as for msa_decode.
+ */
+int msa_decode_fp8(const msa_dims_t *dims, const void *qI, const void *kI, const void *q,
+                   const void *K, const void *V, int32_t *idx, void *O, float *lse, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/*
  * Per-kernel timing, for measurement harnesses.  Between msa_timing_begin and
  * msa_timing_end every launch of the kernel kinds below, by any call on any
  * stream, is bracketed by two HIP events recorded on the stream the kernel is

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from block_sparse_long_index_amd import ops
-from msa_inputs import WORKLOADS, Workload, make_index_inputs
+from msa_inputs import WORKLOADS, Workload, make_index_inputs, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +82,34 @@ def test_fp8_full_equals_bf16(name):
     assert torch.equal(idx16, idx8)
     if w.T == 1:
         assert torch.equal(ops.index_scores(qI, kI), ops.index_scores(to_fp8(qI), to_fp8(kI)))
+
+
+@pytest.mark.parametrize("B,N,Hq,G,k", [
+    (16, 5000, 64, 8, 16),   # 128 rows: the one-workgroup-per-row step
+    (3, 5000, 64, 8, 16),    # 24 rows: the separate top-k, attention and combine
+    (16, 129, 16, 8, 4),     # one key in the last block
+])
+def test_fp8_decode_one_call(B, N, Hq, G, k):
+    """msa_decode_fp8: on integer-valued index inputs the fp8 scan gives the
+    bf16 scan's scores, so idx, O and lse equal msa_decode's bit for bit."""
+    w = Workload("fp8_decode1", B=B, T=1, N=N, Hq=Hq, G=G, k=k, seed=21 + N + B)
+    inp = make_inputs(w, device="cuda")
+    q = inp["q"][:, 0].contiguous()
+    idx, O, lse = ops.decode(inp["qI"], inp["kI"], q, inp["K"], inp["V"], k, return_lse=True)
+    idx8, O8, lse8 = ops.decode(to_fp8(inp["qI"]), to_fp8(inp["kI"]), q, inp["K"], inp["V"], k,
+                                return_lse=True)
+    idx_s = ops.select_blocks(to_fp8(inp["qI"]), to_fp8(inp["kI"]), k)
+    torch.cuda.synchronize()
+    assert torch.equal(idx8, idx_s), "idx differs from msa_select_blocks_fp8"
+    assert torch.equal(idx8, idx) and torch.equal(O8, O) and torch.equal(lse8, lse)
+
+
+def test_fp8_decode_needs_bk128():
+    w = Workload("fp8_decode_bk", B=2, T=1, N=1000, Hq=16, G=2, k=8, Bk=64, seed=4)
+    inp = make_inputs(w, device="cuda")
+    q = inp["q"][:, 0].contiguous()
+    with pytest.raises(ops.MSAError):
+        ops.decode(to_fp8(inp["qI"]), to_fp8(inp["kI"]), q, inp["K"], inp["V"], w.k, Bk=64)
 
 
 def test_fp8_rejects_mixed_dtypes():
