@@ -708,9 +708,13 @@ int msa_sparse_attn_decode(const msa_dims_t* d, const void* q, const void* K, co
 
 }  // extern "C"
 
+// The one-call decode over contiguous caches (pc == kContiguous) or paged
+// pools (pc from check_paged): the scan, then the per-row step kernel or,
+// for small batches, the separate top-k, attention and combine launches.
 static int decode_impl(const msa_dims_t* d, const void* qI, const void* kI, const void* q,
                        const void* K, const void* V, int32_t* idx, void* O, float* lse, void* ws,
-                       size_t ws_bytes, void* stream, bool fp8, const char* name) {
+                       size_t ws_bytes, void* stream, bool fp8, const msa::PagedCache& pc,
+                       const char* name) {
   MSA_TRY(check_dims(d));
   if (d->T != 1) return fail(MSA_ERR_INVALID_ARGUMENT, "%s needs T == 1 (got %lld)", name,
                              (long long)d->T);
@@ -730,21 +734,21 @@ static int decode_impl(const msa_dims_t* d, const void* qI, const void* kI, cons
                 ws_bytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* S = static_cast<float*>(ws);
-  hipError_t e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, d->Bk, kContiguous,
+  hipError_t e = msa::launch_decode_scan(fp8, qI, kI, S, d->B, d->N, d->G, d->Bk, pc,
                                          st);
   if (e == hipSuccess) {
     if (d->B * d->G >= kStepMinRows) {
       e = msa::launch_decode_step(S, q, K, V, idx, O, lse,
                                   static_cast<unsigned char*>(ws) + decode_scores_bytes(d), d->B,
-                                  d->N, d->Hq, d->G, d->k, d->Bk, kContiguous, st);
+                                  d->N, d->Hq, d->G, d->k, d->Bk, pc, st);
     } else {
-      e = msa::launch_topk_rows(S, idx, d->B, 1, 0, 1, d->N, d->G, d->Bk, d->k, kContiguous, st);
+      e = msa::launch_topk_rows(S, idx, d->B, 1, 0, 1, d->N, d->G, d->Bk, d->k, pc, st);
       if (e == hipSuccess) {
         msa::AttnWorkspace w;
         msa::attn_workspace_carve(static_cast<unsigned char*>(ws) + decode_scores_bytes(d), d->B,
                                   d->B, d->N, d->G, d->Hq / d->G, d->k, d->Bk, true, &w);
         e = msa::launch_attn_decode(q, K, V, idx, O, lse, d->B, d->N, d->Hq, d->G, d->k, d->Bk,
-                                    kContiguous, w, st);
+                                    pc, w, st);
       }
     }
   }
@@ -757,14 +761,44 @@ extern "C" {
 int msa_decode(const msa_dims_t* d, const void* qI, const void* kI, const void* q, const void* K,
                const void* V, int32_t* idx, void* O, float* lse, void* ws, size_t ws_bytes,
                void* stream) {
-  return decode_impl(d, qI, kI, q, K, V, idx, O, lse, ws, ws_bytes, stream, false, "msa_decode");
+  return decode_impl(d, qI, kI, q, K, V, idx, O, lse, ws, ws_bytes, stream, false, kContiguous,
+                     "msa_decode");
 }
 
 int msa_decode_fp8(const msa_dims_t* d, const void* qI, const void* kI, const void* q,
                    const void* K, const void* V, int32_t* idx, void* O, float* lse, void* ws,
                    size_t ws_bytes, void* stream) {
-  return decode_impl(d, qI, kI, q, K, V, idx, O, lse, ws, ws_bytes, stream, true,
+  return decode_impl(d, qI, kI, q, K, V, idx, O, lse, ws, ws_bytes, stream, true, kContiguous,
                      "msa_decode_fp8");
+}
+
+static int decode_paged(const msa_dims_t* d, const void* qI, const void* kI_pool, const void* q,
+                        const void* K_pool, const void* V_pool, int64_t num_pages,
+                        const int32_t* block_table, const int64_t* seq_lens, int32_t* idx,
+                        void* O, float* lse, void* ws, size_t ws_bytes, void* stream, bool fp8,
+                        const char* name) {
+  MSA_TRY(check_dims(d));
+  msa::PagedCache pc;
+  MSA_TRY(check_paged(d, num_pages, block_table, seq_lens, &pc));
+  return decode_impl(d, qI, kI_pool, q, K_pool, V_pool, idx, O, lse, ws, ws_bytes, stream, fp8,
+                     pc, name);
+}
+
+int msa_decode_paged(const msa_dims_t* d, const void* qI, const void* kI_pool, const void* q,
+                     const void* K_pool, const void* V_pool, int64_t num_pages,
+                     const int32_t* block_table, const int64_t* seq_lens, int32_t* idx, void* O,
+                     float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return decode_paged(d, qI, kI_pool, q, K_pool, V_pool, num_pages, block_table, seq_lens, idx,
+                      O, lse, ws, ws_bytes, stream, false, "msa_decode_paged");
+}
+
+int msa_decode_paged_fp8(const msa_dims_t* d, const void* qI, const void* kI_pool,
+                         const void* q, const void* K_pool, const void* V_pool,
+                         int64_t num_pages, const int32_t* block_table,
+                         const int64_t* seq_lens, int32_t* idx, void* O, float* lse, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return decode_paged(d, qI, kI_pool, q, K_pool, V_pool, num_pages, block_table, seq_lens, idx,
+                      O, lse, ws, ws_bytes, stream, true, "msa_decode_paged_fp8");
 }
 
 }  // extern "C"

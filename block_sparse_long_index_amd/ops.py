@@ -57,6 +57,10 @@ _SIGS = {
                                                    ctypes.c_size_t, _P]),
     "msa_sparse_attn_decode_paged": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, _P, _P,
                                                     _P, _P, _P, ctypes.c_size_t, _P]),
+    "msa_decode_paged": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int64, _P, _P, _P, _P,
+                                        _P, _P, ctypes.c_size_t, _P]),
+    "msa_decode_paged_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int64, _P, _P, _P,
+                                            _P, _P, _P, ctypes.c_size_t, _P]),
     "msa_timing_begin": (ctypes.c_int, [ctypes.c_int64]),
     "msa_timing_end": (ctypes.c_int, [_P, _P, ctypes.c_int]),
     "msa_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _P]),
@@ -547,3 +551,39 @@ def sparse_attn_decode_paged(q, K_pool, V_pool, block_table, seq_lens, idx, out=
         _ptr(seq_lens), _ptr(idx), _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()),
         "msa_sparse_attn_decode_paged")
     return (O, lse) if return_lse else O
+
+
+def decode_paged(qI, kI_pool, q, K_pool, V_pool, block_table, seq_lens, k, return_lse=False,
+                 out=None, workspace=None):
+    """A decode step over paged pools in one call (msa_decode_paged, or
+    msa_decode_paged_fp8 for float8_e4m3fn index inputs).  qI [B, G, 128] and
+    kI_pool [pages, 128, 128] (same dtype), q [B, Hq, 128] bf16, K_pool /
+    V_pool [pages, G, 128, 128] bf16, block_table int32 [B, nb], seq_lens int64
+    [B] -> (idx [B, G, 1, k], O [B, Hq, 128]) and lse [B, Hq] when return_lse.
+    out: optional (idx, O)."""
+    if qI.dtype not in _INDEX_DTYPES:
+        raise ValueError("qI must be bfloat16 or float8_e4m3fn, got %s" % qI.dtype)
+    B, G, dI = qI.shape
+    _, Hq, dh = q.shape
+    P = K_pool.shape[0]
+    _need(qI, "qI", qI.dtype)
+    _need(kI_pool, "kI_pool", qI.dtype, (P, 128, dI))
+    _need(q, "q", torch.bfloat16, (B, Hq, dh))
+    _need(K_pool, "K_pool", torch.bfloat16, (P, G, 128, dh))
+    _need(V_pool, "V_pool", torch.bfloat16, (P, G, 128, dh))
+    N = _paged_args(block_table, seq_lens, B)
+    d = dims(B, 1, N, Hq, G, k, d_h=dh, d_I=dI)
+    if out is None:
+        idx = torch.empty(B, G, 1, k, dtype=torch.int32, device=q.device)
+        O = torch.empty_like(q)
+    else:
+        idx, O = out
+    _need(idx, "idx", torch.int32, (B, G, 1, k))
+    _need(O, "O", torch.bfloat16, (B, Hq, dh))
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device) if return_lse else None
+    ws, nbytes = _workspace(OP_DECODE, d, workspace)
+    name = "msa_decode_paged" + _INDEX_DTYPES[qI.dtype]
+    _check(getattr(lib(), name)(ctypes.byref(d), _ptr(qI), _ptr(kI_pool), _ptr(q), _ptr(K_pool),
+                                _ptr(V_pool), P, _ptr(block_table), _ptr(seq_lens), _ptr(idx),
+                                _ptr(O), _ptr(lse), _ptr(ws), nbytes, _stream()), name)
+    return (idx, O, lse) if return_lse else (idx, O)

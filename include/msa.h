@@ -363,6 +363,25 @@ int msa_sparse_attn_decode_paged(const msa_dims_t *dims, const void *q, const vo
                                  size_t ws_bytes, void *stream);
 
 /*
+ * msa_decode over paged pools (the serving shape of the llama.cpp analysis
+ * page, sections 4-5): the paged selection and the paged decode attention in
+ * one call, with msa_decode's one-kernel-per-row step.  Arguments as for
+ * msa_select_blocks_paged(_fp8) and msa_sparse_attn_decode_paged, the pools
+ * sharing num_pages and block_table; ws / ws_bytes >= msa_workspace_bytes(
+ * MSA_OP_DECODE).  idx equals msa_select_blocks_paged(_fp8)'s bit for bit, O
+ * and lse are msa_decode's for the sequences the table describes.
+ */
+int msa_decode_paged(const msa_dims_t *dims, const void *qI, const void *kI_pool, const void *q,
+                     const void *K_pool, const void *V_pool, int64_t num_pages,
+                     const int32_t *block_table, const int64_t *seq_lens, int32_t *idx, void *O,
+                     float *lse, void *ws, size_t ws_bytes, void *stream);
+int msa_decode_paged_fp8(const msa_dims_t *dims, const void *qI, const void *kI_pool,
+                         const void *q, const void *K_pool, const void *V_pool,
+                         int64_t num_pages, const int32_t *block_table,
+                         const int64_t *seq_lens, int32_t *idx, void *O, float *lse, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/*
  * A decode step in one call (T == 1): stages 1 to 4 with the results of
  * msa_select_blocks followed by msa_sparse_attn_decode (idx bit for bit; O
  * and lse within the decode tolerance: the slot results are merged in fp32

@@ -22,7 +22,7 @@ def _declared():
 def test_header_functions_are_exported():
     L = ops.lib()
     names = _declared()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(ops._SIGS)

@@ -97,8 +97,18 @@ def test_paged_decode(name, lens, Hq, G, k):
     idx8 = ops.select_blocks_paged(qI.float().to(torch.float8_e4m3fn),
                                    kI_d.float().to(torch.float8_e4m3fn), table_d, lens_t, k)
     O, lse = ops.sparse_attn_decode_paged(q, K_d, V_d, table_d, lens_t, idx, return_lse=True)
+    # the one call (msa_decode_paged, and on the same integer values with
+    # 8-bit index keys: the same scores, so the same bits)
+    idx1, O1, lse1 = ops.decode_paged(qI, kI_d, q, K_d, V_d, table_d, lens_t, k, return_lse=True)
+    idx18, O18, lse18 = ops.decode_paged(qI.float().to(torch.float8_e4m3fn),
+                                         kI_d.float().to(torch.float8_e4m3fn), q, K_d, V_d,
+                                         table_d, lens_t, k, return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx8), "fp8 paged selection differs from bf16"
+    assert torch.equal(idx1, idx), "one-call paged selection differs"
+    assert torch.equal(idx18, idx1) and torch.equal(O18, O1) and torch.equal(lse18, lse1)
+    assert (O1.float() - O.float()).abs().max().item() <= 1e-2
+    assert (lse1 - lse).abs().max().item() <= 1e-3
     for b, sq in enumerate(seqs):
         ref = oracle_seq(sq, Hq, G, k)
         got_idx = idx[b, :, 0].cpu().numpy()
@@ -107,6 +117,9 @@ def test_paged_decode(name, lens, Hq, G, k):
         say("%s seq %d (L=%d) O err max %.3e mean %.3e" % (name, b, sq["L"], err.max(), err.mean()))
         assert err.max() <= O_MAX and err.mean() <= O_MEAN
         assert np.abs(lse[b].cpu().numpy() - ref["lse"][0]).max() <= LSE_TOL
+        err1 = np.abs(O1[b].float().cpu().numpy() - ref["O"][0])
+        assert err1.max() <= O_MAX and err1.mean() <= O_MEAN, (name, b, "one call")
+        assert np.abs(lse1[b].cpu().numpy() - ref["lse"][0]).max() <= LSE_TOL
 
 
 def test_paged_equals_contiguous_full_256k():
@@ -130,6 +143,10 @@ def test_paged_equals_contiguous_full_256k():
     O_c = ops.sparse_attn_decode(q, K, V, idx_c)
     O_p = ops.sparse_attn_decode_paged(q, K_pool.contiguous(), V_pool.contiguous(), table, lens,
                                        idx_p)
+    idx_c1, O_c1 = ops.decode(inp["qI"], kI, q, K, V, w.k)
+    idx_p1, O_p1 = ops.decode_paged(qI, kI_pool, q, K_pool.contiguous(), V_pool.contiguous(),
+                                    table, lens, w.k)
     torch.cuda.synchronize()
     assert torch.equal(idx_c, idx_p)
     assert torch.equal(O_c, O_p)
+    assert torch.equal(idx_p1, idx_c1) and torch.equal(O_p1, O_c1)
