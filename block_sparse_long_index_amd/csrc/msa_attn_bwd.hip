@@ -381,6 +381,9 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
       const int pb = pass & 1;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       f32x16 q0 = f32x16{}, q1 = f32x16{};
+      // raised priority while issuing the MFMAs: the key-gradient waves
+      // wait on the P / dS this wave writes next
+      __builtin_amdgcn_s_setprio(1);
       {
         const unsigned char* qa = qs[pb] + l32 * kBP + half * 16;
         const unsigned char* ga = gs[pb] + l32 * kBP + half * 16;
@@ -401,6 +404,7 @@ __global__ void __launch_bounds__(512, 1) kv_outer_bwd_kernel(BwdArgs a) {
                         q0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // P and c*dS; lane: key key_w, rows m(i) = 8(i/4) + 4 half + i%4
       unsigned char* dsw = dss[pb];
       float pr[16], dsr[16];
